@@ -1,0 +1,381 @@
+"""Pins of the CPU oracle against facts fixed outside it.
+
+The oracle (oracle/oracle.c + oracle/ref.py) defines what the GPU library must
+compute.  These tests tie it to closed forms, library special cases, exact
+rational arithmetic and brute force, so that a dropped term, a wrong sign or
+index, or a transposed operand in the oracle fails here.  No GPU is used.
+"""
+import itertools
+import os
+import random
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+KSP_SETS = [(1, 1, 0), (1, 2, 0), (3, 1, 1), (3, 2, 1), (7, 2, 3)]
+
+
+def rha(fr: Fraction) -> int:
+    """Round half away from zero of an exact rational."""
+    mag = abs(fr)
+    q = int(mag + Fraction(1, 2))  # floor for non-negative
+    return -q if fr < 0 else q
+
+
+def sat8(v: int) -> int:
+    return max(-128, min(127, v))
+
+
+def rand_i8(rng, shape, lo=-128, hi=127):
+    return rng.integers(lo, hi + 1, size=shape, dtype=np.int64).astype(np.int8)
+
+
+def torch_conv_f64(x_nhwc, w_ohwi, stride, pad):
+    """Library special case: float64 conv2d is exact while partial sums < 2^53."""
+    x = torch.from_numpy(x_nhwc.astype(np.float64)).permute(0, 3, 1, 2)
+    w = torch.from_numpy(w_ohwi.astype(np.float64)).permute(0, 3, 1, 2)
+    y = torch.nn.functional.conv2d(x, w, stride=stride, padding=pad)
+    return y.permute(0, 2, 3, 1).numpy().astype(np.int64)
+
+
+# ---------------------------------------------------------------- P1
+@pytest.mark.parametrize("k,s,p", KSP_SETS)
+def test_p1_conv_acc_matches_float64_conv2d(orc, k, s, p):
+    rng = np.random.default_rng(100 + k * 10 + s)
+    for n, h, w, c, oc in [(1, 9, 9, 3, 5), (2, 8, 7, 32, 16), (1, 9, 8, 96, 33), (2, 7, 9, 64, 64)]:
+        if h + 2 * p < k or w + 2 * p < k:
+            continue
+        x = rand_i8(rng, (n, h, w, c))
+        wt = rand_i8(rng, (oc, k, k, c), -127, 127)
+        got = orc.conv_acc(x, wt, s, p).astype(np.int64)
+        exp = torch_conv_f64(x, wt, s, p)
+        assert got.shape == exp.shape
+        np.testing.assert_array_equal(got, exp)
+
+
+# ---------------------------------------------------------------- P2
+@pytest.mark.parametrize("k,s,p", [(3, 2, 1), (7, 2, 3), (3, 1, 1)])
+def test_p2_single_nonzero_kernel(orc, k, s, p):
+    rng = np.random.default_rng(7 * k + s)
+    n, h, w, c, oc = 2, 11, 10, 5, 4
+    x = rand_i8(rng, (n, h, w, c))
+    ho, wo = orc.out_dim(h, k, s, p), orc.out_dim(w, k, s, p)
+    for ky, kx in itertools.product(range(k), range(k)):
+        o_star, i_star, v = (ky + kx) % oc, (ky * k + kx) % c, -117 + ky * 3 + kx
+        wt = np.zeros((oc, k, k, c), np.int8)
+        wt[o_star, ky, kx, i_star] = v
+        acc = orc.conv_acc(x, wt, s, p)
+        exp = np.zeros((n, ho, wo, oc), np.int64)
+        for b, oy, ox in itertools.product(range(n), range(ho), range(wo)):
+            iy, ix = oy * s - p + ky, ox * s - p + kx
+            if 0 <= iy < h and 0 <= ix < w:
+                exp[b, oy, ox, o_star] = v * int(x[b, iy, ix, i_star])
+        np.testing.assert_array_equal(acc, exp)
+
+
+# ---------------------------------------------------------------- P3
+def _golden_pairs(name):
+    rows = []
+    with open(os.path.join(HERE, "golden", name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append([int(t) for t in line.split()])
+    return rows
+
+
+def test_p3_identity_1x1_halves(orc):
+    rows = _golden_pairs("requant_identity_half.txt")
+    xs = np.array([r[0] for r in rows], np.int8)
+    exp = np.array([r[1] for r in rows], np.int8)
+    c = len(xs)
+    # one pixel, C channels; identity weights
+    x = xs.reshape(1, 1, 1, c)
+    wt = np.zeros((c, 1, 1, c), np.int8)
+    for i in range(c):
+        wt[i, 0, 0, i] = 1
+    z = np.zeros(c, np.int32)
+    out = orc.conv_fused(x, wt, z, np.full(c, 1 << 30, np.int32), z, 1, 0, 0)
+    np.testing.assert_array_equal(out.reshape(-1), exp)
+
+
+# ---------------------------------------------------------------- P4
+def _requant_frac(y, mult, shift):
+    return rha(Fraction(y * mult, 2 ** (31 + shift)))
+
+
+def test_p4_requant_matches_exact_rationals(orc):
+    rng = random.Random(4)
+    for shift in range(32):
+        for _ in range(40):
+            mult = rng.randrange(0, 1 << 31)
+            y = rng.randrange(-(1 << 31), 1 << 31)
+            assert orc.requant(y, 0, mult, shift) == _requant_frac(y, mult, shift)
+        # exact ties: v2(y) + v2(mult) = 30 + shift and both odd parts odd
+        for a in range(shift, 31):
+            for _ in range(3):
+                mult = (1 << a) * (2 * rng.randrange(0, 1 << (30 - a)) + 1) if a < 31 else 0
+                if mult >= 1 << 31:
+                    continue
+                e = 30 + shift - a
+                lim = 1 << (31 - e)
+                odd = 2 * rng.randrange(0, max(1, lim // 2)) + 1
+                if odd >= lim:
+                    continue
+                for sign in (1, -1):
+                    y = sign * odd * (1 << e)
+                    if not -(1 << 31) <= y < (1 << 31):
+                        continue
+                    fr = Fraction(y * mult, 2 ** (31 + shift))
+                    assert fr.denominator == 2, (y, mult, shift)  # a genuine tie
+                    assert orc.requant(y, 0, mult, shift) == _requant_frac(y, mult, shift)
+    # extremes
+    for y in (-(1 << 31), (1 << 31) - 1, 0, 1, -1):
+        for mult in (0, 1, (1 << 31) - 1, 1 << 30):
+            for shift in (0, 1, 16, 31):
+                assert orc.requant(y, 0, mult, shift) == _requant_frac(y, mult, shift)
+    # bias enters before the product
+    assert orc.requant(5, -3, 1 << 30, 0) == 1
+    with pytest.raises(OverflowError):
+        orc.requant((1 << 31) - 1, 1, 1 << 30, 0)
+
+
+# ---------------------------------------------------------------- P5
+@pytest.mark.parametrize("c,cpad,k,s,p", [(3, 32, 7, 2, 3), (96, 128, 1, 1, 0), (96, 128, 3, 2, 1)])
+def test_p5_channel_padding_is_neutral(orc, c, cpad, k, s, p):
+    rng = np.random.default_rng(c + k)
+    x = rand_i8(rng, (2, 13, 12, c))
+    wt = rand_i8(rng, (8, k, k, c), -127, 127)
+    xp = np.zeros((2, 13, 12, cpad), np.int8)
+    xp[..., :c] = x
+    wp = np.zeros((8, k, k, cpad), np.int8)
+    wp[..., :c] = wt
+    np.testing.assert_array_equal(orc.conv_acc(x, wt, s, p), orc.conv_acc(xp, wp, s, p))
+
+
+# ---------------------------------------------------------------- P6
+def test_p6_linearity(orc):
+    rng = np.random.default_rng(6)
+    for k, s, p in KSP_SETS:
+        x1 = rand_i8(rng, (2, 9, 9, 6), -64, 63)
+        x2 = rand_i8(rng, (2, 9, 9, 6), -64, 63)
+        w1 = rand_i8(rng, (5, k, k, 6), -63, 63)
+        w2 = rand_i8(rng, (5, k, k, 6), -63, 63)
+        a = lambda xx, ww: orc.conv_acc(xx, ww, s, p).astype(np.int64)  # noqa: E731
+        np.testing.assert_array_equal(a(x1, w1 + w2), a(x1, w1) + a(x1, w2))
+        np.testing.assert_array_equal(a(x1 + x2, w1), a(x1, w1) + a(x2, w1))
+
+
+# ---------------------------------------------------------------- P7
+def test_p7_epilogue_order_hand_cases(orc):
+    rows = _golden_pairs("epilogue_order.txt")
+    qs = np.array([r[0] for r in rows], np.int64)
+    rs = np.array([r[1] for r in rows], np.int8)
+    exp = np.array([r[2] for r in rows], np.int8)
+    c = len(rows)
+    # mult = 2^30, shift = 0 gives q = round(y/2); y = 2q is exact
+    acc = (2 * qs).astype(np.int32).reshape(1, 1, 1, c)
+    out = orc.epilogue(acc, np.zeros(c, np.int32), np.full(c, 1 << 30, np.int32), np.zeros(c, np.int32),
+                       residual=rs.reshape(1, 1, 1, c), flags=orc.RESIDUAL | orc.RELU)
+    np.testing.assert_array_equal(out.reshape(-1), exp)
+
+
+def test_p7_saturation_orders_agree_for_nonnegative_shortcut(orc):
+    qs = np.arange(-(1 << 17), (1 << 17) + 1, 7, dtype=np.int64)
+    for r in (0, 1, 63, 127):
+        c = len(qs)
+        acc = (2 * qs).astype(np.int32).reshape(1, 1, 1, c)
+        out = orc.epilogue(acc, np.zeros(c, np.int32), np.full(c, 1 << 30, np.int32),
+                           np.zeros(c, np.int32), residual=np.full((1, 1, 1, c), r, np.int8),
+                           flags=orc.RESIDUAL | orc.RELU).reshape(-1).astype(np.int64)
+        sat_first = np.clip(np.maximum(np.clip(qs, -128, 127) + r, 0), -128, 127)
+        np.testing.assert_array_equal(out, sat_first)
+
+
+# ---------------------------------------------------------------- P8
+def test_p8_maxpool_matches_torch_and_commutes(orc):
+    rng = np.random.default_rng(8)
+    for h, w in [(7, 7), (8, 9), (112, 112)]:
+        x = rand_i8(rng, (1, h, w, 3))
+        got = orc.maxpool3s2p1(x)
+        t = torch.from_numpy(x.astype(np.float64)).permute(0, 3, 1, 2)
+        exp = torch.nn.functional.max_pool2d(t, 3, 2, 1).permute(0, 2, 3, 1).numpy()
+        np.testing.assert_array_equal(got, exp.astype(np.int8))
+    # pool(epilogue(acc)) == epilogue(pool(acc)) for mult >= 0 (monotone epilogue)
+    acc = rng.integers(-300000, 300000, size=(2, 11, 10, 4)).astype(np.int32)
+    bias = rng.integers(-(1 << 16), 1 << 16, size=4).astype(np.int32)
+    mult = rng.integers(1 << 30, 1 << 31, size=4).astype(np.int32)
+    shift = rng.integers(8, 12, size=4).astype(np.int32)
+    a = orc.maxpool3s2p1(orc.epilogue(acc, bias, mult, shift, flags=orc.RELU))
+    # max-pool the int32 accumulators directly (torch float64 is exact here)
+    t = torch.from_numpy(acc.astype(np.float64)).permute(0, 3, 1, 2)
+    pooled = torch.nn.functional.max_pool2d(t, 3, 2, 1).permute(0, 2, 3, 1).numpy().astype(np.int32)
+    b = orc.epilogue(pooled, bias, mult, shift, flags=orc.RELU)
+    np.testing.assert_array_equal(a, b)
+
+
+# ---------------------------------------------------------------- P9
+def test_p9_bn_folding_in_exact_rationals(orc):
+    """Explicit conv -> BN(gamma, beta, mu, sigma) -> round half away equals
+    the folded integer form (bias, mult, shift) that the oracle evaluates."""
+    rng = np.random.default_rng(9)
+    prng = random.Random(9)
+    n, h, w, c, oc, k, s, p = 1, 6, 5, 7, 3, 3, 1, 1
+    x = rand_i8(rng, (n, h, w, c), 0, 127)
+    wt = rand_i8(rng, (oc, k, k, c), -127, 127)
+    bias = rng.integers(-(1 << 16), 1 << 16, size=oc).astype(np.int32)
+    mult = rng.integers(1 << 30, 1 << 31, size=oc).astype(np.int32)
+    shift = rng.integers(4, 9, size=oc).astype(np.int32)
+    res = rand_i8(rng, (n, h, w, oc), -128, 127)
+    z = torch_conv_f64(x, wt, s, p)  # exact integer conv, independent of the oracle
+    expect = np.empty((n, h, w, oc), np.int8)
+    for o in range(oc):
+        S = Fraction(int(mult[o]), 2 ** (31 + int(shift[o])))
+        sigma = Fraction(prng.randrange(1, 1000), prng.randrange(1, 1000))
+        gamma = S * sigma
+        mu = Fraction(prng.randrange(-10 ** 6, 10 ** 6), prng.randrange(1, 97))
+        beta = int(bias[o]) * S + mu * gamma / sigma
+        for idx in itertools.product(range(n), range(h), range(w)):
+            bn = gamma * (int(z[idx + (o,)]) - mu) / sigma + beta
+            q = rha(bn) + int(res[idx + (o,)])
+            expect[idx + (o,)] = sat8(max(q, 0))
+    got = orc.conv_fused(x, wt, bias, mult, shift, s, p, orc.RESIDUAL | orc.RELU, residual=res)
+    np.testing.assert_array_equal(got, expect)
+    # fold linearity: scaling the weights scales the accumulator
+    w3 = np.clip(wt.astype(np.int64) // 3, -42, 42).astype(np.int8)
+    np.testing.assert_array_equal(orc.conv_acc(x, (3 * w3).astype(np.int8), s, p).astype(np.int64),
+                                  3 * orc.conv_acc(x, w3, s, p).astype(np.int64))
+
+
+# ---------------------------------------------------------------- P10
+def test_p10_avgpool_rounding(orc):
+    rng = np.random.default_rng(10)
+    x = rand_i8(rng, (3, 7, 7, 40))
+    got = orc.avgpool(x)
+    sums = x.astype(np.int64).sum(axis=(1, 2))
+    for b, ch in itertools.product(range(3), range(40)):
+        assert got[b, ch] == sat8(rha(Fraction(int(sums[b, ch]), 49)))
+    # 49 is odd: s/49 is never exactly half-way, over the whole reachable range
+    s = np.arange(-49 * 128, 49 * 127 + 1)
+    assert not np.any((2 * s) % 98 == 49)
+    # a 2x2 pool can tie: ties go away from zero
+    t = np.array([[[[1], [1]], [[0], [0]]], [[[-1], [-1]], [[0], [0]]]], np.int8)  # sums 2 and -2
+    np.testing.assert_array_equal(orc.avgpool(t).reshape(-1), np.array([1, -1], np.int8))
+
+
+# ---------------------------------------------------------------- P11
+def test_p11_fc_matches_int64_matmul(orc):
+    rng = np.random.default_rng(11)
+    a = rand_i8(rng, (5, 2048))
+    w = rand_i8(rng, (1000, 2048), -127, 127)
+    bias = rng.integers(-(1 << 16), 1 << 16, size=1000).astype(np.int32)
+    got = orc.fc(a, w, bias)
+    exp = a.astype(np.int64) @ w.astype(np.int64).T + bias.astype(np.int64)
+    np.testing.assert_array_equal(got.astype(np.int64), exp)
+
+
+# ---------------------------------------------------------------- P12
+def _rand_conv(rng, cin, cout, k, s, p):
+    from oracle.ref import ConvParams
+    return ConvParams(rand_i8(rng, (cout, k, k, cin), -127, 127),
+                      rng.integers(-(1 << 16), 1 << 16, size=cout).astype(np.int32),
+                      rng.integers(1 << 30, 1 << 31, size=cout).astype(np.int32),
+                      rng.integers(8, 12, size=cout).astype(np.int32), s, p)
+
+
+def test_p12_block_composition_and_batch_independence(orc):
+    rng = np.random.default_rng(12)
+    cin, wd = 64, 32
+    c1 = _rand_conv(rng, cin, wd, 1, 1, 0)
+    c2 = _rand_conv(rng, wd, wd, 3, 2, 1)
+    c3 = _rand_conv(rng, wd, 4 * wd, 1, 1, 0)
+    pj = _rand_conv(rng, cin, 4 * wd, 1, 2, 0)
+    x = rand_i8(rng, (3, 9, 8, cin), 0, 127)
+    y = orc.block(x, c1, c2, c3, pj)
+    # composition wired independently: accumulators from torch float64 conv2d,
+    # epilogue from the (separately pinned) oracle epilogue
+    def ep(acc, cp, flags, res=None):
+        return orc.epilogue(acc.astype(np.int32), cp.bias, cp.mult, cp.shift, res, flags)
+    t1 = ep(torch_conv_f64(x, c1.w, 1, 0), c1, orc.RELU)
+    t2 = ep(torch_conv_f64(t1, c2.w, 2, 1), c2, orc.RELU)
+    sc = ep(torch_conv_f64(x, pj.w, 2, 0), pj, 0)
+    y2 = ep(torch_conv_f64(t2, c3.w, 1, 0), c3, orc.RESIDUAL | orc.RELU, sc)
+    np.testing.assert_array_equal(y, y2)
+    # batch independence: permuting images permutes outputs
+    perm = [2, 0, 1]
+    np.testing.assert_array_equal(orc.block(x[perm], c1, c2, c3, pj), y[perm])
+
+
+def test_p12_net_batch_split_invariance(orc):
+    from oracle.ref import BlockParams
+    rng = np.random.default_rng(13)
+    stem = _rand_conv(rng, 3, 16, 7, 2, 3)
+    blocks = [BlockParams(_rand_conv(rng, 16, 8, 1, 1, 0), _rand_conv(rng, 8, 8, 3, 2, 1),
+                          _rand_conv(rng, 8, 32, 1, 1, 0), _rand_conv(rng, 16, 32, 1, 2, 0)),
+              BlockParams(_rand_conv(rng, 32, 8, 1, 1, 0), _rand_conv(rng, 8, 8, 3, 1, 1),
+                          _rand_conv(rng, 8, 32, 1, 1, 0), None)]
+    fw = rand_i8(rng, (10, 32), -127, 127)
+    fb = rng.integers(-100, 100, size=10).astype(np.int32)
+    x = rand_i8(rng, (3, 32, 32, 3))
+    full = orc.net(x, stem, blocks, fw, fb)
+    parts = np.concatenate([orc.net(x[i:i + 1], stem, blocks, fw, fb) for i in range(3)])
+    np.testing.assert_array_equal(full, parts)
+    assert full.dtype == np.int32 and full.shape == (3, 10)
+
+
+# ---------------------------------------------------------------- P13
+def test_p13_act_pack_roundtrip_and_layout(orc):
+    rng = np.random.default_rng(14)
+    for c in (3, 32, 64, 96, 130):
+        x = rand_i8(rng, (2, 5, 6, c))
+        blk = orc.pack_act(x)
+        c1 = (c + 31) // 32
+        # independent statement of the layout: pad channels, split C=(C1,32), move C1 ahead of H,W
+        xp = np.zeros((2, 5, 6, c1 * 32), np.int8)
+        xp[..., :c] = x
+        exp = xp.reshape(2, 5, 6, c1, 32).transpose(0, 3, 1, 2, 4)
+        np.testing.assert_array_equal(blk, exp)
+        np.testing.assert_array_equal(orc.unpack_act(blk, c), x)
+
+
+def test_p13_weight_pack_layout(orc):
+    rng = np.random.default_rng(15)
+    for oc, k, ic in [(512, 1, 128), (64, 3, 64), (1000, 1, 2048), (96, 3, 40), (256, 1, 64)]:
+        w = rand_i8(rng, (oc, k, k, ic), -127, 127)
+        blk = orc.pack_weights(w)
+        o2 = min(128, (oc + 31) // 32 * 32)
+        o1 = (oc + o2 - 1) // o2
+        i1 = (ic + 31) // 32
+        wp = np.zeros((o1 * o2, k, k, i1 * 32), np.int8)
+        wp[:oc, :, :, :ic] = w
+        exp = wp.reshape(o1, o2, k, k, i1, 32).transpose(0, 2, 3, 4, 1, 5)
+        np.testing.assert_array_equal(blk, exp)
+    # the article's 1x1 example: [Ic,Oc] = [128,512] -> [O1,I1,O2,I2] = [4,4,128,32]
+    assert orc.pack_weights(np.zeros((512, 1, 1, 128), np.int8)).shape == (4, 1, 1, 4, 128, 32)
+    w = rand_i8(rng, (64, 7, 7, 3), -127, 127)
+    st = orc.pack_weights_stem(w)
+    exp = np.zeros((64, 8, 8, 4), np.int8)
+    exp[:, :7, :7, :3] = w
+    np.testing.assert_array_equal(st, exp)
+
+
+# ---------------------------------------------------------------- P14
+def test_p14_int32_safety(orc):
+    from convolution_int8_implicit_amd import synth
+    # every layer of every workload keeps |acc + bias| below 2^31
+    net = synth.resnet50_spec()
+    convs = [net.stem] + [c for b in net.blocks for c in (b.c1, b.c2, b.c3, b.proj) if c is not None]
+    for wl in synth.workloads():
+        convs += wl.convs
+    for cs in convs:
+        kred = cs.k * cs.k * cs.c_in
+        assert kred * 128 * 127 + (1 << 16) < (1 << 31), cs
+    assert net.fc_in * 128 * 127 + (1 << 16) < (1 << 31)
+    # a forced overflow is reported, not wrapped
+    x = np.full((1, 1, 1, 140000), -128, np.int8)
+    w = np.full((1, 1, 1, 140000), -127, np.int8)
+    with pytest.raises(OverflowError):
+        orc.conv_acc(x, w, 1, 0)
