@@ -1,1 +1,222 @@
-"""MI355X-native fused int8 ResNet convolution (placeholder; binding added below)."""
+"""MI355X-native fused int8 ResNet convolution: Python binding of libifx.so.
+
+The compute path is the C-ABI library built from csrc/ (hand-written gfx950
+HIP kernels); this module only marshals arguments.  Tensors are torch device
+tensors (torch supplies memory and streams); every step of the path runs in
+the library's kernels.  There is no fallback: if the library is not built the
+first call raises.
+
+Entry points mirror include/ifx.h:
+    conv_validate, conv_out_dims, act_bytes, wpack_bytes,
+    pack_act, unpack_act, pack_weights, conv_fused,
+    block_workspace_bytes, block_forward, net_workspace_bytes, net_forward,
+    status_string, last_hip_error, version
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+__all__ = [
+    "RELU", "RESIDUAL", "MAXPOOL", "OUT_I32", "IfxError", "ConvDesc", "BlockParams", "NetParams", "lib",
+    "conv_desc", "conv_validate", "conv_out_dims", "act_bytes", "wpack_bytes", "pack_act", "unpack_act",
+    "pack_weights", "conv_fused", "block_workspace_bytes", "block_forward", "net_workspace_bytes",
+    "net_forward", "status_string", "last_hip_error", "version", "LIB_PATH",
+]
+
+RELU, RESIDUAL, MAXPOOL, OUT_I32 = 1, 2, 4, 8
+STATUS = {0: "IFX_OK", 1: "IFX_E_NULL", 2: "IFX_E_SHAPE", 3: "IFX_E_UNSUPPORTED", 4: "IFX_E_ALIGN",
+          5: "IFX_E_WORKSPACE", 6: "IFX_E_HIP"}
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libifx.so")
+
+
+class IfxError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        name = STATUS.get(status, str(status))
+        extra = ""
+        if status == 6:
+            extra = f" (hipError {last_hip_error()})"
+        super().__init__(f"{what}: {name}{extra}")
+
+
+class ConvDesc(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int32), ("h", ctypes.c_int32), ("w", ctypes.c_int32), ("c_in", ctypes.c_int32),
+                ("c_out", ctypes.c_int32), ("kh", ctypes.c_int32), ("kw", ctypes.c_int32),
+                ("stride", ctypes.c_int32), ("pad", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
+class BlockParams(ctypes.Structure):
+    _fields_ = [("d", ConvDesc * 4), ("has_proj", ctypes.c_int32), ("w_blk", ctypes.c_void_p * 4),
+                ("bias", ctypes.c_void_p * 4), ("mult", ctypes.c_void_p * 4), ("shift", ctypes.c_void_p * 4)]
+
+
+class NetParams(ctypes.Structure):
+    _fields_ = [("stem", ConvDesc), ("stem_w", ctypes.c_void_p), ("stem_bias", ctypes.c_void_p),
+                ("stem_mult", ctypes.c_void_p), ("stem_shift", ctypes.c_void_p), ("n_blocks", ctypes.c_int32),
+                ("blocks", ctypes.POINTER(BlockParams)), ("fc_w_blk", ctypes.c_void_p),
+                ("fc_bias", ctypes.c_void_p), ("fc_in", ctypes.c_int32), ("fc_out", ctypes.c_int32),
+                ("sub_batch", ctypes.c_int32)]
+
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libifx.so (raises if it has not been built)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"libifx.so not built ({LIB_PATH}); run python -m convolution_int8_implicit_amd.build")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    D = ctypes.POINTER(ConvDesc)
+    sigs = {
+        "ifx_conv_validate": ([D], i32),
+        "ifx_conv_out_dims": ([D, ctypes.POINTER(i32), ctypes.POINTER(i32)], i32),
+        "ifx_act_bytes": ([i32, i32, i32, i32], sz),
+        "ifx_wpack_bytes": ([D], sz),
+        "ifx_pack_act": ([vp, vp, i32, i32, i32, i32, vp], i32),
+        "ifx_unpack_act": ([vp, vp, i32, i32, i32, i32, vp], i32),
+        "ifx_pack_weights": ([D, vp, vp, vp], i32),
+        "ifx_conv_fused": ([D, vp, vp, vp, vp, vp, vp, vp, vp], i32),
+        "ifx_block_workspace_bytes": ([ctypes.POINTER(BlockParams)], sz),
+        "ifx_block_forward": ([ctypes.POINTER(BlockParams), vp, vp, vp, sz, vp], i32),
+        "ifx_net_workspace_bytes": ([ctypes.POINTER(NetParams), i32], sz),
+        "ifx_net_forward": ([ctypes.POINTER(NetParams), vp, vp, i32, vp, sz, vp], i32),
+        "ifx_status_string": ([i32], ctypes.c_char_p),
+        "ifx_last_hip_error": ([], i32),
+        "ifx_version": ([], i32),
+    }
+    for name, (args, res) in sigs.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = res
+    _LIB = L
+    return L
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> Optional[ctypes.c_void_p]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise IfxError(rc, what)
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("libifx takes contiguous device tensors")
+
+
+def conv_desc(n, h, w, c_in, c_out, kh, kw, stride, pad, flags) -> ConvDesc:
+    return ConvDesc(n, h, w, c_in, c_out, kh, kw, stride, pad, flags)
+
+
+def conv_validate(d: ConvDesc) -> int:
+    return lib().ifx_conv_validate(ctypes.byref(d))
+
+
+def conv_out_dims(d: ConvDesc):
+    ho, wo = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().ifx_conv_out_dims(ctypes.byref(d), ctypes.byref(ho), ctypes.byref(wo)), "ifx_conv_out_dims")
+    return ho.value, wo.value
+
+
+def act_bytes(n, h, w, c) -> int:
+    return lib().ifx_act_bytes(n, h, w, c)
+
+
+def wpack_bytes(d: ConvDesc) -> int:
+    return lib().ifx_wpack_bytes(ctypes.byref(d))
+
+
+def pack_act(x_nhwc: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """NHWC int8 -> packed NC/32HW32 [n, ceil(c/32), h, w, 32]."""
+    _dev(x_nhwc, out)
+    n, h, w, c = x_nhwc.shape
+    if out is None:
+        out = torch.empty((n, (c + 31) // 32, h, w, 32), dtype=torch.int8, device=x_nhwc.device)
+    _check(lib().ifx_pack_act(_ptr(x_nhwc), _ptr(out), n, h, w, c, _stream(stream)), "ifx_pack_act")
+    return out
+
+
+def unpack_act(x_blk: torch.Tensor, c: int, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Packed [n, c1, h, w, 32] -> NHWC [n, h, w, c]."""
+    _dev(x_blk, out)
+    n, _, h, w, _ = x_blk.shape
+    if out is None:
+        out = torch.empty((n, h, w, c), dtype=torch.int8, device=x_blk.device)
+    _check(lib().ifx_unpack_act(_ptr(x_blk), _ptr(out), n, h, w, c, _stream(stream)), "ifx_unpack_act")
+    return out
+
+
+def pack_weights(d: ConvDesc, w_ohwi: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """OHWI int8 -> the packed weight layout of d (flat int8 tensor)."""
+    _dev(w_ohwi, out)
+    nbytes = wpack_bytes(d)
+    if nbytes == 0:
+        raise IfxError(conv_validate(d) or 2, "ifx_wpack_bytes")
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.int8, device=w_ohwi.device)
+    _check(lib().ifx_pack_weights(ctypes.byref(d), _ptr(w_ohwi), _ptr(out), _stream(stream)), "ifx_pack_weights")
+    return out
+
+
+def conv_fused(d: ConvDesc, x_blk, w_blk, bias, mult, shift, residual, y, stream=None) -> None:
+    _dev(x_blk, w_blk, bias, mult, shift, residual, y)
+    _check(lib().ifx_conv_fused(ctypes.byref(d), _ptr(x_blk), _ptr(w_blk), _ptr(bias), _ptr(mult), _ptr(shift),
+                                _ptr(residual), _ptr(y), _stream(stream)), "ifx_conv_fused")
+
+
+def block_workspace_bytes(p: BlockParams) -> int:
+    return lib().ifx_block_workspace_bytes(ctypes.byref(p))
+
+
+def block_forward(p: BlockParams, x_blk, y_blk, ws: torch.Tensor, stream=None) -> None:
+    _dev(x_blk, y_blk, ws)
+    _check(lib().ifx_block_forward(ctypes.byref(p), _ptr(x_blk), _ptr(y_blk), _ptr(ws), ws.numel() * ws.element_size(),
+                                   _stream(stream)), "ifx_block_forward")
+
+
+def net_workspace_bytes(p: NetParams, n: int) -> int:
+    return lib().ifx_net_workspace_bytes(ctypes.byref(p), n)
+
+
+def net_forward(p: NetParams, x_blk, logits, n: int, ws: torch.Tensor, stream=None) -> None:
+    _dev(x_blk, logits, ws)
+    _check(lib().ifx_net_forward(ctypes.byref(p), _ptr(x_blk), _ptr(logits), n, _ptr(ws),
+                                 ws.numel() * ws.element_size(), _stream(stream)), "ifx_net_forward")
+
+
+def status_string(s: int) -> str:
+    return lib().ifx_status_string(s).decode()
+
+
+def last_hip_error() -> int:
+    return lib().ifx_last_hip_error()
+
+
+def version() -> int:
+    return lib().ifx_version()
+
+
+def exported_symbols() -> Sequence[str]:
+    return [n for n in dir(lib()) if n.startswith("ifx_")]

@@ -1,0 +1,479 @@
+// C ABI of the fused int8 convolution library: host-side validation, launch
+// dispatch and the bottleneck / network drivers.  Every check runs on the
+// host before the first launch, so error paths need no device; the launch
+// paths only enqueue kernels on the caller's stream (no allocation, no
+// memset, no synchronisation), which also makes them safe to capture into a
+// HIP graph.
+#include "ifx.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "ifx_internal.h"
+
+namespace {
+
+thread_local int32_t g_last_hip = 0;
+
+enum Kind { kGeneric, kStem };
+
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline int out_dim(int in, int k, int s, int p)
+{
+    long long span = (long long)in + 2LL * p - k;
+    if (span < 0 || s <= 0) return 0;
+    return (int)(span / s + 1);
+}
+
+inline int wgroup(int oc)
+{
+    int r = (oc + 31) / 32 * 32;
+    return r < 128 ? r : 128;
+}
+
+inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+size_t act_bytes(long long n, long long h, long long w, long long c)
+{
+    if (n <= 0 || h <= 0 || w <= 0 || c <= 0) return 0;
+    return (size_t)(n * ((c + 31) / 32) * h * w * 32);
+}
+
+struct Dims {
+    int ho, wo;   // convolution output
+    int oh, ow;   // tensor written (pooled when MAXPOOL)
+};
+
+ifx_status check_desc(const ifx_conv_desc *d, Kind *kind, Dims *dims)
+{
+    if (!d) return IFX_E_NULL;
+    if (d->n <= 0 || d->h <= 0 || d->w <= 0 || d->c_in <= 0 || d->c_out <= 0 || d->kh <= 0 || d->kw <= 0 ||
+        d->stride <= 0 || d->pad < 0)
+        return IFX_E_SHAPE;
+    const uint32_t f = d->flags;
+    if (f & ~(uint32_t)(IFX_RELU | IFX_RESIDUAL | IFX_MAXPOOL | IFX_OUT_I32)) return IFX_E_UNSUPPORTED;
+    Dims dm;
+    dm.ho = out_dim(d->h, d->kh, d->stride, d->pad);
+    dm.wo = out_dim(d->w, d->kw, d->stride, d->pad);
+    if (dm.ho <= 0 || dm.wo <= 0) return IFX_E_SHAPE;
+    dm.oh = dm.ho;
+    dm.ow = dm.wo;
+    Kind k;
+    const int kh = d->kh, kw = d->kw, s = d->stride, p = d->pad;
+    if (kh == 7 && kw == 7 && s == 2 && p == 3) {
+        if (!(f & IFX_MAXPOOL) || (f & (IFX_RESIDUAL | IFX_OUT_I32))) return IFX_E_UNSUPPORTED;
+        if (d->c_in > 4 || d->c_out != 64) return IFX_E_UNSUPPORTED;
+        dm.oh = out_dim(dm.ho, 3, 2, 1);
+        dm.ow = out_dim(dm.wo, 3, 2, 1);
+        if (dm.oh <= 0 || dm.ow <= 0) return IFX_E_SHAPE;
+        k = kStem;
+    } else if ((kh == 1 && kw == 1 && p == 0 && (s == 1 || s == 2)) ||
+               (kh == 3 && kw == 3 && p == 1 && (s == 1 || s == 2))) {
+        if (f & IFX_MAXPOOL) return IFX_E_UNSUPPORTED;
+        if ((f & IFX_OUT_I32) && (f & (IFX_RELU | IFX_RESIDUAL))) return IFX_E_UNSUPPORTED;
+        k = kGeneric;
+    } else {
+        return IFX_E_UNSUPPORTED;
+    }
+    // GEMM rows and per-image input planes are indexed with 32-bit integers
+    if ((long long)d->n * dm.ho * dm.wo > 0x7fffffffLL || (long long)d->n * d->h * d->w > 0x7fffffffLL ||
+        (long long)d->c_out * 16 > 0x7fffffffLL)
+        return IFX_E_SHAPE;
+    if (kind) *kind = k;
+    if (dims) *dims = dm;
+    return IFX_OK;
+}
+
+ifx_status hip_status(hipError_t e)
+{
+    if (e == hipSuccess) return IFX_OK;
+    g_last_hip = (int32_t)e;
+    return IFX_E_HIP;
+}
+
+// Launch one validated convolution.
+ifx_status run_conv(const ifx_conv_desc *d, Kind kind, const Dims &dm, const int8_t *x, const int8_t *w,
+                    const int32_t *bias, const int32_t *mult, const int32_t *shift, const int8_t *res, void *y,
+                    hipStream_t s)
+{
+    if (kind == kStem) {
+        ifx::StemArgs a;
+        a.x = x;
+        a.wt = w;
+        a.bias = bias;
+        a.mult = mult;
+        a.shift = shift;
+        a.y = (int8_t *)y;
+        a.n = d->n;
+        a.h = d->h;
+        a.w = d->w;
+        a.ho = dm.ho;
+        a.wo = dm.wo;
+        a.ph = dm.oh;
+        a.pw = dm.ow;
+        a.relu = (d->flags & IFX_RELU) ? 1 : 0;
+        return hip_status(ifx::launch_stem(a, s));
+    }
+    ifx::ConvArgs a;
+    a.x = x;
+    a.wt = w;
+    a.bias = bias;
+    a.mult = mult;
+    a.shift = shift;
+    a.res = res;
+    a.y = y;
+    a.n = d->n;
+    a.h = d->h;
+    a.w = d->w;
+    a.i1 = (d->c_in + 31) / 32;
+    a.ho = dm.ho;
+    a.wo = dm.wo;
+    a.oc = d->c_out;
+    a.oc1 = (d->c_out + 31) / 32;
+    a.o2 = wgroup(d->c_out);
+    a.stride = d->stride;
+    a.pad = d->pad;
+    a.m = d->n * dm.ho * dm.wo;
+    a.nkb = d->kh * d->kw * a.i1;
+    a.relu = (d->flags & IFX_RELU) ? 1 : 0;
+    a.residual = (d->flags & IFX_RESIDUAL) ? 1 : 0;
+    a.out_i32 = (d->flags & IFX_OUT_I32) ? 1 : 0;
+    return hip_status(ifx::launch_conv(a, d->kh, d->kw, s));
+}
+
+ifx_status check_conv_ptrs(const ifx_conv_desc *d, const int8_t *x, const int8_t *w, const int32_t *bias,
+                           const int32_t *mult, const int32_t *shift, const int8_t *res, const void *y)
+{
+    const bool i32 = (d->flags & IFX_OUT_I32) != 0;
+    if (!x || !w || !bias || !y) return IFX_E_NULL;
+    if (!i32 && (!mult || !shift)) return IFX_E_NULL;
+    if ((d->flags & IFX_RESIDUAL) && !res) return IFX_E_NULL;
+    if (!aligned16(x) || !aligned16(w) || !aligned16(bias) || !aligned16(y)) return IFX_E_ALIGN;
+    if (!i32 && (!aligned16(mult) || !aligned16(shift))) return IFX_E_ALIGN;
+    if ((d->flags & IFX_RESIDUAL) && !aligned16(res)) return IFX_E_ALIGN;
+    return IFX_OK;
+}
+
+// ---- bottleneck ----
+
+struct BlockPlan {
+    Kind kind[4];
+    Dims dims[4];
+    size_t t1, t2, sc;  // workspace pieces (bytes, 256-aligned)
+};
+
+bool flags_plain(uint32_t f) { return (f & (IFX_RESIDUAL | IFX_MAXPOOL | IFX_OUT_I32)) == 0; }
+
+// Validate the block's descriptors for batch n (n <= 0: use d[0].n) and their chaining.
+ifx_status plan_block(const ifx_block_params *p, int n, BlockPlan *plan)
+{
+    if (!p) return IFX_E_NULL;
+    ifx_conv_desc d[4];
+    const int nd = p->has_proj ? 4 : 3;
+    for (int i = 0; i < nd; ++i) {
+        d[i] = p->d[i];
+        if (n > 0) d[i].n = n;
+    }
+    for (int i = 0; i < nd; ++i) {
+        ifx_status st = check_desc(&d[i], &plan->kind[i], &plan->dims[i]);
+        if (st != IFX_OK) return st;
+        if (plan->kind[i] != kGeneric) return IFX_E_UNSUPPORTED;
+        if (d[i].flags & IFX_OUT_I32) return IFX_E_UNSUPPORTED;
+    }
+    if (!flags_plain(d[0].flags) || !flags_plain(d[1].flags)) return IFX_E_UNSUPPORTED;
+    if (!(d[2].flags & IFX_RESIDUAL) || (d[2].flags & (IFX_MAXPOOL | IFX_OUT_I32))) return IFX_E_UNSUPPORTED;
+    if (p->has_proj && !flags_plain(d[3].flags)) return IFX_E_UNSUPPORTED;
+    const Dims &a = plan->dims[0], &b = plan->dims[1], &c = plan->dims[2];
+    if (d[1].n != d[0].n || d[2].n != d[0].n) return IFX_E_SHAPE;
+    if (d[1].c_in != d[0].c_out || d[1].h != a.oh || d[1].w != a.ow) return IFX_E_SHAPE;
+    if (d[2].c_in != d[1].c_out || d[2].h != b.oh || d[2].w != b.ow) return IFX_E_SHAPE;
+    if (p->has_proj) {
+        const Dims &q = plan->dims[3];
+        if (d[3].n != d[0].n || d[3].c_in != d[0].c_in || d[3].h != d[0].h || d[3].w != d[0].w) return IFX_E_SHAPE;
+        if (d[3].c_out != d[2].c_out || q.oh != c.oh || q.ow != c.ow) return IFX_E_SHAPE;
+    } else {
+        if (d[2].c_out != d[0].c_in || c.oh != d[0].h || c.ow != d[0].w) return IFX_E_SHAPE;
+    }
+    plan->t1 = round_up(act_bytes(d[0].n, a.oh, a.ow, d[0].c_out), 256);
+    plan->t2 = round_up(act_bytes(d[1].n, b.oh, b.ow, d[1].c_out), 256);
+    plan->sc = p->has_proj ? round_up(act_bytes(d[3].n, plan->dims[3].oh, plan->dims[3].ow, d[3].c_out), 256) : 0;
+    return IFX_OK;
+}
+
+ifx_status check_block_ptrs(const ifx_block_params *p)
+{
+    const int nd = p->has_proj ? 4 : 3;
+    for (int i = 0; i < nd; ++i) {
+        if (!p->w_blk[i] || !p->bias[i] || !p->mult[i] || !p->shift[i]) return IFX_E_NULL;
+        if (!aligned16(p->w_blk[i]) || !aligned16(p->bias[i]) || !aligned16(p->mult[i]) || !aligned16(p->shift[i]))
+            return IFX_E_ALIGN;
+    }
+    return IFX_OK;
+}
+
+// Launch a validated block for batch n; workspace already checked.
+ifx_status run_block(const ifx_block_params *p, const BlockPlan &plan, int n, const int8_t *x, int8_t *y,
+                     int8_t *ws, hipStream_t s)
+{
+    ifx_conv_desc d[4];
+    const int nd = p->has_proj ? 4 : 3;
+    for (int i = 0; i < nd; ++i) {
+        d[i] = p->d[i];
+        d[i].n = n;
+    }
+    int8_t *t1 = ws;
+    int8_t *t2 = ws + plan.t1;
+    int8_t *sc = ws + plan.t1 + plan.t2;
+    ifx_status st;
+    st = run_conv(&d[0], kGeneric, plan.dims[0], x, p->w_blk[0], p->bias[0], p->mult[0], p->shift[0], nullptr, t1, s);
+    if (st != IFX_OK) return st;
+    st = run_conv(&d[1], kGeneric, plan.dims[1], t1, p->w_blk[1], p->bias[1], p->mult[1], p->shift[1], nullptr, t2, s);
+    if (st != IFX_OK) return st;
+    const int8_t *res = x;
+    if (p->has_proj) {
+        st = run_conv(&d[3], kGeneric, plan.dims[3], x, p->w_blk[3], p->bias[3], p->mult[3], p->shift[3], nullptr,
+                      sc, s);
+        if (st != IFX_OK) return st;
+        res = sc;
+    }
+    return run_conv(&d[2], kGeneric, plan.dims[2], t2, p->w_blk[2], p->bias[2], p->mult[2], p->shift[2], res, y, s);
+}
+
+// ---- network ----
+
+struct NetPlan {
+    Kind stem_kind;
+    Dims stem_dims;
+    size_t act, t1, t2, sc, pool;  // workspace pieces for batch nb
+    int out_h, out_w, out_c;       // backbone output
+    int nb;                        // images per pass
+};
+
+ifx_status plan_net(const ifx_net_params *p, int n, NetPlan *plan)
+{
+    if (!p) return IFX_E_NULL;
+    if (n <= 0 || p->n_blocks < 0 || p->sub_batch < 0 || p->fc_in <= 0 || p->fc_out <= 0) return IFX_E_SHAPE;
+    if (p->n_blocks > 0 && !p->blocks) return IFX_E_NULL;
+    const int nb = (p->sub_batch > 0 && p->sub_batch < n) ? p->sub_batch : n;
+    plan->nb = nb;
+    ifx_conv_desc stem = p->stem;
+    stem.n = nb;
+    ifx_status st = check_desc(&stem, &plan->stem_kind, &plan->stem_dims);
+    if (st != IFX_OK) return st;
+    if (plan->stem_kind != kStem) return IFX_E_UNSUPPORTED;
+    int h = plan->stem_dims.oh, w = plan->stem_dims.ow, c = stem.c_out;
+    size_t act = act_bytes(nb, h, w, c), t1 = 0, t2 = 0, sc = 0;
+    for (int i = 0; i < p->n_blocks; ++i) {
+        const ifx_block_params &bp = p->blocks[i];
+        if (bp.d[0].c_in != c || bp.d[0].h != h || bp.d[0].w != w) return IFX_E_SHAPE;
+        BlockPlan b;
+        st = plan_block(&bp, nb, &b);
+        if (st != IFX_OK) return st;
+        t1 = std::max(t1, b.t1);
+        t2 = std::max(t2, b.t2);
+        sc = std::max(sc, b.sc);
+        h = b.dims[2].oh;
+        w = b.dims[2].ow;
+        c = bp.d[2].c_out;
+        act = std::max(act, act_bytes(nb, h, w, c));
+    }
+    if (c != p->fc_in) return IFX_E_SHAPE;
+    if ((long long)nb * p->fc_out > 0x7fffffffLL) return IFX_E_SHAPE;
+    plan->out_h = h;
+    plan->out_w = w;
+    plan->out_c = c;
+    plan->act = round_up(act, 256);
+    plan->t1 = t1;
+    plan->t2 = t2;
+    plan->sc = sc;
+    plan->pool = round_up(act_bytes(nb, 1, 1, c), 256);
+    return IFX_OK;
+}
+
+size_t net_ws_bytes(const NetPlan &pl) { return 2 * pl.act + pl.t1 + pl.t2 + pl.sc + pl.pool; }
+
+}  // namespace
+
+extern "C" {
+
+ifx_status ifx_conv_validate(const ifx_conv_desc *d) { return check_desc(d, nullptr, nullptr); }
+
+ifx_status ifx_conv_out_dims(const ifx_conv_desc *d, int32_t *ho, int32_t *wo)
+{
+    Dims dm;
+    ifx_status st = check_desc(d, nullptr, &dm);
+    if (st != IFX_OK) return st;
+    if (!ho || !wo) return IFX_E_NULL;
+    *ho = dm.oh;
+    *wo = dm.ow;
+    return IFX_OK;
+}
+
+size_t ifx_act_bytes(int32_t n, int32_t h, int32_t w, int32_t c) { return act_bytes(n, h, w, c); }
+
+size_t ifx_wpack_bytes(const ifx_conv_desc *d)
+{
+    Kind k;
+    if (check_desc(d, &k, nullptr) != IFX_OK) return 0;
+    if (k == kStem) return (size_t)d->c_out * 256;
+    const int o2 = wgroup(d->c_out);
+    const size_t o1 = (size_t)(d->c_out + o2 - 1) / o2;
+    return o1 * d->kh * d->kw * ((d->c_in + 31) / 32) * o2 * 32;
+}
+
+ifx_status ifx_pack_act(const int8_t *x_nhwc, int8_t *x_blk, int32_t n, int32_t h, int32_t w, int32_t c,
+                        void *stream)
+{
+    if (!x_nhwc || !x_blk) return IFX_E_NULL;
+    if (n <= 0 || h <= 0 || w <= 0 || c <= 0 || (long long)n * h * w > 0x7fffffffLL) return IFX_E_SHAPE;
+    if (!aligned16(x_blk)) return IFX_E_ALIGN;
+    return hip_status(ifx::launch_pack_act(x_nhwc, x_blk, n, h, w, c, (hipStream_t)stream));
+}
+
+ifx_status ifx_unpack_act(const int8_t *x_blk, int8_t *x_nhwc, int32_t n, int32_t h, int32_t w, int32_t c,
+                          void *stream)
+{
+    if (!x_nhwc || !x_blk) return IFX_E_NULL;
+    if (n <= 0 || h <= 0 || w <= 0 || c <= 0 || (long long)n * h * w > 0x7fffffffLL) return IFX_E_SHAPE;
+    if (!aligned16(x_blk)) return IFX_E_ALIGN;
+    return hip_status(ifx::launch_unpack_act(x_blk, x_nhwc, n, h, w, c, (hipStream_t)stream));
+}
+
+ifx_status ifx_pack_weights(const ifx_conv_desc *d, const int8_t *w_ohwi, int8_t *w_blk, void *stream)
+{
+    Kind k;
+    ifx_status st = check_desc(d, &k, nullptr);
+    if (st != IFX_OK) return st;
+    if (!w_ohwi || !w_blk) return IFX_E_NULL;
+    if (!aligned16(w_blk)) return IFX_E_ALIGN;
+    hipStream_t s = (hipStream_t)stream;
+    if (k == kStem) return hip_status(ifx::launch_pack_weights_stem(w_ohwi, w_blk, d->c_out, d->c_in, s));
+    return hip_status(ifx::launch_pack_weights(w_ohwi, w_blk, d->c_out, d->kh, d->kw, d->c_in, wgroup(d->c_out), s));
+}
+
+ifx_status ifx_conv_fused(const ifx_conv_desc *d, const int8_t *x_blk, const int8_t *w_blk, const int32_t *bias,
+                          const int32_t *mult, const int32_t *shift, const int8_t *residual, void *y, void *stream)
+{
+    Kind k;
+    Dims dm;
+    ifx_status st = check_desc(d, &k, &dm);
+    if (st != IFX_OK) return st;
+    st = check_conv_ptrs(d, x_blk, w_blk, bias, mult, shift, residual, y);
+    if (st != IFX_OK) return st;
+    return run_conv(d, k, dm, x_blk, w_blk, bias, mult, shift, (d->flags & IFX_RESIDUAL) ? residual : nullptr, y,
+                    (hipStream_t)stream);
+}
+
+size_t ifx_block_workspace_bytes(const ifx_block_params *p)
+{
+    BlockPlan plan;
+    if (plan_block(p, 0, &plan) != IFX_OK) return 0;
+    return plan.t1 + plan.t2 + plan.sc;
+}
+
+ifx_status ifx_block_forward(const ifx_block_params *p, const int8_t *x_blk, int8_t *y_blk, void *ws,
+                             size_t ws_bytes, void *stream)
+{
+    BlockPlan plan;
+    ifx_status st = plan_block(p, 0, &plan);
+    if (st != IFX_OK) return st;
+    st = check_block_ptrs(p);
+    if (st != IFX_OK) return st;
+    if (!x_blk || !y_blk || !ws) return IFX_E_NULL;
+    if (!aligned16(x_blk) || !aligned16(y_blk) || !aligned16(ws)) return IFX_E_ALIGN;
+    if (ws_bytes < plan.t1 + plan.t2 + plan.sc) return IFX_E_WORKSPACE;
+    return run_block(p, plan, p->d[0].n, x_blk, y_blk, (int8_t *)ws, (hipStream_t)stream);
+}
+
+size_t ifx_net_workspace_bytes(const ifx_net_params *p, int32_t n)
+{
+    NetPlan plan;
+    if (plan_net(p, n, &plan) != IFX_OK) return 0;
+    return net_ws_bytes(plan);
+}
+
+ifx_status ifx_net_forward(const ifx_net_params *p, const int8_t *x_blk, int32_t *logits, int32_t n, void *ws,
+                           size_t ws_bytes, void *stream)
+{
+    NetPlan plan;
+    ifx_status st = plan_net(p, n, &plan);
+    if (st != IFX_OK) return st;
+    if (!x_blk || !logits || !ws || !p->stem_w || !p->stem_bias || !p->stem_mult || !p->stem_shift || !p->fc_w_blk ||
+        !p->fc_bias)
+        return IFX_E_NULL;
+    if (!aligned16(x_blk) || !aligned16(logits) || !aligned16(ws) || !aligned16(p->stem_w) ||
+        !aligned16(p->stem_bias) || !aligned16(p->stem_mult) || !aligned16(p->stem_shift) ||
+        !aligned16(p->fc_w_blk) || !aligned16(p->fc_bias))
+        return IFX_E_ALIGN;
+    for (int i = 0; i < p->n_blocks; ++i) {
+        st = check_block_ptrs(&p->blocks[i]);
+        if (st != IFX_OK) return st;
+    }
+    if (ws_bytes < net_ws_bytes(plan)) return IFX_E_WORKSPACE;
+
+    hipStream_t s = (hipStream_t)stream;
+    int8_t *base = (int8_t *)ws;
+    int8_t *act[2] = {base, base + plan.act};
+    int8_t *bws = base + 2 * plan.act;  // t1 | t2 | sc of the current block
+    int8_t *pool = bws + plan.t1 + plan.t2 + plan.sc;
+    const size_t in_img = act_bytes(1, p->stem.h, p->stem.w, p->stem.c_in);
+
+    for (int i0 = 0; i0 < n; i0 += plan.nb) {
+        const int nb = std::min(plan.nb, n - i0);
+        ifx_conv_desc sd = p->stem;
+        sd.n = nb;
+        Kind k;
+        Dims dm;
+        st = check_desc(&sd, &k, &dm);
+        if (st != IFX_OK) return st;
+        st = run_conv(&sd, k, dm, x_blk + (size_t)i0 * in_img, p->stem_w, p->stem_bias, p->stem_mult, p->stem_shift,
+                      nullptr, act[0], s);
+        if (st != IFX_OK) return st;
+        int cur = 0;
+        for (int b = 0; b < p->n_blocks; ++b) {
+            BlockPlan bp;
+            st = plan_block(&p->blocks[b], nb, &bp);
+            if (st != IFX_OK) return st;
+            // the block's own workspace pieces are laid out inside the net's t1|t2|sc area
+            BlockPlan lay = bp;
+            lay.t1 = plan.t1;
+            lay.t2 = plan.t2;
+            st = run_block(&p->blocks[b], lay, nb, act[cur], act[cur ^ 1], bws, s);
+            if (st != IFX_OK) return st;
+            cur ^= 1;
+        }
+        const int c1 = (plan.out_c + 31) / 32;
+        st = hip_status(ifx::launch_avgpool(act[cur], pool, nb, c1, plan.out_h * plan.out_w, s));
+        if (st != IFX_OK) return st;
+        ifx_conv_desc fd = {nb, 1, 1, p->fc_in, p->fc_out, 1, 1, 1, 0, IFX_OUT_I32};
+        st = check_desc(&fd, &k, &dm);
+        if (st != IFX_OK) return st;
+        st = run_conv(&fd, k, dm, pool, p->fc_w_blk, p->fc_bias, nullptr, nullptr, nullptr,
+                      logits + (size_t)i0 * p->fc_out, s);
+        if (st != IFX_OK) return st;
+    }
+    return IFX_OK;
+}
+
+const char *ifx_status_string(ifx_status s)
+{
+    switch (s) {
+    case IFX_OK: return "ok";
+    case IFX_E_NULL: return "null pointer";
+    case IFX_E_SHAPE: return "invalid or inconsistent shape";
+    case IFX_E_UNSUPPORTED: return "unsupported kernel/stride/pad/flags";
+    case IFX_E_ALIGN: return "pointer not 16-byte aligned";
+    case IFX_E_WORKSPACE: return "workspace too small";
+    case IFX_E_HIP: return "HIP launch failure";
+    }
+    return "unknown status";
+}
+
+int32_t ifx_last_hip_error(void) { return g_last_hip; }
+
+int32_t ifx_version(void) { return 100; }
+
+}  // extern "C"

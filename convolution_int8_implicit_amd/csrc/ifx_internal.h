@@ -1,0 +1,49 @@
+// Internal interface between the C ABI (api.cpp) and the gfx950 kernels.
+// Everything here is launched on the caller's stream; nothing synchronises.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ifx {
+
+// Arguments of one implicit-GEMM convolution launch.
+struct ConvArgs {
+    const int8_t *x;       // packed input  [n, i1, h, w, 32]
+    const int8_t *wt;      // packed weights [o1, kh, kw, i1, o2, 32]
+    const int32_t *bias;   // [oc]
+    const int32_t *mult;   // [oc]
+    const int32_t *shift;  // [oc]
+    const int8_t *res;     // packed shortcut [n, oc1, ho, wo, 32] or null
+    void *y;               // packed int8 output, or int32 NHWC when out_i32
+    int n, h, w, i1;       // input batch, size, channel blocks
+    int ho, wo, oc, oc1;   // output size, channels, channel blocks
+    int o2;                // output-channel group of the weight layout
+    int stride, pad;
+    int m;                 // n * ho * wo (GEMM rows)
+    int nkb;               // kh * kw * i1 (32-wide reduction blocks)
+    int relu, residual, out_i32;
+};
+
+// Arguments of the fused stem (7x7/s2/p3 conv + ReLU + 3x3/s2/p1 max-pool).
+struct StemArgs {
+    const int8_t *x;       // packed input [n, 1, h, w, 32] (channels 0..3 used)
+    const int8_t *wt;      // stem weights [oc=64, 8, 8, 4]
+    const int32_t *bias, *mult, *shift;
+    int8_t *y;             // packed pooled output [n, 2, ph, pw, 32]
+    int n, h, w;           // input
+    int ho, wo;            // conv output
+    int ph, pw;            // pooled output
+    int relu;
+};
+
+hipError_t launch_conv(const ConvArgs &a, int kh, int kw, hipStream_t s);
+hipError_t launch_stem(const StemArgs &a, hipStream_t s);
+hipError_t launch_avgpool(const int8_t *x, int8_t *y, int n, int c1, int hw, hipStream_t s);
+hipError_t launch_pack_act(const int8_t *x, int8_t *blk, int n, int h, int w, int c, hipStream_t s);
+hipError_t launch_unpack_act(const int8_t *blk, int8_t *x, int n, int h, int w, int c, hipStream_t s);
+hipError_t launch_pack_weights(const int8_t *w, int8_t *blk, int oc, int kh, int kw, int ic, int o2,
+                               hipStream_t s);
+hipError_t launch_pack_weights_stem(const int8_t *w, int8_t *blk, int oc, int ic, hipStream_t s);
+
+}  // namespace ifx

@@ -1,0 +1,209 @@
+/*
+ * ifx.h -- C ABI of the MI355X (gfx950) fused int8 ResNet convolution library.
+ *
+ * The library computes the int8 convolution path described by two of the
+ * source pages:
+ *   - Inspur, MLPerf v2.0 ResNet50 convolution-merge article ("Inspur
+ *     conv-merge article"): section 2.2 (the res3.x bottleneck and the fused
+ *     Conv3+BN+Sum+ReLU), section 3.1 (NC/32HW32 activations, [O1,I1,O2,I2]
+ *     weights), section 3.3 (implicit GEMM data[M,K] . weight[N,K]^T),
+ *     section 3.4 (BN+Sum+ReLU applied to the accumulators in one epilogue).
+ *   - DiDi Cloud IFX DAWNBench blog, inference-optimisation section:
+ *     CONV+BN+RELU and CONV+BN+RELU+MAXPOOL each as one function.
+ *
+ * Conventions for every entry point:
+ *   - Pointers named *_blk, x_nhwc, w_ohwi, bias, mult, shift, residual, y,
+ *     logits and ws are DEVICE pointers (HIP global memory), 16-byte aligned.
+ *     The caller owns all memory; the library never allocates or frees.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls only enqueue kernels on it and never synchronise; results are
+ *     valid once the stream reaches that point.  Calls that overlap on the
+ *     same output or workspace race.
+ *   - Arguments are validated on the host before anything is launched.  On
+ *     an error status nothing has been enqueued.  Validation touches no
+ *     device, so every error path runs without a GPU.
+ *   - All arithmetic is integer; results are deterministic and bit-exact.
+ *
+ * Layouts (Inspur conv-merge article, section 3.1):
+ *   activation  NC/32HW32: [N, C1=ceil(C/32), H, W, 32] int8; channel c of
+ *               pixel (b,y,x) sits at ((b*C1 + c/32)*H + y)*W + x)*32 + c%32;
+ *               channels >= C hold 0.
+ *   weights     [O1, KH, KW, I1, O2, I2=32] int8 with O2 = min(128, Oc
+ *               rounded up to 32), O1 = ceil(Oc/O2), I1 = ceil(Ic/32); zero
+ *               outside Oc x Ic.  For 1x1 this is the article's [O1,I1,O2,I2].
+ *   stem weights (7x7, stride 2, pad 3, MAXPOOL, Ic <= 4): [Oc, 8, 8, 4]
+ *               int8, element (o,ky,kx,c) = w[o,ky,kx,c] for ky,kx < 7,
+ *               c < Ic, else 0.
+ *   int32 out   IFX_OUT_I32 writes acc + bias as int32 NHWC [N, Ho, Wo, Oc].
+ *
+ * Fused epilogue of one convolution, per output element (the BN, Sum and
+ * ReLU of the Inspur article section 3.4 in fixed point; the rounding and
+ * scale readings are the library's, since the pages print no formula):
+ *   y   = acc + bias[o]                                (int32)
+ *   q   = round_half_away_from_zero(y * mult[o] / 2^(31 + shift[o]))
+ *   q  += residual  (IFX_RESIDUAL; same packed shape as the output)
+ *   q   = max(q, 0) (IFX_RELU)
+ *   out = saturate_int8(q)
+ *   IFX_MAXPOOL: 3x3 stride-2 pad-1 max-pool of `out`, out-of-range taps
+ *   ignored (stem only).
+ * Caller contract, not checked on the device: 0 <= mult[o] < 2^31,
+ * 0 <= shift[o] <= 31, |acc + bias| < 2^31.
+ */
+#ifndef IFX_H
+#define IFX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    IFX_OK = 0,
+    IFX_E_NULL = 1,        /* a required pointer is NULL */
+    IFX_E_SHAPE = 2,       /* non-positive or inconsistent dimensions */
+    IFX_E_UNSUPPORTED = 3, /* kernel/stride/pad/flag combination not implemented */
+    IFX_E_ALIGN = 4,       /* a device pointer is not 16-byte aligned */
+    IFX_E_WORKSPACE = 5,   /* workspace smaller than the *_workspace_bytes query */
+    IFX_E_HIP = 6          /* a HIP launch failed; see ifx_last_hip_error() */
+} ifx_status;
+
+/* Per-convolution flags. */
+enum {
+    IFX_RELU = 1u,     /* ReLU before saturation */
+    IFX_RESIDUAL = 2u, /* add the shortcut tensor before ReLU */
+    IFX_MAXPOOL = 4u,  /* fused 3x3/s2/p1 max-pool after ReLU (7x7/s2/p3 stem only) */
+    IFX_OUT_I32 = 8u   /* write int32 acc + bias, NHWC, no requantisation */
+};
+
+/*
+ * One convolution.  Supported (kh, kw, stride, pad):
+ *   (1,1,1,0) (1,1,2,0) (3,3,1,1) (3,3,2,1)  flags: any of RELU|RESIDUAL, or
+ *                                            OUT_I32 alone
+ *   (7,7,2,3) with IFX_MAXPOOL (RELU optional), c_in <= 4
+ * n, h, w, c_in, c_out > 0; the output size must be positive.
+ */
+typedef struct {
+    int32_t n, h, w, c_in, c_out;
+    int32_t kh, kw, stride, pad;
+    uint32_t flags;
+} ifx_conv_desc;
+
+/* Host-only: validate a descriptor (shape and supported set); no device use. */
+ifx_status ifx_conv_validate(const ifx_conv_desc *d);
+
+/* Host-only: output height/width of d (after the pool when IFX_MAXPOOL). */
+ifx_status ifx_conv_out_dims(const ifx_conv_desc *d, int32_t *ho, int32_t *wo);
+
+/* Host-only: bytes of a packed activation, n * ceil(c/32) * h * w * 32. */
+size_t ifx_act_bytes(int32_t n, int32_t h, int32_t w, int32_t c);
+
+/* Host-only: bytes of the packed weights of d (0 if d is invalid). */
+size_t ifx_wpack_bytes(const ifx_conv_desc *d);
+
+/*
+ * Activation pack NHWC -> NC/32HW32 (Inspur conv-merge article, section 3.1:
+ * channels split into groups of 32 so one pixel's group is one 16-byte pair).
+ * x_nhwc: [n,h,w,c] int8 (any alignment); x_blk: ifx_act_bytes() bytes.
+ */
+ifx_status ifx_pack_act(const int8_t *x_nhwc, int8_t *x_blk, int32_t n, int32_t h, int32_t w,
+                        int32_t c, void *stream);
+
+/* Inverse of ifx_pack_act (padding channels dropped); x_nhwc any alignment. */
+ifx_status ifx_unpack_act(const int8_t *x_blk, int8_t *x_nhwc, int32_t n, int32_t h, int32_t w,
+                          int32_t c, void *stream);
+
+/*
+ * Weight reblock OHWI [c_out, kh, kw, c_in] -> the packed layout of d
+ * (Inspur conv-merge article, section 3.1).  w_ohwi any alignment; w_blk
+ * ifx_wpack_bytes(d) bytes.
+ */
+ifx_status ifx_pack_weights(const ifx_conv_desc *d, const int8_t *w_ohwi, int8_t *w_blk, void *stream);
+
+/*
+ * One fused convolution (Inspur conv-merge article sections 3.3-3.4; DiDi
+ * IFX blog inference section): implicit-GEMM int8 convolution with int32
+ * accumulation followed by the fused epilogue above.
+ *   x_blk      packed input [n, ceil(c_in/32), h, w, 32]
+ *   w_blk      packed weights of d (ifx_pack_weights)
+ *   bias, mult, shift   int32 [c_out]
+ *   residual   packed [n, ceil(c_out/32), ho, wo, 32] when IFX_RESIDUAL, else NULL
+ *   y          packed int8 output [n, ceil(c_out/32), ho', wo', 32] (pooled
+ *              size with IFX_MAXPOOL), or int32 NHWC with IFX_OUT_I32
+ * Input and output must not overlap.
+ */
+ifx_status ifx_conv_fused(const ifx_conv_desc *d, const int8_t *x_blk, const int8_t *w_blk,
+                          const int32_t *bias, const int32_t *mult, const int32_t *shift,
+                          const int8_t *residual, void *y, void *stream);
+
+/*
+ * Bottleneck block (Inspur conv-merge article, section 2.2):
+ *   t1 = conv(x; d[0] 1x1, RELU)          c1
+ *   t2 = conv(t1; d[1] 3x3 stride s, RELU) c2
+ *   sc = x, or conv(x; d[3] 1x1 stride s, no ReLU) when has_proj
+ *   y  = conv(t2; d[2] 1x1, RESIDUAL=sc, RELU)   c3
+ * Descriptors carry the batch in n.  Their flags must be: d[0], d[1] without
+ * RESIDUAL/MAXPOOL/OUT_I32, d[2] with RESIDUAL, d[3] without RESIDUAL/MAXPOOL/
+ * OUT_I32.  t1, t2 and sc live in the caller's workspace.
+ */
+typedef struct {
+    ifx_conv_desc d[4]; /* c1, c2, c3, projection */
+    int32_t has_proj;
+    const int8_t *w_blk[4];
+    const int32_t *bias[4];
+    const int32_t *mult[4];
+    const int32_t *shift[4];
+} ifx_block_params;
+
+/* Host-only: workspace bytes ifx_block_forward needs for p (0 if invalid). */
+size_t ifx_block_workspace_bytes(const ifx_block_params *p);
+
+ifx_status ifx_block_forward(const ifx_block_params *p, const int8_t *x_blk, int8_t *y_blk, void *ws,
+                             size_t ws_bytes, void *stream);
+
+/*
+ * ResNet-50-shaped network: stem (7x7/s2/p3 CONV+BN+RELU+MAXPOOL, DiDi IFX
+ * blog) -> bottleneck blocks -> global average pool to int8 (round half away
+ * from zero of the mean) -> FC with int32 logits = a . W^T + bias.
+ * The n field of every descriptor inside p is ignored: the batch is the `n`
+ * argument.  fc_w_blk is the FC weight [fc_out, fc_in] packed as a 1x1
+ * convolution (ifx_pack_weights with kh = kw = 1, c_in = fc_in,
+ * c_out = fc_out).  sub_batch > 0 runs the network over consecutive groups
+ * of sub_batch images (results are identical for every sub_batch); 0 runs
+ * the whole batch at once.
+ *   x_blk   packed input [n, ceil(stem.c_in/32), stem.h, stem.w, 32]
+ *   logits  int32 [n, fc_out]
+ */
+typedef struct {
+    ifx_conv_desc stem;
+    const int8_t *stem_w;
+    const int32_t *stem_bias, *stem_mult, *stem_shift;
+    int32_t n_blocks;
+    const ifx_block_params *blocks;
+    const int8_t *fc_w_blk;
+    const int32_t *fc_bias;
+    int32_t fc_in, fc_out;
+    int32_t sub_batch;
+} ifx_net_params;
+
+/* Host-only: workspace bytes ifx_net_forward needs for p at batch n (0 if invalid). */
+size_t ifx_net_workspace_bytes(const ifx_net_params *p, int32_t n);
+
+ifx_status ifx_net_forward(const ifx_net_params *p, const int8_t *x_blk, int32_t *logits, int32_t n,
+                           void *ws, size_t ws_bytes, void *stream);
+
+/* Host-only: a static, human-readable name of a status. */
+const char *ifx_status_string(ifx_status s);
+
+/* Host-only: the hipError_t behind the calling thread's last IFX_E_HIP (0 if none). */
+int32_t ifx_last_hip_error(void);
+
+/* Host-only: library version, major * 10000 + minor * 100 + patch. */
+int32_t ifx_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IFX_H */

@@ -1,0 +1,146 @@
+"""The C-ABI library loads, exports every entry point of include/ifx.h, and its
+host-side validation rejects bad arguments before any device work (no GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import convolution_int8_implicit_amd as ifx
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "ifx.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ifx_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_entry_point():
+    L = ifx.lib()
+    names = header_functions()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(L, n), n
+    assert ifx.version() == 100
+    assert ifx.status_string(0) == "ok" and "workspace" in ifx.status_string(5)
+    assert ifx.last_hip_error() == 0
+
+
+def D(n=1, h=28, w=28, ci=128, co=512, k=1, s=1, p=0, f=ifx.RELU | ifx.RESIDUAL):
+    return ifx.conv_desc(n, h, w, ci, co, k, k, s, p, f)
+
+
+@pytest.mark.parametrize("d,st", [
+    (D(), 0),
+    (D(k=3, p=1), 0), (D(k=3, s=2, p=1), 0), (D(k=1, s=2), 0),
+    (D(n=0), 2), (D(h=-1), 2), (D(ci=0), 2), (D(co=0), 2),
+    (D(k=5, p=2), 3), (D(k=3, p=0), 3), (D(k=1, p=1), 3), (D(s=3), 3),
+    (D(f=ifx.MAXPOOL), 3), (D(f=ifx.OUT_I32 | ifx.RELU), 3), (D(f=0x40), 3),
+    (D(h=224, w=224, ci=3, co=64, k=7, s=2, p=3, f=ifx.RELU | ifx.MAXPOOL), 0),
+    (D(h=224, w=224, ci=3, co=64, k=7, s=2, p=3, f=ifx.RELU), 3),
+    (D(h=224, w=224, ci=8, co=64, k=7, s=2, p=3, f=ifx.MAXPOOL), 3),
+    (D(h=224, w=224, ci=3, co=32, k=7, s=2, p=3, f=ifx.MAXPOOL), 3),
+    (D(h=1, w=1, k=3, s=1, p=1), 0), (D(h=2, w=2, ci=3, co=64, k=7, s=2, p=3, f=ifx.MAXPOOL), 0),
+    (D(n=1 << 20, h=4096, w=4096), 2),
+])
+def test_descriptor_validation(d, st):
+    assert ifx.conv_validate(d) == st
+
+
+def test_out_dims_and_sizes(orc):
+    for (h, k, s, p) in [(28, 1, 1, 0), (56, 1, 2, 0), (56, 3, 2, 1), (7, 3, 1, 1), (9, 3, 2, 1)]:
+        ho, wo = ifx.conv_out_dims(D(h=h, w=h + 1, k=k, s=s, p=p))
+        assert (ho, wo) == (orc.out_dim(h, k, s, p), orc.out_dim(h + 1, k, s, p))
+    ho, wo = ifx.conv_out_dims(D(h=224, w=224, ci=3, co=64, k=7, s=2, p=3, f=ifx.MAXPOOL))
+    assert (ho, wo) == (56, 56)
+    assert ifx.act_bytes(2, 5, 6, 33) == 2 * 2 * 5 * 6 * 32
+    assert ifx.act_bytes(0, 5, 6, 33) == 0
+    for co, k, ci in [(512, 1, 128), (64, 3, 64), (1000, 1, 2048), (96, 3, 40)]:
+        o2 = orc.wgroup(co)
+        assert ifx.wpack_bytes(D(ci=ci, co=co, k=k, p=k // 2)) == (co + o2 - 1) // o2 * o2 * k * k * ((ci + 31) // 32) * 32
+    assert ifx.wpack_bytes(D(h=224, w=224, ci=3, co=64, k=7, s=2, p=3, f=ifx.MAXPOOL)) == 64 * 256
+    assert ifx.wpack_bytes(D(k=5, p=2)) == 0
+
+
+def test_errors_return_before_any_launch():
+    L = ifx.lib()
+    d = D()
+    fake = ctypes.c_void_p(0x100000)          # aligned, never dereferenced
+    odd = ctypes.c_void_p(0x100001)           # misaligned
+    args = [fake] * 7
+    # null input
+    assert L.ifx_conv_fused(ctypes.byref(d), None, *args[:5], fake, None) == 1
+    # residual required
+    assert L.ifx_conv_fused(ctypes.byref(d), fake, fake, fake, fake, fake, None, fake, None) == 1
+    # mult/shift required unless OUT_I32
+    assert L.ifx_conv_fused(ctypes.byref(d), fake, fake, fake, None, fake, fake, fake, None) == 1
+    # misaligned output
+    assert L.ifx_conv_fused(ctypes.byref(d), fake, fake, fake, fake, fake, fake, odd, None) == 4
+    # unsupported descriptor reported before pointer checks
+    bad = D(k=5, p=2)
+    assert L.ifx_conv_fused(ctypes.byref(bad), None, None, None, None, None, None, None, None) == 3
+    assert L.ifx_pack_act(None, fake, 1, 2, 2, 3, None) == 1
+    assert L.ifx_pack_act(fake, odd, 1, 2, 2, 3, None) == 4
+    assert L.ifx_pack_act(fake, fake, 0, 2, 2, 3, None) == 2
+    assert L.ifx_unpack_act(fake, fake, 1, 2, -2, 3, None) == 2
+    assert L.ifx_pack_weights(ctypes.byref(bad), fake, fake, None) == 3
+    assert L.ifx_conv_out_dims(ctypes.byref(d), None, None) == 1
+    assert L.ifx_conv_validate(None) == 1
+
+
+def _block(n=2, proj=True, c3_flags=ifx.RESIDUAL | ifx.RELU, c2_cin=64):
+    p = ifx.BlockParams()
+    p.d[0] = D(n=n, h=8, w=8, ci=256, co=64, f=ifx.RELU)
+    p.d[1] = D(n=n, h=8, w=8, ci=c2_cin, co=64, k=3, s=2, p=1, f=ifx.RELU)
+    p.d[2] = D(n=n, h=4, w=4, ci=64, co=256, f=c3_flags)
+    p.d[3] = D(n=n, h=8, w=8, ci=256, co=256, s=2, f=0)
+    p.has_proj = 1 if proj else 0
+    for i in range(4):
+        p.w_blk[i] = p.bias[i] = p.mult[i] = p.shift[i] = 0x100000
+    return p
+
+
+def test_block_validation_and_workspace():
+    L = ifx.lib()
+    p = _block()
+    ws = ifx.block_workspace_bytes(p)
+    exp = 2 * 2 * 8 * 8 * 32 + 2 * 2 * 4 * 4 * 32 + 2 * 8 * 4 * 4 * 32
+    assert ws == exp
+    fake = ctypes.c_void_p(0x200000)
+    assert L.ifx_block_forward(ctypes.byref(p), fake, fake, fake, ws - 1, None) == 5
+    assert L.ifx_block_forward(ctypes.byref(p), None, fake, fake, ws, None) == 1
+    assert ifx.block_workspace_bytes(_block(proj=False)) == 0          # identity shortcut needs c3 out == input
+    assert ifx.block_workspace_bytes(_block(c3_flags=ifx.RELU)) == 0   # c3 must add the shortcut
+    assert ifx.block_workspace_bytes(_block(c2_cin=32)) == 0           # channel chain broken
+    q = _block()
+    q.w_blk[3] = None
+    assert L.ifx_block_forward(ctypes.byref(q), fake, fake, fake, ws, None) == 1
+
+
+def test_net_validation_and_workspace():
+    L = ifx.lib()
+    blk = _block(n=1)
+    blk.d[0] = D(n=1, h=56, w=56, ci=64, co=64, f=ifx.RELU)
+    blk.d[1] = D(n=1, h=56, w=56, ci=64, co=64, k=3, s=1, p=1, f=ifx.RELU)
+    blk.d[2] = D(n=1, h=56, w=56, ci=64, co=256, f=ifx.RESIDUAL | ifx.RELU)
+    blk.d[3] = D(n=1, h=56, w=56, ci=64, co=256, s=1, f=0)
+    arr = (ifx.BlockParams * 1)(blk)
+    p = ifx.NetParams()
+    p.stem = D(n=1, h=224, w=224, ci=3, co=64, k=7, s=2, p=3, f=ifx.RELU | ifx.MAXPOOL)
+    p.stem_w = p.stem_bias = p.stem_mult = p.stem_shift = 0x100000
+    p.n_blocks = 1
+    p.blocks = ctypes.cast(arr, ctypes.POINTER(ifx.BlockParams))
+    p.fc_w_blk = p.fc_bias = 0x100000
+    p.fc_in, p.fc_out = 256, 1000
+    ws = ifx.net_workspace_bytes(p, 4)
+    act = 4 * 8 * 56 * 56 * 32
+    t = 4 * 2 * 56 * 56 * 32
+    assert ws == 2 * act + 2 * t + act + 4 * 8 * 32
+    p.sub_batch = 2
+    assert ifx.net_workspace_bytes(p, 4) == ws // 2
+    fake = ctypes.c_void_p(0x200000)
+    assert L.ifx_net_forward(ctypes.byref(p), fake, fake, 4, fake, ws // 2 - 1, None) == 5
+    p.fc_in = 255
+    assert ifx.net_workspace_bytes(p, 4) == 0

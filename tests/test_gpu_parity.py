@@ -1,0 +1,263 @@
+"""GPU parity: libifx.so (through its C ABI) against the CPU oracle, byte for byte.
+
+Every step of the path is integer, so the bar is bit-exactness: int8 outputs,
+int32 accumulators and int32 logits must equal the oracle's on the same seeded
+inputs.  Outputs are written into sentinel-filled buffers with guard bands, and
+runs are repeated to catch races.
+"""
+import itertools
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+SENT = 0x5A
+GUARD = 4096
+
+
+def note(msg):
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def ifx():
+    import convolution_int8_implicit_amd as m
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    m.lib()
+    return m
+
+
+def guarded(nbytes, dtype=torch.int8):
+    """A device buffer of nbytes inside sentinel guard bands; returns (view, whole)."""
+    whole = torch.full((nbytes + 2 * GUARD,), SENT, dtype=torch.int8, device="cuda")
+    view = whole[GUARD:GUARD + nbytes]
+    if dtype != torch.int8:
+        view = view.view(dtype)
+    return view, whole
+
+
+def check_guards(whole):
+    w = whole.cpu().numpy()
+    assert np.all(w[:GUARD] == SENT) and np.all(w[-GUARD:] == SENT), "write outside the output buffer"
+
+
+def rand(rng, shape, lo, hi, dtype=np.int8):
+    return rng.integers(lo, hi + 1, size=shape, dtype=np.int64).astype(dtype)
+
+
+def cu(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def gpu_conv(ifx, x, w, bias, mult, shift, k, s, p, flags, residual=None, check_pad=True):
+    """Run ifx_conv_fused on NHWC/OHWI numpy inputs; returns NHWC numpy output."""
+    n, h, wd, c = x.shape
+    oc = w.shape[0]
+    d = ifx.conv_desc(n, h, wd, c, oc, k, k, s, p, flags)
+    xb = ifx.pack_act(cu(x))
+    wb = ifx.pack_weights(d, cu(w))
+    ho, wo = ifx.conv_out_dims(d)
+    rb = ifx.pack_act(cu(residual)) if residual is not None else None
+    if flags & ifx.OUT_I32:
+        y, whole = guarded(n * ho * wo * oc * 4, torch.int32)
+        y = y.view(n, ho, wo, oc)
+    else:
+        nbytes = ifx.act_bytes(n, ho, wo, oc)
+        y, whole = guarded(nbytes)
+        y = y.view(n, (oc + 31) // 32, ho, wo, 32)
+    ifx.conv_fused(d, xb, wb, cu(bias), cu(mult) if mult is not None else None,
+                   cu(shift) if shift is not None else None, rb, y)
+    torch.cuda.synchronize()
+    check_guards(whole)
+    if flags & ifx.OUT_I32:
+        return y.cpu().numpy()
+    if check_pad and oc % 32:
+        tail = y[:, -1, :, :, oc % 32:].cpu().numpy()
+        assert np.all(tail == 0), "padding channels of the packed output must be zero"
+    return ifx.unpack_act(y, oc).cpu().numpy()
+
+
+def params(rng, oc, shift_lo=8, shift_hi=16):
+    return (rand(rng, oc, -(1 << 16), 1 << 16, np.int32), rand(rng, oc, 1 << 30, (1 << 31) - 1, np.int32),
+            rand(rng, oc, shift_lo, shift_hi, np.int32))
+
+
+# ------------------------------------------------------------------ packers
+@pytest.mark.parametrize("c", [3, 32, 64, 96, 130])
+def test_pack_unpack_act(ifx, orc, c):
+    note(f"pack_act c={c}")
+    rng = np.random.default_rng(c)
+    x = rand(rng, (3, 7, 9, c), -128, 127)
+    xb = ifx.pack_act(cu(x))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(xb.cpu().numpy(), orc.pack_act(x))
+    np.testing.assert_array_equal(ifx.unpack_act(xb, c).cpu().numpy(), x)
+
+
+@pytest.mark.parametrize("oc,k,ic", [(512, 1, 128), (64, 3, 64), (1000, 1, 2048), (96, 3, 40), (128, 3, 128)])
+def test_pack_weights(ifx, orc, oc, k, ic):
+    note(f"pack_weights oc={oc} k={k} ic={ic}")
+    rng = np.random.default_rng(oc + k + ic)
+    w = rand(rng, (oc, k, k, ic), -127, 127)
+    d = ifx.conv_desc(1, 8, 8, ic, oc, k, k, 1, k // 2, 0)
+    wb = ifx.pack_weights(d, cu(w))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(wb.cpu().numpy(), orc.pack_weights(w).reshape(-1))
+
+
+def test_pack_weights_stem(ifx, orc):
+    note("pack_weights stem")
+    rng = np.random.default_rng(77)
+    w = rand(rng, (64, 7, 7, 3), -127, 127)
+    d = ifx.conv_desc(1, 224, 224, 3, 64, 7, 7, 2, 3, ifx.RELU | ifx.MAXPOOL)
+    wb = ifx.pack_weights(d, cu(w))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(wb.cpu().numpy(), orc.pack_weights_stem(w).reshape(-1))
+
+
+# ------------------------------------------------------------------ raw accumulators
+ACC_CASES = [
+    # n, h, w, c, oc, k, s, p
+    (1, 28, 28, 128, 512, 1, 1, 0),
+    (2, 9, 11, 96, 64, 1, 1, 0),
+    (3, 14, 13, 64, 256, 1, 2, 0),
+    (2, 9, 9, 64, 64, 3, 1, 1),
+    (1, 15, 14, 128, 128, 3, 2, 1),
+    (2, 7, 7, 32, 96, 3, 1, 1),
+    (1, 5, 6, 3, 40, 3, 1, 1),
+    (4, 1, 1, 2048, 1000, 1, 1, 0),
+    (1, 3, 3, 33, 200, 3, 2, 1),
+]
+
+
+@pytest.mark.parametrize("case", ACC_CASES)
+def test_int32_accumulators(ifx, orc, case):
+    n, h, w, c, oc, k, s, p = case
+    note(f"acc {case}")
+    rng = np.random.default_rng(sum(case))
+    x = rand(rng, (n, h, w, c), -128, 127)
+    wt = rand(rng, (oc, k, k, c), -127, 127)
+    zero = np.zeros(oc, np.int32)
+    got = gpu_conv(ifx, x, wt, zero, None, None, k, s, p, ifx.OUT_I32)
+    np.testing.assert_array_equal(got, orc.conv_acc(x, wt, s, p))
+    # with a bias: acc + bias
+    bias = rand(rng, oc, -(1 << 16), 1 << 16, np.int32)
+    got = gpu_conv(ifx, x, wt, bias, None, None, k, s, p, ifx.OUT_I32)
+    np.testing.assert_array_equal(got, orc.conv_acc(x, wt, s, p) + bias)
+
+
+# ------------------------------------------------------------------ fused int8 epilogue
+FUSED_SHAPES = [
+    (1, 28, 28, 128, 512, 1, 1, 0),
+    (2, 9, 11, 96, 64, 1, 1, 0),
+    (3, 14, 13, 64, 256, 1, 2, 0),
+    (2, 9, 9, 64, 64, 3, 1, 1),
+    (1, 15, 14, 128, 128, 3, 2, 1),
+    (1, 5, 6, 3, 40, 3, 1, 1),
+    (3, 7, 7, 512, 2048, 1, 1, 0),
+]
+
+
+@pytest.mark.parametrize("shape", FUSED_SHAPES)
+@pytest.mark.parametrize("flags", [0, 1, 2, 3])
+def test_fused_conv(ifx, orc, shape, flags):
+    n, h, w, c, oc, k, s, p = shape
+    note(f"fused {shape} flags={flags}")
+    rng = np.random.default_rng(sum(shape) * 7 + flags)
+    x = rand(rng, (n, h, w, c), 0, 127)
+    wt = rand(rng, (oc, k, k, c), -127, 127)
+    bias, mult, shift = params(rng, oc)
+    ho, wo = orc.out_dim(h, k, s, p), orc.out_dim(w, k, s, p)
+    res = rand(rng, (n, ho, wo, oc), -128, 127) if flags & ifx.RESIDUAL else None
+    got = gpu_conv(ifx, x, wt, bias, mult, shift, k, s, p, flags, res)
+    exp = orc.conv_fused(x, wt, bias, mult, shift, s, p, flags, res)
+    np.testing.assert_array_equal(got, exp)
+
+
+def test_requant_edges(ifx, orc):
+    """shift 0 and 1 (general path), mult 0 and 2^31-1, exact ties, negative values."""
+    note("requant edges")
+    rng = np.random.default_rng(5)
+    n, h, w, c, oc = 2, 6, 5, 64, 128
+    x = rand(rng, (n, h, w, c), -128, 127)
+    wt = rand(rng, (oc, 1, 1, c), -127, 127)
+    bias = rand(rng, oc, -(1 << 16), 1 << 16, np.int32)
+    shift = np.tile(np.array([0, 1, 2, 3, 31, 30, 16, 8], np.int32), oc // 8)
+    mult = np.tile(np.array([1 << 30, (1 << 31) - 1, 0, 1, (1 << 31) - 1, 1 << 29, 12345, 1 << 30], np.int32), oc // 8)
+    for flags in (0, ifx.RELU):
+        got = gpu_conv(ifx, x, wt, bias, mult, shift, 1, 1, 0, flags)
+        np.testing.assert_array_equal(got, orc.conv_fused(x, wt, bias, mult, shift, 1, 0, flags))
+    # all channels on the fast path but with ties: mult = 2^30, shift = 2 -> y/8, ties at y = 8j+4
+    mult2 = np.full(oc, 1 << 30, np.int32)
+    shift2 = np.full(oc, 2, np.int32)
+    got = gpu_conv(ifx, x, wt, bias, mult2, shift2, 1, 1, 0, 0)
+    np.testing.assert_array_equal(got, orc.conv_fused(x, wt, bias, mult2, shift2, 1, 0, 0))
+
+
+def test_identity_halves(ifx, orc):
+    """The golden identity case on the GPU: out = round_half_away(x / 2)."""
+    note("identity halves")
+    vals = np.arange(-128, 128, dtype=np.int16).astype(np.int8)
+    c = 256
+    x = vals.reshape(1, 1, 1, c)
+    wt = np.zeros((c, 1, 1, c), np.int8)
+    wt[np.arange(c), 0, 0, np.arange(c)] = 1
+    z = np.zeros(c, np.int32)
+    got = gpu_conv(ifx, x, wt, z, np.full(c, 1 << 30, np.int32), z, 1, 1, 0, 0).reshape(-1)
+    exp = np.sign(vals.astype(np.int64)) * ((np.abs(vals.astype(np.int64)) + 1) // 2)
+    np.testing.assert_array_equal(got.astype(np.int64), exp)
+
+
+def test_fuzz_small_shapes(ifx, orc):
+    rng = np.random.default_rng(2024)
+    ksp = [(1, 1, 0), (1, 2, 0), (3, 1, 1), (3, 2, 1)]
+    for it in range(24):
+        k, s, p = ksp[it % 4]
+        n = int(rng.integers(1, 4))
+        h, w = int(rng.integers(1, 12)), int(rng.integers(1, 12))
+        c = int(rng.choice([3, 32, 64, 96, 17]))
+        oc = int(rng.choice([32, 64, 96, 40, 160, 256]))
+        flags = int(rng.integers(0, 4))
+        note(f"fuzz it={it} n={n} h={h} w={w} c={c} oc={oc} k={k} s={s} flags={flags}")
+        x = rand(rng, (n, h, w, c), -128, 127)
+        wt = rand(rng, (oc, k, k, c), -127, 127)
+        bias, mult, shift = params(rng, oc, 0, 20)
+        ho, wo = orc.out_dim(h, k, s, p), orc.out_dim(w, k, s, p)
+        res = rand(rng, (n, ho, wo, oc), -128, 127) if flags & ifx.RESIDUAL else None
+        got = gpu_conv(ifx, x, wt, bias, mult, shift, k, s, p, flags, res)
+        np.testing.assert_array_equal(got, orc.conv_fused(x, wt, bias, mult, shift, s, p, flags, res))
+
+
+# ------------------------------------------------------------------ stem
+@pytest.mark.parametrize("n,h,w,c", [(2, 224, 224, 3), (1, 37, 45, 3), (3, 16, 16, 4), (1, 2, 3, 1)])
+def test_stem(ifx, orc, n, h, w, c):
+    note(f"stem n={n} h={h} w={w} c={c}")
+    rng = np.random.default_rng(h + w + c)
+    x = rand(rng, (n, h, w, c), -128, 127)
+    wt = rand(rng, (64, 7, 7, c), -127, 127)
+    bias, mult, shift = params(rng, 64)
+    for flags in (ifx.RELU | ifx.MAXPOOL, ifx.MAXPOOL):
+        got = gpu_conv(ifx, x, wt, bias, mult, shift, 7, 2, 3, flags)
+        np.testing.assert_array_equal(got, orc.conv_fused(x, wt, bias, mult, shift, 2, 3, flags))
+
+
+# ------------------------------------------------------------------ determinism
+def test_repeat_runs_identical(ifx):
+    note("determinism res3 conv3 batch 64")
+    from convolution_int8_implicit_amd import model, synth
+    wl = synth.workload(1, n=64)
+    spec = wl.convs[0]
+    dc = model.device_conv(spec, wl.index, wl.n, wl.h, wl.w)
+    xb = ifx.pack_act(synth.input_tensor(wl, device="cuda"))
+    rb = ifx.pack_act(synth.residual_tensor(wl, device="cuda"))
+    outs = []
+    for _ in range(3):
+        y = torch.full((ifx.act_bytes(wl.n, 28, 28, 512),), SENT, dtype=torch.int8, device="cuda")
+        dc.run(xb, y, rb)
+        outs.append(y)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
