@@ -1,0 +1,335 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused int8 ResNet convolution path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload net|conv1x1|conv1x1_b1|block|stem]
+
+Default workload: the ResNet-50-shaped int8 backbone + average pool + int8 FC
+at batch 2048 on 224x224x3 images (synthetic, seeded).  One step is the whole
+hot path over the batch: NHWC -> NC/32HW32 input pack, fused stem
+(conv 7x7/s2 + BN + ReLU + max-pool), 16 bottlenecks of fused convolutions
+(BN + requant + shortcut + ReLU in the epilogue), average pool and FC to int32
+logits.  Weights are packed once beforehand (offline reblocking).
+
+Prints ONE JSON line with the throughput (images/s), int8 TOPS, a roofline
+object for the dominant kernel (HIP events on the launch stream) and the CPU
+oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_I8 = 5.0e15      # MI355X dense int8 MFMA, ops/s
+PEAK_HBM = 8.0e12     # MI355X HBM3E, bytes/s
+RIDGE = PEAK_I8 / PEAK_HBM
+METRIC = "int8 TOPS + images/s (fused conv stack), % of int8 MFMA peak / HBM BW"
+
+
+def kernel_name(spec) -> str:
+    """Name of the library kernel instance a conv layer dispatches to (mirrors the host dispatch)."""
+    if spec.k == 7:
+        return "stem_kernel"
+    oc_pad = (spec.c_out + 31) // 32 * 32
+    bm, bn = (128, 128) if oc_pad > 64 else (256, 64)
+    return f"conv_kernel<{spec.k},{spec.k},{bm},{bn}>"
+
+
+def layer_work(spec, n, h, w):
+    """(ops, algorithmic bytes, output h, w) of one conv at batch n on an h x w input.
+    ops = 2 per real MAC; bytes = each distinct tensor crossing HBM once: real input
+    channels (only sampled pixels for a strided 1x1), weights, 12 B/channel of
+    bias/mult/shift, the shortcut, and the output (pooled for the stem)."""
+    ho = (h + 2 * spec.pad - spec.k) // spec.stride + 1
+    wo = (w + 2 * spec.pad - spec.k) // spec.stride + 1
+    ops = 2 * n * ho * wo * spec.c_out * spec.k * spec.k * spec.c_in
+    in_px = n * ho * wo if (spec.k == 1 and spec.stride > 1) else n * h * w
+    byts = in_px * spec.c_in + spec.c_out * spec.k * spec.k * spec.c_in + 12 * spec.c_out
+    oh, ow = ho, wo
+    if spec.flags & 4:
+        oh, ow = (ho - 1) // 2 + 1, (wo - 1) // 2 + 1
+    byts += n * oh * ow * spec.c_out
+    if spec.flags & 2:
+        byts += n * ho * wo * spec.c_out
+    return ops, byts, oh, ow
+
+
+def net_layers(net, n):
+    """[(spec, n, h, w)] for every conv launch of the network, in order."""
+    out = [(net.stem, n, 224, 224)]
+    h = w = 56
+    for b in net.blocks:
+        out.append((b.c1, n, h, w))
+        h2 = (h + 2 - 3) // b.c2.stride + 1
+        out.append((b.c2, n, h, w))
+        if b.proj is not None:
+            out.append((b.proj, n, h, w))
+        out.append((b.c3, n, h2, h2))
+        h = w = h2
+    return out
+
+
+def cpu_baseline(workload: str, budget_s: float = 15.0):
+    """The CPU oracle, untuned, on a bounded sample of the same workload."""
+    import numpy as np
+
+    from convolution_int8_implicit_amd import synth
+    from oracle import ref as orc
+    from oracle.ref import BlockParams, ConvParams
+
+    cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+
+    def cp(wl, spec):
+        p = synth.conv_params(wl.index, spec)
+        return ConvParams(p["w"].numpy(), p["bias"].numpy(), p["mult"].numpy(), p["shift"].numpy(), spec.stride,
+                          spec.pad)
+
+    if workload == "net":
+        wl = synth.workload(4)
+        stem = cp(wl, wl.net.stem)
+        blocks = [BlockParams(cp(wl, b.c1), cp(wl, b.c2), cp(wl, b.c3), cp(wl, b.proj) if b.proj else None)
+                  for b in wl.net.blocks]
+        fcp = synth.fc_params(wl.index, wl.net)
+        fw, fb = fcp["w"].numpy(), fcp["bias"].numpy()
+
+        def run(rows):
+            x = synth.input_tensor(wl, rows=rows).numpy()
+            t0 = time.perf_counter()
+            orc.net(x, stem, blocks, fw, fb)
+            return time.perf_counter() - t0
+        per_img_ops = 2 * 4.08925e9
+    else:
+        idx = {"conv1x1": 1, "conv1x1_b1": 0, "block": 2, "stem": 3}[workload]
+        wl = synth.workload(idx)
+        cps = [cp(wl, s) for s in wl.convs]
+
+        def run(rows):
+            x = synth.input_tensor(wl, rows=rows).numpy()
+            r = synth.residual_tensor(wl, rows=rows).numpy() if wl.kind == "conv" else None
+            t0 = time.perf_counter()
+            if wl.kind == "block":
+                orc.block(x, *cps)
+            else:
+                orc.conv_layer(x, cps[0], wl.convs[0].flags, residual=r)
+            return time.perf_counter() - t0
+        per_img_ops = sum(2 * s.macs(1, wl.h, wl.w) for s in wl.convs)
+    t1 = run([0])
+    k = int(max(1, min(wl.n - 1, budget_s / max(t1, 1e-3))))
+    rows = list(range(1, 1 + k))
+    tk = run(rows)
+    return {"value": round(k / tk, 3), "unit": "images/s", "cores": cores, "kind": "oracle",
+            "sample": f"{k} of {wl.n} images of the same workload (after 1 warm-up image), "
+                      f"{tk:.1f} s, {k * per_img_ops / tk / 1e9:.2f} GOPS int8"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="net", choices=["net", "conv1x1", "conv1x1_b1", "block", "stem"])
+    ap.add_argument("--sub-batch", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (data-parallel sharding over the "
+              "batch is described in DESIGN.md); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import convolution_int8_implicit_amd as ifx
+    from convolution_int8_implicit_amd import model, synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    ifx.lib()
+    stream = torch.cuda.current_stream()
+    sub_batch = model.DEFAULT_SUB_BATCH if args.sub_batch is None else args.sub_batch
+
+    # ---------------- workload setup (untimed) ----------------
+    if args.workload == "net":
+        wl = synth.workload(4)
+        n = wl.n
+        net = model.DeviceNet(wl.net, wl.index, sub_batch=sub_batch)
+        x_nhwc = synth.input_tensor(wl, device="cuda")
+        x_blk = model.empty_act(n, 224, 224, 3)
+        ws = torch.empty(net.workspace_bytes(n), dtype=torch.int8, device="cuda")
+        logits = torch.empty((n, wl.net.fc_out), dtype=torch.int32, device="cuda")
+
+        def step():
+            ifx.pack_act(x_nhwc, out=x_blk, stream=stream)
+            net.forward(x_blk, logits, n, ws, stream)
+        layers = net_layers(wl.net, n)
+        total_ops = sum(layer_work(s, nn, h, w)[0] for s, nn, h, w in layers) + 2 * n * wl.net.fc_in * wl.net.fc_out
+        config = {"workload": wl.name, "batch": n, "image": "224x224x3 int8 NHWC", "convs": 53,
+                  "head": "avgpool + FC 2048->1000 int32 logits", "sub_batch": sub_batch,
+                  "step": "input pack + ifx_net_forward"}
+    else:
+        idx = {"conv1x1": 1, "conv1x1_b1": 0, "block": 2, "stem": 3}[args.workload]
+        wl = synth.workload(idx)
+        n = wl.n
+        dcs = [model.device_conv(s, wl.index, n, wl.h, wl.w) if i == 0 else None for i, s in enumerate(wl.convs)]
+        x_blk = ifx.pack_act(synth.input_tensor(wl, device="cuda"))
+        if wl.kind == "block":
+            dcs = [model.device_conv(s, wl.index, n, 28, 28) for s in wl.convs]
+            blk = model.DeviceBlock(dcs, None)
+            ws = torch.empty(blk.workspace_bytes(), dtype=torch.int8, device="cuda")
+            y = model.empty_act(n, 28, 28, 512)
+
+            def step():
+                blk.forward(x_blk, y, ws, stream)
+            layers = [(s, n, 28, 28) for s in wl.convs]
+        else:
+            spec = wl.convs[0]
+            ho, wo = spec.out_hw(wl.h, wl.w)
+            y = model.empty_act(n, ho, wo, spec.c_out)
+            res = ifx.pack_act(synth.residual_tensor(wl, device="cuda")) if spec.flags & 2 else None
+
+            def step():
+                dcs[0].run(x_blk, y, res, stream)
+            layers = [(spec, n, wl.h, wl.w)]
+        total_ops = sum(layer_work(s, nn, h, w)[0] for s, nn, h, w in layers)
+        config = {"workload": wl.name, "batch": n}
+
+    # ---------------- timed region ----------------
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    sec_per_step = max(ev0.elapsed_time(ev1) * 1e-3, 0.0) / args.steps
+    img_s = n / sec_per_step
+    tops = total_ops / sec_per_step / 1e12
+
+    # ---------------- per-kernel durations (HIP events on the launch stream) ----------------
+    # The convolutions of a step are replayed one launch at a time through ifx_conv_fused on
+    # the same stream and the same data flow as the drivers (real activations), each launch
+    # bracketed by HIP events; durations are grouped by kernel instance.
+    def with_batch(dc, nb):
+        d = ifx.ConvDesc.from_buffer_copy(dc.desc)
+        d.n = nb
+        return model.DeviceConv(dc.spec, d, dc.w_blk, dc.bias, dc.mult, dc.shift, dc.out_hw)
+
+    launches = []  # (spec, h, w, fn)
+    if args.workload == "net":
+        nb = sub_batch if 0 < sub_batch < n else n
+        passes = (n + nb - 1) // nb
+        big = max(ifx.act_bytes(nb, h, w, s.c_out if s.k != 7 else 64) for s, _, h, w in layers)
+        big = max(big, ifx.act_bytes(nb, 56, 56, 256))
+        bufs = [torch.empty(big, dtype=torch.int8, device="cuda") for _ in range(5)]
+        cur, nxt, t1, t2, sc = bufs
+        stem = with_batch(net.stem, nb)
+        launches.append((wl.net.stem, 224, 224, lambda: stem.run(x_blk[:nb], cur, None, stream)))
+        h = w = 56
+        state = {"cur": cur, "nxt": nxt}
+        for bs, db in zip(wl.net.blocks, net.blocks):
+            c1, c2, c3 = (with_batch(d, nb) for d in db.convs)
+            pj = with_batch(db.proj, nb) if db.proj is not None else None
+            h2 = c2.out_hw[0]
+
+            def mk(c, xin_key, out, res_key=None):
+                def f():
+                    xin = state[xin_key] if isinstance(xin_key, str) else xin_key
+                    res = None if res_key is None else (state[res_key] if isinstance(res_key, str) else res_key)
+                    o = state[out] if isinstance(out, str) else out
+                    c.run(xin, o, res, stream)
+                return f
+            launches.append((bs.c1, h, w, mk(c1, "cur", t1)))
+            launches.append((bs.c2, h, w, mk(c2, t1, t2)))
+            if pj is not None:
+                launches.append((bs.proj, h, w, mk(pj, "cur", sc)))
+            launches.append((bs.c3, h2, h2, mk(c3, t2, "nxt", sc if pj is not None else "cur")))
+
+            def swap():
+                state["cur"], state["nxt"] = state["nxt"], state["cur"]
+            launches.append((None, 0, 0, swap))
+            h = w = h2
+    else:
+        nb, passes = n, 1
+        if wl.kind == "block":
+            t1b = model.empty_act(n, 28, 28, 128)
+            t2b = model.empty_act(n, 28, 28, 128)
+            c1, c2, c3 = dcs
+            launches = [(wl.convs[0], 28, 28, lambda: c1.run(x_blk, t1b, None, stream)),
+                        (wl.convs[1], 28, 28, lambda: c2.run(t1b, t2b, None, stream)),
+                        (wl.convs[2], 28, 28, lambda: c3.run(t2b, y, x_blk, stream))]
+        else:
+            launches = [(wl.convs[0], wl.h, wl.w, step)]
+    reps = max(1, min(args.steps, 5) if args.workload == "net" else args.steps)
+    evs = []
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        for spec, h, w, fn in launches:
+            if spec is None:
+                fn()
+                continue
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            evs.append((spec, h, w, a, b))
+    torch.cuda.synchronize()
+    per_kernel = {}
+    for spec, h, w, a, b in evs:
+        name = kernel_name(spec)
+        ops, byts, _, _ = layer_work(spec, nb, h, w)
+        d = per_kernel.setdefault(name, {"time": 0.0, "ops": 0, "bytes": 0, "launches": 0})
+        d["time"] += a.elapsed_time(b) * 1e-3
+        d["ops"] += ops
+        d["bytes"] += byts
+        d["launches"] += 1
+    dom_name, dom = max(per_kernel.items(), key=lambda kv: kv[1]["time"])
+    ai = dom["ops"] / dom["bytes"]
+    avg_t = dom["time"] / dom["launches"]
+    if ai >= RIDGE:
+        achieved = dom["ops"] / dom["launches"] / avg_t / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_I8 / 1e12, "unit": "TFLOP/s"}
+    else:
+        achieved = dom["bytes"] / dom["launches"] / avg_t / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
+    roof["frac"] = round(achieved / roof["peak"], 4)
+    roof["traffic"] = None
+    roof["kernel"] = dom_name
+    roof["launches_per_step"] = dom["launches"] // reps * passes
+    roof["avg_launch_us"] = round(avg_t * 1e6, 2)
+    roof["work_per_launch"] = {"ops": dom["ops"] // dom["launches"], "bytes": dom["bytes"] // dom["launches"]}
+    kernel_share = {k: round(v["time"] / reps * passes * 1e3, 3) for k, v in per_kernel.items()}
+
+    line = {
+        "metric": METRIC,
+        "value": round(img_s, 1),
+        "unit": "images/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(sec_per_step * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic (seeded SplitMix64, uniform int8 images/weights)",
+        "config": config,
+        "tops": round(tops, 2),
+        "frac_int8_peak": round(tops * 1e12 / PEAK_I8, 4),
+        "kernel_ms_per_step": kernel_share,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(args.workload)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
