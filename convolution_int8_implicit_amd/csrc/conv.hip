@@ -7,27 +7,29 @@
 // thanks to the NC/32HW32 activation and [O1,KH,KW,I1,O2,32] weight layouts
 // (section 3.1).  The epilogue (section 3.4: BN, Sum with the shortcut, ReLU)
 // runs on the int32 accumulators before anything is written, and the
-// shortcut tile is fetched at kernel start so its latency hides behind the
-// contraction (the article's early asynchronous shortcut copy).
+// shortcut tile is fetched while the contraction runs (the article's early
+// asynchronous shortcut copy).
 //
 // gfx950 design (not the article's A100 tiling):
-//   * one 256-thread workgroup (4 wave64s) owns a BM x BN output tile; each
-//     wave owns 64x64 = 4x4 tiles of v_mfma_i32_16x16x64_i8;
-//   * the K loop steps 64 bytes (two 32-channel blocks) at a time through an
-//     ST-deep LDS ring filled by direct buffer->LDS 16-byte loads
-//     (buffer_load_dwordx4 ... lds): loads for step k+ST-1 are in flight
-//     while the MFMAs consume step k, with no register staging; the buffer
-//     range check turns every out-of-image tap, ragged row or padded channel
-//     into zeros, so the implicit GEMM needs no im2col and no branches;
-//   * LDS rows are 64 bytes with an XOR swizzle of the four 16-byte chunks,
-//     realised by choosing which global chunk each lane fetches;
+//   * persistent 256-thread workgroups (4 wave64s), two per CU; each owns a
+//     list of BM x BN output tiles and streams the flattened sequence of
+//     (tile, K-step) stages through an ST-deep LDS ring, so the loads of the
+//     next tile are in flight while the current tile's epilogue runs;
+//   * ring stages are filled by direct buffer->LDS 16-byte loads
+//     (buffer_load_dwordx4 ... lds), no register staging; the buffer range
+//     check turns every out-of-image tap, ragged row or padded channel into
+//     zeros, so the implicit GEMM needs neither im2col nor branches;
+//   * each wave owns 64x64 outputs = 4x4 v_mfma_i32_16x16x64_i8 tiles; one
+//     K-step is 64 bytes = two 32-channel blocks;
+//   * LDS rows are 64 bytes with an XOR swizzle of their four 16-byte
+//     chunks, realised by choosing which global chunk each lane fetches;
 //   * MFMA columns are permuted so that each lane holds four consecutive
-//     output channels of a pixel: the epilogue requantises in registers,
-//     stages the packed bytes through LDS and writes whole 16-byte chunks of
-//     the NC/32HW32 output (the shortcut arrives the same way);
-//   * the BN bias is folded into the accumulator initial value;
-//   * workgroups are renumbered so that tiles sharing an activation tile run
-//     back to back on the same XCD (own L2).
+//     output channels of a pixel; the epilogue requantises in registers,
+//     stages bytes through LDS and writes whole 16-byte chunks of the
+//     NC/32HW32 output (the shortcut and the per-channel parameters arrive
+//     in LDS by DMA as well);
+//   * tiles are dealt out XCD by XCD so the tiles sharing an activation tile
+//     run together on one XCD (own L2).
 #include "ifx_internal.h"
 
 typedef int ifx_v4i __attribute__((ext_vector_type(4)));
@@ -43,20 +45,20 @@ namespace {
 typedef ifx_v4i v4i;
 
 constexpr int kThreads = 256;
-constexpr int kStages = 4;
+constexpr int kStages = 3;
 constexpr unsigned kOOB = 0x80000000u;  // offset past every buffer range: loads return zero
 
-
 // Buffer resource (gfx9 layout): 48-bit base, stride 0, byte range, raw-buffer config word.
-__device__ __forceinline__ v4i make_rsrc(const void *base, unsigned range)
+__device__ __forceinline__ v4i make_rsrc(const void *base, long long range)
 {
     unsigned long long a = (unsigned long long)base;
-    v4i r;
-    r.x = __builtin_amdgcn_readfirstlane((int)(unsigned)a);
-    r.y = __builtin_amdgcn_readfirstlane((int)(unsigned)(a >> 32) & 0xffff);
-    r.z = __builtin_amdgcn_readfirstlane((int)range);
-    r.w = 0x00020000;
-    return r;
+    unsigned r = (unsigned)(range < 0 ? 0 : (range > 0x7ffffff0ll ? 0x7ffffff0ll : range));
+    v4i v;
+    v.x = __builtin_amdgcn_readfirstlane((int)(unsigned)a);
+    v.y = __builtin_amdgcn_readfirstlane((int)(unsigned)(a >> 32) & 0xffff);
+    v.z = __builtin_amdgcn_readfirstlane((int)r);
+    v.w = 0x00020000;
+    return v;
 }
 
 __device__ __forceinline__ void load16_lds(v4i rsrc, int8_t *lds_wave_base, unsigned voff)
@@ -64,7 +66,9 @@ __device__ __forceinline__ void load16_lds(v4i rsrc, int8_t *lds_wave_base, unsi
     ifx_raw_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void *)(lds_wave_base), 16, voff, 0, 0, 0);
 }
 
-// s_waitcnt vmcnt(n) with expcnt/lgkmcnt left unconstrained (gfx9 encoding).
+// s_waitcnt vmcnt(n), expcnt/lgkmcnt unconstrained (gfx9 encoding).  Vector
+// loads complete in issue order, so "at most n outstanding" guarantees every
+// load older than the last n loads has landed, whatever stores are pending.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt()
 {
@@ -72,16 +76,24 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 0xf) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
 }
 
-// Workgroup barrier for the LDS ring.  Each wave first waits for its own
-// direct-to-LDS loads of the stage (wait_vmcnt); LDS needs no cache
-// maintenance, so a bare s_barrier then makes every wave's stage data visible.
-// (__syncthreads would add a release fence that drains all loads in flight,
-// i.e. the whole ring.)  The empty asm keeps the compiler from moving LDS
-// accesses across the barrier.
+// Workgroup barrier for LDS filled by DMA: every wave has already waited for
+// its own loads, and LDS needs no cache maintenance, so a bare s_barrier
+// publishes them (__syncthreads would add a fence that drains every load in
+// flight).  The empty asm keeps the compiler from moving LDS accesses across.
 __device__ __forceinline__ void ring_barrier()
 {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Intra-wave LDS hand-over (lanes read what other lanes of the same wave
+// wrote): LDS executes a wave's accesses in order; only compiler reordering
+// has to be prevented.
+__device__ __forceinline__ void wave_lds_sync()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_wave_barrier();
     asm volatile("" ::: "memory");
 }
 
@@ -110,8 +122,8 @@ __device__ __forceinline__ int requant_fast(int y, int m, int rnd_hi, int sh_m1)
     return ((int)(p >> 32)) >> sh_m1;
 }
 
-// sh >= 2 and a ReLU with no shortcut: for y < 0 the result is <= 0 either way
-// and the ReLU clears it, so the [y<0] tie correction can be dropped.
+// sh >= 2 followed by a ReLU with no shortcut: for y < 0 the result is <= 0
+// either way and the ReLU clears it, so the [y<0] tie correction is dropped.
 __device__ __forceinline__ int requant_relu(int y, int m, int rnd_hi, int sh_m1)
 {
     long long add = (long long)((unsigned long long)(unsigned)rnd_hi << 32);
@@ -119,15 +131,22 @@ __device__ __forceinline__ int requant_relu(int y, int m, int rnd_hi, int sh_m1)
     return ((int)(p >> 32)) >> sh_m1;
 }
 
-// Requantise a wave's 64x64 accumulator tile and leave the packed int8 bytes
-// in the LDS staging tile (row stride BN), adding the shortcut bytes already
-// there when RES.  MODE 0: general (any shift); 1: shift >= 2 with ReLU and no
-// shortcut; 2: shift >= 2.  Lane (g, c) owns pixel rows 16tm + 4i + g and the
-// 4 bytes at column 4c.
-template <int MODE, bool RES, int BN>
-__device__ __forceinline__ void requant_tile(const v4i (&acc)[4][4], int8_t *rbase, const int (&mul)[4],
-                                             const int (&rnd)[4], const int (&shm)[4], const int (&shf)[4],
-                                             const int (&keep)[4], bool relu)
+// Pack the low bytes of four int32 values (already in [-128, 127]).
+__device__ __forceinline__ unsigned pack4(int q0, int q1, int q2, int q3)
+{
+    unsigned lo = __builtin_amdgcn_perm((unsigned)q1, (unsigned)q0, 0x0c0c0400u);
+    unsigned hi = __builtin_amdgcn_perm((unsigned)q3, (unsigned)q2, 0x0c0c0400u);
+    return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+}
+
+// Requantise a wave's 64x64 accumulator tile into the LDS staging tile (row
+// stride BN), adding the shortcut bytes already there when RES.  MODE 0:
+// general (any shift); 1: shift >= 2, ReLU, no shortcut; 2: shift >= 2.
+// Lane (g, c) owns tile rows 16tm + 4i + g and the 4 bytes at column 4c.
+template <int MODE, bool RES, bool RELU, int BN>
+__device__ __forceinline__ void requant_tile(const v4i (&acc)[4][4], int8_t *rbase, const int (&bias)[4],
+                                             const int (&mul)[4], const int (&rnd)[4], const int (&shm)[4],
+                                             const int (&shf)[4])
 {
 #pragma unroll
     for (int tm = 0; tm < 4; ++tm)
@@ -135,45 +154,46 @@ __device__ __forceinline__ void requant_tile(const v4i (&acc)[4][4], int8_t *rba
         for (int i = 0; i < 4; ++i) {
             unsigned *rp = (unsigned *)(rbase + (16 * tm + 4 * i) * BN);
             const unsigned rr = RES ? *rp : 0u;
-            unsigned packed = 0;
+            int q[4];
 #pragma unroll
             for (int tn = 0; tn < 4; ++tn) {
-                const int yv = acc[tm][tn][i];
-                int q;
+                const int yv = acc[tm][tn][i] + bias[tn];
+                int v;
                 if (MODE == 0)
-                    q = requant_any(yv, mul[tn], shf[tn]);
+                    v = requant_any(yv, mul[tn], shf[tn]);
                 else if (MODE == 1)
-                    q = requant_relu(yv, mul[tn], rnd[tn], shm[tn]);
+                    v = requant_relu(yv, mul[tn], rnd[tn], shm[tn]);
                 else
-                    q = requant_fast(yv, mul[tn], rnd[tn], shm[tn]);
-                if (RES) q += (int)(signed char)(rr >> (8 * tn));
-                q = relu ? min(max(q, 0), 127) : min(max(q, -128), 127);
-                packed |= (unsigned)(q & keep[tn]) << (8 * tn);
+                    v = requant_fast(yv, mul[tn], rnd[tn], shm[tn]);
+                if (RES) v += (int)(signed char)(rr >> (8 * tn));
+                q[tn] = RELU ? min(max(v, 0), 127) : min(max(v, -128), 127);
             }
-            *rp = packed;
+            *rp = pack4(q[0], q[1], q[2], q[3]);
         }
 }
 
-template <int KH, int KW, int BM, int BN, bool RES>
+template <int BM, int BN>
 struct ConvCfg {
     static constexpr int WAVES_M = BM / 64;
     static constexpr int WAVES_N = BN / 64;
     static_assert(WAVES_M * WAVES_N == kThreads / 64, "4 waves per workgroup");
     static constexpr int AI = BM * 64 / 16 / kThreads;  // A-tile loads per thread per stage
     static constexpr int BI = BN * 64 / 16 / kThreads;  // B-tile loads per thread per stage
+    static constexpr int LPS = AI + BI;                 // loads per thread per stage
     static constexpr int STAGE = (BM + BN) * 64;        // bytes per ring stage
     static constexpr int RI = BM * BN / 16 / kThreads;  // shortcut loads per thread
     static constexpr int RING = kStages * STAGE;
-    static constexpr int LDS = RES ? RING + BM * BN : (RING > BM * BN ? RING : BM * BN);
+    static constexpr int LDS = RING + BM * BN + 3 * 1024;  // ring | staging tile | bias,mult,shift
 };
 
-template <int KH, int KW, int BM, int BN, bool RES>
+template <int KH, int KW, int BM, int BN, bool RES, bool RELU>
 __global__ __launch_bounds__(kThreads, 2) void conv_kernel(ConvArgs a)
 {
-    using C = ConvCfg<KH, KW, BM, BN, RES>;
-    constexpr int AI = C::AI, BI = C::BI, STAGE = C::STAGE;
+    using C = ConvCfg<BM, BN>;
+    constexpr int AI = C::AI, BI = C::BI, LPS = C::LPS, STAGE = C::STAGE;
     __shared__ __attribute__((aligned(1024))) int8_t smem[C::LDS];
-    int8_t *R = RES ? smem + C::RING : smem;  // [BM][BN] shortcut / output staging
+    int8_t *const R = smem + C::RING;      // [BM][BN] shortcut in, packed output out
+    int8_t *const Pm = R + BM * BN;        // [3][1024 B]: bias, mult, shift of the tile's channels
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -181,169 +201,276 @@ __global__ __launch_bounds__(kThreads, 2) void conv_kernel(ConvArgs a)
     const int wm0 = (wave % C::WAVES_M) * 64;
     const int wn0 = (wave / C::WAVES_M) * 64;
 
-    // ---- tile of this workgroup (XCD-aware renumbering) ----
+    // ---- this workgroup's tiles: XCD x takes the x-th eighth of the tile
+    //      list (row-major over (m, n)); its workgroups deal it round robin ----
     const int tiles_n = (a.oc1 * 32 + BN - 1) / BN;
-    const int G = gridDim.x;
-    const int bid = blockIdx.x;
-    const int per_xcd = G >> 3;
-    const int lin = bid < (per_xcd << 3) ? (bid & 7) * per_xcd + (bid >> 3) : bid;
-    const int tile_n = lin % tiles_n;
-    const int tile_m = lin / tiles_n;
-    const int m0 = tile_m * BM;
-    const int n0 = tile_n * BN;
+    const int tiles_m = (a.m + BM - 1) / BM;
+    const long long T = (long long)tiles_m * tiles_n;
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, per = gridDim.x >> 3;
+    const long long xb = T * xcd / 8;
+    const long long span = T * (xcd + 1) / 8 - xb;
+    if (span <= slot) return;
+    const int n_items = (int)((span - slot + per - 1) / per);
+    const int nsteps = (a.nkb + 1) >> 1;
 
     const int HoWo = a.ho * a.wo;
     const int HW = a.h * a.w;
-    const int img0 = m0 / HoWo;  // first image touched by this tile
-
-    // per-lane output channels and their folded BN bias (loaded before any
-    // ring traffic so waiting for them never drains the prefetches)
-    const int c = lane & 15;
-    const int g = lane >> 4;
-    const int ocl = n0 + wn0 + 4 * c;  // first of this lane's four output channels
-    int bias_v[4];
-#pragma unroll
-    for (int tn = 0; tn < 4; ++tn) bias_v[tn] = (ocl + tn < a.oc) ? a.bias[ocl + tn] : 0;
-
-    // ---- buffer resources, based at the tile's first image (offsets < 2^31) ----
     const long long in_img = (long long)a.i1 * HW * 32;
     const long long in_total = (long long)a.n * in_img;
-    const long long in_base = (long long)img0 * in_img;
-    const unsigned in_range = (unsigned)min(in_total - in_base, 0x7ffffff0ll);
-    const v4i rsA = make_rsrc(a.x + in_base, in_range);
-    const long long wbytes = (long long)((a.oc + a.o2 - 1) / a.o2) * a.o2 * KH * KW * a.i1 * 32;
-    const v4i rsB = make_rsrc(a.wt, (unsigned)min(wbytes, 0x7ffffff0ll));
+    const long long out_img = (long long)a.oc1 * HoWo * 32;
+    const int wrows = ((a.oc + a.o2 - 1) / a.o2) * a.o2;
+    const v4i rsB = make_rsrc(a.wt, (long long)wrows * KH * KW * a.i1 * 32);
+    const unsigned wstride_c1 = (unsigned)a.o2 * 32;
 
-    // ---- shortcut tile -> LDS (issued first; lands while the K loop runs) ----
-    if (RES) {
-        const long long out_img = (long long)a.oc1 * HoWo * 32;
-        const long long r_base = (long long)img0 * out_img;
-        const unsigned r_range = (unsigned)min((long long)a.n * out_img - r_base, 0x7ffffff0ll);
-        const v4i rsR = make_rsrc(a.res + r_base, r_range);
-        constexpr int CPR = BN / 16;  // 16-byte chunks per staged row
-#pragma unroll
-        for (int j = 0; j < C::RI; ++j) {
-            const int slot = (j * 4 + wave) * 64 + lane;  // 16-byte slot of R
-            const int row = slot / CPR, ch = slot % CPR;
-            const int p = m0 + row;
-            const int oc = n0 + ch * 16;
-            unsigned off = kOOB;
-            if (p < a.m && oc < a.oc1 * 32) {
-                const int b = p / HoWo, hw = p - (p / HoWo) * HoWo;
-                off = (unsigned)((((long long)(b - img0) * a.oc1 + (oc >> 5)) * HoWo + hw) * 32 + (oc & 31));
-            }
-            load16_lds(rsR, R + (j * 4 + wave) * 1024, off);
-        }
-    }
+    auto item_tile = [&](int it, int &m0, int &n0) {
+        const long long lin = xb + slot + (long long)it * per;
+        m0 = (int)(lin / tiles_n) * BM;
+        n0 = (int)(lin % tiles_n) * BN;
+    };
 
-    // ---- per-lane load plans for the A (activation) and B (weight) tiles ----
-    // A: instruction j of wave w fills rows [(4j+w)*16, +16) of the stage;
-    //    lane l -> row (4j+w)*16 + l/4, physical chunk l%4.
+    // ---------------- issue cursor: next (tile, K-step) stage to load ----------------
+    int is_it = 0, is_ks = 0;
+    int s_c1 = 0, s_kx = 0, s_ky = 0, s_kb = 0;  // first block of the step: (ky, kx, c1), flat index
+    v4i rsA;
     unsigned a_img[AI];
     int a_iy[AI], a_ix[AI], a_sel[AI];
     bool a_ok[AI];
-#pragma unroll
-    for (int j = 0; j < AI; ++j) {
-        const int row = (j * 4 + wave) * 16 + (lane >> 2);
-        const int lch = (lane & 3) ^ swz(row);
-        const int p = m0 + row;
-        a_ok[j] = p < a.m;
-        const int pp = a_ok[j] ? p : m0;
-        const int b = pp / HoWo;
-        const int rem = pp - b * HoWo;
-        const int oy = rem / a.wo;
-        const int ox = rem - oy * a.wo;
-        a_iy[j] = oy * a.stride - a.pad;
-        a_ix[j] = ox * a.stride - a.pad;
-        a_img[j] = (unsigned)((long long)(b - img0) * in_img) + (lch & 1) * 16;
-        a_sel[j] = lch >> 1;  // which of the step's two 32-channel blocks
-    }
-    // B: instruction j of wave w fills physical rows [(4j+w)*16, +16); within
-    //    each 64-row group physical row r holds output channel (r%16)*4 + r/16.
     unsigned b_off[BI];
     int b_sel[BI];
     bool b_ok[BI];
-#pragma unroll
-    for (int j = 0; j < BI; ++j) {
-        const int prow = (j * 4 + wave) * 16 + (lane >> 2);
-        const int lch = (lane & 3) ^ swz(prow);
-        const int o = (prow & ~63) + (prow & 15) * 4 + ((prow & 63) >> 4);
-        const int R_ = n0 + o;
-        const int wrows = ((a.oc + a.o2 - 1) / a.o2) * a.o2;
-        b_ok[j] = R_ < wrows;
-        const int RR = b_ok[j] ? R_ : 0;
-        const int o1 = RR / a.o2, o2i = RR - (RR / a.o2) * a.o2;
-        b_off[j] = (unsigned)(((long long)o1 * KH * KW * a.i1 * a.o2 + o2i) * 32) + (lch & 1) * 16;
-        b_sel[j] = lch >> 1;
-    }
 
-    const int nsteps = (a.nkb + 1) >> 1;
-    const unsigned wstride_c1 = (unsigned)a.o2 * 32;
-
-    // uniform reduction position of the step's first block: (ky, kx, c1)
-    int s_c1 = 0, s_kx = 0, s_ky = 0, s_kb = 0;
-    auto issue = [&](int slot) {
-        // second block of the step: the block after (ky, kx, c1)
-        int c1b = s_c1 + 1, kxb = s_kx, kyb = s_ky;
-        if (c1b == a.i1) {
-            c1b = 0;
-            if (++kxb == KW) {
-                kxb = 0;
-                ++kyb;
-            }
-        }
-        int8_t *st = smem + slot * STAGE;
+    auto plan = [&]() {  // per-lane load plans of tile is_it
+        int m0, n0;
+        item_tile(is_it, m0, n0);
+        const int img0 = m0 / HoWo;
+        rsA = make_rsrc(a.x + (long long)img0 * in_img, in_total - (long long)img0 * in_img);
+        // A: instruction j of wave w fills stage rows [(4j+w)*16, +16); lane l -> row (4j+w)*16 + l/4,
+        //    physical chunk l%4, which holds logical chunk (l%4) ^ swz(row).
 #pragma unroll
         for (int j = 0; j < AI; ++j) {
-            const int sel = a_sel[j];
-            const int c1 = sel ? c1b : s_c1;
-            const int kx = sel ? kxb : s_kx;
-            const int ky = sel ? kyb : s_ky;
-            const int iy = a_iy[j] + ky, ix = a_ix[j] + kx;
-            bool ok = a_ok[j] && (s_kb + sel) < a.nkb;
-            if (KH > 1) ok = ok && (unsigned)iy < (unsigned)a.h;
-            if (KW > 1) ok = ok && (unsigned)ix < (unsigned)a.w;
-            const unsigned off = ok ? a_img[j] + (unsigned)(((c1 * a.h + iy) * a.w + ix) * 32) : kOOB;
-            load16_lds(rsA, st + (j * 4 + wave) * 1024, off);
+            const int row = (j * 4 + wave) * 16 + (lane >> 2);
+            const int lch = (lane & 3) ^ swz(row);
+            const int p = m0 + row;
+            a_ok[j] = p < a.m;
+            const int pp = a_ok[j] ? p : m0;
+            const int b = pp / HoWo;
+            const int rem = pp - b * HoWo;
+            const int oy = rem / a.wo;
+            const int ox = rem - oy * a.wo;
+            a_iy[j] = oy * a.stride - a.pad;
+            a_ix[j] = ox * a.stride - a.pad;
+            a_img[j] = (unsigned)((long long)(b - img0) * in_img) + (lch & 1) * 16;
+            a_sel[j] = lch >> 1;  // which of the step's two 32-channel blocks
         }
+        // B: instruction j of wave w fills physical rows [(4j+w)*16, +16); within each
+        //    64-row group physical row r holds output channel (r%16)*4 + r/16.
 #pragma unroll
         for (int j = 0; j < BI; ++j) {
-            const int sel = b_sel[j];
-            const int c1 = sel ? c1b : s_c1;
-            const int kx = sel ? kxb : s_kx;
-            const int ky = sel ? kyb : s_ky;
-            const bool ok = b_ok[j] && (s_kb + sel) < a.nkb;
-            const unsigned off = ok ? b_off[j] + (unsigned)((ky * KW + kx) * a.i1 + c1) * wstride_c1 : kOOB;
-            load16_lds(rsB, st + BM * 64 + (j * 4 + wave) * 1024, off);
+            const int prow = (j * 4 + wave) * 16 + (lane >> 2);
+            const int lch = (lane & 3) ^ swz(prow);
+            const int o = (prow & ~63) + (prow & 15) * 4 + ((prow & 63) >> 4);
+            const int Rw = n0 + o;
+            b_ok[j] = Rw < wrows;
+            const int RR = b_ok[j] ? Rw : 0;
+            const int o1 = RR / a.o2, o2i = RR - (RR / a.o2) * a.o2;
+            b_off[j] = (unsigned)(((long long)o1 * KH * KW * a.i1 * a.o2 + o2i) * 32) + (lch & 1) * 16;
+            b_sel[j] = lch >> 1;
         }
-        // advance two blocks
-        s_kb += 2;
-        s_c1 += 2;
-        while (s_c1 >= a.i1) {
-            s_c1 -= a.i1;
-            if (++s_kx == KW) {
-                s_kx = 0;
-                ++s_ky;
+        s_c1 = s_kx = s_ky = s_kb = 0;
+    };
+
+    auto issue = [&](int ring_slot) {
+        int8_t *st = smem + ring_slot * STAGE;
+        if (is_it < n_items) {
+            int c1b = s_c1 + 1, kxb = s_kx, kyb = s_ky;  // the step's second block
+            if (c1b == a.i1) {
+                c1b = 0;
+                if (++kxb == KW) {
+                    kxb = 0;
+                    ++kyb;
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < AI; ++j) {
+                const int sel = a_sel[j];
+                const int c1 = sel ? c1b : s_c1;
+                const int kx = sel ? kxb : s_kx;
+                const int ky = sel ? kyb : s_ky;
+                const int iy = a_iy[j] + ky, ix = a_ix[j] + kx;
+                bool ok = a_ok[j] && (s_kb + sel) < a.nkb;
+                if (KH > 1) ok = ok && (unsigned)iy < (unsigned)a.h;
+                if (KW > 1) ok = ok && (unsigned)ix < (unsigned)a.w;
+                const unsigned off = ok ? a_img[j] + (unsigned)(((c1 * a.h + iy) * a.w + ix) * 32) : kOOB;
+                load16_lds(rsA, st + (j * 4 + wave) * 1024, off);
+            }
+#pragma unroll
+            for (int j = 0; j < BI; ++j) {
+                const int sel = b_sel[j];
+                const int c1 = sel ? c1b : s_c1;
+                const int kx = sel ? kxb : s_kx;
+                const int ky = sel ? kyb : s_ky;
+                const bool ok = b_ok[j] && (s_kb + sel) < a.nkb;
+                const unsigned off = ok ? b_off[j] + (unsigned)((ky * KW + kx) * a.i1 + c1) * wstride_c1 : kOOB;
+                load16_lds(rsB, st + BM * 64 + (j * 4 + wave) * 1024, off);
+            }
+            s_kb += 2;
+            s_c1 += 2;
+            while (s_c1 >= a.i1) {
+                s_c1 -= a.i1;
+                if (++s_kx == KW) {
+                    s_kx = 0;
+                    ++s_ky;
+                }
+            }
+            if (++is_ks == nsteps) {
+                is_ks = 0;
+                if (++is_it < n_items) plan();
+            }
+        } else {
+            // past the last tile: same number of loads, all out of range (they write zeros)
+#pragma unroll
+            for (int j = 0; j < AI; ++j) load16_lds(rsB, st + (j * 4 + wave) * 1024, kOOB);
+#pragma unroll
+            for (int j = 0; j < BI; ++j) load16_lds(rsB, st + BM * 64 + (j * 4 + wave) * 1024, kOOB);
+        }
+    };
+
+    // per-channel parameters and shortcut of the tile being computed -> LDS
+    auto issue_tile_inputs = [&](int m0, int n0) {
+        if (wave == 0) {
+            const bool v = 4 * lane < BN && n0 + 4 * lane < a.oc;
+            const unsigned off = v ? (unsigned)(n0 + 4 * lane) * 4 : kOOB;
+            load16_lds(make_rsrc(a.bias, (long long)a.oc * 4), Pm, off);
+            if (!a.out_i32) {
+                load16_lds(make_rsrc(a.mult, (long long)a.oc * 4), Pm + 1024, off);
+                load16_lds(make_rsrc(a.shift, (long long)a.oc * 4), Pm + 2048, off);
+            }
+        }
+        if (RES) {
+            const int img0 = m0 / HoWo;
+            const v4i rsR = make_rsrc(a.res + (long long)img0 * out_img, (long long)(a.n - img0) * out_img);
+            constexpr int CPR = BN / 16;  // 16-byte chunks per staged row
+#pragma unroll
+            for (int j = 0; j < C::RI; ++j) {
+                const int q = (j * 4 + wave) * 64 + lane;  // 16-byte slot of R
+                const int row = q / CPR, ch = q % CPR;
+                const int p = m0 + row;
+                const int oc = n0 + ch * 16;
+                unsigned off = kOOB;
+                if (p < a.m && oc < a.oc1 * 32) {
+                    const int b = p / HoWo, hw = p - (p / HoWo) * HoWo;
+                    off = (unsigned)((((long long)(b - img0) * a.oc1 + (oc >> 5)) * HoWo + hw) * 32 + (oc & 31));
+                }
+                load16_lds(rsR, R + (j * 4 + wave) * 1024, off);
             }
         }
     };
 
-    // ---- accumulators, initialised with the folded BN bias ----
+    const int c = lane & 15;
+    const int g = lane >> 4;
     v4i acc[4][4];
-#pragma unroll
-    for (int tn = 0; tn < 4; ++tn) {
-#pragma unroll
-        for (int tm = 0; tm < 4; ++tm) acc[tm][tn] = (v4i){bias_v[tn], bias_v[tn], bias_v[tn], bias_v[tn]};
-    }
 
-    // ---- K loop over the LDS ring ----
+    auto epilogue = [&](int m0, int n0) {
+        // the tile's parameters and shortcut were issued at its first K-step;
+        // at most min(nsteps-1, ST-1) stages of later loads may stay in flight
+        const int later = min(nsteps - 1, kStages - 1);
+        if (later <= 0)
+            wait_vmcnt<0>();
+        else if (later == 1)
+            wait_vmcnt<LPS>();
+        else
+            wait_vmcnt<2 * LPS>();
+        ring_barrier();
+
+        const int ocl = n0 + wn0 + 4 * c;  // first of this lane's four output channels
+        const v4i bias4 = *(const v4i *)(Pm + (wn0 + 4 * c) * 4);
+        const int pbase = m0 + wm0;
+        if (a.out_i32) {
+            int32_t *y = (int32_t *)a.y;
+            const bool vec = (a.oc & 3) == 0 && ocl + 3 < a.oc;
+#pragma unroll
+            for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int p = pbase + 16 * tm + 4 * i + g;
+                    if (p >= a.m) continue;
+                    const long long off = (long long)p * a.oc + ocl;
+                    const v4i v = {acc[tm][0][i] + bias4.x, acc[tm][1][i] + bias4.y, acc[tm][2][i] + bias4.z,
+                                   acc[tm][3][i] + bias4.w};
+                    if (vec) {
+                        *(v4i *)(y + off) = v;
+                    } else {
+#pragma unroll
+                        for (int tn = 0; tn < 4; ++tn)
+                            if (ocl + tn < a.oc) y[off + tn] = v[tn];
+                    }
+                }
+            return;
+        }
+        const v4i mult4 = *(const v4i *)(Pm + 1024 + (wn0 + 4 * c) * 4);
+        const v4i shift4 = *(const v4i *)(Pm + 2048 + (wn0 + 4 * c) * 4);
+        int bias[4], mul[4], rnd[4], shm[4], shf[4];
+        bool fast_lane = true;
+#pragma unroll
+        for (int tn = 0; tn < 4; ++tn) {
+            const bool v = ocl + tn < a.oc;  // padded channels: bias = mult = 0 gives 0
+            bias[tn] = v ? bias4[tn] : 0;
+            mul[tn] = v ? mult4[tn] : 0;
+            shf[tn] = v ? shift4[tn] : 2;
+            fast_lane = fast_lane && shf[tn] >= 2;
+            rnd[tn] = 1 << ((shf[tn] - 2) & 31);
+            shm[tn] = shf[tn] - 1;
+        }
+        int8_t *rbase = R + (wm0 + g) * BN + wn0 + 4 * c;
+        if (!__all(fast_lane))
+            requant_tile<0, RES, RELU, BN>(acc, rbase, bias, mul, rnd, shm, shf);
+        else if (!RES && RELU)
+            requant_tile<1, RES, RELU, BN>(acc, rbase, bias, mul, rnd, shm, shf);
+        else
+            requant_tile<2, RES, RELU, BN>(acc, rbase, bias, mul, rnd, shm, shf);
+        wave_lds_sync();
+
+        // 16-byte stores of the wave's 64 pixels x 64 channels
+        int8_t *y = (int8_t *)a.y;
+        const int k = lane & 3;
+        const int och = n0 + wn0 + 16 * k;  // first channel of this lane's chunk
+        if (och >= a.oc1 * 32) return;
+        const int b0 = pbase / HoWo;
+        const int hw0 = pbase - b0 * HoWo;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int prow = 16 * j + (lane >> 2);
+            if (pbase + prow >= a.m) break;
+            int b = b0, hw = hw0 + prow;
+            while (hw >= HoWo) {
+                hw -= HoWo;
+                ++b;
+            }
+            const v4i v = *(const v4i *)(R + (wm0 + prow) * BN + wn0 + 16 * k);
+            *(v4i *)(y + (((long long)b * a.oc1 + (och >> 5)) * HoWo + hw) * 32 + (och & 31)) = v;
+        }
+    };
+
+    // ---------------- main stream ----------------
+    plan();
 #pragma unroll
     for (int s = 0; s < kStages - 1; ++s) issue(s);
-    for (int step = 0; step < nsteps; ++step) {
-        wait_vmcnt<(kStages - 2) * (AI + BI)>();
+
+    int c_it = 0, c_ks = 0, c_m0, c_n0;
+    item_tile(0, c_m0, c_n0);
+    const int S = n_items * nsteps;
+    for (int s = 0; s < S; ++s) {
+        wait_vmcnt<(kStages - 2) * LPS>();
         ring_barrier();
-        issue((step + kStages - 1) % kStages);  // past the end: all lanes out of range (zeros)
-        const int8_t *st = smem + (step % kStages) * STAGE;
+        issue((s + kStages - 1) % kStages);
+        if (c_ks == 0) {
+            issue_tile_inputs(c_m0, c_n0);
+#pragma unroll
+            for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+                for (int tn = 0; tn < 4; ++tn) acc[tm][tn] = (v4i){0, 0, 0, 0};
+        }
+        const int8_t *st = smem + (s % kStages) * STAGE;
         v4i af[4], bf[4];
 #pragma unroll
         for (int tm = 0; tm < 4; ++tm) {
@@ -361,102 +488,59 @@ __global__ __launch_bounds__(kThreads, 2) void conv_kernel(ConvArgs a)
 #pragma unroll
             for (int tn = 0; tn < 4; ++tn)
                 acc[tm][tn] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[tm], bf[tn], acc[tm][tn], 0, 0, 0);
-    }
-    wait_vmcnt<0>();
-    __syncthreads();
-
-    // ---- fused epilogue ----
-    // lane (g, c) of MFMA tile (tm, tn) holds pixel wm0 + 16tm + 4i + g of the
-    // tile and output channel ocl + tn, for i = 0..3.
-    const int pbase = m0 + wm0;
-    if (a.out_i32) {
-        int32_t *y = (int32_t *)a.y;
-        const bool vec = (a.oc & 3) == 0 && ocl + 3 < a.oc;
-#pragma unroll
-        for (int tm = 0; tm < 4; ++tm)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int p = pbase + 16 * tm + 4 * i + g;
-                if (p >= a.m) continue;
-                const long long off = (long long)p * a.oc + ocl;
-                if (vec) {
-                    *(v4i *)(y + off) = (v4i){acc[tm][0][i], acc[tm][1][i], acc[tm][2][i], acc[tm][3][i]};
-                } else {
-#pragma unroll
-                    for (int tn = 0; tn < 4; ++tn)
-                        if (ocl + tn < a.oc) y[off + tn] = acc[tm][tn][i];
-                }
-            }
-        return;
-    }
-
-    int mul[4], rnd[4], shm[4], shf[4], keep[4];
-    bool fast_lane = true;
-#pragma unroll
-    for (int tn = 0; tn < 4; ++tn) {
-        const int o = ocl + tn;
-        const bool v = o < a.oc;
-        mul[tn] = v ? a.mult[o] : 0;
-        shf[tn] = v ? a.shift[o] : 2;
-        fast_lane = fast_lane && shf[tn] >= 2;
-        rnd[tn] = 1 << ((shf[tn] - 2) & 31);
-        shm[tn] = shf[tn] - 1;
-        keep[tn] = v ? 0xff : 0;
-    }
-    const bool fast = __all(fast_lane);
-    const bool relu = a.relu != 0;
-
-    // requantise in registers; shortcut bytes and results share the staging tile R
-    int8_t *rbase = R + (wm0 + g) * BN + wn0 + 4 * c;
-    if (!fast)
-        requant_tile<0, RES, BN>(acc, rbase, mul, rnd, shm, shf, keep, relu);
-    else if (!RES && relu)
-        requant_tile<1, RES, BN>(acc, rbase, mul, rnd, shm, shf, keep, relu);
-    else
-        requant_tile<2, RES, BN>(acc, rbase, mul, rnd, shm, shf, keep, relu);
-    __syncthreads();
-
-    // 16-byte stores of the wave's 64 pixels x 64 channels
-    int8_t *y = (int8_t *)a.y;
-    const int k = lane & 3;
-    const int och = n0 + wn0 + 16 * k;  // first channel of this lane's chunk
-    if (och >= a.oc1 * 32) return;
-    const int b0 = pbase / HoWo;
-    const int hw0 = pbase - b0 * HoWo;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int prow = 16 * j + (lane >> 2);
-        if (pbase + prow >= a.m) break;
-        int b = b0, hw = hw0 + prow;
-        while (hw >= HoWo) {
-            hw -= HoWo;
-            ++b;
+        if (++c_ks == nsteps) {
+            epilogue(c_m0, c_n0);
+            c_ks = 0;
+            if (++c_it < n_items) item_tile(c_it, c_m0, c_n0);
         }
-        const v4i v = *(const v4i *)(R + (wm0 + prow) * BN + wn0 + 16 * k);
-        *(v4i *)(y + (((long long)b * a.oc1 + (och >> 5)) * HoWo + hw) * 32 + (och & 31)) = v;
     }
+    wait_vmcnt<0>();  // trailing out-of-range ring loads
+}
+
+int g_cus = 0;
+
+int device_cus()
+{
+    if (g_cus <= 0) {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+            g_cus = n;
+        else
+            g_cus = 256;
+    }
+    return g_cus;
+}
+
+template <int KH, int KW, int BM, int BN, bool RES>
+hipError_t launch_tiles(const ConvArgs &a, hipStream_t s)
+{
+    const long long tiles = (long long)((a.m + BM - 1) / BM) * ((a.oc1 * 32 + BN - 1) / BN);
+    if (tiles <= 0) return hipSuccess;
+    // two persistent workgroups per CU, a multiple of 8 (one share per XCD)
+    long long g = 2LL * device_cus();
+    if (g > tiles) g = (tiles + 7) / 8 * 8;
+    if (g < 8) g = 8;
+    g = g / 8 * 8;
+    if (a.relu)
+        hipLaunchKernelGGL((conv_kernel<KH, KW, BM, BN, RES, true>), dim3((unsigned)g), dim3(kThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL((conv_kernel<KH, KW, BM, BN, RES, false>), dim3((unsigned)g), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
 }
 
 template <int KH, int KW, int BM, int BN>
-hipError_t launch_tiles(const ConvArgs &a, hipStream_t s)
+hipError_t launch_res(const ConvArgs &a, hipStream_t s)
 {
-    const long long tiles_m = (a.m + BM - 1) / BM;
-    const long long tiles_n = (a.oc1 * 32 + BN - 1) / BN;
-    const long long blocks = tiles_m * tiles_n;
-    if (blocks <= 0) return hipSuccess;
-    if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    if (a.residual)
-        hipLaunchKernelGGL((conv_kernel<KH, KW, BM, BN, true>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
-    else
-        hipLaunchKernelGGL((conv_kernel<KH, KW, BM, BN, false>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
-    return hipGetLastError();
+    if (a.residual) return launch_tiles<KH, KW, BM, BN, true>(a, s);
+    return launch_tiles<KH, KW, BM, BN, false>(a, s);
 }
 
 template <int KH, int KW>
 hipError_t launch_k(const ConvArgs &a, hipStream_t s)
 {
-    if (a.oc1 * 32 > 64) return launch_tiles<KH, KW, 128, 128>(a, s);
-    return launch_tiles<KH, KW, 256, 64>(a, s);
+    if (a.oc1 * 32 > 64) return launch_res<KH, KW, 128, 128>(a, s);
+    return launch_res<KH, KW, 256, 64>(a, s);
 }
 
 }  // namespace
