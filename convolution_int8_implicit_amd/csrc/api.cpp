@@ -74,6 +74,7 @@ ifx_status check_desc(const ifx_conv_desc *d, Kind *kind, Dims *dims)
                (kh == 3 && kw == 3 && p == 1 && (s == 1 || s == 2))) {
         if (f & IFX_MAXPOOL) return IFX_E_UNSUPPORTED;
         if ((f & IFX_OUT_I32) && (f & (IFX_RELU | IFX_RESIDUAL))) return IFX_E_UNSUPPORTED;
+        if (d->c_out % 4) return IFX_E_UNSUPPORTED;  // per-channel parameters move in 4-channel words
         k = kGeneric;
     } else {
         return IFX_E_UNSUPPORTED;
@@ -141,6 +142,9 @@ ifx_status run_conv(const ifx_conv_desc *d, Kind kind, const Dims &dm, const int
     a.relu = (d->flags & IFX_RELU) ? 1 : 0;
     a.residual = (d->flags & IFX_RESIDUAL) ? 1 : 0;
     a.out_i32 = (d->flags & IFX_OUT_I32) ? 1 : 0;
+    ifx::fastdiv_magic((unsigned)(dm.ho * dm.wo), &a.howo_mul, &a.howo_shr);
+    ifx::fastdiv_magic((unsigned)dm.wo, &a.wo_mul, &a.wo_shr);
+    ifx::fastdiv_magic((unsigned)a.o2, &a.o2_mul, &a.o2_shr);
     return hip_status(ifx::launch_conv(a, d->kh, d->kw, s));
 }
 

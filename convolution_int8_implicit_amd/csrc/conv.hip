@@ -11,10 +11,11 @@
 // asynchronous shortcut copy).
 //
 // gfx950 design (not the article's A100 tiling):
-//   * persistent 256-thread workgroups (4 wave64s), two per CU; each owns a
-//     list of BM x BN output tiles and streams the flattened sequence of
-//     (tile, K-step) stages through an ST-deep LDS ring, so the loads of the
-//     next tile are in flight while the current tile's epilogue runs;
+//   * persistent workgroups of one wave64 per 64x64 sub-tile, as many per CU
+//     as LDS allows; each owns a list of BM x BN output tiles and streams the
+//     flattened sequence of
+//     (tile, K-step) stages through an ST-deep LDS ring, so the loads of
+//     the next tile are in flight while the current tile's epilogue runs;
 //   * ring stages are filled by direct buffer->LDS 16-byte loads
 //     (buffer_load_dwordx4 ... lds), no register staging; the buffer range
 //     check turns every out-of-image tap, ragged row or padded channel into
@@ -44,8 +45,7 @@ namespace {
 
 typedef ifx_v4i v4i;
 
-constexpr int kThreads = 256;
-constexpr int kStages = 3;
+constexpr int kLdsBytes = 160 * 1024;  // LDS per CU on gfx950
 constexpr unsigned kOOB = 0x80000000u;  // offset past every buffer range: loads return zero
 
 // Buffer resource (gfx9 layout): 48-bit base, stride 0, byte range, raw-buffer config word.
@@ -95,6 +95,12 @@ __device__ __forceinline__ void wave_lds_sync()
     asm volatile("" ::: "memory");
     __builtin_amdgcn_wave_barrier();
     asm volatile("" ::: "memory");
+}
+
+// floor(n / d) for 0 <= n < 2^31 with the host-computed magic of d (mul == 0 means d == 1).
+__device__ __forceinline__ int fdiv(int n, unsigned mul, int shr)
+{
+    return mul == 0 ? n : (int)(__umulhi((unsigned)n, mul) >> shr);
 }
 
 // 16-byte-chunk XOR swizzle of a 64-byte LDS row: conflict-free ds_read_b128
@@ -172,24 +178,34 @@ __device__ __forceinline__ void requant_tile(const v4i (&acc)[4][4], int8_t *rba
         }
 }
 
-template <int BM, int BN>
+// Tile geometry: a BM x BN workgroup tile, one wave per 64x64 sub-tile, and
+// an ST-stage LDS ring.
+template <int BM, int BN, int ST>
 struct ConvCfg {
     static constexpr int WAVES_M = BM / 64;
     static constexpr int WAVES_N = BN / 64;
-    static_assert(WAVES_M * WAVES_N == kThreads / 64, "4 waves per workgroup");
-    static constexpr int AI = BM * 64 / 16 / kThreads;  // A-tile loads per thread per stage
-    static constexpr int BI = BN * 64 / 16 / kThreads;  // B-tile loads per thread per stage
+    static constexpr int WAVES = WAVES_M * WAVES_N;
+    static constexpr int THREADS = 64 * WAVES;
+    static constexpr int AI = BM * 64 / 16 / THREADS;  // A-tile loads per thread per stage
+    static constexpr int BI = BN * 64 / 16 / THREADS;  // B-tile loads per thread per stage
+    static_assert(AI * THREADS * 16 == BM * 64 && BI * THREADS * 16 == BN * 64, "whole 16-byte loads");
     static constexpr int LPS = AI + BI;                 // loads per thread per stage
     static constexpr int STAGE = (BM + BN) * 64;        // bytes per ring stage
-    static constexpr int RI = BM * BN / 16 / kThreads;  // shortcut loads per thread
-    static constexpr int RING = kStages * STAGE;
+    static constexpr int RI = BM * BN / 16 / THREADS;   // shortcut loads per thread
+    static constexpr int RING = ST * STAGE;
     static constexpr int LDS = RING + BM * BN + 3 * 1024;  // ring | staging tile | bias,mult,shift
+    static constexpr int WG_PER_CU = kLdsBytes / LDS > 2 ? 2 : kLdsBytes / LDS;
+    static_assert(WG_PER_CU >= 1, "LDS budget");
+    static_assert(ST >= 2 && (ST - 1) * LPS < 64, "ring depth");
 };
 
-template <int KH, int KW, int BM, int BN, bool RES, bool RELU>
-__global__ __launch_bounds__(kThreads, 2) void conv_kernel(ConvArgs a)
+template <int KH, int KW, int BM, int BN, int ST, bool RES, bool RELU>
+__global__ __launch_bounds__((ConvCfg<BM, BN, ST>::THREADS), (ConvCfg<BM, BN, ST>::WG_PER_CU * ConvCfg<BM, BN, ST>::WAVES / 4))
+void conv_kernel(ConvArgs a)
 {
-    using C = ConvCfg<BM, BN>;
+    using C = ConvCfg<BM, BN, ST>;
+    constexpr int NWV = C::WAVES;
+    constexpr int kStages = ST;
     constexpr int AI = C::AI, BI = C::BI, LPS = C::LPS, STAGE = C::STAGE;
     __shared__ __attribute__((aligned(1024))) int8_t smem[C::LDS];
     int8_t *const R = smem + C::RING;      // [BM][BN] shortcut in, packed output out
@@ -197,7 +213,7 @@ __global__ __launch_bounds__(kThreads, 2) void conv_kernel(ConvArgs a)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS bases stay scalar
     const int wm0 = (wave % C::WAVES_M) * 64;
     const int wn0 = (wave / C::WAVES_M) * 64;
 
@@ -224,64 +240,108 @@ __global__ __launch_bounds__(kThreads, 2) void conv_kernel(ConvArgs a)
 
     auto item_tile = [&](int it, int &m0, int &n0) {
         const long long lin = xb + slot + (long long)it * per;
-        m0 = (int)(lin / tiles_n) * BM;
-        n0 = (int)(lin % tiles_n) * BN;
+        const int li = (int)lin;
+        const int tm_ = li / tiles_n;
+        m0 = tm_ * BM;
+        n0 = (li - tm_ * tiles_n) * BN;
     };
 
     // ---------------- issue cursor: next (tile, K-step) stage to load ----------------
     int is_it = 0, is_ks = 0;
     int s_c1 = 0, s_kx = 0, s_ky = 0, s_kb = 0;  // first block of the step: (ky, kx, c1), flat index
     v4i rsA;
+    // general path (any channel-block count): pieces recombined every step
     unsigned a_img[AI];
     int a_iy[AI], a_ix[AI], a_sel[AI];
     bool a_ok[AI];
     unsigned b_off[BI];
     int b_sel[BI];
     bool b_ok[BI];
+    // even channel-block count: both blocks of a step share the kernel tap, so a
+    // lane's offset is its base plus a uniform per-step delta, and 3x3 padding
+    // is a per-lane mask of valid taps
+    const bool even_i1 = (a.i1 & 1) == 0;
+    unsigned a_base[AI], b_base[BI];
+    unsigned a_mask[AI];
 
     auto plan = [&]() {  // per-lane load plans of tile is_it
         int m0, n0;
         item_tile(is_it, m0, n0);
-        const int img0 = m0 / HoWo;
+        const int img0 = fdiv(m0, a.howo_mul, a.howo_shr);
         rsA = make_rsrc(a.x + (long long)img0 * in_img, in_total - (long long)img0 * in_img);
         // A: instruction j of wave w fills stage rows [(4j+w)*16, +16); lane l -> row (4j+w)*16 + l/4,
         //    physical chunk l%4, which holds logical chunk (l%4) ^ swz(row).
 #pragma unroll
         for (int j = 0; j < AI; ++j) {
-            const int row = (j * 4 + wave) * 16 + (lane >> 2);
+            const int row = (j * NWV + wave) * 16 + (lane >> 2);
             const int lch = (lane & 3) ^ swz(row);
             const int p = m0 + row;
             a_ok[j] = p < a.m;
-            const int pp = a_ok[j] ? p : m0;
-            const int b = pp / HoWo;
+            const int pp = a_ok[j] ? p : m0;  // rows past the end load pixel m0 (result discarded)
+            const int b = fdiv(pp, a.howo_mul, a.howo_shr);
             const int rem = pp - b * HoWo;
-            const int oy = rem / a.wo;
+            const int oy = fdiv(rem, a.wo_mul, a.wo_shr);
             const int ox = rem - oy * a.wo;
             a_iy[j] = oy * a.stride - a.pad;
             a_ix[j] = ox * a.stride - a.pad;
             a_img[j] = (unsigned)((long long)(b - img0) * in_img) + (lch & 1) * 16;
             a_sel[j] = lch >> 1;  // which of the step's two 32-channel blocks
+            a_base[j] = a_img[j] + (unsigned)(a_sel[j] * HW * 32) + (unsigned)((a_iy[j] * a.w + a_ix[j]) * 32);
+            unsigned mask = 0;
+#pragma unroll
+            for (int ky = 0; ky < KH; ++ky)
+#pragma unroll
+                for (int kx = 0; kx < KW; ++kx)
+                    if ((unsigned)(a_iy[j] + ky) < (unsigned)a.h && (unsigned)(a_ix[j] + kx) < (unsigned)a.w)
+                        mask |= 1u << (ky * KW + kx);
+            a_mask[j] = mask;
         }
         // B: instruction j of wave w fills physical rows [(4j+w)*16, +16); within each
         //    64-row group physical row r holds output channel (r%16)*4 + r/16.
 #pragma unroll
         for (int j = 0; j < BI; ++j) {
-            const int prow = (j * 4 + wave) * 16 + (lane >> 2);
+            const int prow = (j * NWV + wave) * 16 + (lane >> 2);
             const int lch = (lane & 3) ^ swz(prow);
             const int o = (prow & ~63) + (prow & 15) * 4 + ((prow & 63) >> 4);
             const int Rw = n0 + o;
             b_ok[j] = Rw < wrows;
             const int RR = b_ok[j] ? Rw : 0;
-            const int o1 = RR / a.o2, o2i = RR - (RR / a.o2) * a.o2;
+            const int o1 = fdiv(RR, a.o2_mul, a.o2_shr), o2i = RR - o1 * a.o2;
             b_off[j] = (unsigned)(((long long)o1 * KH * KW * a.i1 * a.o2 + o2i) * 32) + (lch & 1) * 16;
             b_sel[j] = lch >> 1;
+            b_base[j] = b_off[j] + (unsigned)b_sel[j] * wstride_c1;
         }
         s_c1 = s_kx = s_ky = s_kb = 0;
     };
 
     auto issue = [&](int ring_slot) {
         int8_t *st = smem + ring_slot * STAGE;
-        if (is_it < n_items) {
+        if (is_it < n_items && even_i1) {
+            const int tap = s_ky * KW + s_kx;
+            const unsigned ua = (unsigned)((s_ky * a.w + s_kx) * 32 + s_c1 * HW * 32);
+#pragma unroll
+            for (int j = 0; j < AI; ++j) {
+                unsigned off = a_base[j] + ua;
+                if (KH > 1 || KW > 1) off = ((a_mask[j] >> tap) & 1u) ? off : kOOB;
+                load16_lds(rsA, st + (j * NWV + wave) * 1024, off);
+            }
+            const unsigned ub = (unsigned)(tap * a.i1 + s_c1) * wstride_c1;
+#pragma unroll
+            for (int j = 0; j < BI; ++j) load16_lds(rsB, st + BM * 64 + (j * NWV + wave) * 1024, b_base[j] + ub);
+            s_kb += 2;
+            s_c1 += 2;
+            if (s_c1 >= a.i1) {
+                s_c1 = 0;
+                if (++s_kx == KW) {
+                    s_kx = 0;
+                    ++s_ky;
+                }
+            }
+            if (++is_ks == nsteps) {
+                is_ks = 0;
+                if (++is_it < n_items) plan();
+            }
+        } else if (is_it < n_items) {
             int c1b = s_c1 + 1, kxb = s_kx, kyb = s_ky;  // the step's second block
             if (c1b == a.i1) {
                 c1b = 0;
@@ -301,7 +361,7 @@ __global__ __launch_bounds__(kThreads, 2) void conv_kernel(ConvArgs a)
                 if (KH > 1) ok = ok && (unsigned)iy < (unsigned)a.h;
                 if (KW > 1) ok = ok && (unsigned)ix < (unsigned)a.w;
                 const unsigned off = ok ? a_img[j] + (unsigned)(((c1 * a.h + iy) * a.w + ix) * 32) : kOOB;
-                load16_lds(rsA, st + (j * 4 + wave) * 1024, off);
+                load16_lds(rsA, st + (j * NWV + wave) * 1024, off);
             }
 #pragma unroll
             for (int j = 0; j < BI; ++j) {
@@ -311,7 +371,7 @@ __global__ __launch_bounds__(kThreads, 2) void conv_kernel(ConvArgs a)
                 const int ky = sel ? kyb : s_ky;
                 const bool ok = b_ok[j] && (s_kb + sel) < a.nkb;
                 const unsigned off = ok ? b_off[j] + (unsigned)((ky * KW + kx) * a.i1 + c1) * wstride_c1 : kOOB;
-                load16_lds(rsB, st + BM * 64 + (j * 4 + wave) * 1024, off);
+                load16_lds(rsB, st + BM * 64 + (j * NWV + wave) * 1024, off);
             }
             s_kb += 2;
             s_c1 += 2;
@@ -329,9 +389,9 @@ __global__ __launch_bounds__(kThreads, 2) void conv_kernel(ConvArgs a)
         } else {
             // past the last tile: same number of loads, all out of range (they write zeros)
 #pragma unroll
-            for (int j = 0; j < AI; ++j) load16_lds(rsB, st + (j * 4 + wave) * 1024, kOOB);
+            for (int j = 0; j < AI; ++j) load16_lds(rsB, st + (j * NWV + wave) * 1024, kOOB);
 #pragma unroll
-            for (int j = 0; j < BI; ++j) load16_lds(rsB, st + BM * 64 + (j * 4 + wave) * 1024, kOOB);
+            for (int j = 0; j < BI; ++j) load16_lds(rsB, st + BM * 64 + (j * NWV + wave) * 1024, kOOB);
         }
     };
 
@@ -347,21 +407,21 @@ __global__ __launch_bounds__(kThreads, 2) void conv_kernel(ConvArgs a)
             }
         }
         if (RES) {
-            const int img0 = m0 / HoWo;
+            const int img0 = fdiv(m0, a.howo_mul, a.howo_shr);
             const v4i rsR = make_rsrc(a.res + (long long)img0 * out_img, (long long)(a.n - img0) * out_img);
             constexpr int CPR = BN / 16;  // 16-byte chunks per staged row
 #pragma unroll
             for (int j = 0; j < C::RI; ++j) {
-                const int q = (j * 4 + wave) * 64 + lane;  // 16-byte slot of R
+                const int q = (j * NWV + wave) * 64 + lane;  // 16-byte slot of R
                 const int row = q / CPR, ch = q % CPR;
                 const int p = m0 + row;
                 const int oc = n0 + ch * 16;
                 unsigned off = kOOB;
                 if (p < a.m && oc < a.oc1 * 32) {
-                    const int b = p / HoWo, hw = p - (p / HoWo) * HoWo;
+                    const int b = fdiv(p, a.howo_mul, a.howo_shr), hw = p - b * HoWo;
                     off = (unsigned)((((long long)(b - img0) * a.oc1 + (oc >> 5)) * HoWo + hw) * 32 + (oc & 31));
                 }
-                load16_lds(rsR, R + (j * 4 + wave) * 1024, off);
+                load16_lds(rsR, R + (j * NWV + wave) * 1024, off);
             }
         }
     };
@@ -378,8 +438,14 @@ __global__ __launch_bounds__(kThreads, 2) void conv_kernel(ConvArgs a)
             wait_vmcnt<0>();
         else if (later == 1)
             wait_vmcnt<LPS>();
-        else
+        else if (later == 2 || ST <= 3)
             wait_vmcnt<2 * LPS>();
+        else if (later == 3 || ST <= 4)
+            wait_vmcnt<(ST > 3 ? 3 : 2) * LPS>();
+        else if (later == 4 || ST <= 5)
+            wait_vmcnt<(ST > 4 ? 4 : 2) * LPS>();
+        else
+            wait_vmcnt<(ST > 5 ? 5 : 2) * LPS>();
         ring_barrier();
 
         const int ocl = n0 + wn0 + 4 * c;  // first of this lane's four output channels
@@ -435,7 +501,7 @@ __global__ __launch_bounds__(kThreads, 2) void conv_kernel(ConvArgs a)
         const int k = lane & 3;
         const int och = n0 + wn0 + 16 * k;  // first channel of this lane's chunk
         if (och >= a.oc1 * 32) return;
-        const int b0 = pbase / HoWo;
+        const int b0 = fdiv(pbase, a.howo_mul, a.howo_shr);
         const int hw0 = pbase - b0 * HoWo;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -512,35 +578,37 @@ int device_cus()
     return g_cus;
 }
 
-template <int KH, int KW, int BM, int BN, bool RES>
+template <int KH, int KW, int BM, int BN, int ST, bool RES>
 hipError_t launch_tiles(const ConvArgs &a, hipStream_t s)
 {
+    using C = ConvCfg<BM, BN, ST>;
     const long long tiles = (long long)((a.m + BM - 1) / BM) * ((a.oc1 * 32 + BN - 1) / BN);
     if (tiles <= 0) return hipSuccess;
-    // two persistent workgroups per CU, a multiple of 8 (one share per XCD)
-    long long g = 2LL * device_cus();
+    // as many persistent workgroups as fit on the chip, a multiple of 8 (one share per XCD)
+    long long g = (long long)C::WG_PER_CU * device_cus();
     if (g > tiles) g = (tiles + 7) / 8 * 8;
-    if (g < 8) g = 8;
     g = g / 8 * 8;
+    if (g < 8) g = 8;
     if (a.relu)
-        hipLaunchKernelGGL((conv_kernel<KH, KW, BM, BN, RES, true>), dim3((unsigned)g), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((conv_kernel<KH, KW, BM, BN, ST, RES, true>), dim3((unsigned)g), dim3(C::THREADS), 0, s, a);
     else
-        hipLaunchKernelGGL((conv_kernel<KH, KW, BM, BN, RES, false>), dim3((unsigned)g), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((conv_kernel<KH, KW, BM, BN, ST, RES, false>), dim3((unsigned)g), dim3(C::THREADS), 0, s,
+                           a);
     return hipGetLastError();
 }
 
-template <int KH, int KW, int BM, int BN>
+template <int KH, int KW, int BM, int BN, int ST>
 hipError_t launch_res(const ConvArgs &a, hipStream_t s)
 {
-    if (a.residual) return launch_tiles<KH, KW, BM, BN, true>(a, s);
-    return launch_tiles<KH, KW, BM, BN, false>(a, s);
+    if (a.residual) return launch_tiles<KH, KW, BM, BN, ST, true>(a, s);
+    return launch_tiles<KH, KW, BM, BN, ST, false>(a, s);
 }
 
 template <int KH, int KW>
 hipError_t launch_k(const ConvArgs &a, hipStream_t s)
 {
-    if (a.oc1 * 32 > 64) return launch_res<KH, KW, 128, 128>(a, s);
-    return launch_res<KH, KW, 256, 64>(a, s);
+    if (a.oc1 * 32 > 64) return launch_res<KH, KW, 128, 128, 3>(a, s);
+    return launch_res<KH, KW, 256, 64, 3>(a, s);
 }
 
 }  // namespace

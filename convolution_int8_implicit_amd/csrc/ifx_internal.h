@@ -23,7 +23,28 @@ struct ConvArgs {
     int m;                 // n * ho * wo (GEMM rows)
     int nkb;               // kh * kw * i1 (32-wide reduction blocks)
     int relu, residual, out_i32;
+    // magic numbers for exact unsigned division of n < 2^31 by ho*wo, wo, o2
+    // (q = n when d == 1, else umulhi(n, mul) >> shr); see fastdiv_magic()
+    unsigned howo_mul, wo_mul, o2_mul;
+    int howo_shr, wo_shr, o2_shr;
 };
+
+// Magic multiplier and shift for q = floor(n / d), 0 <= n < 2^31, d >= 1:
+// with p = 31 + ceil(log2 d) and m = ceil(2^p / d), floor(n * m / 2^p) = floor(n / d)
+// (the classic round-up method for dividing by an invariant integer; m < 2^32).
+inline void fastdiv_magic(unsigned d, unsigned *mul, int *shr)
+{
+    if (d <= 1) {
+        *mul = 0;
+        *shr = 0;
+        return;
+    }
+    int l = 0;
+    while ((1ull << l) < d) ++l;
+    const int p = 31 + l;
+    *mul = (unsigned)(((1ull << p) + d - 1) / d);
+    *shr = p - 32;
+}
 
 // Arguments of the fused stem (7x7/s2/p3 conv + ReLU + 3x3/s2/p1 max-pool).
 struct StemArgs {

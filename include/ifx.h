@@ -80,7 +80,7 @@ enum {
 /*
  * One convolution.  Supported (kh, kw, stride, pad):
  *   (1,1,1,0) (1,1,2,0) (3,3,1,1) (3,3,2,1)  flags: any of RELU|RESIDUAL, or
- *                                            OUT_I32 alone
+ *                                            OUT_I32 alone; c_out a multiple of 4
  *   (7,7,2,3) with IFX_MAXPOOL (RELU optional), c_in <= 4
  * n, h, w, c_in, c_out > 0; the output size must be positive.
  */
