@@ -5,8 +5,8 @@
 
 Default workload: the ResNet-50-shaped int8 backbone + average pool + int8 FC
 at batch 2048 on 224x224x3 images (synthetic, seeded).  One step is the whole
-hot path over the batch: NHWC -> NC/32HW32 input pack, fused stem
-(conv 7x7/s2 + BN + ReLU + max-pool), 16 bottlenecks of fused convolutions
+hot path over the batch: fused stem reading the NHWC int8 images directly
+(conv 7x7/s2 + BN + ReLU + max-pool, written as NC/32HW32), 16 bottlenecks of fused convolutions
 (BN + requant + shortcut + ReLU in the epilogue), average pool and FC to int32
 logits.  Weights are packed once beforehand (offline reblocking).
 
@@ -135,6 +135,8 @@ def main():
     ap.add_argument("--workload", default="net", choices=["net", "conv1x1", "conv1x1_b1", "block", "stem"])
     ap.add_argument("--sub-batch", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--packed-input", action="store_true",
+                    help="feed the stem a packed NC/32HW32 input made by a separate pack kernel in the step")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (data-parallel sharding over the "
@@ -156,26 +158,35 @@ def main():
     if args.workload == "net":
         wl = synth.workload(4)
         n = wl.n
-        net = model.DeviceNet(wl.net, wl.index, sub_batch=sub_batch)
+        net = model.DeviceNet(wl.net, wl.index, sub_batch=sub_batch, nhwc_input=not args.packed_input)
         x_nhwc = synth.input_tensor(wl, device="cuda")
-        x_blk = model.empty_act(n, 224, 224, 3)
         ws = torch.empty(net.workspace_bytes(n), dtype=torch.int8, device="cuda")
         logits = torch.empty((n, wl.net.fc_out), dtype=torch.int32, device="cuda")
+        if args.packed_input:
+            x_blk = model.empty_act(n, 224, 224, 3)
 
-        def step():
-            ifx.pack_act(x_nhwc, out=x_blk, stream=stream)
-            net.forward(x_blk, logits, n, ws, stream)
+            def step():
+                ifx.pack_act(x_nhwc, out=x_blk, stream=stream)
+                net.forward(x_blk, logits, n, ws, stream)
+        else:
+            x_blk = x_nhwc
+
+            def step():
+                net.forward(x_nhwc, logits, n, ws, stream)
         layers = net_layers(wl.net, n)
         total_ops = sum(layer_work(s, nn, h, w)[0] for s, nn, h, w in layers) + 2 * n * wl.net.fc_in * wl.net.fc_out
         config = {"workload": wl.name, "batch": n, "image": "224x224x3 int8 NHWC", "convs": 53,
                   "head": "avgpool + FC 2048->1000 int32 logits", "sub_batch": sub_batch,
-                  "step": "input pack + ifx_net_forward"}
+                  "step": ("input pack + " if args.packed_input else "") + "ifx_net_forward"}
     else:
         idx = {"conv1x1": 1, "conv1x1_b1": 0, "block": 2, "stem": 3}[args.workload]
         wl = synth.workload(idx)
         n = wl.n
         dcs = [model.device_conv(s, wl.index, n, wl.h, wl.w) if i == 0 else None for i, s in enumerate(wl.convs)]
         x_blk = ifx.pack_act(synth.input_tensor(wl, device="cuda"))
+        if wl.convs[0].k == 7 and not args.packed_input:
+            dcs[0].desc.flags |= ifx.INPUT_NHWC
+            x_blk = synth.input_tensor(wl, device="cuda")
         if wl.kind == "block":
             dcs = [model.device_conv(s, wl.index, n, 28, 28) for s in wl.convs]
             blk = model.DeviceBlock(dcs, None)

@@ -21,13 +21,13 @@ from typing import Optional, Sequence
 import torch
 
 __all__ = [
-    "RELU", "RESIDUAL", "MAXPOOL", "OUT_I32", "IfxError", "ConvDesc", "BlockParams", "NetParams", "lib",
+    "RELU", "RESIDUAL", "MAXPOOL", "OUT_I32", "INPUT_NHWC", "IfxError", "ConvDesc", "BlockParams", "NetParams", "lib",
     "conv_desc", "conv_validate", "conv_out_dims", "act_bytes", "wpack_bytes", "pack_act", "unpack_act",
     "pack_weights", "conv_fused", "block_workspace_bytes", "block_forward", "net_workspace_bytes",
     "net_forward", "status_string", "last_hip_error", "version", "LIB_PATH",
 ]
 
-RELU, RESIDUAL, MAXPOOL, OUT_I32 = 1, 2, 4, 8
+RELU, RESIDUAL, MAXPOOL, OUT_I32, INPUT_NHWC = 1, 2, 4, 8, 16
 STATUS = {0: "IFX_OK", 1: "IFX_E_NULL", 2: "IFX_E_SHAPE", 3: "IFX_E_UNSUPPORTED", 4: "IFX_E_ALIGN",
           5: "IFX_E_WORKSPACE", 6: "IFX_E_HIP"}
 

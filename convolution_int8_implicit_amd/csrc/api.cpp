@@ -54,7 +54,8 @@ ifx_status check_desc(const ifx_conv_desc *d, Kind *kind, Dims *dims)
         d->stride <= 0 || d->pad < 0)
         return IFX_E_SHAPE;
     const uint32_t f = d->flags;
-    if (f & ~(uint32_t)(IFX_RELU | IFX_RESIDUAL | IFX_MAXPOOL | IFX_OUT_I32)) return IFX_E_UNSUPPORTED;
+    if (f & ~(uint32_t)(IFX_RELU | IFX_RESIDUAL | IFX_MAXPOOL | IFX_OUT_I32 | IFX_INPUT_NHWC))
+        return IFX_E_UNSUPPORTED;
     Dims dm;
     dm.ho = out_dim(d->h, d->kh, d->stride, d->pad);
     dm.wo = out_dim(d->w, d->kw, d->stride, d->pad);
@@ -72,7 +73,7 @@ ifx_status check_desc(const ifx_conv_desc *d, Kind *kind, Dims *dims)
         k = kStem;
     } else if ((kh == 1 && kw == 1 && p == 0 && (s == 1 || s == 2)) ||
                (kh == 3 && kw == 3 && p == 1 && (s == 1 || s == 2))) {
-        if (f & IFX_MAXPOOL) return IFX_E_UNSUPPORTED;
+        if (f & (IFX_MAXPOOL | IFX_INPUT_NHWC)) return IFX_E_UNSUPPORTED;
         if ((f & IFX_OUT_I32) && (f & (IFX_RELU | IFX_RESIDUAL))) return IFX_E_UNSUPPORTED;
         if (d->c_out % 4) return IFX_E_UNSUPPORTED;  // per-channel parameters move in 4-channel words
         k = kGeneric;
@@ -111,6 +112,8 @@ ifx_status run_conv(const ifx_conv_desc *d, Kind kind, const Dims &dm, const int
         a.n = d->n;
         a.h = d->h;
         a.w = d->w;
+        a.c = d->c_in;
+        a.nhwc = (d->flags & IFX_INPUT_NHWC) ? 1 : 0;
         a.ho = dm.ho;
         a.wo = dm.wo;
         a.ph = dm.oh;
@@ -423,7 +426,9 @@ ifx_status ifx_net_forward(const ifx_net_params *p, const int8_t *x_blk, int32_t
     int8_t *act[2] = {base, base + plan.act};
     int8_t *bws = base + 2 * plan.act;  // t1 | t2 | sc of the current block
     int8_t *pool = bws + plan.t1 + plan.t2 + plan.sc;
-    const size_t in_img = act_bytes(1, p->stem.h, p->stem.w, p->stem.c_in);
+    const size_t in_img = (p->stem.flags & IFX_INPUT_NHWC)
+                              ? (size_t)p->stem.h * p->stem.w * p->stem.c_in
+                              : act_bytes(1, p->stem.h, p->stem.w, p->stem.c_in);
 
     for (int i0 = 0; i0 < n; i0 += plan.nb) {
         const int nb = std::min(plan.nb, n - i0);

@@ -48,11 +48,12 @@ inline void fastdiv_magic(unsigned d, unsigned *mul, int *shr)
 
 // Arguments of the fused stem (7x7/s2/p3 conv + ReLU + 3x3/s2/p1 max-pool).
 struct StemArgs {
-    const int8_t *x;       // packed input [n, 1, h, w, 32] (channels 0..3 used)
+    const int8_t *x;       // packed input [n, 1, h, w, 32], or compact NHWC [n, h, w, c] when nhwc
     const int8_t *wt;      // stem weights [oc=64, 8, 8, 4]
     const int32_t *bias, *mult, *shift;
     int8_t *y;             // packed pooled output [n, 2, ph, pw, 32]
-    int n, h, w;           // input
+    int n, h, w, c;        // input (c <= 4)
+    int nhwc;              // input layout: 0 packed, 1 compact NHWC
     int ho, wo;            // conv output
     int ph, pw;            // pooled output
     int relu;

@@ -16,7 +16,7 @@ import torch
 # Images per pass of ifx_net_forward used by the benchmark (0 = whole batch).
 DEFAULT_SUB_BATCH = 0
 
-from . import (BlockParams, ConvDesc, NetParams, block_forward, block_workspace_bytes, conv_desc, conv_fused,
+from . import (INPUT_NHWC, BlockParams, ConvDesc, NetParams, block_forward, block_workspace_bytes, conv_desc, conv_fused,
                conv_out_dims, net_forward, net_workspace_bytes, pack_act, pack_weights, synth)
 
 
@@ -80,13 +80,20 @@ def device_block(bs: synth.BlockSpec, seed: int, n: int, h: int, w: int, device=
 
 
 class DeviceNet:
-    """The ResNet-50-shaped network as one ifx_net_params (weights for batch-independent use)."""
+    """The ResNet-50-shaped network as one ifx_net_params (weights for batch-independent use).
+
+    nhwc_input: forward() takes the compact NHWC image [n, h, w, c] and the stem
+    reads it directly; otherwise it takes the packed [n, 1, h, w, 32] tensor.
+    """
 
     def __init__(self, spec: synth.NetSpec, seed: int, h: int = 224, w: int = 224, device="cuda",
-                 sub_batch: int = 0):
+                 sub_batch: int = 0, nhwc_input: bool = False):
         self.spec = spec
         self.seed = seed
+        self.nhwc_input = nhwc_input
         self.stem = device_conv(spec.stem, seed, 1, h, w, device)
+        if nhwc_input:
+            self.stem.desc.flags |= INPUT_NHWC
         hh, ww = self.stem.out_hw
         self.blocks: List[DeviceBlock] = []
         for bs in spec.blocks:
@@ -119,8 +126,8 @@ class DeviceNet:
     def workspace_bytes(self, n: int) -> int:
         return net_workspace_bytes(self.params, n)
 
-    def forward(self, x_blk, logits, n, ws, stream=None):
-        net_forward(self.params, x_blk, logits, n, ws, stream)
+    def forward(self, x, logits, n, ws, stream=None):
+        net_forward(self.params, x, logits, n, ws, stream)
 
 
 def pack_input(x_nhwc: torch.Tensor, stream=None) -> torch.Tensor:

@@ -74,14 +74,17 @@ enum {
     IFX_RELU = 1u,     /* ReLU before saturation */
     IFX_RESIDUAL = 2u, /* add the shortcut tensor before ReLU */
     IFX_MAXPOOL = 4u,  /* fused 3x3/s2/p1 max-pool after ReLU (7x7/s2/p3 stem only) */
-    IFX_OUT_I32 = 8u   /* write int32 acc + bias, NHWC, no requantisation */
+    IFX_OUT_I32 = 8u,  /* write int32 acc + bias, NHWC, no requantisation */
+    IFX_INPUT_NHWC = 16u /* stem only: the input is the compact NHWC image [n, h, w, c_in]
+                            int8 instead of the packed layout (the input pack is folded
+                            into the stem's loads) */
 };
 
 /*
  * One convolution.  Supported (kh, kw, stride, pad):
  *   (1,1,1,0) (1,1,2,0) (3,3,1,1) (3,3,2,1)  flags: any of RELU|RESIDUAL, or
  *                                            OUT_I32 alone; c_out a multiple of 4
- *   (7,7,2,3) with IFX_MAXPOOL (RELU optional), c_in <= 4
+ *   (7,7,2,3) with IFX_MAXPOOL (RELU, INPUT_NHWC optional), c_in <= 4
  * n, h, w, c_in, c_out > 0; the output size must be positive.
  */
 typedef struct {
@@ -125,7 +128,8 @@ ifx_status ifx_pack_weights(const ifx_conv_desc *d, const int8_t *w_ohwi, int8_t
  * One fused convolution (Inspur conv-merge article sections 3.3-3.4; DiDi
  * IFX blog inference section): implicit-GEMM int8 convolution with int32
  * accumulation followed by the fused epilogue above.
- *   x_blk      packed input [n, ceil(c_in/32), h, w, 32]
+ *   x_blk      packed input [n, ceil(c_in/32), h, w, 32], or the compact
+ *              [n, h, w, c_in] image for a stem with IFX_INPUT_NHWC
  *   w_blk      packed weights of d (ifx_pack_weights)
  *   bias, mult, shift   int32 [c_out]
  *   residual   packed [n, ceil(c_out/32), ho, wo, 32] when IFX_RESIDUAL, else NULL
@@ -172,7 +176,9 @@ ifx_status ifx_block_forward(const ifx_block_params *p, const int8_t *x_blk, int
  * c_out = fc_out).  sub_batch > 0 runs the network over consecutive groups
  * of sub_batch images (results are identical for every sub_batch); 0 runs
  * the whole batch at once.
- *   x_blk   packed input [n, ceil(stem.c_in/32), stem.h, stem.w, 32]
+ *   x_blk   packed input [n, ceil(stem.c_in/32), stem.h, stem.w, 32], or the
+ *           compact [n, stem.h, stem.w, stem.c_in] image when stem.flags has
+ *           IFX_INPUT_NHWC
  *   logits  int32 [n, fc_out]
  */
 typedef struct {

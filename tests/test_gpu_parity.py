@@ -58,7 +58,7 @@ def gpu_conv(ifx, x, w, bias, mult, shift, k, s, p, flags, residual=None, check_
     n, h, wd, c = x.shape
     oc = w.shape[0]
     d = ifx.conv_desc(n, h, wd, c, oc, k, k, s, p, flags)
-    xb = ifx.pack_act(cu(x))
+    xb = cu(x) if flags & ifx.INPUT_NHWC else ifx.pack_act(cu(x))
     wb = ifx.pack_weights(d, cu(w))
     ho, wo = ifx.conv_out_dims(d)
     rb = ifx.pack_act(cu(residual)) if residual is not None else None
@@ -242,6 +242,21 @@ def test_stem(ifx, orc, n, h, w, c):
     bias, mult, shift = params(rng, 64)
     for flags in (ifx.RELU | ifx.MAXPOOL, ifx.MAXPOOL):
         got = gpu_conv(ifx, x, wt, bias, mult, shift, 7, 2, 3, flags)
+        np.testing.assert_array_equal(got, orc.conv_fused(x, wt, bias, mult, shift, 2, 3, flags))
+
+
+@pytest.mark.parametrize("n,h,w,c", [(2, 224, 224, 3), (1, 37, 45, 3), (2, 40, 44, 3), (1, 9, 12, 3),
+                                     (3, 16, 16, 4), (1, 2, 3, 1), (2, 30, 28, 2)])
+def test_stem_nhwc_input(ifx, orc, n, h, w, c):
+    """The stem reading the compact NHWC image (aligned 3-channel path when
+    w % 4 == 0, byte path otherwise) gives the packed-input stem's result."""
+    note(f"stem nhwc n={n} h={h} w={w} c={c}")
+    rng = np.random.default_rng(7 * h + w + c)
+    x = rand(rng, (n, h, w, c), -128, 127)
+    wt = rand(rng, (64, 7, 7, c), -127, 127)
+    bias, mult, shift = params(rng, 64)
+    for flags in (ifx.RELU | ifx.MAXPOOL, ifx.MAXPOOL):
+        got = gpu_conv(ifx, x, wt, bias, mult, shift, 7, 2, 3, flags | ifx.INPUT_NHWC)
         np.testing.assert_array_equal(got, orc.conv_fused(x, wt, bias, mult, shift, 2, 3, flags))
 
 

@@ -111,6 +111,14 @@ def test_workload3_stem_sampled(ifx, orc):
     cp = oracle_conv(orc, synth, spec, wl.index)
     exp = orc.conv_layer(synth.input_tensor(wl, rows=rows).numpy(), cp, spec.flags)
     np.testing.assert_array_equal(got, exp)
+    # the same layer reading the compact NHWC image gives the same whole tensor
+    note(wl.name + " nhwc input")
+    dn = model.device_conv(spec, wl.index, wl.n, wl.h, wl.w)
+    dn.desc.flags |= ifx.INPUT_NHWC
+    y2 = model.empty_act(wl.n, 56, 56, 64)
+    dn.run(synth.input_tensor(wl, device="cuda"), y2)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
 
 
 def _oracle_net(orc, synth, wl, rows):
@@ -153,3 +161,13 @@ def test_workload4_net_sampled_and_sub_batch_invariant(ifx, orc):
         torch.cuda.synchronize()
         assert torch.equal(l2, logits)
         del ws2
+    # the network fed the compact NHWC image (stem reads it directly)
+    for sb in (0, 160):
+        note(f"nhwc input, sub_batch {sb}")
+        nn_ = model.DeviceNet(wl.net, wl.index, sub_batch=sb, nhwc_input=True)
+        ws3 = torch.empty(nn_.workspace_bytes(wl.n), dtype=torch.int8, device="cuda")
+        l3 = torch.empty_like(logits)
+        nn_.forward(synth.input_tensor(wl, device="cuda"), l3, wl.n, ws3)
+        torch.cuda.synchronize()
+        assert torch.equal(l3, logits)
+        del ws3, nn_
