@@ -31,13 +31,101 @@ RIDGE = PEAK_I8 / PEAK_HBM
 METRIC = "int8 TOPS + images/s (fused conv stack), % of int8 MFMA peak / HBM BW"
 
 
-def kernel_name(spec) -> str:
-    """Name of the library kernel instance a conv layer dispatches to (mirrors the host dispatch)."""
+def kernel_name(spec, nhwc_input=True) -> str:
+    """The kernel template instance a conv layer dispatches to, spelled as rocprofv3
+    prints it (mirrors the library's host dispatch)."""
     if spec.k == 7:
-        return "stem_kernel"
+        return f"stem_kernel<{1 if nhwc_input else 0}>"
     oc_pad = (spec.c_out + 31) // 32 * 32
     bm, bn = (128, 128) if oc_pad > 64 else (256, 64)
-    return f"conv_kernel<{spec.k},{spec.k},{bm},{bn}>"
+    res = "true" if spec.flags & 2 else "false"
+    relu = "true" if spec.flags & 1 else "false"
+    return f"conv_kernel<{spec.k}, {spec.k}, {bm}, {bn}, 3, {res}, {relu}>"
+
+
+# Sources each kernel family is built from: HBM traffic taken from counters is only
+# reported while these files are unchanged.
+KERNEL_SOURCES = {
+    "conv_kernel": ["conv.hip", "device_common.h", "ifx_internal.h"],
+    "stem_kernel": ["stem.hip", "device_common.h", "ifx_internal.h"],
+}
+
+
+def source_digest(kernel: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel.split("<")[0]]:
+        with open(os.path.join(ROOT, "convolution_int8_implicit_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def profiled_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary of this
+    workload (profiles/hbm_traffic_<workload>.txt), or None when there is none or
+    the kernel's sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        for line in fh:
+            if not line.startswith("kernel: "):
+                continue
+            fields = dict(kv.split("=", 1) for kv in line.strip()[len("kernel: "):].split(" | ")[1:])
+            name = line[len("kernel: "):].split(" | ")[0].strip()
+            if name == kernel and fields.get("digest") == source_digest(kernel):
+                return int(fields["hbm_bytes_per_launch"])
+    return None
+
+
+def summarize_pmc(fetch_csv: str, write_csv: str, calib_bytes: int, out: str, workload: str, note: str):
+    """Turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, WRITE_SIZE;
+    KiB per dispatch) into per-launch HBM bytes per kernel instance, scaled by what the
+    same counters read for a plain copy of calib_bytes (torch bitwise_not, int32)."""
+    import csv
+    import re
+    from collections import defaultdict
+
+    def short(name):
+        m = re.search(r"((?:conv|stem)_kernel<[^>]*>)", name)
+        if m:
+            return m.group(1)
+        return "copy" if "bitwise_not" in name else None
+
+    def read(path, counter):
+        per = defaultdict(list)
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                k = short(r["Kernel_Name"])
+                if k:
+                    per[k].append((int(r["Dispatch_Id"]), float(r["Counter_Value"]) * 1024.0))
+        # the calibration copies are the process's last three bitwise_not dispatches
+        per["copy"] = sorted(per["copy"])[-3:]
+        return {k: [v for _, v in sorted(lst)] for k, lst in per.items()}
+
+    fe, wr = read(fetch_csv, "FETCH_SIZE"), read(write_csv, "WRITE_SIZE")
+    med = lambda v: sorted(v)[len(v) // 2]
+    cf, cw = med(fe["copy"]), med(wr["copy"])
+    fs, ws = calib_bytes / cf, calib_bytes / cw
+    lines = [f"# HBM traffic per dispatch, workload {workload}, from rocprofv3 counters",
+             "# FETCH_SIZE and WRITE_SIZE (KiB per dispatch) from two separate --pmc runs, each",
+             "# scaled by what the counter reads for a plain copy kernel of known size run in the",
+             "# same process (torch bitwise_not over int32: reads and writes calib_bytes).", f"# {note}",
+             f"copy_calibration: calib_bytes={calib_bytes} | fetch_read={cf:.0f} | write_read={cw:.0f} | "
+             f"fetch_scale={fs:.4f} | write_scale={ws:.4f}"]
+    for k in sorted(set(fe) & set(wr)):
+        if k == "copy":
+            continue
+        f_avg = sum(fe[k]) / len(fe[k]) * fs
+        w_avg = sum(wr[k]) / len(wr[k]) * ws
+        lines.append(f"kernel: {k} | digest={source_digest(k)} | dispatches={len(fe[k])} | "
+                     f"fetch_bytes_per_launch={f_avg:.0f} | write_bytes_per_launch={w_avg:.0f} | "
+                     f"hbm_bytes_per_launch={f_avg + w_avg:.0f}")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def layer_work(spec, n, h, w):
@@ -135,9 +223,18 @@ def main():
     ap.add_argument("--workload", default="net", choices=["net", "conv1x1", "conv1x1_b1", "block", "stem"])
     ap.add_argument("--sub-batch", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after the run, copy this many MiB with a plain elementwise kernel (counter calibration)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/hbm_traffic_<workload>.txt from two counter runs and exit")
+    ap.add_argument("--note", default="", help="command lines recorded in the --summarize-pmc output")
     ap.add_argument("--packed-input", action="store_true",
                     help="feed the stem a packed NC/32HW32 input made by a separate pack kernel in the step")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.copy_calibration_mib << 20,
+                      os.path.join(ROOT, "profiles", f"hbm_traffic_{args.workload}.txt"), args.workload, args.note)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (data-parallel sharding over the "
               "batch is described in DESIGN.md); run with --gpus 1.", file=sys.stderr)
@@ -294,7 +391,7 @@ def main():
     torch.cuda.synchronize()
     per_kernel = {}
     for spec, h, w, a, b in evs:
-        name = kernel_name(spec)
+        name = kernel_name(spec, not args.packed_input)
         ops, byts, _, _ = layer_work(spec, nb, h, w)
         d = per_kernel.setdefault(name, {"time": 0.0, "ops": 0, "bytes": 0, "launches": 0})
         d["time"] += a.elapsed_time(b) * 1e-3
@@ -311,7 +408,10 @@ def main():
         achieved = dom["bytes"] / dom["launches"] / avg_t / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
     roof["frac"] = round(achieved / roof["peak"], 4)
-    roof["traffic"] = None
+    traffic = profiled_traffic(dom_name, args.workload)
+    roof["traffic"] = None if traffic is None else round(traffic / avg_t / 1e9, 1)
+    roof["traffic_unit"] = "GB/s of HBM bytes (counters) per launch time"
+    roof["traffic_bytes_per_launch"] = traffic
     roof["kernel"] = dom_name
     roof["launches_per_step"] = dom["launches"] // reps * passes
     roof["avg_launch_us"] = round(avg_t * 1e6, 2)
@@ -340,6 +440,14 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.workload)
     print(json.dumps(line), flush=True)
+    if args.copy_calibration_mib:
+        nb = args.copy_calibration_mib << 20
+        src = torch.randint(-2 ** 31, 2 ** 31 - 1, (nb // 4,), dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            torch.bitwise_not(src, out=dst)
+        torch.cuda.synchronize()
 
 
 if __name__ == "__main__":
