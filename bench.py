@@ -236,8 +236,8 @@ def main():
                       os.path.join(ROOT, "profiles", f"hbm_traffic_{args.workload}.txt"), args.workload, args.note)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (data-parallel sharding over the "
-              "batch is described in DESIGN.md); run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path (images are independent, so a "
+              "batch shards over GPUs with no exchange step); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch

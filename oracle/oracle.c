@@ -19,7 +19,7 @@
  *    (极致推理优化): CONV+BN+RELU and CONV+BN+RELU+MAXPOOL as single
  *    fused functions.
  *
- * Readings where the pages are silent (each is listed in the design doc):
+ * Readings where the pages are silent:
  *  - BN is folded into an int32 bias plus a per-output-channel fixed-point
  *    scale mult * 2^-(31+shift), mult in [0, 2^31), shift in [0, 31].
  *  - One rounding, half away from zero, of (acc + bias) * mult / 2^(31+shift).

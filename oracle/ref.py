@@ -12,9 +12,10 @@ ResNet-50-shaped network exactly as the pages describe:
     Conv2+BN+ReLU, Conv3+BN, then Sum with the block input, then ReLU.
   * DiDi IFX DAWNBench blog, inference section: the stem is one fused
     CONV+BN+RELU+MAXPOOL.
-Readings the pages leave open (stride on the 3x3 and on the projection, no
-ReLU on the projection, integer average pool and FC head) are listed in
-DESIGN.md.
+Readings where the pages are silent: the stride of a downsampling block sits
+on its 3x3 conv and on the projection; the projection has no ReLU; the head is
+an integer average pool (mean rounded half away from zero) and an int8 FC with
+int32 logits.
 """
 from __future__ import annotations
 
