@@ -40,6 +40,9 @@ def kernel_name(spec, nhwc_input=True) -> str:
     bm, bn = (128, 128) if oc_pad > 64 else (256, 64)
     res = "true" if spec.flags & 2 else "false"
     relu = "true" if spec.flags & 1 else "false"
+    i1 = (spec.c_in + 31) // 32
+    if spec.k == 1 and spec.pad == 0 and i1 <= 4:
+        return f"conv1x1_kernel<{bm}, {bn}, {(i1 + 1) // 2}, {res}, {relu}>"
     return f"conv_kernel<{spec.k}, {spec.k}, {bm}, {bn}, 3, {res}, {relu}>"
 
 
@@ -47,6 +50,7 @@ def kernel_name(spec, nhwc_input=True) -> str:
 # reported while these files are unchanged.
 KERNEL_SOURCES = {
     "conv_kernel": ["conv.hip", "device_common.h", "ifx_internal.h"],
+    "conv1x1_kernel": ["conv1x1.hip", "device_common.h", "ifx_internal.h"],
     "stem_kernel": ["stem.hip", "device_common.h", "ifx_internal.h"],
 }
 

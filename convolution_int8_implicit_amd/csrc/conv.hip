@@ -34,81 +34,8 @@
 #include "ifx_internal.h"
 #include "device_common.h"
 
-typedef int ifx_v4i __attribute__((ext_vector_type(4)));
-
-// Direct buffer -> LDS load: each lane's `size` bytes land at lds + lane * size.
-__device__ void ifx_raw_buffer_load_lds(ifx_v4i rsrc, __attribute__((address_space(3))) void *lds, int size,
-                                        unsigned voffset, int soffset, int offset,
-                                        int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
-
 namespace ifx {
 namespace {
-
-typedef ifx_v4i v4i;
-
-constexpr int kLdsBytes = 160 * 1024;  // LDS per CU on gfx950
-constexpr unsigned kOOB = 0x80000000u;  // offset past every buffer range: loads return zero
-
-// Buffer resource (gfx9 layout): 48-bit base, stride 0, byte range, raw-buffer config word.
-__device__ __forceinline__ v4i make_rsrc(const void *base, long long range)
-{
-    unsigned long long a = (unsigned long long)base;
-    unsigned r = (unsigned)(range < 0 ? 0 : (range > 0x7ffffff0ll ? 0x7ffffff0ll : range));
-    v4i v;
-    v.x = __builtin_amdgcn_readfirstlane((int)(unsigned)a);
-    v.y = __builtin_amdgcn_readfirstlane((int)(unsigned)(a >> 32) & 0xffff);
-    v.z = __builtin_amdgcn_readfirstlane((int)r);
-    v.w = 0x00020000;
-    return v;
-}
-
-__device__ __forceinline__ void load16_lds(v4i rsrc, int8_t *lds_wave_base, unsigned voff)
-{
-    ifx_raw_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void *)(lds_wave_base), 16, voff, 0, 0, 0);
-}
-
-// floor(n / d) for 0 <= n < 2^31 with the host-computed magic of d (mul == 0 means d == 1).
-__device__ __forceinline__ int fdiv(int n, unsigned mul, int shr)
-{
-    return mul == 0 ? n : (int)(__umulhi((unsigned)n, mul) >> shr);
-}
-
-// 16-byte-chunk XOR swizzle of a 64-byte LDS row: conflict-free ds_read_b128
-// for both the row-major operand fetch and the permuted pixel order.
-__device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
-
-// Requantise a wave's 64x64 accumulator tile into the LDS staging tile (row
-// stride BN), adding the shortcut bytes already there when RES.  MODE 0:
-// general (any shift); 1: shift >= 2, ReLU, no shortcut; 2: shift >= 2.
-// Lane (g, c) owns tile rows 16tm + 4i + g and the 4 bytes at column 4c.
-template <int MODE, bool RES, bool RELU, int BN>
-__device__ __forceinline__ void requant_tile(const v4i (&acc)[4][4], int8_t *rbase, const int (&bias)[4],
-                                             const int (&mul)[4], const int (&rnd)[4], const int (&shm)[4],
-                                             const int (&shf)[4])
-{
-#pragma unroll
-    for (int tm = 0; tm < 4; ++tm)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            unsigned *rp = (unsigned *)(rbase + (16 * tm + 4 * i) * BN);
-            const unsigned rr = RES ? *rp : 0u;
-            int q[4];
-#pragma unroll
-            for (int tn = 0; tn < 4; ++tn) {
-                const int yv = acc[tm][tn][i] + bias[tn];
-                int v;
-                if (MODE == 0)
-                    v = requant_any(yv, mul[tn], shf[tn]);
-                else if (MODE == 1)
-                    v = requant_relu(yv, mul[tn], rnd[tn], shm[tn]);
-                else
-                    v = requant_fast(yv, mul[tn], rnd[tn], shm[tn]);
-                if (RES) v += (int)(signed char)(rr >> (8 * tn));
-                q[tn] = RELU ? min(max(v, 0), 127) : min(max(v, -128), 127);
-            }
-            *rp = pack4(q[0], q[1], q[2], q[3]);
-        }
-}
 
 // Tile geometry: a BM x BN workgroup tile, one wave per 64x64 sub-tile, and
 // an ST-stage LDS ring.
@@ -547,6 +474,7 @@ hipError_t launch_k(const ConvArgs &a, hipStream_t s)
 
 hipError_t launch_conv(const ConvArgs &a, int kh, int kw, hipStream_t s)
 {
+    if (conv1x1_small_k_supported(a, kh, kw)) return launch_conv1x1_small_k(a, s);
     if (kh == 1 && kw == 1) return launch_k<1, 1>(a, s);
     if (kh == 3 && kw == 3) return launch_k<3, 3>(a, s);
     return hipErrorInvalidValue;

@@ -60,6 +60,9 @@ struct StemArgs {
 };
 
 hipError_t launch_conv(const ConvArgs &a, int kh, int kw, hipStream_t s);
+// 1x1 convolutions with at most 128 input channels (conv1x1.hip)
+bool conv1x1_small_k_supported(const ConvArgs &a, int kh, int kw);
+hipError_t launch_conv1x1_small_k(const ConvArgs &a, hipStream_t s);
 hipError_t launch_stem(const StemArgs &a, hipStream_t s);
 hipError_t launch_avgpool(const int8_t *x, int8_t *y, int n, int c1, int hw, hipStream_t s);
 hipError_t launch_pack_act(const int8_t *x, int8_t *blk, int n, int h, int w, int c, hipStream_t s);
