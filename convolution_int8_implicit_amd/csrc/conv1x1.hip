@@ -136,7 +136,7 @@ void conv1x1_kernel(ConvArgs a, int tiles_n)
                 const int b = fdiv(p, a.howo_mul, a.howo_shr), hw = p - b * HoWo;
                 off = (unsigned)((((long long)(b - img0) * a.oc1 + (oc >> 5)) * HoWo + hw) * 32 + (oc & 31));
             }
-            load16_lds(rsR, Rw + j * 1024, off);
+            load16_lds_stream(rsR, Rw + j * 1024, off);
         }
     }
 
@@ -221,7 +221,12 @@ void conv1x1_kernel(ConvArgs a, int tiles_n)
             ++b;
         }
         const v4i v = *(const v4i *)(Rw + prow * 64 + 16 * k);
-        *(v4i *)(y + (((long long)b * a.oc1 + (och >> 5)) * HoWo + hw) * 32 + (och & 31)) = v;
+        int8_t *dst = y + (((long long)b * a.oc1 + (och >> 5)) * HoWo + hw) * 32 + (och & 31);
+        // with a shortcut stream, both streams go non-temporal (measured faster); without, plain stores
+        if (RES)
+            store16_stream(dst, v);
+        else
+            *(v4i *)dst = v;
     }
 }
 

@@ -105,6 +105,7 @@ typedef ifx_v4i v4i;
 
 constexpr int kLdsBytes = 160 * 1024;  // LDS per CU on gfx950
 constexpr unsigned kOOB = 0x80000000u;  // offset past every buffer range: loads return zero
+constexpr int kCachePolicyNT = 2;       // buffer instruction cache-policy operand: non-temporal
 
 // Buffer resource (gfx9 layout): 48-bit base, stride 0, byte range, raw-buffer config word.
 __device__ __forceinline__ v4i make_rsrc(const void *base, long long range)
@@ -123,6 +124,17 @@ __device__ __forceinline__ void load16_lds(v4i rsrc, int8_t *lds_wave_base, unsi
 {
     ifx_raw_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void *)(lds_wave_base), 16, voff, 0, 0, 0);
 }
+
+// The same for data read once (streamed): the non-temporal policy keeps it from
+// displacing reused operands in L2 and the MALL.
+__device__ __forceinline__ void load16_lds_stream(v4i rsrc, int8_t *lds_wave_base, unsigned voff)
+{
+    ifx_raw_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void *)(lds_wave_base), 16, voff, 0, 0,
+                            kCachePolicyNT);
+}
+
+// 16-byte store of output written once, non-temporal.
+__device__ __forceinline__ void store16_stream(int8_t *p, v4i v) { __builtin_nontemporal_store(v, (v4i *)p); }
 
 // floor(n / d) for 0 <= n < 2^31 with the host-computed magic of d (mul == 0 means d == 1).
 __device__ __forceinline__ int fdiv(int n, unsigned mul, int shr)

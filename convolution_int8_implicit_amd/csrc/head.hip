@@ -22,7 +22,7 @@ __global__ __launch_bounds__(256) void avgpool_kernel(const int8_t *__restrict__
     const unsigned *src = (const unsigned *)(x + plane * hw * 32) + word;
     int s0 = 0, s1 = 0, s2 = 0, s3 = 0;
     for (int p = 0; p < hw; ++p) {
-        unsigned v = src[p * 8];
+        unsigned v = __builtin_nontemporal_load(src + p * 8);  // read once
         s0 += (int)(signed char)(v);
         s1 += (int)(signed char)(v >> 8);
         s2 += (int)(signed char)(v >> 16);

@@ -104,9 +104,9 @@ __device__ __forceinline__ void fetch(const StemArgs &a, const Tile &g, unsigned
             // w % 4 == 0 and gx % 4 == 0: a group lies wholly inside or outside the row
             if (i < kIT * kGroups && (unsigned)iy < (unsigned)a.h && (unsigned)gx < (unsigned)a.w) {
                 const unsigned *src = (const unsigned *)(img + ((long long)iy * a.w + gx) * 3);
-                d0 = src[0];
-                d1 = src[1];
-                d2 = src[2];
+                d0 = __builtin_nontemporal_load(src);
+                d1 = __builtin_nontemporal_load(src + 1);
+                d2 = __builtin_nontemporal_load(src + 2);
             }
             pre[3 * s] = d0;
             pre[3 * s + 1] = d1;
@@ -316,7 +316,7 @@ __global__ __launch_bounds__(kThreads) void stem_kernel(StemArgs a, int tiles, i
 #pragma unroll
             for (int j = 0; j < 4; ++j) mx[j] = (int)((ev[j] | (od[j] << 8)) ^ 0x80808080u);
             int8_t *dst = a.y + ((((long long)g.b * 2 + (cg >> 5)) * a.ph + py) * a.pw + px) * 32 + (cg & 31);
-            *(v4i *)dst = mx;
+            store16_stream(dst, mx);
         }
         if (t_next >= t_end) break;
         t = t_next;
