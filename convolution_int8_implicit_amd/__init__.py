@@ -10,7 +10,7 @@ Entry points mirror include/ifx.h:
     conv_validate, conv_out_dims, act_bytes, wpack_bytes,
     pack_act, unpack_act, pack_weights, conv_fused,
     block_workspace_bytes, block_forward, net_workspace_bytes, net_forward,
-    status_string, last_hip_error, version
+    fold_bn, status_string, last_hip_error, version
 """
 from __future__ import annotations
 
@@ -24,7 +24,7 @@ __all__ = [
     "RELU", "RESIDUAL", "MAXPOOL", "OUT_I32", "INPUT_NHWC", "IfxError", "ConvDesc", "BlockParams", "NetParams", "lib",
     "conv_desc", "conv_validate", "conv_out_dims", "act_bytes", "wpack_bytes", "pack_act", "unpack_act",
     "pack_weights", "conv_fused", "block_workspace_bytes", "block_forward", "net_workspace_bytes",
-    "net_forward", "status_string", "last_hip_error", "version", "LIB_PATH",
+    "net_forward", "fold_bn", "BnFold", "status_string", "last_hip_error", "version", "LIB_PATH",
 ]
 
 RELU, RESIDUAL, MAXPOOL, OUT_I32, INPUT_NHWC = 1, 2, 4, 8, 16
@@ -63,6 +63,13 @@ class NetParams(ctypes.Structure):
                 ("sub_batch", ctypes.c_int32)]
 
 
+class BnFold(ctypes.Structure):
+    _fields_ = [("c_out", ctypes.c_int32), ("x_scale", ctypes.c_float), ("y_scale", ctypes.c_float),
+                ("eps", ctypes.c_float), ("w_per_channel", ctypes.c_int32), ("w_scale", ctypes.c_void_p),
+                ("conv_bias", ctypes.c_void_p), ("gamma", ctypes.c_void_p), ("beta", ctypes.c_void_p),
+                ("mean", ctypes.c_void_p), ("var", ctypes.c_void_p)]
+
+
 _LIB = None
 
 
@@ -89,6 +96,7 @@ def lib() -> ctypes.CDLL:
         "ifx_block_forward": ([ctypes.POINTER(BlockParams), vp, vp, vp, sz, vp], i32),
         "ifx_net_workspace_bytes": ([ctypes.POINTER(NetParams), i32], sz),
         "ifx_net_forward": ([ctypes.POINTER(NetParams), vp, vp, i32, vp, sz, vp], i32),
+        "ifx_fold_bn": ([ctypes.POINTER(BnFold), vp, vp, vp, vp, vp], i32),
         "ifx_status_string": ([i32], ctypes.c_char_p),
         "ifx_last_hip_error": ([], i32),
         "ifx_version": ([], i32),
@@ -204,6 +212,21 @@ def net_forward(p: NetParams, x_blk, logits, n: int, ws: torch.Tensor, stream=No
     _dev(x_blk, logits, ws)
     _check(lib().ifx_net_forward(ctypes.byref(p), _ptr(x_blk), _ptr(logits), n, _ptr(ws),
                                  ws.numel() * ws.element_size(), _stream(stream)), "ifx_net_forward")
+
+
+def fold_bn(x_scale: float, y_scale: float, eps: float, w_scale: torch.Tensor, gamma: torch.Tensor,
+            beta: torch.Tensor, mean: torch.Tensor, var: torch.Tensor, conv_bias: Optional[torch.Tensor] = None,
+            stream=None):
+    """BN folding on the device (ifx_fold_bn): float32 device tensors [c_out] (w_scale
+    may have one element) -> (bias, mult, shift, status) int32 device tensors."""
+    _dev(w_scale, gamma, beta, mean, var, conv_bias)
+    n = gamma.numel()
+    f = BnFold(n, float(x_scale), float(y_scale), float(eps), 0 if w_scale.numel() == 1 else 1,
+               w_scale.data_ptr(), conv_bias.data_ptr() if conv_bias is not None else None, gamma.data_ptr(),
+               beta.data_ptr(), mean.data_ptr(), var.data_ptr())
+    outs = [torch.empty(n, dtype=torch.int32, device=gamma.device) for _ in range(4)]
+    _check(lib().ifx_fold_bn(ctypes.byref(f), *[_ptr(o) for o in outs], _stream(stream)), "ifx_fold_bn")
+    return tuple(outs)
 
 
 def status_string(s: int) -> str:

@@ -361,6 +361,33 @@ ifx_status ifx_pack_weights(const ifx_conv_desc *d, const int8_t *w_ohwi, int8_t
     return hip_status(ifx::launch_pack_weights(w_ohwi, w_blk, d->c_out, d->kh, d->kw, d->c_in, wgroup(d->c_out), s));
 }
 
+ifx_status ifx_fold_bn(const ifx_bn_fold *f, int32_t *bias, int32_t *mult, int32_t *shift, int32_t *status,
+                       void *stream)
+{
+    if (!f) return IFX_E_NULL;
+    if (f->c_out <= 0) return IFX_E_SHAPE;
+    if (!f->w_scale || !f->gamma || !f->beta || !f->mean || !f->var || !bias || !mult || !shift || !status)
+        return IFX_E_NULL;
+    const void *words[] = {f->w_scale, f->gamma, f->beta, f->mean, f->var, status};
+    for (const void *p : words)
+        if (reinterpret_cast<uintptr_t>(p) & 3u) return IFX_E_ALIGN;
+    if (f->conv_bias && (reinterpret_cast<uintptr_t>(f->conv_bias) & 3u)) return IFX_E_ALIGN;
+    if (!aligned16(bias) || !aligned16(mult) || !aligned16(shift)) return IFX_E_ALIGN;
+    ifx::FoldArgs a;
+    a.c_out = f->c_out;
+    a.x_scale = f->x_scale;
+    a.y_scale = f->y_scale;
+    a.eps = f->eps;
+    a.w_per_channel = f->w_per_channel ? 1 : 0;
+    a.w_scale = f->w_scale;
+    a.conv_bias = f->conv_bias;
+    a.gamma = f->gamma;
+    a.beta = f->beta;
+    a.mean = f->mean;
+    a.var = f->var;
+    return hip_status(ifx::launch_fold_bn(a, bias, mult, shift, status, (hipStream_t)stream));
+}
+
 ifx_status ifx_conv_fused(const ifx_conv_desc *d, const int8_t *x_blk, const int8_t *w_blk, const int32_t *bias,
                           const int32_t *mult, const int32_t *shift, const int8_t *residual, void *y, void *stream)
 {

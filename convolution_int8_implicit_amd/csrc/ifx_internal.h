@@ -59,7 +59,17 @@ struct StemArgs {
     int relu;
 };
 
+// Inputs of the BN folding kernel (device pointers; see ifx_fold_bn).
+struct FoldArgs {
+    int c_out;
+    float x_scale, y_scale, eps;
+    int w_per_channel;
+    const float *w_scale, *conv_bias, *gamma, *beta, *mean, *var;
+};
+
 hipError_t launch_conv(const ConvArgs &a, int kh, int kw, hipStream_t s);
+hipError_t launch_fold_bn(const FoldArgs &f, int32_t *bias, int32_t *mult, int32_t *shift, int32_t *status,
+                          hipStream_t s);
 // 1x1 convolutions with at most 128 input channels (conv1x1.hip)
 bool conv1x1_small_k_supported(const ConvArgs &a, int kh, int kw);
 hipError_t launch_conv1x1_small_k(const ConvArgs &a, hipStream_t s);

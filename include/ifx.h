@@ -199,6 +199,38 @@ size_t ifx_net_workspace_bytes(const ifx_net_params *p, int32_t n);
 ifx_status ifx_net_forward(const ifx_net_params *p, const int8_t *x_blk, int32_t *logits, int32_t n,
                            void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * Float -> fixed-point epilogue parameters of one conv + BN layer (BN folding
+ * into the fused convolution: DiDi IFX DAWNBench blog, inference section, and
+ * Inspur conv-merge article, section 3.4; the quantisation scales come from a
+ * calibration outside this library, DiDi blog quantisation section).
+ * Symmetric int8 quantisation, real = scale * code.  For output channel o:
+ *   M[o] = gamma s_x s_w / (s_y sqrt(var + eps))
+ *   B[o] = (b_conv - mean) / (s_x s_w) + beta sqrt(var + eps) / (gamma s_x s_w)
+ * so that the layer's output code is M[o] * (acc + B[o]); the results are
+ *   bias[o]  = round_half_away_from_zero(B[o])
+ *   mult[o], shift[o] with M[o] ~= mult * 2^-(31 + shift), mult in [2^30, 2^31)
+ *            (rounded half away from zero; shift capped at 31 with mult below
+ *            2^30 for tiny scales)
+ *   status[o] = 0 ok; 1 M >= 1 (not representable: mult = 2^31 - 1, shift 0);
+ *               2 M <= 0 or not finite (bias = mult = shift = 0);
+ *               3 bias outside int32 (clamped).
+ * Computed on the device in IEEE double, one rounding per operation in the
+ * order of the formulas, no fused multiply-add: results are reproducible.
+ * A shortcut added by IFX_RESIDUAL must already be in the output's scale s_y.
+ * All array pointers are DEVICE pointers of c_out elements (w_scale has 1
+ * element when w_per_channel is 0; conv_bias may be NULL for no conv bias).
+ */
+typedef struct {
+    int32_t c_out;
+    float x_scale, y_scale, eps;
+    int32_t w_per_channel;
+    const float *w_scale, *conv_bias, *gamma, *beta, *mean, *var;
+} ifx_bn_fold;
+
+ifx_status ifx_fold_bn(const ifx_bn_fold *f, int32_t *bias, int32_t *mult, int32_t *shift, int32_t *status,
+                       void *stream);
+
 /* Host-only: a static, human-readable name of a status. */
 const char *ifx_status_string(ifx_status s);
 

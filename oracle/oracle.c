@@ -31,6 +31,7 @@
  * All arithmetic is integer.  Accumulation runs in int64 and any value that
  * leaves the int32 range is reported (ORC_E_OVERFLOW) instead of wrapping.
  */
+#include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -348,5 +349,91 @@ int orc_pack_weights_stem(const int8_t *wt, int oc, int ic, int8_t *blk)
                                    ? wt[(((int64_t)o * 7 + y) * 7 + xx) * ic + ch]
                                    : 0;
                 }
+    return ORC_OK;
+}
+
+/*
+ * BN folding into the integer epilogue (DiDi IFX DAWNBench blog: CONV+BN+RELU
+ * as one function after post-training quantisation; Inspur conv-merge
+ * article section 3.4: BN applied to the accumulators).  The pages print no
+ * formula; the reading: symmetric int8 quantisation (real = scale * code), so
+ * for output channel o the output code is M * (acc + B) with
+ *   M = gamma * s_x * s_w / (s_y * sqrt(var + eps))
+ *   B = (b_conv - mean) / (s_x * s_w) + beta * sqrt(var + eps) / (gamma * s_x * s_w)
+ * Each value is one IEEE double operation after another, in this order, so a
+ * decision taken on them (a rounding to an integer) is reproducible:
+ *   sd = sqrt(var + eps); sxw = s_x * s_w; M = (gamma * sxw) / (s_y * sd);
+ *   B = (b_conv - mean) / sxw + (beta * sd) / (gamma * sxw).
+ * Then bias = round_half_away(B) and M = f * 2^e (f in [0.5, 1)) gives
+ * shift = -e and mult = round_half_away(f * 2^31), renormalised when that
+ * reaches 2^31; a shift beyond 31 keeps 31 with mult = round(f * 2^(62 + e)).
+ * status: 0 ok; 1 M >= 1 (mult = 2^31 - 1, shift 0); 2 M <= 0 or not finite
+ * (all zero); 3 bias outside int32 (clamped).
+ */
+static double orc_round_half_away(double x)
+{
+    double a = fabs(x);
+    double r = floor(a);
+    double q = (a - r >= 0.5) ? r + 1.0 : r;
+    return x < 0 ? -q : q;
+}
+
+int orc_fold_bn(int c_out, double x_scale, double y_scale, double eps, int w_per_channel, const float *w_scale,
+                const float *conv_bias, const float *gamma, const float *beta, const float *mean, const float *var,
+                int32_t *bias, int32_t *mult, int32_t *shift, int32_t *status)
+{
+    for (int o = 0; o < c_out; o++) {
+        double sw = w_scale[w_per_channel ? o : 0];
+        double cb = conv_bias ? conv_bias[o] : 0.0;
+        double g = gamma[o];
+        double sd = sqrt((double)var[o] + eps);
+        double sxw = x_scale * sw;
+        double num = g * sxw;
+        double den = y_scale * sd;
+        double M = num / den;
+        double t1 = (cb - (double)mean[o]) / sxw;
+        double t2 = ((double)beta[o] * sd) / (g * sxw);
+        double B = t1 + t2;
+        int st = 0;
+        int32_t m = 0, s = 0, b = 0;
+        if (!(M > 0.0) || !isfinite(M) || !isfinite(B)) {
+            st = 2;
+        } else {
+            int e = 0;
+            double f = frexp(M, &e);
+            long sh = -(long)e;
+            double tm;
+            if (sh > 31) {
+                tm = ldexp(f, 62 + e);
+                sh = 31;
+            } else {
+                tm = ldexp(f, 31);
+            }
+            double mr = orc_round_half_away(tm);
+            if (mr >= 2147483648.0) {
+                mr = 1073741824.0;
+                sh -= 1;
+            }
+            if (sh < 0) {
+                st = 1;
+                m = 2147483647;
+                s = 0;
+            } else {
+                m = (int32_t)mr;
+                s = (int32_t)sh;
+            }
+            double br = orc_round_half_away(B);
+            if (br > 2147483647.0 || br < -2147483648.0) {
+                if (!st) st = 3;
+                b = br > 0 ? 2147483647 : INT32_MIN;
+            } else {
+                b = (int32_t)br;
+            }
+        }
+        bias[o] = b;
+        mult[o] = m;
+        shift[o] = s;
+        status[o] = st;
+    }
     return ORC_OK;
 }

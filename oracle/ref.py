@@ -70,6 +70,9 @@ def _load():
     lib.orc_pack_weights.restype = i32
     lib.orc_pack_weights_stem.argtypes = [vp, i32, i32, vp]
     lib.orc_pack_weights_stem.restype = i32
+    f64 = ctypes.c_double
+    lib.orc_fold_bn.argtypes = [i32, f64, f64, f64, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.orc_fold_bn.restype = i32
     return lib
 
 
@@ -282,3 +285,20 @@ def net(x, stem: ConvParams, blocks: Sequence[BlockParams], fc_w, fc_bias,
     if trace is not None:
         trace.append(a)
     return fc(a, fc_w, fc_bias)
+
+
+def fold_bn(x_scale, y_scale, eps, w_scale, gamma, beta, mean, var, conv_bias=None):
+    """BN folding to (bias, mult, shift, status) int32 arrays (orc_fold_bn).  Scales and
+    eps are float32 values (as the library takes them); arrays are float32 [c_out]
+    (w_scale may have one element: per-tensor)."""
+    L = lib()
+    f32 = lambda a: np.ascontiguousarray(np.asarray(a, dtype=np.float32))
+    gamma, beta, mean, var, w_scale = f32(gamma), f32(beta), f32(mean), f32(var), f32(w_scale)
+    n = gamma.size
+    cb = f32(conv_bias) if conv_bias is not None else None
+    outs = [np.zeros(n, np.int32) for _ in range(4)]
+    rc = L.orc_fold_bn(n, float(np.float32(x_scale)), float(np.float32(y_scale)), float(np.float32(eps)),
+                       0 if w_scale.size == 1 else 1, _ptr(w_scale), _ptr(cb), _ptr(gamma), _ptr(beta),
+                       _ptr(mean), _ptr(var), *[_ptr(o) for o in outs])
+    _check(rc, "fold_bn")
+    return tuple(outs)

@@ -146,3 +146,22 @@ def test_net_validation_and_workspace():
     assert L.ifx_net_forward(ctypes.byref(p), fake, fake, 4, fake, ws // 2 - 1, None) == 5
     p.fc_in = 255
     assert ifx.net_workspace_bytes(p, 4) == 0
+
+
+def test_fold_bn_validation_before_any_launch():
+    L = ifx.lib()
+    fake = 0x100000                      # aligned, never dereferenced
+    good = dict(c_out=8, x_scale=0.1, y_scale=0.2, eps=1e-5, w_per_channel=1, w_scale=fake, conv_bias=None,
+                gamma=fake, beta=fake, mean=fake, var=fake)
+    outs = [ctypes.c_void_p(fake)] * 4
+    assert L.ifx_fold_bn(None, *outs, None) == 1
+    f = ifx.BnFold(**{**good, "c_out": 0})
+    assert L.ifx_fold_bn(ctypes.byref(f), *outs, None) == 2
+    f = ifx.BnFold(**{**good, "gamma": None})
+    assert L.ifx_fold_bn(ctypes.byref(f), *outs, None) == 1
+    f = ifx.BnFold(**good)
+    assert L.ifx_fold_bn(ctypes.byref(f), None, *outs[1:], None) == 1
+    f = ifx.BnFold(**{**good, "var": fake + 2})
+    assert L.ifx_fold_bn(ctypes.byref(f), *outs, None) == 4
+    f = ifx.BnFold(**good)
+    assert L.ifx_fold_bn(ctypes.byref(f), ctypes.c_void_p(fake + 4), *outs[1:], None) == 4

@@ -276,3 +276,50 @@ def test_repeat_runs_identical(ifx):
         outs.append(y)
     torch.cuda.synchronize()
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+
+
+# ------------------------------------------------------------------ BN folding
+def _fold_inputs(rng, n):
+    g = rng.uniform(0.05, 4.0, n).astype(np.float32)
+    g[::17] = -g[::17]                          # some channels not representable (status 2)
+    be = rng.uniform(-3, 3, n).astype(np.float32)
+    mu = rng.uniform(-2, 2, n).astype(np.float32)
+    var = rng.uniform(0.0, 9.0, n).astype(np.float32)
+    sw = (2.0 ** rng.uniform(-40, 2, n)).astype(np.float32)  # tiny, normal and >= 1 scales
+    cb = rng.uniform(-1, 1, n).astype(np.float32)
+    cb[::29] = 3e9                               # bias outside int32 (status 3)
+    return sw, g, be, mu, var, cb
+
+
+@pytest.mark.parametrize("n,per_channel,with_bias", [(1, True, False), (64, True, True), (1000, True, True),
+                                                     (300, False, True), (2048, False, False)])
+def test_fold_bn_matches_oracle(ifx, orc, n, per_channel, with_bias):
+    note(f"fold_bn n={n} per_channel={per_channel} bias={with_bias}")
+    rng = np.random.default_rng(n + per_channel)
+    sw, g, be, mu, var, cb = _fold_inputs(rng, n)
+    if not per_channel:
+        sw = sw[:1]
+    xs, ys, eps = 0.0173, 0.0411, 1e-5
+    got = ifx.fold_bn(xs, ys, eps, cu(sw), cu(g), cu(be), cu(mu), cu(var), cu(cb) if with_bias else None)
+    torch.cuda.synchronize()
+    exp = orc.fold_bn(xs, ys, eps, sw, g, be, mu, var, conv_bias=cb if with_bias else None)
+    for name, a, b in zip(("bias", "mult", "shift", "status"), got, exp):
+        np.testing.assert_array_equal(a.cpu().numpy(), b, err_msg=name)
+
+
+def test_fold_bn_feeds_the_fused_conv(ifx, orc):
+    """Parameters derived on the device drive ifx_conv_fused to the oracle's result."""
+    note("fold_bn -> conv_fused")
+    rng = np.random.default_rng(77)
+    oc, c = 64, 96
+    g = rng.uniform(0.2, 2.0, oc).astype(np.float32)
+    be, mu = rng.uniform(-1, 1, oc).astype(np.float32), rng.uniform(-1, 1, oc).astype(np.float32)
+    var = rng.uniform(0.2, 3.0, oc).astype(np.float32)
+    sw = (2.0 ** rng.uniform(-9, -6, oc)).astype(np.float32)
+    bias, mult, shift, st = ifx.fold_bn(0.02, 0.05, 1e-5, cu(sw), cu(g), cu(be), cu(mu), cu(var))
+    assert int(st.abs().sum()) == 0
+    x = rand(rng, (2, 9, 11, c), 0, 127)
+    wt = rand(rng, (oc, 3, 3, c), -127, 127)
+    b_, m_, s_ = bias.cpu().numpy(), mult.cpu().numpy(), shift.cpu().numpy()
+    got = gpu_conv(ifx, x, wt, b_, m_, s_, 3, 1, 1, ifx.RELU)
+    np.testing.assert_array_equal(got, orc.conv_fused(x, wt, b_, m_, s_, 1, 1, ifx.RELU))

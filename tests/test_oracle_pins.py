@@ -379,3 +379,102 @@ def test_p14_int32_safety(orc):
     w = np.full((1, 1, 1, 140000), -127, np.int8)
     with pytest.raises(OverflowError):
         orc.conv_acc(x, w, 1, 0)
+
+
+# ---------------------------------------------------------------- P15: BN folding
+def _dec(v):
+    """Exact decimal of a float32 value."""
+    from decimal import Decimal
+    return Decimal(float(np.float32(v)))
+
+
+def _fold_exact(xs, ys, eps, sw, g, be, mu, var, cb):
+    """M and B of the folding formulas in 60-digit decimal arithmetic from the exact
+    float32 inputs (no double rounding), for comparison with the oracle's doubles."""
+    from decimal import getcontext
+    getcontext().prec = 60
+    sd = (_dec(var) + _dec(eps)).sqrt()
+    sxw = _dec(xs) * _dec(sw)
+    M = _dec(g) * sxw / (_dec(ys) * sd)
+    B = (_dec(cb) - _dec(mu)) / sxw + _dec(be) * sd / (_dec(g) * sxw)
+    return M, B
+
+
+def test_p15_fold_closed_forms(orc):
+    # scale 1/2 with no BN shift: the identity-half parameters of P3 (mult 2^30, shift 0)
+    b, m, s, st = orc.fold_bn(0.5, 1.0, 0.0, [1.0], [1.0], [0.0], [0.0], [1.0])
+    assert (b[0], m[0], s[0], st[0]) == (0, 1 << 30, 0, 0)
+    # gamma 3, sqrt(var) 2, s_x s_w / s_y = 2^-4 * 2^-6 / 2^-2 = 2^-8: M = 3 * 2^-9 = 0.75 * 2^-7
+    b, m, s, st = orc.fold_bn(2.0 ** -4, 2.0 ** -2, 0.0, [2.0 ** -6], [3.0], [0.0], [0.0], [4.0])
+    assert (m[0], s[0], st[0]) == (3 << 29, 7, 0)
+    # B = (b_conv - mean)/(s_x s_w) + beta sd/(gamma s_x s_w) = (5 - 1)/2^-10 + 6*2/(3*2^-10) = 4096 + 4096
+    b, m, s, st = orc.fold_bn(2.0 ** -4, 2.0 ** -2, 0.0, [2.0 ** -6], [3.0], [6.0], [1.0], [4.0], conv_bias=[5.0])
+    assert (b[0], st[0]) == (8192, 0)
+    # ties of the bias round away from zero: B = +-2.5
+    b, _, _, _ = orc.fold_bn(1.0, 1.0, 0.0, [1.0], [1.0, 1.0], [0.0, 0.0], [-2.5, 2.5], [1.0, 1.0])
+    assert list(b) == [3, -3]
+    # status: M >= 1, M <= 0 (negative gamma), bias beyond int32
+    b, m, s, st = orc.fold_bn(1.0, 0.5, 0.0, [1.0, 1.0, 1.0], [1.0, -1.0, 1e-3], [0.0, 0.0, 1e9], [0.0] * 3,
+                              [1.0] * 3)
+    assert (st[0], m[0], s[0]) == (1, (1 << 31) - 1, 0)
+    assert (st[1], b[1], m[1], s[1]) == (2, 0, 0, 0)
+    assert st[2] == 3 and b[2] == (1 << 31) - 1
+    # a tiny scale keeps shift 31 and a mult below 2^30
+    b, m, s, st = orc.fold_bn(2.0 ** -20, 1.0, 0.0, [2.0 ** -20], [1.0], [0.0], [0.0], [1.0])
+    assert (s[0], st[0]) == (31, 0) and m[0] == 1 << 22  # 2^-40 * 2^62
+
+
+def test_p15_fold_matches_exact_rationals(orc):
+    """mult/shift is the nearest 31-bit fixed-point value of the exact scale, the bias
+    the nearest integer of the exact offset (60-digit decimal from the float32 inputs);
+    a difference is allowed only at a tie closer than the double computation's error."""
+    from decimal import Decimal
+    rng = np.random.default_rng(15)
+    n = 400
+    g = rng.uniform(0.05, 4.0, n).astype(np.float32)
+    be = rng.uniform(-3, 3, n).astype(np.float32)
+    mu = rng.uniform(-2, 2, n).astype(np.float32)
+    var = rng.uniform(0.01, 9.0, n).astype(np.float32)
+    sw = (2.0 ** rng.uniform(-12, -4, n)).astype(np.float32)
+    cb = rng.uniform(-1, 1, n).astype(np.float32)
+    xs, ys, eps = np.float32(0.0173), np.float32(0.0411), np.float32(1e-5)
+    b, m, s, st = orc.fold_bn(xs, ys, eps, sw, g, be, mu, var, conv_bias=cb)
+    assert np.all(st == 0)
+    assert np.all((m >= 1 << 30) & (s >= 0) & (s <= 31))
+    for o in range(n):
+        M, B = _fold_exact(xs, ys, eps, sw[o], g[o], be[o], mu[o], var[o], cb[o])
+        T = M * Decimal(2) ** (31 + int(s[o]))
+        assert abs(Decimal(int(m[o])) - T) <= Decimal("0.5") + T * Decimal("1e-14"), o
+        assert abs(Decimal(int(b[o])) - B) <= Decimal("0.5") + abs(B) * Decimal("1e-14") + Decimal("1e-9"), o
+
+
+def test_p15_folded_epilogue_matches_float_model(orc):
+    """End to end: acc -> (acc + bias) * mult / 2^(31+shift), rounded, equals the float
+    model round((s_x s_w acc + b_conv - mean) gamma / sqrt(var + eps) + beta) / s_y)
+    except within the integer model's own error of a half-integer (the bias is rounded
+    before the scale, at most M/2, and M carries 31 bits)."""
+    from decimal import Decimal
+    rng = np.random.default_rng(16)
+    n = 64
+    g = rng.uniform(0.1, 2.0, n).astype(np.float32)
+    be = rng.uniform(-2, 2, n).astype(np.float32)
+    mu = rng.uniform(-1, 1, n).astype(np.float32)
+    var = rng.uniform(0.1, 4.0, n).astype(np.float32)
+    sw = (2.0 ** rng.uniform(-10, -6, n)).astype(np.float32)
+    xs, ys, eps = np.float32(0.02), np.float32(0.05), np.float32(1e-5)
+    b, m, s, st = orc.fold_bn(xs, ys, eps, sw, g, be, mu, var)
+    assert np.all(st == 0)
+    checked = 0
+    for o in range(n):
+        M, B = _fold_exact(xs, ys, eps, sw[o], g[o], be[o], mu[o], var[o], 0.0)
+        for acc in rng.integers(-(1 << 16), 1 << 16, 40):
+            y = M * (Decimal(int(acc)) + B)          # exact code before rounding
+            want = int(rha(Fraction(y)))
+            got = orc.requant(int(acc), int(b[o]), int(m[o]), int(s[o]))
+            dist = abs(abs(y - int(y)) - Decimal("0.5"))
+            slack = M / 2 + abs(y) * Decimal(2) ** -30 + Decimal("1e-12")
+            assert abs(got - want) <= 1
+            if dist > slack:
+                assert got == want, (o, int(acc))
+                checked += 1
+    assert checked > 0.8 * n * 40
