@@ -181,8 +181,8 @@ def cpu_baseline(workload: str, budget_s: float = 20.0):
         return ConvParams(p["w"].numpy(), p["bias"].numpy(), p["mult"].numpy(), p["shift"].numpy(), spec.stride,
                           spec.pad)
 
-    if workload == "net":
-        wl = synth.workload(4)
+    if workload in ("net", "net26_b1"):
+        wl = synth.workload(4) if workload == "net" else synth.latency_workload(64)
         stem = cp(wl, wl.net.stem)
         blocks = [BlockParams(cp(wl, b.c1), cp(wl, b.c2), cp(wl, b.c3), cp(wl, b.proj) if b.proj else None)
                   for b in wl.net.blocks]
@@ -194,7 +194,8 @@ def cpu_baseline(workload: str, budget_s: float = 20.0):
             t0 = time.perf_counter()
             orc.net(x, stem, blocks, fw, fb)
             return time.perf_counter() - t0
-        per_img_ops = 2 * 4.08925e9
+        per_img_ops = sum(layer_work(sp, 1, hh, ww)[0] for sp, _, hh, ww in net_layers(wl.net, 1)) + \
+            2 * wl.net.fc_in * wl.net.fc_out
     else:
         idx = {"conv1x1": 1, "conv1x1_b1": 0, "block": 2, "stem": 3}[workload]
         wl = synth.workload(idx)
@@ -225,7 +226,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="net", choices=["net", "conv1x1", "conv1x1_b1", "block", "stem"])
+    ap.add_argument("--workload", default="net",
+                    choices=["net", "net26_b1", "conv1x1", "conv1x1_b1", "block", "stem"])
     ap.add_argument("--sub-batch", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -257,8 +259,8 @@ def main():
     sub_batch = model.DEFAULT_SUB_BATCH if args.sub_batch is None else args.sub_batch
 
     # ---------------- workload setup (untimed) ----------------
-    if args.workload == "net":
-        wl = synth.workload(4)
+    if args.workload in ("net", "net26_b1"):
+        wl = synth.workload(4) if args.workload == "net" else synth.latency_workload(1)
         n = wl.n
         net = model.DeviceNet(wl.net, wl.index, sub_batch=sub_batch, nhwc_input=not args.packed_input)
         x_nhwc = synth.input_tensor(wl, device="cuda")
@@ -270,6 +272,13 @@ def main():
             def step():
                 ifx.pack_act(x_nhwc, out=x_blk, stream=stream)
                 net.forward(x_blk, logits, n, ws, stream)
+        elif args.workload == "net26_b1":
+            x_blk = x_nhwc
+            net.forward(x_nhwc, logits, n, ws, stream)  # eager once: one-time device queries
+            graph = net.graph(x_nhwc, logits, n, ws)
+
+            def step():
+                graph.launch(stream)
         else:
             x_blk = x_nhwc
 
@@ -277,9 +286,12 @@ def main():
                 net.forward(x_nhwc, logits, n, ws, stream)
         layers = net_layers(wl.net, n)
         total_ops = sum(layer_work(s, nn, h, w)[0] for s, nn, h, w in layers) + 2 * n * wl.net.fc_in * wl.net.fc_out
-        config = {"workload": wl.name, "batch": n, "image": "224x224x3 int8 NHWC", "convs": 53,
+        config = {"workload": wl.name, "batch": n, "image": "224x224x3 int8 NHWC",
+                  "convs": 1 + sum(3 + (b.proj is not None) for b in wl.net.blocks),
                   "head": "avgpool + FC 2048->1000 int32 logits", "sub_batch": sub_batch,
-                  "step": ("input pack + " if args.packed_input else "") + "ifx_net_forward"}
+                  "step": ("input pack + " if args.packed_input else "") +
+                  ("ifx_graph_launch of the recorded ifx_net_forward" if args.workload == "net26_b1"
+                   else "ifx_net_forward")}
     else:
         idx = {"conv1x1": 1, "conv1x1_b1": 0, "block": 2, "stem": 3}[args.workload]
         wl = synth.workload(idx)
@@ -323,6 +335,18 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     sec_per_step = max(ev0.elapsed_time(ev1) * 1e-3, 0.0) / args.steps
+    extra = {}
+    if args.workload == "net26_b1":
+        # the same forward launched kernel by kernel from the host, for comparison
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            net.forward(x_nhwc, logits, n, ws, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        extra = {"latency_us": round(sec_per_step * 1e6, 1),
+                 "eager_latency_us": round(e0.elapsed_time(e1) * 1e3 / args.steps, 1)}
     img_s = n / sec_per_step
     tops = total_ops / sec_per_step / 1e12
 
@@ -336,7 +360,7 @@ def main():
         return model.DeviceConv(dc.spec, d, dc.w_blk, dc.bias, dc.mult, dc.shift, dc.out_hw)
 
     launches = []  # (spec, h, w, fn)
-    if args.workload == "net":
+    if args.workload in ("net", "net26_b1"):
         nb = sub_batch if 0 < sub_batch < n else n
         passes = (n + nb - 1) // nb
         big = max(ifx.act_bytes(nb, h, w, s.c_out if s.k != 7 else 64) for s, _, h, w in layers)
@@ -441,6 +465,7 @@ def main():
         "frac_int8_peak": round(tops * 1e12 / PEAK_I8, 4),
         "kernel_ms_per_step": kernel_share,
         "roofline": roof,
+        **extra,
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.workload)

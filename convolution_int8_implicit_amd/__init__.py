@@ -24,7 +24,7 @@ __all__ = [
     "RELU", "RESIDUAL", "MAXPOOL", "OUT_I32", "INPUT_NHWC", "IfxError", "ConvDesc", "BlockParams", "NetParams", "lib",
     "conv_desc", "conv_validate", "conv_out_dims", "act_bytes", "wpack_bytes", "pack_act", "unpack_act",
     "pack_weights", "conv_fused", "block_workspace_bytes", "block_forward", "net_workspace_bytes",
-    "net_forward", "fold_bn", "BnFold", "status_string", "last_hip_error", "version", "LIB_PATH",
+    "net_forward", "NetGraph", "fold_bn", "BnFold", "status_string", "last_hip_error", "version", "LIB_PATH",
 ]
 
 RELU, RESIDUAL, MAXPOOL, OUT_I32, INPUT_NHWC = 1, 2, 4, 8, 16
@@ -97,6 +97,9 @@ def lib() -> ctypes.CDLL:
         "ifx_net_workspace_bytes": ([ctypes.POINTER(NetParams), i32], sz),
         "ifx_net_forward": ([ctypes.POINTER(NetParams), vp, vp, i32, vp, sz, vp], i32),
         "ifx_fold_bn": ([ctypes.POINTER(BnFold), vp, vp, vp, vp, vp], i32),
+        "ifx_net_graph_create": ([ctypes.POINTER(NetParams), vp, vp, i32, vp, sz, ctypes.POINTER(vp)], i32),
+        "ifx_graph_launch": ([vp, vp], i32),
+        "ifx_graph_destroy": ([vp], i32),
         "ifx_status_string": ([i32], ctypes.c_char_p),
         "ifx_last_hip_error": ([], i32),
         "ifx_version": ([], i32),
@@ -227,6 +230,35 @@ def fold_bn(x_scale: float, y_scale: float, eps: float, w_scale: torch.Tensor, g
     outs = [torch.empty(n, dtype=torch.int32, device=gamma.device) for _ in range(4)]
     _check(lib().ifx_fold_bn(ctypes.byref(f), *[_ptr(o) for o in outs], _stream(stream)), "ifx_fold_bn")
     return tuple(outs)
+
+
+class NetGraph:
+    """ifx_net_forward for fixed buffers recorded once as a HIP graph (ifx_net_graph_create);
+    launch() enqueues the whole network with one call.  Keeps the buffers alive."""
+
+    def __init__(self, p: NetParams, x, logits, n: int, ws: torch.Tensor, keep=()):
+        _dev(x, logits, ws)
+        self._keep = (p, x, logits, ws, *keep)
+        h = ctypes.c_void_p()
+        _check(lib().ifx_net_graph_create(ctypes.byref(p), _ptr(x), _ptr(logits), n, _ptr(ws),
+                                          ws.numel() * ws.element_size(), ctypes.byref(h)), "ifx_net_graph_create")
+        self._h = h
+
+    def launch(self, stream=None) -> None:
+        if self._h is None:
+            raise RuntimeError("graph destroyed")
+        _check(lib().ifx_graph_launch(self._h, _stream(stream)), "ifx_graph_launch")
+
+    def close(self) -> None:
+        if self._h is not None:
+            _check(lib().ifx_graph_destroy(self._h), "ifx_graph_destroy")
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def status_string(s: int) -> str:

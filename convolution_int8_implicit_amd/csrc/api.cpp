@@ -494,6 +494,71 @@ ifx_status ifx_net_forward(const ifx_net_params *p, const int8_t *x_blk, int32_t
     return IFX_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Fixed-shape network launches recorded once into a HIP graph
+// ---------------------------------------------------------------------------
+struct ifx_graph_s {
+    hipGraph_t graph;
+    hipGraphExec_t exec;
+};
+
+ifx_status ifx_net_graph_create(const ifx_net_params *p, const int8_t *x_blk, int32_t *logits, int32_t n, void *ws,
+                                size_t ws_bytes, ifx_graph *out)
+{
+    if (!out) return IFX_E_NULL;
+    *out = nullptr;
+    // validate every argument first: an invalid call records nothing
+    NetPlan plan;
+    ifx_status st = plan_net(p, n, &plan);
+    if (st != IFX_OK) return st;
+    if (!x_blk || !logits || !ws) return IFX_E_NULL;
+    if (ws_bytes < net_ws_bytes(plan)) return IFX_E_WORKSPACE;
+    // one-time device queries of the launchers happen now, outside the capture
+    ifx::warm_conv_queries();
+    st = hip_status(ifx::warm_stem_queries());
+    if (st != IFX_OK) return st;
+
+    hipStream_t cs = nullptr;
+    st = hip_status(hipStreamCreateWithFlags(&cs, hipStreamNonBlocking));  // default priority
+    if (st != IFX_OK) return st;
+    st = hip_status(hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal));
+    if (st != IFX_OK) {
+        (void)hipStreamDestroy(cs);
+        return st;
+    }
+    const ifx_status fst = ifx_net_forward(p, x_blk, logits, n, ws, ws_bytes, cs);
+    hipGraph_t graph = nullptr;
+    st = hip_status(hipStreamEndCapture(cs, &graph));
+    (void)hipStreamDestroy(cs);
+    if (fst != IFX_OK || st != IFX_OK) {
+        if (graph) (void)hipGraphDestroy(graph);
+        return fst != IFX_OK ? fst : st;
+    }
+    hipGraphExec_t exec = nullptr;
+    st = hip_status(hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0));
+    if (st != IFX_OK) {
+        (void)hipGraphDestroy(graph);
+        return st;
+    }
+    *out = new ifx_graph_s{graph, exec};
+    return IFX_OK;
+}
+
+ifx_status ifx_graph_launch(ifx_graph g, void *stream)
+{
+    if (!g) return IFX_E_NULL;
+    return hip_status(hipGraphLaunch(g->exec, (hipStream_t)stream));
+}
+
+ifx_status ifx_graph_destroy(ifx_graph g)
+{
+    if (!g) return IFX_OK;
+    ifx_status st = hip_status(hipGraphExecDestroy(g->exec));
+    const ifx_status st2 = hip_status(hipGraphDestroy(g->graph));
+    delete g;
+    return st != IFX_OK ? st : st2;
+}
+
 const char *ifx_status_string(ifx_status s)
 {
     switch (s) {

@@ -477,6 +477,8 @@ hipError_t launch_k(const ConvArgs &a, hipStream_t s)
 
 }  // namespace
 
+void warm_conv_queries() { (void)device_cus(); }
+
 hipError_t launch_conv(const ConvArgs &a, int kh, int kw, hipStream_t s)
 {
     if (conv1x1_small_k_supported(a, kh, kw)) return launch_conv1x1_small_k(a, s);

@@ -68,6 +68,9 @@ struct FoldArgs {
 };
 
 hipError_t launch_conv(const ConvArgs &a, int kh, int kw, hipStream_t s);
+// Run the launchers' one-time device queries now (before a stream capture).
+void warm_conv_queries();
+hipError_t warm_stem_queries();
 hipError_t launch_fold_bn(const FoldArgs &f, int32_t *bias, int32_t *mult, int32_t *shift, int32_t *status,
                           hipStream_t s);
 // 1x1 convolutions with at most 128 input channels (conv1x1.hip)

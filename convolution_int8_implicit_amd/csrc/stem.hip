@@ -324,11 +324,11 @@ __global__ __launch_bounds__(kThreads) void stem_kernel(StemArgs a, int tiles, i
     }
 }
 
+// Persistent grid size of a path: as many workgroups as fit on the chip at once (never
+// more, so none waits for another to finish); queried once per process.
 template <int PATH>
-hipError_t launch_path(const StemArgs &a, int tiles, hipStream_t s)
+hipError_t stem_grid(long long *g)
 {
-    // persistent grid: as many workgroups as fit on the chip at once (never more, so none
-    // waits for another to finish), a multiple of 8 so every XCD gets the same number
     static int per_cu = 0, cus = 0;
     if (per_cu == 0) {
         int dev = 0;
@@ -339,7 +339,17 @@ hipError_t launch_path(const StemArgs &a, int tiles, hipStream_t s)
         if (e != hipSuccess) return e;
         if (per_cu < 1) per_cu = 1;
     }
-    long long g = (long long)per_cu * cus / 8 * 8;
+    *g = (long long)per_cu * cus;
+    return hipSuccess;
+}
+
+template <int PATH>
+hipError_t launch_path(const StemArgs &a, int tiles, hipStream_t s)
+{
+    long long g = 0;
+    hipError_t e = stem_grid<PATH>(&g);
+    if (e != hipSuccess) return e;
+    g = g / 8 * 8;  // a multiple of 8 so every XCD gets the same number
     if (g < 8) g = 8;
     const long long need = (tiles + 7LL) / 8 * 8;
     if (g > need) g = need;
@@ -349,6 +359,15 @@ hipError_t launch_path(const StemArgs &a, int tiles, hipStream_t s)
 }
 
 }  // namespace
+
+hipError_t warm_stem_queries()
+{
+    long long g;
+    hipError_t e = stem_grid<kPacked>(&g);
+    if (e == hipSuccess) e = stem_grid<kNhwc3>(&g);
+    if (e == hipSuccess) e = stem_grid<kNhwcAny>(&g);
+    return e;
+}
 
 hipError_t launch_stem(const StemArgs &a, hipStream_t s)
 {

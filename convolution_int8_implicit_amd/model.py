@@ -16,7 +16,7 @@ import torch
 # Images per pass of ifx_net_forward used by the benchmark (0 = whole batch).
 DEFAULT_SUB_BATCH = 0
 
-from . import (INPUT_NHWC, BlockParams, ConvDesc, NetParams, block_forward, block_workspace_bytes, conv_desc, conv_fused,
+from . import (INPUT_NHWC, BlockParams, ConvDesc, NetGraph, NetParams, block_forward, block_workspace_bytes, conv_desc, conv_fused,
                conv_out_dims, net_forward, net_workspace_bytes, pack_act, pack_weights, synth)
 
 
@@ -128,6 +128,10 @@ class DeviceNet:
 
     def forward(self, x, logits, n, ws, stream=None):
         net_forward(self.params, x, logits, n, ws, stream)
+
+    def graph(self, x, logits, n, ws) -> NetGraph:
+        """The forward pass over these buffers recorded as one HIP graph."""
+        return NetGraph(self.params, x, logits, n, ws, keep=(self,))
 
 
 def pack_input(x_nhwc: torch.Tensor, stream=None) -> torch.Tensor:

@@ -186,6 +186,13 @@ def resnet50_spec(stages=(3, 4, 6, 3), widths=(64, 128, 256, 512), expansion: in
     return NetSpec(stem, blocks, fc_layer=layer, fc_in=c_in, fc_out=1000)
 
 
+def resnet26_spec() -> NetSpec:
+    """ResNet-26-shaped backbone (the DAWNBench inference model of the DiDi IFX
+    blog, read as the ResNet-50 layout with two bottlenecks per stage): 26
+    weighted layers = stem + 8 x 3 bottleneck convs + FC, plus 4 projections."""
+    return resnet50_spec(stages=(2, 2, 2, 2))
+
+
 @dataclass
 class Workload:
     """One of the five synthetic workloads (seed = its index)."""
@@ -223,6 +230,12 @@ def stem_workload(index: int, n: int) -> Workload:
 def net_workload(index: int, n: int) -> Workload:
     return Workload(index, f"ResNet-50-shaped int8 backbone + avgpool + FC, 224x224, batch {n}", "net",
                     n, 224, 224, [], IMAGE_RANGE, resnet50_spec())
+
+
+def latency_workload(n: int = 1) -> Workload:
+    """The batch-1 latency setting: ResNet-26-shaped network on 224x224x3 images (seed 5)."""
+    return Workload(5, f"ResNet-26-shaped int8 backbone + avgpool + FC, 224x224, batch {n}", "net",
+                    n, 224, 224, [], IMAGE_RANGE, resnet26_spec())
 
 
 def workloads() -> List[Workload]:

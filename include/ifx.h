@@ -200,6 +200,25 @@ ifx_status ifx_net_forward(const ifx_net_params *p, const int8_t *x_blk, int32_t
                            void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * Fixed-shape network launches as one HIP graph (the batch-1 latency setting of
+ * the DiDi IFX DAWNBench blog, whose ResNet26 inference is timed per image):
+ * ifx_net_graph_create records the kernels ifx_net_forward(p, x_blk, logits,
+ * n, ws, ws_bytes, .) enqueues, with exactly these buffers, into a graph;
+ * ifx_graph_launch enqueues that whole sequence with one call (results as
+ * ifx_net_forward; the buffers must stay valid and the parameter arrays p
+ * points at unchanged while the graph exists); ifx_graph_destroy frees it.
+ * Validation as ifx_net_forward; nothing runs during creation (the recording
+ * uses a library-owned stream).  The graph handle is host state owned by the
+ * library until ifx_graph_destroy (NULL is accepted there).
+ */
+typedef struct ifx_graph_s *ifx_graph;
+
+ifx_status ifx_net_graph_create(const ifx_net_params *p, const int8_t *x_blk, int32_t *logits, int32_t n, void *ws,
+                                size_t ws_bytes, ifx_graph *out);
+ifx_status ifx_graph_launch(ifx_graph g, void *stream);
+ifx_status ifx_graph_destroy(ifx_graph g);
+
+/*
  * Float -> fixed-point epilogue parameters of one conv + BN layer (BN folding
  * into the fused convolution: DiDi IFX DAWNBench blog, inference section, and
  * Inspur conv-merge article, section 3.4; the quantisation scales come from a

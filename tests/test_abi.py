@@ -165,3 +165,13 @@ def test_fold_bn_validation_before_any_launch():
     assert L.ifx_fold_bn(ctypes.byref(f), *outs, None) == 4
     f = ifx.BnFold(**good)
     assert L.ifx_fold_bn(ctypes.byref(f), ctypes.c_void_p(fake + 4), *outs[1:], None) == 4
+
+
+def test_graph_entry_points_validate_before_recording():
+    L = ifx.lib()
+    h = ctypes.c_void_p(123)
+    assert L.ifx_net_graph_create(None, None, None, 1, None, 0, None) == 1       # no handle pointer
+    assert L.ifx_net_graph_create(None, None, None, 1, None, 0, ctypes.byref(h)) == 1
+    assert h.value is None                                                        # cleared on error
+    assert L.ifx_graph_launch(None, None) == 1
+    assert L.ifx_graph_destroy(None) == 0

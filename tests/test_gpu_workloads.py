@@ -171,3 +171,32 @@ def test_workload4_net_sampled_and_sub_batch_invariant(ifx, orc):
         torch.cuda.synchronize()
         assert torch.equal(l3, logits)
         del ws3, nn_
+
+
+@pytest.mark.parametrize("n", [1, 3])
+def test_latency_net26_graph_replays(ifx, orc, n):
+    """The ResNet-26-shaped network (batch-1 latency setting): eager forward equals the
+    oracle; the same forward recorded as one HIP graph gives the same logits on every
+    replay, with other device work and synchronisations between replays."""
+    from convolution_int8_implicit_amd import model, synth
+    wl = synth.latency_workload(n)
+    note(wl.name)
+    net = model.DeviceNet(wl.net, wl.index, nhwc_input=True)
+    x = synth.input_tensor(wl, device="cuda")
+    ws = torch.empty(net.workspace_bytes(n), dtype=torch.int8, device="cuda")
+    logits = torch.empty((n, 1000), dtype=torch.int32, device="cuda")
+    net.forward(x, logits, n, ws)
+    torch.cuda.synchronize()
+    eager = logits.clone()
+    exp = _oracle_net(orc, synth, wl, list(range(n)))
+    np.testing.assert_array_equal(eager.cpu().numpy(), exp)
+    g = net.graph(x, logits, n, ws)
+    for rep in range(3):
+        note(f"graph replay {rep}")
+        logits.fill_(-7)                      # eager work between replays
+        ws.fill_(rep)
+        torch.cuda.synchronize()
+        g.launch()
+        torch.cuda.synchronize()
+        assert torch.equal(logits, eager), rep
+    g.close()

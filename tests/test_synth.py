@@ -93,3 +93,15 @@ def test_workload_table(idx):
     assert wl.n == [1, 2048, 256, 128, 2048][idx]
     shp = synth.input_shape(wl)
     assert shp[1:3] == ((28, 28) if idx < 3 else (224, 224))
+
+
+def test_resnet26_spec_counts():
+    from convolution_int8_implicit_amd import synth
+    net = synth.resnet26_spec()
+    assert len(net.blocks) == 8
+    assert sum(b.proj is not None for b in net.blocks) == 4
+    # 26 weighted layers: stem + 8 x 3 bottleneck convs + FC (projections extra)
+    assert 1 + 3 * len(net.blocks) + 1 == 26
+    assert net.fc_in == 2048 and net.fc_out == 1000
+    wl = synth.latency_workload()
+    assert (wl.index, wl.n, wl.h, wl.w) == (5, 1, 224, 224)
