@@ -482,9 +482,7 @@ void warm_conv_queries() { (void)device_cus(); }
 hipError_t launch_conv(const ConvArgs &a, int kh, int kw, hipStream_t s)
 {
     if (conv1x1_small_k_supported(a, kh, kw)) return launch_conv1x1_small_k(a, s);
-    if (kh == 1 && kw == 1) return launch_k<1, 1>(a, s);
-    if (kh == 3 && kw == 3) return launch_k<3, 3>(a, s);
-    return hipErrorInvalidValue;
+    return launch_igemm(a, kh, kw, s);
 }
 
 }  // namespace ifx

@@ -68,6 +68,8 @@ struct FoldArgs {
 };
 
 hipError_t launch_conv(const ConvArgs &a, int kh, int kw, hipStream_t s);
+// General implicit-GEMM kernel (igemm.hip)
+hipError_t launch_igemm(const ConvArgs &a, int kh, int kw, hipStream_t s);
 // Run the launchers' one-time device queries now (before a stream capture).
 void warm_conv_queries();
 hipError_t warm_stem_queries();

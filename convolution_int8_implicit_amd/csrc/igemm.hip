@@ -1,0 +1,379 @@
+// General implicit-GEMM convolution (any kernel size, stride, padding and
+// channel count): one BM x BN output tile per workgroup.
+//
+// Computation: Inspur conv-merge article, section 3.3 (data[M,K] .
+// weight[N,K]^T over NC/32HW32 activations and [O1,KH,KW,I1,O2,32] weights)
+// and section 3.4 (BN + Sum + ReLU applied to the accumulators before the
+// store).  The design is the gfx950 one:
+//   * K advances 64 bytes per step: two 32-channel blocks, taken in the flat
+//     (tap, channel-block) order of the weight layout, so any channel count
+//     and any kernel size share one loop;
+//   * each step's operands reach LDS by buffer->LDS DMA in 1 KB
+//     instructions, and every instruction reads ONE contiguous 1 KB piece of
+//     HBM: 32 pixels x 32 channels of one block of the activation (a run of
+//     consecutive pixels, shifted by the tap), or 32 output channels x 32
+//     input channels of one weight block.  Gathering several segments per
+//     instruction (as a row-per-pixel layout would) costs more than half of
+//     the DMA rate on this chip;
+//   * out-of-image taps, rows past the end and blocks past K read through
+//     the buffer range check as zeros (no im2col, no branches);
+//   * two LDS stages (double buffer, one barrier per step) and small LDS
+//     (33-50 KB), so 3-4 workgroups share a CU and hide each other's
+//     latency, prologue and epilogue;
+//   * within a stage an operand block is [rows][32 B] with a 16-byte-slot
+//     swizzle per 128-byte line, so the DMA writes whole lines and the
+//     ds_read_b128 fragment reads of v_mfma_i32_16x16x64_i8 are free of bank
+//     conflicts;
+//   * the epilogue (per-channel bias, fixed-point requant, shortcut add,
+//     ReLU, saturate) runs on the accumulators and writes whole 16-byte
+//     chunks of the NC/32HW32 output.
+#include "device_common.h"
+#include "ifx_internal.h"
+
+namespace ifx {
+namespace {
+
+template <int BM, int BN>
+struct IgCfg {
+    static constexpr int WAVES_M = BM / 64;
+    static constexpr int WAVES = WAVES_M * (BN / 64);
+    static_assert(WAVES == 4, "four waves, one 64x64 sub-tile each");
+    static constexpr int THREADS = 256;
+    static constexpr int A_CH = BM / 32;  // 32-row chunks of a tile's pixels
+    static constexpr int B_CH = BN / 32;  // 32-row chunks of a tile's output channels
+    static constexpr int AI = 2 * A_CH / WAVES;  // activation DMAs per wave per K-step
+    static constexpr int BI = 2 * B_CH / WAVES;  // weight DMAs per wave per K-step
+    static_assert(AI * WAVES == 2 * A_CH && BI * WAVES == 2 * B_CH && A_CH % WAVES == 0, "whole DMAs");
+    static constexpr int STAGE = (BM + BN) * 64;  // A: [2][BM][32 B], then B: [2][BN][32 B]
+    static constexpr int PARAM = WAVES * 768;     // per wave: bias, mult, shift of its 64 channels
+    static constexpr int lds(bool res) { return 2 * STAGE + PARAM + (res ? BM * BN : 0); }
+    static constexpr int wg_per_cu(bool res) { return kLdsBytes / lds(res) > 4 ? 4 : kLdsBytes / lds(res); }
+};
+
+// Byte offset, inside one operand block of a stage, of the 16-byte half h of
+// row `row`.  Rows pair up four to a 128-byte line; the slot of (row, h) in
+// its line is XOR-swizzled so that the eight lanes served together by a
+// ds_read_b128 (same half, rows 0,4,8,12,1,5,9,13 or 2,6,...,15 of a 16-row
+// group for the activation fragment; rows 4c + tn, c = 0..7 for the weight
+// fragment) hit eight different slots.
+__device__ __forceinline__ int a_swz(int row, int h)
+{
+    return ((row >> 2) << 7) | (((((row & 3) ^ ((row >> 2) & 3)) << 1) | (h ^ (row & 1))) << 4);
+}
+__device__ __forceinline__ int b_swz(int row, int h)
+{
+    return ((row >> 2) << 7) | (((((row & 3) ^ ((row >> 2) & 3)) << 1) | (h ^ ((row >> 4) & 1))) << 4);
+}
+// Inverse for the DMA: lane l of an instruction that fills rows [32 c, 32 c + 32)
+// lands at byte 16 l of that 1 KB; it must fetch row 32 c + dma_row(l).
+__device__ __forceinline__ int dma_row(int lane)
+{
+    const int line = lane >> 3;
+    return 4 * line + (((lane & 7) >> 1) ^ (line & 3));
+}
+
+template <int KH, int KW, int BM, int BN, bool RES, bool RELU>
+__global__ __launch_bounds__(256, (IgCfg<BM, BN>::wg_per_cu(RES)))
+void igemm_kernel(ConvArgs a, int tiles_n, int per_xcd)
+{
+    using C = IgCfg<BM, BN>;
+    constexpr int NWV = C::WAVES;
+    __shared__ __attribute__((aligned(1024))) int8_t smem[C::lds(RES)];
+    int8_t *const Pm = smem + 2 * C::STAGE;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm0 = (wave % C::WAVES_M) * 64;
+    const int wn0 = (wave / C::WAVES_M) * 64;
+    int8_t *const Pw = Pm + wave * 768;
+
+    // tile: XCD x (blockIdx & 7) owns M-tiles [x * per_xcd, (x + 1) * per_xcd), so neighbouring
+    // pixel tiles (which share 3x3 halo rows) and the N-tiles of one pixel tile share an L2
+    const int xcd = blockIdx.x & 7;
+    const int kk = blockIdx.x >> 3;
+    const int mq = kk / tiles_n;
+    const int m0 = (xcd * per_xcd + mq) * BM;
+    if (m0 >= a.m) return;
+    const int n0 = (kk - mq * tiles_n) * BN;
+
+    const int HoWo = a.ho * a.wo;
+    const int HW = a.h * a.w;
+    const long long in_img = (long long)a.i1 * HW * 32;
+    const long long out_img = (long long)a.oc1 * HoWo * 32;
+    const int img0 = fdiv(m0, a.howo_mul, a.howo_shr);
+    const v4i rsA = make_rsrc(a.x + (long long)img0 * in_img, (long long)(a.n - img0) * in_img);
+    const int wrows = ((a.oc + a.o2 - 1) / a.o2) * a.o2;
+    const v4i rsB = make_rsrc(a.wt, (long long)wrows * KH * KW * a.i1 * 32);
+
+    // ---- per-lane DMA plans.  Activation DMA j of wave w fills chunk (4j + w) % A_CH of
+    //      block (4j + w) / A_CH: the lane's pixel, its tap-validity mask and base offset.
+    int a_base[C::AI];
+    unsigned a_mask[C::AI];
+#pragma unroll
+    for (int j = 0; j < C::AI; ++j) {
+        const int chunk = (j * NWV + wave) % C::A_CH;
+        const int row = chunk * 32 + dma_row(lane);
+        const int h = (lane & 1) ^ (row & 1);
+        const int p = m0 + row;
+        const bool ok = p < a.m;
+        const int pp = ok ? p : m0;
+        const int b = fdiv(pp, a.howo_mul, a.howo_shr);
+        const int rem = pp - b * HoWo;
+        const int oy = fdiv(rem, a.wo_mul, a.wo_shr);
+        const int ox = rem - oy * a.wo;
+        const int iy0 = oy * a.stride - a.pad;
+        const int ix0 = ox * a.stride - a.pad;
+        a_base[j] = (int)((long long)(b - img0) * in_img) + (iy0 * a.w + ix0) * 32 + h * 16;
+        unsigned mask = 0;
+#pragma unroll
+        for (int ky = 0; ky < KH; ++ky)
+#pragma unroll
+            for (int kx = 0; kx < KW; ++kx)
+                if ((unsigned)(iy0 + ky) < (unsigned)a.h && (unsigned)(ix0 + kx) < (unsigned)a.w)
+                    mask |= 1u << (ky * KW + kx);
+        a_mask[j] = ok ? mask : 0u;
+    }
+    // Weight DMA j of wave w fills chunk (4j + w) % B_CH of block (4j + w) / B_CH.
+    int b_base[C::BI];
+    bool b_ok[C::BI];
+    const int wblk = a.o2 * 32;  // bytes of one (tap, channel-block) slice of an O1 group
+#pragma unroll
+    for (int j = 0; j < C::BI; ++j) {
+        const int chunk = (j * NWV + wave) % C::B_CH;
+        const int row = chunk * 32 + dma_row(lane);
+        const int h = (lane & 1) ^ ((row >> 4) & 1);
+        const int R = n0 + row;
+        b_ok[j] = R < wrows;
+        const int RR = b_ok[j] ? R : 0;
+        const int o1 = fdiv(RR, a.o2_mul, a.o2_shr);
+        b_base[j] = o1 * (KH * KW * a.i1 * wblk) + (RR - o1 * a.o2) * 32 + h * 16;
+    }
+
+    // ---- K-step cursor: flat block kb = 2s (+1) -> (tap, channel block)
+    const int nsteps = (a.nkb + 1) >> 1;
+    int cur_c1 = 0, cur_tap = 0;  // block 2s
+    auto issue = [&](int s, int slot) {
+        int8_t *st = smem + slot * C::STAGE;
+        int c1b = cur_c1 + 1, tapb = cur_tap;  // block 2s + 1
+        if (c1b == a.i1) {
+            c1b = 0;
+            ++tapb;
+        }
+        const int kb0 = 2 * s;
+        const bool v0 = kb0 < a.nkb, v1 = kb0 + 1 < a.nkb;
+        const int ky0 = cur_tap / KW, kx0 = cur_tap - ky0 * KW;
+        const int ky1 = tapb / KW, kx1 = tapb - ky1 * KW;
+        const int dA0 = cur_c1 * HW * 32 + (ky0 * a.w + kx0) * 32;
+        const int dA1 = c1b * HW * 32 + (ky1 * a.w + kx1) * 32;
+        const int dB0 = kb0 * wblk, dB1 = dB0 + wblk;
+#pragma unroll
+        for (int j = 0; j < C::AI; ++j) {
+            const int q = j * NWV + wave;
+            const int blk = (j * NWV) / C::A_CH;  // A_CH is a multiple of NWV: independent of the wave
+            const int chunk = q % C::A_CH;
+            const bool v = blk ? v1 : v0;
+            const int tap = blk ? tapb : cur_tap;
+            const unsigned off =
+                (v && ((a_mask[j] >> tap) & 1u)) ? (unsigned)(a_base[j] + (blk ? dA1 : dA0)) : kOOB;
+            load16_lds(rsA, st + blk * (BM * 32) + chunk * 1024, off);
+        }
+#pragma unroll
+        for (int j = 0; j < C::BI; ++j) {
+            const int q = j * NWV + wave;
+            const int blk = q / C::B_CH;
+            const int chunk = q % C::B_CH;
+            const bool v = (blk ? v1 : v0) && b_ok[j];
+            const unsigned off = v ? (unsigned)(b_base[j] + (blk ? dB1 : dB0)) : kOOB;
+            load16_lds(rsB, st + BM * 64 + blk * (BN * 32) + chunk * 1024, off);
+        }
+        cur_c1 += 2;
+        while (cur_c1 >= a.i1) {
+            cur_c1 -= a.i1;
+            ++cur_tap;
+        }
+    };
+
+    issue(0, 0);
+
+    // ---- this wave's per-channel parameters and shortcut tile (landed by the first wait)
+    const int ch0 = n0 + wn0;
+    if (lane < 16) {
+        const bool v = ch0 + 4 * lane < a.oc;
+        const unsigned off = v ? (unsigned)(ch0 + 4 * lane) * 4 : kOOB;
+        load16_lds(make_rsrc(a.bias, (long long)a.oc * 4), Pw, off);
+        if (!a.out_i32) {
+            load16_lds(make_rsrc(a.mult, (long long)a.oc * 4), Pw + 256, off);
+            load16_lds(make_rsrc(a.shift, (long long)a.oc * 4), Pw + 512, off);
+        }
+    }
+    int8_t *const Rres = Pm + C::PARAM + wave * 4096;  // RES: per wave [64 pixels][64 B]
+    if (RES) {
+        const v4i rsR = make_rsrc(a.res + (long long)img0 * out_img, (long long)(a.n - img0) * out_img);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int p = m0 + wm0 + 16 * j + (lane >> 2);
+            const int oc = ch0 + (lane & 3) * 16;
+            unsigned off = kOOB;
+            if (p < a.m && oc < a.oc1 * 32) {
+                const int b = fdiv(p, a.howo_mul, a.howo_shr), hw = p - b * HoWo;
+                off = (unsigned)((((long long)(b - img0) * a.oc1 + (oc >> 5)) * HoWo + hw) * 32 + (oc & 31));
+            }
+            load16_lds_stream(rsR, Rres + j * 1024, off);
+        }
+    }
+
+    // ---- fragment addresses (stage-relative): lane (r = lane % 16, g = lane / 16) reads
+    //      pixel row 4(r%4) + r/4 of each 16-row group and weight row 4r + tn, K bytes [16g, 16g+16)
+    const int c = lane & 15;
+    const int g = lane >> 4;
+    int a_frag[4], b_frag[4];
+#pragma unroll
+    for (int tm = 0; tm < 4; ++tm) {
+        const int row = wm0 + 16 * tm + 4 * (c & 3) + (c >> 2);
+        a_frag[tm] = (g >> 1) * (BM * 32) + a_swz(row, g & 1);
+    }
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn) {
+        const int row = wn0 + 4 * c + tn;
+        b_frag[tn] = BM * 64 + (g >> 1) * (BN * 32) + b_swz(row, g & 1);
+    }
+
+    v4i acc[4][4];
+#pragma unroll
+    for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+        for (int tn = 0; tn < 4; ++tn) acc[tm][tn] = (v4i){0, 0, 0, 0};
+
+    for (int s = 0; s < nsteps; ++s) {
+        wait_vmcnt<0>();  // this wave's DMAs of stage s (and, at s = 0, its tile inputs)
+        ring_barrier();   // ... and every other wave's; stage s-1's slot is free again
+        if (s + 1 < nsteps) issue(s + 1, (s + 1) & 1);
+        const int8_t *st = smem + (s & 1) * C::STAGE;
+        v4i af[4], bf[4];
+#pragma unroll
+        for (int tm = 0; tm < 4; ++tm) af[tm] = *(const v4i *)(st + a_frag[tm]);
+#pragma unroll
+        for (int tn = 0; tn < 4; ++tn) bf[tn] = *(const v4i *)(st + b_frag[tn]);
+#pragma unroll
+        for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+            for (int tn = 0; tn < 4; ++tn)
+                acc[tm][tn] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[tm], bf[tn], acc[tm][tn], 0, 0, 0);
+    }
+
+    // ---- epilogue: lane (g, c) holds pixel rows 16tm + 4i + g and channels 4c .. 4c+3 of the wave's tile
+    const int ocl = ch0 + 4 * c;
+    const v4i bias4 = *(const v4i *)(Pw + c * 16);
+    const int pbase = m0 + wm0;
+    if (a.out_i32) {
+        int32_t *y = (int32_t *)a.y;
+        const bool vec = (a.oc & 3) == 0 && ocl + 3 < a.oc;
+#pragma unroll
+        for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int p = pbase + 16 * tm + 4 * i + g;
+                if (p >= a.m) continue;
+                const long long off = (long long)p * a.oc + ocl;
+                const v4i v = {acc[tm][0][i] + bias4.x, acc[tm][1][i] + bias4.y, acc[tm][2][i] + bias4.z,
+                               acc[tm][3][i] + bias4.w};
+                if (vec) {
+                    *(v4i *)(y + off) = v;
+                } else {
+#pragma unroll
+                    for (int tn = 0; tn < 4; ++tn)
+                        if (ocl + tn < a.oc) y[off + tn] = v[tn];
+                }
+            }
+        return;
+    }
+    const v4i mult4 = *(const v4i *)(Pw + 256 + c * 16);
+    const v4i shift4 = *(const v4i *)(Pw + 512 + c * 16);
+    int bias[4], mul[4], rnd[4], shm[4], shf[4];
+    bool fast_lane = true;
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn) {
+        const bool v = ocl + tn < a.oc;  // padded channels: bias = mult = 0 gives 0
+        bias[tn] = v ? bias4[tn] : 0;
+        mul[tn] = v ? mult4[tn] : 0;
+        shf[tn] = v ? shift4[tn] : 2;
+        fast_lane = fast_lane && shf[tn] >= 2;
+        rnd[tn] = 1 << ((shf[tn] - 2) & 31);
+        shm[tn] = shf[tn] - 1;
+    }
+    // staging: the shortcut tile itself (requantised in place), else the ring slot no wave reads any more
+    int8_t *const Rw = RES ? Rres : smem + (nsteps & 1) * C::STAGE + wave * 4096;
+    int8_t *rbase = Rw + g * 64 + 4 * c;
+    if (!__all(fast_lane))
+        requant_tile<0, RES, RELU, 64>(acc, rbase, bias, mul, rnd, shm, shf);
+    else if (!RES && RELU)
+        requant_tile<1, RES, RELU, 64>(acc, rbase, bias, mul, rnd, shm, shf);
+    else
+        requant_tile<2, RES, RELU, 64>(acc, rbase, bias, mul, rnd, shm, shf);
+    wave_lds_sync();
+
+    // 16-byte stores of the wave's 64 pixels x 64 channels
+    int8_t *y = (int8_t *)a.y;
+    const int k = lane & 3;
+    const int och = ch0 + 16 * k;  // first channel of this lane's chunk
+    if (och >= a.oc1 * 32 || pbase >= a.m) return;
+    const int b0 = fdiv(pbase, a.howo_mul, a.howo_shr);
+    const int hw0 = pbase - b0 * HoWo;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int prow = 16 * j + (lane >> 2);
+        if (pbase + prow >= a.m) break;
+        int b = b0, hw = hw0 + prow;
+        while (hw >= HoWo) {
+            hw -= HoWo;
+            ++b;
+        }
+        const v4i v = *(const v4i *)(Rw + prow * 64 + 16 * k);
+        int8_t *dst = y + (((long long)b * a.oc1 + (och >> 5)) * HoWo + hw) * 32 + (och & 31);
+        if (RES)
+            store16_stream(dst, v);
+        else
+            *(v4i *)dst = v;
+    }
+}
+
+template <int KH, int KW, int BM, int BN, bool RES>
+hipError_t launch_ig(const ConvArgs &a, hipStream_t s)
+{
+    const int tiles_n = (a.oc1 * 32 + BN - 1) / BN;
+    const long long tiles_m = (a.m + BM - 1) / BM;
+    const long long per = (tiles_m + 7) / 8;
+    const long long grid = 8 * per * tiles_n;
+    if (grid <= 0) return hipSuccess;
+    if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    // activation offsets are taken relative to a tile's first image and must fit 31 bits
+    const long long in_img = (long long)a.i1 * a.h * a.w * 32;
+    const long long imgs = BM / ((long long)a.ho * a.wo) + 2;
+    if (imgs * in_img >= 0x7fffffffLL) return hipErrorInvalidValue;
+    if (a.relu)
+        hipLaunchKernelGGL((igemm_kernel<KH, KW, BM, BN, RES, true>), dim3((unsigned)grid), dim3(256), 0, s, a,
+                           tiles_n, (int)per);
+    else
+        hipLaunchKernelGGL((igemm_kernel<KH, KW, BM, BN, RES, false>), dim3((unsigned)grid), dim3(256), 0, s, a,
+                           tiles_n, (int)per);
+    return hipGetLastError();
+}
+
+template <int KH, int KW>
+hipError_t launch_ig_k(const ConvArgs &a, hipStream_t s)
+{
+    const bool wide = a.oc1 * 32 > 64;
+    if (a.residual) return wide ? launch_ig<KH, KW, 128, 128, true>(a, s) : launch_ig<KH, KW, 256, 64, true>(a, s);
+    return wide ? launch_ig<KH, KW, 128, 128, false>(a, s) : launch_ig<KH, KW, 256, 64, false>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_igemm(const ConvArgs &a, int kh, int kw, hipStream_t s)
+{
+    if (kh == 1 && kw == 1) return launch_ig_k<1, 1>(a, s);
+    if (kh == 3 && kw == 3) return launch_ig_k<3, 3>(a, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace ifx
