@@ -23,7 +23,7 @@ LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libifx.so")
 ARCH = "gfx950"
 
-SOURCES = ["conv.hip", "igemm.hip", "conv1x1.hip", "fold.hip", "stem.hip", "head.hip", "pack.hip", "api.cpp"]
+SOURCES = ["igemm.hip", "conv1x1.hip", "fold.hip", "stem.hip", "head.hip", "pack.hip", "api.cpp"]
 # gfx950 device code is built without packed-FP32 instructions; the host pass
 # warns that it does not know the feature, which is harmless.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

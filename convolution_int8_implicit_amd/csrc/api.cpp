@@ -96,6 +96,9 @@ ifx_status hip_status(hipError_t e)
     return IFX_E_HIP;
 }
 
+ifx::ConvArgs conv_args(const ifx_conv_desc *d, const Dims &dm, const int8_t *x, const int8_t *w, const int32_t *bias,
+                        const int32_t *mult, const int32_t *shift, const int8_t *res, void *y);
+
 // Launch one validated convolution.
 ifx_status run_conv(const ifx_conv_desc *d, Kind kind, const Dims &dm, const int8_t *x, const int8_t *w,
                     const int32_t *bias, const int32_t *mult, const int32_t *shift, const int8_t *res, void *y,
@@ -121,6 +124,13 @@ ifx_status run_conv(const ifx_conv_desc *d, Kind kind, const Dims &dm, const int
         a.relu = (d->flags & IFX_RELU) ? 1 : 0;
         return hip_status(ifx::launch_stem(a, s));
     }
+    return hip_status(ifx::launch_conv(conv_args(d, dm, x, w, bias, mult, shift, res, y), d->kh, d->kw, s));
+}
+
+// Kernel arguments of a validated non-stem convolution.
+ifx::ConvArgs conv_args(const ifx_conv_desc *d, const Dims &dm, const int8_t *x, const int8_t *w, const int32_t *bias,
+                        const int32_t *mult, const int32_t *shift, const int8_t *res, void *y)
+{
     ifx::ConvArgs a;
     a.x = x;
     a.wt = w;
@@ -148,7 +158,7 @@ ifx_status run_conv(const ifx_conv_desc *d, Kind kind, const Dims &dm, const int
     ifx::fastdiv_magic((unsigned)(dm.ho * dm.wo), &a.howo_mul, &a.howo_shr);
     ifx::fastdiv_magic((unsigned)dm.wo, &a.wo_mul, &a.wo_shr);
     ifx::fastdiv_magic((unsigned)a.o2, &a.o2_mul, &a.o2_shr);
-    return hip_status(ifx::launch_conv(a, d->kh, d->kw, s));
+    return a;
 }
 
 ifx_status check_conv_ptrs(const ifx_conv_desc *d, const int8_t *x, const int8_t *w, const int32_t *bias,
@@ -241,6 +251,14 @@ ifx_status run_block(const ifx_block_params *p, const BlockPlan &plan, int n, co
     if (st != IFX_OK) return st;
     const int8_t *res = x;
     if (p->has_proj) {
+        if (d[2].kh == 1 && d[2].kw == 1 && d[3].kh == 1 && d[3].kw == 1) {
+            // conv3 and the projection in one kernel: the shortcut never goes through HBM
+            const ifx::ConvArgs a = conv_args(&d[2], plan.dims[2], t2, p->w_blk[2], p->bias[2], p->mult[2],
+                                              p->shift[2], nullptr, y);
+            const ifx::ConvArgs pj = conv_args(&d[3], plan.dims[3], x, p->w_blk[3], p->bias[3], p->mult[3],
+                                               p->shift[3], nullptr, nullptr);
+            return hip_status(ifx::launch_conv_proj(a, pj, s));
+        }
         st = run_conv(&d[3], kGeneric, plan.dims[3], x, p->w_blk[3], p->bias[3], p->mult[3], p->shift[3], nullptr,
                       sc, s);
         if (st != IFX_OK) return st;
@@ -513,8 +531,7 @@ ifx_status ifx_net_graph_create(const ifx_net_params *p, const int8_t *x_blk, in
     if (st != IFX_OK) return st;
     if (!x_blk || !logits || !ws) return IFX_E_NULL;
     if (ws_bytes < net_ws_bytes(plan)) return IFX_E_WORKSPACE;
-    // one-time device queries of the launchers happen now, outside the capture
-    ifx::warm_conv_queries();
+    // the stem launcher's one-time device query happens now, outside the capture
     st = hip_status(ifx::warm_stem_queries());
     if (st != IFX_OK) return st;
 

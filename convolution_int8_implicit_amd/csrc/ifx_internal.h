@@ -68,10 +68,11 @@ struct FoldArgs {
 };
 
 hipError_t launch_conv(const ConvArgs &a, int kh, int kw, hipStream_t s);
-// General implicit-GEMM kernel (igemm.hip)
-hipError_t launch_igemm(const ConvArgs &a, int kh, int kw, hipStream_t s);
-// Run the launchers' one-time device queries now (before a stream capture).
-void warm_conv_queries();
+// The 1x1 shortcut conv `a` (RESIDUAL) of a bottleneck fused with its 1x1 projection shortcut
+// `pj` (same output pixels and channels, no ReLU): the projection's requantised output is the
+// shortcut and never reaches HBM; a.res is not read.
+hipError_t launch_conv_proj(const ConvArgs &a, const ConvArgs &pj, hipStream_t s);
+// Run the stem launcher's one-time device query now (before a stream capture).
 hipError_t warm_stem_queries();
 hipError_t launch_fold_bn(const FoldArgs &f, int32_t *bias, int32_t *mult, int32_t *shift, int32_t *status,
                           hipStream_t s);

@@ -33,7 +33,7 @@
 namespace ifx {
 namespace {
 
-template <int BM, int BN>
+template <int BM, int BN, int ST>
 struct IgCfg {
     static constexpr int WAVES_M = BM / 64;
     static constexpr int WAVES = WAVES_M * (BN / 64);
@@ -46,7 +46,9 @@ struct IgCfg {
     static_assert(AI * WAVES == 2 * A_CH && BI * WAVES == 2 * B_CH && A_CH % WAVES == 0, "whole DMAs");
     static constexpr int STAGE = (BM + BN) * 64;  // A: [2][BM][32 B], then B: [2][BN][32 B]
     static constexpr int PARAM = WAVES * 768;     // per wave: bias, mult, shift of its 64 channels
-    static constexpr int lds(bool res) { return 2 * STAGE + PARAM + (res ? BM * BN : 0); }
+    static constexpr int LPS = AI + BI;          // DMAs per wave per stage
+    // ring | parameters | shortcut tile (RES) | parameters of the projection (PROJ)
+    static constexpr int lds(bool res) { return ST * STAGE + PARAM + (res ? BM * BN : 0); }  // ring | params | shortcut
     static constexpr int wg_per_cu(bool res) { return kLdsBytes / lds(res) > 4 ? 4 : kLdsBytes / lds(res); }
 };
 
@@ -72,20 +74,55 @@ __device__ __forceinline__ int dma_row(int lane)
     return 4 * line + (((lane & 7) >> 1) ^ (line & 3));
 }
 
-template <int KH, int KW, int BM, int BN, bool RES, bool RELU>
-__global__ __launch_bounds__(256, (IgCfg<BM, BN>::wg_per_cu(RES)))
-void igemm_kernel(ConvArgs a, int tiles_n, int per_xcd)
+// Requantise the wave's accumulators (MODE picked by a wave vote on the shifts) into the LDS
+// tile at rbase (row stride 64 B), adding the shortcut bytes already there when RES.
+template <bool RES, bool RELU>
+__device__ __forceinline__ void requant_to_lds(const v4i (&acc)[4][4], int8_t *rbase, const int8_t *Pw, int c,
+                                               int ocl, int oc)
 {
-    using C = IgCfg<BM, BN>;
+    const v4i bias4 = *(const v4i *)(Pw + c * 16);
+    const v4i mult4 = *(const v4i *)(Pw + 256 + c * 16);
+    const v4i shift4 = *(const v4i *)(Pw + 512 + c * 16);
+    int bias[4], mul[4], rnd[4], shm[4], shf[4];
+    bool fast_lane = true;
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn) {
+        const bool v = ocl + tn < oc;  // padded channels: bias = mult = 0 gives 0
+        bias[tn] = v ? bias4[tn] : 0;
+        mul[tn] = v ? mult4[tn] : 0;
+        shf[tn] = v ? shift4[tn] : 2;
+        fast_lane = fast_lane && shf[tn] >= 2;
+        rnd[tn] = 1 << ((shf[tn] - 2) & 31);
+        shm[tn] = shf[tn] - 1;
+    }
+    if (!__all(fast_lane))
+        requant_tile<0, RES, RELU, 64>(acc, rbase, bias, mul, rnd, shm, shf);
+    else if (!RES && RELU)
+        requant_tile<1, RES, RELU, 64>(acc, rbase, bias, mul, rnd, shm, shf);
+    else
+        requant_tile<2, RES, RELU, 64>(acc, rbase, bias, mul, rnd, shm, shf);
+}
+
+// One convolution `a` (with its epilogue), or, when PROJ, the last 1x1 convolution `a` of a
+// bottleneck whose shortcut is the 1x1 projection `pj` of the block input: the tile's
+// projection is computed first and requantised (no ReLU) into the LDS that otherwise receives
+// a shortcut tile, so the shortcut never goes through HBM.
+template <int KH, int KW, int BM, int BN, int ST, bool RES, bool RELU, bool PROJ>
+__global__ __launch_bounds__(256, (IgCfg<BM, BN, ST>::wg_per_cu(RES)))
+void igemm_kernel(ConvArgs a, ConvArgs pj, int tiles_n, int per_xcd)
+{
+    using C = IgCfg<BM, BN, ST>;
     constexpr int NWV = C::WAVES;
+    static_assert(!PROJ || (RES && KH == 1 && KW == 1), "a projection shortcut feeds a 1x1 shortcut conv");
     __shared__ __attribute__((aligned(1024))) int8_t smem[C::lds(RES)];
-    int8_t *const Pm = smem + 2 * C::STAGE;
+    int8_t *const Pm = smem + ST * C::STAGE;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm0 = (wave % C::WAVES_M) * 64;
     const int wn0 = (wave / C::WAVES_M) * 64;
-    int8_t *const Pw = Pm + wave * 768;
+    int8_t *const Pw = Pm + wave * 768;                 // bias, mult, shift of the wave's 64 channels
+    int8_t *const Rres = Pm + C::PARAM + wave * 4096;  // RES: the wave's [64 pixels][64 B] shortcut
 
     // tile: XCD x (blockIdx & 7) owns M-tiles [x * per_xcd, (x + 1) * per_xcd), so neighbouring
     // pixel tiles (which share 3x3 halo rows) and the N-tiles of one pixel tile share an L2
@@ -95,119 +132,152 @@ void igemm_kernel(ConvArgs a, int tiles_n, int per_xcd)
     const int m0 = (xcd * per_xcd + mq) * BM;
     if (m0 >= a.m) return;
     const int n0 = (kk - mq * tiles_n) * BN;
+    const int ch0 = n0 + wn0;
 
     const int HoWo = a.ho * a.wo;
-    const int HW = a.h * a.w;
-    const long long in_img = (long long)a.i1 * HW * 32;
     const long long out_img = (long long)a.oc1 * HoWo * 32;
     const int img0 = fdiv(m0, a.howo_mul, a.howo_shr);
-    const v4i rsA = make_rsrc(a.x + (long long)img0 * in_img, (long long)(a.n - img0) * in_img);
-    const int wrows = ((a.oc + a.o2 - 1) / a.o2) * a.o2;
-    const v4i rsB = make_rsrc(a.wt, (long long)wrows * KH * KW * a.i1 * 32);
 
-    // ---- per-lane DMA plans.  Activation DMA j of wave w fills chunk (4j + w) % A_CH of
-    //      block (4j + w) / A_CH: the lane's pixel, its tap-validity mask and base offset.
-    int a_base[C::AI];
+    // ---- fragment addresses (stage-relative): lane (r = lane % 16, g = lane / 16) reads
+    //      pixel row 4(r%4) + r/4 of each 16-row group and weight row 4r + tn, K bytes [16g, 16g+16)
+    const int c = lane & 15;
+    const int g = lane >> 4;
+    // rows 16 apart sit 4 lines (512 B) apart with the same slot
+    const int a_frag = (g >> 1) * (BM * 32) + a_swz(wm0 + 4 * (c & 3) + (c >> 2), g & 1);
+    int b_frag[4];
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn) {
+        const int row = wn0 + 4 * c + tn;
+        b_frag[tn] = BM * 64 + (g >> 1) * (BN * 32) + b_swz(row, g & 1);
+    }
+
+    v4i acc[4][4];
+
+    // ---- per-lane DMA plans of convolution q.  Activation DMA j of wave w fills chunk
+    //      (4j + w) % A_CH of block (4j + w) / A_CH: the lane's pixel, its tap-validity mask and
+    //      base offset.  Weight DMA j likewise for B_CH.
+    // geometry of the convolution whose K-steps are being issued
+    int HW = 0, wblk = 0, qi1 = 0, qnkb = 0, qw = 0;
+    v4i rsA, rsB;
+    int a_base[C::AI], b_base[C::BI];
     unsigned a_mask[C::AI];
-#pragma unroll
-    for (int j = 0; j < C::AI; ++j) {
-        const int chunk = (j * NWV + wave) % C::A_CH;
-        const int row = chunk * 32 + dma_row(lane);
-        const int h = (lane & 1) ^ (row & 1);
-        const int p = m0 + row;
-        const bool ok = p < a.m;
-        const int pp = ok ? p : m0;
-        const int b = fdiv(pp, a.howo_mul, a.howo_shr);
-        const int rem = pp - b * HoWo;
-        const int oy = fdiv(rem, a.wo_mul, a.wo_shr);
-        const int ox = rem - oy * a.wo;
-        const int iy0 = oy * a.stride - a.pad;
-        const int ix0 = ox * a.stride - a.pad;
-        a_base[j] = (int)((long long)(b - img0) * in_img) + (iy0 * a.w + ix0) * 32 + h * 16;
-        unsigned mask = 0;
-#pragma unroll
-        for (int ky = 0; ky < KH; ++ky)
-#pragma unroll
-            for (int kx = 0; kx < KW; ++kx)
-                if ((unsigned)(iy0 + ky) < (unsigned)a.h && (unsigned)(ix0 + kx) < (unsigned)a.w)
-                    mask |= 1u << (ky * KW + kx);
-        a_mask[j] = ok ? mask : 0u;
-    }
-    // Weight DMA j of wave w fills chunk (4j + w) % B_CH of block (4j + w) / B_CH.
-    int b_base[C::BI];
     bool b_ok[C::BI];
-    const int wblk = a.o2 * 32;  // bytes of one (tap, channel-block) slice of an O1 group
+    auto plan = [&](const ConvArgs &q) {
+        HW = q.h * q.w;
+        qi1 = q.i1;
+        qnkb = q.nkb;
+        qw = q.w;
+        const long long in_img = (long long)q.i1 * HW * 32;
+        rsA = make_rsrc(q.x + (long long)img0 * in_img, (long long)(q.n - img0) * in_img);
+        const int wrows = ((q.oc + q.o2 - 1) / q.o2) * q.o2;
+        rsB = make_rsrc(q.wt, (long long)wrows * KH * KW * q.i1 * 32);
+        wblk = q.o2 * 32;  // bytes of one (tap, channel-block) slice of an O1 group
 #pragma unroll
-    for (int j = 0; j < C::BI; ++j) {
-        const int chunk = (j * NWV + wave) % C::B_CH;
-        const int row = chunk * 32 + dma_row(lane);
-        const int h = (lane & 1) ^ ((row >> 4) & 1);
-        const int R = n0 + row;
-        b_ok[j] = R < wrows;
-        const int RR = b_ok[j] ? R : 0;
-        const int o1 = fdiv(RR, a.o2_mul, a.o2_shr);
-        b_base[j] = o1 * (KH * KW * a.i1 * wblk) + (RR - o1 * a.o2) * 32 + h * 16;
-    }
+        for (int j = 0; j < C::AI; ++j) {
+            const int chunk = (j * NWV + wave) % C::A_CH;
+            const int row = chunk * 32 + dma_row(lane);
+            const int h = (lane & 1) ^ (row & 1);
+            const int p = m0 + row;
+            const bool ok = p < q.m;
+            const int pp = ok ? p : m0;
+            const int b = fdiv(pp, q.howo_mul, q.howo_shr);
+            const int rem = pp - b * HoWo;
+            const int oy = fdiv(rem, q.wo_mul, q.wo_shr);
+            const int ox = rem - oy * q.wo;
+            const int iy0 = oy * q.stride - q.pad;
+            const int ix0 = ox * q.stride - q.pad;
+            a_base[j] = (int)((long long)(b - img0) * in_img) + (iy0 * q.w + ix0) * 32 + h * 16;
+            unsigned mask = 0;
+#pragma unroll
+            for (int ky = 0; ky < KH; ++ky)
+#pragma unroll
+                for (int kx = 0; kx < KW; ++kx)
+                    if ((unsigned)(iy0 + ky) < (unsigned)q.h && (unsigned)(ix0 + kx) < (unsigned)q.w)
+                        mask |= 1u << (ky * KW + kx);
+            a_mask[j] = ok ? mask : 0u;
+        }
+#pragma unroll
+        for (int j = 0; j < C::BI; ++j) {
+            const int chunk = (j * NWV + wave) % C::B_CH;
+            const int row = chunk * 32 + dma_row(lane);
+            const int h = (lane & 1) ^ ((row >> 4) & 1);
+            const int R = n0 + row;
+            b_ok[j] = R < wrows;
+            const int RR = b_ok[j] ? R : 0;
+            const int o1 = fdiv(RR, q.o2_mul, q.o2_shr);
+            b_base[j] = o1 * (KH * KW * q.i1 * wblk) + (RR - o1 * q.o2) * 32 + h * 16;
+        }
+    };
 
-    // ---- K-step cursor: flat block kb = 2s (+1) -> (tap, channel block)
-    const int nsteps = (a.nkb + 1) >> 1;
-    int cur_c1 = 0, cur_tap = 0;  // block 2s
-    auto issue = [&](int s, int slot) {
+    // ---- the K-step stream: the steps of pj (PROJ only), then those of a.  Step s covers
+    //      the flat 32-channel blocks kb = 2s, 2s+1 of its convolution, kb -> (tap, channel block).
+    const int n1 = PROJ ? (pj.nkb + 1) >> 1 : 0;
+    const int nsteps = n1 + ((a.nkb + 1) >> 1);
+    int iss = 0;                  // next step to issue
+    int cur_c1 = 0, cur_tap = 0;  // block 2s of that step, within its convolution
+    if (PROJ)
+        plan(pj);
+    else
+        plan(a);
+    auto issue = [&](int slot) {
+        const int s = iss - (iss >= n1 ? n1 : 0);
+        ++iss;
         int8_t *st = smem + slot * C::STAGE;
         int c1b = cur_c1 + 1, tapb = cur_tap;  // block 2s + 1
-        if (c1b == a.i1) {
+        if (c1b == qi1) {
             c1b = 0;
             ++tapb;
         }
         const int kb0 = 2 * s;
-        const bool v0 = kb0 < a.nkb, v1 = kb0 + 1 < a.nkb;
+        const bool v0 = kb0 < qnkb, v1 = kb0 + 1 < qnkb;
         const int ky0 = cur_tap / KW, kx0 = cur_tap - ky0 * KW;
         const int ky1 = tapb / KW, kx1 = tapb - ky1 * KW;
-        const int dA0 = cur_c1 * HW * 32 + (ky0 * a.w + kx0) * 32;
-        const int dA1 = c1b * HW * 32 + (ky1 * a.w + kx1) * 32;
+        const int dA0 = cur_c1 * HW * 32 + (ky0 * qw + kx0) * 32;
+        const int dA1 = c1b * HW * 32 + (ky1 * qw + kx1) * 32;
         const int dB0 = kb0 * wblk, dB1 = dB0 + wblk;
 #pragma unroll
         for (int j = 0; j < C::AI; ++j) {
-            const int q = j * NWV + wave;
             const int blk = (j * NWV) / C::A_CH;  // A_CH is a multiple of NWV: independent of the wave
-            const int chunk = q % C::A_CH;
-            const bool v = blk ? v1 : v0;
-            const int tap = blk ? tapb : cur_tap;
-            const unsigned off =
-                (v && ((a_mask[j] >> tap) & 1u)) ? (unsigned)(a_base[j] + (blk ? dA1 : dA0)) : kOOB;
+            const int chunk = (j * NWV + wave) % C::A_CH;
+            // an invalid lane gets bit 31 set: past every buffer range, so its DMA writes zeros
+            const unsigned bad = (blk ? v1 : v0) ? (~a_mask[j] >> (blk ? tapb : cur_tap)) & 1u : 1u;
+            const unsigned off = (unsigned)(a_base[j] + (blk ? dA1 : dA0)) | (bad << 31);
             load16_lds(rsA, st + blk * (BM * 32) + chunk * 1024, off);
         }
 #pragma unroll
         for (int j = 0; j < C::BI; ++j) {
-            const int q = j * NWV + wave;
-            const int blk = q / C::B_CH;
-            const int chunk = q % C::B_CH;
+            const int qq = j * NWV + wave;
+            const int blk = qq / C::B_CH;
+            const int chunk = qq % C::B_CH;
             const bool v = (blk ? v1 : v0) && b_ok[j];
             const unsigned off = v ? (unsigned)(b_base[j] + (blk ? dB1 : dB0)) : kOOB;
             load16_lds(rsB, st + BM * 64 + blk * (BN * 32) + chunk * 1024, off);
         }
         cur_c1 += 2;
-        while (cur_c1 >= a.i1) {
-            cur_c1 -= a.i1;
+        while (cur_c1 >= qi1) {
+            cur_c1 -= qi1;
             ++cur_tap;
         }
     };
 
-    issue(0, 0);
-
-    // ---- this wave's per-channel parameters and shortcut tile (landed by the first wait)
-    const int ch0 = n0 + wn0;
-    if (lane < 16) {
-        const bool v = ch0 + 4 * lane < a.oc;
-        const unsigned off = v ? (unsigned)(ch0 + 4 * lane) * 4 : kOOB;
-        load16_lds(make_rsrc(a.bias, (long long)a.oc * 4), Pw, off);
-        if (!a.out_i32) {
-            load16_lds(make_rsrc(a.mult, (long long)a.oc * 4), Pw + 256, off);
-            load16_lds(make_rsrc(a.shift, (long long)a.oc * 4), Pw + 512, off);
+    issue(0);
+    // per-channel parameters (of pj first, PROJ) and the shortcut part of this wave
+    auto issue_params = [&](const ConvArgs &q, int8_t *dst) {
+        if (lane < 16) {
+            const bool v = ch0 + 4 * lane < q.oc;
+            const unsigned off = v ? (unsigned)(ch0 + 4 * lane) * 4 : kOOB;
+            load16_lds(make_rsrc(q.bias, (long long)q.oc * 4), dst, off);
+            if (!q.out_i32) {
+                load16_lds(make_rsrc(q.mult, (long long)q.oc * 4), dst + 256, off);
+                load16_lds(make_rsrc(q.shift, (long long)q.oc * 4), dst + 512, off);
+            }
         }
-    }
-    int8_t *const Rres = Pm + C::PARAM + wave * 4096;  // RES: per wave [64 pixels][64 B]
-    if (RES) {
+    };
+    if (PROJ)
+        issue_params(pj, Pw);
+    else
+        issue_params(a, Pw);
+    if (RES && !PROJ) {
         const v4i rsR = make_rsrc(a.res + (long long)img0 * out_img, (long long)(a.n - img0) * out_img);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -221,37 +291,48 @@ void igemm_kernel(ConvArgs a, int tiles_n, int per_xcd)
             load16_lds_stream(rsR, Rres + j * 1024, off);
         }
     }
-
-    // ---- fragment addresses (stage-relative): lane (r = lane % 16, g = lane / 16) reads
-    //      pixel row 4(r%4) + r/4 of each 16-row group and weight row 4r + tn, K bytes [16g, 16g+16)
-    const int c = lane & 15;
-    const int g = lane >> 4;
-    int a_frag[4], b_frag[4];
+    // Stages after the tile inputs, so the first wait needs no count of them.  A stream that fits
+    // the ring (nsteps <= ST, the short 1x1 convolutions) is requested whole, up front; a longer
+    // one keeps ST-1 stages in flight and requests stage s+ST-1 at step s.
+    const bool upfront = nsteps <= ST;
+    if (upfront) {
+        for (int s = 1; s < nsteps; ++s) {
+            if (PROJ && s == n1) {  // the stream moves on to a's first step
+                plan(a);
+                cur_c1 = 0;
+                cur_tap = 0;
+            }
+            issue(s);
+        }
+    } else {
 #pragma unroll
-    for (int tm = 0; tm < 4; ++tm) {
-        const int row = wm0 + 16 * tm + 4 * (c & 3) + (c >> 2);
-        a_frag[tm] = (g >> 1) * (BM * 32) + a_swz(row, g & 1);
-    }
-#pragma unroll
-    for (int tn = 0; tn < 4; ++tn) {
-        const int row = wn0 + 4 * c + tn;
-        b_frag[tn] = BM * 64 + (g >> 1) * (BN * 32) + b_swz(row, g & 1);
+        for (int s = 1; s < ST - 1; ++s)
+            if (s < nsteps) issue(s);
     }
 
-    v4i acc[4][4];
+    // ---- epilogue geometry: lane (g, c) holds pixel rows 16tm + 4i + g and channels 4c .. 4c+3
+    const int ocl = ch0 + 4 * c;
+    const int pbase = m0 + wm0;
+
 #pragma unroll
     for (int tm = 0; tm < 4; ++tm)
 #pragma unroll
         for (int tn = 0; tn < 4; ++tn) acc[tm][tn] = (v4i){0, 0, 0, 0};
 
-    for (int s = 0; s < nsteps; ++s) {
-        wait_vmcnt<0>();  // this wave's DMAs of stage s (and, at s = 0, its tile inputs)
-        ring_barrier();   // ... and every other wave's; stage s-1's slot is free again
-        if (s + 1 < nsteps) issue(s + 1, (s + 1) & 1);
-        const int8_t *st = smem + (s & 1) * C::STAGE;
+    static_assert(ST == 2, "the up-front waits below count one stage in flight");
+    auto step = [&](int s) {
+        // this wave's DMAs of stage s (and, at s = 0, the tile inputs); stage s+1 may stay in flight
+        // when it was requested before them (up front), never when it was requested at step s-1
+        if (upfront && s + 1 < nsteps)
+            wait_vmcnt<C::LPS>();
+        else
+            wait_vmcnt<0>();
+        ring_barrier();  // ... and every other wave's; stage s-1's slot is free again
+        if (!upfront && s + ST - 1 < nsteps) issue((s + ST - 1) % ST);
+        const int8_t *st = smem + (s % ST) * C::STAGE;
         v4i af[4], bf[4];
 #pragma unroll
-        for (int tm = 0; tm < 4; ++tm) af[tm] = *(const v4i *)(st + a_frag[tm]);
+        for (int tm = 0; tm < 4; ++tm) af[tm] = *(const v4i *)(st + a_frag + 512 * tm);
 #pragma unroll
         for (int tn = 0; tn < 4; ++tn) bf[tn] = *(const v4i *)(st + b_frag[tn]);
 #pragma unroll
@@ -259,13 +340,30 @@ void igemm_kernel(ConvArgs a, int tiles_n, int per_xcd)
 #pragma unroll
             for (int tn = 0; tn < 4; ++tn)
                 acc[tm][tn] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[tm], bf[tn], acc[tm][tn], 0, 0, 0);
+    };
+    if (PROJ) {
+        for (int s = 0; s + 1 < n1; ++s) step(s);
+        if (!upfront) {
+            plan(a);  // the last projection step requests a's first stage
+            cur_c1 = 0;
+            cur_tap = 0;
+        }
+        step(n1 - 1);
+        // the projection is complete: its requantised output (no ReLU) is the shortcut.  The
+        // parameters of a then replace the projection's in LDS (the next step's wait covers them).
+        requant_to_lds<false, false>(acc, Rres + g * 64 + 4 * c, Pw, c, ocl, pj.oc);
+        issue_params(a, Pw);
+#pragma unroll
+        for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+            for (int tn = 0; tn < 4; ++tn) acc[tm][tn] = (v4i){0, 0, 0, 0};
+        for (int s = n1; s < nsteps; ++s) step(s);
+    } else {
+        for (int s = 0; s < nsteps; ++s) step(s);
     }
-
-    // ---- epilogue: lane (g, c) holds pixel rows 16tm + 4i + g and channels 4c .. 4c+3 of the wave's tile
-    const int ocl = ch0 + 4 * c;
-    const v4i bias4 = *(const v4i *)(Pw + c * 16);
-    const int pbase = m0 + wm0;
+    if (PROJ) wait_vmcnt<0>();  // a's parameters, requested at step n1, may be the last DMA
     if (a.out_i32) {
+        const v4i bias4 = *(const v4i *)(Pw + c * 16);
         int32_t *y = (int32_t *)a.y;
         const bool vec = (a.oc & 3) == 0 && ocl + 3 < a.oc;
 #pragma unroll
@@ -287,29 +385,9 @@ void igemm_kernel(ConvArgs a, int tiles_n, int per_xcd)
             }
         return;
     }
-    const v4i mult4 = *(const v4i *)(Pw + 256 + c * 16);
-    const v4i shift4 = *(const v4i *)(Pw + 512 + c * 16);
-    int bias[4], mul[4], rnd[4], shm[4], shf[4];
-    bool fast_lane = true;
-#pragma unroll
-    for (int tn = 0; tn < 4; ++tn) {
-        const bool v = ocl + tn < a.oc;  // padded channels: bias = mult = 0 gives 0
-        bias[tn] = v ? bias4[tn] : 0;
-        mul[tn] = v ? mult4[tn] : 0;
-        shf[tn] = v ? shift4[tn] : 2;
-        fast_lane = fast_lane && shf[tn] >= 2;
-        rnd[tn] = 1 << ((shf[tn] - 2) & 31);
-        shm[tn] = shf[tn] - 1;
-    }
     // staging: the shortcut tile itself (requantised in place), else the ring slot no wave reads any more
-    int8_t *const Rw = RES ? Rres : smem + (nsteps & 1) * C::STAGE + wave * 4096;
-    int8_t *rbase = Rw + g * 64 + 4 * c;
-    if (!__all(fast_lane))
-        requant_tile<0, RES, RELU, 64>(acc, rbase, bias, mul, rnd, shm, shf);
-    else if (!RES && RELU)
-        requant_tile<1, RES, RELU, 64>(acc, rbase, bias, mul, rnd, shm, shf);
-    else
-        requant_tile<2, RES, RELU, 64>(acc, rbase, bias, mul, rnd, shm, shf);
+    int8_t *const Rw = RES ? Rres : smem + (nsteps % ST) * C::STAGE + wave * 4096;
+    requant_to_lds<RES, RELU>(acc, Rw + g * 64 + 4 * c, Pw, c, ocl, a.oc);
     wave_lds_sync();
 
     // 16-byte stores of the wave's 64 pixels x 64 channels
@@ -337,8 +415,8 @@ void igemm_kernel(ConvArgs a, int tiles_n, int per_xcd)
     }
 }
 
-template <int KH, int KW, int BM, int BN, bool RES>
-hipError_t launch_ig(const ConvArgs &a, hipStream_t s)
+template <int KH, int KW, int BM, int BN, int ST, bool RES, bool PROJ>
+hipError_t launch_ig(const ConvArgs &a, const ConvArgs &pj, hipStream_t s)
 {
     const int tiles_n = (a.oc1 * 32 + BN - 1) / BN;
     const long long tiles_m = (a.m + BM - 1) / BM;
@@ -347,30 +425,42 @@ hipError_t launch_ig(const ConvArgs &a, hipStream_t s)
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     // activation offsets are taken relative to a tile's first image and must fit 31 bits
-    const long long in_img = (long long)a.i1 * a.h * a.w * 32;
     const long long imgs = BM / ((long long)a.ho * a.wo) + 2;
-    if (imgs * in_img >= 0x7fffffffLL) return hipErrorInvalidValue;
+    if (imgs * (long long)a.i1 * a.h * a.w * 32 >= 0x7fffffffLL) return hipErrorInvalidValue;
+    if (PROJ && imgs * (long long)pj.i1 * pj.h * pj.w * 32 >= 0x7fffffffLL) return hipErrorInvalidValue;
     if (a.relu)
-        hipLaunchKernelGGL((igemm_kernel<KH, KW, BM, BN, RES, true>), dim3((unsigned)grid), dim3(256), 0, s, a,
-                           tiles_n, (int)per);
+        hipLaunchKernelGGL((igemm_kernel<KH, KW, BM, BN, ST, RES, true, PROJ>), dim3((unsigned)grid), dim3(256), 0, s,
+                           a, pj, tiles_n, (int)per);
     else
-        hipLaunchKernelGGL((igemm_kernel<KH, KW, BM, BN, RES, false>), dim3((unsigned)grid), dim3(256), 0, s, a,
-                           tiles_n, (int)per);
+        hipLaunchKernelGGL((igemm_kernel<KH, KW, BM, BN, ST, RES, false, PROJ>), dim3((unsigned)grid), dim3(256), 0,
+                           s, a, pj, tiles_n, (int)per);
     return hipGetLastError();
 }
 
 template <int KH, int KW>
 hipError_t launch_ig_k(const ConvArgs &a, hipStream_t s)
 {
+    constexpr int ST = 2;
     const bool wide = a.oc1 * 32 > 64;
-    if (a.residual) return wide ? launch_ig<KH, KW, 128, 128, true>(a, s) : launch_ig<KH, KW, 256, 64, true>(a, s);
-    return wide ? launch_ig<KH, KW, 128, 128, false>(a, s) : launch_ig<KH, KW, 256, 64, false>(a, s);
+    if (a.residual)
+        return wide ? launch_ig<KH, KW, 128, 128, ST, true, false>(a, a, s)
+                    : launch_ig<KH, KW, 256, 64, ST, true, false>(a, a, s);
+    return wide ? launch_ig<KH, KW, 128, 128, ST, false, false>(a, a, s)
+                : launch_ig<KH, KW, 256, 64, ST, false, false>(a, a, s);
 }
 
 }  // namespace
 
-hipError_t launch_igemm(const ConvArgs &a, int kh, int kw, hipStream_t s)
+hipError_t launch_conv_proj(const ConvArgs &a, const ConvArgs &pj, hipStream_t s)
 {
+    constexpr int ST = 2;
+    if (a.oc1 * 32 > 64) return launch_ig<1, 1, 128, 128, ST, true, true>(a, pj, s);
+    return launch_ig<1, 1, 256, 64, ST, true, true>(a, pj, s);
+}
+
+hipError_t launch_conv(const ConvArgs &a, int kh, int kw, hipStream_t s)
+{
+    if (conv1x1_small_k_supported(a, kh, kw)) return launch_conv1x1_small_k(a, s);
     if (kh == 1 && kw == 1) return launch_ig_k<1, 1>(a, s);
     if (kh == 3 && kw == 3) return launch_ig_k<3, 3>(a, s);
     return hipErrorInvalidValue;

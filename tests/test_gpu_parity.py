@@ -232,6 +232,55 @@ def test_fuzz_small_shapes(ifx, orc):
         np.testing.assert_array_equal(got, orc.conv_fused(x, wt, bias, mult, shift, s, p, flags, res))
 
 
+# ------------------------------------------------------------------ bottleneck with projection
+# (n, h, w, c_in, c_mid, c_out, stride, c3 kernel): conv3 and the projection run as one kernel
+# when both are 1x1 (the shortcut tile never reaches HBM); a 3x3 conv3 takes the unfused path.
+PROJ_BLOCKS = [
+    (3, 9, 9, 96, 48, 160, 2, 1),    # strided, two output-channel tiles, padded channels
+    (2, 13, 11, 64, 32, 96, 1, 1),   # unit stride, ragged pixel tile
+    (1, 7, 7, 256, 64, 64, 1, 1),    # 64 output channels: the tall tile shape
+    (5, 11, 6, 40, 24, 200, 2, 1),   # odd channel-block counts (32-channel blocks 2 and 1)
+    (2, 8, 8, 64, 32, 128, 1, 3),    # 3x3 conv3: projection and conv3 launched separately
+]
+
+
+@pytest.mark.parametrize("shape", PROJ_BLOCKS)
+def test_projection_block(ifx, orc, shape):
+    from oracle.ref import ConvParams
+    n, h, w, c_in, c_mid, c_out, s, k3 = shape
+    note(f"projection block {shape}")
+    rng = np.random.default_rng(sum(shape) * 13)
+    x = rand(rng, (n, h, w, c_in), 0, 127)
+    # (c_in, c_out, k, stride, pad, flags) of c1, c2, c3 and the projection
+    layers = [(c_in, c_mid, 1, 1, 0, ifx.RELU), (c_mid, c_mid, 3, s, 1, ifx.RELU),
+              (c_mid, c_out, k3, 1, k3 // 2, ifx.RESIDUAL | ifx.RELU), (c_in, c_out, 1, s, 0, 0)]
+    hs = [(h, w), (h, w)]
+    ho, wo = orc.out_dim(h, 3, s, 1), orc.out_dim(w, 3, s, 1)
+    hs += [(ho, wo), (h, w)]
+    bp = ifx.BlockParams()
+    keep, cps = [], []
+    for i, ((ci, co, k, st, pd, fl), (hh, ww)) in enumerate(zip(layers, hs)):
+        wt = rand(rng, (co, k, k, ci), -127, 127)
+        bias, mult, shift = params(rng, co, 0, 20)
+        d = ifx.conv_desc(n, hh, ww, ci, co, k, k, st, pd, fl)
+        tensors = [ifx.pack_weights(d, cu(wt)), cu(bias), cu(mult), cu(shift)]
+        keep += tensors
+        bp.d[i] = d
+        bp.w_blk[i], bp.bias[i], bp.mult[i], bp.shift[i] = (t.data_ptr() for t in tensors)
+        cps.append(ConvParams(wt, bias, mult, shift, st, pd))
+    bp.has_proj = 1
+    ws = torch.empty(ifx.block_workspace_bytes(bp), dtype=torch.int8, device="cuda")
+    nbytes = ifx.act_bytes(n, ho, wo, c_out)
+    for rep in range(2):
+        y, whole = guarded(nbytes)
+        ifx.block_forward(bp, ifx.pack_act(cu(x)), y, ws)
+        torch.cuda.synchronize()
+        check_guards(whole)
+        got = ifx.unpack_act(y.view(n, (c_out + 31) // 32, ho, wo, 32), c_out).cpu().numpy()
+        exp = orc.block(x, cps[0], cps[1], cps[2], cps[3])
+        np.testing.assert_array_equal(got, exp)
+
+
 # ------------------------------------------------------------------ stem
 @pytest.mark.parametrize("n,h,w,c", [(2, 224, 224, 3), (1, 37, 45, 3), (3, 16, 16, 4), (1, 2, 3, 1)])
 def test_stem(ifx, orc, n, h, w, c):
