@@ -31,9 +31,10 @@ RIDGE = PEAK_I8 / PEAK_HBM
 METRIC = "int8 TOPS + images/s (fused conv stack), % of int8 MFMA peak / HBM BW"
 
 
-def kernel_name(spec, nhwc_input=True) -> str:
+def kernel_name(spec, nhwc_input=True, proj=False) -> str:
     """The kernel template instance a conv layer dispatches to, spelled as rocprofv3
-    prints it (mirrors the library's host dispatch)."""
+    prints it (mirrors the library's host dispatch).  proj: conv3 fused with its
+    projection shortcut (ifx_conv_proj_fused)."""
     if spec.k == 7:
         return f"stem_kernel<{1 if nhwc_input else 0}>"
     oc_pad = (spec.c_out + 31) // 32 * 32
@@ -41,15 +42,15 @@ def kernel_name(spec, nhwc_input=True) -> str:
     res = "true" if spec.flags & 2 else "false"
     relu = "true" if spec.flags & 1 else "false"
     i1 = (spec.c_in + 31) // 32
-    if spec.k == 1 and spec.pad == 0 and i1 <= 4:
+    if spec.k == 1 and spec.pad == 0 and i1 <= 4 and not proj:
         return f"conv1x1_kernel<{bm}, {bn}, {(i1 + 1) // 2}, {res}, {relu}>"
-    return f"conv_kernel<{spec.k}, {spec.k}, {bm}, {bn}, 3, {res}, {relu}>"
+    return f"igemm_kernel<{spec.k}, {spec.k}, {bm}, {bn}, 2, {res}, {relu}, {'true' if proj else 'false'}>"
 
 
 # Sources each kernel family is built from: HBM traffic taken from counters is only
 # reported while these files are unchanged.
 KERNEL_SOURCES = {
-    "conv_kernel": ["conv.hip", "device_common.h", "ifx_internal.h"],
+    "igemm_kernel": ["igemm.hip", "device_common.h", "ifx_internal.h"],
     "conv1x1_kernel": ["conv1x1.hip", "device_common.h", "ifx_internal.h"],
     "stem_kernel": ["stem.hip", "device_common.h", "ifx_internal.h"],
 }
@@ -91,7 +92,7 @@ def summarize_pmc(fetch_csv: str, write_csv: str, calib_bytes: int, out: str, wo
     from collections import defaultdict
 
     def short(name):
-        m = re.search(r"((?:conv1x1|conv|stem)_kernel<[^>]*>)", name)
+        m = re.search(r"((?:conv1x1|igemm|stem)_kernel<[^>]*>)", name)
         if m:
             return m.group(1)
         return "copy" if "bitwise_not" in name else None
@@ -359,16 +360,29 @@ def main():
         d.n = nb
         return model.DeviceConv(dc.spec, d, dc.w_blk, dc.bias, dc.mult, dc.shift, dc.out_hw)
 
-    launches = []  # (spec, h, w, fn)
+    launches = []  # (kernel instance, ops, algorithmic bytes, fn); fn only, for bookkeeping steps
+    nhwc = not args.packed_input
+
+    def conv_launch(spec, nb_, h, w, fn):
+        ops, byts, _, _ = layer_work(spec, nb_, h, w)
+        return (kernel_name(spec, nhwc), ops, byts, fn)
+
+    def proj_launch(c3spec, pspec, nb_, h3, w3, hp, wp, fn):
+        # conv3 + projection in one kernel: both contractions; the shortcut is not a tensor
+        o3, b3, oh, ow = layer_work(c3spec, nb_, h3, w3)
+        op, bp, _, _ = layer_work(pspec, nb_, hp, wp)
+        shortcut = nb_ * oh * ow * c3spec.c_out
+        return (kernel_name(c3spec, nhwc, proj=True), o3 + op, b3 + bp - 2 * shortcut, fn)
+
     if args.workload in ("net", "net26_b1"):
         nb = sub_batch if 0 < sub_batch < n else n
         passes = (n + nb - 1) // nb
         big = max(ifx.act_bytes(nb, h, w, s.c_out if s.k != 7 else 64) for s, _, h, w in layers)
         big = max(big, ifx.act_bytes(nb, 56, 56, 256))
-        bufs = [torch.empty(big, dtype=torch.int8, device="cuda") for _ in range(5)]
-        cur, nxt, t1, t2, sc = bufs
+        bufs = [torch.empty(big, dtype=torch.int8, device="cuda") for _ in range(4)]
+        cur, nxt, t1, t2 = bufs
         stem = with_batch(net.stem, nb)
-        launches.append((wl.net.stem, 224, 224, lambda: stem.run(x_blk[:nb], cur, None, stream)))
+        launches.append(conv_launch(wl.net.stem, nb, 224, 224, lambda: stem.run(x_blk[:nb], cur, None, stream)))
         h = w = 56
         state = {"cur": cur, "nxt": nxt}
         for bs, db in zip(wl.net.blocks, net.blocks):
@@ -383,11 +397,18 @@ def main():
                     o = state[out] if isinstance(out, str) else out
                     c.run(xin, o, res, stream)
                 return f
-            launches.append((bs.c1, h, w, mk(c1, "cur", t1)))
-            launches.append((bs.c2, h, w, mk(c2, t1, t2)))
+
+            def mk_proj(c3_, pj_):
+                def f():
+                    ifx.conv_proj_fused(c3_.desc, t2, c3_.w_blk, c3_.bias, c3_.mult, c3_.shift, pj_.desc,
+                                        state["cur"], pj_.w_blk, pj_.bias, pj_.mult, pj_.shift, state["nxt"], stream)
+                return f
+            launches.append(conv_launch(bs.c1, nb, h, w, mk(c1, "cur", t1)))
+            launches.append(conv_launch(bs.c2, nb, h, w, mk(c2, t1, t2)))
             if pj is not None:
-                launches.append((bs.proj, h, w, mk(pj, "cur", sc)))
-            launches.append((bs.c3, h2, h2, mk(c3, t2, "nxt", sc if pj is not None else "cur")))
+                launches.append(proj_launch(bs.c3, bs.proj, nb, h2, h2, h, w, mk_proj(c3, pj)))
+            else:
+                launches.append(conv_launch(bs.c3, nb, h2, h2, mk(c3, t2, "nxt", "cur")))
 
             def swap():
                 state["cur"], state["nxt"] = state["nxt"], state["cur"]
@@ -399,29 +420,27 @@ def main():
             t1b = model.empty_act(n, 28, 28, 128)
             t2b = model.empty_act(n, 28, 28, 128)
             c1, c2, c3 = dcs
-            launches = [(wl.convs[0], 28, 28, lambda: c1.run(x_blk, t1b, None, stream)),
-                        (wl.convs[1], 28, 28, lambda: c2.run(t1b, t2b, None, stream)),
-                        (wl.convs[2], 28, 28, lambda: c3.run(t2b, y, x_blk, stream))]
+            launches = [conv_launch(wl.convs[0], n, 28, 28, lambda: c1.run(x_blk, t1b, None, stream)),
+                        conv_launch(wl.convs[1], n, 28, 28, lambda: c2.run(t1b, t2b, None, stream)),
+                        conv_launch(wl.convs[2], n, 28, 28, lambda: c3.run(t2b, y, x_blk, stream))]
         else:
-            launches = [(wl.convs[0], wl.h, wl.w, step)]
+            launches = [conv_launch(wl.convs[0], n, wl.h, wl.w, step)]
     reps = max(1, min(args.steps, 5) if args.workload == "net" else args.steps)
     evs = []
     torch.cuda.synchronize()
     for _ in range(reps):
-        for spec, h, w, fn in launches:
-            if spec is None:
+        for name, ops, byts, fn in launches:
+            if name is None:
                 fn()
                 continue
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
             fn()
             b.record(stream)
-            evs.append((spec, h, w, a, b))
+            evs.append((name, ops, byts, a, b))
     torch.cuda.synchronize()
     per_kernel = {}
-    for spec, h, w, a, b in evs:
-        name = kernel_name(spec, not args.packed_input)
-        ops, byts, _, _ = layer_work(spec, nb, h, w)
+    for name, ops, byts, a, b in evs:
         d = per_kernel.setdefault(name, {"time": 0.0, "ops": 0, "bytes": 0, "launches": 0})
         d["time"] += a.elapsed_time(b) * 1e-3
         d["ops"] += ops

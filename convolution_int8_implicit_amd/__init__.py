@@ -92,6 +92,7 @@ def lib() -> ctypes.CDLL:
         "ifx_unpack_act": ([vp, vp, i32, i32, i32, i32, vp], i32),
         "ifx_pack_weights": ([D, vp, vp, vp], i32),
         "ifx_conv_fused": ([D, vp, vp, vp, vp, vp, vp, vp, vp], i32),
+        "ifx_conv_proj_fused": ([D, vp, vp, vp, vp, vp, D, vp, vp, vp, vp, vp, vp, vp], i32),
         "ifx_block_workspace_bytes": ([ctypes.POINTER(BlockParams)], sz),
         "ifx_block_forward": ([ctypes.POINTER(BlockParams), vp, vp, vp, sz, vp], i32),
         "ifx_net_workspace_bytes": ([ctypes.POINTER(NetParams), i32], sz),
@@ -195,6 +196,15 @@ def conv_fused(d: ConvDesc, x_blk, w_blk, bias, mult, shift, residual, y, stream
     _dev(x_blk, w_blk, bias, mult, shift, residual, y)
     _check(lib().ifx_conv_fused(ctypes.byref(d), _ptr(x_blk), _ptr(w_blk), _ptr(bias), _ptr(mult), _ptr(shift),
                                 _ptr(residual), _ptr(y), _stream(stream)), "ifx_conv_fused")
+
+
+def conv_proj_fused(d3: ConvDesc, t_blk, w3_blk, bias3, mult3, shift3, dp: ConvDesc, x_blk, wp_blk, biasp, multp,
+                    shiftp, y, stream=None) -> None:
+    """conv3 of a bottleneck with its 1x1 projection shortcut in one launch (ifx_conv_proj_fused)."""
+    _dev(t_blk, w3_blk, bias3, mult3, shift3, x_blk, wp_blk, biasp, multp, shiftp, y)
+    _check(lib().ifx_conv_proj_fused(ctypes.byref(d3), _ptr(t_blk), _ptr(w3_blk), _ptr(bias3), _ptr(mult3),
+                                     _ptr(shift3), ctypes.byref(dp), _ptr(x_blk), _ptr(wp_blk), _ptr(biasp),
+                                     _ptr(multp), _ptr(shiftp), _ptr(y), _stream(stream)), "ifx_conv_proj_fused")
 
 
 def block_workspace_bytes(p: BlockParams) -> int:

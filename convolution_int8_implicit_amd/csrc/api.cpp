@@ -231,6 +231,13 @@ ifx_status check_block_ptrs(const ifx_block_params *p)
     return IFX_OK;
 }
 
+// A conv3 / projection pair that ifx_conv_proj_fused computes (descriptors already valid and chained).
+bool proj_fusable(const ifx_conv_desc *d3, const ifx_conv_desc *dp)
+{
+    return d3->kh == 1 && d3->kw == 1 && d3->stride == 1 && d3->pad == 0 && dp->kh == 1 && dp->kw == 1 &&
+           dp->pad == 0 && (d3->flags & ~(uint32_t)IFX_RELU) == IFX_RESIDUAL && dp->flags == 0;
+}
+
 // Launch a validated block for batch n; workspace already checked.
 ifx_status run_block(const ifx_block_params *p, const BlockPlan &plan, int n, const int8_t *x, int8_t *y,
                      int8_t *ws, hipStream_t s)
@@ -251,7 +258,7 @@ ifx_status run_block(const ifx_block_params *p, const BlockPlan &plan, int n, co
     if (st != IFX_OK) return st;
     const int8_t *res = x;
     if (p->has_proj) {
-        if (d[2].kh == 1 && d[2].kw == 1 && d[3].kh == 1 && d[3].kw == 1) {
+        if (proj_fusable(&d[2], &d[3])) {
             // conv3 and the projection in one kernel: the shortcut never goes through HBM
             const ifx::ConvArgs a = conv_args(&d[2], plan.dims[2], t2, p->w_blk[2], p->bias[2], p->mult[2],
                                               p->shift[2], nullptr, y);
@@ -424,6 +431,31 @@ size_t ifx_block_workspace_bytes(const ifx_block_params *p)
     BlockPlan plan;
     if (plan_block(p, 0, &plan) != IFX_OK) return 0;
     return plan.t1 + plan.t2 + plan.sc;
+}
+
+ifx_status ifx_conv_proj_fused(const ifx_conv_desc *d3, const int8_t *t_blk, const int8_t *w3_blk,
+                               const int32_t *bias3, const int32_t *mult3, const int32_t *shift3,
+                               const ifx_conv_desc *dp, const int8_t *x_blk, const int8_t *wp_blk,
+                               const int32_t *biasp, const int32_t *multp, const int32_t *shiftp,
+                               int8_t *y_blk, void *stream)
+{
+    if (!d3 || !dp) return IFX_E_NULL;
+    Kind k3, kp;
+    Dims m3, mp;
+    ifx_status st = check_desc(d3, &k3, &m3);
+    if (st != IFX_OK) return st;
+    st = check_desc(dp, &kp, &mp);
+    if (st != IFX_OK) return st;
+    if (k3 != kGeneric || kp != kGeneric || !proj_fusable(d3, dp)) return IFX_E_UNSUPPORTED;
+    if (dp->n != d3->n || dp->c_out != d3->c_out || mp.oh != m3.oh || mp.ow != m3.ow) return IFX_E_SHAPE;
+    const void *ptrs[] = {t_blk, w3_blk, bias3, mult3, shift3, x_blk, wp_blk, biasp, multp, shiftp, y_blk};
+    for (const void *q : ptrs)
+        if (!q) return IFX_E_NULL;
+    for (const void *q : ptrs)
+        if (!aligned16(q)) return IFX_E_ALIGN;
+    const ifx::ConvArgs a = conv_args(d3, m3, t_blk, w3_blk, bias3, mult3, shift3, nullptr, y_blk);
+    const ifx::ConvArgs pj = conv_args(dp, mp, x_blk, wp_blk, biasp, multp, shiftp, nullptr, nullptr);
+    return hip_status(ifx::launch_conv_proj(a, pj, (hipStream_t)stream));
 }
 
 ifx_status ifx_block_forward(const ifx_block_params *p, const int8_t *x_blk, int8_t *y_blk, void *ws,

@@ -142,11 +142,42 @@ ifx_status ifx_conv_fused(const ifx_conv_desc *d, const int8_t *x_blk, const int
                           const int8_t *residual, void *y, void *stream);
 
 /*
+ * Conv3 of a bottleneck together with its projection shortcut, as one launch.
+ * The Inspur conv-merge article (section 2.1) merges operators into one kernel
+ * so that a tensor passed between them is neither written to nor read back from
+ * global memory; here the passed tensor is the projection shortcut of the first
+ * block of a stage (section 2.2 structure, with a 1x1 projection of the block
+ * input in place of the input itself):
+ *   sc = conv(x_blk; dp)                 requantised to int8, no ReLU
+ *   y  = conv(t_blk; d3, RESIDUAL = sc)
+ * The result is bit-identical to ifx_conv_fused(dp) followed by ifx_conv_fused(d3)
+ * with that output as the residual; sc is never stored.
+ *   d3      1x1, stride 1, pad 0, flags IFX_RESIDUAL, optionally IFX_RELU
+ *   t_blk   packed input of d3, [n, ceil(d3.c_in/32), d3.h, d3.w, 32]
+ *   dp      1x1, any stride, pad 0, flags 0
+ *   x_blk   packed input of dp, [n, ceil(dp.c_in/32), dp.h, dp.w, 32]
+ *   w3_blk, bias3, mult3, shift3 / wp_blk, biasp, multp, shiftp: packed weights
+ *           and per-channel parameters of d3 / dp, as for ifx_conv_fused
+ *   y_blk   packed int8 output [n, ceil(c_out/32), ho, wo, 32]; must not overlap
+ *           the inputs
+ * Both descriptors must have the same n and c_out and the same output height and
+ * width (IFX_E_SHAPE otherwise); other kernel sizes, pads or flags give
+ * IFX_E_UNSUPPORTED.  Nothing is launched on an error.
+ */
+ifx_status ifx_conv_proj_fused(const ifx_conv_desc *d3, const int8_t *t_blk, const int8_t *w3_blk,
+                               const int32_t *bias3, const int32_t *mult3, const int32_t *shift3,
+                               const ifx_conv_desc *dp, const int8_t *x_blk, const int8_t *wp_blk,
+                               const int32_t *biasp, const int32_t *multp, const int32_t *shiftp,
+                               int8_t *y_blk, void *stream);
+
+/*
  * Bottleneck block (Inspur conv-merge article, section 2.2):
  *   t1 = conv(x; d[0] 1x1, RELU)          c1
  *   t2 = conv(t1; d[1] 3x3 stride s, RELU) c2
  *   sc = x, or conv(x; d[3] 1x1 stride s, no ReLU) when has_proj
  *   y  = conv(t2; d[2] 1x1, RESIDUAL=sc, RELU)   c3
+ * When c3 and the projection are 1x1 and the projection has no ReLU, both run
+ * as ifx_conv_proj_fused and sc is not materialised.
  * Descriptors carry the batch in n.  Their flags must be: d[0], d[1] without
  * RESIDUAL/MAXPOOL/OUT_I32, d[2] with RESIDUAL, d[3] without RESIDUAL/MAXPOOL/
  * OUT_I32.  t1, t2 and sc live in the caller's workspace.

@@ -92,6 +92,31 @@ def test_errors_return_before_any_launch():
     assert L.ifx_conv_validate(None) == 1
 
 
+def test_conv_proj_fused_validation():
+    """conv3 + projection in one launch: descriptors, pairing and pointers are checked on the
+    host and nothing is launched on an error."""
+    L = ifx.lib()
+    fake = ctypes.c_void_p(0x100000)
+    odd = ctypes.c_void_p(0x100001)
+    d3 = D(n=2, h=14, w=14, ci=64, co=256)
+    dp = D(n=2, h=28, w=28, ci=128, co=256, s=2, f=0)
+    four = [fake] * 4  # weights, bias, mult, shift
+
+    def call(a3, ap, t=fake, y=fake):
+        return L.ifx_conv_proj_fused(ctypes.byref(a3), t, *four, ctypes.byref(ap), fake, *four, y, None)
+
+    assert L.ifx_conv_proj_fused(None, fake, *four, ctypes.byref(dp), fake, *four, fake, None) == 1
+    assert call(d3, dp, t=None) == 1
+    assert call(d3, dp, y=odd) == 4
+    assert call(D(n=2, h=14, w=14, ci=64, co=256, k=3, p=1), dp) == 3           # conv3 must be 1x1
+    assert call(d3, D(n=2, h=28, w=28, ci=128, co=256, s=2, f=ifx.RELU)) == 3    # projection without ReLU
+    assert call(D(n=2, h=14, w=14, ci=64, co=256, f=ifx.RELU), dp) == 3         # conv3 adds the shortcut
+    assert call(d3, D(n=2, h=28, w=28, ci=128, co=128, s=2, f=0)) == 2          # channel counts differ
+    assert call(d3, D(n=2, h=28, w=28, ci=128, co=256, s=1, f=0)) == 2          # output sizes differ
+    assert call(d3, D(n=3, h=28, w=28, ci=128, co=256, s=2, f=0)) == 2          # batches differ
+    assert call(D(k=5, p=2), dp) == 3
+
+
 def _block(n=2, proj=True, c3_flags=ifx.RESIDUAL | ifx.RELU, c2_cin=64):
     p = ifx.BlockParams()
     p.d[0] = D(n=n, h=8, w=8, ci=256, co=64, f=ifx.RELU)

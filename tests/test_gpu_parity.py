@@ -269,6 +269,16 @@ def test_projection_block(ifx, orc, shape):
         bp.w_blk[i], bp.bias[i], bp.mult[i], bp.shift[i] = (t.data_ptr() for t in tensors)
         cps.append(ConvParams(wt, bias, mult, shift, st, pd))
     bp.has_proj = 1
+    if k3 == 1:
+        # the same conv3 + projection through the public one-launch entry point
+        t = rand(rng, (n, ho, wo, c_mid), 0, 127)
+        y, whole = guarded(ifx.act_bytes(n, ho, wo, c_out))
+        ifx.conv_proj_fused(bp.d[2], ifx.pack_act(cu(t)), *keep[8:12], bp.d[3], ifx.pack_act(cu(x)), *keep[12:16], y)
+        torch.cuda.synchronize()
+        check_guards(whole)
+        got = ifx.unpack_act(y.view(n, (c_out + 31) // 32, ho, wo, 32), c_out).cpu().numpy()
+        sc = orc.conv_layer(x, cps[3], 0)
+        np.testing.assert_array_equal(got, orc.conv_layer(t, cps[2], ifx.RESIDUAL | ifx.RELU, residual=sc))
     ws = torch.empty(ifx.block_workspace_bytes(bp), dtype=torch.int8, device="cuda")
     nbytes = ifx.act_bytes(n, ho, wo, c_out)
     for rep in range(2):
