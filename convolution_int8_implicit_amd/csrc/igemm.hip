@@ -74,9 +74,10 @@ __device__ __forceinline__ int dma_row(int lane)
     return 4 * line + (((lane & 7) >> 1) ^ (line & 3));
 }
 
-// Requantise the wave's accumulators (MODE picked by a wave vote on the shifts) into the LDS
-// tile at rbase (row stride 64 B), adding the shortcut bytes already there when RES.
-template <bool RES, bool RELU>
+// Requantise the wave's accumulators (MODE picked by a wave vote on the shifts) into the LDS tile
+// at rbase (row stride 64 B), adding the shortcut bytes already there when RES.  ADD_BIAS: the
+// accumulators do not hold the bias yet.
+template <bool RES, bool RELU, bool ADD_BIAS>
 __device__ __forceinline__ void requant_to_lds(const v4i (&acc)[4][4], int8_t *rbase, const int8_t *Pw, int c,
                                                int ocl, int oc)
 {
@@ -87,8 +88,8 @@ __device__ __forceinline__ void requant_to_lds(const v4i (&acc)[4][4], int8_t *r
     bool fast_lane = true;
 #pragma unroll
     for (int tn = 0; tn < 4; ++tn) {
-        const bool v = ocl + tn < oc;  // padded channels: bias = mult = 0 gives 0
-        bias[tn] = v ? bias4[tn] : 0;
+        const bool v = ocl + tn < oc;  // padded channels: accumulator (or bias) and mult are 0, giving 0
+        bias[tn] = ADD_BIAS && v ? bias4[tn] : 0;
         mul[tn] = v ? mult4[tn] : 0;
         shf[tn] = v ? shift4[tn] : 2;
         fast_lane = fast_lane && shf[tn] >= 2;
@@ -261,7 +262,7 @@ void igemm_kernel(ConvArgs a, ConvArgs pj, int tiles_n, int per_xcd)
     };
 
     issue(0);
-    // per-channel parameters (of pj first, PROJ) and the shortcut part of this wave
+    // per-channel parameters and the shortcut part of this wave
     auto issue_params = [&](const ConvArgs &q, int8_t *dst) {
         if (lane < 16) {
             const bool v = ch0 + 4 * lane < q.oc;
@@ -273,10 +274,10 @@ void igemm_kernel(ConvArgs a, ConvArgs pj, int tiles_n, int per_xcd)
             }
         }
     };
-    if (PROJ)
-        issue_params(pj, Pw);
-    else
-        issue_params(a, Pw);
+    issue_params(a, Pw);
+    // PROJ: the projection's parameters wait in the wave's shortcut region, which the
+    // projection's requantisation overwrites only after reading them
+    if (PROJ) issue_params(pj, Rres);
     if (RES && !PROJ) {
         const v4i rsR = make_rsrc(a.res + (long long)img0 * out_img, (long long)(a.n - img0) * out_img);
 #pragma unroll
@@ -314,10 +315,24 @@ void igemm_kernel(ConvArgs a, ConvArgs pj, int tiles_n, int per_xcd)
     const int ocl = ch0 + 4 * c;
     const int pbase = m0 + wm0;
 
+    // Without a projection the accumulators start at the per-channel bias (y = acc + bias needs no
+    // add afterwards; channels past Oc read a zero bias, their DMA lanes being out of range).  The
+    // fused form starts both contractions at zero and adds the bias in the requantisation: holding
+    // bias-filled accumulators next to the projection's would cost registers it does not have.
+    auto init_acc = [&](const int8_t *P) {
+        if (PROJ) {
 #pragma unroll
-    for (int tm = 0; tm < 4; ++tm)
+            for (int tm = 0; tm < 4; ++tm)
 #pragma unroll
-        for (int tn = 0; tn < 4; ++tn) acc[tm][tn] = (v4i){0, 0, 0, 0};
+                for (int tn = 0; tn < 4; ++tn) acc[tm][tn] = (v4i){0, 0, 0, 0};
+            return;
+        }
+        const v4i bias4 = *(const v4i *)(P + c * 16);
+#pragma unroll
+        for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+            for (int tn = 0; tn < 4; ++tn) acc[tm][tn] = (v4i){bias4[tn], bias4[tn], bias4[tn], bias4[tn]};
+    };
 
     static_assert(ST == 2, "the up-front waits below count one stage in flight");
     auto step = [&](int s) {
@@ -328,6 +343,7 @@ void igemm_kernel(ConvArgs a, ConvArgs pj, int tiles_n, int per_xcd)
         else
             wait_vmcnt<0>();
         ring_barrier();  // ... and every other wave's; stage s-1's slot is free again
+        if (s == 0) init_acc(PROJ ? Rres : Pw);  // this wave's parameters have landed too
         if (!upfront && s + ST - 1 < nsteps) issue((s + ST - 1) % ST);
         const int8_t *st = smem + (s % ST) * C::STAGE;
         v4i af[4], bf[4];
@@ -349,21 +365,14 @@ void igemm_kernel(ConvArgs a, ConvArgs pj, int tiles_n, int per_xcd)
             cur_tap = 0;
         }
         step(n1 - 1);
-        // the projection is complete: its requantised output (no ReLU) is the shortcut.  The
-        // parameters of a then replace the projection's in LDS (the next step's wait covers them).
-        requant_to_lds<false, false>(acc, Rres + g * 64 + 4 * c, Pw, c, ocl, pj.oc);
-        issue_params(a, Pw);
-#pragma unroll
-        for (int tm = 0; tm < 4; ++tm)
-#pragma unroll
-            for (int tn = 0; tn < 4; ++tn) acc[tm][tn] = (v4i){0, 0, 0, 0};
+        // the projection is complete: its requantised output (no ReLU) is the shortcut
+        requant_to_lds<false, false, true>(acc, Rres + g * 64 + 4 * c, Rres, c, ocl, pj.oc);
+        init_acc(Pw);
         for (int s = n1; s < nsteps; ++s) step(s);
     } else {
         for (int s = 0; s < nsteps; ++s) step(s);
     }
-    if (PROJ) wait_vmcnt<0>();  // a's parameters, requested at step n1, may be the last DMA
     if (a.out_i32) {
-        const v4i bias4 = *(const v4i *)(Pw + c * 16);
         int32_t *y = (int32_t *)a.y;
         const bool vec = (a.oc & 3) == 0 && ocl + 3 < a.oc;
 #pragma unroll
@@ -373,8 +382,7 @@ void igemm_kernel(ConvArgs a, ConvArgs pj, int tiles_n, int per_xcd)
                 const int p = pbase + 16 * tm + 4 * i + g;
                 if (p >= a.m) continue;
                 const long long off = (long long)p * a.oc + ocl;
-                const v4i v = {acc[tm][0][i] + bias4.x, acc[tm][1][i] + bias4.y, acc[tm][2][i] + bias4.z,
-                               acc[tm][3][i] + bias4.w};
+                const v4i v = {acc[tm][0][i], acc[tm][1][i], acc[tm][2][i], acc[tm][3][i]};
                 if (vec) {
                     *(v4i *)(y + off) = v;
                 } else {
@@ -387,7 +395,7 @@ void igemm_kernel(ConvArgs a, ConvArgs pj, int tiles_n, int per_xcd)
     }
     // staging: the shortcut tile itself (requantised in place), else the ring slot no wave reads any more
     int8_t *const Rw = RES ? Rres : smem + (nsteps % ST) * C::STAGE + wave * 4096;
-    requant_to_lds<RES, RELU>(acc, Rw + g * 64 + 4 * c, Pw, c, ocl, a.oc);
+    requant_to_lds<RES, RELU, PROJ>(acc, Rw + g * 64 + 4 * c, Pw, c, ocl, a.oc);
     wave_lds_sync();
 
     // 16-byte stores of the wave's 64 pixels x 64 channels
