@@ -178,28 +178,10 @@ void conv1x1_kernel(ConvArgs a, int tiles_n)
     // ---- epilogue: this wave's own shortcut and parameters (no other wave's data)
     wait_vmcnt<0>();
     const int ocl = ch0 + 4 * c;  // first of this lane's four output channels
-    const v4i bias4 = *(const v4i *)(Pw + c * 16);
-    const v4i mult4 = *(const v4i *)(Pw + 256 + c * 16);
-    const v4i shift4 = *(const v4i *)(Pw + 512 + c * 16);
-    int bias[4], mul[4], rnd[4], shm[4], shf[4];
-    bool fast_lane = true;
-#pragma unroll
-    for (int tn = 0; tn < 4; ++tn) {
-        const bool v = ocl + tn < a.oc;  // padded channels: bias = mult = 0 gives 0
-        bias[tn] = v ? bias4[tn] : 0;
-        mul[tn] = v ? mult4[tn] : 0;
-        shf[tn] = v ? shift4[tn] : 2;
-        fast_lane = fast_lane && shf[tn] >= 2;
-        rnd[tn] = 1 << ((shf[tn] - 2) & 31);
-        shm[tn] = shf[tn] - 1;
-    }
-    int8_t *rbase = Rw + g * 64 + 4 * c;
-    if (!__all(fast_lane))
-        requant_tile<0, RES, RELU, 64>(acc, rbase, bias, mul, rnd, shm, shf);
-    else if (!RES && RELU)
-        requant_tile<1, RES, RELU, 64>(acc, rbase, bias, mul, rnd, shm, shf);
-    else
-        requant_tile<2, RES, RELU, 64>(acc, rbase, bias, mul, rnd, shm, shf);
+    RqLane r;
+    const int mode = rq_setup<RES, RELU>(r, *(const v4i *)(Pw + c * 16), *(const v4i *)(Pw + 256 + c * 16),
+                                         *(const v4i *)(Pw + 512 + c * 16), false, ocl, a.oc);
+    requant_tile_any<RES, RELU, 64>(mode, acc, Rw + g * 64 + 4 * c, r);
     wave_lds_sync();
 
     // 16-byte stores of the wave's 64 pixels x 64 channels

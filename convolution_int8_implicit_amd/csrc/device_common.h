@@ -146,14 +146,53 @@ __device__ __forceinline__ int fdiv(int n, unsigned mul, int shr)
 // for both the row-major operand fetch and the permuted pixel order.
 __device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
 
-// Requantise a wave's 64x64 accumulator tile into the LDS staging tile (row
-// stride BN), adding the shortcut bytes already there when RES.  MODE 0:
-// general (any shift); 1: shift >= 2, ReLU, no shortcut; 2: shift >= 2.
-// Lane (g, c) owns tile rows 16tm + 4i + g and the 4 bytes at column 4c.
+// Requantisation parameters of the four output channels a lane owns.
+struct RqLane {
+    int bias[4];       // added to the accumulator (modes 0 and 2; 0 when it already holds the bias)
+    int mul[4], shf[4];
+    int rnd[4], shm[4];  // 2^(shift-2) and shift-1 (modes 1 and 2)
+    long long add[4];  // mode 1: bias*mult + 2^(30+shift), the whole rounding addend
+};
+
+// Set up the lane's channels ocl .. ocl+3 (channels >= oc: mult 0, so they give 0) and pick the
+// wave's mode:
+//   0  any shift: one general requant_any per element;
+//   1  every shift >= 2 and no rounding tie possible (or ReLU without a shortcut, where a tie
+//      on a negative value ends at 0 either way): q = hi(acc*m + add) >> (shift-1), one
+//      v_mad_i64_i32 and one shift per element, the bias folded into `add`;
+//   2  every shift >= 2: requant_fast, which carries the [y<0] tie correction.
+// A tie (y*m/2^(31+s) exactly halfway) needs v2(y) + v2(m) = 30 + s with v2(y) <= 30 for
+// |y| < 2^31, so it cannot happen when m has fewer than s trailing zero bits (or m == 0).
+template <bool RES, bool RELU>
+__device__ __forceinline__ int rq_setup(RqLane &r, v4i bias4, v4i mult4, v4i shift4, bool bias_in_acc, int ocl,
+                                        int oc)
+{
+    bool fast = true, tiefree = true;
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn) {
+        const bool v = ocl + tn < oc;
+        const int b = v && !bias_in_acc ? bias4[tn] : 0;
+        const int m = v ? mult4[tn] : 0;
+        const int s = v ? shift4[tn] : 2;
+        r.bias[tn] = b;
+        r.mul[tn] = m;
+        r.shf[tn] = s;
+        r.rnd[tn] = 1 << ((s - 2) & 31);
+        r.shm[tn] = s - 1;
+        r.add[tn] = (long long)b * (long long)m + (long long)((unsigned long long)(unsigned)r.rnd[tn] << 32);
+        fast = fast && s >= 2;
+        tiefree = tiefree && (m == 0 || (int)__builtin_ctz((unsigned)m) < s);
+    }
+    if (!__all(fast)) return 0;
+    if ((!RES && RELU) || __all(tiefree)) return 1;
+    return 2;
+}
+
+// Requantise a wave's 64x64 accumulator tile into the LDS staging tile (row stride BN),
+// adding the shortcut bytes already there when RES.  Lane (g, c) owns tile rows
+// 16tm + 4i + g and the 4 bytes at column 4c.
 template <int MODE, bool RES, bool RELU, int BN>
-__device__ __forceinline__ void requant_tile(const v4i (&acc)[4][4], int8_t *rbase, const int (&bias)[4],
-                                             const int (&mul)[4], const int (&rnd)[4], const int (&shm)[4],
-                                             const int (&shf)[4])
+__device__ __forceinline__ void requant_tile(const v4i (&acc)[4][4], int8_t *rbase, const RqLane &r)
 {
 #pragma unroll
     for (int tm = 0; tm < 4; ++tm)
@@ -164,19 +203,32 @@ __device__ __forceinline__ void requant_tile(const v4i (&acc)[4][4], int8_t *rba
             int q[4];
 #pragma unroll
             for (int tn = 0; tn < 4; ++tn) {
-                const int yv = acc[tm][tn][i] + bias[tn];
                 int v;
-                if (MODE == 0)
-                    v = requant_any(yv, mul[tn], shf[tn]);
-                else if (MODE == 1)
-                    v = requant_relu(yv, mul[tn], rnd[tn], shm[tn]);
-                else
-                    v = requant_fast(yv, mul[tn], rnd[tn], shm[tn]);
+                if (MODE == 0) {
+                    v = requant_any(acc[tm][tn][i] + r.bias[tn], r.mul[tn], r.shf[tn]);
+                } else if (MODE == 1) {
+                    const long long p = (long long)acc[tm][tn][i] * (long long)r.mul[tn] + r.add[tn];
+                    v = ((int)(p >> 32)) >> r.shm[tn];
+                } else {
+                    v = requant_fast(acc[tm][tn][i] + r.bias[tn], r.mul[tn], r.rnd[tn], r.shm[tn]);
+                }
                 if (RES) v += (int)(signed char)(rr >> (8 * tn));
                 q[tn] = RELU ? min(max(v, 0), 127) : min(max(v, -128), 127);
             }
             *rp = pack4(q[0], q[1], q[2], q[3]);
         }
+}
+
+// The three modes dispatched on rq_setup's wave-uniform choice.
+template <bool RES, bool RELU, int BN>
+__device__ __forceinline__ void requant_tile_any(int mode, const v4i (&acc)[4][4], int8_t *rbase, const RqLane &r)
+{
+    if (mode == 0)
+        requant_tile<0, RES, RELU, BN>(acc, rbase, r);
+    else if (mode == 1)
+        requant_tile<1, RES, RELU, BN>(acc, rbase, r);
+    else
+        requant_tile<2, RES, RELU, BN>(acc, rbase, r);
 }
 
 }  // namespace ifx

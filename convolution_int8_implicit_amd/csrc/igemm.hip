@@ -81,27 +81,10 @@ template <bool RES, bool RELU, bool ADD_BIAS>
 __device__ __forceinline__ void requant_to_lds(const v4i (&acc)[4][4], int8_t *rbase, const int8_t *Pw, int c,
                                                int ocl, int oc)
 {
-    const v4i bias4 = *(const v4i *)(Pw + c * 16);
-    const v4i mult4 = *(const v4i *)(Pw + 256 + c * 16);
-    const v4i shift4 = *(const v4i *)(Pw + 512 + c * 16);
-    int bias[4], mul[4], rnd[4], shm[4], shf[4];
-    bool fast_lane = true;
-#pragma unroll
-    for (int tn = 0; tn < 4; ++tn) {
-        const bool v = ocl + tn < oc;  // padded channels: accumulator (or bias) and mult are 0, giving 0
-        bias[tn] = ADD_BIAS && v ? bias4[tn] : 0;
-        mul[tn] = v ? mult4[tn] : 0;
-        shf[tn] = v ? shift4[tn] : 2;
-        fast_lane = fast_lane && shf[tn] >= 2;
-        rnd[tn] = 1 << ((shf[tn] - 2) & 31);
-        shm[tn] = shf[tn] - 1;
-    }
-    if (!__all(fast_lane))
-        requant_tile<0, RES, RELU, 64>(acc, rbase, bias, mul, rnd, shm, shf);
-    else if (!RES && RELU)
-        requant_tile<1, RES, RELU, 64>(acc, rbase, bias, mul, rnd, shm, shf);
-    else
-        requant_tile<2, RES, RELU, 64>(acc, rbase, bias, mul, rnd, shm, shf);
+    RqLane r;
+    const int mode = rq_setup<RES, RELU>(r, *(const v4i *)(Pw + c * 16), *(const v4i *)(Pw + 256 + c * 16),
+                                         *(const v4i *)(Pw + 512 + c * 16), !ADD_BIAS, ocl, oc);
+    requant_tile_any<RES, RELU, 64>(mode, acc, rbase, r);
 }
 
 // One convolution `a` (with its epilogue), or, when PROJ, the last 1x1 convolution `a` of a

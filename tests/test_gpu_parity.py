@@ -198,6 +198,30 @@ def test_requant_edges(ifx, orc):
     np.testing.assert_array_equal(got, orc.conv_fused(x, wt, bias, mult2, shift2, 1, 0, 0))
 
 
+@pytest.mark.parametrize("k", [1, 3])
+def test_requant_ties_with_shortcut(ifx, orc, k):
+    """The requantisation modes with a shortcut: channel groups whose multipliers can tie
+    (2^30, 3*2^28, shift 2-4: the tie-correcting path) beside tie-free ones (odd multipliers:
+    the one-multiply path); negative sums near halfway, through the small-K and general kernels."""
+    note(f"requant ties with shortcut k={k}")
+    rng = np.random.default_rng(17 + k)
+    n, h, w, c, oc = 2, 9, 7, 64 if k == 1 else 96, 128
+    x = rand(rng, (n, h, w, c), -128, 127)
+    wt = rand(rng, (oc, k, k, c), -127, 127)
+    bias = rand(rng, oc, -(1 << 12), 1 << 12, np.int32)
+    # 64-channel groups (one wave each): tie-prone, tie-free, then mixed within the group
+    mult = np.empty(oc, np.int32)
+    mult[:64] = np.tile(np.array([1 << 30, 3 << 28], np.int32), 32)
+    mult[64:] = rand(rng, 64, 1 << 30, (1 << 31) - 1, np.int32) | 1
+    mult[96:100] = 1 << 30
+    shift = np.tile(np.array([2, 3, 4, 2], np.int32), oc // 4)
+    ho, wo = orc.out_dim(h, k, 1, k // 2), orc.out_dim(w, k, 1, k // 2)
+    res = rand(rng, (n, ho, wo, oc), -128, 127)
+    for flags in (ifx.RESIDUAL, ifx.RESIDUAL | ifx.RELU):
+        got = gpu_conv(ifx, x, wt, bias, mult, shift, k, 1, k // 2, flags, res)
+        np.testing.assert_array_equal(got, orc.conv_fused(x, wt, bias, mult, shift, 1, k // 2, flags, res))
+
+
 def test_identity_halves(ifx, orc):
     """The golden identity case on the GPU: out = round_half_away(x / 2)."""
     note("identity halves")
