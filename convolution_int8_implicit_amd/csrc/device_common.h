@@ -142,9 +142,12 @@ __device__ __forceinline__ int fdiv(int n, unsigned mul, int shr)
     return mul == 0 ? n : (int)(__umulhi((unsigned)n, mul) >> shr);
 }
 
-// 16-byte-chunk XOR swizzle of a 64-byte LDS row: conflict-free ds_read_b128
-// for both the row-major operand fetch and the permuted pixel order.
-__device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+// 16-byte-chunk XOR swizzle of a 64-byte LDS row (chunk k of row r stored at slot k ^ swz(r)).
+// A ds_read_b128 serves lanes {0-7, 24-31}, {8-15, 16-23}, {32-39, 56-63}, {40-47, 48-55}
+// one group per cycle; a lane (c = l % 16, g = l / 16) reads chunk g of row 16 t + c (weights)
+// or 16 t + 4(c % 4) + c / 4 (pixels).  With swz = (r / 4 ^ r) % 4 every group of either
+// pattern reaches 16 distinct 16-byte bank slots.
+__device__ __forceinline__ int swz(int row) { return ((row >> 2) ^ row) & 3; }
 
 // Requantisation parameters of the four output channels a lane owns.
 struct RqLane {

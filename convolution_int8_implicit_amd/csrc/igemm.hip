@@ -52,27 +52,31 @@ struct IgCfg {
     static constexpr int wg_per_cu(bool res) { return kLdsBytes / lds(res) > 4 ? 4 : kLdsBytes / lds(res); }
 };
 
-// Byte offset, inside one operand block of a stage, of the 16-byte half h of
-// row `row`.  Rows pair up four to a 128-byte line; the slot of (row, h) in
-// its line is XOR-swizzled so that the eight lanes served together by a
-// ds_read_b128 (same half, rows 0,4,8,12,1,5,9,13 or 2,6,...,15 of a 16-row
-// group for the activation fragment; rows 4c + tn, c = 0..7 for the weight
-// fragment) hit eight different slots.
+// LDS layouts of one operand block of a stage (32 K-bytes per row, two 16-byte halves h).
+// Rows go four to a 128-byte line, so each 8-lane group of a DMA fetches one whole
+// 128-byte line of consecutive pixels or weight rows; the slot of (row, h) inside its
+// line is XOR-swizzled against the ds_read_b128 fragment reads.  Such a read serves
+// its 64 lanes in four passes of 16 lanes, {0-7, 24-31}, {8-15, 16-23}, {32-39, 56-63}
+// and {40-47, 48-55}; a pass takes one cycle when its lanes hit 16 different 16-byte
+// bank slots (16 per 256 bytes).  Fragment lane (c = l % 16, g = l / 16) reads half
+// g % 2 of pixel row 4(c%4) + c/4 of a 16-row group, or of weight row 4c + tn, so each
+// pass reads half 0 of eight rows and half 1 of eight others; both swizzles give every
+// pass 16 distinct slots.
 __device__ __forceinline__ int a_swz(int row, int h)
 {
     return ((row >> 2) << 7) | (((((row & 3) ^ ((row >> 2) & 3)) << 1) | (h ^ (row & 1))) << 4);
 }
 __device__ __forceinline__ int b_swz(int row, int h)
 {
-    return ((row >> 2) << 7) | (((((row & 3) ^ ((row >> 2) & 3)) << 1) | (h ^ ((row >> 4) & 1))) << 4);
+    return ((row >> 2) << 7) | ((((row & 3) << 1 | h) ^ ((row >> 2) & 6)) << 4);
 }
-// Inverse for the DMA: lane l of an instruction that fills rows [32 c, 32 c + 32)
-// lands at byte 16 l of that 1 KB; it must fetch row 32 c + dma_row(l).
-__device__ __forceinline__ int dma_row(int lane)
-{
-    const int line = lane >> 3;
-    return 4 * line + (((lane & 7) >> 1) ^ (line & 3));
-}
+// Inverses for the DMA: lane l of an instruction that fills rows [32 c, 32 c + 32) lands at
+// byte 16 l of that 1 KB and must fetch half dma_*_h(l) of row 32 c + dma_*_row(l); lanes
+// 8k..8k+7 fetch rows 4k..4k+3.
+__device__ __forceinline__ int dma_a_row(int lane) { return 4 * (lane >> 3) + (((lane & 7) >> 1) ^ ((lane >> 3) & 3)); }
+__device__ __forceinline__ int dma_a_h(int lane) { return (lane & 1) ^ (dma_a_row(lane) & 1); }
+__device__ __forceinline__ int dma_b_row(int lane) { return 4 * (lane >> 3) + (((lane & 7) ^ ((lane >> 3) & 6)) >> 1); }
+__device__ __forceinline__ int dma_b_h(int lane) { return lane & 1; }
 
 // Requantise the wave's accumulators (MODE picked by a wave vote on the shifts) into the LDS tile
 // at rbase (row stride 64 B), adding the shortcut bytes already there when RES.  ADD_BIAS: the
@@ -126,14 +130,12 @@ void igemm_kernel(ConvArgs a, ConvArgs pj, int tiles_n, int per_xcd)
     //      pixel row 4(r%4) + r/4 of each 16-row group and weight row 4r + tn, K bytes [16g, 16g+16)
     const int c = lane & 15;
     const int g = lane >> 4;
-    // rows 16 apart sit 4 lines (512 B) apart with the same slot
+    // rows 16 apart sit 4 lines (512 B) apart with the same slot; weight row 4c + tn sits at
+    // the slot of row 4c XOR 32 tn
     const int a_frag = (g >> 1) * (BM * 32) + a_swz(wm0 + 4 * (c & 3) + (c >> 2), g & 1);
     int b_frag[4];
 #pragma unroll
-    for (int tn = 0; tn < 4; ++tn) {
-        const int row = wn0 + 4 * c + tn;
-        b_frag[tn] = BM * 64 + (g >> 1) * (BN * 32) + b_swz(row, g & 1);
-    }
+    for (int tn = 0; tn < 4; ++tn) b_frag[tn] = (BM * 64 + (g >> 1) * (BN * 32) + b_swz(wn0 + 4 * c, g & 1)) ^ (tn << 5);
 
     v4i acc[4][4];
 
@@ -159,8 +161,8 @@ void igemm_kernel(ConvArgs a, ConvArgs pj, int tiles_n, int per_xcd)
 #pragma unroll
         for (int j = 0; j < C::AI; ++j) {
             const int chunk = (j * NWV + wave) % C::A_CH;
-            const int row = chunk * 32 + dma_row(lane);
-            const int h = (lane & 1) ^ (row & 1);
+            const int row = chunk * 32 + dma_a_row(lane);
+            const int h = dma_a_h(lane);
             const int p = m0 + row;
             const bool ok = p < q.m;
             const int pp = ok ? p : m0;
@@ -183,8 +185,8 @@ void igemm_kernel(ConvArgs a, ConvArgs pj, int tiles_n, int per_xcd)
 #pragma unroll
         for (int j = 0; j < C::BI; ++j) {
             const int chunk = (j * NWV + wave) % C::B_CH;
-            const int row = chunk * 32 + dma_row(lane);
-            const int h = (lane & 1) ^ ((row >> 4) & 1);
+            const int row = chunk * 32 + dma_b_row(lane);
+            const int h = dma_b_h(lane);
             const int R = n0 + row;
             b_ok[j] = R < wrows;
             const int RR = b_ok[j] ? R : 0;
