@@ -37,8 +37,8 @@ template <int BM, int BN, int ST>
 struct IgCfg {
     static constexpr int WAVES_M = BM / 64;
     static constexpr int WAVES = WAVES_M * (BN / 64);
-    static_assert(WAVES == 4, "four waves, one 64x64 sub-tile each");
-    static constexpr int THREADS = 256;
+    static_assert(WAVES == 4 || WAVES == 8, "four or eight waves, one 64x64 sub-tile each");
+    static constexpr int THREADS = 64 * WAVES;
     static constexpr int A_CH = BM / 32;  // 32-row chunks of a tile's pixels
     static constexpr int B_CH = BN / 32;  // 32-row chunks of a tile's output channels
     static constexpr int AI = 2 * A_CH / WAVES;  // activation DMAs per wave per K-step
@@ -49,7 +49,14 @@ struct IgCfg {
     static constexpr int LPS = AI + BI;          // DMAs per wave per stage
     // ring | parameters | shortcut tile (RES) | parameters of the projection (PROJ)
     static constexpr int lds(bool res) { return ST * STAGE + PARAM + (res ? BM * BN : 0); }  // ring | params | shortcut
-    static constexpr int wg_per_cu(bool res) { return kLdsBytes / lds(res) > 4 ? 4 : kLdsBytes / lds(res); }
+    // at most four waves per SIMD (so up to 128 VGPRs each), as LDS allows
+    static constexpr int wg_per_cu(bool res)
+    {
+        return kLdsBytes / lds(res) > 16 / WAVES ? 16 / WAVES : kLdsBytes / lds(res);
+    }
+    // the epilogue stages each wave's 64x64 output in the ring slot no wave reads any more, or,
+    // when the waves' 4 KB parts do not fit one slot, across the ring after a workgroup barrier
+    static constexpr bool STAGE_IN_SLOT = WAVES * 4096 <= STAGE;
 };
 
 // LDS layouts of one operand block of a stage (32 K-bytes per row, two 16-byte halves h).
@@ -78,6 +85,11 @@ __device__ __forceinline__ int dma_a_h(int lane) { return (lane & 1) ^ (dma_a_ro
 __device__ __forceinline__ int dma_b_row(int lane) { return 4 * (lane >> 3) + (((lane & 7) ^ ((lane >> 3) & 6)) >> 1); }
 __device__ __forceinline__ int dma_b_h(int lane) { return lane & 1; }
 
+template <int V>
+struct Slot {
+    static constexpr int value = V;
+};
+
 // Requantise the wave's accumulators (MODE picked by a wave vote on the shifts) into the LDS tile
 // at rbase (row stride 64 B), adding the shortcut bytes already there when RES.  ADD_BIAS: the
 // accumulators do not hold the bias yet.
@@ -96,12 +108,13 @@ __device__ __forceinline__ void requant_to_lds(const v4i (&acc)[4][4], int8_t *r
 // projection is computed first and requantised (no ReLU) into the LDS that otherwise receives
 // a shortcut tile, so the shortcut never goes through HBM.
 template <int KH, int KW, int BM, int BN, int ST, bool RES, bool RELU, bool PROJ>
-__global__ __launch_bounds__(256, (IgCfg<BM, BN, ST>::wg_per_cu(RES)))
+__global__ __launch_bounds__((IgCfg<BM, BN, ST>::THREADS), (IgCfg<BM, BN, ST>::wg_per_cu(RES)))
 void igemm_kernel(ConvArgs a, ConvArgs pj, int tiles_n, int per_xcd)
 {
     using C = IgCfg<BM, BN, ST>;
     constexpr int NWV = C::WAVES;
     static_assert(!PROJ || (RES && KH == 1 && KW == 1), "a projection shortcut feeds a 1x1 shortcut conv");
+    static_assert(!PROJ || ST == 2, "the stream switches convolutions one stage ahead");
     __shared__ __attribute__((aligned(1024))) int8_t smem[C::lds(RES)];
     int8_t *const Pm = smem + ST * C::STAGE;
 
@@ -146,8 +159,8 @@ void igemm_kernel(ConvArgs a, ConvArgs pj, int tiles_n, int per_xcd)
     int HW = 0, wblk = 0, qi1 = 0, qnkb = 0, qw = 0;
     v4i rsA, rsB;
     int a_base[C::AI], b_base[C::BI];
-    unsigned a_mask[C::AI];
-    bool b_ok[C::BI];
+    unsigned a_nmask[C::AI];  // complement of the lane's tap-validity mask (bit 31 always set)
+    unsigned b_bad[C::BI];    // 1 << 31 for a weight row past the buffer, else 0
     auto plan = [&](const ConvArgs &q) {
         HW = q.h * q.w;
         qi1 = q.i1;
@@ -180,7 +193,7 @@ void igemm_kernel(ConvArgs a, ConvArgs pj, int tiles_n, int per_xcd)
                 for (int kx = 0; kx < KW; ++kx)
                     if ((unsigned)(iy0 + ky) < (unsigned)q.h && (unsigned)(ix0 + kx) < (unsigned)q.w)
                         mask |= 1u << (ky * KW + kx);
-            a_mask[j] = ok ? mask : 0u;
+            a_nmask[j] = ok ? ~mask : ~0u;
         }
 #pragma unroll
         for (int j = 0; j < C::BI; ++j) {
@@ -188,8 +201,9 @@ void igemm_kernel(ConvArgs a, ConvArgs pj, int tiles_n, int per_xcd)
             const int row = chunk * 32 + dma_b_row(lane);
             const int h = dma_b_h(lane);
             const int R = n0 + row;
-            b_ok[j] = R < wrows;
-            const int RR = b_ok[j] ? R : 0;
+            const bool rok = R < wrows;
+            b_bad[j] = rok ? 0u : 0x80000000u;
+            const int RR = rok ? R : 0;
             const int o1 = fdiv(RR, q.o2_mul, q.o2_shr);
             b_base[j] = o1 * (KH * KW * q.i1 * wblk) + (RR - o1 * q.o2) * 32 + h * 16;
         }
@@ -221,12 +235,16 @@ void igemm_kernel(ConvArgs a, ConvArgs pj, int tiles_n, int per_xcd)
         const int dA0 = cur_c1 * HW * 32 + (ky0 * qw + kx0) * 32;
         const int dA1 = c1b * HW * 32 + (ky1 * qw + kx1) * 32;
         const int dB0 = kb0 * wblk, dB1 = dB0 + wblk;
+        // a block past the convolution's K reads tap 31 of the complemented masks (always invalid)
+        // and ORs bit 31 into the weight offsets: either way its lanes fall outside every buffer
+        const int tap0 = v0 ? cur_tap : 31, tap1 = v1 ? tapb : 31;
+        const unsigned nv0 = v0 ? 0u : 0x80000000u, nv1 = v1 ? 0u : 0x80000000u;
 #pragma unroll
         for (int j = 0; j < C::AI; ++j) {
             const int blk = (j * NWV) / C::A_CH;  // A_CH is a multiple of NWV: independent of the wave
             const int chunk = (j * NWV + wave) % C::A_CH;
             // an invalid lane gets bit 31 set: past every buffer range, so its DMA writes zeros
-            const unsigned bad = (blk ? v1 : v0) ? (~a_mask[j] >> (blk ? tapb : cur_tap)) & 1u : 1u;
+            const unsigned bad = (a_nmask[j] >> (blk ? tap1 : tap0)) & 1u;
             const unsigned off = (unsigned)(a_base[j] + (blk ? dA1 : dA0)) | (bad << 31);
             load16_lds(rsA, st + blk * (BM * 32) + chunk * 1024, off);
         }
@@ -235,8 +253,7 @@ void igemm_kernel(ConvArgs a, ConvArgs pj, int tiles_n, int per_xcd)
             const int qq = j * NWV + wave;
             const int blk = qq / C::B_CH;
             const int chunk = qq % C::B_CH;
-            const bool v = (blk ? v1 : v0) && b_ok[j];
-            const unsigned off = v ? (unsigned)(b_base[j] + (blk ? dB1 : dB0)) : kOOB;
+            const unsigned off = (unsigned)(b_base[j] + (blk ? dB1 : dB0)) | b_bad[j] | (blk ? nv1 : nv0);
             load16_lds(rsB, st + BM * 64 + blk * (BN * 32) + chunk * 1024, off);
         }
         cur_c1 += 2;
@@ -319,18 +336,21 @@ void igemm_kernel(ConvArgs a, ConvArgs pj, int tiles_n, int per_xcd)
             for (int tn = 0; tn < 4; ++tn) acc[tm][tn] = (v4i){bias4[tn], bias4[tn], bias4[tn], bias4[tn]};
     };
 
-    static_assert(ST == 2, "the up-front waits below count one stage in flight");
-    auto step = [&](int s) {
-        // this wave's DMAs of stage s (and, at s = 0, the tile inputs); stage s+1 may stay in flight
-        // when it was requested before them (up front), never when it was requested at step s-1
-        if (upfront && s + 1 < nsteps)
-            wait_vmcnt<C::LPS>();
+    static_assert(ST == 2 || ST == 3, "the waits below count at most one later stage in flight");
+    // step s reads ring slot SL = s % ST, a compile-time constant so the fragment addresses
+    // need no per-step arithmetic
+    auto step = [&](auto slot, int s) {
+        constexpr int SL = decltype(slot)::value;
+        // this wave's DMAs of stage s (and, at s = 0, the tile inputs): later stages requested
+        // before them may stay in flight (one when up front, ST-2 in the ring)
+        if (upfront ? s + 1 < nsteps : (ST > 2 && s + ST - 2 < nsteps))
+            wait_vmcnt<(ST > 2 ? ST - 2 : 1) * C::LPS>();
         else
             wait_vmcnt<0>();
         ring_barrier();  // ... and every other wave's; stage s-1's slot is free again
         if (s == 0) init_acc(PROJ ? Rres : Pw);  // this wave's parameters have landed too
-        if (!upfront && s + ST - 1 < nsteps) issue((s + ST - 1) % ST);
-        const int8_t *st = smem + (s % ST) * C::STAGE;
+        if (!upfront && s + ST - 1 < nsteps) issue((SL + ST - 1) % ST);
+        const int8_t *st = smem + SL * C::STAGE;
         v4i af[4], bf[4];
 #pragma unroll
         for (int tm = 0; tm < 4; ++tm) af[tm] = *(const v4i *)(st + a_frag + 512 * tm);
@@ -342,20 +362,30 @@ void igemm_kernel(ConvArgs a, ConvArgs pj, int tiles_n, int per_xcd)
             for (int tn = 0; tn < 4; ++tn)
                 acc[tm][tn] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[tm], bf[tn], acc[tm][tn], 0, 0, 0);
     };
+    auto step_rt = [&](int s) {  // runtime slot (ST == 2)
+        if (s & 1)
+            step(Slot<1>(), s);
+        else
+            step(Slot<0>(), s);
+    };
     if (PROJ) {
-        for (int s = 0; s + 1 < n1; ++s) step(s);
+        for (int s = 0; s + 1 < n1; ++s) step_rt(s);
         if (!upfront) {
             plan(a);  // the last projection step requests a's first stage
             cur_c1 = 0;
             cur_tap = 0;
         }
-        step(n1 - 1);
+        step_rt(n1 - 1);
         // the projection is complete: its requantised output (no ReLU) is the shortcut
         requant_to_lds<false, false, true>(acc, Rres + g * 64 + 4 * c, Rres, c, ocl, pj.oc);
         init_acc(Pw);
-        for (int s = n1; s < nsteps; ++s) step(s);
+        for (int s = n1; s < nsteps; ++s) step_rt(s);
     } else {
-        for (int s = 0; s < nsteps; ++s) step(s);
+        for (int s = 0; s < nsteps; s += ST) {
+            step(Slot<0>(), s);
+            if (s + 1 < nsteps) step(Slot<1>(), s + 1);
+            if (ST > 2 && s + 2 < nsteps) step(Slot<ST - 1>(), s + 2);
+        }
     }
     if (a.out_i32) {
         int32_t *y = (int32_t *)a.y;
@@ -378,8 +408,9 @@ void igemm_kernel(ConvArgs a, ConvArgs pj, int tiles_n, int per_xcd)
             }
         return;
     }
-    // staging: the shortcut tile itself (requantised in place), else the ring slot no wave reads any more
-    int8_t *const Rw = RES ? Rres : smem + (nsteps % ST) * C::STAGE + wave * 4096;
+    // staging: the shortcut tile itself (requantised in place), else free ring memory
+    if (!RES && !C::STAGE_IN_SLOT) ring_barrier();
+    int8_t *const Rw = RES ? Rres : smem + (C::STAGE_IN_SLOT ? (nsteps % ST) * C::STAGE : 0) + wave * 4096;
     requant_to_lds<RES, RELU, PROJ>(acc, Rw + g * 64 + 4 * c, Pw, c, ocl, a.oc);
     wave_lds_sync();
 
@@ -422,10 +453,10 @@ hipError_t launch_ig(const ConvArgs &a, const ConvArgs &pj, hipStream_t s)
     if (imgs * (long long)a.i1 * a.h * a.w * 32 >= 0x7fffffffLL) return hipErrorInvalidValue;
     if (PROJ && imgs * (long long)pj.i1 * pj.h * pj.w * 32 >= 0x7fffffffLL) return hipErrorInvalidValue;
     if (a.relu)
-        hipLaunchKernelGGL((igemm_kernel<KH, KW, BM, BN, ST, RES, true, PROJ>), dim3((unsigned)grid), dim3(256), 0, s,
+        hipLaunchKernelGGL((igemm_kernel<KH, KW, BM, BN, ST, RES, true, PROJ>), dim3((unsigned)grid), dim3(IgCfg<BM, BN, ST>::THREADS), 0, s,
                            a, pj, tiles_n, (int)per);
     else
-        hipLaunchKernelGGL((igemm_kernel<KH, KW, BM, BN, ST, RES, false, PROJ>), dim3((unsigned)grid), dim3(256), 0,
+        hipLaunchKernelGGL((igemm_kernel<KH, KW, BM, BN, ST, RES, false, PROJ>), dim3((unsigned)grid), dim3(IgCfg<BM, BN, ST>::THREADS), 0,
                            s, a, pj, tiles_n, (int)per);
     return hipGetLastError();
 }
