@@ -44,7 +44,10 @@ def kernel_name(spec, nhwc_input=True, proj=False) -> str:
     i1 = (spec.c_in + 31) // 32
     if spec.k == 1 and spec.pad == 0 and i1 <= 4 and not proj:
         return f"conv1x1_kernel<{bm}, {bn}, {(i1 + 1) // 2}, {res}, {relu}>"
-    return f"igemm_kernel<{spec.k}, {spec.k}, {bm}, {bn}, 2, {res}, {relu}, {'true' if proj else 'false'}>"
+    st = 2
+    if spec.k == 1 and oc_pad > 64 and res == "false":
+        bm, bn, st = 256, 128, 3  # wide 1x1 convolutions without a shortcut
+    return f"igemm_kernel<{spec.k}, {spec.k}, {bm}, {bn}, {st}, {res}, {relu}, {'true' if proj else 'false'}>"
 
 
 # Sources each kernel family is built from: HBM traffic taken from counters is only

@@ -469,6 +469,9 @@ hipError_t launch_ig_k(const ConvArgs &a, hipStream_t s)
     if (a.residual)
         return wide ? launch_ig<KH, KW, 128, 128, ST, true, false>(a, a, s)
                     : launch_ig<KH, KW, 256, 64, ST, true, false>(a, a, s);
+    // the wide 1x1 convolutions without a shortcut (K of 256..2048, few pixels per tile column)
+    // run eight-wave 256x128 tiles on a three-stage ring: twice the MACs per operand byte
+    if (KH == 1 && KW == 1 && wide) return launch_ig<1, 1, 256, 128, 3, false, false>(a, a, s);
     return wide ? launch_ig<KH, KW, 128, 128, ST, false, false>(a, a, s)
                 : launch_ig<KH, KW, 256, 64, ST, false, false>(a, a, s);
 }

@@ -159,6 +159,11 @@ FUSED_SHAPES = [
     (1, 15, 14, 128, 128, 3, 2, 1),
     (1, 5, 6, 3, 40, 3, 1, 1),
     (3, 7, 7, 512, 2048, 1, 1, 0),
+    # wide 1x1 without a shortcut: 256x128 tiles on a three-stage ring
+    (2, 9, 7, 160, 200, 1, 1, 0),    # 5 channel blocks: 3 K-steps, all requested up front, odd tail
+    (1, 11, 10, 192, 136, 1, 2, 0),  # strided, exactly 3 K-steps, ragged output channels
+    (1, 6, 7, 256, 384, 1, 1, 0),    # 4 K-steps through the ring
+    (2, 5, 5, 320, 256, 1, 1, 0),    # 5 K-steps through the ring
 ]
 
 
