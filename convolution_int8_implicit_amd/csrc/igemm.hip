@@ -161,7 +161,7 @@ void igemm_kernel(ConvArgs a, ConvArgs pj, int tiles_n, int per_xcd)
     int a_base[C::AI], b_base[C::BI];
     unsigned a_nmask[C::AI];  // complement of the lane's tap-validity mask (bit 31 always set)
     unsigned b_bad[C::BI];    // 1 << 31 for a weight row past the buffer, else 0
-    auto plan = [&](const ConvArgs &q) {
+    auto plan = [&](const ConvArgs &q) __attribute__((always_inline)) {
         HW = q.h * q.w;
         qi1 = q.i1;
         qnkb = q.nkb;
@@ -219,7 +219,7 @@ void igemm_kernel(ConvArgs a, ConvArgs pj, int tiles_n, int per_xcd)
         plan(pj);
     else
         plan(a);
-    auto issue = [&](int slot) {
+    auto issue = [&](int slot) __attribute__((always_inline)) {
         const int s = iss - (iss >= n1 ? n1 : 0);
         ++iss;
         int8_t *st = smem + slot * C::STAGE;
@@ -265,7 +265,7 @@ void igemm_kernel(ConvArgs a, ConvArgs pj, int tiles_n, int per_xcd)
 
     issue(0);
     // per-channel parameters and the shortcut part of this wave
-    auto issue_params = [&](const ConvArgs &q, int8_t *dst) {
+    auto issue_params = [&](const ConvArgs &q, int8_t *dst) __attribute__((always_inline)) {
         if (lane < 16) {
             const bool v = ch0 + 4 * lane < q.oc;
             const unsigned off = v ? (unsigned)(ch0 + 4 * lane) * 4 : kOOB;
@@ -317,30 +317,16 @@ void igemm_kernel(ConvArgs a, ConvArgs pj, int tiles_n, int per_xcd)
     const int ocl = ch0 + 4 * c;
     const int pbase = m0 + wm0;
 
-    // Without a projection the accumulators start at the per-channel bias (y = acc + bias needs no
-    // add afterwards; channels past Oc read a zero bias, their DMA lanes being out of range).  The
-    // fused form starts both contractions at zero and adds the bias in the requantisation: holding
-    // bias-filled accumulators next to the projection's would cost registers it does not have.
-    auto init_acc = [&](const int8_t *P) {
-        if (PROJ) {
-#pragma unroll
-            for (int tm = 0; tm < 4; ++tm)
-#pragma unroll
-                for (int tn = 0; tn < 4; ++tn) acc[tm][tn] = (v4i){0, 0, 0, 0};
-            return;
-        }
-        const v4i bias4 = *(const v4i *)(P + c * 16);
-#pragma unroll
-        for (int tm = 0; tm < 4; ++tm)
-#pragma unroll
-            for (int tn = 0; tn < 4; ++tn) acc[tm][tn] = (v4i){bias4[tn], bias4[tn], bias4[tn], bias4[tn]};
-    };
+    // The first K-step of a contraction takes 0 as the MFMA's C operand, so no accumulator is
+    // ever cleared; the per-channel bias enters in the requantisation (folded into its added
+    // constant, free in the common mode).
 
     static_assert(ST == 2 || ST == 3, "the waits below count at most one later stage in flight");
     // step s reads ring slot SL = s % ST, a compile-time constant so the fragment addresses
     // need no per-step arithmetic
-    auto step = [&](auto slot, int s) {
+    auto step = [&](auto slot, auto first, int s) __attribute__((always_inline)) {
         constexpr int SL = decltype(slot)::value;
+        constexpr bool FIRST = decltype(first)::value != 0;
         // this wave's DMAs of stage s (and, at s = 0, the tile inputs): later stages requested
         // before them may stay in flight (one when up front, ST-2 in the ring)
         if (upfront ? s + 1 < nsteps : (ST > 2 && s + ST - 2 < nsteps))
@@ -348,7 +334,6 @@ void igemm_kernel(ConvArgs a, ConvArgs pj, int tiles_n, int per_xcd)
         else
             wait_vmcnt<0>();
         ring_barrier();  // ... and every other wave's; stage s-1's slot is free again
-        if (s == 0) init_acc(PROJ ? Rres : Pw);  // this wave's parameters have landed too
         if (!upfront && s + ST - 1 < nsteps) issue((SL + ST - 1) % ST);
         const int8_t *st = smem + SL * C::STAGE;
         v4i af[4], bf[4];
@@ -360,36 +345,49 @@ void igemm_kernel(ConvArgs a, ConvArgs pj, int tiles_n, int per_xcd)
         for (int tm = 0; tm < 4; ++tm)
 #pragma unroll
             for (int tn = 0; tn < 4; ++tn)
-                acc[tm][tn] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[tm], bf[tn], acc[tm][tn], 0, 0, 0);
+                if constexpr (FIRST)
+                    acc[tm][tn] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[tm], bf[tn], (v4i){0, 0, 0, 0}, 0, 0, 0);
+                else
+                    acc[tm][tn] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[tm], bf[tn], acc[tm][tn], 0, 0, 0);
     };
-    auto step_rt = [&](int s) {  // runtime slot (ST == 2)
-        if (s & 1)
-            step(Slot<1>(), s);
-        else
-            step(Slot<0>(), s);
+    auto step_rt = [&](int s, bool first) __attribute__((always_inline)) {  // runtime slot (ST == 2)
+        if (first) {
+            if (s & 1)
+                step(Slot<1>(), Slot<1>(), s);
+            else
+                step(Slot<0>(), Slot<1>(), s);
+        } else {
+            if (s & 1)
+                step(Slot<1>(), Slot<0>(), s);
+            else
+                step(Slot<0>(), Slot<0>(), s);
+        }
     };
     if (PROJ) {
-        for (int s = 0; s + 1 < n1; ++s) step_rt(s);
+        for (int s = 0; s + 1 < n1; ++s) step_rt(s, s == 0);
         if (!upfront) {
             plan(a);  // the last projection step requests a's first stage
             cur_c1 = 0;
             cur_tap = 0;
         }
-        step_rt(n1 - 1);
+        step_rt(n1 - 1, n1 == 1);
         // the projection is complete: its requantised output (no ReLU) is the shortcut
         requant_to_lds<false, false, true>(acc, Rres + g * 64 + 4 * c, Rres, c, ocl, pj.oc);
-        init_acc(Pw);
-        for (int s = n1; s < nsteps; ++s) step_rt(s);
+        for (int s = n1; s < nsteps; ++s) step_rt(s, s == n1);
     } else {
-        for (int s = 0; s < nsteps; s += ST) {
-            step(Slot<0>(), s);
-            if (s + 1 < nsteps) step(Slot<1>(), s + 1);
-            if (ST > 2 && s + 2 < nsteps) step(Slot<ST - 1>(), s + 2);
+        step(Slot<0>(), Slot<1>(), 0);
+        if (1 < nsteps) step(Slot<1>(), Slot<0>(), 1);
+        if (ST > 2 && 2 < nsteps) step(Slot<ST - 1>(), Slot<0>(), 2);
+        for (int s = ST; s < nsteps; s += ST) {
+            step(Slot<0>(), Slot<0>(), s);
+            if (s + 1 < nsteps) step(Slot<1>(), Slot<0>(), s + 1);
+            if (ST > 2 && s + 2 < nsteps) step(Slot<ST - 1>(), Slot<0>(), s + 2);
         }
     }
     if (a.out_i32) {
         int32_t *y = (int32_t *)a.y;
         const bool vec = (a.oc & 3) == 0 && ocl + 3 < a.oc;
+        const v4i bias4 = *(const v4i *)(Pw + c * 16);  // zero past Oc (out-of-range DMA lanes)
 #pragma unroll
         for (int tm = 0; tm < 4; ++tm)
 #pragma unroll
@@ -397,7 +395,7 @@ void igemm_kernel(ConvArgs a, ConvArgs pj, int tiles_n, int per_xcd)
                 const int p = pbase + 16 * tm + 4 * i + g;
                 if (p >= a.m) continue;
                 const long long off = (long long)p * a.oc + ocl;
-                const v4i v = {acc[tm][0][i], acc[tm][1][i], acc[tm][2][i], acc[tm][3][i]};
+                const v4i v = (v4i){acc[tm][0][i], acc[tm][1][i], acc[tm][2][i], acc[tm][3][i]} + bias4;
                 if (vec) {
                     *(v4i *)(y + off) = v;
                 } else {
@@ -411,7 +409,7 @@ void igemm_kernel(ConvArgs a, ConvArgs pj, int tiles_n, int per_xcd)
     // staging: the shortcut tile itself (requantised in place), else free ring memory
     if (!RES && !C::STAGE_IN_SLOT) ring_barrier();
     int8_t *const Rw = RES ? Rres : smem + (C::STAGE_IN_SLOT ? (nsteps % ST) * C::STAGE : 0) + wave * 4096;
-    requant_to_lds<RES, RELU, PROJ>(acc, Rw + g * 64 + 4 * c, Pw, c, ocl, a.oc);
+    requant_to_lds<RES, RELU, true>(acc, Rw + g * 64 + 4 * c, Pw, c, ocl, a.oc);
     wave_lds_sync();
 
     // 16-byte stores of the wave's 64 pixels x 64 channels
