@@ -148,11 +148,8 @@ void conv1x1_kernel(ConvArgs a, int tiles_n)
     ring_barrier();
     const int c = lane & 15;
     const int g = lane >> 4;
+    // the first K-step's MFMAs take 0 as their C operand: no accumulator is cleared
     v4i acc[4][4];
-#pragma unroll
-    for (int tm = 0; tm < 4; ++tm)
-#pragma unroll
-        for (int tn = 0; tn < 4; ++tn) acc[tm][tn] = (v4i){0, 0, 0, 0};
 #pragma unroll
     for (int s = 0; s < NST; ++s) {
         const int8_t *st = smem + s * C::STAGE;
@@ -172,7 +169,8 @@ void conv1x1_kernel(ConvArgs a, int tiles_n)
         for (int tm = 0; tm < 4; ++tm)
 #pragma unroll
             for (int tn = 0; tn < 4; ++tn)
-                acc[tm][tn] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[tm], bf[tn], acc[tm][tn], 0, 0, 0);
+                acc[tm][tn] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[tm], bf[tn], s == 0 ? (v4i){0, 0, 0, 0} : acc[tm][tn],
+                                                                    0, 0, 0);
     }
 
     // ---- epilogue: this wave's own shortcut and parameters (no other wave's data)

@@ -172,6 +172,7 @@ __device__ __forceinline__ unsigned pkmax(unsigned x, unsigned y)
 // shift, and for shift >= 2 the rounding high word 2^(shift-2) and shift - 1.
 struct ChanParams {
     int bias[kOC], mul[kOC], shf[kOC], rnd[kOC], shm[kOC];
+    int add_lo[kOC], add_hi[kOC];  // bias * mult + (rnd << 32): the bias folded into mode 1's constant
 };
 
 // Convolution of one tile into sConv (biased int8 [pixel][channel]).
@@ -184,6 +185,7 @@ __device__ __forceinline__ void conv_tile(const StemArgs &a, const Tile &g, cons
     const int wave = threadIdx.x >> 6;
     const int c = lane & 15, grp = lane >> 4;
     const int kh_off = grp >> 1;    // kernel row within a K step (two rows per step)
+    const bool interior = g.cy0 >= 0 && g.cx0 >= 0 && g.cy0 + kCT <= a.ho && g.cx0 + kCT <= a.wo;
     const int kw0 = 4 * (grp & 1);  // first kernel column of this lane's 16 bytes
     for (int tm = wave; tm < kMT; tm += 4) {
         int q = 16 * tm + (lane & 15);
@@ -204,32 +206,38 @@ __device__ __forceinline__ void conv_tile(const StemArgs &a, const Tile &g, cons
         const v4i shf = *(const v4i *)&P.shf[4 * c];
         const v4i rnd = *(const v4i *)&P.rnd[4 * c];
         const v4i shm = *(const v4i *)&P.shm[4 * c];
+        const v4i alo = *(const v4i *)&P.add_lo[4 * c];
+        const v4i ahi = *(const v4i *)&P.add_hi[4 * c];
+        // only tiles at the image border (or the last, partial row tile) need per-pixel checks
+        const bool edge = !interior || tm == kMT - 1;
         // lane (grp, c) holds conv pixels 16tm + 4grp + i, channels 4c + tn; pixels outside
         // the convolution output are stored as 0 (= -128) so the max ignores them (every
         // pooling window holds its centre pixel, which is inside)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int qq = 16 * tm + 4 * grp + i;
-            if (qq >= kCPix) continue;
-            const int qy = qq / kCT, qx = qq - (qq / kCT) * kCT;
-            const bool inside = (unsigned)(g.cy0 + qy) < (unsigned)a.ho && (unsigned)(g.cx0 + qx) < (unsigned)a.wo;
+            bool inside = true;
+            if (edge) {
+                const int qy = qq / kCT, qx = qq - (qq / kCT) * kCT;
+                inside = qq < kCPix && (unsigned)(g.cy0 + qy) < (unsigned)a.ho && (unsigned)(g.cx0 + qx) < (unsigned)a.wo;
+            }
             int r[4];
 #pragma unroll
             for (int tn = 0; tn < 4; ++tn) {
-                const int y = acc[tn][i] + bias[tn];
                 int v;
                 if (MODE == 0) {
-                    v = requant_any(y, mul[tn], shf[tn]);
+                    v = requant_any(acc[tn][i] + bias[tn], mul[tn], shf[tn]);
                     if (a.relu) v = max(v, 0);
                 } else if (MODE == 1) {
-                    v = max(requant_relu(y, mul[tn], rnd[tn], shm[tn]), 0);
+                    const long long add = (long long)(((unsigned long long)(unsigned)ahi[tn] << 32) | (unsigned)alo[tn]);
+                    v = max(((int)(((long long)acc[tn][i] * (long long)mul[tn] + add) >> 32)) >> shm[tn], 0);
                 } else {
-                    v = requant_fast(y, mul[tn], rnd[tn], shm[tn]);
+                    v = requant_fast(acc[tn][i] + bias[tn], mul[tn], rnd[tn], shm[tn]);
                 }
                 r[tn] = min(max(v, -128), 127);
             }
             const unsigned word = inside ? (pack4(r[0], r[1], r[2], r[3]) ^ 0x80808080u) : 0u;
-            *(unsigned *)&sConv[qq * kOC + 4 * c] = word;
+            if (!edge || qq < kCPix) *(unsigned *)&sConv[qq * kOC + 4 * c] = word;
         }
     }
 }
@@ -270,6 +278,9 @@ __global__ __launch_bounds__(kThreads) void stem_kernel(StemArgs a, int tiles, i
         sP.shf[tid] = sh;
         sP.rnd[tid] = 1 << ((sh - 2) & 31);
         sP.shm[tid] = sh - 1;
+        const long long add = (long long)a.bias[tid] * a.mult[tid] + ((long long)(1 << ((sh - 2) & 31)) << 32);
+        sP.add_lo[tid] = (int)(unsigned)(add & 0xffffffffLL);
+        sP.add_hi[tid] = (int)(add >> 32);
     }
     // one wave reads all 64 shifts, and every wave takes the same decision
     const bool fast = __all(a.shift[lane] >= 2);
