@@ -47,6 +47,8 @@ def kernel_name(spec, nhwc_input=True, proj=False) -> str:
     st = 2
     if spec.k == 1 and oc_pad > 64 and res == "false":
         bm, bn, st = 256, 128, 3  # wide 1x1 convolutions without a shortcut
+    if spec.k == 3 and spec.stride == 2 and oc_pad >= 256 and res == "false":
+        bm, bn = 128, 256  # strided 3x3 with >= 256 output channels
     return f"igemm_kernel<{spec.k}, {spec.k}, {bm}, {bn}, {st}, {res}, {relu}, {'true' if proj else 'false'}>"
 
 

@@ -43,7 +43,7 @@ struct IgCfg {
     static constexpr int B_CH = BN / 32;  // 32-row chunks of a tile's output channels
     static constexpr int AI = 2 * A_CH / WAVES;  // activation DMAs per wave per K-step
     static constexpr int BI = 2 * B_CH / WAVES;  // weight DMAs per wave per K-step
-    static_assert(AI * WAVES == 2 * A_CH && BI * WAVES == 2 * B_CH && A_CH % WAVES == 0, "whole DMAs");
+    static_assert(AI * WAVES == 2 * A_CH && BI * WAVES == 2 * B_CH, "whole DMAs");
     static constexpr int STAGE = (BM + BN) * 64;  // A: [2][BM][32 B], then B: [2][BN][32 B]
     static constexpr int PARAM = WAVES * 768;     // per wave: bias, mult, shift of its 64 channels
     static constexpr int LPS = AI + BI;          // DMAs per wave per stage
@@ -241,7 +241,7 @@ void igemm_kernel(ConvArgs a, ConvArgs pj, int tiles_n, int per_xcd)
         const unsigned nv0 = v0 ? 0u : 0x80000000u, nv1 = v1 ? 0u : 0x80000000u;
 #pragma unroll
         for (int j = 0; j < C::AI; ++j) {
-            const int blk = (j * NWV) / C::A_CH;  // A_CH is a multiple of NWV: independent of the wave
+            const int blk = (j * NWV + wave) / C::A_CH;
             const int chunk = (j * NWV + wave) % C::A_CH;
             // an invalid lane gets bit 31 set: past every buffer range, so its DMA writes zeros
             const unsigned bad = (a_nmask[j] >> (blk ? tap1 : tap0)) & 1u;
@@ -470,6 +470,9 @@ hipError_t launch_ig_k(const ConvArgs &a, hipStream_t s)
     // the wide 1x1 convolutions without a shortcut (K of 256..2048, few pixels per tile column)
     // run eight-wave 256x128 tiles on a three-stage ring: twice the MACs per operand byte
     if (KH == 1 && KW == 1 && wide) return launch_ig<1, 1, 256, 128, 3, false, false>(a, a, s);
+    // strided 3x3 with >= 256 output channels: each activation DMA gathers 32-byte pieces, so
+    // 128x256 tiles (eight waves) that read each activation tile once for 256 channels win
+    if (KH == 3 && a.stride == 2 && a.oc1 * 32 >= 256) return launch_ig<3, 3, 128, 256, ST, false, false>(a, a, s);
     return wide ? launch_ig<KH, KW, 128, 128, ST, false, false>(a, a, s)
                 : launch_ig<KH, KW, 256, 64, ST, false, false>(a, a, s);
 }

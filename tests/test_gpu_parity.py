@@ -164,6 +164,9 @@ FUSED_SHAPES = [
     (1, 11, 10, 192, 136, 1, 2, 0),  # strided, exactly 3 K-steps, ragged output channels
     (1, 6, 7, 256, 384, 1, 1, 0),    # 4 K-steps through the ring
     (2, 5, 5, 320, 256, 1, 1, 0),    # 5 K-steps through the ring
+    # strided 3x3 with >= 256 output channels: 128x256 tiles of eight waves
+    (2, 9, 11, 64, 256, 3, 2, 1),
+    (1, 8, 7, 96, 288, 3, 2, 1),     # ragged output channels, odd channel-block count
 ]
 
 
