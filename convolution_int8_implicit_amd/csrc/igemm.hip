@@ -350,30 +350,43 @@ void igemm_kernel(ConvArgs a, ConvArgs pj, int tiles_n, int per_xcd)
                 else
                     acc[tm][tn] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[tm], bf[tn], acc[tm][tn], 0, 0, 0);
     };
-    auto step_rt = [&](int s, bool first) __attribute__((always_inline)) {  // runtime slot (ST == 2)
-        if (first) {
-            if (s & 1)
-                step(Slot<1>(), Slot<1>(), s);
-            else
-                step(Slot<0>(), Slot<1>(), s);
-        } else {
-            if (s & 1)
-                step(Slot<1>(), Slot<0>(), s);
-            else
-                step(Slot<0>(), Slot<0>(), s);
+    // fused form (ST == 2): steps s0 <= s < s1 of one contraction, none its first, slots alternating
+    // inside the loop (a run-time slot choice per step would merge two register allocations of the
+    // accumulators every iteration)
+    auto run_range = [&](int s0, int s1) __attribute__((always_inline)) {
+        int s = s0;
+        if (s < s1 && (s & 1)) step(Slot<1>(), Slot<0>(), s++);
+        for (; s + 1 < s1; s += 2) {
+            step(Slot<0>(), Slot<0>(), s);
+            step(Slot<1>(), Slot<0>(), s + 1);
         }
+        if (s < s1) step(Slot<0>(), Slot<0>(), s);
     };
     if (PROJ) {
-        for (int s = 0; s + 1 < n1; ++s) step_rt(s, s == 0);
-        if (!upfront) {
-            plan(a);  // the last projection step requests a's first stage
-            cur_c1 = 0;
-            cur_tap = 0;
+        // the projection's steps 0 .. n1-1; its last one requests a's first stage
+        auto switch_to_a = [&]() __attribute__((always_inline)) {
+            if (!upfront) {
+                plan(a);
+                cur_c1 = 0;
+                cur_tap = 0;
+            }
+        };
+        if (n1 == 1) {
+            switch_to_a();
+            step(Slot<0>(), Slot<1>(), 0);
+        } else {
+            step(Slot<0>(), Slot<1>(), 0);
+            run_range(1, n1 - 1);
+            switch_to_a();
+            run_range(n1 - 1, n1);
         }
-        step_rt(n1 - 1, n1 == 1);
         // the projection is complete: its requantised output (no ReLU) is the shortcut
         requant_to_lds<false, false, true>(acc, Rres + g * 64 + 4 * c, Rres, c, ocl, pj.oc);
-        for (int s = n1; s < nsteps; ++s) step_rt(s, s == n1);
+        if (n1 & 1)
+            step(Slot<1>(), Slot<1>(), n1);
+        else
+            step(Slot<0>(), Slot<1>(), n1);
+        run_range(n1 + 1, nsteps);
     } else {
         step(Slot<0>(), Slot<1>(), 0);
         if (1 < nsteps) step(Slot<1>(), Slot<0>(), 1);
