@@ -102,7 +102,7 @@ ifx::ConvArgs conv_args(const ifx_conv_desc *d, const Dims &dm, const int8_t *x,
 // Launch one validated convolution.
 ifx_status run_conv(const ifx_conv_desc *d, Kind kind, const Dims &dm, const int8_t *x, const int8_t *w,
                     const int32_t *bias, const int32_t *mult, const int32_t *shift, const int8_t *res, void *y,
-                    hipStream_t s)
+                    hipStream_t s, int32_t *part = nullptr, size_t part_bytes = 0)
 {
     if (kind == kStem) {
         ifx::StemArgs a;
@@ -124,7 +124,15 @@ ifx_status run_conv(const ifx_conv_desc *d, Kind kind, const Dims &dm, const int
         a.relu = (d->flags & IFX_RELU) ? 1 : 0;
         return hip_status(ifx::launch_stem(a, s));
     }
-    return hip_status(ifx::launch_conv(conv_args(d, dm, x, w, bias, mult, shift, res, y), d->kh, d->kw, s));
+    return hip_status(
+        ifx::launch_conv_split(conv_args(d, dm, x, w, bias, mult, shift, res, y), d->kh, d->kw, part, part_bytes, s));
+}
+
+// Partial-sum bytes run_conv may use for a validated non-stem convolution (split-K).
+size_t conv_part_bytes(const ifx_conv_desc *d, const Dims &dm)
+{
+    return ifx::splitk_bytes(conv_args(d, dm, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr), d->kh,
+                             d->kw);
 }
 
 // Kernel arguments of a validated non-stem convolution.
@@ -155,6 +163,8 @@ ifx::ConvArgs conv_args(const ifx_conv_desc *d, const Dims &dm, const int8_t *x,
     a.relu = (d->flags & IFX_RELU) ? 1 : 0;
     a.residual = (d->flags & IFX_RESIDUAL) ? 1 : 0;
     a.out_i32 = (d->flags & IFX_OUT_I32) ? 1 : 0;
+    a.ksplit = 1;
+    a.kb_per = 0;
     ifx::fastdiv_magic((unsigned)(dm.ho * dm.wo), &a.howo_mul, &a.howo_shr);
     ifx::fastdiv_magic((unsigned)dm.wo, &a.wo_mul, &a.wo_shr);
     ifx::fastdiv_magic((unsigned)a.o2, &a.o2_mul, &a.o2_shr);
@@ -180,9 +190,11 @@ struct BlockPlan {
     Kind kind[4];
     Dims dims[4];
     size_t t1, t2, sc;  // workspace pieces (bytes, 256-aligned)
+    size_t part;        // split-K partial sums (bytes, 256-aligned; 0 when no conv splits)
 };
 
 bool flags_plain(uint32_t f) { return (f & (IFX_RESIDUAL | IFX_MAXPOOL | IFX_OUT_I32)) == 0; }
+bool proj_fusable(const ifx_conv_desc *d3, const ifx_conv_desc *dp);
 
 // Validate the block's descriptors for batch n (n <= 0: use d[0].n) and their chaining.
 ifx_status plan_block(const ifx_block_params *p, int n, BlockPlan *plan)
@@ -217,6 +229,12 @@ ifx_status plan_block(const ifx_block_params *p, int n, BlockPlan *plan)
     plan->t1 = round_up(act_bytes(d[0].n, a.oh, a.ow, d[0].c_out), 256);
     plan->t2 = round_up(act_bytes(d[1].n, b.oh, b.ow, d[1].c_out), 256);
     plan->sc = p->has_proj ? round_up(act_bytes(d[3].n, plan->dims[3].oh, plan->dims[3].ow, d[3].c_out), 256) : 0;
+    // split-K partial sums of c1, c2 and the conv3 / projection that do not run fused
+    plan->part = std::max(conv_part_bytes(&d[0], plan->dims[0]), conv_part_bytes(&d[1], plan->dims[1]));
+    if (!(p->has_proj && proj_fusable(&d[2], &d[3]))) {
+        plan->part = std::max(plan->part, conv_part_bytes(&d[2], plan->dims[2]));
+        if (p->has_proj) plan->part = std::max(plan->part, conv_part_bytes(&d[3], plan->dims[3]));
+    }
     return IFX_OK;
 }
 
@@ -240,7 +258,7 @@ bool proj_fusable(const ifx_conv_desc *d3, const ifx_conv_desc *dp)
 
 // Launch a validated block for batch n; workspace already checked.
 ifx_status run_block(const ifx_block_params *p, const BlockPlan &plan, int n, const int8_t *x, int8_t *y,
-                     int8_t *ws, hipStream_t s)
+                     int8_t *ws, int32_t *part, size_t part_bytes, hipStream_t s)
 {
     ifx_conv_desc d[4];
     const int nd = p->has_proj ? 4 : 3;
@@ -252,9 +270,11 @@ ifx_status run_block(const ifx_block_params *p, const BlockPlan &plan, int n, co
     int8_t *t2 = ws + plan.t1;
     int8_t *sc = ws + plan.t1 + plan.t2;
     ifx_status st;
-    st = run_conv(&d[0], kGeneric, plan.dims[0], x, p->w_blk[0], p->bias[0], p->mult[0], p->shift[0], nullptr, t1, s);
+    st = run_conv(&d[0], kGeneric, plan.dims[0], x, p->w_blk[0], p->bias[0], p->mult[0], p->shift[0], nullptr, t1, s,
+                  part, part_bytes);
     if (st != IFX_OK) return st;
-    st = run_conv(&d[1], kGeneric, plan.dims[1], t1, p->w_blk[1], p->bias[1], p->mult[1], p->shift[1], nullptr, t2, s);
+    st = run_conv(&d[1], kGeneric, plan.dims[1], t1, p->w_blk[1], p->bias[1], p->mult[1], p->shift[1], nullptr, t2, s,
+                  part, part_bytes);
     if (st != IFX_OK) return st;
     const int8_t *res = x;
     if (p->has_proj) {
@@ -267,11 +287,12 @@ ifx_status run_block(const ifx_block_params *p, const BlockPlan &plan, int n, co
             return hip_status(ifx::launch_conv_proj(a, pj, s));
         }
         st = run_conv(&d[3], kGeneric, plan.dims[3], x, p->w_blk[3], p->bias[3], p->mult[3], p->shift[3], nullptr,
-                      sc, s);
+                      sc, s, part, part_bytes);
         if (st != IFX_OK) return st;
         res = sc;
     }
-    return run_conv(&d[2], kGeneric, plan.dims[2], t2, p->w_blk[2], p->bias[2], p->mult[2], p->shift[2], res, y, s);
+    return run_conv(&d[2], kGeneric, plan.dims[2], t2, p->w_blk[2], p->bias[2], p->mult[2], p->shift[2], res, y, s,
+                    part, part_bytes);
 }
 
 // ---- network ----
@@ -280,6 +301,7 @@ struct NetPlan {
     Kind stem_kind;
     Dims stem_dims;
     size_t act, t1, t2, sc, pool;  // workspace pieces for batch nb
+    size_t part;                   // split-K partial sums (max over the network's convolutions)
     int out_h, out_w, out_c;       // backbone output
     int nb;                        // images per pass
 };
@@ -297,7 +319,7 @@ ifx_status plan_net(const ifx_net_params *p, int n, NetPlan *plan)
     if (st != IFX_OK) return st;
     if (plan->stem_kind != kStem) return IFX_E_UNSUPPORTED;
     int h = plan->stem_dims.oh, w = plan->stem_dims.ow, c = stem.c_out;
-    size_t act = act_bytes(nb, h, w, c), t1 = 0, t2 = 0, sc = 0;
+    size_t act = act_bytes(nb, h, w, c), t1 = 0, t2 = 0, sc = 0, part = 0;
     for (int i = 0; i < p->n_blocks; ++i) {
         const ifx_block_params &bp = p->blocks[i];
         if (bp.d[0].c_in != c || bp.d[0].h != h || bp.d[0].w != w) return IFX_E_SHAPE;
@@ -307,6 +329,7 @@ ifx_status plan_net(const ifx_net_params *p, int n, NetPlan *plan)
         t1 = std::max(t1, b.t1);
         t2 = std::max(t2, b.t2);
         sc = std::max(sc, b.sc);
+        part = std::max(part, b.part);
         h = b.dims[2].oh;
         w = b.dims[2].ow;
         c = bp.d[2].c_out;
@@ -322,10 +345,15 @@ ifx_status plan_net(const ifx_net_params *p, int n, NetPlan *plan)
     plan->t2 = t2;
     plan->sc = sc;
     plan->pool = round_up(act_bytes(nb, 1, 1, c), 256);
+    ifx_conv_desc fd = {nb, 1, 1, p->fc_in, p->fc_out, 1, 1, 1, 0, IFX_OUT_I32};
+    Kind fk;
+    Dims fdm;
+    if (check_desc(&fd, &fk, &fdm) == IFX_OK) part = std::max(part, conv_part_bytes(&fd, fdm));
+    plan->part = part;
     return IFX_OK;
 }
 
-size_t net_ws_bytes(const NetPlan &pl) { return 2 * pl.act + pl.t1 + pl.t2 + pl.sc + pl.pool; }
+size_t net_ws_bytes(const NetPlan &pl) { return 2 * pl.act + pl.t1 + pl.t2 + pl.sc + pl.pool + pl.part; }
 
 }  // namespace
 
@@ -430,7 +458,7 @@ size_t ifx_block_workspace_bytes(const ifx_block_params *p)
 {
     BlockPlan plan;
     if (plan_block(p, 0, &plan) != IFX_OK) return 0;
-    return plan.t1 + plan.t2 + plan.sc;
+    return plan.t1 + plan.t2 + plan.sc + plan.part;
 }
 
 ifx_status ifx_conv_proj_fused(const ifx_conv_desc *d3, const int8_t *t_blk, const int8_t *w3_blk,
@@ -468,8 +496,9 @@ ifx_status ifx_block_forward(const ifx_block_params *p, const int8_t *x_blk, int
     if (st != IFX_OK) return st;
     if (!x_blk || !y_blk || !ws) return IFX_E_NULL;
     if (!aligned16(x_blk) || !aligned16(y_blk) || !aligned16(ws)) return IFX_E_ALIGN;
-    if (ws_bytes < plan.t1 + plan.t2 + plan.sc) return IFX_E_WORKSPACE;
-    return run_block(p, plan, p->d[0].n, x_blk, y_blk, (int8_t *)ws, (hipStream_t)stream);
+    if (ws_bytes < plan.t1 + plan.t2 + plan.sc + plan.part) return IFX_E_WORKSPACE;
+    int32_t *part = (int32_t *)((int8_t *)ws + plan.t1 + plan.t2 + plan.sc);
+    return run_block(p, plan, p->d[0].n, x_blk, y_blk, (int8_t *)ws, part, plan.part, (hipStream_t)stream);
 }
 
 size_t ifx_net_workspace_bytes(const ifx_net_params *p, int32_t n)
@@ -503,6 +532,7 @@ ifx_status ifx_net_forward(const ifx_net_params *p, const int8_t *x_blk, int32_t
     int8_t *act[2] = {base, base + plan.act};
     int8_t *bws = base + 2 * plan.act;  // t1 | t2 | sc of the current block
     int8_t *pool = bws + plan.t1 + plan.t2 + plan.sc;
+    int32_t *part = (int32_t *)(pool + plan.pool);  // split-K partial sums
     const size_t in_img = (p->stem.flags & IFX_INPUT_NHWC)
                               ? (size_t)p->stem.h * p->stem.w * p->stem.c_in
                               : act_bytes(1, p->stem.h, p->stem.w, p->stem.c_in);
@@ -527,7 +557,7 @@ ifx_status ifx_net_forward(const ifx_net_params *p, const int8_t *x_blk, int32_t
             BlockPlan lay = bp;
             lay.t1 = plan.t1;
             lay.t2 = plan.t2;
-            st = run_block(&p->blocks[b], lay, nb, act[cur], act[cur ^ 1], bws, s);
+            st = run_block(&p->blocks[b], lay, nb, act[cur], act[cur ^ 1], bws, part, plan.part, s);
             if (st != IFX_OK) return st;
             cur ^= 1;
         }
@@ -538,7 +568,7 @@ ifx_status ifx_net_forward(const ifx_net_params *p, const int8_t *x_blk, int32_t
         st = check_desc(&fd, &k, &dm);
         if (st != IFX_OK) return st;
         st = run_conv(&fd, k, dm, pool, p->fc_w_blk, p->fc_bias, nullptr, nullptr, nullptr,
-                      logits + (size_t)i0 * p->fc_out, s);
+                      logits + (size_t)i0 * p->fc_out, s, part, plan.part);
         if (st != IFX_OK) return st;
     }
     return IFX_OK;

@@ -23,6 +23,10 @@ struct ConvArgs {
     int m;                 // n * ho * wo (GEMM rows)
     int nkb;               // kh * kw * i1 (32-wide reduction blocks)
     int relu, residual, out_i32;
+    // split-K (partial launches only): workgroup row blockIdx.y covers 32-channel blocks
+    // [blockIdx.y * kb_per, +kb_per) of the reduction and writes its int32 sums, without the
+    // bias, to slice blockIdx.y of y ([ksplit][m][oc]); ksplit = 1 is the whole reduction
+    int ksplit, kb_per;
     // magic numbers for exact unsigned division of n < 2^31 by ho*wo, wo, o2
     // (q = n when d == 1, else umulhi(n, mul) >> shr); see fastdiv_magic()
     unsigned howo_mul, wo_mul, o2_mul;
@@ -68,6 +72,12 @@ struct FoldArgs {
 };
 
 hipError_t launch_conv(const ConvArgs &a, int kh, int kw, hipStream_t s);
+// Bytes of int32 partial sums launch_conv_split would use for `a` (0: it would not split).  A
+// convolution on few output tiles with a long reduction is split over workgroups along K.
+size_t splitk_bytes(const ConvArgs &a, int kh, int kw);
+// launch_conv, split along K when that pays and `part` (part_bytes of device memory) holds the
+// partial sums; a second kernel then sums them and applies the epilogue.  Results are identical.
+hipError_t launch_conv_split(const ConvArgs &a, int kh, int kw, int32_t *part, size_t part_bytes, hipStream_t s);
 // The 1x1 shortcut conv `a` (RESIDUAL) of a bottleneck fused with its 1x1 projection shortcut
 // `pj` (same output pixels and channels, no ReLU): the projection's requantised output is the
 // shortcut and never reaches HBM; a.res is not read.

@@ -156,7 +156,7 @@ void igemm_kernel(ConvArgs a, ConvArgs pj, int tiles_n, int per_xcd)
     //      (4j + w) % A_CH of block (4j + w) / A_CH: the lane's pixel, its tap-validity mask and
     //      base offset.  Weight DMA j likewise for B_CH.
     // geometry of the convolution whose K-steps are being issued
-    int HW = 0, wblk = 0, qi1 = 0, qnkb = 0, qw = 0;
+    int HW = 0, wblk = 0, qi1 = 0, qnkb = 0, qw = 0, qkb0 = 0;
     v4i rsA, rsB;
     int a_base[C::AI], b_base[C::BI];
     unsigned a_nmask[C::AI];  // complement of the lane's tap-validity mask (bit 31 always set)
@@ -164,7 +164,9 @@ void igemm_kernel(ConvArgs a, ConvArgs pj, int tiles_n, int per_xcd)
     auto plan = [&](const ConvArgs &q) __attribute__((always_inline)) {
         HW = q.h * q.w;
         qi1 = q.i1;
-        qnkb = q.nkb;
+        // this workgroup's part of the reduction: blocks [qkb0, qnkb)
+        qkb0 = (PROJ || q.ksplit <= 1) ? 0 : (int)blockIdx.y * q.kb_per;
+        qnkb = (PROJ || q.ksplit <= 1) ? q.nkb : min(q.nkb, qkb0 + q.kb_per);
         qw = q.w;
         const long long in_img = (long long)q.i1 * HW * 32;
         rsA = make_rsrc(q.x + (long long)img0 * in_img, (long long)(q.n - img0) * in_img);
@@ -212,13 +214,17 @@ void igemm_kernel(ConvArgs a, ConvArgs pj, int tiles_n, int per_xcd)
     // ---- the K-step stream: the steps of pj (PROJ only), then those of a.  Step s covers
     //      the flat 32-channel blocks kb = 2s, 2s+1 of its convolution, kb -> (tap, channel block).
     const int n1 = PROJ ? (pj.nkb + 1) >> 1 : 0;
-    const int nsteps = n1 + ((a.nkb + 1) >> 1);
     int iss = 0;                  // next step to issue
     int cur_c1 = 0, cur_tap = 0;  // block 2s of that step, within its convolution
     if (PROJ)
         plan(pj);
     else
         plan(a);
+    if (!PROJ && qkb0 > 0) {  // a split-K part starts inside the reduction
+        cur_tap = qkb0 / qi1;
+        cur_c1 = qkb0 - cur_tap * qi1;
+    }
+    const int nsteps = n1 + (PROJ ? (a.nkb + 1) >> 1 : (qnkb - qkb0 + 1) >> 1);
     auto issue = [&](int slot) __attribute__((always_inline)) {
         const int s = iss - (iss >= n1 ? n1 : 0);
         ++iss;
@@ -228,7 +234,7 @@ void igemm_kernel(ConvArgs a, ConvArgs pj, int tiles_n, int per_xcd)
             c1b = 0;
             ++tapb;
         }
-        const int kb0 = 2 * s;
+        const int kb0 = qkb0 + 2 * s;
         const bool v0 = kb0 < qnkb, v1 = kb0 + 1 < qnkb;
         const int ky0 = cur_tap / KW, kx0 = cur_tap - ky0 * KW;
         const int ky1 = tapb / KW, kx1 = tapb - ky1 * KW;
@@ -398,9 +404,11 @@ void igemm_kernel(ConvArgs a, ConvArgs pj, int tiles_n, int per_xcd)
         }
     }
     if (a.out_i32) {
-        int32_t *y = (int32_t *)a.y;
+        // a split-K part writes its own slice of partial sums; the bias is added once, after the sum
+        int32_t *y = (int32_t *)a.y + (a.ksplit > 1 ? (long long)blockIdx.y * a.m * a.oc : 0LL);
         const bool vec = (a.oc & 3) == 0 && ocl + 3 < a.oc;
-        const v4i bias4 = *(const v4i *)(Pw + c * 16);  // zero past Oc (out-of-range DMA lanes)
+        const v4i bias4 = a.ksplit > 1 ? (v4i){0, 0, 0, 0}
+                                       : *(const v4i *)(Pw + c * 16);  // zero past Oc (out-of-range DMA lanes)
 #pragma unroll
         for (int tm = 0; tm < 4; ++tm)
 #pragma unroll
@@ -464,10 +472,10 @@ hipError_t launch_ig(const ConvArgs &a, const ConvArgs &pj, hipStream_t s)
     if (imgs * (long long)a.i1 * a.h * a.w * 32 >= 0x7fffffffLL) return hipErrorInvalidValue;
     if (PROJ && imgs * (long long)pj.i1 * pj.h * pj.w * 32 >= 0x7fffffffLL) return hipErrorInvalidValue;
     if (a.relu)
-        hipLaunchKernelGGL((igemm_kernel<KH, KW, BM, BN, ST, RES, true, PROJ>), dim3((unsigned)grid), dim3(IgCfg<BM, BN, ST>::THREADS), 0, s,
+        hipLaunchKernelGGL((igemm_kernel<KH, KW, BM, BN, ST, RES, true, PROJ>), dim3((unsigned)grid, (unsigned)(a.ksplit > 1 ? a.ksplit : 1)), dim3(IgCfg<BM, BN, ST>::THREADS), 0, s,
                            a, pj, tiles_n, (int)per);
     else
-        hipLaunchKernelGGL((igemm_kernel<KH, KW, BM, BN, ST, RES, false, PROJ>), dim3((unsigned)grid), dim3(IgCfg<BM, BN, ST>::THREADS), 0,
+        hipLaunchKernelGGL((igemm_kernel<KH, KW, BM, BN, ST, RES, false, PROJ>), dim3((unsigned)grid, (unsigned)(a.ksplit > 1 ? a.ksplit : 1)), dim3(IgCfg<BM, BN, ST>::THREADS), 0,
                            s, a, pj, tiles_n, (int)per);
     return hipGetLastError();
 }
@@ -505,6 +513,124 @@ hipError_t launch_conv(const ConvArgs &a, int kh, int kw, hipStream_t s)
     if (kh == 1 && kw == 1) return launch_ig_k<1, 1>(a, s);
     if (kh == 3 && kw == 3) return launch_ig_k<3, 3>(a, s);
     return hipErrorInvalidValue;
+}
+
+// ---- split-K: few output tiles, long reduction (the batch-1 layers) ----------------------------
+
+namespace {
+
+// Output tile of the general kernel for `a` without a shortcut (the partial launch drops it).
+void partial_tile(const ConvArgs &a, int kh, int kw, int *bm, int *bn)
+{
+    const bool wide = a.oc1 * 32 > 64;
+    *bm = wide ? 128 : 256;
+    *bn = wide ? 128 : 64;
+    if (kh == 1 && kw == 1 && wide) {
+        *bm = 256;
+        *bn = 128;
+    } else if (kh == 3 && a.stride == 2 && a.oc1 * 32 >= 256) {
+        *bm = 128;
+        *bn = 256;
+    }
+}
+
+// Number of K parts for `a` (1: no split) and the 32-channel blocks per part (even).  A launch
+// with fewer than 64 output tiles and at least 16 K-steps is split into at most 16 parts of at
+// least two K-steps, aiming at 256 workgroups, while the int32 partial sums fit in 8 MB.
+int split_count(const ConvArgs &a, int kh, int kw, int *kb_per)
+{
+    if (conv1x1_small_k_supported(a, kh, kw) || (a.oc & 3) != 0) return 1;
+    if (!((kh == 1 && kw == 1) || (kh == 3 && kw == 3))) return 1;
+    int bm, bn;
+    partial_tile(a, kh, kw, &bm, &bn);
+    const long long tiles = (long long)((a.m + bm - 1) / bm) * ((a.oc1 * 32 + bn - 1) / bn);
+    const int nsteps = (a.nkb + 1) / 2;
+    if (tiles >= 64 || nsteps < 16) return 1;
+    long long parts = (256 + tiles - 1) / tiles;
+    if (parts > nsteps / 2) parts = nsteps / 2;
+    if (parts > 16) parts = 16;
+    const int per = 2 * (int)((nsteps + parts - 1) / parts);
+    const int n = (a.nkb + per - 1) / per;
+    if (n < 2 || (long long)n * a.m * a.oc * 4 > (8LL << 20)) return 1;
+    *kb_per = per;
+    return n;
+}
+
+// Sum of the K parts, bias, then the epilogue of `a`: fixed-point requantisation, shortcut, ReLU
+// and saturation into the NC/32HW32 output (padding channels of a 32-channel block written as
+// 0), or the int32 sums for an int32 output.  An item is one pixel and 4 channels; a workgroup
+// takes 64 items, its four waves summing every fourth part with 16-byte loads, wave 0 adding
+// the three other waves' sums from LDS.  Requires Oc % 4 == 0 (16-byte aligned part rows).
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(ConvArgs a, const int32_t *part, int parts)
+{
+    __shared__ v4i red[3][64];
+    const int groups = a.out_i32 ? a.oc >> 2 : a.oc1 * 8;
+    const int t = threadIdx.x & 63, pl = threadIdx.x >> 6;
+    const int idx = blockIdx.x * 64 + t;
+    const bool live = idx < a.m * groups;
+    const int p = live ? idx / groups : 0;
+    const int ch = (idx - p * groups) * 4;
+    const bool real = live && ch < a.oc;
+    v4i acc = {0, 0, 0, 0};
+    if (real) {
+        const long long slice = (long long)a.m * a.oc;
+        const int32_t *src = part + (long long)p * a.oc + ch;
+#pragma unroll 4
+        for (int q = pl; q < parts; q += 4) acc += *(const v4i *)(src + q * slice);
+    }
+    if (pl) red[pl - 1][t] = acc;
+    __syncthreads();
+    if (pl || !live) return;
+    acc += red[0][t] + red[1][t] + red[2][t];
+    if (a.out_i32) {
+        const v4i b = {a.bias[ch], a.bias[ch + 1], a.bias[ch + 2], a.bias[ch + 3]};
+        *(v4i *)((int32_t *)a.y + (long long)p * a.oc + ch) = acc + b;
+        return;
+    }
+    const int HoWo = a.ho * a.wo;
+    const int b = p / HoWo, hw = p - b * HoWo;
+    const long long off = (((long long)b * a.oc1 + (ch >> 5)) * HoWo + hw) * 32 + (ch & 31);
+    int v[4] = {0, 0, 0, 0};
+    if (real) {
+        const unsigned rr = a.residual ? *(const unsigned *)(a.res + off) : 0u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            int r = requant_any(acc[j] + a.bias[ch + j], a.mult[ch + j], a.shift[ch + j]);
+            if (a.residual) r += (int)(signed char)(rr >> (8 * j));
+            if (a.relu) r = max(r, 0);
+            v[j] = min(max(r, -128), 127);
+        }
+    }
+    *(unsigned *)((int8_t *)a.y + off) = pack4(v[0], v[1], v[2], v[3]);
+}
+
+}  // namespace
+
+size_t splitk_bytes(const ConvArgs &a, int kh, int kw)
+{
+    int per = 0;
+    const int n = split_count(a, kh, kw, &per);
+    return n > 1 ? (((size_t)n * a.m * a.oc * 4 + 255) & ~(size_t)255) : 0;
+}
+
+hipError_t launch_conv_split(const ConvArgs &a, int kh, int kw, int32_t *part, size_t part_bytes, hipStream_t s)
+{
+    int per = 0;
+    const int n = part ? split_count(a, kh, kw, &per) : 1;
+    if (n <= 1 || (size_t)n * a.m * a.oc * 4 > part_bytes) return launch_conv(a, kh, kw, s);
+    ConvArgs q = a;  // the partial launch: int32 sums of each K part, no shortcut, no bias
+    q.out_i32 = 1;
+    q.residual = 0;
+    q.res = nullptr;
+    q.relu = 0;
+    q.y = part;
+    q.ksplit = n;
+    q.kb_per = per;
+    hipError_t e = kh == 1 ? launch_ig_k<1, 1>(q, s) : launch_ig_k<3, 3>(q, s);
+    if (e != hipSuccess) return e;
+    const long long items = (long long)a.m * (a.out_i32 ? a.oc / 4 : a.oc1 * 8);
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((items + 63) / 64)), dim3(256), 0, s, a, part, n);
+    return hipGetLastError();
 }
 
 }  // namespace ifx

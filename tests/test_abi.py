@@ -129,11 +129,54 @@ def _block(n=2, proj=True, c3_flags=ifx.RESIDUAL | ifx.RELU, c2_cin=64):
     return p
 
 
+def _split_bytes(n, ho, wo, ci, co, k, stride, pad=0, out_i32=False):
+    """Partial-sum bytes of a split-K launch: a launch of fewer than 64 output tiles and at least
+    16 K-steps (two 32-channel blocks each) is split into at most 16 parts of an even number of
+    blocks, at least two steps each, aiming at 256 workgroups, while the int32 partials fit in
+    8 MB (and Oc is a multiple of 4)."""
+    i1, oc1 = -(-ci // 32), -(-co // 32)
+    if (k == 1 and pad == 0 and not out_i32 and i1 <= 4) or co % 4:
+        return 0                                     # the small-K 1x1 kernel: one pass, no split
+    m, nkb = n * ho * wo, k * k * i1
+    wide = oc1 * 32 > 64
+    bm, bn = (128, 128) if wide else (256, 64)
+    if k == 1 and wide:
+        bm, bn = 256, 128
+    elif k == 3 and stride == 2 and oc1 * 32 >= 256:
+        bm, bn = 128, 256
+    tiles = -(-m // bm) * -(-(oc1 * 32) // bn)
+    steps = (nkb + 1) // 2
+    if tiles >= 64 or steps < 16:
+        return 0
+    parts = min(-(-256 // tiles), steps // 2, 16)
+    if parts < 2:
+        return 0
+    per = 2 * -(-steps // parts)
+    nparts = -(-nkb // per)
+    if nparts < 2 or nparts * m * co * 4 > 8 << 20:
+        return 0
+    return -(-(nparts * m * co * 4) // 256) * 256
+
+
+def test_split_rule_examples():
+    # 3x3/s2 of 64 channels on 8x8: 18 blocks are too short a reduction to split
+    assert _split_bytes(2, 4, 4, 64, 64, 3, 2, 1) == 0
+    # 28x28x256 3x3 at batch 8: 72 blocks, 25 tiles -> 9 parts would need 14.5 MB -> no split
+    assert _split_bytes(8, 28, 28, 256, 64, 3, 1, 1) == 0
+    # the classifier at batch 1: 2048 -> 1000, 8 tiles, 64 blocks -> 16 parts of 4 blocks
+    assert _split_bytes(1, 1, 1, 2048, 1000, 1, 1, out_i32=True) == 16 * 1000 * 4
+    # 7x7x512 3x3 at batch 1: 4 tiles, 144 blocks -> 15 parts of 10 blocks (the last 4)
+    assert _split_bytes(1, 7, 7, 512, 512, 3, 1, 1) == 15 * 49 * 512 * 4
+    # Oc not a multiple of 4: never split
+    assert _split_bytes(1, 7, 7, 512, 510, 3, 1, 1) == 0
+
+
 def test_block_validation_and_workspace():
     L = ifx.lib()
     p = _block()
     ws = ifx.block_workspace_bytes(p)
     exp = 2 * 2 * 8 * 8 * 32 + 2 * 2 * 4 * 4 * 32 + 2 * 8 * 4 * 4 * 32
+    exp += _split_bytes(2, 4, 4, 64, 64, 3, 2, 1)    # 0: every K is short; c3 runs fused
     assert ws == exp
     fake = ctypes.c_void_p(0x200000)
     assert L.ifx_block_forward(ctypes.byref(p), fake, fake, fake, ws - 1, None) == 5
@@ -166,7 +209,7 @@ def test_net_validation_and_workspace():
     t = 4 * 2 * 56 * 56 * 32
     assert ws == 2 * act + 2 * t + act + 4 * 8 * 32
     p.sub_batch = 2
-    assert ifx.net_workspace_bytes(p, 4) == ws // 2
+    assert ifx.net_workspace_bytes(p, 4) == ws // 2 + _split_bytes(2, 56, 56, 64, 64, 3, 1, 1)
     fake = ctypes.c_void_p(0x200000)
     assert L.ifx_net_forward(ctypes.byref(p), fake, fake, 4, fake, ws // 2 - 1, None) == 5
     p.fc_in = 255

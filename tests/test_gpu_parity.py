@@ -5,6 +5,7 @@ int32 accumulators and int32 logits must equal the oracle's on the same seeded
 inputs.  Outputs are written into sentinel-filled buffers with guard bands, and
 runs are repeated to catch races.
 """
+import ctypes
 import itertools
 import sys
 
@@ -273,6 +274,9 @@ PROJ_BLOCKS = [
     (1, 7, 7, 256, 64, 64, 1, 1),    # 64 output channels: the tall tile shape
     (5, 11, 6, 40, 24, 200, 2, 1),   # odd channel-block counts (32-channel blocks 2 and 1)
     (2, 8, 8, 64, 32, 128, 1, 3),    # 3x3 conv3: projection and conv3 launched separately
+    (1, 14, 14, 1024, 256, 1024, 2, 1),  # batch 1, long K: c1 (8 parts) and c2 (18 parts) split K
+    (1, 9, 9, 96, 200, 96, 1, 3),    # 63 blocks in 16 parts (odd tail), 200 channels (padding
+                                     # groups); the split 3x3 conv3 adds the shortcut
 ]
 
 
@@ -349,6 +353,68 @@ def test_stem_nhwc_input(ifx, orc, n, h, w, c):
     for flags in (ifx.RELU | ifx.MAXPOOL, ifx.MAXPOOL):
         got = gpu_conv(ifx, x, wt, bias, mult, shift, 7, 2, 3, flags | ifx.INPUT_NHWC)
         np.testing.assert_array_equal(got, orc.conv_fused(x, wt, bias, mult, shift, 2, 3, flags))
+
+
+# ------------------------------------------------------------------ small networks: pool and head
+@pytest.mark.parametrize("n,h,w,nblk", [(2, 40, 44, 0), (1, 224, 224, 0), (3, 16, 16, 1), (1, 9, 12, 1)])
+def test_small_net_pool_and_head(ifx, orc, n, h, w, nblk):
+    """Stem -> 0 or 1 bottleneck -> average pool -> FC through ifx_net_forward: the pool over
+    9 to 3136 pixels per plane (pixel groups of the wave left partly empty) and the int32
+    logits equal the oracle's; a batch run in single-image passes gives the same logits."""
+    from oracle.ref import BlockParams as OracleBlock, ConvParams
+    note(f"small net n={n} h={h} w={w} blocks={nblk}")
+    rng = np.random.default_rng(n * 1000 + h + w + nblk)
+    x = rand(rng, (n, h, w, 3), -128, 127)
+    keep = []
+
+    def conv(ci, co, k, st, pd, fl, hh, ww):
+        wt = rand(rng, (co, k, k, ci), -127, 127)
+        bias, mult, shift = params(rng, co, 0, 20)
+        d = ifx.conv_desc(n, hh, ww, ci, co, k, k, st, pd, fl)
+        t = [ifx.pack_weights(d, cu(wt)), cu(bias), cu(mult), cu(shift)]
+        keep.extend(t)
+        return d, t, ConvParams(wt, bias, mult, shift, st, pd)
+
+    sd, st_, sp = conv(3, 64, 7, 2, 3, ifx.RELU | ifx.MAXPOOL | ifx.INPUT_NHWC, h, w)
+    ph, pw = ifx.conv_out_dims(sd)
+    p = ifx.NetParams()
+    p.stem = sd
+    p.stem_w, p.stem_bias, p.stem_mult, p.stem_shift = (t.data_ptr() for t in st_)
+    blocks, c = [], 64
+    if nblk:
+        bp = ifx.BlockParams()
+        layers = [(64, 32, 1, ifx.RELU), (32, 32, 3, ifx.RELU), (32, 128, 1, ifx.RESIDUAL | ifx.RELU), (64, 128, 1, 0)]
+        cps = []
+        for i, (ci, co, k, fl) in enumerate(layers):
+            d, t, cp = conv(ci, co, k, 1, k // 2, fl, ph, pw)
+            bp.d[i] = d
+            bp.w_blk[i], bp.bias[i], bp.mult[i], bp.shift[i] = (q.data_ptr() for q in t)
+            cps.append(cp)
+        bp.has_proj = 1
+        arr = (ifx.BlockParams * 1)(bp)
+        keep.append(arr)
+        p.blocks = ctypes.cast(arr, ctypes.POINTER(ifx.BlockParams))
+        blocks.append(OracleBlock(*cps))
+        c = 128
+    p.n_blocks = nblk
+    fc_out = 1000
+    fw = rand(rng, (fc_out, c), -127, 127)
+    fb = rand(rng, fc_out, -(1 << 20), 1 << 20, np.int32)
+    fd = ifx.conv_desc(n, 1, 1, c, fc_out, 1, 1, 1, 0, ifx.OUT_I32)
+    fwb, fbb = ifx.pack_weights(fd, cu(fw.reshape(fc_out, 1, 1, c))), cu(fb)
+    keep += [fwb, fbb]
+    p.fc_w_blk, p.fc_bias = fwb.data_ptr(), fbb.data_ptr()
+    p.fc_in, p.fc_out = c, fc_out
+    exp = orc.net(x, sp, blocks, fw, fb)
+    xd = cu(x)
+    for sub in (0, 1):
+        p.sub_batch = sub
+        ws = torch.empty(ifx.net_workspace_bytes(p, n), dtype=torch.int8, device="cuda")
+        logits, whole = guarded(n * fc_out * 4, torch.int32)
+        ifx.net_forward(p, xd, logits, n, ws)
+        torch.cuda.synchronize()
+        check_guards(whole)
+        np.testing.assert_array_equal(logits.view(n, fc_out).cpu().numpy(), exp)
 
 
 # ------------------------------------------------------------------ determinism
