@@ -31,10 +31,10 @@ RIDGE = PEAK_I8 / PEAK_HBM
 METRIC = "int8 TOPS + images/s (fused conv stack), % of int8 MFMA peak / HBM BW"
 
 
-def kernel_name(spec, nhwc_input=True, proj=False) -> str:
+def kernel_name(spec, nhwc_input=True, proj=None) -> str:
     """The kernel template instance a conv layer dispatches to, spelled as rocprofv3
-    prints it (mirrors the library's host dispatch).  proj: conv3 fused with its
-    projection shortcut (ifx_conv_proj_fused)."""
+    prints it (mirrors the library's host dispatch).  proj: the projection shortcut's
+    spec when `spec` is a conv3 fused with it (ifx_conv_proj_fused)."""
     if spec.k == 7:
         return f"stem_kernel<{1 if nhwc_input else 0}>"
     oc_pad = (spec.c_out + 31) // 32 * 32
@@ -42,14 +42,17 @@ def kernel_name(spec, nhwc_input=True, proj=False) -> str:
     res = "true" if spec.flags & 2 else "false"
     relu = "true" if spec.flags & 1 else "false"
     i1 = (spec.c_in + 31) // 32
-    if spec.k == 1 and spec.pad == 0 and i1 <= 4 and not proj:
+    if proj is not None and spec.k == 1 and spec.stride == 1 and i1 <= 4 and (proj.c_in + 31) // 32 <= 4:
+        # both contractions short: the small-K fused kernel, shortcut kept in registers
+        return f"conv1x1_proj_kernel<{bm}, {bn}, {((proj.c_in + 31) // 32 + 1) // 2}, {(i1 + 1) // 2}, {relu}>"
+    if spec.k == 1 and spec.pad == 0 and i1 <= 4 and proj is None:
         return f"conv1x1_kernel<{bm}, {bn}, {(i1 + 1) // 2}, {res}, {relu}>"
     st = 2
     if spec.k == 1 and oc_pad > 64 and res == "false":
         bm, bn, st = 256, 128, 3  # wide 1x1 convolutions without a shortcut
     if spec.k == 3 and spec.stride == 2 and oc_pad >= 256 and res == "false":
         bm, bn = 128, 256  # strided 3x3 with >= 256 output channels
-    return f"igemm_kernel<{spec.k}, {spec.k}, {bm}, {bn}, {st}, {res}, {relu}, {'true' if proj else 'false'}>"
+    return f"igemm_kernel<{spec.k}, {spec.k}, {bm}, {bn}, {st}, {res}, {relu}, {'false' if proj is None else 'true'}>"
 
 
 # Sources each kernel family is built from: HBM traffic taken from counters is only
@@ -57,6 +60,7 @@ def kernel_name(spec, nhwc_input=True, proj=False) -> str:
 KERNEL_SOURCES = {
     "igemm_kernel": ["igemm.hip", "device_common.h", "ifx_internal.h"],
     "conv1x1_kernel": ["conv1x1.hip", "device_common.h", "ifx_internal.h"],
+    "conv1x1_proj_kernel": ["conv1x1.hip", "device_common.h", "ifx_internal.h"],
     "stem_kernel": ["stem.hip", "device_common.h", "ifx_internal.h"],
 }
 
@@ -377,7 +381,7 @@ def main():
         o3, b3, oh, ow = layer_work(c3spec, nb_, h3, w3)
         op, bp, _, _ = layer_work(pspec, nb_, hp, wp)
         shortcut = nb_ * oh * ow * c3spec.c_out
-        return (kernel_name(c3spec, nhwc, proj=True), o3 + op, b3 + bp - 2 * shortcut, fn)
+        return (kernel_name(c3spec, nhwc, proj=pspec), o3 + op, b3 + bp - 2 * shortcut, fn)
 
     if args.workload in ("net", "net26_b1"):
         nb = sub_batch if 0 < sub_batch < n else n

@@ -191,6 +191,29 @@ __device__ __forceinline__ int rq_setup(RqLane &r, v4i bias4, v4i mult4, v4i shi
     return 2;
 }
 
+// One tile row of a lane: its 4 channels of row 16tm + 4i + g requantised (mode MODE), plus the
+// shortcut bytes rr when RES, clamped (ReLU or not) and packed into one word.
+template <int MODE, bool RES, bool RELU>
+__device__ __forceinline__ unsigned requant_row(const v4i (&acc)[4][4], int tm, int i, const RqLane &r, unsigned rr)
+{
+    int q[4];
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn) {
+        int v;
+        if (MODE == 0) {
+            v = requant_any(acc[tm][tn][i] + r.bias[tn], r.mul[tn], r.shf[tn]);
+        } else if (MODE == 1) {
+            const long long p = (long long)acc[tm][tn][i] * (long long)r.mul[tn] + r.add[tn];
+            v = ((int)(p >> 32)) >> r.shm[tn];
+        } else {
+            v = requant_fast(acc[tm][tn][i] + r.bias[tn], r.mul[tn], r.rnd[tn], r.shm[tn]);
+        }
+        if (RES) v += (int)(signed char)(rr >> (8 * tn));
+        q[tn] = RELU ? min(max(v, 0), 127) : min(max(v, -128), 127);
+    }
+    return pack4(q[0], q[1], q[2], q[3]);
+}
+
 // Requantise a wave's 64x64 accumulator tile into the LDS staging tile (row stride BN),
 // adding the shortcut bytes already there when RES.  Lane (g, c) owns tile rows
 // 16tm + 4i + g and the 4 bytes at column 4c.
@@ -202,23 +225,7 @@ __device__ __forceinline__ void requant_tile(const v4i (&acc)[4][4], int8_t *rba
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             unsigned *rp = (unsigned *)(rbase + (16 * tm + 4 * i) * BN);
-            const unsigned rr = RES ? *rp : 0u;
-            int q[4];
-#pragma unroll
-            for (int tn = 0; tn < 4; ++tn) {
-                int v;
-                if (MODE == 0) {
-                    v = requant_any(acc[tm][tn][i] + r.bias[tn], r.mul[tn], r.shf[tn]);
-                } else if (MODE == 1) {
-                    const long long p = (long long)acc[tm][tn][i] * (long long)r.mul[tn] + r.add[tn];
-                    v = ((int)(p >> 32)) >> r.shm[tn];
-                } else {
-                    v = requant_fast(acc[tm][tn][i] + r.bias[tn], r.mul[tn], r.rnd[tn], r.shm[tn]);
-                }
-                if (RES) v += (int)(signed char)(rr >> (8 * tn));
-                q[tn] = RELU ? min(max(v, 0), 127) : min(max(v, -128), 127);
-            }
-            *rp = pack4(q[0], q[1], q[2], q[3]);
+            *rp = requant_row<MODE, RES, RELU>(acc, tm, i, r, RES ? *rp : 0u);
         }
 }
 
@@ -232,6 +239,53 @@ __device__ __forceinline__ void requant_tile_any(int mode, const v4i (&acc)[4][4
         requant_tile<1, RES, RELU, BN>(acc, rbase, r);
     else
         requant_tile<2, RES, RELU, BN>(acc, rbase, r);
+}
+
+// A lane's 16 requantised rows kept in registers (a shortcut that never leaves the lane):
+// sc[tm][i] holds the 4 bytes of row 16tm + 4i + g, no ReLU, no shortcut of its own.
+template <int MODE>
+__device__ __forceinline__ void requant_regs(const v4i (&acc)[4][4], const RqLane &r, unsigned (&sc)[4][4])
+{
+#pragma unroll
+    for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[tm][i] = requant_row<MODE, false, false>(acc, tm, i, r, 0u);
+}
+
+__device__ __forceinline__ void requant_regs_any(int mode, const v4i (&acc)[4][4], const RqLane &r,
+                                                 unsigned (&sc)[4][4])
+{
+    if (mode == 0)
+        requant_regs<0>(acc, r, sc);
+    else if (mode == 1)
+        requant_regs<1>(acc, r, sc);
+    else
+        requant_regs<2>(acc, r, sc);
+}
+
+// The final requantisation with the shortcut taken from registers (sc as requant_regs leaves
+// it), written to the LDS staging tile (row stride BN).
+template <int MODE, bool RELU, int BN>
+__device__ __forceinline__ void requant_tile_sc(const v4i (&acc)[4][4], int8_t *rbase, const RqLane &r,
+                                                const unsigned (&sc)[4][4])
+{
+#pragma unroll
+    for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            *(unsigned *)(rbase + (16 * tm + 4 * i) * BN) = requant_row<MODE, true, RELU>(acc, tm, i, r, sc[tm][i]);
+}
+
+template <bool RELU, int BN>
+__device__ __forceinline__ void requant_tile_sc_any(int mode, const v4i (&acc)[4][4], int8_t *rbase,
+                                                    const RqLane &r, const unsigned (&sc)[4][4])
+{
+    if (mode == 0)
+        requant_tile_sc<0, RELU, BN>(acc, rbase, r, sc);
+    else if (mode == 1)
+        requant_tile_sc<1, RELU, BN>(acc, rbase, r, sc);
+    else
+        requant_tile_sc<2, RELU, BN>(acc, rbase, r, sc);
 }
 
 }  // namespace ifx

@@ -88,6 +88,8 @@ hipError_t launch_fold_bn(const FoldArgs &f, int32_t *bias, int32_t *mult, int32
                           hipStream_t s);
 // 1x1 convolutions with at most 128 input channels (conv1x1.hip)
 bool conv1x1_small_k_supported(const ConvArgs &a, int kh, int kw);
+bool conv1x1_proj_supported(const ConvArgs &a, const ConvArgs &pj);
+hipError_t launch_conv1x1_proj(const ConvArgs &a, const ConvArgs &pj, hipStream_t s);
 hipError_t launch_conv1x1_small_k(const ConvArgs &a, hipStream_t s);
 hipError_t launch_stem(const StemArgs &a, hipStream_t s);
 hipError_t launch_avgpool(const int8_t *x, int8_t *y, int n, int c1, int hw, hipStream_t s);

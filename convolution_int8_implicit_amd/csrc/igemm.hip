@@ -502,6 +502,7 @@ hipError_t launch_ig_k(const ConvArgs &a, hipStream_t s)
 
 hipError_t launch_conv_proj(const ConvArgs &a, const ConvArgs &pj, hipStream_t s)
 {
+    if (conv1x1_proj_supported(a, pj)) return launch_conv1x1_proj(a, pj, s);
     constexpr int ST = 2;
     if (a.oc1 * 32 > 64) return launch_ig<1, 1, 128, 128, ST, true, true>(a, pj, s);
     return launch_ig<1, 1, 256, 64, ST, true, true>(a, pj, s);
