@@ -10,6 +10,8 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
+#include <vector>
 
 #include "ifx_internal.h"
 
@@ -304,15 +306,23 @@ struct NetPlan {
     size_t part;                   // split-K partial sums (max over the network's convolutions)
     int out_h, out_w, out_c;       // backbone output
     int nb;                        // images per pass
+    int lanes;                     // passes in flight at once, each with its own workspace
 };
+
+// A whole batch of at least this many images (sub_batch 0) runs as two concurrent halves, one on
+// the caller's stream and one on a library stream: the last, partly filled round of tiles of
+// each launch then overlaps the other half's work.
+constexpr int kTwoLaneMin = 512;
 
 ifx_status plan_net(const ifx_net_params *p, int n, NetPlan *plan)
 {
     if (!p) return IFX_E_NULL;
     if (n <= 0 || p->n_blocks < 0 || p->sub_batch < 0 || p->fc_in <= 0 || p->fc_out <= 0) return IFX_E_SHAPE;
     if (p->n_blocks > 0 && !p->blocks) return IFX_E_NULL;
-    const int nb = (p->sub_batch > 0 && p->sub_batch < n) ? p->sub_batch : n;
+    const bool halves = p->sub_batch == 0 && n >= kTwoLaneMin;
+    const int nb = halves ? (n + 1) / 2 : (p->sub_batch > 0 && p->sub_batch < n) ? p->sub_batch : n;
     plan->nb = nb;
+    plan->lanes = halves ? 2 : 1;
     ifx_conv_desc stem = p->stem;
     stem.n = nb;
     ifx_status st = check_desc(&stem, &plan->stem_kind, &plan->stem_dims);
@@ -353,7 +363,30 @@ ifx_status plan_net(const ifx_net_params *p, int n, NetPlan *plan)
     return IFX_OK;
 }
 
-size_t net_ws_bytes(const NetPlan &pl) { return 2 * pl.act + pl.t1 + pl.t2 + pl.sc + pl.pool + pl.part; }
+size_t lane_ws_bytes(const NetPlan &pl) { return 2 * pl.act + pl.t1 + pl.t2 + pl.sc + pl.pool + pl.part; }
+size_t net_ws_bytes(const NetPlan &pl) { return pl.lanes * lane_ws_bytes(pl); }
+
+// The library's second stream on the current device (non-blocking, default priority), created
+// on first use and kept for the process.
+hipError_t lane_stream(hipStream_t *out)
+{
+    static std::mutex mu;
+    static std::vector<hipStream_t> streams;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(mu);
+    if ((size_t)dev >= streams.size()) streams.resize(dev + 1, nullptr);
+    if (!streams[dev]) {
+        e = hipStreamCreateWithFlags(&streams[dev], hipStreamNonBlocking);
+        if (e != hipSuccess) {
+            streams[dev] = nullptr;
+            return e;
+        }
+    }
+    *out = streams[dev];
+    return hipSuccess;
+}
 
 }  // namespace
 
@@ -527,51 +560,78 @@ ifx_status ifx_net_forward(const ifx_net_params *p, const int8_t *x_blk, int32_t
     }
     if (ws_bytes < net_ws_bytes(plan)) return IFX_E_WORKSPACE;
 
-    hipStream_t s = (hipStream_t)stream;
-    int8_t *base = (int8_t *)ws;
-    int8_t *act[2] = {base, base + plan.act};
-    int8_t *bws = base + 2 * plan.act;  // t1 | t2 | sc of the current block
-    int8_t *pool = bws + plan.t1 + plan.t2 + plan.sc;
-    int32_t *part = (int32_t *)(pool + plan.pool);  // split-K partial sums
     const size_t in_img = (p->stem.flags & IFX_INPUT_NHWC)
                               ? (size_t)p->stem.h * p->stem.w * p->stem.c_in
                               : act_bytes(1, p->stem.h, p->stem.w, p->stem.c_in);
-
-    for (int i0 = 0; i0 < n; i0 += plan.nb) {
+    // pass i runs on lane i % lanes: lane 0 is the caller's stream, lane 1 the library stream,
+    // forked from and joined back into the caller's stream by events
+    hipStream_t ls[2] = {(hipStream_t)stream, nullptr};
+    hipEvent_t fork = nullptr, join = nullptr;
+    if (plan.lanes > 1) {
+        st = hip_status(lane_stream(&ls[1]));
+        if (st == IFX_OK) st = hip_status(hipEventCreateWithFlags(&fork, hipEventDisableTiming));
+        if (st == IFX_OK) st = hip_status(hipEventCreateWithFlags(&join, hipEventDisableTiming));
+        if (st == IFX_OK) st = hip_status(hipEventRecord(fork, ls[0]));
+        if (st == IFX_OK) st = hip_status(hipStreamWaitEvent(ls[1], fork, 0));
+        if (st != IFX_OK) {
+            if (fork) (void)hipEventDestroy(fork);
+            if (join) (void)hipEventDestroy(join);
+            return st;
+        }
+    }
+    int pass = 0;
+    for (int i0 = 0; i0 < n && st == IFX_OK; i0 += plan.nb, ++pass) {
+        const int lane = pass % plan.lanes;
+        hipStream_t s = ls[lane];
+        int8_t *base = (int8_t *)ws + lane * lane_ws_bytes(plan);
+        int8_t *act[2] = {base, base + plan.act};
+        int8_t *bws = base + 2 * plan.act;  // t1 | t2 | sc of the current block
+        int8_t *pool = bws + plan.t1 + plan.t2 + plan.sc;
+        int32_t *part = (int32_t *)(pool + plan.pool);  // split-K partial sums
         const int nb = std::min(plan.nb, n - i0);
         ifx_conv_desc sd = p->stem;
         sd.n = nb;
         Kind k;
         Dims dm;
         st = check_desc(&sd, &k, &dm);
-        if (st != IFX_OK) return st;
+        if (st != IFX_OK) break;
         st = run_conv(&sd, k, dm, x_blk + (size_t)i0 * in_img, p->stem_w, p->stem_bias, p->stem_mult, p->stem_shift,
                       nullptr, act[0], s);
-        if (st != IFX_OK) return st;
+        if (st != IFX_OK) break;
         int cur = 0;
         for (int b = 0; b < p->n_blocks; ++b) {
             BlockPlan bp;
             st = plan_block(&p->blocks[b], nb, &bp);
-            if (st != IFX_OK) return st;
+            if (st != IFX_OK) break;
             // the block's own workspace pieces are laid out inside the net's t1|t2|sc area
             BlockPlan lay = bp;
             lay.t1 = plan.t1;
             lay.t2 = plan.t2;
             st = run_block(&p->blocks[b], lay, nb, act[cur], act[cur ^ 1], bws, part, plan.part, s);
-            if (st != IFX_OK) return st;
+            if (st != IFX_OK) break;
             cur ^= 1;
         }
+        if (st != IFX_OK) break;
         const int c1 = (plan.out_c + 31) / 32;
         st = hip_status(ifx::launch_avgpool(act[cur], pool, nb, c1, plan.out_h * plan.out_w, s));
-        if (st != IFX_OK) return st;
+        if (st != IFX_OK) break;
         ifx_conv_desc fd = {nb, 1, 1, p->fc_in, p->fc_out, 1, 1, 1, 0, IFX_OUT_I32};
         st = check_desc(&fd, &k, &dm);
-        if (st != IFX_OK) return st;
+        if (st != IFX_OK) break;
         st = run_conv(&fd, k, dm, pool, p->fc_w_blk, p->fc_bias, nullptr, nullptr, nullptr,
                       logits + (size_t)i0 * p->fc_out, s, part, plan.part);
-        if (st != IFX_OK) return st;
+        if (st != IFX_OK) break;
     }
-    return IFX_OK;
+    if (plan.lanes > 1) {
+        // the join is enqueued whatever happened above, so the caller's stream always follows
+        // every pass; the events can go once the wait is enqueued
+        ifx_status st2 = hip_status(hipEventRecord(join, ls[1]));
+        if (st2 == IFX_OK) st2 = hip_status(hipStreamWaitEvent(ls[0], join, 0));
+        (void)hipEventDestroy(fork);
+        (void)hipEventDestroy(join);
+        if (st == IFX_OK) st = st2;
+    }
+    return st;
 }
 
 // ---------------------------------------------------------------------------
@@ -593,6 +653,12 @@ ifx_status ifx_net_graph_create(const ifx_net_params *p, const int8_t *x_blk, in
     if (st != IFX_OK) return st;
     if (!x_blk || !logits || !ws) return IFX_E_NULL;
     if (ws_bytes < net_ws_bytes(plan)) return IFX_E_WORKSPACE;
+    // the library stream of a two-lane batch is created now, outside the capture
+    if (plan.lanes > 1) {
+        hipStream_t lane1 = nullptr;
+        st = hip_status(lane_stream(&lane1));
+        if (st != IFX_OK) return st;
+    }
     // the stem launcher's one-time device query happens now, outside the capture
     st = hip_status(ifx::warm_stem_queries());
     if (st != IFX_OK) return st;

@@ -205,8 +205,15 @@ ifx_status ifx_block_forward(const ifx_block_params *p, const int8_t *x_blk, int
  * argument.  fc_w_blk is the FC weight [fc_out, fc_in] packed as a 1x1
  * convolution (ifx_pack_weights with kh = kw = 1, c_in = fc_in,
  * c_out = fc_out).  sub_batch > 0 runs the network over consecutive groups
- * of sub_batch images (results are identical for every sub_batch); 0 runs
- * the whole batch at once.
+ * of sub_batch images, one after another on `stream`; 0 runs the whole batch
+ * at once, and a batch of 512 or more images then runs as two halves at the
+ * same time: the first on `stream`, the second on a stream the library
+ * creates (default priority, once per device, kept for the process), forked
+ * from `stream` and joined back into it by events, so every result is still
+ * ordered on `stream`.  Each half has its own part of the workspace.  Results
+ * are identical for every sub_batch.  Calls from several host threads on one
+ * device share that library stream (their work is serialised there, still
+ * correct).
  *   x_blk   packed input [n, ceil(stem.c_in/32), stem.h, stem.w, 32], or the
  *           compact [n, stem.h, stem.w, stem.c_in] image when stem.flags has
  *           IFX_INPUT_NHWC

@@ -212,6 +212,14 @@ def test_net_validation_and_workspace():
     assert ifx.net_workspace_bytes(p, 4) == ws // 2 + _split_bytes(2, 56, 56, 64, 64, 3, 1, 1)
     fake = ctypes.c_void_p(0x200000)
     assert L.ifx_net_forward(ctypes.byref(p), fake, fake, 4, fake, ws // 2 - 1, None) == 5
+    # a whole batch of >= 512 images runs as two concurrent halves, each with its own workspace
+    p.sub_batch = 0
+    half = ifx.net_workspace_bytes(p, 256)
+    p.sub_batch = 256
+    assert ifx.net_workspace_bytes(p, 512) == half          # consecutive passes share one workspace
+    p.sub_batch = 0
+    assert ifx.net_workspace_bytes(p, 512) == 2 * half
+    assert ifx.net_workspace_bytes(p, 511) > half           # one pass of 511 images
     p.fc_in = 255
     assert ifx.net_workspace_bytes(p, 4) == 0
 

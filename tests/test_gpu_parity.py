@@ -356,11 +356,14 @@ def test_stem_nhwc_input(ifx, orc, n, h, w, c):
 
 
 # ------------------------------------------------------------------ small networks: pool and head
-@pytest.mark.parametrize("n,h,w,nblk", [(2, 40, 44, 0), (1, 224, 224, 0), (3, 16, 16, 1), (1, 9, 12, 1)])
+@pytest.mark.parametrize("n,h,w,nblk", [(2, 40, 44, 0), (1, 224, 224, 0), (3, 16, 16, 1), (1, 9, 12, 1),
+                                        (515, 16, 16, 1)])
 def test_small_net_pool_and_head(ifx, orc, n, h, w, nblk):
     """Stem -> 0 or 1 bottleneck -> average pool -> FC through ifx_net_forward: the pool over
     9 to 3136 pixels per plane (pixel groups of the wave left partly empty) and the int32
-    logits equal the oracle's; a batch run in single-image passes gives the same logits."""
+    logits equal the oracle's; a batch run in single-image passes gives the same logits.
+    515 images run as two concurrent halves (258 + 257) on two streams, eagerly and recorded
+    as one graph (fork and join inside the capture), replayed with other work between."""
     from oracle.ref import BlockParams as OracleBlock, ConvParams
     note(f"small net n={n} h={h} w={w} blocks={nblk}")
     rng = np.random.default_rng(n * 1000 + h + w + nblk)
@@ -407,7 +410,7 @@ def test_small_net_pool_and_head(ifx, orc, n, h, w, nblk):
     p.fc_in, p.fc_out = c, fc_out
     exp = orc.net(x, sp, blocks, fw, fb)
     xd = cu(x)
-    for sub in (0, 1):
+    for sub in (0, 1) if n < 64 else (0, 100):
         p.sub_batch = sub
         ws = torch.empty(ifx.net_workspace_bytes(p, n), dtype=torch.int8, device="cuda")
         logits, whole = guarded(n * fc_out * 4, torch.int32)
@@ -415,6 +418,21 @@ def test_small_net_pool_and_head(ifx, orc, n, h, w, nblk):
         torch.cuda.synchronize()
         check_guards(whole)
         np.testing.assert_array_equal(logits.view(n, fc_out).cpu().numpy(), exp)
+    if n >= 512:
+        p.sub_batch = 0
+        ws = torch.empty(ifx.net_workspace_bytes(p, n), dtype=torch.int8, device="cuda")
+        logits, whole = guarded(n * fc_out * 4, torch.int32)
+        g = ifx.NetGraph(p, xd, logits, n, ws)
+        for rep in range(3):
+            note(f"two-lane graph replay {rep}")
+            logits.fill_(-7)
+            ws.fill_(rep)
+            torch.cuda.synchronize()
+            g.launch()
+            torch.cuda.synchronize()
+            check_guards(whole)
+            np.testing.assert_array_equal(logits.view(n, fc_out).cpu().numpy(), exp)
+        g.close()
 
 
 # ------------------------------------------------------------------ determinism
