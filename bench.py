@@ -101,7 +101,7 @@ def summarize_pmc(fetch_csv: str, write_csv: str, calib_bytes: int, out: str, wo
     from collections import defaultdict
 
     def short(name):
-        m = re.search(r"((?:conv1x1|igemm|stem)_kernel<[^>]*>)", name)
+        m = re.search(r"((?:conv1x1_proj|conv1x1|igemm|stem)_kernel<[^>]*>)", name)
         if m:
             return m.group(1)
         return "copy" if "bitwise_not" in name else None
@@ -109,12 +109,14 @@ def summarize_pmc(fetch_csv: str, write_csv: str, calib_bytes: int, out: str, wo
     def read(path, counter):
         per = defaultdict(list)
         with open(path) as fh:
-            for r in csv.DictReader(fh):
-                if r["Counter_Name"] != counter:
-                    continue
-                k = short(r["Kernel_Name"])
-                if k:
-                    per[k].append((int(r["Dispatch_Id"]), float(r["Counter_Value"]) * 1024.0))
+            rows = [r for r in csv.DictReader(fh) if r["Counter_Name"] == counter]
+        # only the per-launch replays, which follow the network's last average-pool dispatch:
+        # they are the launches the roofline times (the forward's concurrent passes are not)
+        last_pool = max((int(r["Dispatch_Id"]) for r in rows if "avgpool_kernel" in r["Kernel_Name"]), default=-1)
+        for r in rows:
+            k = short(r["Kernel_Name"])
+            if k and (k == "copy" or int(r["Dispatch_Id"]) > last_pool):
+                per[k].append((int(r["Dispatch_Id"]), float(r["Counter_Value"]) * 1024.0))
         # the calibration copies are the process's last three bitwise_not dispatches
         per["copy"] = sorted(per["copy"])[-3:]
         return {k: [v for _, v in sorted(lst)] for k, lst in per.items()}
@@ -126,7 +128,9 @@ def summarize_pmc(fetch_csv: str, write_csv: str, calib_bytes: int, out: str, wo
     lines = [f"# HBM traffic per dispatch, workload {workload}, from rocprofv3 counters",
              "# FETCH_SIZE and WRITE_SIZE (KiB per dispatch) from two separate --pmc runs, each",
              "# scaled by what the counter reads for a plain copy kernel of known size run in the",
-             "# same process (torch bitwise_not over int32: reads and writes calib_bytes).", f"# {note}",
+             "# same process (torch bitwise_not over int32: reads and writes calib_bytes).",
+             "# Dispatches: the per-launch replays bench.py times for the roofline (those after the",
+             "# network's last average-pool dispatch).", f"# {note}",
              f"copy_calibration: calib_bytes={calib_bytes} | fetch_read={cf:.0f} | write_read={cw:.0f} | "
              f"fetch_scale={fs:.4f} | write_scale={ws:.4f}"]
     for k in sorted(set(fe) & set(wr)):
@@ -137,6 +141,45 @@ def summarize_pmc(fetch_csv: str, write_csv: str, calib_bytes: int, out: str, wo
         lines.append(f"kernel: {k} | digest={source_digest(k)} | dispatches={len(fe[k])} | "
                      f"fetch_bytes_per_launch={f_avg:.0f} | write_bytes_per_launch={w_avg:.0f} | "
                      f"hbm_bytes_per_launch={f_avg + w_avg:.0f}")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_trace(trace_csv: str, stats_csv: str, out: str, workload: str, note: str):
+    """The rocprofv3 --kernel-trace --stats summary of a bench.py run: the --stats table (all
+    dispatches), then per kernel instance the average of the per-launch replays alone (the
+    dispatches after the network's last average-pool dispatch), which is what the roofline's
+    avg_launch_us measures with HIP events."""
+    import csv
+    import re
+    from collections import defaultdict
+
+    def clean(nm):
+        nm = nm.replace("void ifx::(anonymous namespace)::", "").replace("ifx::(anonymous namespace)::", "")
+        return nm if len(nm) <= 100 or nm.startswith(("igemm", "conv1x1", "stem", "avgpool", "splitk")) else nm[:100] + "..."
+
+    lines = [f"# rocprofv3 kernel statistics, workload {workload}", f"# {note}", "#",
+             "# all dispatches (rocprofv3 --stats):",
+             "# name | calls | average ns | total ns | percent | min ns | max ns"]
+    with open(stats_csv) as fh:
+        for r in csv.DictReader(fh):
+            lines.append(f'{clean(r["Name"])} | {r["Calls"]} | {float(r["AverageNs"]):.0f} | '
+                         f'{float(r["TotalDurationNs"]):.0f} | {float(r["Percentage"]):.2f} | '
+                         f'{float(r["MinNs"]):.0f} | {float(r["MaxNs"]):.0f}')
+    with open(trace_csv) as fh:
+        rows = list(csv.DictReader(fh))
+    last_pool = max((int(r["Dispatch_Id"]) for r in rows if "avgpool_kernel" in r["Kernel_Name"]), default=-1)
+    rep = defaultdict(list)
+    for r in rows:
+        m = re.search(r"((?:conv1x1_proj|conv1x1|igemm|stem)_kernel<[^>]*>)", r["Kernel_Name"])
+        if m and int(r["Dispatch_Id"]) > last_pool:
+            rep[m.group(1)].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    lines += ["#", "# per-launch replays only (one conv launch at a time on one stream; bench.py's",
+              "# roofline avg_launch_us is the HIP-event average of these launches):",
+              "# name | replays | average ns | min ns | max ns"]
+    for k, v in sorted(rep.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"replay: {k} | {len(v)} | {sum(v) / len(v):.0f} | {min(v)} | {max(v)}")
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -244,10 +287,16 @@ def main():
                     help="after the run, copy this many MiB with a plain elementwise kernel (counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/hbm_traffic_<workload>.txt from two counter runs and exit")
-    ap.add_argument("--note", default="", help="command lines recorded in the --summarize-pmc output")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_CSV", "STATS_CSV"),
+                    help="write profiles/kernel_stats_<workload>.txt from a --kernel-trace --stats run and exit")
+    ap.add_argument("--note", default="", help="command lines recorded in the --summarize-* output")
     ap.add_argument("--packed-input", action="store_true",
                     help="feed the stem a packed NC/32HW32 input made by a separate pack kernel in the step")
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace[0], args.summarize_trace[1],
+                        os.path.join(ROOT, "profiles", f"kernel_stats_{args.workload}.txt"), args.workload, args.note)
+        return
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.copy_calibration_mib << 20,
                       os.path.join(ROOT, "profiles", f"hbm_traffic_{args.workload}.txt"), args.workload, args.note)
@@ -384,7 +433,11 @@ def main():
         return (kernel_name(c3spec, nhwc, proj=pspec), o3 + op, b3 + bp - 2 * shortcut, fn)
 
     if args.workload in ("net", "net26_b1"):
-        nb = sub_batch if 0 < sub_batch < n else n
+        # the forward's passes: a whole batch of >= 512 images runs as two concurrent halves
+        if sub_batch == 0 and n >= 512:
+            nb = (n + 1) // 2
+        else:
+            nb = sub_batch if 0 < sub_batch < n else n
         passes = (n + nb - 1) // nb
         big = max(ifx.act_bytes(nb, h, w, s.c_out if s.k != 7 else 64) for s, _, h, w in layers)
         big = max(big, ifx.act_bytes(nb, 56, 56, 256))
