@@ -433,8 +433,8 @@ def main():
         return (kernel_name(c3spec, nhwc, proj=pspec), o3 + op, b3 + bp - 2 * shortcut, fn)
 
     if args.workload in ("net", "net26_b1"):
-        # the forward's passes: a whole batch of >= 512 images runs as two concurrent halves
-        if sub_batch == 0 and n >= 512:
+        # the forward's passes: a whole batch of >= 192 images runs as two concurrent halves
+        if sub_batch == 0 and n >= 192:
             nb = (n + 1) // 2
         else:
             nb = sub_batch if 0 < sub_batch < n else n

@@ -312,7 +312,7 @@ struct NetPlan {
 // A whole batch of at least this many images (sub_batch 0) runs as two concurrent halves, one on
 // the caller's stream and one on a library stream: the last, partly filled round of tiles of
 // each launch then overlaps the other half's work.
-constexpr int kTwoLaneMin = 512;
+constexpr int kTwoLaneMin = 192;
 
 ifx_status plan_net(const ifx_net_params *p, int n, NetPlan *plan)
 {

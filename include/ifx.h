@@ -206,7 +206,7 @@ ifx_status ifx_block_forward(const ifx_block_params *p, const int8_t *x_blk, int
  * convolution (ifx_pack_weights with kh = kw = 1, c_in = fc_in,
  * c_out = fc_out).  sub_batch > 0 runs the network over consecutive groups
  * of sub_batch images, one after another on `stream`; 0 runs the whole batch
- * at once, and a batch of 512 or more images then runs as two halves at the
+ * at once, and a batch of 192 or more images then runs as two halves at the
  * same time: the first on `stream`, the second on a stream the library
  * creates (default priority, once per device, kept for the process), forked
  * from `stream` and joined back into it by events, so every result is still

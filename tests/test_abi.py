@@ -212,14 +212,20 @@ def test_net_validation_and_workspace():
     assert ifx.net_workspace_bytes(p, 4) == ws // 2 + _split_bytes(2, 56, 56, 64, 64, 3, 1, 1)
     fake = ctypes.c_void_p(0x200000)
     assert L.ifx_net_forward(ctypes.byref(p), fake, fake, 4, fake, ws // 2 - 1, None) == 5
-    # a whole batch of >= 512 images runs as two concurrent halves, each with its own workspace
-    p.sub_batch = 0
-    half = ifx.net_workspace_bytes(p, 256)
+    # a whole batch of >= 192 images runs as two concurrent halves, each with its own workspace
     p.sub_batch = 256
+    half = ifx.net_workspace_bytes(p, 256)                  # one pass of 256 images
     assert ifx.net_workspace_bytes(p, 512) == half          # consecutive passes share one workspace
     p.sub_batch = 0
     assert ifx.net_workspace_bytes(p, 512) == 2 * half
-    assert ifx.net_workspace_bytes(p, 511) > half           # one pass of 511 images
+    p.sub_batch = 96
+    lane96 = ifx.net_workspace_bytes(p, 96)
+    p.sub_batch = 0
+    assert ifx.net_workspace_bytes(p, 192) == 2 * lane96
+    p.sub_batch = 191
+    one = ifx.net_workspace_bytes(p, 191)
+    p.sub_batch = 0
+    assert ifx.net_workspace_bytes(p, 191) == one           # below 192: one pass
     p.fc_in = 255
     assert ifx.net_workspace_bytes(p, 4) == 0
 

@@ -418,7 +418,7 @@ def test_small_net_pool_and_head(ifx, orc, n, h, w, nblk):
         torch.cuda.synchronize()
         check_guards(whole)
         np.testing.assert_array_equal(logits.view(n, fc_out).cpu().numpy(), exp)
-    if n >= 512:
+    if n >= 192:
         p.sub_batch = 0
         ws = torch.empty(ifx.net_workspace_bytes(p, n), dtype=torch.int8, device="cuda")
         logits, whole = guarded(n * fc_out * 4, torch.int32)
