@@ -14,11 +14,16 @@
  * Conventions for every entry point:
  *   - Pointers named *_blk, x_nhwc, w_ohwi, bias, mult, shift, residual, y,
  *     logits and ws are DEVICE pointers (HIP global memory), 16-byte aligned.
- *     The caller owns all memory; the library never allocates or frees.
+ *     The caller owns all memory; the library never allocates or frees
+ *     device memory (its only resources are a graph handle's host state and,
+ *     for ifx_net_forward on a large batch, one stream per device and two
+ *     events per call).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
- *     Calls only enqueue kernels on it and never synchronise; results are
- *     valid once the stream reaches that point.  Calls that overlap on the
- *     same output or workspace race.
+ *     Calls only enqueue work on it (kernels; for ifx_net_forward on a batch
+ *     of 192 or more images also an event fork to the library's stream and
+ *     the join back) and never synchronise; results are valid once the
+ *     stream reaches that point.  Calls that overlap on the same output or
+ *     workspace race.
  *   - Arguments are validated on the host before anything is launched.  On
  *     an error status nothing has been enqueued.  Validation touches no
  *     device, so every error path runs without a GPU.
@@ -180,7 +185,11 @@ ifx_status ifx_conv_proj_fused(const ifx_conv_desc *d3, const int8_t *t_blk, con
  * as ifx_conv_proj_fused and sc is not materialised.
  * Descriptors carry the batch in n.  Their flags must be: d[0], d[1] without
  * RESIDUAL/MAXPOOL/OUT_I32, d[2] with RESIDUAL, d[3] without RESIDUAL/MAXPOOL/
- * OUT_I32.  t1, t2 and sc live in the caller's workspace.
+ * OUT_I32.  t1, t2 and sc live in the caller's workspace, and so do the int32
+ * partial sums of a convolution that has few output tiles and a long
+ * reduction (a small batch): it is split over K into parts whose sums a
+ * second kernel adds (integer addition, so the result is the same in any
+ * order) before applying the convolution's epilogue.
  */
 typedef struct {
     ifx_conv_desc d[4]; /* c1, c2, c3, projection */
