@@ -31,10 +31,10 @@ RIDGE = PEAK_I8 / PEAK_HBM
 METRIC = "int8 TOPS + images/s (fused conv stack), % of int8 MFMA peak / HBM BW"
 
 
-def kernel_name(spec, nhwc_input=True, proj=None) -> str:
+def kernel_name(spec, nhwc_input=True, proj=None, w=None) -> str:
     """The kernel template instance a conv layer dispatches to, spelled as rocprofv3
     prints it (mirrors the library's host dispatch).  proj: the projection shortcut's
-    spec when `spec` is a conv3 fused with it (ifx_conv_proj_fused)."""
+    spec when `spec` is a conv3 fused with it (ifx_conv_proj_fused); w: the input width."""
     if spec.k == 7:
         return f"stem_kernel<{1 if nhwc_input else 0}>"
     oc_pad = (spec.c_out + 31) // 32 * 32
@@ -45,6 +45,9 @@ def kernel_name(spec, nhwc_input=True, proj=None) -> str:
     if proj is not None and spec.k == 1 and spec.stride == 1 and i1 <= 4 and (proj.c_in + 31) // 32 <= 4:
         # both contractions short: the small-K fused kernel, shortcut kept in registers
         return f"conv1x1_proj_kernel<{bm}, {bn}, {((proj.c_in + 31) // 32 + 1) // 2}, {(i1 + 1) // 2}, {relu}>"
+    if spec.k == 3 and spec.stride == 1 and i1 <= 2 and w is not None and 48 <= w <= 62 and res == "false" \
+            and proj is None:
+        return f"conv3x3_halo_kernel<{relu}>"  # stride-1 3x3, <= 64 input channels: haloed window
     if spec.k == 1 and spec.pad == 0 and i1 <= 4 and proj is None:
         return f"conv1x1_kernel<{bm}, {bn}, {(i1 + 1) // 2}, {res}, {relu}>"
     st = 2
@@ -61,6 +64,7 @@ KERNEL_SOURCES = {
     "igemm_kernel": ["igemm.hip", "device_common.h", "ifx_internal.h"],
     "conv1x1_kernel": ["conv1x1.hip", "device_common.h", "ifx_internal.h"],
     "conv1x1_proj_kernel": ["conv1x1.hip", "device_common.h", "ifx_internal.h"],
+    "conv3x3_halo_kernel": ["igemm.hip", "device_common.h", "ifx_internal.h"],
     "stem_kernel": ["stem.hip", "device_common.h", "ifx_internal.h"],
 }
 
@@ -101,7 +105,7 @@ def summarize_pmc(fetch_csv: str, write_csv: str, calib_bytes: int, out: str, wo
     from collections import defaultdict
 
     def short(name):
-        m = re.search(r"((?:conv1x1_proj|conv1x1|igemm|stem)_kernel<[^>]*>)", name)
+        m = re.search(r"((?:conv1x1_proj|conv1x1|conv3x3_halo|igemm|stem)_kernel<[^>]*>)", name)
         if m:
             return m.group(1)
         return "copy" if "bitwise_not" in name else None
@@ -172,7 +176,7 @@ def summarize_trace(trace_csv: str, stats_csv: str, out: str, workload: str, not
     last_pool = max((int(r["Dispatch_Id"]) for r in rows if "avgpool_kernel" in r["Kernel_Name"]), default=-1)
     rep = defaultdict(list)
     for r in rows:
-        m = re.search(r"((?:conv1x1_proj|conv1x1|igemm|stem)_kernel<[^>]*>)", r["Kernel_Name"])
+        m = re.search(r"((?:conv1x1_proj|conv1x1|conv3x3_halo|igemm|stem)_kernel<[^>]*>)", r["Kernel_Name"])
         if m and int(r["Dispatch_Id"]) > last_pool:
             rep[m.group(1)].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
     lines += ["#", "# per-launch replays only (one conv launch at a time on one stream; bench.py's",
@@ -423,7 +427,7 @@ def main():
 
     def conv_launch(spec, nb_, h, w, fn):
         ops, byts, _, _ = layer_work(spec, nb_, h, w)
-        return (kernel_name(spec, nhwc), ops, byts, fn)
+        return (kernel_name(spec, nhwc, w=w), ops, byts, fn)
 
     def proj_launch(c3spec, pspec, nb_, h3, w3, hp, wp, fn):
         # conv3 + projection in one kernel: both contractions; the shortcut is not a tensor

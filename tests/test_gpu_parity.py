@@ -168,6 +168,12 @@ FUSED_SHAPES = [
     # strided 3x3 with >= 256 output channels: 128x256 tiles of eight waves
     (2, 9, 11, 64, 256, 3, 2, 1),
     (1, 8, 7, 96, 288, 3, 2, 1),     # ragged output channels, odd channel-block count
+    # stride-1 3x3, <= 64 input channels, 48 <= W <= 62: the haloed-window kernel (flags 0 and 1;
+    # with a shortcut the general kernel runs)
+    (2, 56, 56, 64, 64, 3, 1, 1),    # the res2 shape: 14 row bands of 4 rows
+    (3, 13, 50, 40, 96, 3, 1, 1),    # ragged last band (13 rows), two channel blocks, padded channels
+    (1, 7, 62, 32, 64, 3, 1, 1),     # widest window (pitch 64), one channel block
+    (2, 5, 48, 64, 200, 3, 1, 1),    # narrowest, four output-channel tiles, padding in the last
 ]
 
 
