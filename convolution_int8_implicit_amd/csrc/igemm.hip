@@ -510,69 +510,55 @@ hipError_t launch_conv_proj(const ConvArgs &a, const ConvArgs &pj, hipStream_t s
 
 namespace {
 
-// ---- stride-1 3x3 over at most 64 input channels: one haloed input window per tile ------------
+// ---- stride-1 3x3 over at most 64 input channels: haloed input windows ------------------------
 //
 // The general kernel fetches each tap's activation rows again (nine 64-byte K-steps per pixel
-// for 64 input channels), so for the res2-shaped 3x3 (56x56, 64 -> 64) the activation DMA is the
-// largest cost.  Here a workgroup owns 4 whole output rows of one image x 64 output channels: it
-// stages the input window (6 rows, pitch 64 pixels, both 32-channel blocks, zero outside the
-// image) and all nine taps of the weights in LDS once, then runs the nine K-steps reading shifted
-// window rows.  The window uses the general kernel's row swizzle; with a pitch that is a multiple
-// of 16 rows the kernel-row offset is a constant (2048 bytes per row), so only the three column
-// offsets need swizzled base addresses.
+// for 64 input channels), so for the res2-shaped 3x3 (56x56, 64 -> 64) the activation DMA is its
+// largest cost.  Here a persistent workgroup of eight waves owns one 64-channel output tile: it
+// stages all nine taps of those weights (and their parameters) in LDS once, then walks a
+// contiguous run of 8-row bands of whole image rows.  Each band's input window (10 rows at a
+// pitch of 64 pixels, both 32-channel blocks, zero outside the image) is fetched once, into one
+// of two buffers, while the previous band computes; the nine K-steps read shifted window rows.
+// The window keeps the general kernel's row swizzle; with a pitch that is a multiple of 16 rows
+// the kernel-row offset is a constant (2048 bytes per row), so only the three column offsets
+// need swizzled base addresses, and those do not depend on the band.
 
 constexpr int kHaloPitch = 64;                          // window row pitch (pixels), >= W + 2
-constexpr int kHaloTR = 4;                              // output rows per tile
-constexpr int kHaloRows = (kHaloTR + 2) * kHaloPitch;  // 384 window pixels per 32-channel block
-constexpr int kHaloA = 2 * kHaloRows * 32;              // window: 24 KB
+constexpr int kHaloTR = 8;                              // output rows per band
+constexpr int kHaloRows = (kHaloTR + 2) * kHaloPitch;  // 640 window pixels per 32-channel block
+constexpr int kHaloWin = 2 * kHaloRows * 32;            // one window: 40 KB
 constexpr int kHaloB = 9 * 2 * 64 * 32;                 // weights: 9 taps x 2 blocks x 64 rows, 36 KB
-constexpr int kHaloLds = kHaloA + kHaloB + 4 * 768;     // + per-wave parameters
+constexpr int kHaloLds = kHaloB + 2 * kHaloWin + 8 * 768;
+constexpr int kHaloWinDma = kHaloWin / 1024 / 8;        // window DMAs per wave (5)
+static_assert(kHaloWinDma * 8 * 1024 == kHaloWin, "whole window DMAs per wave");
 
 template <bool RELU>
-__global__ __launch_bounds__(256, 2) void conv3x3_halo_kernel(ConvArgs a, int bands, int tiles_n, int tiles,
-                                                              int per_xcd)
+__global__ __launch_bounds__(512, 1) void conv3x3_halo_kernel(ConvArgs a, int bands, int tiles_n, int per_wg)
 {
     __shared__ __attribute__((aligned(1024))) int8_t smem[kHaloLds];
-    int8_t *const WA = smem;           // [block][384 rows][32 B], slots as a_swz; later the output staging
-    int8_t *const WB = smem + kHaloA;  // [tap][block][64 rows][32 B], slots as b_swz
+    int8_t *const WB = smem;                      // [tap][block][64 rows][32 B], slots as b_swz
+    int8_t *const Win = smem + kHaloB;            // two windows [block][640 rows][32 B], slots as a_swz
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    int8_t *const Pw = WB + kHaloB + wave * 768;
+    int8_t *const Pw = smem + kHaloB + 2 * kHaloWin + wave * 768;
 
-    // tiles of XCD x are [x * per_xcd, (x + 1) * per_xcd): the channel tiles of one band, then the
-    // next band of the same image (sharing two window rows), share an L2
-    const int t = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
-    if (t >= tiles) return;
-    const int bt = t / tiles_n;
-    const int n0 = (t - bt * tiles_n) * 64;
-    const int b = bt / bands;
-    const int y0 = (bt - b * bands) * kHaloTR;
+    const int n0 = (int)(blockIdx.x % (unsigned)tiles_n) * 64;
+    const int first = (int)(blockIdx.x / (unsigned)tiles_n) * per_wg;  // this workgroup's bands
+    const int nbands = min(per_wg, a.n * bands - first);
+    if (nbands <= 0) return;
     const int W = a.w, H = a.h, HW = H * W;
-    const int m_tile = kHaloTR * W;                 // fragment rows of the tile (<= 248)
-    const int m_valid = min(kHaloTR, H - y0) * W;   // rows inside the image
-
-    // window: 2 blocks x 12 DMAs of 32 rows, 6 per wave; row R = window pixel (R / 64, R % 64)
     const long long in_img = (long long)a.i1 * HW * 32;
-    const v4i rsA = make_rsrc(a.x + (long long)b * in_img, in_img);
-#pragma unroll
-    for (int j = 0; j < 6; ++j) {
-        const int q = j * 4 + wave;
-        const int blk = q / 12, chunk = q - blk * 12;
-        const int R = chunk * 32 + dma_a_row(lane);
-        const int h = dma_a_h(lane);
-        const int y = y0 - 1 + (R >> 6), x = (R & 63) - 1;
-        const bool ok = blk < a.i1 && (unsigned)y < (unsigned)H && (unsigned)x < (unsigned)W;
-        const unsigned off = ok ? (unsigned)((blk * HW + y * W + x) * 32 + h * 16) : kOOB;
-        load16_lds(rsA, WA + blk * (kHaloRows * 32) + chunk * 1024, off);
-    }
-    // weights of channels n0 .. n0+63: 9 taps x 2 blocks x 2 DMAs of 32 rows, 9 per wave
+    const long long out_img = (long long)a.oc1 * HW * 32;
+
+    // weights and parameters of channels n0 .. n0+63, once: 36 DMAs over the eight waves
     const int wrows = ((a.oc + a.o2 - 1) / a.o2) * a.o2;
     const v4i rsB = make_rsrc(a.wt, (long long)wrows * 9 * a.i1 * 32);
     const int wblk = a.o2 * 32;
 #pragma unroll
-    for (int j = 0; j < 9; ++j) {
-        const int q = j * 4 + wave;
+    for (int j = 0; j < 5; ++j) {
+        const int q = j * 8 + wave;
+        if (q >= 36) break;
         const int tb = q >> 1, chunk = q & 1;  // (tap, block) slice and its 32-row half
         const int tap = tb >> 1, blk = tb & 1;
         const int R = n0 + chunk * 32 + dma_b_row(lane);
@@ -593,16 +579,37 @@ __global__ __launch_bounds__(256, 2) void conv3x3_halo_kernel(ConvArgs a, int ba
         load16_lds(make_rsrc(a.shift, (long long)a.oc * 4), Pw + 512, off);
     }
 
-    // fragment addresses: lane (c, g) reads half g % 2 of block g / 2 at window pixel
-    // R0 + 64 ky + kx of its output pixel m = 64 wave + 16 tm + 4 (c % 4) + c / 4 (rows past the
-    // tile repeat its last row; they are never stored)
+    // a band's window into buffer buf: 2 blocks x 20 DMAs of 32 rows, 5 per wave; row R is window
+    // pixel (R / 64, R % 64), image pixel (y0 - 1 + R / 64, R % 64 - 1)
+    auto issue_window = [&](int band_id, int buf) __attribute__((always_inline)) {
+        const int b = band_id / bands;
+        const int y0 = (band_id - b * bands) * kHaloTR;
+        const v4i rsA = make_rsrc(a.x + (long long)b * in_img, in_img);
+        int8_t *const dst = Win + buf * kHaloWin;
+#pragma unroll
+        for (int j = 0; j < kHaloWinDma; ++j) {
+            const int q = j * 8 + wave;
+            const int blk = q / 20, chunk = q - blk * 20;
+            const int R = chunk * 32 + dma_a_row(lane);
+            const int h = dma_a_h(lane);
+            const int y = y0 - 1 + (R >> 6), x = (R & 63) - 1;
+            const bool ok = blk < a.i1 && (unsigned)y < (unsigned)H && (unsigned)x < (unsigned)W;
+            const unsigned off = ok ? (unsigned)((blk * HW + y * W + x) * 32 + h * 16) : kOOB;
+            load16_lds(rsA, dst + blk * (kHaloRows * 32) + chunk * 1024, off);
+        }
+    };
+
+    // fragment addresses (band-independent): lane (c, g) reads half g % 2 of block g / 2 at
+    // window pixel R0 + 64 ky + kx of its output pixel m = 64 wave + 16 tm + 4 (c % 4) + c / 4
+    // of the band (rows past the band repeat its last row; they are never stored)
     const int c = lane & 15;
     const int g = lane >> 4;
     const int wm0 = wave * 64;
+    const int m_band = kHaloTR * W;  // <= 496
     int abase[4][3];
 #pragma unroll
     for (int tm = 0; tm < 4; ++tm) {
-        const int m = min(wm0 + 16 * tm + 4 * (c & 3) + (c >> 2), m_tile - 1);
+        const int m = min(wm0 + 16 * tm + 4 * (c & 3) + (c >> 2), m_band - 1);
         const int oy = fdiv(m, a.wo_mul, a.wo_shr);
         const int R0 = oy * kHaloPitch + (m - oy * W);
 #pragma unroll
@@ -611,43 +618,59 @@ __global__ __launch_bounds__(256, 2) void conv3x3_halo_kernel(ConvArgs a, int ba
     int bfr[4];
 #pragma unroll
     for (int tn = 0; tn < 4; ++tn) bfr[tn] = ((g >> 1) * 2048 + b_swz(4 * c, g & 1)) ^ (tn << 5);
+    const int k = lane & 3;
+    const int och = n0 + 16 * k;  // first channel of this lane's 16-byte output chunk
 
-    wait_vmcnt<0>();
-    ring_barrier();
-    v4i acc[4][4];
+    issue_window(first, 0);
+    for (int i = 0; i < nbands; ++i) {
+        const int buf = i & 1;
+        // the other buffer's last readers (band i-1's staging) are behind this barrier
+        if (i > 0) ring_barrier();
+        if (i + 1 < nbands) {
+            issue_window(first + i + 1, buf ^ 1);
+            wait_vmcnt<kHaloWinDma>();  // all but the next window's DMAs have landed
+        } else {
+            wait_vmcnt<0>();
+        }
+        ring_barrier();  // ... for every wave: band i's window (and the weights) are visible
+        const int8_t *const win = Win + buf * kHaloWin;
+        v4i acc[4][4];
 #pragma unroll
-    for (int ky = 0; ky < 3; ++ky)
+        for (int ky = 0; ky < 3; ++ky)
 #pragma unroll
-        for (int kx = 0; kx < 3; ++kx) {
-            const int8_t *wb = WB + (ky * 3 + kx) * 4096;
-            v4i bf[4];
+            for (int kx = 0; kx < 3; ++kx) {
+                const int8_t *wb = WB + (ky * 3 + kx) * 4096;
+                v4i bf[4];
 #pragma unroll
-            for (int tn = 0; tn < 4; ++tn) bf[tn] = *(const v4i *)(wb + bfr[tn]);
+                for (int tn = 0; tn < 4; ++tn) bf[tn] = *(const v4i *)(wb + bfr[tn]);
 #pragma unroll
-            for (int tm = 0; tm < 4; ++tm) {
-                const v4i af = *(const v4i *)(WA + abase[tm][kx] + 2048 * ky);
+                for (int tm = 0; tm < 4; ++tm) {
+                    const v4i af = *(const v4i *)(win + abase[tm][kx] + 2048 * ky);
 #pragma unroll
-                for (int tn = 0; tn < 4; ++tn)
-                    acc[tm][tn] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
-                        af, bf[tn], (ky == 0 && kx == 0) ? (v4i){0, 0, 0, 0} : acc[tm][tn], 0, 0, 0);
+                    for (int tn = 0; tn < 4; ++tn)
+                        acc[tm][tn] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                            af, bf[tn], (ky == 0 && kx == 0) ? (v4i){0, 0, 0, 0} : acc[tm][tn], 0, 0, 0);
+                }
+            }
+        // every wave's fragment reads of this window are done: it takes the 4 KB staging tiles
+        ring_barrier();
+        int8_t *const Rw = (int8_t *)win + wave * 4096;
+        requant_to_lds<false, RELU, true>(acc, Rw + g * 64 + 4 * c, Pw, c, n0 + 4 * c, a.oc);
+        wave_lds_sync();
+        // 16-byte stores: lane -> band row 16 j + lane / 4, channels och .. och + 15
+        const int band_id = first + i;
+        const int b = band_id / bands;
+        const int y0 = (band_id - b * bands) * kHaloTR;
+        const int m_valid = min(kHaloTR, H - y0) * W;
+        if (och < a.oc1 * 32) {
+            int8_t *const yb = (int8_t *)a.y + (long long)b * out_img + ((long long)(och >> 5) * HW + y0 * W) * 32 +
+                               (och & 31);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 16 * j + (lane >> 2);
+                if (wm0 + r < m_valid) *(v4i *)(yb + (long long)(wm0 + r) * 32) = *(const v4i *)(Rw + r * 64 + 16 * k);
             }
         }
-
-    // epilogue: every wave's fragment reads are done, so the window takes the 4 KB staging tiles
-    ring_barrier();
-    int8_t *const Rw = WA + wave * 4096;
-    requant_to_lds<false, RELU, true>(acc, Rw + g * 64 + 4 * c, Pw, c, n0 + 4 * c, a.oc);
-    wave_lds_sync();
-    // 16-byte stores: lane -> tile row 16 j + lane / 4, channels n0 + 16 (lane % 4) .. + 15
-    const int k = lane & 3;
-    const int och = n0 + 16 * k;
-    if (och >= a.oc1 * 32) return;
-    int8_t *const yb = (int8_t *)a.y + (long long)b * a.oc1 * HW * 32 + ((long long)(och >> 5) * HW + y0 * W) * 32 +
-                       (och & 31);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int r = 16 * j + (lane >> 2);
-        if (wm0 + r < m_valid) *(v4i *)(yb + (long long)(wm0 + r) * 32) = *(const v4i *)(Rw + r * 64 + 16 * k);
     }
 }
 
@@ -657,20 +680,36 @@ bool conv3x3_halo_supported(const ConvArgs &a, int kh, int kw)
            !a.residual && !a.out_i32 && a.ksplit <= 1 && a.ho == a.h && a.wo == a.w;
 }
 
+// Persistent grid: as many eight-wave workgroups as fit on the chip, in groups of tiles_n (one per
+// 64-channel output tile), each group taking an equal contiguous run of bands.
 hipError_t launch_conv3x3_halo(const ConvArgs &a, hipStream_t s)
 {
+    static int slots = 0;  // workgroups resident on the chip at once
+    if (slots == 0) {
+        int dev = 0, cus = 0, per_cu = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e == hipSuccess)
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, conv3x3_halo_kernel<true>, 512, 0);
+        if (e != hipSuccess) return e;
+        slots = (per_cu < 1 ? 1 : per_cu) * cus;
+    }
     const int bands = (a.h + kHaloTR - 1) / kHaloTR;
     const int tiles_n = (a.oc1 * 32 + 63) / 64;
-    const long long tiles = (long long)a.n * bands * tiles_n;
-    if (tiles <= 0) return hipSuccess;
-    if (tiles > 0x7ffffff0LL) return hipErrorInvalidConfiguration;
+    const long long total = (long long)a.n * bands;  // bands of the whole batch
+    if (total <= 0) return hipSuccess;
+    if (total > 0x7ffffff0LL) return hipErrorInvalidConfiguration;
     if ((long long)a.i1 * a.h * a.w * 32 >= 0x7fffffffLL) return hipErrorInvalidValue;
-    const int per_xcd = (int)((tiles + 7) / 8);
-    const dim3 grid((unsigned)per_xcd * 8u);
+    long long groups = slots / tiles_n;
+    if (groups < 1) groups = 1;
+    if (groups > total) groups = total;
+    const int per_wg = (int)((total + groups - 1) / groups);
+    groups = (total + per_wg - 1) / per_wg;
+    const dim3 grid((unsigned)(groups * tiles_n));
     if (a.relu)
-        hipLaunchKernelGGL(conv3x3_halo_kernel<true>, grid, dim3(256), 0, s, a, bands, tiles_n, (int)tiles, per_xcd);
+        hipLaunchKernelGGL(conv3x3_halo_kernel<true>, grid, dim3(512), 0, s, a, bands, tiles_n, per_wg);
     else
-        hipLaunchKernelGGL(conv3x3_halo_kernel<false>, grid, dim3(256), 0, s, a, bands, tiles_n, (int)tiles, per_xcd);
+        hipLaunchKernelGGL(conv3x3_halo_kernel<false>, grid, dim3(512), 0, s, a, bands, tiles_n, per_wg);
     return hipGetLastError();
 }
 
