@@ -659,8 +659,9 @@ ifx_status ifx_net_graph_create(const ifx_net_params *p, const int8_t *x_blk, in
         st = hip_status(lane_stream(&lane1));
         if (st != IFX_OK) return st;
     }
-    // the stem launcher's one-time device query happens now, outside the capture
+    // the stem and window-kernel launchers' one-time device queries happen now, outside the capture
     st = hip_status(ifx::warm_stem_queries());
+    if (st == IFX_OK) st = hip_status(ifx::warm_halo_query());
     if (st != IFX_OK) return st;
 
     hipStream_t cs = nullptr;

@@ -71,6 +71,8 @@ struct FoldArgs {
     const float *w_scale, *conv_bias, *gamma, *beta, *mean, *var;
 };
 
+// One-time device query of the haloed-window 3x3 launcher (run before any stream capture).
+hipError_t warm_halo_query();
 hipError_t launch_conv(const ConvArgs &a, int kh, int kw, hipStream_t s);
 // Bytes of int32 partial sums launch_conv_split would use for `a` (0: it would not split).  A
 // convolution on few output tiles with a long reduction is split over workgroups along K.

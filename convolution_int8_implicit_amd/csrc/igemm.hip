@@ -682,9 +682,10 @@ bool conv3x3_halo_supported(const ConvArgs &a, int kh, int kw)
 
 // Persistent grid: as many eight-wave workgroups as fit on the chip, in groups of tiles_n (one per
 // 64-channel output tile), each group taking an equal contiguous run of bands.
-hipError_t launch_conv3x3_halo(const ConvArgs &a, hipStream_t s)
+// Workgroups of the persistent kernel resident on the chip at once; queried once per process.
+hipError_t halo_slots(int *out)
 {
-    static int slots = 0;  // workgroups resident on the chip at once
+    static int slots = 0;
     if (slots == 0) {
         int dev = 0, cus = 0, per_cu = 0;
         hipError_t e = hipGetDevice(&dev);
@@ -694,6 +695,15 @@ hipError_t launch_conv3x3_halo(const ConvArgs &a, hipStream_t s)
         if (e != hipSuccess) return e;
         slots = (per_cu < 1 ? 1 : per_cu) * cus;
     }
+    *out = slots;
+    return hipSuccess;
+}
+
+hipError_t launch_conv3x3_halo(const ConvArgs &a, hipStream_t s)
+{
+    int slots = 0;
+    hipError_t e = halo_slots(&slots);
+    if (e != hipSuccess) return e;
     const int bands = (a.h + kHaloTR - 1) / kHaloTR;
     const int tiles_n = (a.oc1 * 32 + 63) / 64;
     const long long total = (long long)a.n * bands;  // bands of the whole batch
@@ -714,6 +724,12 @@ hipError_t launch_conv3x3_halo(const ConvArgs &a, hipStream_t s)
 }
 
 }  // namespace
+
+hipError_t warm_halo_query()
+{
+    int slots = 0;
+    return halo_slots(&slots);
+}
 
 hipError_t launch_conv(const ConvArgs &a, int kh, int kw, hipStream_t s)
 {
