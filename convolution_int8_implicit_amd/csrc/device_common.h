@@ -49,7 +49,7 @@ __device__ __forceinline__ void lds_barrier()
     asm volatile("" ::: "memory");
 }
 
-// Requantisation, exact for every |y| < 2^31, 0 <= m < 2^31, 0 <= sh <= 31:
+// Requantisation, exact for every int32 y (-2^31 <= y < 2^31), 0 <= m < 2^31, 0 <= sh <= 31:
 //   q = round_half_away_from_zero(y * m / 2^(31+sh))
 //     = floor((y*m + 2^(30+sh) - [y<0]) / 2^(31+sh))     (floor = arithmetic shift)
 // General form: one 64-bit product and one 64-bit shift.
@@ -164,8 +164,9 @@ struct RqLane {
 //      on a negative value ends at 0 either way): q = hi(acc*m + add) >> (shift-1), one
 //      v_mad_i64_i32 and one shift per element, the bias folded into `add`;
 //   2  every shift >= 2: requant_fast, which carries the [y<0] tie correction.
-// A tie (y*m/2^(31+s) exactly halfway) needs v2(y) + v2(m) = 30 + s with v2(y) <= 30 for
-// |y| < 2^31, so it cannot happen when m has fewer than s trailing zero bits (or m == 0).
+// A tie (y*m/2^(31+s) exactly halfway) needs v2(y) + v2(m) = 30 + s.  An int32 y has
+// v2(y) <= 31, with 31 only for y = -2^31 (a bias of INT32_MIN on a zero sum reaches it), so no
+// tie can happen when m has at most s - 2 trailing zero bits (or m == 0).
 template <bool RES, bool RELU>
 __device__ __forceinline__ int rq_setup(RqLane &r, v4i bias4, v4i mult4, v4i shift4, bool bias_in_acc, int ocl,
                                         int oc)
@@ -184,7 +185,7 @@ __device__ __forceinline__ int rq_setup(RqLane &r, v4i bias4, v4i mult4, v4i shi
         r.shm[tn] = s - 1;
         r.add[tn] = (long long)b * (long long)m + (long long)((unsigned long long)(unsigned)r.rnd[tn] << 32);
         fast = fast && s >= 2;
-        tiefree = tiefree && (m == 0 || (int)__builtin_ctz((unsigned)m) < s);
+        tiefree = tiefree && (m == 0 || (int)__builtin_ctz((unsigned)m) + 1 < s);
     }
     if (!__all(fast)) return 0;
     if ((!RES && RELU) || __all(tiefree)) return 1;

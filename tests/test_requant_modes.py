@@ -4,7 +4,8 @@ oracle's round-half-away-from-zero requantisation.
 The kernels compute q = round_half_away(y * m / 2^(31+s)) three ways (device_common.h): a
 general 64-bit form, a one-multiply form without the tie correction, and a form with it.  The
 one-multiply form is used only when every channel of a wave has s >= 2 and either a multiplier
-with fewer than s trailing zero bits (a halfway tie cannot occur) or ReLU without a shortcut.
+with at most s - 2 trailing zero bits (no halfway tie can occur for any int32 sum, -2^31
+included) or ReLU without a shortcut.
 These tests model that arithmetic in Python integers and require it to agree with the oracle,
 including on the values most likely to tie.
 """
@@ -21,21 +22,23 @@ def one_multiply(y, m, s):
 
 
 def tie_free(m, s):
-    return m == 0 or (m & -m).bit_length() - 1 < s
+    """The kernels' predicate: m == 0, or ctz(m) + 1 < s."""
+    return m == 0 or (m & -m).bit_length() - 1 + 1 < s
 
 
 def candidates(rng, m, s, count=400):
     """Random sums plus the sums nearest to every halfway point reachable in int32."""
-    ys = list(rng.integers(-(1 << 31) + 1, 1 << 31, size=count))
+    ys = list(rng.integers(-(1 << 31), 1 << 31, size=count))
     k = 31 + s
     for j in range(-200, 200):  # y*m close to (j + 1/2) * 2^k
         target = (2 * j + 1) << (k - 1)
         if m:
             for y0 in (target // m - 1, target // m, target // m + 1, -(-target // m)):
-                if -(1 << 31) < y0 < (1 << 31):
+                if -(1 << 31) <= y0 < (1 << 31):
                     ys.append(y0)
     for e in range(0, 31):  # high powers of two in y
         ys += [1 << e, -(1 << e), 3 << e if (3 << e) < (1 << 31) else 1]
+    ys += [-(1 << 31), (1 << 31) - 1]  # both ends of the int32 range (the oracle accepts both)
     return [int(y) for y in ys]
 
 
@@ -49,6 +52,17 @@ def test_tie_free_multipliers_need_no_tie_correction(s):
             continue
         for y in candidates(rng, m, s):
             assert one_multiply(y, m, s) == orc.requant(y, 0, m, s), (y, m, s)
+
+
+@pytest.mark.parametrize("m,s,want", [(128, 8, -1), ((1 << 30) | (1 << 15), 16, -16385)])
+def test_int32_min_ties_with_s_minus_1_trailing_zeros(m, s, want):
+    """y = -2^31 has 31 trailing zero bits, so a multiplier with exactly s - 1 of them puts it on
+    a tie: the one-multiply form rounds it up, the oracle away from zero.  The predicate must
+    send such a channel to the tie-correcting form."""
+    y = -(1 << 31)
+    assert orc.requant(y, 0, m, s) == want
+    assert one_multiply(y, m, s) == want + 1
+    assert not tie_free(m, s)
 
 
 def test_multipliers_with_many_trailing_zeros_do_tie():
