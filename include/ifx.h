@@ -16,8 +16,8 @@
  *     logits and ws are DEVICE pointers (HIP global memory), 16-byte aligned.
  *     The caller owns all memory; the library never allocates or frees
  *     device memory (its only resources are a graph handle's host state and,
- *     for ifx_net_forward on a large batch, one stream per device and two
- *     events per call).
+ *     for ifx_net_forward on a large batch, one stream and two events per
+ *     device, created on first use and kept for the process).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Calls only enqueue work on it (kernels; for ifx_net_forward on a batch
  *     of 192 or more images also an event fork to the library's stream and
@@ -52,7 +52,8 @@
  *   IFX_MAXPOOL: 3x3 stride-2 pad-1 max-pool of `out`, out-of-range taps
  *   ignored (stem only).
  * Caller contract, not checked on the device: 0 <= mult[o] < 2^31,
- * 0 <= shift[o] <= 31, |acc + bias| < 2^31.
+ * 0 <= shift[o] <= 31, and acc + bias inside the int32 range
+ * [-2^31, 2^31 - 1] (INT32_MIN included).
  */
 #ifndef IFX_H
 #define IFX_H
@@ -221,8 +222,10 @@ ifx_status ifx_block_forward(const ifx_block_params *p, const int8_t *x_blk, int
  * from `stream` and joined back into it by events, so every result is still
  * ordered on `stream`.  Each half has its own part of the workspace.  Results
  * are identical for every sub_batch.  Calls from several host threads on one
- * device share that library stream (their work is serialised there, still
- * correct).
+ * device share that library stream (their second halves are serialised
+ * there, still correct).  While `stream` is being captured into a graph both
+ * halves run on `stream` itself, one after the other: the shared library
+ * stream never joins a capture.
  *   x_blk   packed input [n, ceil(stem.c_in/32), stem.h, stem.w, 32], or the
  *           compact [n, stem.h, stem.w, stem.c_in] image when stem.flags has
  *           IFX_INPUT_NHWC
@@ -254,9 +257,11 @@ ifx_status ifx_net_forward(const ifx_net_params *p, const int8_t *x_blk, int32_t
  * ifx_graph_launch enqueues that whole sequence with one call (results as
  * ifx_net_forward; the buffers must stay valid and the parameter arrays p
  * points at unchanged while the graph exists); ifx_graph_destroy frees it.
- * Validation as ifx_net_forward; nothing runs during creation (the recording
- * uses a library-owned stream).  The graph handle is host state owned by the
- * library until ifx_graph_destroy (NULL is accepted there).
+ * Validation as ifx_net_forward; nothing runs during creation.  The recording
+ * uses a stream (and, for two halves, a second stream and two events) of its
+ * own, created for it and destroyed after it, so recording is independent of
+ * other threads' calls.  The graph handle is host state owned by the library
+ * until ifx_graph_destroy (NULL is accepted there).
  */
 typedef struct ifx_graph_s *ifx_graph;
 

@@ -170,7 +170,7 @@ FUSED_SHAPES = [
     (1, 8, 7, 96, 288, 3, 2, 1),     # ragged output channels, odd channel-block count
     # stride-1 3x3, <= 64 input channels, 48 <= W <= 62: the haloed-window kernel (flags 0 and 1;
     # with a shortcut the general kernel runs)
-    (2, 56, 56, 64, 64, 3, 1, 1),    # the res2 shape: 14 row bands of 4 rows
+    (2, 56, 56, 64, 64, 3, 1, 1),    # the res2 shape: 14 row bands of 8 rows, one per workgroup
     (3, 13, 50, 40, 96, 3, 1, 1),    # ragged last band (13 rows), two channel blocks, padded channels
     (1, 7, 62, 32, 64, 3, 1, 1),     # widest window (pitch 64), one channel block
     (2, 5, 48, 64, 200, 3, 1, 1),    # narrowest, four output-channel tiles, padding in the last
@@ -191,6 +191,24 @@ def test_fused_conv(ifx, orc, shape, flags):
     got = gpu_conv(ifx, x, wt, bias, mult, shift, k, s, p, flags, res)
     exp = orc.conv_fused(x, wt, bias, mult, shift, s, p, flags, res)
     np.testing.assert_array_equal(got, exp)
+
+
+# The haloed-window kernel is persistent: one workgroup per CU per 64-channel tile, each walking a
+# contiguous run of 8-row bands with the next band's window fetched into the second buffer while
+# the current one computes.  With 256 CUs a run holds two or more bands from 37 images of 56 rows
+# on (7 bands each), so these batches drive the double-buffered loop: 37 images leave a last
+# workgroup with a single band (ragged), 75 give three bands to every workgroup, and 128 output
+# channels halve the workgroups per tile (three bands each).
+@pytest.mark.parametrize("n,oc", [(37, 64), (75, 64), (37, 128)])
+@pytest.mark.parametrize("flags", [0, 1])
+def test_halo_window_multi_band(ifx, orc, n, oc, flags):
+    note(f"halo window multi-band n={n} oc={oc} flags={flags}")
+    rng = np.random.default_rng(n * 3 + oc + flags)
+    x = rand(rng, (n, 56, 56, 64), 0, 127)
+    wt = rand(rng, (oc, 3, 3, 64), -127, 127)
+    bias, mult, shift = params(rng, oc)
+    got = gpu_conv(ifx, x, wt, bias, mult, shift, 3, 1, 1, flags)
+    np.testing.assert_array_equal(got, orc.conv_fused(x, wt, bias, mult, shift, 1, 1, flags))
 
 
 def test_requant_edges(ifx, orc):
@@ -235,6 +253,33 @@ def test_requant_ties_with_shortcut(ifx, orc, k):
     for flags in (ifx.RESIDUAL, ifx.RESIDUAL | ifx.RELU):
         got = gpu_conv(ifx, x, wt, bias, mult, shift, k, 1, k // 2, flags, res)
         np.testing.assert_array_equal(got, orc.conv_fused(x, wt, bias, mult, shift, 1, k // 2, flags, res))
+
+
+@pytest.mark.parametrize("c,k", [(64, 1), (256, 1), (64, 3)])
+def test_requant_int32_min_sum(ifx, orc, c, k):
+    """acc + bias = -2^31 exactly (zero input, bias INT32_MIN, which the BN folding emits when it
+    clamps): with a multiplier of exactly shift - 1 trailing zero bits the value is a rounding
+    tie, so the tie-correcting requantisation must run.  Small-K 1x1 (c = 64), general 1x1
+    (c = 256) and 3x3 kernels; with and without a shortcut."""
+    note(f"requant int32-min sum c={c} k={k}")
+    rng = np.random.default_rng(31 + c + k)
+    n, h, w, oc = 2, 6, 5, 128
+    x = np.zeros((n, h, w, c), np.int8)
+    wt = rand(rng, (oc, k, k, c), -127, 127)
+    bias = np.full(oc, -(1 << 31), np.int32)
+    # y * m / 2^(31+s) = -m / 2^s: -1/2, -3/2, -255/2 (ties) and -1/2 - 2^-31 (no tie)
+    mult = np.tile(np.array([128, 3 << 14, 255 << 7, (1 << 30) | 1], np.int32), oc // 4)
+    shift = np.tile(np.array([8, 15, 8, 31], np.int32), oc // 4)
+    res = rand(rng, (n, h, w, oc), -128, 127)
+    for flags in (0, ifx.RESIDUAL, ifx.RESIDUAL | ifx.RELU):
+        r = res if flags & ifx.RESIDUAL else None
+        got = gpu_conv(ifx, x, wt, bias, mult, shift, k, 1, k // 2, flags, r)
+        exp = orc.conv_fused(x, wt, bias, mult, shift, 1, k // 2, flags, r)
+        np.testing.assert_array_equal(got, exp)
+    # the values themselves, rounded away from zero: -1, -2, -128, -1
+    exp = orc.conv_fused(x, wt, bias, mult, shift, 1, k // 2, 0)
+    assert np.all(exp[..., 0::4] == -1) and np.all(exp[..., 1::4] == -2)
+    assert np.all(exp[..., 2::4] == -128) and np.all(exp[..., 3::4] == -1)
 
 
 def test_identity_halves(ifx, orc):

@@ -121,7 +121,7 @@ def test_workload3_stem_sampled(ifx, orc):
     assert torch.equal(y, y2)
 
 
-def _oracle_net(orc, synth, wl, rows):
+def _oracle_net(orc, synth, wl, rows, trace=None):
     from oracle.ref import BlockParams
     net = wl.net
     stem = oracle_conv(orc, synth, net.stem, wl.index)
@@ -131,7 +131,7 @@ def _oracle_net(orc, synth, wl, rows):
               for b in net.blocks]
     fcp = synth.fc_params(wl.index, net)
     x = synth.input_tensor(wl, rows=rows).numpy()
-    return orc.net(x, stem, blocks, fcp["w"].numpy(), fcp["bias"].numpy())
+    return orc.net(x, stem, blocks, fcp["w"].numpy(), fcp["bias"].numpy(), trace=trace)
 
 
 def test_workload4_net_sampled_and_sub_batch_invariant(ifx, orc):
@@ -171,6 +171,55 @@ def test_workload4_net_sampled_and_sub_batch_invariant(ifx, orc):
         torch.cuda.synchronize()
         assert torch.equal(l3, logits)
         del ws3, nn_
+
+
+def test_workload4_every_layer_sampled(ifx, orc):
+    """Every layer of the batch-2048 network for sampled images, against the oracle's trace.
+
+    ifx_net_forward runs a batch of 2048 as two concurrent passes of 1024 images.  Here the
+    same launches are issued pass by pass through the C ABI (the fused stem reading the NHWC
+    images, then ifx_block_forward per bottleneck at batch 1024, i.e. the same kernels and
+    grids, the fused conv3 + projection included), and after each layer the sampled images
+    (the first and last of the batch, one in each pass, and two more) are compared byte for
+    byte with the oracle: the pooled stem output and all 16 block outputs."""
+    from convolution_int8_implicit_amd import model, synth
+    wl = synth.workload(4)
+    net = model.DeviceNet(wl.net, wl.index, nhwc_input=True)
+    rows = sample_rows(wl.n)
+    note(f"oracle trace on images {rows}")
+    trace = []
+    _oracle_net(orc, synth, wl, rows, trace=trace)
+    half = wl.n // 2
+    for p0 in (0, half):
+        mine = [i for i, r in enumerate(rows) if p0 <= r < p0 + half]
+        local = [rows[i] - p0 for i in mine]
+        note(f"pass of images {p0}..{p0 + half - 1}: sampled {[rows[i] for i in mine]}")
+        x = synth.input_tensor(wl, device="cuda", rows=list(range(p0, p0 + half)))
+        sd = ifx.ConvDesc.from_buffer_copy(net.stem.desc)
+        sd.n = half
+        t = model.empty_act(half, 56, 56, 64)
+        ifx.conv_fused(sd, x, net.stem.w_blk, net.stem.bias, net.stem.mult, net.stem.shift, None, t)
+        del x
+        torch.cuda.synchronize()
+        got = ifx.unpack_act(t[local].contiguous(), 64).cpu().numpy()
+        np.testing.assert_array_equal(got, trace[0][mine], err_msg="stem")
+        hh = ww = 56
+        for bi, blk in enumerate(net.blocks):
+            bp = ifx.BlockParams.from_buffer_copy(blk.params)
+            for i in range(4):
+                bp.d[i].n = half
+            ws = torch.empty(ifx.block_workspace_bytes(bp), dtype=torch.int8, device="cuda")
+            c3 = blk.convs[2]
+            ho, wo = c3.out_hw
+            y = model.empty_act(half, ho, wo, c3.spec.c_out)
+            ifx.block_forward(bp, t, y, ws)
+            torch.cuda.synchronize()
+            del ws, t
+            got = ifx.unpack_act(y[local].contiguous(), c3.spec.c_out).cpu().numpy()
+            np.testing.assert_array_equal(got, trace[1 + bi][mine], err_msg=f"block {bi}")
+            t = y
+        del t
+        torch.cuda.synchronize()
 
 
 @pytest.mark.parametrize("n", [1, 3])

@@ -326,6 +326,96 @@ def test_p12_net_batch_split_invariance(orc):
     assert full.dtype == np.int32 and full.shape == (3, 10)
 
 
+def _epilogue_rational(acc, cp, flags, res=None):
+    """The fused epilogue from its definition, element by element in exact rationals:
+    round_half_away((acc + bias) * mult / 2^(31 + shift)), + shortcut, ReLU, saturate."""
+    out = np.empty(acc.shape, np.int8)
+    oc = acc.shape[-1]
+    flat_acc = acc.reshape(-1, oc)
+    flat_res = None if res is None else res.reshape(-1, oc).astype(np.int64)
+    flat_out = out.reshape(-1, oc)
+    for i in range(flat_acc.shape[0]):
+        for o in range(oc):
+            y = int(flat_acc[i, o]) + int(cp.bias[o])
+            q = rha(Fraction(y * int(cp.mult[o]), 1 << (31 + int(cp.shift[o]))))
+            if flags & 2:
+                q += int(flat_res[i, o])
+            if flags & 1:
+                q = max(q, 0)
+            flat_out[i, o] = sat8(q)
+    return out
+
+
+def _torch_maxpool_f64(x_nhwc):
+    """Library special case: float64 max_pool2d (3x3, stride 2, pad 1; torch pads with -inf)."""
+    t = torch.from_numpy(x_nhwc.astype(np.float64)).permute(0, 3, 1, 2)
+    y = torch.nn.functional.max_pool2d(t, 3, 2, 1)
+    return y.permute(0, 2, 3, 1).numpy().astype(np.int8)
+
+
+def test_p12_net_equals_independent_composition(orc):
+    """net() against the network wired by hand from pieces pinned elsewhere or fixed by a
+    library: stem = float64 conv2d -> rational epilogue with ReLU -> float64 max_pool2d; each
+    bottleneck = float64 conv2d + rational epilogue for c1, c2, projection and c3 (+ shortcut,
+    ReLU); head = mean rounded half away from zero in Fraction, then an int64 matmul plus bias.
+    A dropped pool, a skipped block or a swapped head order fails here; every intermediate the
+    oracle reports through `trace` is compared too."""
+    from oracle.ref import BlockParams
+    rng = np.random.default_rng(1212)
+    stem = _rand_conv(rng, 3, 16, 7, 2, 3)
+    blocks = [BlockParams(_rand_conv(rng, 16, 8, 1, 1, 0), _rand_conv(rng, 8, 8, 3, 1, 1),
+                          _rand_conv(rng, 8, 32, 1, 1, 0), _rand_conv(rng, 16, 32, 1, 1, 0)),
+              BlockParams(_rand_conv(rng, 32, 8, 1, 1, 0), _rand_conv(rng, 8, 8, 3, 2, 1),
+                          _rand_conv(rng, 8, 64, 1, 1, 0), _rand_conv(rng, 32, 64, 1, 2, 0)),
+              BlockParams(_rand_conv(rng, 64, 16, 1, 1, 0), _rand_conv(rng, 16, 16, 3, 1, 1),
+                          _rand_conv(rng, 16, 64, 1, 1, 0), None)]
+    fw = rand_i8(rng, (10, 64), -127, 127)
+    fb = rng.integers(-(1 << 16), 1 << 16, size=10).astype(np.int32)
+    x = rand_i8(rng, (2, 30, 26, 3))
+    trace = []
+    logits = orc.net(x, stem, blocks, fw, fb, trace=trace)
+
+    exp_trace = []
+    t = _torch_maxpool_f64(_epilogue_rational(torch_conv_f64(x, stem.w, 2, 3), stem, 1))
+    exp_trace.append(t)
+    for bp in blocks:
+        t1 = _epilogue_rational(torch_conv_f64(t, bp.c1.w, 1, 0), bp.c1, 1)
+        t2 = _epilogue_rational(torch_conv_f64(t1, bp.c2.w, bp.c2.stride, 1), bp.c2, 1)
+        sc = t if bp.proj is None else _epilogue_rational(torch_conv_f64(t, bp.proj.w, bp.proj.stride, 0),
+                                                          bp.proj, 0)
+        t = _epilogue_rational(torch_conv_f64(t2, bp.c3.w, 1, 0), bp.c3, 3, sc)
+        exp_trace.append(t)
+    n, h, w, c = t.shape
+    pooled = np.empty((n, c), np.int8)
+    for b in range(n):
+        for ch in range(c):
+            pooled[b, ch] = rha(Fraction(int(t[b, :, :, ch].astype(np.int64).sum()), h * w))
+    exp_trace.append(pooled)
+    exp_logits = pooled.astype(np.int64) @ fw.astype(np.int64).T + fb.astype(np.int64)
+
+    assert len(trace) == len(exp_trace) == 2 + len(blocks)
+    for i, (got, exp) in enumerate(zip(trace, exp_trace)):
+        assert got.shape == exp.shape, i
+        np.testing.assert_array_equal(got, exp, err_msg=f"network stage {i}")
+    np.testing.assert_array_equal(logits.astype(np.int64), exp_logits)
+    # the example is not degenerate: pooling changes the size, values vary
+    assert trace[0].shape == (2, 8, 7, 16) and len(np.unique(logits)) > 10
+
+
+@pytest.mark.parametrize("flags", [1 | 4, 4])
+def test_p8_conv_fused_maxpool_branch(orc, flags):
+    """conv_fused with MAXPOOL is the 3x3/s2/p1 max-pool (torch float64, -inf padding) of the
+    same convolution without it, with and without ReLU, on odd and even output sizes."""
+    rng = np.random.default_rng(88 + flags)
+    for n, h, w, c, oc in [(2, 23, 18, 3, 8), (1, 16, 21, 4, 12)]:
+        x = rand_i8(rng, (n, h, w, c))
+        cp = _rand_conv(rng, c, oc, 7, 2, 3)
+        full = orc.conv_fused(x, cp.w, cp.bias, cp.mult, cp.shift, 2, 3, flags & 1)
+        pooled = orc.conv_fused(x, cp.w, cp.bias, cp.mult, cp.shift, 2, 3, flags)
+        np.testing.assert_array_equal(pooled, _torch_maxpool_f64(full))
+        assert pooled.shape[1] == (full.shape[1] - 1) // 2 + 1
+
+
 # ---------------------------------------------------------------- P13
 def test_p13_act_pack_roundtrip_and_layout(orc):
     rng = np.random.default_rng(14)
