@@ -366,25 +366,55 @@ ifx_status plan_net(const ifx_net_params *p, int n, NetPlan *plan)
 size_t lane_ws_bytes(const NetPlan &pl) { return 2 * pl.act + pl.t1 + pl.t2 + pl.sc + pl.pool + pl.part; }
 size_t net_ws_bytes(const NetPlan &pl) { return pl.lanes * lane_ws_bytes(pl); }
 
-// The library's second stream on the current device (non-blocking, default priority), created
-// on first use and kept for the process.
-hipError_t lane_stream(hipStream_t *out)
+// The second lane of a two-pass batch: a stream plus the events that fork it from the caller's
+// stream and join it back.
+struct Lane {
+    hipStream_t stream = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+
+hipError_t make_lane(Lane *l)
+{
+    hipError_t e = hipStreamCreateWithFlags(&l->stream, hipStreamNonBlocking);  // default priority
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&l->fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&l->join, hipEventDisableTiming);
+    return e;
+}
+
+void free_lane(Lane *l)
+{
+    if (l->fork) (void)hipEventDestroy(l->fork);
+    if (l->join) (void)hipEventDestroy(l->join);
+    if (l->stream) (void)hipStreamDestroy(l->stream);
+    *l = Lane();
+}
+
+// The library's lane on the current device, created on first use and kept for the process.
+// Callers hold lane_mutex() around the fork (record + wait) and around the join, so two host
+// threads never interleave on one event; their second-lane work is serialised on the stream.
+std::mutex &lane_mutex()
 {
     static std::mutex mu;
-    static std::vector<hipStream_t> streams;
+    return mu;
+}
+
+hipError_t device_lane(Lane *out)
+{
+    static std::vector<Lane> lanes;
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    std::lock_guard<std::mutex> lock(mu);
-    if ((size_t)dev >= streams.size()) streams.resize(dev + 1, nullptr);
-    if (!streams[dev]) {
-        e = hipStreamCreateWithFlags(&streams[dev], hipStreamNonBlocking);
+    if ((size_t)dev >= lanes.size()) lanes.resize(dev + 1);
+    if (!lanes[dev].stream) {
+        Lane l;
+        e = make_lane(&l);
         if (e != hipSuccess) {
-            streams[dev] = nullptr;
+            free_lane(&l);
             return e;
         }
+        lanes[dev] = l;
     }
-    *out = streams[dev];
+    *out = lanes[dev];
     return hipSuccess;
 }
 
@@ -541,11 +571,15 @@ size_t ifx_net_workspace_bytes(const ifx_net_params *p, int32_t n)
     return net_ws_bytes(plan);
 }
 
-ifx_status ifx_net_forward(const ifx_net_params *p, const int8_t *x_blk, int32_t *logits, int32_t n, void *ws,
-                           size_t ws_bytes, void *stream)
+}  // extern "C"
+
+namespace {
+
+// Validation of ifx_net_forward's arguments (nothing is launched).
+ifx_status check_net_call(const ifx_net_params *p, const int8_t *x_blk, const int32_t *logits, int32_t n,
+                          const void *ws, size_t ws_bytes, NetPlan *plan)
 {
-    NetPlan plan;
-    ifx_status st = plan_net(p, n, &plan);
+    ifx_status st = plan_net(p, n, plan);
     if (st != IFX_OK) return st;
     if (!x_blk || !logits || !ws || !p->stem_w || !p->stem_bias || !p->stem_mult || !p->stem_shift || !p->fc_w_blk ||
         !p->fc_bias)
@@ -558,26 +592,27 @@ ifx_status ifx_net_forward(const ifx_net_params *p, const int8_t *x_blk, int32_t
         st = check_block_ptrs(&p->blocks[i]);
         if (st != IFX_OK) return st;
     }
-    if (ws_bytes < net_ws_bytes(plan)) return IFX_E_WORKSPACE;
+    if (ws_bytes < net_ws_bytes(*plan)) return IFX_E_WORKSPACE;
+    return IFX_OK;
+}
 
+// The passes of a validated network call.  Pass i runs on lane i % plan.lanes: lane 0 is s0,
+// lane 1 is l1's stream, forked from s0 and joined back into it by l1's events.  `lock` (or
+// null) is held around the fork and around the join.
+ifx_status run_net(const ifx_net_params *p, const NetPlan &plan, const int8_t *x_blk, int32_t *logits, int32_t n,
+                   void *ws, hipStream_t s0, const Lane &l1, std::mutex *lock)
+{
     const size_t in_img = (p->stem.flags & IFX_INPUT_NHWC)
                               ? (size_t)p->stem.h * p->stem.w * p->stem.c_in
                               : act_bytes(1, p->stem.h, p->stem.w, p->stem.c_in);
-    // pass i runs on lane i % lanes: lane 0 is the caller's stream, lane 1 the library stream,
-    // forked from and joined back into the caller's stream by events
-    hipStream_t ls[2] = {(hipStream_t)stream, nullptr};
-    hipEvent_t fork = nullptr, join = nullptr;
+    hipStream_t ls[2] = {s0, l1.stream};
+    ifx_status st = IFX_OK;
     if (plan.lanes > 1) {
-        st = hip_status(lane_stream(&ls[1]));
-        if (st == IFX_OK) st = hip_status(hipEventCreateWithFlags(&fork, hipEventDisableTiming));
-        if (st == IFX_OK) st = hip_status(hipEventCreateWithFlags(&join, hipEventDisableTiming));
-        if (st == IFX_OK) st = hip_status(hipEventRecord(fork, ls[0]));
-        if (st == IFX_OK) st = hip_status(hipStreamWaitEvent(ls[1], fork, 0));
-        if (st != IFX_OK) {
-            if (fork) (void)hipEventDestroy(fork);
-            if (join) (void)hipEventDestroy(join);
-            return st;
-        }
+        std::unique_lock<std::mutex> g;
+        if (lock) g = std::unique_lock<std::mutex>(*lock);
+        st = hip_status(hipEventRecord(l1.fork, s0));
+        if (st == IFX_OK) st = hip_status(hipStreamWaitEvent(l1.stream, l1.fork, 0));
+        if (st != IFX_OK) return st;
     }
     int pass = 0;
     for (int i0 = 0; i0 < n && st == IFX_OK; i0 += plan.nb, ++pass) {
@@ -623,15 +658,43 @@ ifx_status ifx_net_forward(const ifx_net_params *p, const int8_t *x_blk, int32_t
         if (st != IFX_OK) break;
     }
     if (plan.lanes > 1) {
-        // the join is enqueued whatever happened above, so the caller's stream always follows
-        // every pass; the events can go once the wait is enqueued
-        ifx_status st2 = hip_status(hipEventRecord(join, ls[1]));
-        if (st2 == IFX_OK) st2 = hip_status(hipStreamWaitEvent(ls[0], join, 0));
-        (void)hipEventDestroy(fork);
-        (void)hipEventDestroy(join);
+        // the join is enqueued whatever happened above, so s0 always follows every pass
+        std::unique_lock<std::mutex> g;
+        if (lock) g = std::unique_lock<std::mutex>(*lock);
+        ifx_status st2 = hip_status(hipEventRecord(l1.join, l1.stream));
+        if (st2 == IFX_OK) st2 = hip_status(hipStreamWaitEvent(s0, l1.join, 0));
         if (st == IFX_OK) st = st2;
     }
     return st;
+}
+
+}  // namespace
+
+extern "C" {
+
+ifx_status ifx_net_forward(const ifx_net_params *p, const int8_t *x_blk, int32_t *logits, int32_t n, void *ws,
+                           size_t ws_bytes, void *stream)
+{
+    NetPlan plan;
+    ifx_status st = check_net_call(p, x_blk, logits, n, ws, ws_bytes, &plan);
+    if (st != IFX_OK) return st;
+    hipStream_t s0 = (hipStream_t)stream;
+    Lane l1;
+    if (plan.lanes > 1) {
+        // a stream being captured by the caller keeps every pass on itself: the library's lane
+        // is shared by every caller on the device and must not be pulled into a capture
+        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+        st = hip_status(hipStreamIsCapturing(s0, &cap));
+        if (st != IFX_OK) return st;
+        if (cap != hipStreamCaptureStatusNone) {
+            plan.lanes = 1;
+        } else {
+            std::lock_guard<std::mutex> g(lane_mutex());
+            st = hip_status(device_lane(&l1));
+            if (st != IFX_OK) return st;
+        }
+    }
+    return run_net(p, plan, x_blk, logits, n, ws, s0, l1, &lane_mutex());
 }
 
 // ---------------------------------------------------------------------------
@@ -649,32 +712,24 @@ ifx_status ifx_net_graph_create(const ifx_net_params *p, const int8_t *x_blk, in
     *out = nullptr;
     // validate every argument first: an invalid call records nothing
     NetPlan plan;
-    ifx_status st = plan_net(p, n, &plan);
+    ifx_status st = check_net_call(p, x_blk, logits, n, ws, ws_bytes, &plan);
     if (st != IFX_OK) return st;
-    if (!x_blk || !logits || !ws) return IFX_E_NULL;
-    if (ws_bytes < net_ws_bytes(plan)) return IFX_E_WORKSPACE;
-    // the library stream of a two-lane batch is created now, outside the capture
-    if (plan.lanes > 1) {
-        hipStream_t lane1 = nullptr;
-        st = hip_status(lane_stream(&lane1));
-        if (st != IFX_OK) return st;
-    }
-    // the stem and window-kernel launchers' one-time device queries happen now, outside the capture
-    st = hip_status(ifx::warm_stem_queries());
-    if (st == IFX_OK) st = hip_status(ifx::warm_halo_query());
-    if (st != IFX_OK) return st;
-
+    // the recording uses streams and events of its own, created outside the capture and
+    // destroyed after it: the recorded graph shares nothing with other callers' work
     hipStream_t cs = nullptr;
+    Lane l1;
     st = hip_status(hipStreamCreateWithFlags(&cs, hipStreamNonBlocking));  // default priority
-    if (st != IFX_OK) return st;
-    st = hip_status(hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal));
+    if (st == IFX_OK && plan.lanes > 1) st = hip_status(make_lane(&l1));
+    if (st == IFX_OK) st = hip_status(hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal));
     if (st != IFX_OK) {
-        (void)hipStreamDestroy(cs);
+        free_lane(&l1);
+        if (cs) (void)hipStreamDestroy(cs);
         return st;
     }
-    const ifx_status fst = ifx_net_forward(p, x_blk, logits, n, ws, ws_bytes, cs);
+    const ifx_status fst = run_net(p, plan, x_blk, logits, n, ws, cs, l1, nullptr);
     hipGraph_t graph = nullptr;
     st = hip_status(hipStreamEndCapture(cs, &graph));
+    free_lane(&l1);
     (void)hipStreamDestroy(cs);
     if (fst != IFX_OK || st != IFX_OK) {
         if (graph) (void)hipGraphDestroy(graph);

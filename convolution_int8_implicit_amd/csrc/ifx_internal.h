@@ -33,6 +33,18 @@ struct ConvArgs {
     int howo_shr, wo_shr, o2_shr;
 };
 
+// Compute units of the current device: a device property the runtime keeps on the host, so
+// reading it launches nothing and is safe while a stream is being captured.  The persistent
+// kernels size their grids from it and from their compile-time residency per CU.
+inline hipError_t current_cus(int *cus)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess && *cus < 1) *cus = 1;
+    return e;
+}
+
 // Magic multiplier and shift for q = floor(n / d), 0 <= n < 2^31, d >= 1:
 // with p = 31 + ceil(log2 d) and m = ceil(2^p / d), floor(n * m / 2^p) = floor(n / d)
 // (the classic round-up method for dividing by an invariant integer; m < 2^32).
@@ -71,8 +83,6 @@ struct FoldArgs {
     const float *w_scale, *conv_bias, *gamma, *beta, *mean, *var;
 };
 
-// One-time device query of the haloed-window 3x3 launcher (run before any stream capture).
-hipError_t warm_halo_query();
 hipError_t launch_conv(const ConvArgs &a, int kh, int kw, hipStream_t s);
 // Bytes of int32 partial sums launch_conv_split would use for `a` (0: it would not split).  A
 // convolution on few output tiles with a long reduction is split over workgroups along K.
@@ -84,8 +94,6 @@ hipError_t launch_conv_split(const ConvArgs &a, int kh, int kw, int32_t *part, s
 // `pj` (same output pixels and channels, no ReLU): the projection's requantised output is the
 // shortcut and never reaches HBM; a.res is not read.
 hipError_t launch_conv_proj(const ConvArgs &a, const ConvArgs &pj, hipStream_t s);
-// Run the stem launcher's one-time device query now (before a stream capture).
-hipError_t warm_stem_queries();
 hipError_t launch_fold_bn(const FoldArgs &f, int32_t *bias, int32_t *mult, int32_t *shift, int32_t *status,
                           hipStream_t s);
 // 1x1 convolutions with at most 128 input channels (conv1x1.hip)

@@ -680,29 +680,15 @@ bool conv3x3_halo_supported(const ConvArgs &a, int kh, int kw)
            !a.residual && !a.out_i32 && a.ksplit <= 1 && a.ho == a.h && a.wo == a.w;
 }
 
-// Persistent grid: as many eight-wave workgroups as fit on the chip, in groups of tiles_n (one per
-// 64-channel output tile), each group taking an equal contiguous run of bands.
-// Workgroups of the persistent kernel resident on the chip at once; queried once per process.
-hipError_t halo_slots(int *out)
-{
-    static int slots = 0;
-    if (slots == 0) {
-        int dev = 0, cus = 0, per_cu = 0;
-        hipError_t e = hipGetDevice(&dev);
-        if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-        if (e == hipSuccess)
-            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, conv3x3_halo_kernel<true>, 512, 0);
-        if (e != hipSuccess) return e;
-        slots = (per_cu < 1 ? 1 : per_cu) * cus;
-    }
-    *out = slots;
-    return hipSuccess;
-}
+// Persistent grid: one eight-wave workgroup per CU (its LDS leaves room for no second one), in
+// groups of tiles_n (one per 64-channel output tile), each group taking an equal contiguous run
+// of bands.
+static_assert(2 * kHaloLds > kLdsBytes, "one haloed-window workgroup per CU");
 
 hipError_t launch_conv3x3_halo(const ConvArgs &a, hipStream_t s)
 {
     int slots = 0;
-    hipError_t e = halo_slots(&slots);
+    hipError_t e = current_cus(&slots);
     if (e != hipSuccess) return e;
     const int bands = (a.h + kHaloTR - 1) / kHaloTR;
     const int tiles_n = (a.oc1 * 32 + 63) / 64;
@@ -724,12 +710,6 @@ hipError_t launch_conv3x3_halo(const ConvArgs &a, hipStream_t s)
 }
 
 }  // namespace
-
-hipError_t warm_halo_query()
-{
-    int slots = 0;
-    return halo_slots(&slots);
-}
 
 hipError_t launch_conv(const ConvArgs &a, int kh, int kw, hipStream_t s)
 {

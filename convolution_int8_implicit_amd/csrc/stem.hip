@@ -242,8 +242,12 @@ __device__ __forceinline__ void conv_tile(const StemArgs &a, const Tile &g, cons
     }
 }
 
+// Workgroups resident per CU: the register budget (at most 168 VGPRs, three waves per SIMD)
+// sets it; the launch bounds hold the compiler to it and the persistent grid is sized by it.
+constexpr int kStemPerCu = 3;
+
 template <int PATH>
-__global__ __launch_bounds__(kThreads) void stem_kernel(StemArgs a, int tiles, int per_xcd)
+__global__ __launch_bounds__(kThreads, kStemPerCu) void stem_kernel(StemArgs a, int tiles, int per_xcd)
 {
     __shared__ __attribute__((aligned(16))) int32_t sIn[kIT * kIT];      // 4 channel bytes per pixel
     __shared__ __attribute__((aligned(16))) int8_t sConv[kCPix * kOC];  // biased int8 conv outputs [px][ch]
@@ -335,31 +339,14 @@ __global__ __launch_bounds__(kThreads) void stem_kernel(StemArgs a, int tiles, i
     }
 }
 
-// Persistent grid size of a path: as many workgroups as fit on the chip at once (never
-// more, so none waits for another to finish); queried once per process.
-template <int PATH>
-hipError_t stem_grid(long long *g)
-{
-    static int per_cu = 0, cus = 0;
-    if (per_cu == 0) {
-        int dev = 0;
-        hipError_t e = hipGetDevice(&dev);
-        if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-        if (e == hipSuccess)
-            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, stem_kernel<PATH>, kThreads, 0);
-        if (e != hipSuccess) return e;
-        if (per_cu < 1) per_cu = 1;
-    }
-    *g = (long long)per_cu * cus;
-    return hipSuccess;
-}
-
 template <int PATH>
 hipError_t launch_path(const StemArgs &a, int tiles, hipStream_t s)
 {
-    long long g = 0;
-    hipError_t e = stem_grid<PATH>(&g);
+    // as many workgroups as the chip holds at once (never more, so none waits for another)
+    int cus = 0;
+    hipError_t e = current_cus(&cus);
     if (e != hipSuccess) return e;
+    long long g = (long long)kStemPerCu * cus;
     g = g / 8 * 8;  // a multiple of 8 so every XCD gets the same number
     if (g < 8) g = 8;
     const long long need = (tiles + 7LL) / 8 * 8;
@@ -370,15 +357,6 @@ hipError_t launch_path(const StemArgs &a, int tiles, hipStream_t s)
 }
 
 }  // namespace
-
-hipError_t warm_stem_queries()
-{
-    long long g;
-    hipError_t e = stem_grid<kPacked>(&g);
-    if (e == hipSuccess) e = stem_grid<kNhwc3>(&g);
-    if (e == hipSuccess) e = stem_grid<kNhwcAny>(&g);
-    return e;
-}
 
 hipError_t launch_stem(const StemArgs &a, hipStream_t s)
 {

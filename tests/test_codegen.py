@@ -32,3 +32,41 @@ def test_kernels_stay_in_registers(src, tmp_path):
     assert not re.search(r"^\s+scratch_(load|store)", asm, re.M), f"{src}: a kernel uses scratch memory"
     sizes = [int(v) for v in re.findall(r"\.private_segment_fixed_size:\s+(\d+)", asm)]
     assert sizes and max(sizes) == 0, f"{src}: private segment sizes {sizes}"
+
+
+def _kernel_resources(asm: str):
+    """{kernel symbol: {field: int}} from the code object metadata of a gfx950 assembly file."""
+    out = {}
+    for block in asm.split("  - .agpr_count:")[1:]:
+        block = ".agpr_count:" + block
+        name = re.search(r"\.name:\s+(\S+)", block)
+        if not name:
+            continue
+        fields = {}
+        for key in ("agpr_count", "vgpr_count", "group_segment_fixed_size", "max_flat_workgroup_size"):
+            m = re.search(rf"\.{key}:\s+(\d+)", block)
+            if m:
+                fields[key] = int(m.group(1))
+        out[name.group(1)] = fields
+    return out
+
+
+@pytest.mark.skipif(HIPCC is None, reason="hipcc not available")
+def test_stem_residency_fits(tmp_path):
+    """The stem's persistent grid assumes kStemPerCu workgroups per CU: their waves must fit the
+    512 registers of a SIMD lane and their LDS the CU's 160 KB."""
+    src = os.path.join(CSRC, "stem.hip")
+    per_cu = int(re.search(r"constexpr int kStemPerCu = (\d+);", open(src).read()).group(1))
+    out = tmp_path / "stem.s"
+    cmd = [HIPCC, "-O3", "-std=c++17", "--offload-arch=gfx950", "--cuda-device-only", "-S",
+           "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", src, "-o", str(out)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    res = {k: v for k, v in _kernel_resources(out.read_text()).items() if "stem_kernel" in k}
+    assert res, "no stem kernel found"
+    for name, f in res.items():
+        waves_per_simd = per_cu * f["max_flat_workgroup_size"] // 64 // 4
+        regs = f["vgpr_count"] + f.get("agpr_count", 0)
+        assert waves_per_simd * regs <= 512, (name, f)
+        assert per_cu * f["group_segment_fixed_size"] <= 160 * 1024, (name, f)
