@@ -23,7 +23,8 @@ import torch
 __all__ = [
     "RELU", "RESIDUAL", "MAXPOOL", "OUT_I32", "INPUT_NHWC", "IfxError", "ConvDesc", "BlockParams", "NetParams", "lib",
     "conv_desc", "conv_validate", "conv_out_dims", "act_bytes", "wpack_bytes", "pack_act", "unpack_act",
-    "pack_weights", "conv_fused", "block_workspace_bytes", "block_forward", "net_workspace_bytes",
+    "pack_weights", "conv_fused", "block_workspace_bytes", "block_forward", "block_forward_noalloc",
+    "BLOCK_SCRATCH_BYTES", "net_workspace_bytes",
     "net_forward", "NetGraph", "fold_bn", "BnFold", "status_string", "last_hip_error", "version", "LIB_PATH",
 ]
 
@@ -95,6 +96,7 @@ def lib() -> ctypes.CDLL:
         "ifx_conv_proj_fused": ([D, vp, vp, vp, vp, vp, D, vp, vp, vp, vp, vp, vp, vp], i32),
         "ifx_block_workspace_bytes": ([ctypes.POINTER(BlockParams)], sz),
         "ifx_block_forward": ([ctypes.POINTER(BlockParams), vp, vp, vp, sz, vp], i32),
+        "ifx_block_forward_noalloc": ([ctypes.POINTER(BlockParams), vp, vp, vp], i32),
         "ifx_net_workspace_bytes": ([ctypes.POINTER(NetParams), i32], sz),
         "ifx_net_forward": ([ctypes.POINTER(NetParams), vp, vp, i32, vp, sz, vp], i32),
         "ifx_fold_bn": ([ctypes.POINTER(BnFold), vp, vp, vp, vp, vp], i32),
@@ -215,6 +217,16 @@ def block_forward(p: BlockParams, x_blk, y_blk, ws: torch.Tensor, stream=None) -
     _dev(x_blk, y_blk, ws)
     _check(lib().ifx_block_forward(ctypes.byref(p), _ptr(x_blk), _ptr(y_blk), _ptr(ws), ws.numel() * ws.element_size(),
                                    _stream(stream)), "ifx_block_forward")
+
+
+# Bytes of the library-held scratch ifx_block_forward_noalloc uses (IFX_BLOCK_SCRATCH_BYTES).
+BLOCK_SCRATCH_BYTES = 64 << 20
+
+
+def block_forward_noalloc(p: BlockParams, x_blk, y_blk, stream=None) -> None:
+    _dev(x_blk, y_blk)
+    _check(lib().ifx_block_forward_noalloc(ctypes.byref(p), _ptr(x_blk), _ptr(y_blk), _stream(stream)),
+           "ifx_block_forward_noalloc")
 
 
 def net_workspace_bytes(p: NetParams, n: int) -> int:

@@ -309,6 +309,32 @@ struct NetPlan {
     int lanes;                     // passes in flight at once, each with its own workspace
 };
 
+// Library-held block workspace for callers that cannot allocate (ifx_block_forward_noalloc).
+// Each device holds its own copy for the life of the process.  In host code the name is a
+// host-side stand-in, never a device address: kernels get the address scratch_ptr() looked up.
+static __device__ __align__(256) int8_t scratch[IFX_BLOCK_SCRATCH_BYTES];
+
+// Device address of `scratch` on the current device, looked up once per device (with that
+// device current) and kept.
+hipError_t scratch_ptr(int8_t **out)
+{
+    static std::mutex mu;
+    static std::vector<int8_t *> ptrs;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> g(mu);
+    if ((size_t)dev >= ptrs.size()) ptrs.resize(dev + 1, nullptr);
+    if (!ptrs[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        ptrs[dev] = (int8_t *)p;
+    }
+    *out = ptrs[dev];
+    return hipSuccess;
+}
+
 // A whole batch of at least this many images (sub_batch 0) runs as two concurrent halves, one on
 // the caller's stream and one on a library stream: the last, partly filled round of tiles of
 // each launch then overlaps the other half's work.
@@ -562,6 +588,25 @@ ifx_status ifx_block_forward(const ifx_block_params *p, const int8_t *x_blk, int
     if (ws_bytes < plan.t1 + plan.t2 + plan.sc + plan.part) return IFX_E_WORKSPACE;
     int32_t *part = (int32_t *)((int8_t *)ws + plan.t1 + plan.t2 + plan.sc);
     return run_block(p, plan, p->d[0].n, x_blk, y_blk, (int8_t *)ws, part, plan.part, (hipStream_t)stream);
+}
+
+ifx_status ifx_block_forward_noalloc(const ifx_block_params *p, const int8_t *x_blk, int8_t *y_blk, void *stream)
+{
+    BlockPlan plan;
+    ifx_status st = plan_block(p, 0, &plan);
+    if (st != IFX_OK) return st;
+    st = check_block_ptrs(p);
+    if (st != IFX_OK) return st;
+    if (!x_blk || !y_blk) return IFX_E_NULL;
+    if (!aligned16(x_blk) || !aligned16(y_blk)) return IFX_E_ALIGN;
+    if (plan.t1 + plan.t2 + plan.sc + plan.part > (size_t)IFX_BLOCK_SCRATCH_BYTES) return IFX_E_WORKSPACE;
+    int8_t *ws = nullptr;
+    st = hip_status(scratch_ptr(&ws));
+    if (st != IFX_OK) return st;
+    // every byte the kernels read from the scratch (t1, t2, shortcut, split-K partial sums) is
+    // written earlier in the same call, so nothing needs clearing
+    int32_t *part = (int32_t *)(ws + plan.t1 + plan.t2 + plan.sc);
+    return run_block(p, plan, p->d[0].n, x_blk, y_blk, ws, part, plan.part, (hipStream_t)stream);
 }
 
 size_t ifx_net_workspace_bytes(const ifx_net_params *p, int32_t n)

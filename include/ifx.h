@@ -208,6 +208,25 @@ ifx_status ifx_block_forward(const ifx_block_params *p, const int8_t *x_blk, int
                              size_t ws_bytes, void *stream);
 
 /*
+ * ifx_block_forward for callers that cannot allocate device memory (code
+ * running under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same block, bit-identical results, with t1, t2, the
+ * projection shortcut and the split-K partial sums in a scratch array the
+ * library holds in device memory (IFX_BLOCK_SCRATCH_BYTES per device, for the
+ * life of the process) instead of a caller workspace.  The call allocates
+ * nothing.  A block whose ifx_block_workspace_bytes() exceeds
+ * IFX_BLOCK_SCRATCH_BYTES returns IFX_E_WORKSPACE and launches nothing.
+ * Every call on one device shares that device's scratch, which keeps the last
+ * call's contents (nothing in it has to start cleared): calls that overlap in
+ * time on one device, on any streams, race.  The first call on a device looks
+ * up the scratch's device address (host-side, no device work).
+ */
+#define IFX_BLOCK_SCRATCH_BYTES (64u << 20)
+
+ifx_status ifx_block_forward_noalloc(const ifx_block_params *p, const int8_t *x_blk, int8_t *y_blk,
+                                     void *stream);
+
+/*
  * ResNet-50-shaped network: stem (7x7/s2/p3 CONV+BN+RELU+MAXPOOL, DiDi IFX
  * blog) -> bottleneck blocks -> global average pool to int8 (round half away
  * from zero of the mean) -> FC with int32 logits = a . W^T + bias.
