@@ -1,277 +1,382 @@
 // Fused stem: 7x7 stride-2 pad-3 convolution over <= 4 input channels, folded
 // BN, ReLU and a 3x3 stride-2 pad-1 max-pool, in one kernel (the
 // CONV+BN+RELU+MAXPOOL single function of the DiDi IFX DAWNBench blog,
-// inference-optimisation section).  The pre-pool tensor never leaves LDS.
+// inference-optimisation section).  The pre-pool tensor never leaves the
+// registers.
 //
 // gfx950 design:
-//   * persistent 256-thread workgroups, each walking a list of 8x8 tiles of
-//     pooled pixels x 64 channels; the 64 filters stay in registers for the
-//     whole launch, and the next tile's input window is loaded into
-//     registers while the current tile computes;
-//   * per tile, the 17x17 convolution pixels under the pooling windows are
-//     computed (the one-pixel halo shared with neighbouring tiles is
-//     recomputed) from a 40x40-pixel input window staged in LDS as 4 bytes
-//     per pixel (the <= 4 channels, zero-filled), so one 16-byte MFMA operand
-//     is four consecutive kernel columns x four channels;
-//   * the window is read either from the packed NC/32HW32 tensor (first word
-//     of each 32-byte pixel vector) or straight from the compact NHWC image
-//     (aligned dword loads of three-byte pixels, unpacked with v_perm), which
-//     folds the input pack into the stem;
+//   * persistent 256-thread workgroups walk units of 8 pooled rows x 28
+//     pooled columns x 64 channels; the 64 filters stay in registers for the
+//     whole launch;
+//   * the v_mfma_i32_16x16x64_i8 operands are oriented so that a lane's
+//     results are 16 consecutive output channels of ONE convolution pixel:
+//     the filters are the A operand (rows = channels), the input patches the
+//     B operand (columns = 16 consecutive convolution columns of one row, a
+//     "strip"); each wave owns a strip and walks down the 17 convolution
+//     rows of the unit;
+//   * the max-pool runs on the int32 accumulators, before requantisation:
+//     the epilogue (bias, fixed-point scale with a non-negative multiplier,
+//     ReLU, saturation) is non-decreasing, so the maximum of the epilogues is
+//     the epilogue of the maximum.  Rows pool in registers (each odd
+//     convolution row serves two pooled rows), columns across neighbouring
+//     lanes of a 16-lane DPP row; only the pooled outputs are requantised,
+//     two pooled rows packed into one register set;
 //   * reduction order per output channel: (ky, kx, c) with 32 bytes per
 //     kernel row (column 7 and channel 3 are zero weights, row 7 a zero row):
-//     K = 256 = four v_mfma_i32_16x16x64_i8 steps;
-//   * each convolution pixel is requantised (bias, fixed-point scale, ReLU,
-//     saturation) as soon as its MFMAs finish and kept as a biased byte in
-//     LDS; the 3x3 max-pool runs on those bytes, exactly as the layer is
-//     defined, and writes whole 16-byte chunks of the packed output;
-//   * tiles are dealt out in contiguous runs per XCD, so the input rows two
-//     neighbouring tiles share are read through the same L2.
+//     K = 256 = four K-steps; the input window sits in LDS at 4 bytes per
+//     pixel, so a lane's 16 K-bytes are 4 consecutive pixels of one row;
+//   * the window of the next unit is fetched while the current one computes:
+//     the compact NHWC image (3 bytes per pixel) goes by buffer->LDS DMA into
+//     a staging area as whole row segments, and one pass spreads it to 4
+//     bytes per pixel with zeros outside the image (the input pack folded
+//     into the stem).  A packed NC/32HW32 input (first word of each pixel) or
+//     an NHWC image of other channel counts is gathered into the window at
+//     the start of its unit;
+//   * units are dealt out in contiguous runs per XCD, so the input rows two
+//     neighbouring units share are read through the same L2.
 #include "device_common.h"
 #include "ifx_internal.h"
 
 namespace ifx {
 namespace {
 
-typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v2i __attribute__((ext_vector_type(2)));
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kThreads = 256;
-constexpr int kPT = 8;                  // pooled tile edge
-constexpr int kCT = 2 * kPT + 1;        // convolution tile edge (17)
-constexpr int kCPix = kCT * kCT;        // 289 convolution pixels
-constexpr int kMT = (kCPix + 15) / 16;  // 19 MFMA row tiles
-constexpr int kIT = 2 * kCT + 6;        // 40 input rows/cols staged
+constexpr int kThreads = 256;               // four waves, one strip each
 constexpr int kOC = 64;
+constexpr int kPR = 8;                      // pooled rows per unit
+constexpr int kSP = 7;                      // pooled columns per strip (centres at odd lanes 1..13)
+constexpr int kStrips = 4;                  // strips per unit
+constexpr int kUnitPW = kStrips * kSP;      // 28 pooled columns per unit
+static_assert(kPR % 2 == 0, "pooled rows are requantised in pairs");
+constexpr int kCR = 2 * kPR + 1;            // convolution rows per unit (17)
+constexpr int kWR = 2 * (kCR - 1) + 8;      // window rows (40)
+constexpr int kWC = 128;                    // window columns, 4 bytes per pixel
+constexpr int kWPitch = kWC * 4;            // 512 bytes
+constexpr int kWinBytes = kWR * kWPitch;    // 20 KB
+// A staged raw row starts 16 pixels (48 bytes, three whole DMA chunks) before input column
+// 4 px0, so at the image's first row and column the chunks fall either wholly before the image
+// (read as zeros) or wholly inside it.  Window column wc is raw pixel wc + 9, i.e. raw byte
+// 3 wc + 27: the four window columns 4j .. 4j + 3 (one aligned 16-byte LDS word) come from raw
+// bytes 12j + 27 .. 12j + 38, inside the four dwords at 12j + 24.
+constexpr int kRawLead = 16;                // raw pixels before input column 4 px0
+constexpr int kRawChunks = 27;              // 16-byte DMA chunks per raw row (432 >= 12 * 31 + 40 bytes)
+constexpr int kRawPitch = 16 * kRawChunks;  // 432 bytes per raw row in the staging area
+constexpr int kRawDma = 5;                  // DMA instructions per wave per unit (4 waves x 5 x 64 >= 40 x 27)
+constexpr int kStageBytes = kRawDma * 4 * 1024;  // 20 KB: every lane of those instructions lands inside
+static_assert(kRawDma * 4 * 64 >= kWR * kRawChunks, "one DMA lane per raw chunk");
+static_assert(12 * (kWC / 4 - 1) + 40 <= kRawPitch, "the last window word's raw bytes fit the pitch");
+static_assert(3 * (kRawLead - 7) == 27, "window column wc is raw byte 3 wc + 27");
 
 // input paths
-constexpr int kPacked = 0;   // packed [n, 1, h, w, 32]
-constexpr int kNhwc3 = 1;    // compact NHWC, c == 3, w % 4 == 0: 12-byte groups of 4 pixels
+constexpr int kPacked = 0;   // packed [n, 1, h, w, 32]: the first word of each pixel
+constexpr int kNhwc3 = 1;    // compact NHWC, c == 3, w % 4 == 0: raw row segments by DMA
 constexpr int kNhwcAny = 2;  // compact NHWC, any c <= 4 and w: byte loads
 
-constexpr int kPkSlots = (kIT * kIT + kThreads - 1) / kThreads;      // 7 pixels per thread
-constexpr int kGroups = kIT / 4 + 1;                                // 11 groups cover a window row
-constexpr int kG3Slots = (kIT * kGroups + kThreads - 1) / kThreads;  // 2 groups per thread
-constexpr int kPre = 8;                                             // prefetch registers
-static_assert(kPkSlots <= kPre && 3 * kG3Slots <= kPre, "prefetch registers");
-
-struct Tile {
-    int b, py0, px0, cy0, cx0, iy0, ix0;
+// Unit geometry: pooled rows [py0, py0 + 8), pooled columns [px0, px0 + 28) of image b.
+// Convolution row r of the unit is y = 2 py0 - 1 + r; window row wr holds input row
+// 4 py0 - 5 + wr and window column wc input column 4 px0 - 7 + wc (odd, so every B fragment
+// starts on an 8-byte boundary); raw pixel p of a staging row is input column 4 px0 - 16 + p.
+struct Unit {
+    int b, py0, px0;
 };
 
-__device__ __forceinline__ Tile tile_geo(int t, int tiles_x, int tiles_y)
+__device__ __forceinline__ Unit unit_geo(int u, int bands, int halves)
 {
-    Tile g;
-    const int tx = t % tiles_x;
-    t /= tiles_x;
-    const int ty = t % tiles_y;
-    g.b = t / tiles_y;
-    g.py0 = ty * kPT;
-    g.px0 = tx * kPT;
-    g.cy0 = 2 * g.py0 - 1;  // first convolution pixel of the tile
-    g.cx0 = 2 * g.px0 - 1;
-    g.iy0 = 2 * g.cy0 - 3;  // first input pixel of the window
-    g.ix0 = 2 * g.cx0 - 3;
+    Unit g;
+    const int half = u % halves;
+    u /= halves;
+    g.px0 = half * kUnitPW;
+    g.py0 = (u % bands) * kPR;
+    g.b = u / bands;
     return g;
 }
 
-// Issue the loads of a tile's input window into registers.
-template <int PATH>
-__device__ __forceinline__ void fetch(const StemArgs &a, const Tile &g, unsigned (&pre)[kPre])
-{
-    const int tid = threadIdx.x;
-    if (PATH == kPacked) {
-        const int8_t *img = a.x + (long long)g.b * a.h * a.w * 32;
-#pragma unroll
-        for (int s = 0; s < kPkSlots; ++s) {
-            const int i = tid + s * kThreads;
-            const int ry = i / kIT, rx = i - (i / kIT) * kIT;
-            const int iy = g.iy0 + ry, ix = g.ix0 + rx;
-            unsigned v = 0;
-            if (i < kIT * kIT && (unsigned)iy < (unsigned)a.h && (unsigned)ix < (unsigned)a.w)
-                v = *(const unsigned *)(img + ((long long)iy * a.w + ix) * 32);
-            pre[s] = v;
-        }
-    } else if (PATH == kNhwc3) {
-        // ix0 = 4 px0 - 5 = 3 (mod 4): the groups of 4 pixels start at ix0 - 3
-        const int8_t *img = a.x + (long long)g.b * a.h * a.w * 3;
-#pragma unroll
-        for (int s = 0; s < kG3Slots; ++s) {
-            const int i = tid + s * kThreads;
-            const int ry = i / kGroups, gi = i - (i / kGroups) * kGroups;
-            const int iy = g.iy0 + ry, gx = g.ix0 - 3 + 4 * gi;
-            unsigned d0 = 0, d1 = 0, d2 = 0;
-            // w % 4 == 0 and gx % 4 == 0: a group lies wholly inside or outside the row
-            if (i < kIT * kGroups && (unsigned)iy < (unsigned)a.h && (unsigned)gx < (unsigned)a.w) {
-                const unsigned *src = (const unsigned *)(img + ((long long)iy * a.w + gx) * 3);
-                d0 = __builtin_nontemporal_load(src);
-                d1 = __builtin_nontemporal_load(src + 1);
-                d2 = __builtin_nontemporal_load(src + 2);
-            }
-            pre[3 * s] = d0;
-            pre[3 * s + 1] = d1;
-            pre[3 * s + 2] = d2;
-        }
-    }
-}
-
-// Write a tile's input window into LDS: sIn[ry][rx] = the channel bytes of
-// input pixel (iy0 + ry, ix0 + rx), zero outside the image.
-template <int PATH>
-__device__ __forceinline__ void put(const StemArgs &a, const Tile &g, const unsigned (&pre)[kPre], int32_t *sIn)
-{
-    const int tid = threadIdx.x;
-    if (PATH == kPacked) {
-#pragma unroll
-        for (int s = 0; s < kPkSlots; ++s) {
-            const int i = tid + s * kThreads;
-            if (i < kIT * kIT) sIn[i] = (int)pre[s];
-        }
-    } else if (PATH == kNhwc3) {
-#pragma unroll
-        for (int s = 0; s < kG3Slots; ++s) {
-            const int i = tid + s * kThreads;
-            if (i >= kIT * kGroups) continue;
-            const int ry = i / kGroups, gi = i - (i / kGroups) * kGroups;
-            const unsigned d0 = pre[3 * s], d1 = pre[3 * s + 1], d2 = pre[3 * s + 2];
-            unsigned p[4];
-            p[0] = __builtin_amdgcn_perm(d1, d0, 0x0c020100u);  // bytes 0..2
-            p[1] = __builtin_amdgcn_perm(d1, d0, 0x0c050403u);  // bytes 3..5
-            p[2] = __builtin_amdgcn_perm(d2, d1, 0x0c040302u);  // bytes 6..8
-            p[3] = __builtin_amdgcn_perm(d2, d2, 0x0c030201u);  // bytes 9..11
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int rx = 4 * gi + e - 3;  // window column of pixel e of the group
-                if ((unsigned)rx < (unsigned)kIT) sIn[ry * kIT + rx] = (int)p[e];
-            }
-        }
-    } else {
-        const int8_t *img = a.x + (long long)g.b * a.h * a.w * a.c;
-        for (int i = tid; i < kIT * kIT; i += kThreads) {
-            const int ry = i / kIT, rx = i - (i / kIT) * kIT;
-            const int iy = g.iy0 + ry, ix = g.ix0 + rx;
-            unsigned v = 0;
-            if ((unsigned)iy < (unsigned)a.h && (unsigned)ix < (unsigned)a.w) {
-                const unsigned char *src = (const unsigned char *)(img + ((long long)iy * a.w + ix) * a.c);
-                for (int ch = 0; ch < a.c; ++ch) v |= (unsigned)src[ch] << (8 * ch);
-            }
-            sIn[i] = (int)v;
-        }
-    }
-}
-
-// Packed 16-bit maxima: the pooled tile keeps int8 values biased to unsigned
-// (q + 128), so the 3x3 maximum runs on the even and odd bytes separately.
-__device__ __forceinline__ unsigned pkmax(unsigned x, unsigned y)
-{
-    const u16x2 r = __builtin_elementwise_max(__builtin_bit_cast(u16x2, x), __builtin_bit_cast(u16x2, y));
-    return __builtin_bit_cast(unsigned, r);
-}
-
-// Per-channel parameters in LDS, one int32 per channel each: bias, multiplier,
-// shift, and for shift >= 2 the rounding high word 2^(shift-2) and shift - 1.
+// Per-channel parameters in LDS.
 struct ChanParams {
     int bias[kOC], mul[kOC], shf[kOC], rnd[kOC], shm[kOC];
     int add_lo[kOC], add_hi[kOC];  // bias * mult + (rnd << 32): the bias folded into mode 1's constant
 };
 
-// Convolution of one tile into sConv (biased int8 [pixel][channel]).
-// MODE 0: general requant, ReLU if a.relu; 1: shift >= 2 with ReLU; 2: shift >= 2, no ReLU.
-template <int MODE>
-__device__ __forceinline__ void conv_tile(const StemArgs &a, const Tile &g, const int32_t *sIn, int8_t *sConv,
-                                          const v4i (&wf)[4][4], const ChanParams &P)
+// DMA the raw NHWC (3-byte) row segments of unit g into the staging area: chunk k (16 bytes)
+// of window row wr is lane idx = 27 wr + k of this workgroup's 20 instructions, which lands at
+// staging byte 16 idx = 432 wr + 16 k.
+__device__ __forceinline__ void issue_raw(const StemArgs &a, const Unit &g, int8_t *stage, int wave, int lane)
 {
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int c = lane & 15, grp = lane >> 4;
-    const int kh_off = grp >> 1;    // kernel row within a K step (two rows per step)
-    const bool interior = g.cy0 >= 0 && g.cx0 >= 0 && g.cy0 + kCT <= a.ho && g.cx0 + kCT <= a.wo;
-    const int kw0 = 4 * (grp & 1);  // first kernel column of this lane's 16 bytes
-    for (int tm = wave; tm < kMT; tm += 4) {
-        int q = 16 * tm + (lane & 15);
-        if (q >= kCPix) q = kCPix - 1;  // padding rows: any valid address, results dropped
-        const int ly = q / kCT, lx = q - (q / kCT) * kCT;
-        v4i acc[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
+    const long long img = (long long)a.h * a.w * 3;
+    const v4i rs = make_rsrc(a.x + (long long)g.b * img, img);
+    const int iy0 = 4 * g.py0 - 5, rx0 = 4 * g.px0 - kRawLead;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const v2i *src = (const v2i *)&sIn[(2 * ly + 2 * ks + kh_off) * kIT + 2 * lx + kw0];
-            const v2i lo = src[0], hi = src[1];
-            const v4i af = {lo.x, lo.y, hi.x, hi.y};
+    for (int q = 0; q < kRawDma; ++q) {
+        const int inst = q * 4 + wave;
+        const int idx = inst * 64 + lane;
+        const int wr = idx / kRawChunks, k = idx - wr * kRawChunks;
+        const int iy = iy0 + wr;
+        const long long off = ((long long)iy * a.w + rx0) * 3 + 16 * k;
+        const bool ok = wr < kWR && (unsigned)iy < (unsigned)a.h && off >= 0;
+        load16_lds_stream(rs, stage + inst * 1024, ok ? (unsigned)off : kOOB);
+    }
+}
+
+// Spread the staged raw rows into the window: 4 bytes per pixel (channel 3 = 0), zero outside
+// the image.  Thread item (wr, j) writes window columns 4j .. 4j + 3 as one 16-byte word.
+__device__ __forceinline__ void unpack_raw(const StemArgs &a, const Unit &g, const int8_t *stage, int8_t *win,
+                                           int tid)
+{
+    const int iy0 = 4 * g.py0 - 5, wx0 = 4 * g.px0 - 7;
+    for (int it = tid; it < kWR * (kWC / 4); it += kThreads) {
+        const int wr = it / (kWC / 4), j = it - wr * (kWC / 4);
+        const unsigned *src = (const unsigned *)(stage + wr * kRawPitch + 12 * j + 24);
+        const unsigned d0 = src[0], d1 = src[1], d2 = src[2], d3 = src[3];
+        // pixel k of the word starts at byte 3 + 3k of d0..d3
+        unsigned p[4];
+        p[0] = __builtin_amdgcn_perm(d1, d0, 0x0c050403u);  // d0[3], d1[0], d1[1]
+        p[1] = __builtin_amdgcn_perm(d2, d1, 0x0c040302u);  // d1[2], d1[3], d2[0]
+        p[2] = __builtin_amdgcn_perm(d2, d2, 0x0c030201u);  // d2[1], d2[2], d2[3]
+        p[3] = __builtin_amdgcn_perm(d3, d3, 0x0c020100u);  // d3[0], d3[1], d3[2]
+        const bool row_ok = (unsigned)(iy0 + wr) < (unsigned)a.h;
+        v4i w;
 #pragma unroll
-            for (int tn = 0; tn < 4; ++tn)
-                acc[tn] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, wf[tn][ks], acc[tn], 0, 0, 0);
+        for (int k = 0; k < 4; ++k) w[k] = (row_ok && (unsigned)(wx0 + 4 * j + k) < (unsigned)a.w) ? (int)p[k] : 0;
+        *(v4i *)(win + wr * kWPitch + 16 * j) = w;
+    }
+}
+
+// Fill the window of unit g directly (paths without a staging area); the caller waits.
+template <int PATH>
+__device__ __forceinline__ void gather_window(const StemArgs &a, const Unit &g, int8_t *win, int wave, int lane,
+                                              int tid)
+{
+    const int iy0 = 4 * g.py0 - 5, wx0 = 4 * g.px0 - 7;
+    if (PATH == kPacked) {
+        // one word per lane: window row wr, half hh covers columns [64 hh, 64 hh + 64)
+        const long long img = (long long)a.h * a.w * 32;
+        const v4i rs = make_rsrc(a.x + (long long)g.b * img, img);
+        for (int q = wave; q < 2 * kWR; q += 4) {
+            const int wr = q >> 1, wc = (q & 1) * 64 + lane;
+            const int iy = iy0 + wr, ix = wx0 + wc;
+            const bool ok = (unsigned)iy < (unsigned)a.h && (unsigned)ix < (unsigned)a.w;
+            ifx_raw_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)(win + q * 256), 4,
+                                    ok ? (unsigned)((iy * a.w + ix) * 32) : kOOB, 0, 0, 0);
         }
-        const v4i bias = *(const v4i *)&P.bias[4 * c];
-        const v4i mul = *(const v4i *)&P.mul[4 * c];
-        const v4i shf = *(const v4i *)&P.shf[4 * c];
-        const v4i rnd = *(const v4i *)&P.rnd[4 * c];
-        const v4i shm = *(const v4i *)&P.shm[4 * c];
-        const v4i alo = *(const v4i *)&P.add_lo[4 * c];
-        const v4i ahi = *(const v4i *)&P.add_hi[4 * c];
-        // only tiles at the image border (or the last, partial row tile) need per-pixel checks
-        const bool edge = !interior || tm == kMT - 1;
-        // lane (grp, c) holds conv pixels 16tm + 4grp + i, channels 4c + tn; pixels outside
-        // the convolution output are stored as 0 (= -128) so the max ignores them (every
-        // pooling window holds its centre pixel, which is inside)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int qq = 16 * tm + 4 * grp + i;
-            bool inside = true;
-            if (edge) {
-                const int qy = qq / kCT, qx = qq - (qq / kCT) * kCT;
-                inside = qq < kCPix && (unsigned)(g.cy0 + qy) < (unsigned)a.ho && (unsigned)(g.cx0 + qx) < (unsigned)a.wo;
+    } else {
+        const int8_t *img = a.x + (long long)g.b * a.h * a.w * a.c;
+        for (int i = tid; i < kWR * kWC; i += kThreads) {
+            const int wr = i / kWC, wc = i - wr * kWC;
+            const int iy = iy0 + wr, ix = wx0 + wc;
+            unsigned v = 0;
+            if ((unsigned)iy < (unsigned)a.h && (unsigned)ix < (unsigned)a.w) {
+                const unsigned char *src = (const unsigned char *)(img + ((long long)iy * a.w + ix) * a.c);
+                for (int ch = 0; ch < a.c; ++ch) v |= (unsigned)src[ch] << (8 * ch);
             }
-            int r[4];
-#pragma unroll
-            for (int tn = 0; tn < 4; ++tn) {
-                int v;
-                if (MODE == 0) {
-                    v = requant_any(acc[tn][i] + bias[tn], mul[tn], shf[tn]);
-                    if (a.relu) v = max(v, 0);
-                } else if (MODE == 1) {
-                    const long long add = (long long)(((unsigned long long)(unsigned)ahi[tn] << 32) | (unsigned)alo[tn]);
-                    v = max(((int)(((long long)acc[tn][i] * (long long)mul[tn] + add) >> 32)) >> shm[tn], 0);
-                } else {
-                    v = requant_fast(acc[tn][i] + bias[tn], mul[tn], rnd[tn], shm[tn]);
-                }
-                r[tn] = min(max(v, -128), 127);
-            }
-            const unsigned word = inside ? (pack4(r[0], r[1], r[2], r[3]) ^ 0x80808080u) : 0u;
-            if (!edge || qq < kCPix) *(unsigned *)&sConv[qq * kOC + 4 * c] = word;
+            ((unsigned *)win)[i] = v;
         }
     }
 }
 
-// Workgroups resident per CU: the register budget (at most 168 VGPRs, three waves per SIMD)
+constexpr int kIMin = (int)0x80000000;
+
+// Lane c of a 16-lane DPP row gets lane c - 1's value / lane c + 1's / lane c + 2's; a lane
+// without a source in its row gets 0 (lanes 0, 14 and 15, whose results are never stored).
+__device__ __forceinline__ int from_left(int v) { return __builtin_amdgcn_mov_dpp(v, 0x111, 0xf, 0xf, true); }
+__device__ __forceinline__ int from_right(int v) { return __builtin_amdgcn_mov_dpp(v, 0x101, 0xf, 0xf, true); }
+__device__ __forceinline__ int from_right2(int v) { return __builtin_amdgcn_mov_dpp(v, 0x102, 0xf, 0xf, true); }
+__device__ __forceinline__ int max3(int a, int b, int c) { return max(max(a, b), c); }
+// max(a, dpp(b)) then max(., dpp(b)) as two-operand maxima: the empty barrier keeps the compiler
+// from merging them into one three-input max, so each DPP move folds into its max (v_max_i32
+// with a DPP operand) instead of costing an instruction of its own
+__device__ __forceinline__ int max_lr(int v, int l, int r)
+{
+    int t = max(v, l);
+    asm volatile("" : "+v"(t));
+    return max(t, r);
+}
+
+// One convolution row of the wave's strip: acc[tn][i] = channel 16 (lane / 16) + 4 tn + i of
+// convolution column c = lane % 16.  wrow: the window bytes of the row's first K-step at this
+// lane's fragment offset.
+__device__ __forceinline__ void conv_row(const int8_t *wrow, const v4i (&wf)[4][4], v4i (&acc)[4])
+{
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        const v2i lo = *(const v2i *)(wrow + ks * 2 * kWPitch);
+        const v2i hi = *(const v2i *)(wrow + ks * 2 * kWPitch + 8);
+        const v4i bfrag = {lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+        for (int tn = 0; tn < 4; ++tn)
+            acc[tn] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[tn][ks], bfrag, ks == 0 ? (v4i){0, 0, 0, 0} : acc[tn], 0,
+                                                            0, 0);
+    }
+}
+
+// Requantise the 16 pooled accumulators of a lane (channels ch0 + 4 tn + i, held at m[tn][i])
+// and pack them into 16 output bytes.  MODE 0: general form (ReLU if relu); 1: shift >= 2 with
+// ReLU; 2: shift >= 2, no ReLU.
+template <int MODE>
+__device__ __forceinline__ v4i requant16(const v4i (&m)[4], const ChanParams &P, int ch0, bool relu)
+{
+    v4i out;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int ch = ch0 + 4 * k;
+        int r[4];
+        if (MODE == 1) {
+            const v4i mul = *(const v4i *)&P.mul[ch], shm = *(const v4i *)&P.shm[ch];
+            const v4i alo = *(const v4i *)&P.add_lo[ch], ahi = *(const v4i *)&P.add_hi[ch];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const long long add = (long long)(((unsigned long long)(unsigned)ahi[i] << 32) | (unsigned)alo[i]);
+                const int v = ((int)(((long long)m[k][i] * (long long)mul[i] + add) >> 32)) >> shm[i];
+                r[i] = min(max(v, 0), 127);
+            }
+        } else if (MODE == 2) {
+            const v4i bias = *(const v4i *)&P.bias[ch], mul = *(const v4i *)&P.mul[ch];
+            const v4i rnd = *(const v4i *)&P.rnd[ch], shm = *(const v4i *)&P.shm[ch];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                r[i] = min(max(requant_fast(m[k][i] + bias[i], mul[i], rnd[i], shm[i]), -128), 127);
+        } else {
+            const v4i bias = *(const v4i *)&P.bias[ch], mul = *(const v4i *)&P.mul[ch];
+            const v4i shf = *(const v4i *)&P.shf[ch];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                int v = requant_any(m[k][i] + bias[i], mul[i], shf[i]);
+                if (relu) v = max(v, 0);
+                r[i] = min(max(v, -128), 127);
+            }
+        }
+        out[k] = (int)pack4(r[0], r[1], r[2], r[3]);
+    }
+    return out;
+}
+
+// The wave's strip of unit g: 17 convolution rows, pooled rows in pairs.  Pooled row p is the
+// maximum over convolution rows 2p, 2p + 1, 2p + 2 and, per centre column, over its neighbours.
+// Rows and columns outside the convolution output are replaced by the nearest row or column
+// inside it, which belongs to the same pooling window, so the maximum is unchanged and no
+// masking is needed (a strip or row past the output reads in-window data that is never stored).
+//
+// Software pipeline: once the vertical maximum of pooled row p is taken, rows 2p and 2p + 1
+// are dead, and the matrix pipe computes convolution rows 2p + 3 and 2p + 4 into their
+// registers while the VALU finishes row p (the horizontal maximum, the requantisation).  Rows
+// live in three rotating register sets (row r in set r % 3); the band is unrolled so every set
+// index is a constant.
+template <int MODE>
+__device__ __forceinline__ void compute_unit(const StemArgs &a, const Unit &g, const int8_t *win,
+                                             const v4i (&wf)[4][4], const ChanParams &P, int wave, int lane)
+{
+    const int c = lane & 15, grp = lane >> 4;
+    const int xs = 2 * g.px0 - 1 + 14 * wave;  // convolution column of lane c = 0
+    const int x = max(min(max(xs + c, 0), a.wo - 1), xs);
+    // window bytes of this lane's B fragment for convolution row 0, K-step 0: window column
+    // 2 x - 3 + 4 (grp & 1) - (4 px0 - 7)
+    const int8_t *wl = win + (grp >> 1) * kWPitch + (2 * (x - xs) + 28 * wave + 4 * (grp & 1) + 2) * 4;
+    const int y0 = 2 * g.py0 - 1;
+    const int ymax = max(a.ho - 1, y0);
+    v4i R[3][4], vm[4];
+    auto row = [&](int r) __attribute__((always_inline)) {
+        const int re = min(max(y0 + r, 0), ymax) - y0;  // nearest row inside the output
+        conv_row(wl + re * 2 * kWPitch, wf, R[r % 3]);
+    };
+    auto vertical = [&](int p) __attribute__((always_inline)) {
+#pragma unroll
+        for (int tn = 0; tn < 4; ++tn)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                vm[tn][i] = max3(R[(2 * p) % 3][tn][i], R[(2 * p + 1) % 3][tn][i], R[(2 * p + 2) % 3][tn][i]);
+    };
+    v4i pm[4];
+    // pooled row p into pm: odd (centre) lanes of a first row of a pair keep their own 3-max;
+    // even lanes of a second row take the 3-max of the lane to their right (a centre column,
+    // moved one lane left)
+    auto pool = [&](int p) __attribute__((always_inline)) {
+#pragma unroll
+        for (int tn = 0; tn < 4; ++tn)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int v = vm[tn][i];
+                if ((p & 1) == 0) {
+                    pm[tn][i] = max_lr(v, from_left(v), from_right(v));
+                } else {
+                    // computed in every lane: a DPP read of a lane that the exec mask has switched
+                    // off returns the old value, and the compiler would otherwise compute it only
+                    // in the even lanes that use it (the volatile barrier keeps it out of any branch)
+                    int t = max_lr(v, from_right(v), from_right2(v));
+                    asm volatile("" : "+v"(t));
+                    pm[tn][i] = (c & 1) ? pm[tn][i] : t;
+                }
+            }
+    };
+    auto requant_store = [&](int pp) __attribute__((always_inline)) {
+        // the parameters are re-read from LDS each time (a fence keeps the compiler from
+        // hoisting all 64 of a lane's words out of the band)
+        asm volatile("" ::: "memory");
+        const v4i q = requant16<MODE>(pm, P, 16 * grp, a.relu != 0);
+        // before the unit's last store, this wave's memory operations are waited for: the next
+        // unit's raw rows (requested a whole unit of work ago) and the earlier stores.  Loads and
+        // stores share one counter whose order is not guaranteed between them, so this is a
+        // wait for zero; at the top of the next unit no store is left to wait for but this one.
+        if (pp == kPR / 2 - 1) wait_vmcnt<0>();
+        // odd lanes: pooled row 2pp, column (c - 1) / 2 of the strip; even lanes: row 2pp + 1,
+        // column c / 2
+        const int py = g.py0 + 2 * pp + ((c & 1) ? 0 : 1);
+        const int px = g.px0 + kSP * wave + (c >> 1);
+        if (c < 14 && py < a.ph && px < a.pw) {
+            int8_t *dst = a.y + ((((long long)g.b * 2 + (grp >> 1)) * a.ph + py) * a.pw + px) * 32 + 16 * (grp & 1);
+            store16_stream(dst, q);
+        }
+    };
+
+    row(0);
+    row(1);
+    row(2);
+#pragma unroll
+    for (int p = 0; p < kPR; ++p) {
+        // one scheduling region per pooled row: nothing is hoisted into the previous one, which
+        // would only cost registers
+        __builtin_amdgcn_sched_barrier(0);
+        vertical(p);
+        if (p + 1 < kPR) {
+            row(2 * p + 3);
+            row(2 * p + 4);
+        }
+        pool(p);
+        if (p & 1) requant_store(p >> 1);
+    }
+}
+
+// Workgroups resident per CU: the register budget (at most 256 VGPRs, two waves per SIMD)
 // sets it; the launch bounds hold the compiler to it and the persistent grid is sized by it.
-constexpr int kStemPerCu = 3;
+constexpr int kStemPerCu = 2;
 
 template <int PATH>
-__global__ __launch_bounds__(kThreads, kStemPerCu) void stem_kernel(StemArgs a, int tiles, int per_xcd)
+__global__ __launch_bounds__(kThreads, kStemPerCu) void stem_kernel(StemArgs a, int units, int per_xcd)
 {
-    __shared__ __attribute__((aligned(16))) int32_t sIn[kIT * kIT];      // 4 channel bytes per pixel
-    __shared__ __attribute__((aligned(16))) int8_t sConv[kCPix * kOC];  // biased int8 conv outputs [px][ch]
+    __shared__ __attribute__((aligned(1024))) int8_t sWin[kWinBytes];
+    __shared__ __attribute__((aligned(1024))) int8_t sStage[PATH == kNhwc3 ? kStageBytes : 16];
     __shared__ __attribute__((aligned(16))) ChanParams sP;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int tiles_x = (a.pw + kPT - 1) / kPT;
-    const int tiles_y = (a.ph + kPT - 1) / kPT;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int bands = (a.ph + kPR - 1) / kPR;
+    const int halves = (a.pw + kUnitPW - 1) / kUnitPW;
 
-    // tile list: XCD x = blockIdx % 8 owns tiles [x * per_xcd, (x + 1) * per_xcd); its
+    // unit list: XCD x = blockIdx % 8 owns units [x * per_xcd, (x + 1) * per_xcd); its
     // workgroups take them round robin
     const int xcd = blockIdx.x & 7;
     const int stride = gridDim.x >> 3;
-    const int t_end = min(tiles, (xcd + 1) * per_xcd);
-    int t = xcd * per_xcd + (int)(blockIdx.x >> 3);
-    if (t >= t_end) return;
+    const int u_end = min(units, (xcd + 1) * per_xcd);
+    int u = xcd * per_xcd + (int)(blockIdx.x >> 3);
+    if (u >= u_end) return;
 
-    // filters and per-channel parameters of this lane: MFMA column c of tile tn = channel 4c + tn
+    // filters: A operand of tile tn, K-step ks; MFMA row m = lane % 16 is output channel
+    // 16 (m / 4) + 4 tn + m % 4, so a lane's results are 16 consecutive channels
     const int c = lane & 15, grp = lane >> 4;
     v4i wf[4][4];
 #pragma unroll
     for (int tn = 0; tn < 4; ++tn) {
-        const int8_t *wp = a.wt + (4 * c + tn) * 256 + grp * 16;
+        const int8_t *wp = a.wt + (16 * (c >> 2) + 4 * tn + (c & 3)) * 256 + grp * 16;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) wf[tn][ks] = *(const v4i *)(wp + ks * 64);
     }
@@ -290,58 +395,42 @@ __global__ __launch_bounds__(kThreads, kStemPerCu) void stem_kernel(StemArgs a, 
     const bool fast = __all(a.shift[lane] >= 2);
     const int mode = !fast ? 0 : (a.relu ? 1 : 2);
 
-    unsigned pre[kPre];
-    Tile g = tile_geo(t, tiles_x, tiles_y);
-    fetch<PATH>(a, g, pre);
+    Unit g = unit_geo(u, bands, halves);
+    if (PATH == kNhwc3) {
+        issue_raw(a, g, sStage, wave, lane);
+        wait_vmcnt<0>();
+    }
     for (;;) {
-        // sIn is free: every wave's MFMA reads of the previous tile are behind the
-        // barrier before its pool; sConv is free once every wave passes this barrier,
-        // since each wave's pool reads come before it
-        put<PATH>(a, g, pre, sIn);
-        lds_barrier();
-        const int t_next = t + stride;
-        if (t_next < t_end) fetch<PATH>(a, tile_geo(t_next, tiles_x, tiles_y), pre);  // in flight during this tile
-        if (mode == 0)
-            conv_tile<0>(a, g, sIn, sConv, wf, sP);
-        else if (mode == 1)
-            conv_tile<1>(a, g, sIn, sConv, wf, sP);
-        else
-            conv_tile<2>(a, g, sIn, sConv, wf, sP);
-        lds_barrier();
-
-        // 3x3/s2 max-pool of the biased bytes: thread = pooled pixel x 16 channels
-        const int pp = tid >> 2;
-        const int cg = (tid & 3) * 16;
-        const int ply = pp / kPT, plx = pp - (pp / kPT) * kPT;
-        const int py = g.py0 + ply, px = g.px0 + plx;
-        if (py < a.ph && px < a.pw) {
-            unsigned ev[4] = {0u, 0u, 0u, 0u}, od[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-            for (int dy = 0; dy < 3; ++dy)
-#pragma unroll
-                for (int dx = 0; dx < 3; ++dx) {
-                    const v4i v = *(const v4i *)&sConv[((2 * ply + dy) * kCT + 2 * plx + dx) * kOC + cg];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        ev[j] = pkmax(ev[j], (unsigned)v[j] & 0x00ff00ffu);
-                        od[j] = pkmax(od[j], ((unsigned)v[j] >> 8) & 0x00ff00ffu);
-                    }
-                }
-            v4i mx;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) mx[j] = (int)((ev[j] | (od[j] << 8)) ^ 0x80808080u);
-            int8_t *dst = a.y + ((((long long)g.b * 2 + (cg >> 5)) * a.ph + py) * a.pw + px) * 32 + (cg & 31);
-            store16_stream(dst, mx);
+        // the previous unit's reads of the window are behind this barrier
+        if (PATH == kNhwc3) {
+            lds_barrier();  // every wave's raw DMAs have landed (each waited before its last store)
+            unpack_raw(a, g, sStage, sWin, tid);
+            lds_barrier();  // the window is complete and the staging area free
+        } else {
+            lds_barrier();
+            gather_window<PATH>(a, g, sWin, wave, lane, tid);
+            wait_vmcnt<0>();
+            lds_barrier();
         }
-        if (t_next >= t_end) break;
-        t = t_next;
-        g = tile_geo(t, tiles_x, tiles_y);
+        const int u_next = u + stride;
+        const Unit gn = unit_geo(u_next < u_end ? u_next : u, bands, halves);
+        if (PATH == kNhwc3 && u_next < u_end) issue_raw(a, gn, sStage, wave, lane);  // lands during this unit
+        if (mode == 0)
+            compute_unit<0>(a, g, sWin, wf, sP, wave, lane);
+        else if (mode == 1)
+            compute_unit<1>(a, g, sWin, wf, sP, wave, lane);
+        else
+            compute_unit<2>(a, g, sWin, wf, sP, wave, lane);
+        if (u_next >= u_end) break;
+        u = u_next;
+        g = gn;
     }
 }
 
 template <int PATH>
-hipError_t launch_path(const StemArgs &a, int tiles, hipStream_t s)
+hipError_t launch_path(const StemArgs &a, int units, hipStream_t s)
 {
+    if (answer_query("stem_kernel<%d>", PATH)) return hipSuccess;
     // as many workgroups as the chip holds at once (never more, so none waits for another)
     int cus = 0;
     hipError_t e = current_cus(&cus);
@@ -349,10 +438,10 @@ hipError_t launch_path(const StemArgs &a, int tiles, hipStream_t s)
     long long g = (long long)kStemPerCu * cus;
     g = g / 8 * 8;  // a multiple of 8 so every XCD gets the same number
     if (g < 8) g = 8;
-    const long long need = (tiles + 7LL) / 8 * 8;
+    const long long need = (units + 7LL) / 8 * 8;
     if (g > need) g = need;
-    const int per_xcd = (int)((tiles + 7LL) / 8);
-    hipLaunchKernelGGL(stem_kernel<PATH>, dim3((unsigned)g), dim3(kThreads), 0, s, a, tiles, per_xcd);
+    const int per_xcd = (int)((units + 7LL) / 8);
+    hipLaunchKernelGGL(stem_kernel<PATH>, dim3((unsigned)g), dim3(kThreads), 0, s, a, units, per_xcd);
     return hipGetLastError();
 }
 
@@ -360,12 +449,13 @@ hipError_t launch_path(const StemArgs &a, int tiles, hipStream_t s)
 
 hipError_t launch_stem(const StemArgs &a, hipStream_t s)
 {
-    const long long tiles = (long long)a.n * ((a.ph + kPT - 1) / kPT) * ((a.pw + kPT - 1) / kPT);
-    if (tiles <= 0) return hipSuccess;
-    if (tiles > 0x7ffffff0LL) return hipErrorInvalidConfiguration;
-    if (!a.nhwc) return launch_path<kPacked>(a, (int)tiles, s);
-    if (a.c == 3 && (a.w & 3) == 0) return launch_path<kNhwc3>(a, (int)tiles, s);
-    return launch_path<kNhwcAny>(a, (int)tiles, s);
+    const long long units = (long long)a.n * ((a.ph + kPR - 1) / kPR) * ((a.pw + kUnitPW - 1) / kUnitPW);
+    if (units <= 0) return hipSuccess;
+    if (units > 0x7ffffff0LL) return hipErrorInvalidConfiguration;
+    if ((long long)a.h * a.w * 32 >= 0x7fffffffLL) return hipErrorInvalidValue;  // per-image offsets
+    if (!a.nhwc) return launch_path<kPacked>(a, (int)units, s);
+    if (a.c == 3 && (a.w & 3) == 0) return launch_path<kNhwc3>(a, (int)units, s);
+    return launch_path<kNhwcAny>(a, (int)units, s);
 }
 
 }  // namespace ifx

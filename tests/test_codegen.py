@@ -70,3 +70,29 @@ def test_stem_residency_fits(tmp_path):
         regs = f["vgpr_count"] + f.get("agpr_count", 0)
         assert waves_per_simd * regs <= 512, (name, f)
         assert per_cu * f["group_segment_fixed_size"] <= 160 * 1024, (name, f)
+
+
+@pytest.mark.skipif(HIPCC is None, reason="hipcc not available")
+def test_stem_dpp_moves_run_in_every_lane(tmp_path):
+    """The stem pools across lanes with DPP moves.  A DPP read of a lane that the exec mask has
+    switched off returns the old value, so no DPP move may sit inside an exec-masked region."""
+    out = tmp_path / "stem.s"
+    cmd = [HIPCC, "-O3", "-std=c++17", "--offload-arch=gfx950", "--cuda-device-only", "-S",
+           "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", os.path.join(CSRC, "stem.hip"),
+           "-o", str(out)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    total = 0
+    for body in re.split(r"\n(?=_Z\S*stem_kernel\S*:)", out.read_text())[1:]:
+        body = body.split("s_endpgm")[0]
+        depth = 0
+        for line in body.split("\n"):
+            if "s_and_saveexec" in line:
+                depth += 1
+            elif re.search(r"s_or_b64\s+exec", line):
+                depth = max(0, depth - 1)
+            elif "_dpp" in line:
+                total += 1
+                assert depth == 0, f"DPP move under a partial exec mask: {line.strip()}"
+    assert total > 0
