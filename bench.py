@@ -31,33 +31,6 @@ RIDGE = PEAK_I8 / PEAK_HBM
 METRIC = "int8 TOPS + images/s (fused conv stack), % of int8 MFMA peak / HBM BW"
 
 
-def kernel_name(spec, nhwc_input=True, proj=None, w=None) -> str:
-    """The kernel template instance a conv layer dispatches to, spelled as rocprofv3
-    prints it (mirrors the library's host dispatch).  proj: the projection shortcut's
-    spec when `spec` is a conv3 fused with it (ifx_conv_proj_fused); w: the input width."""
-    if spec.k == 7:
-        return f"stem_kernel<{1 if nhwc_input else 0}>"
-    oc_pad = (spec.c_out + 31) // 32 * 32
-    bm, bn = (128, 128) if oc_pad > 64 else (256, 64)
-    res = "true" if spec.flags & 2 else "false"
-    relu = "true" if spec.flags & 1 else "false"
-    i1 = (spec.c_in + 31) // 32
-    if proj is not None and spec.k == 1 and spec.stride == 1 and i1 <= 4 and (proj.c_in + 31) // 32 <= 4:
-        # both contractions short: the small-K fused kernel, shortcut kept in registers
-        return f"conv1x1_proj_kernel<{bm}, {bn}, {((proj.c_in + 31) // 32 + 1) // 2}, {(i1 + 1) // 2}, {relu}>"
-    if spec.k == 3 and spec.stride == 1 and i1 <= 2 and w is not None and 48 <= w <= 62 and res == "false" \
-            and proj is None:
-        return f"conv3x3_halo_kernel<{relu}>"  # stride-1 3x3, <= 64 input channels: haloed window
-    if spec.k == 1 and spec.pad == 0 and i1 <= 4 and proj is None:
-        return f"conv1x1_kernel<{bm}, {bn}, {(i1 + 1) // 2}, {res}, {relu}>"
-    st = 2
-    if spec.k == 1 and oc_pad > 64 and res == "false":
-        bm, bn, st = 256, 128, 3  # wide 1x1 convolutions without a shortcut
-    if spec.k == 3 and spec.stride == 2 and oc_pad >= 256 and res == "false":
-        bm, bn = 128, 256  # strided 3x3 with >= 256 output channels
-    return f"igemm_kernel<{spec.k}, {spec.k}, {bm}, {bn}, {st}, {res}, {relu}, {'false' if proj is None else 'true'}>"
-
-
 # Sources each kernel family is built from: HBM traffic taken from counters is only
 # reported while these files are unchanged.
 KERNEL_SOURCES = {
@@ -189,6 +162,37 @@ def summarize_trace(trace_csv: str, stats_csv: str, out: str, workload: str, not
     print("\n".join(lines))
 
 
+def summarize_counters(csvs, out: str, workload: str, note: str):
+    """Per kernel instance, the average per dispatch of every counter in one or more rocprofv3
+    --pmc counter_collection.csv files.  For the network only the per-launch replays count (the
+    dispatches after the network's last average-pool dispatch); otherwise every dispatch."""
+    import csv
+    import re
+    from collections import defaultdict
+
+    per = defaultdict(lambda: defaultdict(list))
+    for path in csvs:
+        with open(path) as fh:
+            rows = list(csv.DictReader(fh))
+        last_pool = max((int(r["Dispatch_Id"]) for r in rows if "avgpool_kernel" in r["Kernel_Name"]), default=-1)
+        for r in rows:
+            m = re.search(r"((?:conv1x1_proj|conv1x1|conv3x3_halo|igemm|stem)_kernel<[^>]*>)", r["Kernel_Name"])
+            if m and int(r["Dispatch_Id"]) > last_pool:
+                per[m.group(1)][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    counters = sorted({c for k in per.values() for c in k})
+    lines = [f"# rocprofv3 counters per dispatch, workload {workload}", f"# {note}",
+             "# average over the dispatches of each kernel instance (per-launch replays only for the network)",
+             "# kernel | dispatches | " + " | ".join(counters)]
+    for k in sorted(per):
+        d = per[k]
+        nd = max(len(v) for v in d.values())
+        vals = [f"{sum(d[c]) / len(d[c]):.4g}" if d.get(c) else "-" for c in counters]
+        lines.append(f"{k} | {nd} | " + " | ".join(vals))
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def layer_work(spec, n, h, w):
     """(ops, algorithmic bytes, output h, w) of one conv at batch n on an h x w input.
     ops = 2 per real MAC; bytes = each distinct tensor crossing HBM once: real input
@@ -221,6 +225,28 @@ def net_layers(net, n):
         out.append((b.c3, n, h2, h2))
         h = w = h2
     return out
+
+
+def net_kernel_names(net_spec, nb: int, nhwc: bool = True) -> list:
+    """The kernel instance of every conv launch of the network at pass size nb, in order, as the
+    library reports it (host-only query: ifx_conv_kernel_name / ifx_conv_proj_kernel_name)."""
+    import convolution_int8_implicit_amd as ifx
+
+    def desc(spec, h, w, extra=0):
+        return ifx.conv_desc(nb, h, w, spec.c_in, spec.c_out, spec.k, spec.k, spec.stride, spec.pad,
+                             spec.flags | extra)
+    names = [ifx.conv_kernel_name(desc(net_spec.stem, 224, 224, ifx.INPUT_NHWC if nhwc else 0))]
+    h = w = 56
+    for b in net_spec.blocks:
+        h2 = (h + 2 - 3) // b.c2.stride + 1
+        names.append(ifx.conv_kernel_name(desc(b.c1, h, w)))
+        names.append(ifx.conv_kernel_name(desc(b.c2, h, w)))
+        if b.proj is not None:
+            names.append(ifx.conv_kernel_name(desc(b.c3, h2, h2), desc(b.proj, h, w)))
+        else:
+            names.append(ifx.conv_kernel_name(desc(b.c3, h2, h2)))
+        h = w = h2
+    return names
 
 
 def cpu_baseline(workload: str, budget_s: float = 20.0):
@@ -278,6 +304,159 @@ def cpu_baseline(workload: str, budget_s: float = 20.0):
                       f"{tk:.1f} s, {k * per_img_ops / tk / 1e9:.2f} GOPS int8"}
 
 
+WORKLOAD_INDEX = {"conv1x1_b1": 0, "conv1x1": 1, "block": 2, "stem": 3, "net": 4}
+
+
+def setup(workload: str, stream, sub_batch: int, packed_input: bool = False):
+    """Device buffers and the step of one workload (untimed).  Returns a dict with the step
+    callable, the batch, the total ops and algorithmic bytes of a step, the conv layers
+    [(spec, n, h, w)], the config description and what the per-launch replay needs."""
+    import torch
+
+    import convolution_int8_implicit_amd as ifx
+    from convolution_int8_implicit_amd import model, synth
+
+    w = {}
+    if workload in ("net", "net26_b1"):
+        wl = synth.workload(4) if workload == "net" else synth.latency_workload(1)
+        n = wl.n
+        net = model.DeviceNet(wl.net, wl.index, sub_batch=sub_batch, nhwc_input=not packed_input)
+        x_nhwc = synth.input_tensor(wl, device="cuda")
+        ws = torch.empty(net.workspace_bytes(n), dtype=torch.int8, device="cuda")
+        logits = torch.empty((n, wl.net.fc_out), dtype=torch.int32, device="cuda")
+        if packed_input:
+            x_blk = model.empty_act(n, 224, 224, 3)
+
+            def step():
+                ifx.pack_act(x_nhwc, out=x_blk, stream=stream)
+                net.forward(x_blk, logits, n, ws, stream)
+        elif workload == "net26_b1":
+            x_blk = x_nhwc
+            graph = net.graph(x_nhwc, logits, n, ws)
+            w["eager"] = lambda: net.forward(x_nhwc, logits, n, ws, stream)
+
+            def step():
+                graph.launch(stream)
+        else:
+            x_blk = x_nhwc
+
+            def step():
+                net.forward(x_nhwc, logits, n, ws, stream)
+        layers = net_layers(wl.net, n)
+        ops = sum(layer_work(sp, nn, h, ww)[0] for sp, nn, h, ww in layers) + 2 * n * wl.net.fc_in * wl.net.fc_out
+        config = {"workload": wl.name, "batch": n, "image": "224x224x3 int8 NHWC",
+                  "convs": 1 + sum(3 + (b.proj is not None) for b in wl.net.blocks),
+                  "head": "avgpool + FC 2048->1000 int32 logits", "sub_batch": sub_batch,
+                  "step": ("input pack + " if packed_input else "") +
+                  ("ifx_graph_launch of the recorded ifx_net_forward" if workload == "net26_b1"
+                   else "ifx_net_forward")}
+        w.update(net=net, x_blk=x_blk, wl=wl)
+    else:
+        wl = synth.workload(WORKLOAD_INDEX[workload])
+        n = wl.n
+        dcs = [model.device_conv(s_, wl.index, n, wl.h, wl.w) if i == 0 else None for i, s_ in enumerate(wl.convs)]
+        if wl.convs[0].k == 7 and not packed_input:
+            dcs[0].desc.flags |= ifx.INPUT_NHWC
+            x_blk = synth.input_tensor(wl, device="cuda")
+        else:
+            x_blk = ifx.pack_act(synth.input_tensor(wl, device="cuda"))
+        if wl.kind == "block":
+            dcs = [model.device_conv(s_, wl.index, n, 28, 28) for s_ in wl.convs]
+            blk = model.DeviceBlock(dcs, None)
+            ws = torch.empty(blk.workspace_bytes(), dtype=torch.int8, device="cuda")
+            y = model.empty_act(n, 28, 28, 512)
+
+            def step():
+                blk.forward(x_blk, y, ws, stream)
+            layers = [(s_, n, 28, 28) for s_ in wl.convs]
+        else:
+            spec = wl.convs[0]
+            ho, wo = spec.out_hw(wl.h, wl.w)
+            y = model.empty_act(n, ho, wo, spec.c_out)
+            res = ifx.pack_act(synth.residual_tensor(wl, device="cuda")) if spec.flags & 2 else None
+
+            def step():
+                dcs[0].run(x_blk, y, res, stream)
+            layers = [(spec, n, wl.h, wl.w)]
+        ops = sum(layer_work(s_, nn, h, ww)[0] for s_, nn, h, ww in layers)
+        config = {"workload": wl.name, "batch": n}
+        w.update(dcs=dcs, x_blk=x_blk, y=y, wl=wl)
+    byts = sum(layer_work(s_, nn, h, ww)[1] for s_, nn, h, ww in layers)
+    floor = sum(max(o / PEAK_I8, b / PEAK_HBM) for o, b in (layer_work(s_, nn, h, ww)[:2] for s_, nn, h, ww in layers))
+    w.update(step=step, n=n, ops=ops, bytes=byts, floor_s=floor, layers=layers, config=config)
+    return w
+
+
+def time_steps(step, stream, steps: int, warmup: int) -> float:
+    """Seconds per step: `warmup` untimed steps, then `steps` bracketed by HIP events on `stream`."""
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return max(e0.elapsed_time(e1) * 1e-3, 0.0) / steps
+
+
+def config_line(w: dict, t: float) -> dict:
+    """A config's timing against its rooflines: algorithmic bytes and real ops per second, and the
+    per-conv floor (sum over its convolutions of max(ops/peak, bytes/HBM BW)) over the time."""
+    return {"us": round(t * 1e6, 2), "images_per_s": round(w["n"] / t, 1), "tops": round(w["ops"] / t / 1e12, 2),
+            "alg_gbps": round(w["bytes"] / t / 1e9, 1), "frac_hbm": round(w["bytes"] / t / PEAK_HBM, 4),
+            "frac_int8_peak": round(w["ops"] / t / PEAK_I8, 4), "floor_us": round(w["floor_s"] * 1e6, 2),
+            "floor_frac": round(w["floor_s"] / t, 4)}
+
+
+def extra_configs(stream, steps: int, warmup: int, skip: str) -> dict:
+    """Every other workload timed in the same run (the headline one excluded)."""
+    import gc
+
+    import torch
+    out = {}
+    for name in ("conv1x1_b1", "conv1x1", "block", "stem", "net26_b1"):
+        if name == skip:
+            continue
+        w = setup(name, stream, 0)
+        t = time_steps(w["step"], stream, steps, warmup)
+        line = {"workload": w["config"]["workload"], **config_line(w, t)}
+        if name == "net26_b1":
+            line["eager_us"] = round(time_steps(w["eager"], stream, steps, 1) * 1e6, 2)
+        out[name] = line
+        del w
+        gc.collect()
+        torch.cuda.empty_cache()
+    return out
+
+
+def ceilings(stream) -> dict:
+    """Practical ceilings of this device from the library's probes (ifx_probe.h): a 1 GiB
+    non-temporal streaming copy (2 GiB through HBM) and an int8 MFMA loop on registers."""
+    import torch
+
+    import convolution_int8_implicit_amd as ifx
+    nbytes = 1 << 30
+    src = torch.ones(nbytes, dtype=torch.int8, device="cuda")
+    dst = torch.empty_like(src)
+    t_copy = time_steps(lambda: ifx.probe_copy(src, dst, stream), stream, 10, 2)
+    del src, dst
+    props = torch.cuda.get_device_properties(0)
+    blocks = 4 * props.multi_processor_count
+    out = torch.empty(4 * blocks, dtype=torch.int32, device="cuda")
+    ops = [0]
+
+    def mfma():
+        ops[0] = ifx.probe_mfma_i8(out, blocks, 4096, stream)
+    t_mfma = time_steps(mfma, stream, 10, 2)
+    return {"copy_gbps": round(2 * nbytes / t_copy / 1e9, 1), "copy_frac_hbm": round(2 * nbytes / t_copy / PEAK_HBM, 4),
+            "mfma_i8_tops": round(ops[0] / t_mfma / 1e12, 1), "mfma_frac_peak": round(ops[0] / t_mfma / PEAK_I8, 4),
+            "note": "copy: 1 GiB read + 1 GiB written by 16-byte non-temporal vector loads/stores; "
+                    f"mfma: {blocks} workgroups x 4 waves x a 4x4 tile of independent v_mfma_i32_16x16x64_i8 chains"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -287,12 +466,16 @@ def main():
                     choices=["net", "net26_b1", "conv1x1", "conv1x1_b1", "block", "stem"])
     ap.add_argument("--sub-batch", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the other workloads and the ceiling probes")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the run, copy this many MiB with a plain elementwise kernel (counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/hbm_traffic_<workload>.txt from two counter runs and exit")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_CSV", "STATS_CSV"),
                     help="write profiles/kernel_stats_<workload>.txt from a --kernel-trace --stats run and exit")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="CSV",
+                    help="write profiles/<--counters-name>.txt from rocprofv3 --pmc runs and exit")
+    ap.add_argument("--counters-name", default=None, help="file name (without .txt) for --summarize-counters")
     ap.add_argument("--note", default="", help="command lines recorded in the --summarize-* output")
     ap.add_argument("--packed-input", action="store_true",
                     help="feed the stem a packed NC/32HW32 input made by a separate pack kernel in the step")
@@ -300,6 +483,11 @@ def main():
     if args.summarize_trace:
         summarize_trace(args.summarize_trace[0], args.summarize_trace[1],
                         os.path.join(ROOT, "profiles", f"kernel_stats_{args.workload}.txt"), args.workload, args.note)
+        return
+    if args.summarize_counters:
+        name = args.counters_name or f"counters_{args.workload}"
+        summarize_counters(args.summarize_counters, os.path.join(ROOT, "profiles", f"{name}.txt"), args.workload,
+                           args.note)
         return
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.copy_calibration_mib << 20,
@@ -313,7 +501,7 @@ def main():
     import torch
 
     import convolution_int8_implicit_amd as ifx
-    from convolution_int8_implicit_amd import model, synth
+    from convolution_int8_implicit_amd import model
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
@@ -322,134 +510,60 @@ def main():
     sub_batch = model.DEFAULT_SUB_BATCH if args.sub_batch is None else args.sub_batch
 
     # ---------------- workload setup (untimed) ----------------
-    if args.workload in ("net", "net26_b1"):
-        wl = synth.workload(4) if args.workload == "net" else synth.latency_workload(1)
-        n = wl.n
-        net = model.DeviceNet(wl.net, wl.index, sub_batch=sub_batch, nhwc_input=not args.packed_input)
-        x_nhwc = synth.input_tensor(wl, device="cuda")
-        ws = torch.empty(net.workspace_bytes(n), dtype=torch.int8, device="cuda")
-        logits = torch.empty((n, wl.net.fc_out), dtype=torch.int32, device="cuda")
-        if args.packed_input:
-            x_blk = model.empty_act(n, 224, 224, 3)
-
-            def step():
-                ifx.pack_act(x_nhwc, out=x_blk, stream=stream)
-                net.forward(x_blk, logits, n, ws, stream)
-        elif args.workload == "net26_b1":
-            x_blk = x_nhwc
-            net.forward(x_nhwc, logits, n, ws, stream)  # eager once: one-time device queries
-            graph = net.graph(x_nhwc, logits, n, ws)
-
-            def step():
-                graph.launch(stream)
-        else:
-            x_blk = x_nhwc
-
-            def step():
-                net.forward(x_nhwc, logits, n, ws, stream)
-        layers = net_layers(wl.net, n)
-        total_ops = sum(layer_work(s, nn, h, w)[0] for s, nn, h, w in layers) + 2 * n * wl.net.fc_in * wl.net.fc_out
-        config = {"workload": wl.name, "batch": n, "image": "224x224x3 int8 NHWC",
-                  "convs": 1 + sum(3 + (b.proj is not None) for b in wl.net.blocks),
-                  "head": "avgpool + FC 2048->1000 int32 logits", "sub_batch": sub_batch,
-                  "step": ("input pack + " if args.packed_input else "") +
-                  ("ifx_graph_launch of the recorded ifx_net_forward" if args.workload == "net26_b1"
-                   else "ifx_net_forward")}
-    else:
-        idx = {"conv1x1": 1, "conv1x1_b1": 0, "block": 2, "stem": 3}[args.workload]
-        wl = synth.workload(idx)
-        n = wl.n
-        dcs = [model.device_conv(s, wl.index, n, wl.h, wl.w) if i == 0 else None for i, s in enumerate(wl.convs)]
-        x_blk = ifx.pack_act(synth.input_tensor(wl, device="cuda"))
-        if wl.convs[0].k == 7 and not args.packed_input:
-            dcs[0].desc.flags |= ifx.INPUT_NHWC
-            x_blk = synth.input_tensor(wl, device="cuda")
-        if wl.kind == "block":
-            dcs = [model.device_conv(s, wl.index, n, 28, 28) for s in wl.convs]
-            blk = model.DeviceBlock(dcs, None)
-            ws = torch.empty(blk.workspace_bytes(), dtype=torch.int8, device="cuda")
-            y = model.empty_act(n, 28, 28, 512)
-
-            def step():
-                blk.forward(x_blk, y, ws, stream)
-            layers = [(s, n, 28, 28) for s in wl.convs]
-        else:
-            spec = wl.convs[0]
-            ho, wo = spec.out_hw(wl.h, wl.w)
-            y = model.empty_act(n, ho, wo, spec.c_out)
-            res = ifx.pack_act(synth.residual_tensor(wl, device="cuda")) if spec.flags & 2 else None
-
-            def step():
-                dcs[0].run(x_blk, y, res, stream)
-            layers = [(spec, n, wl.h, wl.w)]
-        total_ops = sum(layer_work(s, nn, h, w)[0] for s, nn, h, w in layers)
-        config = {"workload": wl.name, "batch": n}
+    w = setup(args.workload, stream, sub_batch, args.packed_input)
+    n, wl, x_blk = w["n"], w["wl"], w["x_blk"]
 
     # ---------------- timed region ----------------
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    sec_per_step = max(ev0.elapsed_time(ev1) * 1e-3, 0.0) / args.steps
+    sec_per_step = time_steps(w["step"], stream, args.steps, args.warmup)
     extra = {}
     if args.workload == "net26_b1":
         # the same forward launched kernel by kernel from the host, for comparison
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(args.steps):
-            net.forward(x_nhwc, logits, n, ws, stream)
-        e1.record(stream)
-        torch.cuda.synchronize()
         extra = {"latency_us": round(sec_per_step * 1e6, 1),
-                 "eager_latency_us": round(e0.elapsed_time(e1) * 1e3 / args.steps, 1)}
+                 "eager_latency_us": round(time_steps(w["eager"], stream, args.steps, 1) * 1e6, 1)}
     img_s = n / sec_per_step
-    tops = total_ops / sec_per_step / 1e12
+    tops = w["ops"] / sec_per_step / 1e12
 
     # ---------------- per-kernel durations (HIP events on the launch stream) ----------------
     # The convolutions of a step are replayed one launch at a time through ifx_conv_fused on
     # the same stream and the same data flow as the drivers (real activations), each launch
-    # bracketed by HIP events; durations are grouped by kernel instance.
+    # bracketed by HIP events; durations are grouped by the kernel instance the library reports
+    # for each launch (ifx_conv_kernel_name: the launch's own dispatch code, run without launching).
     def with_batch(dc, nb):
         d = ifx.ConvDesc.from_buffer_copy(dc.desc)
         d.n = nb
         return model.DeviceConv(dc.spec, d, dc.w_blk, dc.bias, dc.mult, dc.shift, dc.out_hw)
 
-    launches = []  # (kernel instance, ops, algorithmic bytes, fn); fn only, for bookkeeping steps
-    nhwc = not args.packed_input
+    launches = []  # (kernel instance, ops, algorithmic bytes, fn); name None: bookkeeping only
 
-    def conv_launch(spec, nb_, h, w, fn):
-        ops, byts, _, _ = layer_work(spec, nb_, h, w)
-        return (kernel_name(spec, nhwc, w=w), ops, byts, fn)
+    def conv_launch(dc, spec, nb_, h, w_, fn):
+        ops, byts, _, _ = layer_work(spec, nb_, h, w_)
+        return (ifx.conv_kernel_name(dc.desc), ops, byts, fn)
 
-    def proj_launch(c3spec, pspec, nb_, h3, w3, hp, wp, fn):
+    def proj_launch(c3, pj, c3spec, pspec, nb_, h3, w3, hp, wp, fn):
         # conv3 + projection in one kernel: both contractions; the shortcut is not a tensor
         o3, b3, oh, ow = layer_work(c3spec, nb_, h3, w3)
         op, bp, _, _ = layer_work(pspec, nb_, hp, wp)
         shortcut = nb_ * oh * ow * c3spec.c_out
-        return (kernel_name(c3spec, nhwc, proj=pspec), o3 + op, b3 + bp - 2 * shortcut, fn)
+        return (ifx.conv_kernel_name(c3.desc, pj.desc), o3 + op, b3 + bp - 2 * shortcut, fn)
 
+    head_floor = 0.0
     if args.workload in ("net", "net26_b1"):
+        net = w["net"]
         # the forward's passes: a whole batch of >= 192 images runs as two concurrent halves
         if sub_batch == 0 and n >= 192:
             nb = (n + 1) // 2
         else:
             nb = sub_batch if 0 < sub_batch < n else n
         passes = (n + nb - 1) // nb
-        big = max(ifx.act_bytes(nb, h, w, s.c_out if s.k != 7 else 64) for s, _, h, w in layers)
+        layers = w["layers"]
+        big = max(ifx.act_bytes(nb, h, ww, s_.c_out if s_.k != 7 else 64) for s_, _, h, ww in layers)
         big = max(big, ifx.act_bytes(nb, 56, 56, 256))
         bufs = [torch.empty(big, dtype=torch.int8, device="cuda") for _ in range(4)]
         cur, nxt, t1, t2 = bufs
         stem = with_batch(net.stem, nb)
-        launches.append(conv_launch(wl.net.stem, nb, 224, 224, lambda: stem.run(x_blk[:nb], cur, None, stream)))
-        h = w = 56
+        launches.append(conv_launch(stem, wl.net.stem, nb, 224, 224, lambda: stem.run(x_blk[:nb], cur, None, stream)))
+        h = ww = 56
         state = {"cur": cur, "nxt": nxt}
         for bs, db in zip(wl.net.blocks, net.blocks):
             c1, c2, c3 = (with_batch(d, nb) for d in db.convs)
@@ -469,28 +583,34 @@ def main():
                     ifx.conv_proj_fused(c3_.desc, t2, c3_.w_blk, c3_.bias, c3_.mult, c3_.shift, pj_.desc,
                                         state["cur"], pj_.w_blk, pj_.bias, pj_.mult, pj_.shift, state["nxt"], stream)
                 return f
-            launches.append(conv_launch(bs.c1, nb, h, w, mk(c1, "cur", t1)))
-            launches.append(conv_launch(bs.c2, nb, h, w, mk(c2, t1, t2)))
+            launches.append(conv_launch(c1, bs.c1, nb, h, ww, mk(c1, "cur", t1)))
+            launches.append(conv_launch(c2, bs.c2, nb, h, ww, mk(c2, t1, t2)))
             if pj is not None:
-                launches.append(proj_launch(bs.c3, bs.proj, nb, h2, h2, h, w, mk_proj(c3, pj)))
+                launches.append(proj_launch(c3, pj, bs.c3, bs.proj, nb, h2, h2, h, ww, mk_proj(c3, pj)))
             else:
-                launches.append(conv_launch(bs.c3, nb, h2, h2, mk(c3, t2, "nxt", "cur")))
+                launches.append(conv_launch(c3, bs.c3, nb, h2, h2, mk(c3, t2, "nxt", "cur")))
 
             def swap():
                 state["cur"], state["nxt"] = state["nxt"], state["cur"]
             launches.append((None, 0, 0, swap))
-            h = w = h2
+            h = ww = h2
+        # head: average pool (read the last activation, write the pooled vector) and the FC
+        fc_in, fc_out = wl.net.fc_in, wl.net.fc_out
+        pool_bytes = n * h * ww * fc_in + n * fc_in
+        fc_ops, fc_bytes = 2 * n * fc_in * fc_out, n * fc_in + fc_in * fc_out + 4 * fc_out + 4 * n * fc_out
+        head_floor = pool_bytes / PEAK_HBM + max(fc_ops / PEAK_I8, fc_bytes / PEAK_HBM)
     else:
         nb, passes = n, 1
+        dcs, y = w["dcs"], w["y"]
         if wl.kind == "block":
             t1b = model.empty_act(n, 28, 28, 128)
             t2b = model.empty_act(n, 28, 28, 128)
             c1, c2, c3 = dcs
-            launches = [conv_launch(wl.convs[0], n, 28, 28, lambda: c1.run(x_blk, t1b, None, stream)),
-                        conv_launch(wl.convs[1], n, 28, 28, lambda: c2.run(t1b, t2b, None, stream)),
-                        conv_launch(wl.convs[2], n, 28, 28, lambda: c3.run(t2b, y, x_blk, stream))]
+            launches = [conv_launch(c1, wl.convs[0], n, 28, 28, lambda: c1.run(x_blk, t1b, None, stream)),
+                        conv_launch(c2, wl.convs[1], n, 28, 28, lambda: c2.run(t1b, t2b, None, stream)),
+                        conv_launch(c3, wl.convs[2], n, 28, 28, lambda: c3.run(t2b, y, x_blk, stream))]
         else:
-            launches = [conv_launch(wl.convs[0], n, wl.h, wl.w, step)]
+            launches = [conv_launch(dcs[0], wl.convs[0], n, wl.h, wl.w, w["step"])]
     reps = max(1, min(args.steps, 5) if args.workload == "net" else args.steps)
     evs = []
     torch.cuda.synchronize()
@@ -531,6 +651,9 @@ def main():
     roof["avg_launch_us"] = round(avg_t * 1e6, 2)
     roof["work_per_launch"] = {"ops": dom["ops"] // dom["launches"], "bytes": dom["bytes"] // dom["launches"]}
     kernel_share = {k: round(v["time"] / reps * passes * 1e3, 3) for k, v in per_kernel.items()}
+    # the step's floor: every launch at its own bound (ops / int8 peak or algorithmic bytes / HBM),
+    # summed over the launches of all passes, plus the head
+    floor_s = passes * sum(max(o / PEAK_I8, b / PEAK_HBM) for nm, o, b, _ in launches if nm is not None) + head_floor
 
     line = {
         "metric": METRIC,
@@ -545,19 +668,30 @@ def main():
         "vs_baseline": None,
         "dtype": "int8",
         "data": "synthetic (seeded SplitMix64, uniform int8 images/weights)",
-        "config": config,
+        "config": w["config"],
         "tops": round(tops, 2),
         "frac_int8_peak": round(tops * 1e12 / PEAK_I8, 4),
+        "floor_ms": round(floor_s * 1e3, 4),
+        "floor_frac": round(floor_s / sec_per_step, 4),
         "kernel_ms_per_step": kernel_share,
         "roofline": roof,
         **extra,
     }
+    del launches, evs
+    if args.workload in ("net", "net26_b1"):
+        del bufs, cur, nxt, t1, t2, state
+    if not args.no_extra:
+        del w
+        torch.cuda.empty_cache()
+        line["configs"] = extra_configs(stream, args.steps, args.warmup, args.workload)
+        line["ceilings"] = ceilings(stream)
+    line["gpu_s"] = round(time.perf_counter() - t0, 1)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.workload)
     print(json.dumps(line), flush=True)
     if args.copy_calibration_mib:
-        nb = args.copy_calibration_mib << 20
-        src = torch.randint(-2 ** 31, 2 ** 31 - 1, (nb // 4,), dtype=torch.int32, device="cuda")
+        nbc = args.copy_calibration_mib << 20
+        src = torch.randint(-2 ** 31, 2 ** 31 - 1, (nbc // 4,), dtype=torch.int32, device="cuda")
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
         for _ in range(3):

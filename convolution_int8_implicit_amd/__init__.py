@@ -23,7 +23,7 @@ import torch
 __all__ = [
     "RELU", "RESIDUAL", "MAXPOOL", "OUT_I32", "INPUT_NHWC", "IfxError", "ConvDesc", "BlockParams", "NetParams", "lib",
     "conv_desc", "conv_validate", "conv_out_dims", "act_bytes", "wpack_bytes", "pack_act", "unpack_act",
-    "pack_weights", "conv_fused", "block_workspace_bytes", "block_forward", "block_forward_noalloc",
+    "pack_weights", "conv_fused", "conv_kernel_name", "block_workspace_bytes", "block_forward", "block_forward_noalloc",
     "BLOCK_SCRATCH_BYTES", "net_workspace_bytes",
     "net_forward", "NetGraph", "fold_bn", "BnFold", "status_string", "last_hip_error", "version", "LIB_PATH",
 ]
@@ -103,7 +103,11 @@ def lib() -> ctypes.CDLL:
         "ifx_net_graph_create": ([ctypes.POINTER(NetParams), vp, vp, i32, vp, sz, ctypes.POINTER(vp)], i32),
         "ifx_graph_launch": ([vp, vp], i32),
         "ifx_graph_destroy": ([vp], i32),
+        "ifx_conv_kernel_name": ([D, ctypes.c_char_p, sz], i32),
+        "ifx_conv_proj_kernel_name": ([D, D, ctypes.c_char_p, sz], i32),
         "ifx_status_string": ([i32], ctypes.c_char_p),
+        "ifx_probe_copy": ([vp, vp, sz, vp], i32),
+        "ifx_probe_mfma_i8": ([vp, i32, i32, vp], i32),
         "ifx_last_hip_error": ([], i32),
         "ifx_version": ([], i32),
     }
@@ -217,6 +221,34 @@ def block_forward(p: BlockParams, x_blk, y_blk, ws: torch.Tensor, stream=None) -
     _dev(x_blk, y_blk, ws)
     _check(lib().ifx_block_forward(ctypes.byref(p), _ptr(x_blk), _ptr(y_blk), _ptr(ws), ws.numel() * ws.element_size(),
                                    _stream(stream)), "ifx_block_forward")
+
+
+def conv_kernel_name(d: ConvDesc, proj: Optional[ConvDesc] = None) -> str:
+    """The kernel instance ifx_conv_fused(d) (or ifx_conv_proj_fused(d, proj)) launches, as
+    profilers print it (host-only query)."""
+    buf = ctypes.create_string_buffer(256)
+    if proj is None:
+        _check(lib().ifx_conv_kernel_name(ctypes.byref(d), buf, len(buf)), "ifx_conv_kernel_name")
+    else:
+        _check(lib().ifx_conv_proj_kernel_name(ctypes.byref(d), ctypes.byref(proj), buf, len(buf)),
+               "ifx_conv_proj_kernel_name")
+    return buf.value.decode()
+
+
+def probe_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
+    """Streaming-copy ceiling probe (ifx_probe.h): dst = src, 16-byte non-temporal chunks."""
+    _dev(src, dst)
+    nbytes = src.numel() * src.element_size()
+    assert dst.numel() * dst.element_size() >= nbytes
+    _check(lib().ifx_probe_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)), "ifx_probe_copy")
+
+
+def probe_mfma_i8(out: torch.Tensor, blocks: int, iters: int, stream=None) -> int:
+    """int8 MFMA ceiling probe (ifx_probe.h); returns the ops it performs."""
+    _dev(out)
+    assert out.dtype == torch.int32 and out.numel() >= 4 * blocks
+    _check(lib().ifx_probe_mfma_i8(_ptr(out), blocks, iters, _stream(stream)), "ifx_probe_mfma_i8")
+    return blocks * 4 * iters * 16 * 32768
 
 
 # Bytes of the library-held scratch ifx_block_forward_noalloc uses (IFX_BLOCK_SCRATCH_BYTES).

@@ -9,15 +9,50 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <string.h>
+
 #include <algorithm>
 #include <mutex>
 #include <vector>
 
 #include "ifx_internal.h"
 
+namespace ifx {
+
+KernelQuery *&armed_query()
+{
+    thread_local KernelQuery *q = nullptr;
+    return q;
+}
+
+}  // namespace ifx
+
 namespace {
 
 thread_local int32_t g_last_hip = 0;
+
+// Arms a kernel-name query for the calling thread for the object's lifetime.
+struct ArmedQuery {
+    ifx::KernelQuery q;
+    ArmedQuery()
+    {
+        q.name[0] = 0;
+        q.answered = false;
+        ifx::armed_query() = &q;
+    }
+    ~ArmedQuery() { ifx::armed_query() = nullptr; }
+    ArmedQuery(const ArmedQuery &) = delete;
+    ArmedQuery &operator=(const ArmedQuery &) = delete;
+};
+
+ifx_status copy_name(const ifx::KernelQuery &q, char *buf, size_t len)
+{
+    if (!q.answered) return IFX_E_UNSUPPORTED;
+    const size_t n = strlen(q.name);
+    if (n + 1 > len) return IFX_E_WORKSPACE;
+    memcpy(buf, q.name, n + 1);
+    return IFX_OK;
+}
 
 enum Kind { kGeneric, kStem };
 
@@ -541,6 +576,39 @@ ifx_status ifx_conv_fused(const ifx_conv_desc *d, const int8_t *x_blk, const int
     if (st != IFX_OK) return st;
     return run_conv(d, k, dm, x_blk, w_blk, bias, mult, shift, (d->flags & IFX_RESIDUAL) ? residual : nullptr, y,
                     (hipStream_t)stream);
+}
+
+ifx_status ifx_conv_kernel_name(const ifx_conv_desc *d, char *buf, size_t len)
+{
+    Kind k;
+    Dims dm;
+    ifx_status st = check_desc(d, &k, &dm);
+    if (st != IFX_OK) return st;
+    if (!buf) return IFX_E_NULL;
+    ArmedQuery aq;
+    st = run_conv(d, k, dm, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
+    if (st != IFX_OK) return st;
+    return copy_name(aq.q, buf, len);
+}
+
+ifx_status ifx_conv_proj_kernel_name(const ifx_conv_desc *d3, const ifx_conv_desc *dp, char *buf, size_t len)
+{
+    if (!d3 || !dp) return IFX_E_NULL;
+    Kind k3, kp;
+    Dims m3, mp;
+    ifx_status st = check_desc(d3, &k3, &m3);
+    if (st != IFX_OK) return st;
+    st = check_desc(dp, &kp, &mp);
+    if (st != IFX_OK) return st;
+    if (k3 != kGeneric || kp != kGeneric || !proj_fusable(d3, dp)) return IFX_E_UNSUPPORTED;
+    if (dp->n != d3->n || dp->c_out != d3->c_out || mp.oh != m3.oh || mp.ow != m3.ow) return IFX_E_SHAPE;
+    if (!buf) return IFX_E_NULL;
+    ArmedQuery aq;
+    const ifx::ConvArgs a = conv_args(d3, m3, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
+    const ifx::ConvArgs pj = conv_args(dp, mp, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
+    st = hip_status(ifx::launch_conv_proj(a, pj, nullptr));
+    if (st != IFX_OK) return st;
+    return copy_name(aq.q, buf, len);
 }
 
 size_t ifx_block_workspace_bytes(const ifx_block_params *p)

@@ -331,6 +331,7 @@ void conv1x1_proj_kernel(ConvArgs a, ConvArgs pj, int tiles_n)
 template <int BM, int BN, int NSP, int NSA>
 hipError_t launch_1x1_proj(const ConvArgs &a, const ConvArgs &pj, hipStream_t s)
 {
+    if (answer_query("conv1x1_proj_kernel<%d, %d, %d, %d, %s>", BM, BN, NSP, NSA, tf(a.relu != 0))) return hipSuccess;
     using P = C1PCfg<BM, BN, NSP, NSA>;
     const int tiles_n = (a.oc1 * 32 + BN - 1) / BN;
     const long long tiles_m = (a.m + BM - 1) / BM;
@@ -357,6 +358,7 @@ hipError_t launch_1x1_proj_k(const ConvArgs &a, const ConvArgs &pj, hipStream_t 
 template <int BM, int BN, int NST, bool RES>
 hipError_t launch_1x1(const ConvArgs &a, hipStream_t s)
 {
+    if (answer_query("conv1x1_kernel<%d, %d, %d, %s, %s>", BM, BN, NST, tf(RES), tf(a.relu != 0))) return hipSuccess;
     using C = C1Cfg<BM, BN, NST>;
     const int tiles_n = (a.oc1 * 32 + BN - 1) / BN;
     const long long tiles_m = (a.m + BM - 1) / BM;

@@ -3,7 +3,9 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stdarg.h>
 #include <stdint.h>
+#include <stdio.h>
 
 namespace ifx {
 
@@ -32,6 +34,33 @@ struct ConvArgs {
     unsigned howo_mul, wo_mul, o2_mul;
     int howo_shr, wo_shr, o2_shr;
 };
+
+// Host-side kernel-name query.  While a thread has a query armed, the launchers it reaches
+// launch nothing: the first one writes the name of the kernel instance it would launch, as
+// profilers print it (e.g. "igemm_kernel<3, 3, 128, 128, 2, false, true, false>"), and returns
+// hipSuccess.  The query therefore runs exactly the dispatch code of the launch it describes.
+struct KernelQuery {
+    char name[160];
+    bool answered;
+};
+KernelQuery *&armed_query();  // this thread's armed query, or null
+
+// Called first by every leaf launcher: true when a query took the call (nothing to launch).
+inline bool answer_query(const char *fmt, ...)
+{
+    KernelQuery *q = armed_query();
+    if (!q) return false;
+    if (!q->answered) {
+        va_list ap;
+        va_start(ap, fmt);
+        vsnprintf(q->name, sizeof(q->name), fmt, ap);
+        va_end(ap);
+        q->answered = true;
+    }
+    return true;
+}
+
+inline const char *tf(bool b) { return b ? "true" : "false"; }
 
 // Compute units of the current device: a device property the runtime keeps on the host, so
 // reading it launches nothing and is safe while a stream is being captured.  The persistent

@@ -461,6 +461,9 @@ void igemm_kernel(ConvArgs a, ConvArgs pj, int tiles_n, int per_xcd)
 template <int KH, int KW, int BM, int BN, int ST, bool RES, bool PROJ>
 hipError_t launch_ig(const ConvArgs &a, const ConvArgs &pj, hipStream_t s)
 {
+    if (answer_query("igemm_kernel<%d, %d, %d, %d, %d, %s, %s, %s>", KH, KW, BM, BN, ST, tf(RES), tf(a.relu != 0),
+                     tf(PROJ)))
+        return hipSuccess;
     const int tiles_n = (a.oc1 * 32 + BN - 1) / BN;
     const long long tiles_m = (a.m + BM - 1) / BM;
     const long long per = (tiles_m + 7) / 8;
@@ -687,6 +690,7 @@ static_assert(2 * kHaloLds > kLdsBytes, "one haloed-window workgroup per CU");
 
 hipError_t launch_conv3x3_halo(const ConvArgs &a, hipStream_t s)
 {
+    if (answer_query("conv3x3_halo_kernel<%s>", tf(a.relu != 0))) return hipSuccess;
     int slots = 0;
     hipError_t e = current_cus(&slots);
     if (e != hipSuccess) return e;
@@ -833,6 +837,7 @@ hipError_t launch_conv_split(const ConvArgs &a, int kh, int kw, int32_t *part, s
     q.kb_per = per;
     hipError_t e = kh == 1 ? launch_ig_k<1, 1>(q, s) : launch_ig_k<3, 3>(q, s);
     if (e != hipSuccess) return e;
+    if (armed_query()) return hipSuccess;  // the partial launch named the kernel
     const long long items = (long long)a.m * (a.out_i32 ? a.oc / 4 : a.oc1 * 8);
     hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((items + 63) / 64)), dim3(256), 0, s, a, part, n);
     return hipGetLastError();

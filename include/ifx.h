@@ -321,6 +321,18 @@ typedef struct {
 ifx_status ifx_fold_bn(const ifx_bn_fold *f, int32_t *bias, int32_t *mult, int32_t *shift, int32_t *status,
                        void *stream);
 
+/*
+ * Host-only: the kernel instance ifx_conv_fused(d, ...) launches, named as
+ * profilers print it (e.g. "igemm_kernel<3, 3, 128, 128, 2, false, true,
+ * false>"), written NUL-terminated into buf.  The name comes from the very
+ * dispatch code of the launch, run with launching switched off, so it cannot
+ * drift from what runs; it lets a measurement attribute per-kernel times.
+ * ifx_conv_proj_kernel_name does the same for ifx_conv_proj_fused(d3, dp).
+ * Validation as the launching calls; IFX_E_WORKSPACE when len is too small.
+ */
+ifx_status ifx_conv_kernel_name(const ifx_conv_desc *d, char *buf, size_t len);
+ifx_status ifx_conv_proj_kernel_name(const ifx_conv_desc *d3, const ifx_conv_desc *dp, char *buf, size_t len);
+
 /* Host-only: a static, human-readable name of a status. */
 const char *ifx_status_string(ifx_status s);
 

@@ -1,0 +1,44 @@
+/*
+ * ifx_probe.h -- practical-ceiling probes of the device (part of libifx.so).
+ *
+ * Not part of the convolution path: these kernels measure what the device
+ * reaches at all, so a measurement can report each convolution kernel both
+ * against the published peaks (HBM 8 TB/s, dense int8 MFMA 5.0 POP/s) and
+ * against what a plain kernel attains on the same box.  The pages time their
+ * fused kernels against the memory and tensor-core limits of their GPUs
+ * (Inspur conv-merge article, section 4); these probes give the MI355X
+ * counterparts.  Return values are ifx_status codes (ifx.h): 0 ok, 1 null,
+ * 2 bad size, 4 misaligned, 6 HIP launch failure.
+ */
+#ifndef IFX_PROBE_H
+#define IFX_PROBE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * Copy `bytes` (a multiple of 16) from src to dst, DEVICE pointers, 16-byte
+ * aligned, not overlapping: 16-byte non-temporal vector loads and stores in a
+ * grid-stride loop over at most 64 workgroups of 256 threads per CU.  Moves
+ * 2 * bytes through HBM.  Enqueued on `stream` (hipStream_t as void*).
+ */
+int32_t ifx_probe_copy(const void *src, void *dst, size_t bytes, void *stream);
+
+/*
+ * `blocks` workgroups of four waves, each wave running `iters` rounds of a
+ * 4 x 4 tile of independent v_mfma_i32_16x16x64_i8 (16 x 16 x 64 int8
+ * products, 32768 ops each) on register operands, then writing one int32 per
+ * wave to out (DEVICE, blocks * 4 elements).
+ * Ops = blocks * 4 * iters * 16 * 32768.
+ */
+int32_t ifx_probe_mfma_i8(int32_t *out, int32_t blocks, int32_t iters, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IFX_PROBE_H */

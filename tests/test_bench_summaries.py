@@ -62,3 +62,17 @@ def test_trace_summary_replay_averages(tmp_path):
     assert "igemm_kernel<3, 3, 128, 128, 2, false, true, false>(ifx::ConvArgs, int) | 3 | 433 | 1300" in text
     assert "replay: igemm_kernel<3, 3, 128, 128, 2, false, true, false> | 2 | 200 | 100 | 300" in text
     assert "replay: conv1x1_kernel<128, 128, 2, true, true> | 1 | 300 | 300 | 300" in text
+
+
+def test_kernel_names_match_the_profiled_instances():
+    """The library's kernel-name query (the launch's own dispatch, run without launching) names
+    exactly the kernel instances rocprofv3 recorded for the network's per-launch replays in
+    profiles/kernel_stats_net.txt (the FC's instance may appear there too)."""
+    import convolution_int8_implicit_amd as ifx
+    from convolution_int8_implicit_amd import synth
+    names = set(bench.net_kernel_names(synth.workload(4).net, 1024))
+    fc = ifx.conv_kernel_name(ifx.conv_desc(1024, 1, 1, 2048, 1000, 1, 1, 1, 0, ifx.OUT_I32))
+    with open(os.path.join(ROOT, "profiles", "kernel_stats_net.txt")) as fh:
+        profiled = {ln.split(" | ")[0][len("replay: "):] for ln in fh if ln.startswith("replay: ")}
+    assert names <= profiled, names - profiled
+    assert profiled <= names | {fc}, profiled - names
