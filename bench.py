@@ -37,6 +37,7 @@ KERNEL_SOURCES = {
     "igemm_kernel": ["igemm.hip", "device_common.h", "ifx_internal.h"],
     "conv1x1_kernel": ["conv1x1.hip", "device_common.h", "ifx_internal.h"],
     "conv1x1_proj_kernel": ["conv1x1.hip", "device_common.h", "ifx_internal.h"],
+    "conv1x1_chain_kernel": ["conv1x1.hip", "device_common.h", "ifx_internal.h"],
     "conv3x3_halo_kernel": ["igemm.hip", "device_common.h", "ifx_internal.h"],
     "stem_kernel": ["stem.hip", "device_common.h", "ifx_internal.h"],
 }
@@ -78,7 +79,7 @@ def summarize_pmc(fetch_csv: str, write_csv: str, calib_bytes: int, out: str, wo
     from collections import defaultdict
 
     def short(name):
-        m = re.search(r"((?:conv1x1_proj|conv1x1|conv3x3_halo|igemm|stem)_kernel<[^>]*>)", name)
+        m = re.search(r"((?:conv1x1_chain|conv1x1_proj|conv1x1|conv3x3_halo|igemm|stem)_kernel<[^>]*>)", name)
         if m:
             return m.group(1)
         return "copy" if "bitwise_not" in name else None
@@ -149,7 +150,7 @@ def summarize_trace(trace_csv: str, stats_csv: str, out: str, workload: str, not
     last_pool = max((int(r["Dispatch_Id"]) for r in rows if "avgpool_kernel" in r["Kernel_Name"]), default=-1)
     rep = defaultdict(list)
     for r in rows:
-        m = re.search(r"((?:conv1x1_proj|conv1x1|conv3x3_halo|igemm|stem)_kernel<[^>]*>)", r["Kernel_Name"])
+        m = re.search(r"((?:conv1x1_chain|conv1x1_proj|conv1x1|conv3x3_halo|igemm|stem)_kernel<[^>]*>)", r["Kernel_Name"])
         if m and int(r["Dispatch_Id"]) > last_pool:
             rep[m.group(1)].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
     lines += ["#", "# per-launch replays only (one conv launch at a time on one stream; bench.py's",
@@ -176,7 +177,7 @@ def summarize_counters(csvs, out: str, workload: str, note: str):
             rows = list(csv.DictReader(fh))
         last_pool = max((int(r["Dispatch_Id"]) for r in rows if "avgpool_kernel" in r["Kernel_Name"]), default=-1)
         for r in rows:
-            m = re.search(r"((?:conv1x1_proj|conv1x1|conv3x3_halo|igemm|stem)_kernel<[^>]*>)", r["Kernel_Name"])
+            m = re.search(r"((?:conv1x1_chain|conv1x1_proj|conv1x1|conv3x3_halo|igemm|stem)_kernel<[^>]*>)", r["Kernel_Name"])
             if m and int(r["Dispatch_Id"]) > last_pool:
                 per[m.group(1)][r["Counter_Name"]].append(float(r["Counter_Value"]))
     counters = sorted({c for k in per.values() for c in k})
@@ -237,14 +238,23 @@ def net_kernel_names(net_spec, nb: int, nhwc: bool = True) -> list:
                              spec.flags | extra)
     names = [ifx.conv_kernel_name(desc(net_spec.stem, 224, 224, ifx.INPUT_NHWC if nhwc else 0))]
     h = w = 56
-    for b in net_spec.blocks:
+    have_t1 = False
+    for i, b in enumerate(net_spec.blocks):
         h2 = (h + 2 - 3) // b.c2.stride + 1
-        names.append(ifx.conv_kernel_name(desc(b.c1, h, w)))
+        if not have_t1:
+            names.append(ifx.conv_kernel_name(desc(b.c1, h, w)))
         names.append(ifx.conv_kernel_name(desc(b.c2, h, w)))
+        nxt = net_spec.blocks[i + 1] if i + 1 < len(net_spec.blocks) else None
+        chain = None
+        if b.proj is None and nxt is not None:
+            chain = ifx.conv_chain_kernel_name(desc(b.c3, h2, h2), desc(nxt.c1, h2, h2))
         if b.proj is not None:
             names.append(ifx.conv_kernel_name(desc(b.c3, h2, h2), desc(b.proj, h, w)))
+        elif chain is not None:
+            names.append(chain)
         else:
             names.append(ifx.conv_kernel_name(desc(b.c3, h2, h2)))
+        have_t1 = chain is not None
         h = w = h2
     return names
 
@@ -540,6 +550,13 @@ def main():
         ops, byts, _, _ = layer_work(spec, nb_, h, w_)
         return (ifx.conv_kernel_name(dc.desc), ops, byts, fn)
 
+    def chain_launch(c3, c1n, c3spec, c1spec, nb_, h3, w3, name, fn):
+        # conv3 + the next block's conv1 in one kernel: both contractions; conv1 reads the block
+        # output on chip, so that read is not a tensor crossing HBM
+        o3, b3, oh, ow = layer_work(c3spec, nb_, h3, w3)
+        o1, b1, _, _ = layer_work(c1spec, nb_, oh, ow)
+        return (name, o3 + o1, b3 + b1 - nb_ * oh * ow * c3spec.c_out, fn)
+
     def proj_launch(c3, pj, c3spec, pspec, nb_, h3, w3, hp, wp, fn):
         # conv3 + projection in one kernel: both contractions; the shortcut is not a tensor
         o3, b3, oh, ow = layer_work(c3spec, nb_, h3, w3)
@@ -565,10 +582,14 @@ def main():
         launches.append(conv_launch(stem, wl.net.stem, nb, 224, 224, lambda: stem.run(x_blk[:nb], cur, None, stream)))
         h = ww = 56
         state = {"cur": cur, "nxt": nxt}
-        for bs, db in zip(wl.net.blocks, net.blocks):
+        have_t1 = False
+        for bi, (bs, db) in enumerate(zip(wl.net.blocks, net.blocks)):
             c1, c2, c3 = (with_batch(d, nb) for d in db.convs)
             pj = with_batch(db.proj, nb) if db.proj is not None else None
             h2 = c2.out_hw[0]
+            nb_blk = net.blocks[bi + 1] if bi + 1 < len(net.blocks) else None
+            c1n = with_batch(nb_blk.convs[0], nb) if nb_blk is not None else None
+            chain = ifx.conv_chain_kernel_name(c3.desc, c1n.desc) if (pj is None and c1n is not None) else None
 
             def mk(c, xin_key, out, res_key=None):
                 def f():
@@ -583,12 +604,23 @@ def main():
                     ifx.conv_proj_fused(c3_.desc, t2, c3_.w_blk, c3_.bias, c3_.mult, c3_.shift, pj_.desc,
                                         state["cur"], pj_.w_blk, pj_.bias, pj_.mult, pj_.shift, state["nxt"], stream)
                 return f
-            launches.append(conv_launch(c1, bs.c1, nb, h, ww, mk(c1, "cur", t1)))
+            def mk_chain(c3_, c1n_):
+                def f():
+                    ifx.conv_chain_fused(c3_.desc, t2, c3_.w_blk, c3_.bias, c3_.mult, c3_.shift, state["cur"],
+                                         state["nxt"], c1n_.desc, c1n_.w_blk, c1n_.bias, c1n_.mult, c1n_.shift, t1,
+                                         stream)
+                return f
+            if not have_t1:
+                launches.append(conv_launch(c1, bs.c1, nb, h, ww, mk(c1, "cur", t1)))
             launches.append(conv_launch(c2, bs.c2, nb, h, ww, mk(c2, t1, t2)))
             if pj is not None:
                 launches.append(proj_launch(c3, pj, bs.c3, bs.proj, nb, h2, h2, h, ww, mk_proj(c3, pj)))
+            elif chain is not None:
+                launches.append(chain_launch(c3, c1n, bs.c3, wl.net.blocks[bi + 1].c1, nb, h2, h2, chain,
+                                             mk_chain(c3, c1n)))
             else:
                 launches.append(conv_launch(c3, bs.c3, nb, h2, h2, mk(c3, t2, "nxt", "cur")))
+            have_t1 = chain is not None
 
             def swap():
                 state["cur"], state["nxt"] = state["nxt"], state["cur"]

@@ -23,7 +23,8 @@ import torch
 __all__ = [
     "RELU", "RESIDUAL", "MAXPOOL", "OUT_I32", "INPUT_NHWC", "IfxError", "ConvDesc", "BlockParams", "NetParams", "lib",
     "conv_desc", "conv_validate", "conv_out_dims", "act_bytes", "wpack_bytes", "pack_act", "unpack_act",
-    "pack_weights", "conv_fused", "conv_kernel_name", "block_workspace_bytes", "block_forward", "block_forward_noalloc",
+    "pack_weights", "conv_fused", "conv_chain_fused", "conv_chain_kernel_name", "conv_kernel_name",
+    "block_workspace_bytes", "block_forward", "block_forward_noalloc",
     "BLOCK_SCRATCH_BYTES", "net_workspace_bytes",
     "net_forward", "NetGraph", "fold_bn", "BnFold", "status_string", "last_hip_error", "version", "LIB_PATH",
 ]
@@ -105,6 +106,8 @@ def lib() -> ctypes.CDLL:
         "ifx_graph_destroy": ([vp], i32),
         "ifx_conv_kernel_name": ([D, ctypes.c_char_p, sz], i32),
         "ifx_conv_proj_kernel_name": ([D, D, ctypes.c_char_p, sz], i32),
+        "ifx_conv_chain_kernel_name": ([D, D, ctypes.c_char_p, sz], i32),
+        "ifx_conv_chain_fused": ([D, vp, vp, vp, vp, vp, vp, vp, D, vp, vp, vp, vp, vp, vp], i32),
         "ifx_status_string": ([i32], ctypes.c_char_p),
         "ifx_probe_copy": ([vp, vp, sz, vp], i32),
         "ifx_probe_mfma_i8": ([vp, i32, i32, vp], i32),
@@ -221,6 +224,25 @@ def block_forward(p: BlockParams, x_blk, y_blk, ws: torch.Tensor, stream=None) -
     _dev(x_blk, y_blk, ws)
     _check(lib().ifx_block_forward(ctypes.byref(p), _ptr(x_blk), _ptr(y_blk), _ptr(ws), ws.numel() * ws.element_size(),
                                    _stream(stream)), "ifx_block_forward")
+
+
+def conv_chain_fused(d3: ConvDesc, t_blk, w3_blk, bias3, mult3, shift3, residual, y, d1: ConvDesc, w1_blk, bias1,
+                     mult1, shift1, t1, stream=None) -> None:
+    """conv3 (with its shortcut) and the next block's conv1 as one launch (ifx_conv_chain_fused)."""
+    ts = (t_blk, w3_blk, bias3, mult3, shift3, residual, y, w1_blk, bias1, mult1, shift1, t1)
+    _dev(*ts)
+    _check(lib().ifx_conv_chain_fused(ctypes.byref(d3), *[_ptr(t) for t in ts[:7]], ctypes.byref(d1),
+                                      *[_ptr(t) for t in ts[7:]], _stream(stream)), "ifx_conv_chain_fused")
+
+
+def conv_chain_kernel_name(d3: ConvDesc, d1: ConvDesc):
+    """The kernel ifx_conv_chain_fused(d3, d1) launches, or None when the pair does not chain."""
+    buf = ctypes.create_string_buffer(256)
+    rc = lib().ifx_conv_chain_kernel_name(ctypes.byref(d3), ctypes.byref(d1), buf, len(buf))
+    if rc == 3:
+        return None
+    _check(rc, "ifx_conv_chain_kernel_name")
+    return buf.value.decode()
 
 
 def conv_kernel_name(d: ConvDesc, proj: Optional[ConvDesc] = None) -> str:

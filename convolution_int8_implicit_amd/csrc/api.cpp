@@ -293,9 +293,26 @@ bool proj_fusable(const ifx_conv_desc *d3, const ifx_conv_desc *dp)
            dp->pad == 0 && (d3->flags & ~(uint32_t)IFX_RELU) == IFX_RESIDUAL && dp->flags == 0;
 }
 
-// Launch a validated block for batch n; workspace already checked.
+// A conv3 (with its shortcut) and the next block's conv1 that ifx_conv_chain_fused computes in one
+// launch (descriptors already valid; both at the same batch).
+bool chain_fusable(const ifx_conv_desc *d3, const Dims &m3, const ifx_conv_desc *d1, const Dims &m1)
+{
+    if (d3->kh != 1 || d3->kw != 1 || d3->stride != 1 || d3->pad != 0) return false;
+    if (d1->kh != 1 || d1->kw != 1 || d1->stride != 1 || d1->pad != 0) return false;
+    if (d3->flags != (IFX_RESIDUAL | IFX_RELU) || (d1->flags & ~(uint32_t)IFX_RELU)) return false;
+    if (d1->n != d3->n || d1->h != m3.oh || d1->w != m3.ow || d1->c_in != d3->c_out) return false;
+    const ifx::ConvArgs a = conv_args(d3, m3, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
+    const ifx::ConvArgs b = conv_args(d1, m1, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
+    return ifx::conv1x1_chain_supported(a, b);
+}
+
+// Launch a validated block for batch n; workspace already checked.  skip_c1: the block's conv1
+// output is already in the workspace's t1 (the previous block chained it).  next (or null): the
+// following block; when this block's conv3 chains with next's conv1, both run as one launch that
+// also leaves next's t1 in the workspace, and *chained is set.
 ifx_status run_block(const ifx_block_params *p, const BlockPlan &plan, int n, const int8_t *x, int8_t *y,
-                     int8_t *ws, int32_t *part, size_t part_bytes, hipStream_t s)
+                     int8_t *ws, int32_t *part, size_t part_bytes, hipStream_t s, bool skip_c1 = false,
+                     const ifx_block_params *next = nullptr, bool *chained = nullptr)
 {
     ifx_conv_desc d[4];
     const int nd = p->has_proj ? 4 : 3;
@@ -303,13 +320,16 @@ ifx_status run_block(const ifx_block_params *p, const BlockPlan &plan, int n, co
         d[i] = p->d[i];
         d[i].n = n;
     }
+    if (chained) *chained = false;
     int8_t *t1 = ws;
     int8_t *t2 = ws + plan.t1;
     int8_t *sc = ws + plan.t1 + plan.t2;
     ifx_status st;
-    st = run_conv(&d[0], kGeneric, plan.dims[0], x, p->w_blk[0], p->bias[0], p->mult[0], p->shift[0], nullptr, t1, s,
-                  part, part_bytes);
-    if (st != IFX_OK) return st;
+    if (!skip_c1) {
+        st = run_conv(&d[0], kGeneric, plan.dims[0], x, p->w_blk[0], p->bias[0], p->mult[0], p->shift[0], nullptr, t1,
+                      s, part, part_bytes);
+        if (st != IFX_OK) return st;
+    }
     st = run_conv(&d[1], kGeneric, plan.dims[1], t1, p->w_blk[1], p->bias[1], p->mult[1], p->shift[1], nullptr, t2, s,
                   part, part_bytes);
     if (st != IFX_OK) return st;
@@ -327,6 +347,20 @@ ifx_status run_block(const ifx_block_params *p, const BlockPlan &plan, int n, co
                       sc, s, part, part_bytes);
         if (st != IFX_OK) return st;
         res = sc;
+    } else if (next) {
+        ifx_conv_desc d1 = next->d[0];
+        d1.n = n;
+        Dims m1;
+        if (check_desc(&d1, nullptr, &m1) == IFX_OK && chain_fusable(&d[2], plan.dims[2], &d1, m1)) {
+            // conv3 and the next block's conv1 in one launch: the block output is read from LDS
+            const ifx::ConvArgs a = conv_args(&d[2], plan.dims[2], t2, p->w_blk[2], p->bias[2], p->mult[2],
+                                              p->shift[2], x, y);
+            const ifx::ConvArgs b = conv_args(&d1, m1, y, next->w_blk[0], next->bias[0], next->mult[0],
+                                              next->shift[0], nullptr, t1);
+            st = hip_status(ifx::launch_conv1x1_chain(a, b, s));
+            if (st == IFX_OK && chained) *chained = true;
+            return st;
+        }
     }
     return run_conv(&d[2], kGeneric, plan.dims[2], t2, p->w_blk[2], p->bias[2], p->mult[2], p->shift[2], res, y, s,
                     part, part_bytes);
@@ -477,6 +511,21 @@ hipError_t device_lane(Lane *out)
     }
     *out = lanes[dev];
     return hipSuccess;
+}
+
+// Validation shared by ifx_conv_chain_fused and its name query.
+ifx_status check_chain(const ifx_conv_desc *d3, const ifx_conv_desc *d1, Dims *m3, Dims *m1)
+{
+    if (!d3 || !d1) return IFX_E_NULL;
+    Kind k3, k1;
+    ifx_status st = check_desc(d3, &k3, m3);
+    if (st != IFX_OK) return st;
+    st = check_desc(d1, &k1, m1);
+    if (st != IFX_OK) return st;
+    if (k3 != kGeneric || k1 != kGeneric) return IFX_E_UNSUPPORTED;
+    if (d1->n != d3->n || d1->h != m3->oh || d1->w != m3->ow || d1->c_in != d3->c_out) return IFX_E_SHAPE;
+    if (!chain_fusable(d3, *m3, d1, *m1)) return IFX_E_UNSUPPORTED;
+    return IFX_OK;
 }
 
 }  // namespace
@@ -643,6 +692,39 @@ ifx_status ifx_conv_proj_fused(const ifx_conv_desc *d3, const int8_t *t_blk, con
     return hip_status(ifx::launch_conv_proj(a, pj, (hipStream_t)stream));
 }
 
+ifx_status ifx_conv_chain_fused(const ifx_conv_desc *d3, const int8_t *t_blk, const int8_t *w3_blk,
+                                const int32_t *bias3, const int32_t *mult3, const int32_t *shift3,
+                                const int8_t *residual_blk, int8_t *y_blk, const ifx_conv_desc *d1,
+                                const int8_t *w1_blk, const int32_t *bias1, const int32_t *mult1,
+                                const int32_t *shift1, int8_t *t1_blk, void *stream)
+{
+    Dims m3, m1;
+    ifx_status st = check_chain(d3, d1, &m3, &m1);
+    if (st != IFX_OK) return st;
+    const void *ptrs[] = {t_blk, w3_blk, bias3, mult3, shift3, residual_blk, y_blk, w1_blk, bias1, mult1, shift1, t1_blk};
+    for (const void *q : ptrs)
+        if (!q) return IFX_E_NULL;
+    for (const void *q : ptrs)
+        if (!aligned16(q)) return IFX_E_ALIGN;
+    const ifx::ConvArgs a = conv_args(d3, m3, t_blk, w3_blk, bias3, mult3, shift3, residual_blk, y_blk);
+    const ifx::ConvArgs b = conv_args(d1, m1, y_blk, w1_blk, bias1, mult1, shift1, nullptr, t1_blk);
+    return hip_status(ifx::launch_conv1x1_chain(a, b, (hipStream_t)stream));
+}
+
+ifx_status ifx_conv_chain_kernel_name(const ifx_conv_desc *d3, const ifx_conv_desc *d1, char *buf, size_t len)
+{
+    Dims m3, m1;
+    ifx_status st = check_chain(d3, d1, &m3, &m1);
+    if (st != IFX_OK) return st;
+    if (!buf) return IFX_E_NULL;
+    ArmedQuery aq;
+    const ifx::ConvArgs a = conv_args(d3, m3, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
+    const ifx::ConvArgs b = conv_args(d1, m1, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
+    st = hip_status(ifx::launch_conv1x1_chain(a, b, nullptr));
+    if (st != IFX_OK) return st;
+    return copy_name(aq.q, buf, len);
+}
+
 ifx_status ifx_block_forward(const ifx_block_params *p, const int8_t *x_blk, int8_t *y_blk, void *ws,
                              size_t ws_bytes, void *stream)
 {
@@ -747,6 +829,7 @@ ifx_status run_net(const ifx_net_params *p, const NetPlan &plan, const int8_t *x
                       nullptr, act[0], s);
         if (st != IFX_OK) break;
         int cur = 0;
+        bool have_t1 = false;  // the previous block chained this block's conv1 into t1
         for (int b = 0; b < p->n_blocks; ++b) {
             BlockPlan bp;
             st = plan_block(&p->blocks[b], nb, &bp);
@@ -755,8 +838,12 @@ ifx_status run_net(const ifx_net_params *p, const NetPlan &plan, const int8_t *x
             BlockPlan lay = bp;
             lay.t1 = plan.t1;
             lay.t2 = plan.t2;
-            st = run_block(&p->blocks[b], lay, nb, act[cur], act[cur ^ 1], bws, part, plan.part, s);
+            const ifx_block_params *next = b + 1 < p->n_blocks ? &p->blocks[b + 1] : nullptr;
+            bool chained = false;
+            st = run_block(&p->blocks[b], lay, nb, act[cur], act[cur ^ 1], bws, part, plan.part, s, have_t1, next,
+                           &chained);
             if (st != IFX_OK) break;
+            have_t1 = chained;
             cur ^= 1;
         }
         if (st != IFX_OK) break;

@@ -380,6 +380,283 @@ hipError_t launch_1x1_res(const ConvArgs &a, hipStream_t s)
     return a.residual ? launch_1x1<BM, BN, NST, true>(a, s) : launch_1x1<BM, BN, NST, false>(a, s);
 }
 
+
+// ---- conv3 of one bottleneck chained with conv1 of the next (256-channel block output) ----
+//
+// y  = ReLU(requant(conv3(t2)) + shortcut)          the block output, stored (the next block's
+//                                                    shortcut) and kept in LDS
+// t1 = [ReLU](requant(conv1'(y)))                   the next block's first convolution
+// The Inspur conv-merge article (section 2.1) merges consecutive operators so that the tensor
+// passed between them is neither written by one nor read back by the other; here y is still
+// written (the next block adds it as its shortcut) but conv1' reads it from LDS, saving one full
+// read of the block output.  Persistent workgroups of four waves walk 64-pixel tiles:
+//   * both convolutions' weights live in registers for the whole launch (conv3: 16 bytes x 4 per
+//     lane, conv1': 16 bytes x 4 K-steps per 16 output channels), as do their parameters;
+//   * a ring of kChainNB LDS buffers holds each tile's activations (64 x 64 bytes) and shortcut
+//     (four 64 x 64 byte regions, one per wave's 64 channels, in the XOR-swizzled row layout of
+//     an MFMA operand); the DMAs of the tiles kChainNB - 2 ahead stay in flight while a tile is
+//     computed, which is what keeps HBM busy: a tile carries ~40 KB of traffic and ~2 us of work;
+//   * phase 1 (each wave 64 pixels x 64 channels, K <= 64) requantises in place, turning its
+//     shortcut region into y; those four regions are exactly conv1''s four 64-byte K-steps;
+//   * phase 2 multiplies with the weights as the row operand (each wave N1/4 channels x 64
+//     pixels), so a lane ends with 4 (N1 = 64) or 8 (N1 = 128) consecutive channels of one pixel
+//     and stores them straight from registers.
+constexpr int kChainC = 256;                   // block-output channels (four waves x 64)
+constexpr int kChainA = 4096;                  // a tile's conv3 activations: [64 rows][64 B]
+constexpr int kChainBuf = kChainA + 4 * 4096;  // + shortcut / y: four [64 rows][64 B] regions
+constexpr int kChainNB = 4;                    // ring depth (tiles resident in LDS)
+constexpr int kChainDma = 5;                   // DMAs per wave per tile: 1 activation, 4 shortcut
+constexpr int kChainPerCu = 2;                 // resident workgroups per CU
+static_assert(kChainNB >= 3 && kChainPerCu * kChainNB * kChainBuf <= kLdsBytes, "ring fits the LDS");
+
+// Physical LDS byte of logical 16-byte chunk k of row r in a [rows][64 B] swizzled region.
+__device__ __forceinline__ int swz_at(int r, int k) { return r * 64 + ((k ^ swz(r)) << 4); }
+
+// This wave's DMAs of the tile at pixel m0 (m0 >= a.m: every load is out of range, so the
+// buffer fills with zeros and the count of DMAs stays the same): activation rows 16 wave .. +15
+// into the buffer's first 4 KB, the shortcut bytes of channels 64 wave .. +63 into its region.
+__device__ __forceinline__ void chain_issue(const ConvArgs &a, int8_t *buf, int m0, int wave, int lane)
+{
+    const int HoWo = a.ho * a.wo;  // = h * w: unit stride, no padding
+    const int img0 = fdiv(m0, a.howo_mul, a.howo_shr);
+    {
+        const long long in_img = (long long)a.i1 * HoWo * 32;
+        const v4i rsA = make_rsrc(a.x + (long long)img0 * in_img, (long long)(a.n - img0) * in_img);
+        const int row = 16 * wave + (lane >> 2);
+        const int lch = (lane & 3) ^ swz(row);  // logical chunk: input channels 16 lch .. +15
+        const int sel = lch >> 1;
+        const int p = m0 + row;
+        unsigned off = kOOB;
+        if (p < a.m && sel < a.i1) {
+            const int bb = fdiv(p, a.howo_mul, a.howo_shr), hw = p - bb * HoWo;
+            off = (unsigned)((((long long)(bb - img0) * a.i1 + sel) * HoWo + hw) * 32 + (lch & 1) * 16);
+        }
+        load16_lds_stream(rsA, buf + wave * 1024, off);
+    }
+    {
+        const long long out_img = (long long)a.oc1 * HoWo * 32;
+        const v4i rsR = make_rsrc(a.res + (long long)img0 * out_img, (long long)(a.n - img0) * out_img);
+        int8_t *const Rw = buf + kChainA + wave * 4096;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = 16 * j + (lane >> 2);
+            const int k = (lane & 3) ^ swz(row);  // logical chunk: channels 64 wave + 16k .. +15
+            const int p = m0 + row;
+            const int oc = 64 * wave + 16 * k;
+            unsigned off = kOOB;
+            if (p < a.m) {
+                const int bb = fdiv(p, a.howo_mul, a.howo_shr), hw = p - bb * HoWo;
+                off = (unsigned)((((long long)(bb - img0) * a.oc1 + (oc >> 5)) * HoWo + hw) * 32 + (oc & 31));
+            }
+            load16_lds_stream(rsR, Rw + j * 1024, off);
+        }
+    }
+}
+
+// 16 weight bytes of output channel o, reduction bytes 16 kc .. +15 (zero past the input
+// channels), from the [o1][i1][o2][32] layout of a 1x1 convolution.
+__device__ __forceinline__ v4i chain_weights(const ConvArgs &q, int o, int kc)
+{
+    const int kb = kc >> 1;
+    if (kb >= q.i1) return (v4i){0, 0, 0, 0};
+    const int o1 = fdiv(o, q.o2_mul, q.o2_shr), o2i = o - o1 * q.o2;
+    return *(const v4i *)(q.wt + ((long long)(o1 * q.i1 + kb) * q.o2 + o2i) * 32 + (kc & 1) * 16);
+}
+
+// Phase 2's output channel for row r (0..15) of channel tile mt of a wave: N1 = 64 gives each
+// wave 16 consecutive channels; N1 = 128 gives it 32 (one 32-channel block) with rows ordered so
+// that accumulator row 4g + i of tiles 0 and 1 are channels 8g + i and 8g + 4 + i.
+template <int N1>
+__device__ __forceinline__ int chain_ch2(int wave, int mt, int r)
+{
+    return N1 == 64 ? 16 * wave + r : 32 * wave + 8 * (r >> 2) + 4 * mt + (r & 3);
+}
+
+template <int N1, bool RELU1>
+__global__ __launch_bounds__(256, kChainPerCu) void conv1x1_chain_kernel(ConvArgs a, ConvArgs b, int tiles)
+{
+    constexpr int MT2 = N1 / 64;  // phase-2 channel tiles per wave
+    __shared__ __attribute__((aligned(1024))) int8_t smem[kChainNB * kChainBuf];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c = lane & 15, g = lane >> 4;
+    const int ch0 = 64 * wave;  // this wave's phase-1 channels
+    const int HoWo = a.ho * a.wo;
+    const int first = blockIdx.x;
+    if (first >= tiles) return;
+    const int ntile = (tiles - 1 - first) / (int)gridDim.x + 1;
+
+    // ---- weights and parameters into registers (before any DMA, so their waits are short)
+    v4i w3[4];  // phase-1 column operand: lane (c, g), tile tn -> channel ch0 + 4c + tn, bytes 16g ..
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn) w3[tn] = chain_weights(a, ch0 + 4 * c + tn, g);
+    v4i w1[MT2][4];  // phase-2 row operand: lane (c, g), K-step s -> channel chain_ch2(c), bytes 64s + 16g ..
+#pragma unroll
+    for (int mt = 0; mt < MT2; ++mt)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) w1[mt][s] = chain_weights(b, chain_ch2<N1>(wave, mt, c), 4 * s + g);
+    RqPacked r1;
+    int mode1;
+    {
+        RqLane r;
+        mode1 = rq_setup<true, true>(r, *(const v4i *)(a.bias + ch0 + 4 * c), *(const v4i *)(a.mult + ch0 + 4 * c),
+                                     *(const v4i *)(a.shift + ch0 + 4 * c), false, ch0 + 4 * c, a.oc);
+        r1 = rq_pack(r, mode1);
+    }
+    RqPacked r2[MT2];
+    int mode2 = 1;
+    {
+        RqLane r[MT2];
+#pragma unroll
+        for (int mt = 0; mt < MT2; ++mt) {
+            const int cb = chain_ch2<N1>(wave, mt, 4 * g);  // the lane's 4 consecutive channels
+            const int md = rq_setup<false, RELU1>(r[mt], *(const v4i *)(b.bias + cb), *(const v4i *)(b.mult + cb),
+                                                  *(const v4i *)(b.shift + cb), false, cb, b.oc);
+            mode2 = (md == 0 || mode2 == 0) ? 0 : (md == 1 && mode2 == 1 ? 1 : 2);  // valid for both sets
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT2; ++mt) r2[mt] = rq_pack(r[mt], mode2);
+    }
+
+    // ---- ring prologue: tiles 0 .. kChainNB-2 (tiles past the end load zeros)
+    auto tile_m0 = [&](int j) { const int t = first + j * (int)gridDim.x; return t < tiles ? t * 64 : a.m; };
+#pragma unroll
+    for (int j = 0; j < kChainNB - 1; ++j) chain_issue(a, smem + j * kChainBuf, tile_m0(j), wave, lane);
+
+    for (int j = 0; j < ntile; ++j) {
+        int8_t *const buf = smem + (j % kChainNB) * kChainBuf;
+        const int m0 = tile_m0(j);
+        // exactly kChainNB - 2 tiles were issued after this one; loads land in issue order, so
+        // this leaves only theirs in flight (pending stores only make the wait longer)
+        wait_vmcnt<(kChainNB - 2) * kChainDma>();
+        ring_barrier();  // tile j visible to every wave; every wave is done with tile j - 1
+        chain_issue(a, smem + ((j + kChainNB - 1) % kChainNB) * kChainBuf, tile_m0(j + kChainNB - 1), wave, lane);
+
+        // ---- phase 1: conv3, 64 pixels x this wave's 64 channels, one K-step, in two halves of
+        //      32 pixels (half the accumulators live at a time)
+        int8_t *const Rw = buf + kChainA + wave * 4096;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            v4i acc[4][4];  // rows 2h, 2h+1 of the 16-row tiles used
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int tm = 2 * h + t;
+                const v4i af = *(const v4i *)(buf + swz_at(16 * tm + 4 * (c & 3) + (c >> 2), g));
+#pragma unroll
+                for (int tn = 0; tn < 4; ++tn)
+                    acc[t][tn] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, w3[tn], (v4i){0, 0, 0, 0}, 0, 0, 0);
+            }
+            // lane (g, c) holds rows 16 tm + 4 i + g, channels 4c .. 4c+3 (logical chunk c / 4 of
+            // the row); each word is read (the shortcut bytes) and overwritten (y) in place
+            auto rq = [&](auto md) __attribute__((always_inline)) {
+                constexpr int MD = decltype(md)::value;
+                unsigned rr[2][4];  // every shortcut word first: the reads overlap, not read-wait-write
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        rr[t][i] = *(const unsigned *)(Rw + swz_at(16 * (2 * h + t) + 4 * i + g, c >> 2) + 4 * (c & 3));
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        *(unsigned *)(Rw + swz_at(16 * (2 * h + t) + 4 * i + g, c >> 2) + 4 * (c & 3)) =
+                            requant_row_p<MD, true, true>(acc, t, i, r1, rr[t][i]);
+            };
+            if (mode1 == 0)
+                rq(Slot0());
+            else if (mode1 == 1)
+                rq(Slot1());
+            else
+                rq(Slot2());
+        }
+        lds_barrier();  // y complete in all four regions
+
+        // y (the block output) to HBM: the wave's region, 16-byte chunks
+        {
+            int8_t *y = (int8_t *)a.y;
+            const int k = lane & 3;
+            const int och = ch0 + 16 * k;
+            v4i v[4];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) v[jj] = *(const v4i *)(Rw + swz_at(16 * jj + (lane >> 2), k));
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int p = m0 + 16 * jj + (lane >> 2);
+                if (p < a.m) {
+                    const int bb = fdiv(p, a.howo_mul, a.howo_shr), hw = p - bb * HoWo;
+                    store16_stream(y + (((long long)bb * a.oc1 + (och >> 5)) * HoWo + hw) * 32 + (och & 31), v[jj]);
+                }
+            }
+        }
+
+        // ---- phase 2: conv1' = W1 . y^T, this wave's N1/4 channels x 64 pixels, K = 256 (the
+        //      four regions); lane (c, g) gets channels chain_ch2(4g .. 4g+3) of pixel 16 pg + c
+        v4i acc2[4][MT2];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int8_t *const Rs = buf + kChainA + s * 4096;
+#pragma unroll
+            for (int pg = 0; pg < 4; ++pg) {
+                const v4i bf = *(const v4i *)(Rs + swz_at(16 * pg + c, g));
+#pragma unroll
+                for (int mt = 0; mt < MT2; ++mt)
+                    acc2[pg][mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w1[mt][s], bf,
+                                                                         s == 0 ? (v4i){0, 0, 0, 0} : acc2[pg][mt], 0, 0, 0);
+            }
+        }
+        {
+            int8_t *t1 = (int8_t *)b.y;
+            const int cb = chain_ch2<N1>(wave, 0, 4 * g);
+            auto rq2 = [&](auto md) __attribute__((always_inline)) {
+                constexpr int MD = decltype(md)::value;
+#pragma unroll
+                for (int pg = 0; pg < 4; ++pg) {
+                    const int p = m0 + 16 * pg + c;
+                    if (p < b.m) {
+                        const int bb = fdiv(p, a.howo_mul, a.howo_shr), hw = p - bb * HoWo;
+                        int8_t *dst = t1 + (((long long)bb * b.oc1 + (cb >> 5)) * HoWo + hw) * 32 + (cb & 31);
+                        if (MT2 == 1) {
+                            *(unsigned *)dst = requant_quad_p<MD, RELU1>(acc2[pg][0], r2[0]);
+                        } else {
+                            const unsigned lo = requant_quad_p<MD, RELU1>(acc2[pg][0], r2[0]);
+                            const unsigned hi = requant_quad_p<MD, RELU1>(acc2[pg][MT2 - 1], r2[MT2 - 1]);
+                            *(uint2 *)dst = make_uint2(lo, hi);
+                        }
+                    }
+                }
+            };
+            if (mode2 == 0)
+                rq2(Slot0());
+            else if (mode2 == 1)
+                rq2(Slot1());
+            else
+                rq2(Slot2());
+        }
+    }
+    wait_vmcnt<0>();  // the ring's last (zero-fill) DMAs land before the workgroup's LDS is released
+}
+
+template <int N1>
+hipError_t launch_chain(const ConvArgs &a, const ConvArgs &b, hipStream_t s)
+{
+    if (answer_query("conv1x1_chain_kernel<%d, %s>", N1, tf(b.relu != 0))) return hipSuccess;
+    const long long tiles = (a.m + 63) / 64;
+    if (tiles <= 0) return hipSuccess;
+    if (tiles > 0x7fffffffLL / 64) return hipErrorInvalidConfiguration;
+    int cus = 0;
+    const hipError_t e = current_cus(&cus);
+    if (e != hipSuccess) return e;
+    const long long grid = tiles < (long long)kChainPerCu * cus ? tiles : (long long)kChainPerCu * cus;
+    if (b.relu)
+        hipLaunchKernelGGL((conv1x1_chain_kernel<N1, true>), dim3((unsigned)grid), dim3(256), 0, s, a, b, (int)tiles);
+    else
+        hipLaunchKernelGGL((conv1x1_chain_kernel<N1, false>), dim3((unsigned)grid), dim3(256), 0, s, a, b, (int)tiles);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 bool conv1x1_small_k_supported(const ConvArgs &a, int kh, int kw)
@@ -398,6 +675,20 @@ bool conv1x1_proj_supported(const ConvArgs &a, const ConvArgs &pj)
 hipError_t launch_conv1x1_proj(const ConvArgs &a, const ConvArgs &pj, hipStream_t s)
 {
     return a.oc1 * 32 > 64 ? launch_1x1_proj_k<128, 128>(a, pj, s) : launch_1x1_proj_k<256, 64>(a, pj, s);
+}
+
+// conv3 (a: 1x1, unit stride, K <= 64, 256 output channels, shortcut and ReLU) chained with the
+// next block's conv1 (b: 1x1, unit stride, 256 -> 64 or 128 channels, same pixels).
+bool conv1x1_chain_supported(const ConvArgs &a, const ConvArgs &b)
+{
+    return a.i1 <= 2 && a.oc == kChainC && a.stride == 1 && a.pad == 0 && a.residual && a.relu && !a.out_i32 &&
+           b.i1 * 32 == kChainC && (b.oc == 64 || b.oc == 128) && b.stride == 1 && b.pad == 0 && !b.residual &&
+           !b.out_i32 && a.m == b.m && a.ho == b.h && a.wo == b.w && a.n == b.n && b.ho == b.h && b.wo == b.w;
+}
+
+hipError_t launch_conv1x1_chain(const ConvArgs &a, const ConvArgs &b, hipStream_t s)
+{
+    return b.oc == 64 ? launch_chain<64>(a, b, s) : launch_chain<128>(a, b, s);
 }
 
 hipError_t launch_conv1x1_small_k(const ConvArgs &a, hipStream_t s)

@@ -149,6 +149,17 @@ __device__ __forceinline__ int fdiv(int n, unsigned mul, int shr)
 // pattern reaches 16 distinct 16-byte bank slots.
 __device__ __forceinline__ int swz(int row) { return ((row >> 2) ^ row) & 3; }
 
+// Compile-time tags for dispatching a wave-uniform runtime mode into template code.
+struct Slot0 {
+    static constexpr int value = 0;
+};
+struct Slot1 {
+    static constexpr int value = 1;
+};
+struct Slot2 {
+    static constexpr int value = 2;
+};
+
 // Requantisation parameters of the four output channels a lane owns.
 struct RqLane {
     int bias[4];       // added to the accumulator (modes 0 and 2; 0 when it already holds the bias)
@@ -211,6 +222,71 @@ __device__ __forceinline__ unsigned requant_row(const v4i (&acc)[4][4], int tm, 
         }
         if (RES) v += (int)(signed char)(rr >> (8 * tn));
         q[tn] = RELU ? min(max(v, 0), 127) : min(max(v, -128), 127);
+    }
+    return pack4(q[0], q[1], q[2], q[3]);
+}
+
+// The fields of the chosen mode only, 16 registers for a lane's four channels (a kernel that keeps
+// several channel sets resident across a loop cannot afford RqLane's 28):
+//   mode 0: a = bias, b = shift
+//   mode 1: (b, a) = the 64-bit addend bias*mult + 2^(30+shift) (high, low word), s = shift - 1
+//   mode 2: a = bias, b = 2^(shift-2), s = shift - 1
+// and m = mult in every mode.
+struct RqPacked {
+    int m[4], a[4], b[4], s[4];
+};
+
+__device__ __forceinline__ RqPacked rq_pack(const RqLane &r, int mode)
+{
+    RqPacked p;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        p.m[j] = r.mul[j];
+        p.a[j] = mode == 1 ? (int)(unsigned)r.add[j] : r.bias[j];
+        p.b[j] = mode == 0 ? r.shf[j] : (mode == 1 ? (int)(r.add[j] >> 32) : r.rnd[j]);
+        p.s[j] = r.shm[j];
+    }
+    return p;
+}
+
+// Channel j of a packed set applied to one accumulator (mode MODE, no clamp).
+template <int MODE>
+__device__ __forceinline__ int rq_apply(int acc, const RqPacked &p, int j)
+{
+    if (MODE == 0) return requant_any(acc + p.a[j], p.m[j], p.b[j]);
+    if (MODE == 1) {
+        const long long add = (long long)(((unsigned long long)(unsigned)p.b[j] << 32) | (unsigned)p.a[j]);
+        const long long q = (long long)acc * (long long)p.m[j] + add;
+        return ((int)(q >> 32)) >> p.s[j];
+    }
+    return requant_fast(acc + p.a[j], p.m[j], p.b[j], p.s[j]);
+}
+
+// requant_row with a packed set: the lane's 4 channels of row 16tm + 4i + g.
+template <int MODE, bool RES, bool RELU>
+__device__ __forceinline__ unsigned requant_row_p(const v4i (&acc)[4][4], int tm, int i, const RqPacked &p,
+                                                  unsigned rr)
+{
+    int q[4];
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn) {
+        int v = rq_apply<MODE>(acc[tm][tn][i], p, tn);
+        if (RES) v += (int)(signed char)(rr >> (8 * tn));
+        q[tn] = RELU ? min(max(v, 0), 127) : min(max(v, -128), 127);
+    }
+    return pack4(q[0], q[1], q[2], q[3]);
+}
+
+// Four channels of one output pixel (channel j of the set in acc[j]) requantised, no shortcut,
+// clamped (ReLU or not) and packed into one word.
+template <int MODE, bool RELU>
+__device__ __forceinline__ unsigned requant_quad_p(v4i acc, const RqPacked &p)
+{
+    int q[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int v = rq_apply<MODE>(acc[j], p, j);
+        q[j] = RELU ? min(max(v, 0), 127) : min(max(v, -128), 127);
     }
     return pack4(q[0], q[1], q[2], q[3]);
 }

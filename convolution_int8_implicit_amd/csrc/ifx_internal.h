@@ -130,6 +130,10 @@ bool conv1x1_small_k_supported(const ConvArgs &a, int kh, int kw);
 bool conv1x1_proj_supported(const ConvArgs &a, const ConvArgs &pj);
 hipError_t launch_conv1x1_proj(const ConvArgs &a, const ConvArgs &pj, hipStream_t s);
 hipError_t launch_conv1x1_small_k(const ConvArgs &a, hipStream_t s);
+// conv3 of one bottleneck (a, with its shortcut) chained with conv1 of the next (b): the block
+// output a.y is stored and conv1 reads it from LDS (conv1x1.hip)
+bool conv1x1_chain_supported(const ConvArgs &a, const ConvArgs &b);
+hipError_t launch_conv1x1_chain(const ConvArgs &a, const ConvArgs &b, hipStream_t s);
 hipError_t launch_stem(const StemArgs &a, hipStream_t s);
 hipError_t launch_avgpool(const int8_t *x, int8_t *y, int n, int c1, int hw, hipStream_t s);
 hipError_t launch_pack_act(const int8_t *x, int8_t *blk, int n, int h, int w, int c, hipStream_t s);

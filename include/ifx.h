@@ -177,6 +177,32 @@ ifx_status ifx_conv_proj_fused(const ifx_conv_desc *d3, const int8_t *t_blk, con
                                int8_t *y_blk, void *stream);
 
 /*
+ * Conv3 of one bottleneck together with conv1 of the next, as one launch (the
+ * consecutive-operator merge of the Inspur conv-merge article, section 2.1, across
+ * the block boundary of the section 2.2 structure):
+ *   y  = conv(t_blk; d3, RESIDUAL = residual_blk)    the block output, stored to y_blk
+ *   t1 = conv(y; d1)                                 the next block's conv1, stored to t1_blk
+ * y_blk is written (it is the next block's shortcut) but conv1 reads y on chip, so
+ * the block output is read once less.  The result is bit-identical to
+ * ifx_conv_fused(d3) followed by ifx_conv_fused(d1) on y_blk.
+ *   d3   1x1, stride 1, pad 0, flags IFX_RESIDUAL | IFX_RELU, c_in <= 64,
+ *        c_out = 256 (the block outputs of a ResNet-50 res2 stage)
+ *   d1   1x1, stride 1, pad 0, flags IFX_RELU or 0, c_in = d3.c_out,
+ *        c_out = 64 or 128, same n and the spatial size of d3's output
+ *   t_blk, residual_blk: packed inputs of d3; y_blk, t1_blk: packed outputs;
+ *   w3_blk, bias3, mult3, shift3 / w1_blk, bias1, mult1, shift1: as for
+ *   ifx_conv_fused.  Buffers must not overlap.  Other shapes or flags give
+ *   IFX_E_UNSUPPORTED (use two ifx_conv_fused calls); nothing is launched on an
+ *   error.  ifx_net_forward chains every block whose shortcut is its input with
+ *   the following block this way.
+ */
+ifx_status ifx_conv_chain_fused(const ifx_conv_desc *d3, const int8_t *t_blk, const int8_t *w3_blk,
+                                const int32_t *bias3, const int32_t *mult3, const int32_t *shift3,
+                                const int8_t *residual_blk, int8_t *y_blk, const ifx_conv_desc *d1,
+                                const int8_t *w1_blk, const int32_t *bias1, const int32_t *mult1,
+                                const int32_t *shift1, int8_t *t1_blk, void *stream);
+
+/*
  * Bottleneck block (Inspur conv-merge article, section 2.2):
  *   t1 = conv(x; d[0] 1x1, RELU)          c1
  *   t2 = conv(t1; d[1] 3x3 stride s, RELU) c2
@@ -332,6 +358,8 @@ ifx_status ifx_fold_bn(const ifx_bn_fold *f, int32_t *bias, int32_t *mult, int32
  */
 ifx_status ifx_conv_kernel_name(const ifx_conv_desc *d, char *buf, size_t len);
 ifx_status ifx_conv_proj_kernel_name(const ifx_conv_desc *d3, const ifx_conv_desc *dp, char *buf, size_t len);
+/* The same for ifx_conv_chain_fused(d3, d1); IFX_E_UNSUPPORTED when the pair does not chain. */
+ifx_status ifx_conv_chain_kernel_name(const ifx_conv_desc *d3, const ifx_conv_desc *d1, char *buf, size_t len);
 
 /* Host-only: a static, human-readable name of a status. */
 const char *ifx_status_string(ifx_status s);

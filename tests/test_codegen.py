@@ -52,19 +52,23 @@ def _kernel_resources(asm: str):
 
 
 @pytest.mark.skipif(HIPCC is None, reason="hipcc not available")
-def test_stem_residency_fits(tmp_path):
-    """The stem's persistent grid assumes kStemPerCu workgroups per CU: their waves must fit the
-    512 registers of a SIMD lane and their LDS the CU's 160 KB."""
-    src = os.path.join(CSRC, "stem.hip")
-    per_cu = int(re.search(r"constexpr int kStemPerCu = (\d+);", open(src).read()).group(1))
-    out = tmp_path / "stem.s"
+@pytest.mark.parametrize("src,kernel,per_cu_name", [
+    ("stem.hip", "stem_kernel", "kStemPerCu"),
+    ("conv1x1.hip", "conv1x1_chain_kernel", "kChainPerCu"),
+])
+def test_persistent_residency_fits(src, kernel, per_cu_name, tmp_path):
+    """A persistent grid sized as per_cu workgroups per CU assumes they are all resident: their
+    waves must fit the 512 registers of a SIMD lane and their LDS the CU's 160 KB."""
+    path = os.path.join(CSRC, src)
+    per_cu = int(re.search(rf"constexpr int {per_cu_name} = (\d+);", open(path).read()).group(1))
+    out = tmp_path / (src + ".s")
     cmd = [HIPCC, "-O3", "-std=c++17", "--offload-arch=gfx950", "--cuda-device-only", "-S",
            "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", src, "-o", str(out)]
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", path, "-o", str(out)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
-    res = {k: v for k, v in _kernel_resources(out.read_text()).items() if "stem_kernel" in k}
-    assert res, "no stem kernel found"
+    res = {k: v for k, v in _kernel_resources(out.read_text()).items() if kernel in k}
+    assert res, f"no {kernel} found"
     for name, f in res.items():
         waves_per_simd = per_cu * f["max_flat_workgroup_size"] // 64 // 4
         regs = f["vgpr_count"] + f.get("agpr_count", 0)

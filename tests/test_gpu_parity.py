@@ -378,6 +378,45 @@ def test_projection_block(ifx, orc, shape):
         np.testing.assert_array_equal(got, exp)
 
 
+# ------------------------------------------------------------------ conv3 chained with the next conv1
+# (n, h, w, c_in of conv3, conv1 output channels, conv1 flags): conv3 is 1x1 c_in -> 256 with
+# shortcut and ReLU, conv1 1x1 256 -> N1; pixel counts that are and are not multiples of the
+# 64-pixel tile, a padded channel block in conv3's input
+CHAIN_SHAPES = [
+    (2, 56, 56, 64, 64, 1),    # the res2.2 -> res2.3 shape
+    (1, 56, 56, 64, 128, 1),   # the res2.3 -> res3.1 shape
+    (3, 9, 7, 40, 64, 0),      # 189 pixels: a ragged last tile; conv1 without ReLU
+    (1, 5, 5, 32, 128, 0),     # one partial tile
+]
+
+
+@pytest.mark.parametrize("shape", CHAIN_SHAPES)
+def test_conv_chain_fused(ifx, orc, shape):
+    n, h, w, c3in, n1, f1 = shape
+    note(f"chain {shape}")
+    rng = np.random.default_rng(sum(shape) * 11)
+    t2 = rand(rng, (n, h, w, c3in), 0, 127)
+    res = rand(rng, (n, h, w, 256), -128, 127)
+    w3 = rand(rng, (256, 1, 1, c3in), -127, 127)
+    w1 = rand(rng, (n1, 1, 1, 256), -127, 127)
+    b3, m3, s3 = params(rng, 256, 0, 20)
+    b1, m1, s1 = params(rng, n1, 0, 20)
+    d3 = ifx.conv_desc(n, h, w, c3in, 256, 1, 1, 1, 0, ifx.RESIDUAL | ifx.RELU)
+    d1 = ifx.conv_desc(n, h, w, 256, n1, 1, 1, 1, 0, f1)
+    assert ifx.conv_chain_kernel_name(d3, d1) is not None
+    y, yw = guarded(ifx.act_bytes(n, h, w, 256))
+    t1, tw = guarded(ifx.act_bytes(n, h, w, n1))
+    ifx.conv_chain_fused(d3, ifx.pack_act(cu(t2)), ifx.pack_weights(d3, cu(w3)), cu(b3), cu(m3), cu(s3),
+                         ifx.pack_act(cu(res)), y, d1, ifx.pack_weights(d1, cu(w1)), cu(b1), cu(m1), cu(s1), t1)
+    torch.cuda.synchronize()
+    check_guards(yw)
+    check_guards(tw)
+    exp_y = orc.conv_fused(t2, w3, b3, m3, s3, 1, 0, ifx.RESIDUAL | ifx.RELU, res)
+    exp_t1 = orc.conv_fused(exp_y, w1, b1, m1, s1, 1, 0, f1)
+    np.testing.assert_array_equal(ifx.unpack_act(y.view(n, 8, h, w, 32), 256).cpu().numpy(), exp_y)
+    np.testing.assert_array_equal(ifx.unpack_act(t1.view(n, n1 // 32, h, w, 32), n1).cpu().numpy(), exp_t1)
+
+
 # ------------------------------------------------------------------ stem
 @pytest.mark.parametrize("n,h,w,c", [(2, 224, 224, 3), (1, 37, 45, 3), (3, 16, 16, 4), (1, 2, 3, 1)])
 def test_stem(ifx, orc, n, h, w, c):

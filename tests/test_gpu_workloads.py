@@ -177,11 +177,12 @@ def test_workload4_every_layer_sampled(ifx, orc):
     """Every layer of the batch-2048 network for sampled images, against the oracle's trace.
 
     ifx_net_forward runs a batch of 2048 as two concurrent passes of 1024 images.  Here the
-    same launches are issued pass by pass through the C ABI (the fused stem reading the NHWC
-    images, then ifx_block_forward per bottleneck at batch 1024, i.e. the same kernels and
-    grids, the fused conv3 + projection included), and after each layer the sampled images
-    (the first and last of the batch, one in each pass, and two more) are compared byte for
-    byte with the oracle: the pooled stem output and all 16 block outputs."""
+    driver's launches are issued pass by pass through the C ABI, with the same kernels and
+    grids: the fused stem reading the NHWC images; per bottleneck conv1 (unless the previous
+    block chained it), conv2, then conv3 fused with its projection, or chained with the next
+    block's conv1 where the library reports that pair as chainable, or alone.  After each layer
+    the sampled images (the first and last of the batch, one in each pass, and two more) are
+    compared byte for byte with the oracle: the pooled stem output and all 16 block outputs."""
     from convolution_int8_implicit_amd import model, synth
     wl = synth.workload(4)
     net = model.DeviceNet(wl.net, wl.index, nhwc_input=True)
@@ -190,36 +191,54 @@ def test_workload4_every_layer_sampled(ifx, orc):
     trace = []
     _oracle_net(orc, synth, wl, rows, trace=trace)
     half = wl.n // 2
+
+    def at(dc, n):
+        d = ifx.ConvDesc.from_buffer_copy(dc.desc)
+        d.n = n
+        return d
+
+    chained = 0
     for p0 in (0, half):
         mine = [i for i, r in enumerate(rows) if p0 <= r < p0 + half]
         local = [rows[i] - p0 for i in mine]
         note(f"pass of images {p0}..{p0 + half - 1}: sampled {[rows[i] for i in mine]}")
         x = synth.input_tensor(wl, device="cuda", rows=list(range(p0, p0 + half)))
-        sd = ifx.ConvDesc.from_buffer_copy(net.stem.desc)
-        sd.n = half
         t = model.empty_act(half, 56, 56, 64)
-        ifx.conv_fused(sd, x, net.stem.w_blk, net.stem.bias, net.stem.mult, net.stem.shift, None, t)
+        ifx.conv_fused(at(net.stem, half), x, net.stem.w_blk, net.stem.bias, net.stem.mult, net.stem.shift, None, t)
         del x
         torch.cuda.synchronize()
         got = ifx.unpack_act(t[local].contiguous(), 64).cpu().numpy()
         np.testing.assert_array_equal(got, trace[0][mine], err_msg="stem")
-        hh = ww = 56
+        t1 = None  # the block's conv1 output when the previous block chained it
         for bi, blk in enumerate(net.blocks):
-            bp = ifx.BlockParams.from_buffer_copy(blk.params)
-            for i in range(4):
-                bp.d[i].n = half
-            ws = torch.empty(ifx.block_workspace_bytes(bp), dtype=torch.int8, device="cuda")
-            c3 = blk.convs[2]
-            ho, wo = c3.out_hw
-            y = model.empty_act(half, ho, wo, c3.spec.c_out)
-            ifx.block_forward(bp, t, y, ws)
+            c1, c2, c3 = blk.convs
+            if t1 is None:
+                t1 = model.empty_act(half, *c1.out_hw, c1.spec.c_out)
+                ifx.conv_fused(at(c1, half), t, c1.w_blk, c1.bias, c1.mult, c1.shift, None, t1)
+            t2 = model.empty_act(half, *c2.out_hw, c2.spec.c_out)
+            ifx.conv_fused(at(c2, half), t1, c2.w_blk, c2.bias, c2.mult, c2.shift, None, t2)
+            y = model.empty_act(half, *c3.out_hw, c3.spec.c_out)
+            nxt = net.blocks[bi + 1].convs[0] if bi + 1 < len(net.blocks) else None
+            t1 = None
+            if blk.proj is not None:
+                pj = blk.proj
+                ifx.conv_proj_fused(at(c3, half), t2, c3.w_blk, c3.bias, c3.mult, c3.shift, at(pj, half), t,
+                                    pj.w_blk, pj.bias, pj.mult, pj.shift, y)
+            elif nxt is not None and ifx.conv_chain_kernel_name(at(c3, half), at(nxt, half)) is not None:
+                t1 = model.empty_act(half, *nxt.out_hw, nxt.spec.c_out)
+                ifx.conv_chain_fused(at(c3, half), t2, c3.w_blk, c3.bias, c3.mult, c3.shift, t, y, at(nxt, half),
+                                     nxt.w_blk, nxt.bias, nxt.mult, nxt.shift, t1)
+                chained += 1
+            else:
+                ifx.conv_fused(at(c3, half), t2, c3.w_blk, c3.bias, c3.mult, c3.shift, t, y)
             torch.cuda.synchronize()
-            del ws, t
+            del t2, t
             got = ifx.unpack_act(y[local].contiguous(), c3.spec.c_out).cpu().numpy()
             np.testing.assert_array_equal(got, trace[1 + bi][mine], err_msg=f"block {bi}")
             t = y
         del t
         torch.cuda.synchronize()
+    assert chained == 4  # res2.2 -> res2.3 and res2.3 -> res3.1, in both passes
 
 
 @pytest.mark.parametrize("n", [1, 3])
