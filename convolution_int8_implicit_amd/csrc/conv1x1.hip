@@ -657,6 +657,196 @@ hipError_t launch_chain(const ConvArgs &a, const ConvArgs &b, hipStream_t s)
     return hipGetLastError();
 }
 
+
+// ---- 1x1 with a shortcut, K <= 128, 256 or 512 output channels: persistent, ring-buffered ----
+//
+// The same layers as conv1x1_kernel (res3 conv3, the 28x28x128 -> 512 fused layer, unchained res2
+// conv3), walked by persistent workgroups the way the chained kernel walks its tiles: one wave per
+// 64 output channels holds its weights (KS x 4 x 16 bytes per lane) and parameters in registers
+// for the whole launch, and a ring of NB LDS buffers, each a 64-pixel tile's activations (KS
+// 64-byte K-steps) and shortcut (one 64 x 64-byte region per wave), keeps NB - 2 tiles of DMA in
+// flight while one is computed.  The shortcut region is requantised in place and stored from
+// there by its own wave, so a tile needs one barrier.  These layers read and write ~60 KB of HBM
+// per 64-pixel tile for ~1.5 MOP of MFMA work: the bytes in flight, not the arithmetic, set the
+// rate.
+template <int NW, int KS>
+struct RingCfg {
+    static constexpr int A = KS * 4096;           // activations: KS x [64 rows][64 B]
+    static constexpr int BUF = A + NW * 4096;     // + shortcut / output, one region per wave
+    static constexpr int PER_CU = NW == 4 ? 2 : 1;
+    static constexpr int NB = kLdsBytes / PER_CU / BUF > 4 ? 4 : kLdsBytes / PER_CU / BUF;
+    static constexpr int ADMA = KS * 4 / NW;      // activation DMAs per wave per tile
+    static constexpr int DMA = ADMA + 4;          // + four shortcut DMAs
+    static_assert(ADMA >= 1 && ADMA * NW == KS * 4, "every wave issues the same DMAs");
+    static_assert(NB >= 3, "a ring of at least three tiles");
+};
+
+template <int NW, int KS>
+__device__ __forceinline__ void ring_issue(const ConvArgs &a, int8_t *buf, int m0, int wave, int lane)
+{
+    using C = RingCfg<NW, KS>;
+    const int HoWo = a.ho * a.wo;  // = h * w: unit stride, no padding
+    const int img0 = fdiv(m0, a.howo_mul, a.howo_shr);
+    {
+        const long long in_img = (long long)a.i1 * HoWo * 32;
+        const v4i rsA = make_rsrc(a.x + (long long)img0 * in_img, (long long)(a.n - img0) * in_img);
+#pragma unroll
+        for (int j = 0; j < C::ADMA; ++j) {
+            const int q = j * NW + wave;  // 16-row group q % 4 of K-step q / 4
+            const int s = q >> 2;
+            const int row = 16 * (q & 3) + (lane >> 2);
+            const int lch = (lane & 3) ^ swz(row);
+            const int blk = 2 * s + (lch >> 1);
+            const int p = m0 + row;
+            unsigned off = kOOB;
+            if (p < a.m && blk < a.i1) {
+                const int bb = fdiv(p, a.howo_mul, a.howo_shr), hw = p - bb * HoWo;
+                off = (unsigned)((((long long)(bb - img0) * a.i1 + blk) * HoWo + hw) * 32 + (lch & 1) * 16);
+            }
+            load16_lds_stream(rsA, buf + s * 4096 + (q & 3) * 1024, off);
+        }
+    }
+    {
+        const long long out_img = (long long)a.oc1 * HoWo * 32;
+        const v4i rsR = make_rsrc(a.res + (long long)img0 * out_img, (long long)(a.n - img0) * out_img);
+        int8_t *const Rw = buf + C::A + wave * 4096;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = 16 * j + (lane >> 2);
+            const int k = (lane & 3) ^ swz(row);
+            const int p = m0 + row;
+            const int oc = 64 * wave + 16 * k;
+            unsigned off = kOOB;
+            if (p < a.m) {
+                const int bb = fdiv(p, a.howo_mul, a.howo_shr), hw = p - bb * HoWo;
+                off = (unsigned)((((long long)(bb - img0) * a.oc1 + (oc >> 5)) * HoWo + hw) * 32 + (oc & 31));
+            }
+            load16_lds_stream(rsR, Rw + j * 1024, off);
+        }
+    }
+}
+
+template <int NW, int KS, bool RELU>
+__global__ __launch_bounds__(64 * NW, (RingCfg<NW, KS>::PER_CU)) void conv1x1_ring_kernel(ConvArgs a, int tiles)
+{
+    using C = RingCfg<NW, KS>;
+    __shared__ __attribute__((aligned(1024))) int8_t smem[C::NB * C::BUF];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c = lane & 15, g = lane >> 4;
+    const int ch0 = 64 * wave;
+    const int HoWo = a.ho * a.wo;
+    const int first = blockIdx.x;
+    if (first >= tiles) return;
+    const int ntile = (tiles - 1 - first) / (int)gridDim.x + 1;
+
+    // weights (column operand: lane (c, g), tile tn -> channel ch0 + 4c + tn, K-step s bytes
+    // 64s + 16g ..) and parameters into registers, before any DMA
+    v4i w[KS][4];
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int tn = 0; tn < 4; ++tn) w[s][tn] = chain_weights(a, ch0 + 4 * c + tn, 4 * s + g);
+    RqPacked rp;
+    int mode;
+    {
+        RqLane r;
+        mode = rq_setup<true, RELU>(r, *(const v4i *)(a.bias + ch0 + 4 * c), *(const v4i *)(a.mult + ch0 + 4 * c),
+                                    *(const v4i *)(a.shift + ch0 + 4 * c), false, ch0 + 4 * c, a.oc);
+        rp = rq_pack(r, mode);
+    }
+
+    auto tile_m0 = [&](int j) { const int t = first + j * (int)gridDim.x; return t < tiles ? t * 64 : a.m; };
+#pragma unroll
+    for (int j = 0; j < C::NB - 1; ++j) ring_issue<NW, KS>(a, smem + j * C::BUF, tile_m0(j), wave, lane);
+
+    int8_t *y = (int8_t *)a.y;
+    const int k4 = lane & 3;
+    const int och = ch0 + 16 * k4;  // this lane's 16-byte output chunk
+    for (int j = 0; j < ntile; ++j) {
+        int8_t *const buf = smem + (j % C::NB) * C::BUF;
+        const int m0 = tile_m0(j);
+        wait_vmcnt<(C::NB - 2) * C::DMA>();  // tile j landed (loads complete in issue order)
+        ring_barrier();                        // ... for every wave; every wave is done with tile j - 1
+        ring_issue<NW, KS>(a, smem + ((j + C::NB - 1) % C::NB) * C::BUF, tile_m0(j + C::NB - 1), wave, lane);
+
+        int8_t *const Rw = buf + C::A + wave * 4096;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {  // two halves of 32 pixels
+            v4i acc[4][4];
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const int tm = 2 * h + t;
+                    const v4i af = *(const v4i *)(buf + s * 4096 + swz_at(16 * tm + 4 * (c & 3) + (c >> 2), g));
+#pragma unroll
+                    for (int tn = 0; tn < 4; ++tn)
+                        acc[t][tn] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, w[s][tn], s == 0 ? (v4i){0, 0, 0, 0}
+                                                                                                 : acc[t][tn], 0, 0, 0);
+                }
+            auto rq = [&](auto md) __attribute__((always_inline)) {
+                constexpr int MD = decltype(md)::value;
+                unsigned rr[2][4];
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        rr[t][i] = *(const unsigned *)(Rw + swz_at(16 * (2 * h + t) + 4 * i + g, c >> 2) + 4 * (c & 3));
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        *(unsigned *)(Rw + swz_at(16 * (2 * h + t) + 4 * i + g, c >> 2) + 4 * (c & 3)) =
+                            requant_row_p<MD, true, RELU>(acc, t, i, rp, rr[t][i]);
+            };
+            if (mode == 0)
+                rq(Slot0());
+            else if (mode == 1)
+                rq(Slot1());
+            else
+                rq(Slot2());
+        }
+        wave_lds_sync();  // the wave's own region: no other wave reads it
+        v4i v[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) v[jj] = *(const v4i *)(Rw + swz_at(16 * jj + (lane >> 2), k4));
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int p = m0 + 16 * jj + (lane >> 2);
+            if (p < a.m) {
+                const int bb = fdiv(p, a.howo_mul, a.howo_shr), hw = p - bb * HoWo;
+                store16_stream(y + (((long long)bb * a.oc1 + (och >> 5)) * HoWo + hw) * 32 + (och & 31), v[jj]);
+            }
+        }
+    }
+    wait_vmcnt<0>();  // the ring's last (zero-fill) DMAs land before the workgroup's LDS is released
+}
+
+template <int NW, int KS>
+hipError_t launch_ring(const ConvArgs &a, hipStream_t s)
+{
+    using C = RingCfg<NW, KS>;
+    if (answer_query("conv1x1_ring_kernel<%d, %d, %s>", NW, KS, tf(a.relu != 0))) return hipSuccess;
+    const long long tiles = (a.m + 63) / 64;
+    if (tiles <= 0) return hipSuccess;
+    if (tiles > 0x7fffffffLL / 64) return hipErrorInvalidConfiguration;
+    int cus = 0;
+    const hipError_t e = current_cus(&cus);
+    if (e != hipSuccess) return e;
+    const long long slots = (long long)C::PER_CU * cus;
+    const long long grid = tiles < slots ? tiles : slots;
+    if (a.relu)
+        hipLaunchKernelGGL((conv1x1_ring_kernel<NW, KS, true>), dim3((unsigned)grid), dim3(64 * NW), 0, s, a,
+                           (int)tiles);
+    else
+        hipLaunchKernelGGL((conv1x1_ring_kernel<NW, KS, false>), dim3((unsigned)grid), dim3(64 * NW), 0, s, a,
+                           (int)tiles);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 bool conv1x1_small_k_supported(const ConvArgs &a, int kh, int kw)
@@ -693,6 +883,11 @@ hipError_t launch_conv1x1_chain(const ConvArgs &a, const ConvArgs &b, hipStream_
 
 hipError_t launch_conv1x1_small_k(const ConvArgs &a, hipStream_t s)
 {
+    // unit-stride layers with a shortcut and 256 or 512 output channels: the persistent ring kernel
+    if (a.residual && a.stride == 1 && a.pad == 0 && a.ho == a.h && a.wo == a.w) {
+        if (a.oc == 256) return a.i1 <= 2 ? launch_ring<4, 1>(a, s) : launch_ring<4, 2>(a, s);
+        if (a.oc == 512 && a.i1 > 2) return launch_ring<8, 2>(a, s);
+    }
     const bool wide = a.oc1 * 32 > 64;
     if (a.i1 <= 2) return wide ? launch_1x1_res<128, 128, 1>(a, s) : launch_1x1_res<256, 64, 1>(a, s);
     return wide ? launch_1x1_res<128, 128, 2>(a, s) : launch_1x1_res<256, 64, 2>(a, s);

@@ -211,6 +211,38 @@ def test_halo_window_multi_band(ifx, orc, n, oc, flags):
     np.testing.assert_array_equal(got, orc.conv_fused(x, wt, bias, mult, shift, 1, 1, flags))
 
 
+# 1x1 layers with a shortcut, unit stride and 256 or 512 output channels run on persistent
+# workgroups (two per CU for 256 channels, one for 512) that walk 64-pixel tiles through a ring
+# of 3-4 LDS buffers.  These batches give every workgroup several tiles, more than the ring holds,
+# so the ring wraps; the small shapes leave ragged tiles spanning images.  Sampled images are
+# compared (each image's outputs depend on that image alone).
+RING_SHAPES = [
+    (100, 28, 28, 128, 512),  # the res3 conv3 shape: 1225 tiles over 256 workgroups
+    (200, 28, 28, 64, 256),   # K = 64: 2450 tiles over 512 workgroups, four-deep ring
+    (40, 56, 56, 96, 256),    # K = 96 (two K-steps, the second half zero): three-deep ring
+    (3, 7, 7, 128, 512),      # 147 pixels: tiles spanning images, a ragged last tile
+    (1, 5, 5, 32, 256),       # one partial tile, K = 32
+]
+
+
+@pytest.mark.parametrize("shape", RING_SHAPES)
+@pytest.mark.parametrize("flags", [2, 3])  # shortcut, shortcut + ReLU
+def test_ring_1x1_shortcut(ifx, orc, shape, flags):
+    n, h, w, c, oc = shape
+    note(f"ring 1x1 {shape} flags={flags}")
+    rng = np.random.default_rng(sum(shape) * 5 + flags)
+    x = rand(rng, (n, h, w, c), 0, 127)
+    wt = rand(rng, (oc, 1, 1, c), -127, 127)
+    bias, mult, shift = params(rng, oc, 0, 20)  # shifts 0-1 take the general requantisation
+    res = rand(rng, (n, h, w, oc), -128, 127)
+    d = ifx.conv_desc(n, h, w, c, oc, 1, 1, 1, 0, flags)
+    assert ifx.conv_kernel_name(d).startswith("conv1x1_ring_kernel<")
+    got = gpu_conv(ifx, x, wt, bias, mult, shift, 1, 1, 0, flags, res)
+    idx = sorted({0, n // 2, n - 1})
+    exp = orc.conv_fused(x[idx], wt, bias, mult, shift, 1, 0, flags, res[idx])
+    np.testing.assert_array_equal(got[idx], exp)
+
+
 def test_requant_edges(ifx, orc):
     """shift 0 and 1 (general path), mult 0 and 2^31-1, exact ties, negative values."""
     note("requant edges")
