@@ -239,25 +239,41 @@ def net_kernel_names(net_spec, nb: int, nhwc: bool = True) -> list:
                              spec.flags | extra)
     names = [ifx.conv_kernel_name(desc(net_spec.stem, 224, 224, ifx.INPUT_NHWC if nhwc else 0))]
     h = w = 56
-    have_t1 = False
+    have_t1 = x_even = False
     for i, b in enumerate(net_spec.blocks):
         h2 = (h + 2 - 3) // b.c2.stride + 1
         if not have_t1:
             names.append(ifx.conv_kernel_name(desc(b.c1, h, w)))
         names.append(ifx.conv_kernel_name(desc(b.c2, h, w)))
         nxt = net_spec.blocks[i + 1] if i + 1 < len(net_spec.blocks) else None
-        chain = None
+        chain, y_even = None, False
         if b.proj is None and nxt is not None:
-            chain = ifx.conv_chain_kernel_name(desc(b.c3, h2, h2), desc(nxt.c1, h2, h2))
+            y_even = reads_input_even(nxt)
+            chain = ifx.conv_chain_kernel_name(desc(b.c3, h2, h2, ifx.OUT_EVEN if y_even else 0),
+                                               desc(nxt.c1, h2, h2))
         if b.proj is not None:
-            names.append(ifx.conv_kernel_name(desc(b.c3, h2, h2), desc(b.proj, h, w)))
+            dp = desc(b.proj, h, w)
+            if x_even:
+                dp.stride, dp.h, dp.w = 1, (h + 1) // 2, (w + 1) // 2
+            if nxt is not None:
+                chain = ifx.conv_proj_chain_kernel_name(desc(b.c3, h2, h2), dp, desc(nxt.c1, h2, h2))
+            names.append(chain if chain is not None else ifx.conv_kernel_name(desc(b.c3, h2, h2), dp))
         elif chain is not None:
             names.append(chain)
         else:
             names.append(ifx.conv_kernel_name(desc(b.c3, h2, h2)))
         have_t1 = chain is not None
+        x_even = have_t1 and y_even
         h = w = h2
     return names
+
+
+def reads_input_even(block_spec) -> bool:
+    """The block's input is read only by its conv1 and a stride-2 1x1 projection: when the
+    previous block chains that conv1, the network driver stores only the input's even pixels
+    (IFX_OUT_EVEN) and runs the projection with stride 1 on them."""
+    pj = block_spec.proj
+    return pj is not None and pj.k == 1 and pj.stride == 2 and pj.pad == 0
 
 
 def cpu_baseline(workload: str, budget_s: float = 20.0):
@@ -551,12 +567,15 @@ def main():
         ops, byts, _, _ = layer_work(spec, nb_, h, w_)
         return (ifx.conv_kernel_name(dc.desc), ops, byts, fn)
 
-    def chain_launch(c3, c1n, c3spec, c1spec, nb_, h3, w3, name, fn):
+    def chain_launch(c3, c1n, c3spec, c1spec, nb_, h3, w3, name, fn, even=False):
         # conv3 + the next block's conv1 in one kernel: both contractions; conv1 reads the block
-        # output on chip, so that read is not a tensor crossing HBM
+        # output on chip, so that read is not a tensor crossing HBM; with `even` only the block
+        # output's even pixels are written
         o3, b3, oh, ow = layer_work(c3spec, nb_, h3, w3)
         o1, b1, _, _ = layer_work(c1spec, nb_, oh, ow)
-        return (name, o3 + o1, b3 + b1 - nb_ * oh * ow * c3spec.c_out, fn)
+        y_full = nb_ * oh * ow * c3spec.c_out
+        y_stored = nb_ * ((oh + 1) // 2) * ((ow + 1) // 2) * c3spec.c_out if even else y_full
+        return (name, o3 + o1, b3 - y_full + y_stored + b1 - y_full, fn)
 
     def proj_launch(c3, pj, c3spec, pspec, nb_, h3, w3, hp, wp, fn):
         # conv3 + projection in one kernel: both contractions; the shortcut is not a tensor
@@ -564,6 +583,15 @@ def main():
         op, bp, _, _ = layer_work(pspec, nb_, hp, wp)
         shortcut = nb_ * oh * ow * c3spec.c_out
         return (ifx.conv_kernel_name(c3.desc, pj.desc), o3 + op, b3 + bp - 2 * shortcut, fn)
+
+    def proj_chain_launch(c3spec, pspec, c1spec, nb_, h3, w3, hp, wp, name, fn):
+        # conv3 + projection + the next block's conv1 in one kernel: the shortcut is not a tensor,
+        # and conv1 reads the block output on chip
+        o3, b3, oh, ow = layer_work(c3spec, nb_, h3, w3)
+        op, bp, _, _ = layer_work(pspec, nb_, hp, wp)
+        o1, b1, _, _ = layer_work(c1spec, nb_, oh, ow)
+        y_full = nb_ * oh * ow * c3spec.c_out
+        return (name, o3 + op + o1, b3 + bp - 2 * y_full + b1 - y_full, fn)
 
     head_floor = 0.0
     if args.workload in ("net", "net26_b1"):
@@ -583,14 +611,22 @@ def main():
         launches.append(conv_launch(stem, wl.net.stem, nb, 224, 224, lambda: stem.run(x_blk[:nb], cur, None, stream)))
         h = ww = 56
         state = {"cur": cur, "nxt": nxt}
-        have_t1 = False
+        have_t1 = x_even = False
         for bi, (bs, db) in enumerate(zip(wl.net.blocks, net.blocks)):
             c1, c2, c3 = (with_batch(d, nb) for d in db.convs)
             pj = with_batch(db.proj, nb) if db.proj is not None else None
+            if pj is not None and x_even:  # the projection reads the subsampled block input
+                pj.desc.stride, pj.desc.h, pj.desc.w = 1, (pj.desc.h + 1) // 2, (pj.desc.w + 1) // 2
             h2 = c2.out_hw[0]
             nb_blk = net.blocks[bi + 1] if bi + 1 < len(net.blocks) else None
             c1n = with_batch(nb_blk.convs[0], nb) if nb_blk is not None else None
-            chain = ifx.conv_chain_kernel_name(c3.desc, c1n.desc) if (pj is None and c1n is not None) else None
+            y_even = nb_blk is not None and reads_input_even(wl.net.blocks[bi + 1])
+            c3c = with_batch(db.convs[2], nb)
+            if y_even:
+                c3c.desc.flags |= ifx.OUT_EVEN
+            chain = ifx.conv_chain_kernel_name(c3c.desc, c1n.desc) if (pj is None and c1n is not None) else None
+            pchain = ifx.conv_proj_chain_kernel_name(c3.desc, pj.desc, c1n.desc) \
+                if (pj is not None and c1n is not None) else None
 
             def mk(c, xin_key, out, res_key=None):
                 def f():
@@ -611,17 +647,28 @@ def main():
                                          state["nxt"], c1n_.desc, c1n_.w_blk, c1n_.bias, c1n_.mult, c1n_.shift, t1,
                                          stream)
                 return f
+            def mk_pchain(c3_, pj_, c1n_):
+                def f():
+                    ifx.conv_proj_chain_fused(c3_.desc, t2, c3_.w_blk, c3_.bias, c3_.mult, c3_.shift, pj_.desc,
+                                              state["cur"], pj_.w_blk, pj_.bias, pj_.mult, pj_.shift, state["nxt"],
+                                              c1n_.desc, c1n_.w_blk, c1n_.bias, c1n_.mult, c1n_.shift, t1, stream)
+                return f
             if not have_t1:
                 launches.append(conv_launch(c1, bs.c1, nb, h, ww, mk(c1, "cur", t1)))
             launches.append(conv_launch(c2, bs.c2, nb, h, ww, mk(c2, t1, t2)))
-            if pj is not None:
+            if pchain is not None:
+                launches.append(proj_chain_launch(bs.c3, bs.proj, wl.net.blocks[bi + 1].c1, nb, h2, h2, h, ww,
+                                                  pchain, mk_pchain(c3, pj, c1n)))
+                chain = pchain
+            elif pj is not None:
                 launches.append(proj_launch(c3, pj, bs.c3, bs.proj, nb, h2, h2, h, ww, mk_proj(c3, pj)))
             elif chain is not None:
-                launches.append(chain_launch(c3, c1n, bs.c3, wl.net.blocks[bi + 1].c1, nb, h2, h2, chain,
-                                             mk_chain(c3, c1n)))
+                launches.append(chain_launch(c3c, c1n, bs.c3, wl.net.blocks[bi + 1].c1, nb, h2, h2, chain,
+                                             mk_chain(c3c, c1n), y_even))
             else:
                 launches.append(conv_launch(c3, bs.c3, nb, h2, h2, mk(c3, t2, "nxt", "cur")))
             have_t1 = chain is not None
+            x_even = have_t1 and y_even
 
             def swap():
                 state["cur"], state["nxt"] = state["nxt"], state["cur"]

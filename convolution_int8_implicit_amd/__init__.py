@@ -21,15 +21,16 @@ from typing import Optional, Sequence
 import torch
 
 __all__ = [
-    "RELU", "RESIDUAL", "MAXPOOL", "OUT_I32", "INPUT_NHWC", "IfxError", "ConvDesc", "BlockParams", "NetParams", "lib",
+    "RELU", "RESIDUAL", "MAXPOOL", "OUT_I32", "INPUT_NHWC", "OUT_EVEN", "IfxError", "ConvDesc", "BlockParams", "NetParams", "lib",
     "conv_desc", "conv_validate", "conv_out_dims", "act_bytes", "wpack_bytes", "pack_act", "unpack_act",
-    "pack_weights", "conv_fused", "conv_chain_fused", "conv_chain_kernel_name", "conv_kernel_name",
+    "pack_weights", "conv_fused", "conv_chain_fused", "conv_chain_kernel_name", "conv_proj_chain_fused",
+    "conv_proj_chain_kernel_name", "conv_kernel_name",
     "block_workspace_bytes", "block_forward", "block_forward_noalloc",
     "BLOCK_SCRATCH_BYTES", "net_workspace_bytes",
     "net_forward", "NetGraph", "fold_bn", "BnFold", "status_string", "last_hip_error", "version", "LIB_PATH",
 ]
 
-RELU, RESIDUAL, MAXPOOL, OUT_I32, INPUT_NHWC = 1, 2, 4, 8, 16
+RELU, RESIDUAL, MAXPOOL, OUT_I32, INPUT_NHWC, OUT_EVEN = 1, 2, 4, 8, 16, 32
 STATUS = {0: "IFX_OK", 1: "IFX_E_NULL", 2: "IFX_E_SHAPE", 3: "IFX_E_UNSUPPORTED", 4: "IFX_E_ALIGN",
           5: "IFX_E_WORKSPACE", 6: "IFX_E_HIP"}
 
@@ -108,6 +109,9 @@ def lib() -> ctypes.CDLL:
         "ifx_conv_proj_kernel_name": ([D, D, ctypes.c_char_p, sz], i32),
         "ifx_conv_chain_kernel_name": ([D, D, ctypes.c_char_p, sz], i32),
         "ifx_conv_chain_fused": ([D, vp, vp, vp, vp, vp, vp, vp, D, vp, vp, vp, vp, vp, vp], i32),
+        "ifx_conv_proj_chain_kernel_name": ([D, D, D, ctypes.c_char_p, sz], i32),
+        "ifx_conv_proj_chain_fused": ([D, vp, vp, vp, vp, vp, D, vp, vp, vp, vp, vp, vp, D, vp, vp, vp, vp, vp,
+                                       vp], i32),
         "ifx_status_string": ([i32], ctypes.c_char_p),
         "ifx_probe_copy": ([vp, vp, sz, vp], i32),
         "ifx_probe_mfma_i8": ([vp, i32, i32, vp], i32),
@@ -242,6 +246,29 @@ def conv_chain_kernel_name(d3: ConvDesc, d1: ConvDesc):
     if rc == 3:
         return None
     _check(rc, "ifx_conv_chain_kernel_name")
+    return buf.value.decode()
+
+
+def conv_proj_chain_fused(d3: ConvDesc, t_blk, w3_blk, bias3, mult3, shift3, dp: ConvDesc, x_blk, wp_blk, biasp,
+                          multp, shiftp, y, d1: ConvDesc, w1_blk, bias1, mult1, shift1, t1, stream=None) -> None:
+    """conv3 with its projection shortcut and the next block's conv1 as one launch
+    (ifx_conv_proj_chain_fused)."""
+    a = (t_blk, w3_blk, bias3, mult3, shift3)
+    b = (x_blk, wp_blk, biasp, multp, shiftp, y)
+    c = (w1_blk, bias1, mult1, shift1, t1)
+    _dev(*a, *b, *c)
+    _check(lib().ifx_conv_proj_chain_fused(ctypes.byref(d3), *[_ptr(t) for t in a], ctypes.byref(dp),
+                                           *[_ptr(t) for t in b], ctypes.byref(d1), *[_ptr(t) for t in c],
+                                           _stream(stream)), "ifx_conv_proj_chain_fused")
+
+
+def conv_proj_chain_kernel_name(d3: ConvDesc, dp: ConvDesc, d1: ConvDesc):
+    """The kernel ifx_conv_proj_chain_fused(d3, dp, d1) launches, or None when they do not chain."""
+    buf = ctypes.create_string_buffer(256)
+    rc = lib().ifx_conv_proj_chain_kernel_name(ctypes.byref(d3), ctypes.byref(dp), ctypes.byref(d1), buf, len(buf))
+    if rc == 3:
+        return None
+    _check(rc, "ifx_conv_proj_chain_kernel_name")
     return buf.value.decode()
 
 

@@ -200,6 +200,7 @@ ifx::ConvArgs conv_args(const ifx_conv_desc *d, const Dims &dm, const int8_t *x,
     a.relu = (d->flags & IFX_RELU) ? 1 : 0;
     a.residual = (d->flags & IFX_RESIDUAL) ? 1 : 0;
     a.out_i32 = (d->flags & IFX_OUT_I32) ? 1 : 0;
+    a.out_even = 0;
     a.ksplit = 1;
     a.kb_per = 0;
     ifx::fastdiv_magic((unsigned)(dm.ho * dm.wo), &a.howo_mul, &a.howo_shr);
@@ -306,13 +307,37 @@ bool chain_fusable(const ifx_conv_desc *d3, const Dims &m3, const ifx_conv_desc 
     return ifx::conv1x1_chain_supported(a, b);
 }
 
+// A block whose input is read only by its conv1 and by a stride-2 1x1 projection: when the
+// previous block chains this conv1, it needs to store only the input's even rows and columns.
+bool reads_input_even(const ifx_block_params *p)
+{
+    const ifx_conv_desc &pj = p->d[3];
+    return p->has_proj && pj.kh == 1 && pj.kw == 1 && pj.stride == 2 && pj.pad == 0;
+}
+
+// A conv3 with its projection (proj_fusable) and the next block's conv1 that
+// ifx_conv_proj_chain_fused computes in one launch (descriptors already valid).
+bool proj_chain_fusable(const ifx_conv_desc *d3, const Dims &m3, const ifx_conv_desc *dp, const Dims &mp,
+                        const ifx_conv_desc *d1, const Dims &m1)
+{
+    if (!chain_fusable(d3, m3, d1, m1)) return false;
+    const ifx::ConvArgs a = conv_args(d3, m3, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
+    const ifx::ConvArgs pj = conv_args(dp, mp, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
+    const ifx::ConvArgs b = conv_args(d1, m1, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
+    return ifx::conv1x1_proj_chain_supported(a, pj, b);
+}
+
 // Launch a validated block for batch n; workspace already checked.  skip_c1: the block's conv1
-// output is already in the workspace's t1 (the previous block chained it).  next (or null): the
-// following block; when this block's conv3 chains with next's conv1, both run as one launch that
-// also leaves next's t1 in the workspace, and *chained is set.
+// output is already in the workspace's t1 (the previous block chained it).  x_even (with skip_c1
+// and a stride-2 1x1 projection only): x holds only the input's even rows and columns, and the
+// projection runs with stride 1 on it.  next (or null): the following block; when this block's
+// conv3 chains with next's conv1, both run as one launch that also leaves next's t1 in the
+// workspace, and *chained is set; if next reads its input only that way, y receives only the
+// even rows and columns and *y_even is set.
 ifx_status run_block(const ifx_block_params *p, const BlockPlan &plan, int n, const int8_t *x, int8_t *y,
                      int8_t *ws, int32_t *part, size_t part_bytes, hipStream_t s, bool skip_c1 = false,
-                     const ifx_block_params *next = nullptr, bool *chained = nullptr)
+                     const ifx_block_params *next = nullptr, bool *chained = nullptr, bool x_even = false,
+                     bool *y_even = nullptr)
 {
     ifx_conv_desc d[4];
     const int nd = p->has_proj ? 4 : 3;
@@ -321,6 +346,13 @@ ifx_status run_block(const ifx_block_params *p, const BlockPlan &plan, int n, co
         d[i].n = n;
     }
     if (chained) *chained = false;
+    if (y_even) *y_even = false;
+    if (x_even) {
+        if (!skip_c1 || !reads_input_even(p)) return IFX_E_UNSUPPORTED;
+        d[3].stride = 1;  // the same output pixels, read from the subsampled input
+        d[3].h = (d[3].h + 1) / 2;
+        d[3].w = (d[3].w + 1) / 2;
+    }
     int8_t *t1 = ws;
     int8_t *t2 = ws + plan.t1;
     int8_t *sc = ws + plan.t1 + plan.t2;
@@ -334,6 +366,24 @@ ifx_status run_block(const ifx_block_params *p, const BlockPlan &plan, int n, co
                   part, part_bytes);
     if (st != IFX_OK) return st;
     const int8_t *res = x;
+    if (p->has_proj && next && proj_fusable(&d[2], &d[3])) {
+        ifx_conv_desc d1 = next->d[0];
+        d1.n = n;
+        Dims m1;
+        if (check_desc(&d1, nullptr, &m1) == IFX_OK &&
+            proj_chain_fusable(&d[2], plan.dims[2], &d[3], plan.dims[3], &d1, m1)) {
+            // conv3, its projection and the next block's conv1 in one launch
+            const ifx::ConvArgs a = conv_args(&d[2], plan.dims[2], t2, p->w_blk[2], p->bias[2], p->mult[2],
+                                              p->shift[2], nullptr, y);
+            const ifx::ConvArgs pj = conv_args(&d[3], plan.dims[3], x, p->w_blk[3], p->bias[3], p->mult[3],
+                                               p->shift[3], nullptr, nullptr);
+            const ifx::ConvArgs b = conv_args(&d1, m1, y, next->w_blk[0], next->bias[0], next->mult[0],
+                                              next->shift[0], nullptr, t1);
+            st = hip_status(ifx::launch_conv1x1_proj_chain(a, pj, b, s));
+            if (st == IFX_OK && chained) *chained = true;
+            return st;
+        }
+    }
     if (p->has_proj) {
         if (proj_fusable(&d[2], &d[3])) {
             // conv3 and the projection in one kernel: the shortcut never goes through HBM
@@ -353,12 +403,17 @@ ifx_status run_block(const ifx_block_params *p, const BlockPlan &plan, int n, co
         Dims m1;
         if (check_desc(&d1, nullptr, &m1) == IFX_OK && chain_fusable(&d[2], plan.dims[2], &d1, m1)) {
             // conv3 and the next block's conv1 in one launch: the block output is read from LDS
-            const ifx::ConvArgs a = conv_args(&d[2], plan.dims[2], t2, p->w_blk[2], p->bias[2], p->mult[2],
-                                              p->shift[2], x, y);
+            ifx::ConvArgs a = conv_args(&d[2], plan.dims[2], t2, p->w_blk[2], p->bias[2], p->mult[2],
+                                        p->shift[2], x, y);
+            const bool even = y_even && reads_input_even(next);
+            a.out_even = even ? 1 : 0;
             const ifx::ConvArgs b = conv_args(&d1, m1, y, next->w_blk[0], next->bias[0], next->mult[0],
                                               next->shift[0], nullptr, t1);
             st = hip_status(ifx::launch_conv1x1_chain(a, b, s));
-            if (st == IFX_OK && chained) *chained = true;
+            if (st == IFX_OK) {
+                if (chained) *chained = true;
+                if (y_even) *y_even = even;
+            }
             return st;
         }
     }
@@ -513,18 +568,40 @@ hipError_t device_lane(Lane *out)
     return hipSuccess;
 }
 
-// Validation shared by ifx_conv_chain_fused and its name query.
-ifx_status check_chain(const ifx_conv_desc *d3, const ifx_conv_desc *d1, Dims *m3, Dims *m1)
+// Validation shared by ifx_conv_chain_fused and its name query.  *d3c receives d3 without
+// IFX_OUT_EVEN (a flag of this call only) and *even whether it was set.
+ifx_status check_chain(const ifx_conv_desc *d3, const ifx_conv_desc *d1, Dims *m3, Dims *m1, ifx_conv_desc *d3c,
+                       bool *even)
 {
     if (!d3 || !d1) return IFX_E_NULL;
+    *d3c = *d3;
+    *even = (d3->flags & IFX_OUT_EVEN) != 0;
+    d3c->flags &= ~(uint32_t)IFX_OUT_EVEN;
     Kind k3, k1;
-    ifx_status st = check_desc(d3, &k3, m3);
+    ifx_status st = check_desc(d3c, &k3, m3);
     if (st != IFX_OK) return st;
     st = check_desc(d1, &k1, m1);
     if (st != IFX_OK) return st;
     if (k3 != kGeneric || k1 != kGeneric) return IFX_E_UNSUPPORTED;
+    if (d1->n != d3c->n || d1->h != m3->oh || d1->w != m3->ow || d1->c_in != d3c->c_out) return IFX_E_SHAPE;
+    if (!chain_fusable(d3c, *m3, d1, *m1)) return IFX_E_UNSUPPORTED;
+    return IFX_OK;
+}
+
+// Validation shared by ifx_conv_proj_chain_fused and its name query.
+ifx_status check_proj_chain(const ifx_conv_desc *d3, const ifx_conv_desc *dp, const ifx_conv_desc *d1, Dims *m3,
+                            Dims *mp, Dims *m1)
+{
+    if (!d3 || !dp || !d1) return IFX_E_NULL;
+    Kind k3, kp, k1;
+    ifx_status st = check_desc(d3, &k3, m3);
+    if (st == IFX_OK) st = check_desc(dp, &kp, mp);
+    if (st == IFX_OK) st = check_desc(d1, &k1, m1);
+    if (st != IFX_OK) return st;
+    if (k3 != kGeneric || kp != kGeneric || k1 != kGeneric) return IFX_E_UNSUPPORTED;
+    if (dp->n != d3->n || dp->c_out != d3->c_out || mp->oh != m3->oh || mp->ow != m3->ow) return IFX_E_SHAPE;
     if (d1->n != d3->n || d1->h != m3->oh || d1->w != m3->ow || d1->c_in != d3->c_out) return IFX_E_SHAPE;
-    if (!chain_fusable(d3, *m3, d1, *m1)) return IFX_E_UNSUPPORTED;
+    if (!proj_fusable(d3, dp) || !proj_chain_fusable(d3, *m3, dp, *mp, d1, *m1)) return IFX_E_UNSUPPORTED;
     return IFX_OK;
 }
 
@@ -699,14 +776,17 @@ ifx_status ifx_conv_chain_fused(const ifx_conv_desc *d3, const int8_t *t_blk, co
                                 const int32_t *shift1, int8_t *t1_blk, void *stream)
 {
     Dims m3, m1;
-    ifx_status st = check_chain(d3, d1, &m3, &m1);
+    ifx_conv_desc d3c;
+    bool even;
+    ifx_status st = check_chain(d3, d1, &m3, &m1, &d3c, &even);
     if (st != IFX_OK) return st;
     const void *ptrs[] = {t_blk, w3_blk, bias3, mult3, shift3, residual_blk, y_blk, w1_blk, bias1, mult1, shift1, t1_blk};
     for (const void *q : ptrs)
         if (!q) return IFX_E_NULL;
     for (const void *q : ptrs)
         if (!aligned16(q)) return IFX_E_ALIGN;
-    const ifx::ConvArgs a = conv_args(d3, m3, t_blk, w3_blk, bias3, mult3, shift3, residual_blk, y_blk);
+    ifx::ConvArgs a = conv_args(&d3c, m3, t_blk, w3_blk, bias3, mult3, shift3, residual_blk, y_blk);
+    a.out_even = even ? 1 : 0;
     const ifx::ConvArgs b = conv_args(d1, m1, y_blk, w1_blk, bias1, mult1, shift1, nullptr, t1_blk);
     return hip_status(ifx::launch_conv1x1_chain(a, b, (hipStream_t)stream));
 }
@@ -714,13 +794,55 @@ ifx_status ifx_conv_chain_fused(const ifx_conv_desc *d3, const int8_t *t_blk, co
 ifx_status ifx_conv_chain_kernel_name(const ifx_conv_desc *d3, const ifx_conv_desc *d1, char *buf, size_t len)
 {
     Dims m3, m1;
-    ifx_status st = check_chain(d3, d1, &m3, &m1);
+    ifx_conv_desc d3c;
+    bool even;
+    ifx_status st = check_chain(d3, d1, &m3, &m1, &d3c, &even);
+    if (st != IFX_OK) return st;
+    if (!buf) return IFX_E_NULL;
+    ArmedQuery aq;
+    ifx::ConvArgs a = conv_args(&d3c, m3, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
+    a.out_even = even ? 1 : 0;
+    const ifx::ConvArgs b = conv_args(d1, m1, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
+    st = hip_status(ifx::launch_conv1x1_chain(a, b, nullptr));
+    if (st != IFX_OK) return st;
+    return copy_name(aq.q, buf, len);
+}
+
+ifx_status ifx_conv_proj_chain_fused(const ifx_conv_desc *d3, const int8_t *t_blk, const int8_t *w3_blk,
+                                     const int32_t *bias3, const int32_t *mult3, const int32_t *shift3,
+                                     const ifx_conv_desc *dp, const int8_t *x_blk, const int8_t *wp_blk,
+                                     const int32_t *biasp, const int32_t *multp, const int32_t *shiftp,
+                                     int8_t *y_blk, const ifx_conv_desc *d1, const int8_t *w1_blk,
+                                     const int32_t *bias1, const int32_t *mult1, const int32_t *shift1,
+                                     int8_t *t1_blk, void *stream)
+{
+    Dims m3, mp, m1;
+    ifx_status st = check_proj_chain(d3, dp, d1, &m3, &mp, &m1);
+    if (st != IFX_OK) return st;
+    const void *ptrs[] = {t_blk,  w3_blk, bias3, mult3,  shift3, x_blk, wp_blk, biasp,  multp,
+                          shiftp, y_blk,  w1_blk, bias1, mult1, shift1, t1_blk};
+    for (const void *q : ptrs)
+        if (!q) return IFX_E_NULL;
+    for (const void *q : ptrs)
+        if (!aligned16(q)) return IFX_E_ALIGN;
+    const ifx::ConvArgs a = conv_args(d3, m3, t_blk, w3_blk, bias3, mult3, shift3, nullptr, y_blk);
+    const ifx::ConvArgs pj = conv_args(dp, mp, x_blk, wp_blk, biasp, multp, shiftp, nullptr, nullptr);
+    const ifx::ConvArgs b = conv_args(d1, m1, y_blk, w1_blk, bias1, mult1, shift1, nullptr, t1_blk);
+    return hip_status(ifx::launch_conv1x1_proj_chain(a, pj, b, (hipStream_t)stream));
+}
+
+ifx_status ifx_conv_proj_chain_kernel_name(const ifx_conv_desc *d3, const ifx_conv_desc *dp,
+                                           const ifx_conv_desc *d1, char *buf, size_t len)
+{
+    Dims m3, mp, m1;
+    ifx_status st = check_proj_chain(d3, dp, d1, &m3, &mp, &m1);
     if (st != IFX_OK) return st;
     if (!buf) return IFX_E_NULL;
     ArmedQuery aq;
     const ifx::ConvArgs a = conv_args(d3, m3, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
+    const ifx::ConvArgs pj = conv_args(dp, mp, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
     const ifx::ConvArgs b = conv_args(d1, m1, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
-    st = hip_status(ifx::launch_conv1x1_chain(a, b, nullptr));
+    st = hip_status(ifx::launch_conv1x1_proj_chain(a, pj, b, nullptr));
     if (st != IFX_OK) return st;
     return copy_name(aq.q, buf, len);
 }
@@ -830,6 +952,7 @@ ifx_status run_net(const ifx_net_params *p, const NetPlan &plan, const int8_t *x
         if (st != IFX_OK) break;
         int cur = 0;
         bool have_t1 = false;  // the previous block chained this block's conv1 into t1
+        bool x_even = false;   // ... and stored only the even pixels of this block's input
         for (int b = 0; b < p->n_blocks; ++b) {
             BlockPlan bp;
             st = plan_block(&p->blocks[b], nb, &bp);
@@ -839,11 +962,12 @@ ifx_status run_net(const ifx_net_params *p, const NetPlan &plan, const int8_t *x
             lay.t1 = plan.t1;
             lay.t2 = plan.t2;
             const ifx_block_params *next = b + 1 < p->n_blocks ? &p->blocks[b + 1] : nullptr;
-            bool chained = false;
+            bool chained = false, y_even = false;
             st = run_block(&p->blocks[b], lay, nb, act[cur], act[cur ^ 1], bws, part, plan.part, s, have_t1, next,
-                           &chained);
+                           &chained, x_even, &y_even);
             if (st != IFX_OK) break;
             have_t1 = chained;
+            x_even = y_even;
             cur ^= 1;
         }
         if (st != IFX_OK) break;

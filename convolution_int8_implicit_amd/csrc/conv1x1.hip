@@ -401,54 +401,119 @@ hipError_t launch_1x1_res(const ConvArgs &a, hipStream_t s)
 //   * phase 2 multiplies with the weights as the row operand (each wave N1/4 channels x 64
 //     pixels), so a lane ends with 4 (N1 = 64) or 8 (N1 = 128) consecutive channels of one pixel
 //     and stores them straight from registers.
-constexpr int kChainC = 256;                   // block-output channels (four waves x 64)
-constexpr int kChainA = 4096;                  // a tile's conv3 activations: [64 rows][64 B]
-constexpr int kChainBuf = kChainA + 4 * 4096;  // + shortcut / y: four [64 rows][64 B] regions
-constexpr int kChainNB = 4;                    // ring depth (tiles resident in LDS)
-constexpr int kChainDma = 5;                   // DMAs per wave per tile: 1 activation, 4 shortcut
-constexpr int kChainPerCu = 2;                 // resident workgroups per CU
-static_assert(kChainNB >= 3 && kChainPerCu * kChainNB * kChainBuf <= kLdsBytes, "ring fits the LDS");
+// With PROJ the block's shortcut is its 1x1 projection (the first block of a stage, Inspur article
+// section 2.2): a slot holds the projection's input tile (64 pixels x K <= 64) instead of the
+// shortcut, each wave computes the projection of its 64 channels, requantises it (no ReLU) into
+// registers and adds it in conv3's epilogue, as the fused projection kernel does; y is staged in
+// one region after the ring (conv1' with 64 output channels only: the projection's weights and
+// parameters take the registers that 128 would need).
+constexpr int kChainC = 256;      // block-output channels (four waves x 64)
+constexpr int kChainA = 4096;     // a tile's conv3 activations (or projection input): [64 rows][64 B]
+constexpr int kChainPerCu = 2;    // resident workgroups per CU
+
+template <bool PROJ>
+struct ChainLay {
+    // slot: conv3 activations + the four shortcut / y regions; y is computed in place
+    static constexpr int SLOT = kChainA + 4 * 4096;
+    static constexpr int NB = 4;    // ring depth (tiles resident in LDS)
+    static constexpr int DMA = 5;   // DMAs per wave per tile: 1 activation, 4 shortcut
+    static constexpr int LDS = NB * SLOT;
+};
+template <>
+struct ChainLay<true> {
+    // slot: conv3 activations + projection input; y in one region after the ring
+    static constexpr int SLOT = 2 * kChainA;
+    static constexpr int NB = 6;
+    static constexpr int DMA = 2;   // 1 activation, 1 projection input
+    static constexpr int LDS = NB * SLOT + 4 * 4096;
+};
+static_assert(kChainPerCu * ChainLay<false>::LDS <= kLdsBytes && kChainPerCu * ChainLay<true>::LDS <= kLdsBytes,
+              "ring fits the LDS");
 
 // Physical LDS byte of logical 16-byte chunk k of row r in a [rows][64 B] swizzled region.
 __device__ __forceinline__ int swz_at(int r, int k) { return r * 64 + ((k ^ swz(r)) << 4); }
 
-// This wave's DMAs of the tile at pixel m0 (m0 >= a.m: every load is out of range, so the
-// buffer fills with zeros and the count of DMAs stays the same): activation rows 16 wave .. +15
-// into the buffer's first 4 KB, the shortcut bytes of channels 64 wave .. +63 into its region.
-__device__ __forceinline__ void chain_issue(const ConvArgs &a, int8_t *buf, int m0, int wave, int lane)
+// Where a 64-pixel tile starts (unit stride, so input and output pixels coincide): first pixel
+// m0, its image img0 and position hw0 in that image, the image size and the per-image byte
+// counts of a packed tensor with c1 channel blocks (c1 * HoWo * 32).  All wave-uniform.
+struct TileOrg {
+    int m0, img0, hw0, HoWo;
+};
+
+__device__ __forceinline__ TileOrg tile_org(const ConvArgs &a, int m0)
 {
-    const int HoWo = a.ho * a.wo;  // = h * w: unit stride, no padding
-    const int img0 = fdiv(m0, a.howo_mul, a.howo_shr);
-    {
-        const long long in_img = (long long)a.i1 * HoWo * 32;
-        const v4i rsA = make_rsrc(a.x + (long long)img0 * in_img, (long long)(a.n - img0) * in_img);
-        const int row = 16 * wave + (lane >> 2);
-        const int lch = (lane & 3) ^ swz(row);  // logical chunk: input channels 16 lch .. +15
-        const int sel = lch >> 1;
-        const int p = m0 + row;
-        unsigned off = kOOB;
-        if (p < a.m && sel < a.i1) {
-            const int bb = fdiv(p, a.howo_mul, a.howo_shr), hw = p - bb * HoWo;
-            off = (unsigned)((((long long)(bb - img0) * a.i1 + sel) * HoWo + hw) * 32 + (lch & 1) * 16);
+    TileOrg t;
+    t.m0 = m0;
+    t.HoWo = a.ho * a.wo;
+    t.img0 = fdiv(m0, a.howo_mul, a.howo_shr);
+    t.hw0 = m0 - t.img0 * t.HoWo;
+    return t;
+}
+
+// Pixel m0 + r (0 <= r < 64) of the tile: image img0 + d, position hw.  Images of at least 64
+// pixels take one conditional subtraction; smaller ones a short loop.
+__device__ __forceinline__ void split_px(const TileOrg &t, int r, int &d, int &hw)
+{
+    hw = t.hw0 + r;
+    d = 0;
+    if (t.HoWo >= 64) {
+        if (hw >= t.HoWo) {
+            hw -= t.HoWo;
+            d = 1;
         }
-        load16_lds_stream(rsA, buf + wave * 1024, off);
+    } else {
+        while (hw >= t.HoWo) {
+            hw -= t.HoWo;
+            ++d;
+        }
+    }
+}
+
+// Rows 16 wave .. +15 of a 64-pixel tile of q's input (K <= 64: two 32-channel blocks, zero past
+// q.i1) into a [64 rows][64 B] swizzled region: one DMA per wave.
+__device__ __forceinline__ void tile_rows_issue(const ConvArgs &q, const TileOrg &t, int8_t *dst, int wave, int lane)
+{
+    const unsigned plane = (unsigned)t.HoWo * 32;  // bytes of one 32-channel block of an image
+    const unsigned in_img = (unsigned)q.i1 * plane;
+    const v4i rs = make_rsrc(q.x + (long long)t.img0 * in_img, (long long)(q.n - t.img0) * in_img);
+    const int row = 16 * wave + (lane >> 2);
+    const int lch = (lane & 3) ^ swz(row);  // logical chunk: input channels 16 lch .. +15
+    const int sel = lch >> 1;
+    int d, hw;
+    split_px(t, row, d, hw);
+    const bool ok = t.m0 + row < q.m && sel < q.i1;
+    const unsigned off = (unsigned)d * in_img + (unsigned)sel * plane + (unsigned)hw * 32 + (lch & 1) * 16;
+    load16_lds_stream(rs, dst + wave * 1024, ok ? off : kOOB);
+}
+
+// This wave's DMAs of the tile at pixel m0 (m0 >= a.m: every load is out of range, so the
+// slot fills with zeros and the count of DMAs stays the same): conv3 activation rows 16 wave ..
+// +15 into the slot's first 4 KB, then the shortcut bytes of channels 64 wave .. +63 into the
+// wave's region or, with PROJ, the projection input's rows into the second 4 KB.
+template <bool PROJ>
+__device__ __forceinline__ void chain_issue(const ConvArgs &a, const ConvArgs &pj, int8_t *buf, int m0, int wave,
+                                            int lane)
+{
+    const TileOrg t = tile_org(a, m0);
+    const unsigned plane = (unsigned)t.HoWo * 32;
+    tile_rows_issue(a, t, buf, wave, lane);
+    if (PROJ) {
+        tile_rows_issue(pj, t, buf + kChainA, wave, lane);
+        return;
     }
     {
-        const long long out_img = (long long)a.oc1 * HoWo * 32;
-        const v4i rsR = make_rsrc(a.res + (long long)img0 * out_img, (long long)(a.n - img0) * out_img);
+        const unsigned out_img = (unsigned)a.oc1 * plane;
+        const v4i rsR = make_rsrc(a.res + (long long)t.img0 * out_img, (long long)(a.n - t.img0) * out_img);
         int8_t *const Rw = buf + kChainA + wave * 4096;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int row = 16 * j + (lane >> 2);
             const int k = (lane & 3) ^ swz(row);  // logical chunk: channels 64 wave + 16k .. +15
-            const int p = m0 + row;
             const int oc = 64 * wave + 16 * k;
-            unsigned off = kOOB;
-            if (p < a.m) {
-                const int bb = fdiv(p, a.howo_mul, a.howo_shr), hw = p - bb * HoWo;
-                off = (unsigned)((((long long)(bb - img0) * a.oc1 + (oc >> 5)) * HoWo + hw) * 32 + (oc & 31));
-            }
-            load16_lds_stream(rsR, Rw + j * 1024, off);
+            int d, hw;
+            split_px(t, row, d, hw);
+            const unsigned off = (unsigned)d * out_img + (unsigned)(oc >> 5) * plane + (unsigned)hw * 32 + (oc & 31);
+            load16_lds_stream(rsR, Rw + j * 1024, m0 + row < a.m ? off : kOOB);
         }
     }
 }
@@ -472,11 +537,13 @@ __device__ __forceinline__ int chain_ch2(int wave, int mt, int r)
     return N1 == 64 ? 16 * wave + r : 32 * wave + 8 * (r >> 2) + 4 * mt + (r & 3);
 }
 
-template <int N1, bool RELU1>
-__global__ __launch_bounds__(256, kChainPerCu) void conv1x1_chain_kernel(ConvArgs a, ConvArgs b, int tiles)
+template <int N1, bool RELU1, bool EVEN, bool PROJ>
+__global__ __launch_bounds__(256, kChainPerCu) void conv1x1_chain_kernel(ConvArgs a, ConvArgs b, ConvArgs pj,
+                                                                          int tiles)
 {
+    using L = ChainLay<PROJ>;
     constexpr int MT2 = N1 / 64;  // phase-2 channel tiles per wave
-    __shared__ __attribute__((aligned(1024))) int8_t smem[kChainNB * kChainBuf];
+    __shared__ __attribute__((aligned(1024))) int8_t smem[L::LDS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -505,6 +572,17 @@ __global__ __launch_bounds__(256, kChainPerCu) void conv1x1_chain_kernel(ConvArg
                                      *(const v4i *)(a.shift + ch0 + 4 * c), false, ch0 + 4 * c, a.oc);
         r1 = rq_pack(r, mode1);
     }
+    v4i wp[4];  // the projection's weights, as w3 (PROJ only)
+    RqPacked rpj;
+    int modep = 0;
+    if (PROJ) {
+#pragma unroll
+        for (int tn = 0; tn < 4; ++tn) wp[tn] = chain_weights(pj, ch0 + 4 * c + tn, g);
+        RqLane r;
+        modep = rq_setup<false, false>(r, *(const v4i *)(pj.bias + ch0 + 4 * c), *(const v4i *)(pj.mult + ch0 + 4 * c),
+                                       *(const v4i *)(pj.shift + ch0 + 4 * c), false, ch0 + 4 * c, pj.oc);
+        rpj = rq_pack(r, modep);
+    }
     RqPacked r2[MT2];
     int mode2 = 1;
     {
@@ -520,26 +598,61 @@ __global__ __launch_bounds__(256, kChainPerCu) void conv1x1_chain_kernel(ConvArg
         for (int mt = 0; mt < MT2; ++mt) r2[mt] = rq_pack(r[mt], mode2);
     }
 
-    // ---- ring prologue: tiles 0 .. kChainNB-2 (tiles past the end load zeros)
+    // ---- ring prologue: tiles 0 .. NB-2 (tiles past the end load zeros)
     auto tile_m0 = [&](int j) { const int t = first + j * (int)gridDim.x; return t < tiles ? t * 64 : a.m; };
 #pragma unroll
-    for (int j = 0; j < kChainNB - 1; ++j) chain_issue(a, smem + j * kChainBuf, tile_m0(j), wave, lane);
+    for (int j = 0; j < L::NB - 1; ++j) chain_issue<PROJ>(a, pj, smem + j * L::SLOT, tile_m0(j), wave, lane);
 
     for (int j = 0; j < ntile; ++j) {
-        int8_t *const buf = smem + (j % kChainNB) * kChainBuf;
+        int8_t *const buf = smem + (j % L::NB) * L::SLOT;
         const int m0 = tile_m0(j);
-        // exactly kChainNB - 2 tiles were issued after this one; loads land in issue order, so
-        // this leaves only theirs in flight (pending stores only make the wait longer)
-        wait_vmcnt<(kChainNB - 2) * kChainDma>();
+        // exactly NB - 2 tiles were issued after this one; loads land in issue order, so this
+        // leaves only theirs in flight (pending stores only make the wait longer)
+        wait_vmcnt<(L::NB - 2) * L::DMA>();
         ring_barrier();  // tile j visible to every wave; every wave is done with tile j - 1
-        chain_issue(a, smem + ((j + kChainNB - 1) % kChainNB) * kChainBuf, tile_m0(j + kChainNB - 1), wave, lane);
+        chain_issue<PROJ>(a, pj, smem + ((j + L::NB - 1) % L::NB) * L::SLOT, tile_m0(j + L::NB - 1), wave, lane);
 
         // ---- phase 1: conv3, 64 pixels x this wave's 64 channels, one K-step, in two halves of
         //      32 pixels (half the accumulators live at a time)
-        int8_t *const Rw = buf + kChainA + wave * 4096;
+        int8_t *const Rb = PROJ ? smem + L::NB * L::SLOT : buf + kChainA;  // the four y regions
+        int8_t *const Rw = Rb + wave * 4096;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             v4i acc[4][4];  // rows 2h, 2h+1 of the 16-row tiles used
+            // lane (g, c) holds rows 16 tm + 4 i + g, channels 4c .. 4c+3 (logical chunk c / 4 of
+            // the row); the shortcut words of those rows: the projection's, requantised into
+            // registers, or the DMA'd shortcut bytes, which y then overwrites in place
+            unsigned rr[2][4];
+            if (PROJ) {
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const int tm = 2 * h + t;
+                    const v4i af = *(const v4i *)(buf + kChainA + swz_at(16 * tm + 4 * (c & 3) + (c >> 2), g));
+#pragma unroll
+                    for (int tn = 0; tn < 4; ++tn)
+                        acc[t][tn] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, wp[tn], (v4i){0, 0, 0, 0}, 0, 0, 0);
+                }
+                auto rqp = [&](auto md) __attribute__((always_inline)) {
+                    constexpr int MD = decltype(md)::value;
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) rr[t][i] = requant_row_p<MD, false, false>(acc, t, i, rpj, 0u);
+                };
+                if (modep == 0)
+                    rqp(Slot0());
+                else if (modep == 1)
+                    rqp(Slot1());
+                else
+                    rqp(Slot2());
+            } else {
+                // every shortcut word first: the reads overlap, not read-wait-write
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        rr[t][i] = *(const unsigned *)(Rw + swz_at(16 * (2 * h + t) + 4 * i + g, c >> 2) + 4 * (c & 3));
+            }
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 const int tm = 2 * h + t;
@@ -548,16 +661,8 @@ __global__ __launch_bounds__(256, kChainPerCu) void conv1x1_chain_kernel(ConvArg
                 for (int tn = 0; tn < 4; ++tn)
                     acc[t][tn] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, w3[tn], (v4i){0, 0, 0, 0}, 0, 0, 0);
             }
-            // lane (g, c) holds rows 16 tm + 4 i + g, channels 4c .. 4c+3 (logical chunk c / 4 of
-            // the row); each word is read (the shortcut bytes) and overwritten (y) in place
             auto rq = [&](auto md) __attribute__((always_inline)) {
                 constexpr int MD = decltype(md)::value;
-                unsigned rr[2][4];  // every shortcut word first: the reads overlap, not read-wait-write
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        rr[t][i] = *(const unsigned *)(Rw + swz_at(16 * (2 * h + t) + 4 * i + g, c >> 2) + 4 * (c & 3));
 #pragma unroll
                 for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -574,21 +679,34 @@ __global__ __launch_bounds__(256, kChainPerCu) void conv1x1_chain_kernel(ConvArg
         }
         lds_barrier();  // y complete in all four regions
 
-        // y (the block output) to HBM: the wave's region, 16-byte chunks
+        // y (the block output) to HBM: the wave's region, 16-byte chunks; with EVEN only the
+        // pixels at even rows and columns, into a tensor of half the height and width (rounded up)
+        const TileOrg to = tile_org(a, m0);
         {
-            int8_t *y = (int8_t *)a.y;
             const int k = lane & 3;
             const int och = ch0 + 16 * k;
+            const int ho2 = (a.ho + 1) >> 1, wo2 = (a.wo + 1) >> 1;
+            const unsigned plane = (unsigned)(EVEN ? ho2 * wo2 : to.HoWo) * 32;
+            const unsigned out_img = (unsigned)a.oc1 * plane;
+            int8_t *const ybase = (int8_t *)a.y + (long long)to.img0 * out_img;
             v4i v[4];
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) v[jj] = *(const v4i *)(Rw + swz_at(16 * jj + (lane >> 2), k));
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
-                const int p = m0 + 16 * jj + (lane >> 2);
-                if (p < a.m) {
-                    const int bb = fdiv(p, a.howo_mul, a.howo_shr), hw = p - bb * HoWo;
-                    store16_stream(y + (((long long)bb * a.oc1 + (och >> 5)) * HoWo + hw) * 32 + (och & 31), v[jj]);
+                const int row = 16 * jj + (lane >> 2);
+                int d, hw;
+                split_px(to, row, d, hw);
+                bool ok = m0 + row < a.m;
+                unsigned pix = (unsigned)hw;
+                if (EVEN) {
+                    const int oy = fdiv(hw, a.wo_mul, a.wo_shr), ox = hw - oy * a.wo;
+                    ok = ok && ((oy | ox) & 1) == 0;
+                    pix = (unsigned)((oy >> 1) * wo2 + (ox >> 1));
                 }
+                if (ok)
+                    store16_stream(ybase + ((unsigned)d * out_img + (unsigned)(och >> 5) * plane + pix * 32 + (och & 31)),
+                                   v[jj]);
             }
         }
 
@@ -597,7 +715,7 @@ __global__ __launch_bounds__(256, kChainPerCu) void conv1x1_chain_kernel(ConvArg
         v4i acc2[4][MT2];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            const int8_t *const Rs = buf + kChainA + s * 4096;
+            const int8_t *const Rs = Rb + s * 4096;
 #pragma unroll
             for (int pg = 0; pg < 4; ++pg) {
                 const v4i bf = *(const v4i *)(Rs + swz_at(16 * pg + c, g));
@@ -608,16 +726,19 @@ __global__ __launch_bounds__(256, kChainPerCu) void conv1x1_chain_kernel(ConvArg
             }
         }
         {
-            int8_t *t1 = (int8_t *)b.y;
             const int cb = chain_ch2<N1>(wave, 0, 4 * g);
+            const unsigned plane = (unsigned)to.HoWo * 32;
+            const unsigned t1_img = (unsigned)b.oc1 * plane;
+            int8_t *const t1 = (int8_t *)b.y + (long long)to.img0 * t1_img + (unsigned)(cb >> 5) * plane + (cb & 31);
             auto rq2 = [&](auto md) __attribute__((always_inline)) {
                 constexpr int MD = decltype(md)::value;
 #pragma unroll
                 for (int pg = 0; pg < 4; ++pg) {
-                    const int p = m0 + 16 * pg + c;
-                    if (p < b.m) {
-                        const int bb = fdiv(p, a.howo_mul, a.howo_shr), hw = p - bb * HoWo;
-                        int8_t *dst = t1 + (((long long)bb * b.oc1 + (cb >> 5)) * HoWo + hw) * 32 + (cb & 31);
+                    const int row = 16 * pg + c;
+                    if (m0 + row < b.m) {
+                        int d, hw;
+                        split_px(to, row, d, hw);
+                        int8_t *dst = t1 + ((unsigned)d * t1_img + (unsigned)hw * 32);
                         if (MT2 == 1) {
                             *(unsigned *)dst = requant_quad_p<MD, RELU1>(acc2[pg][0], r2[0]);
                         } else {
@@ -639,22 +760,42 @@ __global__ __launch_bounds__(256, kChainPerCu) void conv1x1_chain_kernel(ConvArg
     wait_vmcnt<0>();  // the ring's last (zero-fill) DMAs land before the workgroup's LDS is released
 }
 
-template <int N1>
-hipError_t launch_chain(const ConvArgs &a, const ConvArgs &b, hipStream_t s)
+template <int N1, bool RELU1, bool EVEN, bool PROJ>
+hipError_t launch_chain_k(const ConvArgs &a, const ConvArgs &b, const ConvArgs &pj, long long tiles, hipStream_t s)
 {
-    if (answer_query("conv1x1_chain_kernel<%d, %s>", N1, tf(b.relu != 0))) return hipSuccess;
-    const long long tiles = (a.m + 63) / 64;
-    if (tiles <= 0) return hipSuccess;
-    if (tiles > 0x7fffffffLL / 64) return hipErrorInvalidConfiguration;
     int cus = 0;
     const hipError_t e = current_cus(&cus);
     if (e != hipSuccess) return e;
     const long long grid = tiles < (long long)kChainPerCu * cus ? tiles : (long long)kChainPerCu * cus;
-    if (b.relu)
-        hipLaunchKernelGGL((conv1x1_chain_kernel<N1, true>), dim3((unsigned)grid), dim3(256), 0, s, a, b, (int)tiles);
-    else
-        hipLaunchKernelGGL((conv1x1_chain_kernel<N1, false>), dim3((unsigned)grid), dim3(256), 0, s, a, b, (int)tiles);
+    hipLaunchKernelGGL((conv1x1_chain_kernel<N1, RELU1, EVEN, PROJ>), dim3((unsigned)grid), dim3(256), 0, s, a, b,
+                       pj, (int)tiles);
     return hipGetLastError();
+}
+
+// pj: the block's projection (conv3's shortcut computed in the kernel) or null (DMA'd shortcut).
+template <int N1>
+hipError_t launch_chain(const ConvArgs &a, const ConvArgs &b, const ConvArgs *pj, hipStream_t s)
+{
+    const bool relu = b.relu != 0, even = a.out_even != 0, proj = pj != nullptr;
+    if (answer_query("conv1x1_chain_kernel<%d, %s, %s, %s>", N1, tf(relu), tf(even), tf(proj))) return hipSuccess;
+    const long long tiles = (a.m + 63) / 64;
+    if (tiles <= 0) return hipSuccess;
+    if (tiles > 0x7fffffffLL / 64) return hipErrorInvalidConfiguration;
+    if (proj) {
+        // the projection's weights and parameters fit the registers beside 64 conv1 channels only
+        if constexpr (N1 == 64) {
+            if (even) return hipErrorInvalidValue;
+            return relu ? launch_chain_k<N1, true, false, true>(a, b, *pj, tiles, s)
+                        : launch_chain_k<N1, false, false, true>(a, b, *pj, tiles, s);
+        } else {
+            return hipErrorInvalidValue;
+        }
+    }
+    if (even)
+        return relu ? launch_chain_k<N1, true, true, false>(a, b, a, tiles, s)
+                    : launch_chain_k<N1, false, true, false>(a, b, a, tiles, s);
+    return relu ? launch_chain_k<N1, true, false, false>(a, b, a, tiles, s)
+                : launch_chain_k<N1, false, false, false>(a, b, a, tiles, s);
 }
 
 
@@ -685,11 +826,11 @@ template <int NW, int KS>
 __device__ __forceinline__ void ring_issue(const ConvArgs &a, int8_t *buf, int m0, int wave, int lane)
 {
     using C = RingCfg<NW, KS>;
-    const int HoWo = a.ho * a.wo;  // = h * w: unit stride, no padding
-    const int img0 = fdiv(m0, a.howo_mul, a.howo_shr);
+    const TileOrg t = tile_org(a, m0);
+    const unsigned plane = (unsigned)t.HoWo * 32;
     {
-        const long long in_img = (long long)a.i1 * HoWo * 32;
-        const v4i rsA = make_rsrc(a.x + (long long)img0 * in_img, (long long)(a.n - img0) * in_img);
+        const unsigned in_img = (unsigned)a.i1 * plane;
+        const v4i rsA = make_rsrc(a.x + (long long)t.img0 * in_img, (long long)(a.n - t.img0) * in_img);
 #pragma unroll
         for (int j = 0; j < C::ADMA; ++j) {
             const int q = j * NW + wave;  // 16-row group q % 4 of K-step q / 4
@@ -697,31 +838,26 @@ __device__ __forceinline__ void ring_issue(const ConvArgs &a, int8_t *buf, int m
             const int row = 16 * (q & 3) + (lane >> 2);
             const int lch = (lane & 3) ^ swz(row);
             const int blk = 2 * s + (lch >> 1);
-            const int p = m0 + row;
-            unsigned off = kOOB;
-            if (p < a.m && blk < a.i1) {
-                const int bb = fdiv(p, a.howo_mul, a.howo_shr), hw = p - bb * HoWo;
-                off = (unsigned)((((long long)(bb - img0) * a.i1 + blk) * HoWo + hw) * 32 + (lch & 1) * 16);
-            }
-            load16_lds_stream(rsA, buf + s * 4096 + (q & 3) * 1024, off);
+            int d, hw;
+            split_px(t, row, d, hw);
+            const bool ok = m0 + row < a.m && blk < a.i1;
+            const unsigned off = (unsigned)d * in_img + (unsigned)blk * plane + (unsigned)hw * 32 + (lch & 1) * 16;
+            load16_lds_stream(rsA, buf + s * 4096 + (q & 3) * 1024, ok ? off : kOOB);
         }
     }
     {
-        const long long out_img = (long long)a.oc1 * HoWo * 32;
-        const v4i rsR = make_rsrc(a.res + (long long)img0 * out_img, (long long)(a.n - img0) * out_img);
+        const unsigned out_img = (unsigned)a.oc1 * plane;
+        const v4i rsR = make_rsrc(a.res + (long long)t.img0 * out_img, (long long)(a.n - t.img0) * out_img);
         int8_t *const Rw = buf + C::A + wave * 4096;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int row = 16 * j + (lane >> 2);
             const int k = (lane & 3) ^ swz(row);
-            const int p = m0 + row;
             const int oc = 64 * wave + 16 * k;
-            unsigned off = kOOB;
-            if (p < a.m) {
-                const int bb = fdiv(p, a.howo_mul, a.howo_shr), hw = p - bb * HoWo;
-                off = (unsigned)((((long long)(bb - img0) * a.oc1 + (oc >> 5)) * HoWo + hw) * 32 + (oc & 31));
-            }
-            load16_lds_stream(rsR, Rw + j * 1024, off);
+            int d, hw;
+            split_px(t, row, d, hw);
+            const unsigned off = (unsigned)d * out_img + (unsigned)(oc >> 5) * plane + (unsigned)hw * 32 + (oc & 31);
+            load16_lds_stream(rsR, Rw + j * 1024, m0 + row < a.m ? off : kOOB);
         }
     }
 }
@@ -813,12 +949,17 @@ __global__ __launch_bounds__(64 * NW, (RingCfg<NW, KS>::PER_CU)) void conv1x1_ri
         v4i v[4];
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) v[jj] = *(const v4i *)(Rw + swz_at(16 * jj + (lane >> 2), k4));
+        const TileOrg to = tile_org(a, m0);
+        const unsigned plane = (unsigned)to.HoWo * 32;
+        const unsigned out_img = (unsigned)a.oc1 * plane;
+        int8_t *const ybase = y + (long long)to.img0 * out_img + (unsigned)(och >> 5) * plane + (och & 31);
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-            const int p = m0 + 16 * jj + (lane >> 2);
-            if (p < a.m) {
-                const int bb = fdiv(p, a.howo_mul, a.howo_shr), hw = p - bb * HoWo;
-                store16_stream(y + (((long long)bb * a.oc1 + (och >> 5)) * HoWo + hw) * 32 + (och & 31), v[jj]);
+            const int row = 16 * jj + (lane >> 2);
+            if (m0 + row < a.m) {
+                int d, hw;
+                split_px(to, row, d, hw);
+                store16_stream(ybase + ((unsigned)d * out_img + (unsigned)hw * 32), v[jj]);
             }
         }
     }
@@ -878,7 +1019,21 @@ bool conv1x1_chain_supported(const ConvArgs &a, const ConvArgs &b)
 
 hipError_t launch_conv1x1_chain(const ConvArgs &a, const ConvArgs &b, hipStream_t s)
 {
-    return b.oc == 64 ? launch_chain<64>(a, b, s) : launch_chain<128>(a, b, s);
+    return b.oc == 64 ? launch_chain<64>(a, b, nullptr, s) : launch_chain<128>(a, b, nullptr, s);
+}
+
+// The same with conv3's shortcut its 1x1 projection pj (unit stride, K <= 64, conv3's pixels and
+// channels, no ReLU), computed in the kernel.
+bool conv1x1_proj_chain_supported(const ConvArgs &a, const ConvArgs &pj, const ConvArgs &b)
+{
+    return conv1x1_chain_supported(a, b) && b.oc == 64 && !a.out_even && pj.i1 <= 2 && pj.oc == a.oc &&
+           pj.stride == 1 && pj.pad == 0 && !pj.relu && !pj.residual && !pj.out_i32 && pj.m == a.m &&
+           pj.ho == a.ho && pj.wo == a.wo && pj.h == a.h && pj.w == a.w && pj.n == a.n;
+}
+
+hipError_t launch_conv1x1_proj_chain(const ConvArgs &a, const ConvArgs &pj, const ConvArgs &b, hipStream_t s)
+{
+    return b.oc == 64 ? launch_chain<64>(a, b, &pj, s) : hipErrorInvalidValue;
 }
 
 hipError_t launch_conv1x1_small_k(const ConvArgs &a, hipStream_t s)

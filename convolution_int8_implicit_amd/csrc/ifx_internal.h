@@ -25,6 +25,7 @@ struct ConvArgs {
     int m;                 // n * ho * wo (GEMM rows)
     int nkb;               // kh * kw * i1 (32-wide reduction blocks)
     int relu, residual, out_i32;
+    int out_even;          // store only the even rows and columns of the output (chained conv3)
     // split-K (partial launches only): workgroup row blockIdx.y covers 32-channel blocks
     // [blockIdx.y * kb_per, +kb_per) of the reduction and writes its int32 sums, without the
     // bias, to slice blockIdx.y of y ([ksplit][m][oc]); ksplit = 1 is the whole reduction
@@ -134,6 +135,8 @@ hipError_t launch_conv1x1_small_k(const ConvArgs &a, hipStream_t s);
 // output a.y is stored and conv1 reads it from LDS (conv1x1.hip)
 bool conv1x1_chain_supported(const ConvArgs &a, const ConvArgs &b);
 hipError_t launch_conv1x1_chain(const ConvArgs &a, const ConvArgs &b, hipStream_t s);
+bool conv1x1_proj_chain_supported(const ConvArgs &a, const ConvArgs &pj, const ConvArgs &b);
+hipError_t launch_conv1x1_proj_chain(const ConvArgs &a, const ConvArgs &pj, const ConvArgs &b, hipStream_t s);
 hipError_t launch_stem(const StemArgs &a, hipStream_t s);
 hipError_t launch_avgpool(const int8_t *x, int8_t *y, int n, int c1, int hw, hipStream_t s);
 hipError_t launch_pack_act(const int8_t *x, int8_t *blk, int n, int h, int w, int c, hipStream_t s);

@@ -81,9 +81,12 @@ enum {
     IFX_RESIDUAL = 2u, /* add the shortcut tensor before ReLU */
     IFX_MAXPOOL = 4u,  /* fused 3x3/s2/p1 max-pool after ReLU (7x7/s2/p3 stem only) */
     IFX_OUT_I32 = 8u,  /* write int32 acc + bias, NHWC, no requantisation */
-    IFX_INPUT_NHWC = 16u /* stem only: the input is the compact NHWC image [n, h, w, c_in]
-                            int8 instead of the packed layout (the input pack is folded
-                            into the stem's loads) */
+    IFX_INPUT_NHWC = 16u, /* stem only: the input is the compact NHWC image [n, h, w, c_in]
+                             int8 instead of the packed layout (the input pack is folded
+                             into the stem's loads) */
+    IFX_OUT_EVEN = 32u    /* d3 of ifx_conv_chain_fused only: the block output is stored
+                             only at even rows and columns, the pixels a stride-2 1x1
+                             projection reads */
 };
 
 /*
@@ -186,7 +189,11 @@ ifx_status ifx_conv_proj_fused(const ifx_conv_desc *d3, const int8_t *t_blk, con
  * the block output is read once less.  The result is bit-identical to
  * ifx_conv_fused(d3) followed by ifx_conv_fused(d1) on y_blk.
  *   d3   1x1, stride 1, pad 0, flags IFX_RESIDUAL | IFX_RELU, c_in <= 64,
- *        c_out = 256 (the block outputs of a ResNet-50 res2 stage)
+ *        c_out = 256 (the block outputs of a ResNet-50 res2 stage); with
+ *        IFX_OUT_EVEN added, y_blk receives only the even rows and columns of y,
+ *        packed as [n, 8, ceil(h/2), ceil(w/2), 32] (what the next block's
+ *        stride-2 projection reads: it then runs with stride 1 on that tensor),
+ *        while conv1 still sees every pixel
  *   d1   1x1, stride 1, pad 0, flags IFX_RELU or 0, c_in = d3.c_out,
  *        c_out = 64 or 128, same n and the spatial size of d3's output
  *   t_blk, residual_blk: packed inputs of d3; y_blk, t1_blk: packed outputs;
@@ -194,13 +201,42 @@ ifx_status ifx_conv_proj_fused(const ifx_conv_desc *d3, const int8_t *t_blk, con
  *   ifx_conv_fused.  Buffers must not overlap.  Other shapes or flags give
  *   IFX_E_UNSUPPORTED (use two ifx_conv_fused calls); nothing is launched on an
  *   error.  ifx_net_forward chains every block whose shortcut is its input with
- *   the following block this way.
+ *   the following block this way, with IFX_OUT_EVEN when the following block has a
+ *   stride-2 projection (its only other reader of y).
  */
 ifx_status ifx_conv_chain_fused(const ifx_conv_desc *d3, const int8_t *t_blk, const int8_t *w3_blk,
                                 const int32_t *bias3, const int32_t *mult3, const int32_t *shift3,
                                 const int8_t *residual_blk, int8_t *y_blk, const ifx_conv_desc *d1,
                                 const int8_t *w1_blk, const int32_t *bias1, const int32_t *mult1,
                                 const int32_t *shift1, int8_t *t1_blk, void *stream);
+
+/*
+ * Conv3 of a bottleneck whose shortcut is a 1x1 projection, together with that
+ * projection and with conv1 of the next block, as one launch (the section 2.1
+ * merge of ifx_conv_chain_fused, for the first block of a stage):
+ *   sc = conv(x_blk; dp)                           the projection, no ReLU; not stored
+ *   y  = conv(t_blk; d3, RESIDUAL = sc)            the block output, stored to y_blk
+ *   t1 = conv(y; d1)                               the next block's conv1, stored to t1_blk
+ * Bit-identical to ifx_conv_proj_fused(d3, dp) followed by ifx_conv_fused(d1) on
+ * y_blk; conv1 reads y on chip.
+ *   d3   1x1, stride 1, pad 0, flags IFX_RESIDUAL | IFX_RELU, c_in <= 64, c_out = 256
+ *   dp   1x1, stride 1, pad 0, flags 0, c_in <= 64, c_out = d3.c_out, the same
+ *        n, h and w as d3
+ *   d1   1x1, stride 1, pad 0, flags IFX_RELU or 0, c_in = d3.c_out, c_out = 64,
+ *        the same n, h and w
+ *   Pointers as for ifx_conv_proj_fused and ifx_conv_chain_fused (device, packed,
+ *   16-byte aligned, not overlapping).  Other shapes or flags give
+ *   IFX_E_UNSUPPORTED; nothing is launched on an error.  ifx_net_forward runs the
+ *   first block of a stage with the next block's conv1 this way where it applies
+ *   (res2.1 -> res2.2 of ResNet-50).
+ */
+ifx_status ifx_conv_proj_chain_fused(const ifx_conv_desc *d3, const int8_t *t_blk, const int8_t *w3_blk,
+                                     const int32_t *bias3, const int32_t *mult3, const int32_t *shift3,
+                                     const ifx_conv_desc *dp, const int8_t *x_blk, const int8_t *wp_blk,
+                                     const int32_t *biasp, const int32_t *multp, const int32_t *shiftp,
+                                     int8_t *y_blk, const ifx_conv_desc *d1, const int8_t *w1_blk,
+                                     const int32_t *bias1, const int32_t *mult1, const int32_t *shift1,
+                                     int8_t *t1_blk, void *stream);
 
 /*
  * Bottleneck block (Inspur conv-merge article, section 2.2):
@@ -360,6 +396,9 @@ ifx_status ifx_conv_kernel_name(const ifx_conv_desc *d, char *buf, size_t len);
 ifx_status ifx_conv_proj_kernel_name(const ifx_conv_desc *d3, const ifx_conv_desc *dp, char *buf, size_t len);
 /* The same for ifx_conv_chain_fused(d3, d1); IFX_E_UNSUPPORTED when the pair does not chain. */
 ifx_status ifx_conv_chain_kernel_name(const ifx_conv_desc *d3, const ifx_conv_desc *d1, char *buf, size_t len);
+/* The same for ifx_conv_proj_chain_fused(d3, dp, d1). */
+ifx_status ifx_conv_proj_chain_kernel_name(const ifx_conv_desc *d3, const ifx_conv_desc *dp,
+                                           const ifx_conv_desc *d1, char *buf, size_t len);
 
 /* Host-only: a static, human-readable name of a status. */
 const char *ifx_status_string(ifx_status s);

@@ -50,6 +50,7 @@ def D(n=1, h=28, w=28, ci=128, co=512, k=1, s=1, p=0, f=ifx.RELU | ifx.RESIDUAL)
     (D(n=1 << 20, h=4096, w=4096), 2), (D(co=42), 3), (D(co=44), 0),
     (D(h=224, w=224, ci=3, co=64, k=7, s=2, p=3, f=ifx.RELU | ifx.MAXPOOL | ifx.INPUT_NHWC), 0),
     (D(f=ifx.RELU | ifx.INPUT_NHWC), 3), (D(k=3, p=1, f=ifx.INPUT_NHWC), 3),
+    (D(f=ifx.RELU | ifx.RESIDUAL | ifx.OUT_EVEN), 3),  # a flag of the chained call only
 ])
 def test_descriptor_validation(d, st):
     assert ifx.conv_validate(d) == st

@@ -414,17 +414,62 @@ def test_projection_block(ifx, orc, shape):
 # (n, h, w, c_in of conv3, conv1 output channels, conv1 flags): conv3 is 1x1 c_in -> 256 with
 # shortcut and ReLU, conv1 1x1 256 -> N1; pixel counts that are and are not multiples of the
 # 64-pixel tile, a padded channel block in conv3's input
+# conv3 + its projection shortcut + the next conv1 (64 channels) in one launch:
+# (n, h, w, conv3 input channels, projection input channels, conv1 flags)
+PROJ_CHAIN_SHAPES = [
+    (2, 56, 56, 64, 64, 1),    # the res2.1 -> res2.2 shape
+    (3, 9, 7, 40, 32, 0),      # ragged last tile, one-block projection input, conv1 without ReLU
+    (1, 5, 6, 64, 48, 1),      # one partial tile
+]
+
+
+@pytest.mark.parametrize("shape", PROJ_CHAIN_SHAPES)
+def test_conv_proj_chain_fused(ifx, orc, shape):
+    n, h, w, c3in, cpin, f1 = shape
+    note(f"proj chain {shape}")
+    rng = np.random.default_rng(sum(shape) * 13)
+    t2 = rand(rng, (n, h, w, c3in), 0, 127)
+    x = rand(rng, (n, h, w, cpin), 0, 127)
+    w3 = rand(rng, (256, 1, 1, c3in), -127, 127)
+    wp = rand(rng, (256, 1, 1, cpin), -127, 127)
+    w1 = rand(rng, (64, 1, 1, 256), -127, 127)
+    b3, m3, s3 = params(rng, 256, 0, 20)
+    bp, mp, sp = params(rng, 256, 0, 20)
+    b1, m1, s1 = params(rng, 64, 0, 20)
+    d3 = ifx.conv_desc(n, h, w, c3in, 256, 1, 1, 1, 0, ifx.RESIDUAL | ifx.RELU)
+    dp = ifx.conv_desc(n, h, w, cpin, 256, 1, 1, 1, 0, 0)
+    d1 = ifx.conv_desc(n, h, w, 256, 64, 1, 1, 1, 0, f1)
+    assert ifx.conv_proj_chain_kernel_name(d3, dp, d1).endswith(", true>")
+    y, yw = guarded(ifx.act_bytes(n, h, w, 256))
+    t1, tw = guarded(ifx.act_bytes(n, h, w, 64))
+    ifx.conv_proj_chain_fused(d3, ifx.pack_act(cu(t2)), ifx.pack_weights(d3, cu(w3)), cu(b3), cu(m3), cu(s3),
+                              dp, ifx.pack_act(cu(x)), ifx.pack_weights(dp, cu(wp)), cu(bp), cu(mp), cu(sp),
+                              y, d1, ifx.pack_weights(d1, cu(w1)), cu(b1), cu(m1), cu(s1), t1)
+    torch.cuda.synchronize()
+    check_guards(yw)
+    check_guards(tw)
+    sc = orc.conv_fused(x, wp, bp, mp, sp, 1, 0, 0)
+    exp_y = orc.conv_fused(t2, w3, b3, m3, s3, 1, 0, ifx.RESIDUAL | ifx.RELU, sc)
+    exp_t1 = orc.conv_fused(exp_y, w1, b1, m1, s1, 1, 0, f1)
+    np.testing.assert_array_equal(ifx.unpack_act(y.view(n, 8, h, w, 32), 256).cpu().numpy(), exp_y)
+    np.testing.assert_array_equal(ifx.unpack_act(t1.view(n, 2, h, w, 32), 64).cpu().numpy(), exp_t1)
+
+
+# (n, h, w, conv3 input channels, conv1 output channels, conv1 flags, y at even pixels only)
 CHAIN_SHAPES = [
-    (2, 56, 56, 64, 64, 1),    # the res2.2 -> res2.3 shape
-    (1, 56, 56, 64, 128, 1),   # the res2.3 -> res3.1 shape
-    (3, 9, 7, 40, 64, 0),      # 189 pixels: a ragged last tile; conv1 without ReLU
-    (1, 5, 5, 32, 128, 0),     # one partial tile
+    (2, 56, 56, 64, 64, 1, False),    # the res2.2 -> res2.3 shape
+    (1, 56, 56, 64, 128, 1, True),    # the res2.3 -> res3.1 shape (res3.1's projection has stride 2)
+    (1, 56, 56, 64, 128, 1, False),
+    (3, 9, 7, 40, 64, 0, False),      # 189 pixels: a ragged last tile; conv1 without ReLU
+    (3, 9, 7, 40, 128, 1, True),      # odd height and width: the last row and column are even
+    (1, 5, 5, 32, 128, 0, False),     # one partial tile
+    (2, 6, 10, 64, 64, 0, True),      # even sizes, tiles spanning images
 ]
 
 
 @pytest.mark.parametrize("shape", CHAIN_SHAPES)
 def test_conv_chain_fused(ifx, orc, shape):
-    n, h, w, c3in, n1, f1 = shape
+    n, h, w, c3in, n1, f1, even = shape
     note(f"chain {shape}")
     rng = np.random.default_rng(sum(shape) * 11)
     t2 = rand(rng, (n, h, w, c3in), 0, 127)
@@ -433,19 +478,22 @@ def test_conv_chain_fused(ifx, orc, shape):
     w1 = rand(rng, (n1, 1, 1, 256), -127, 127)
     b3, m3, s3 = params(rng, 256, 0, 20)
     b1, m1, s1 = params(rng, n1, 0, 20)
-    d3 = ifx.conv_desc(n, h, w, c3in, 256, 1, 1, 1, 0, ifx.RESIDUAL | ifx.RELU)
+    d3p = ifx.conv_desc(n, h, w, c3in, 256, 1, 1, 1, 0, ifx.RESIDUAL | ifx.RELU)  # for the weight pack
+    d3 = ifx.conv_desc(n, h, w, c3in, 256, 1, 1, 1, 0, ifx.RESIDUAL | ifx.RELU | (ifx.OUT_EVEN if even else 0))
     d1 = ifx.conv_desc(n, h, w, 256, n1, 1, 1, 1, 0, f1)
-    assert ifx.conv_chain_kernel_name(d3, d1) is not None
-    y, yw = guarded(ifx.act_bytes(n, h, w, 256))
+    assert ifx.conv_chain_kernel_name(d3, d1).endswith(", true, false>" if even else ", false, false>")
+    hy, wy = ((h + 1) // 2, (w + 1) // 2) if even else (h, w)
+    y, yw = guarded(ifx.act_bytes(n, hy, wy, 256))
     t1, tw = guarded(ifx.act_bytes(n, h, w, n1))
-    ifx.conv_chain_fused(d3, ifx.pack_act(cu(t2)), ifx.pack_weights(d3, cu(w3)), cu(b3), cu(m3), cu(s3),
+    ifx.conv_chain_fused(d3, ifx.pack_act(cu(t2)), ifx.pack_weights(d3p, cu(w3)), cu(b3), cu(m3), cu(s3),
                          ifx.pack_act(cu(res)), y, d1, ifx.pack_weights(d1, cu(w1)), cu(b1), cu(m1), cu(s1), t1)
     torch.cuda.synchronize()
     check_guards(yw)
     check_guards(tw)
     exp_y = orc.conv_fused(t2, w3, b3, m3, s3, 1, 0, ifx.RESIDUAL | ifx.RELU, res)
     exp_t1 = orc.conv_fused(exp_y, w1, b1, m1, s1, 1, 0, f1)
-    np.testing.assert_array_equal(ifx.unpack_act(y.view(n, 8, h, w, 32), 256).cpu().numpy(), exp_y)
+    got_y = ifx.unpack_act(y.view(n, 8, hy, wy, 32), 256).cpu().numpy()
+    np.testing.assert_array_equal(got_y, exp_y[:, ::2, ::2] if even else exp_y)
     np.testing.assert_array_equal(ifx.unpack_act(t1.view(n, n1 // 32, h, w, 32), n1).cpu().numpy(), exp_t1)
 
 
