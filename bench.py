@@ -237,26 +237,33 @@ def net_kernel_names(net_spec, nb: int, nhwc: bool = True) -> list:
     def desc(spec, h, w, extra=0):
         return ifx.conv_desc(nb, h, w, spec.c_in, spec.c_out, spec.k, spec.k, spec.stride, spec.pad,
                              spec.flags | extra)
+    def phase_in_ok(spec, h, w):  # a stride-2 3x3 reading conv1's phase-split output (the driver's rule)
+        return spec.k == 3 and spec.stride == 2 and spec.pad == 1 and h % 2 == 0 and w % 2 == 0 \
+            and ifx.conv_validate(desc(spec, h, w, ifx.IN_PHASE)) == 0
+
     names = [ifx.conv_kernel_name(desc(net_spec.stem, 224, 224, ifx.INPUT_NHWC if nhwc else 0))]
     h = w = 56
-    have_t1 = x_even = False
+    have_t1 = x_even = t1_ps = False
     for i, b in enumerate(net_spec.blocks):
         h2 = (h + 2 - 3) // b.c2.stride + 1
         if not have_t1:
-            names.append(ifx.conv_kernel_name(desc(b.c1, h, w)))
-        names.append(ifx.conv_kernel_name(desc(b.c2, h, w)))
+            t1_ps = phase_in_ok(b.c2, h, w) and ifx.conv_validate(desc(b.c1, h, w, ifx.OUT_PHASE)) == 0
+            names.append(ifx.conv_kernel_name(desc(b.c1, h, w, ifx.OUT_PHASE if t1_ps else 0)))
+        names.append(ifx.conv_kernel_name(desc(b.c2, h, w, ifx.IN_PHASE if t1_ps else 0)))
         nxt = net_spec.blocks[i + 1] if i + 1 < len(net_spec.blocks) else None
         chain, y_even = None, False
+        nps = nxt is not None and phase_in_ok(nxt.c2, h2, h2)  # chained conv1 writes phase-split
         if b.proj is None and nxt is not None:
             y_even = reads_input_even(nxt)
             chain = ifx.conv_chain_kernel_name(desc(b.c3, h2, h2, ifx.OUT_EVEN if y_even else 0),
-                                               desc(nxt.c1, h2, h2))
+                                               desc(nxt.c1, h2, h2, ifx.OUT_PHASE if nps else 0))
         if b.proj is not None:
             dp = desc(b.proj, h, w)
             if x_even:
                 dp.stride, dp.h, dp.w = 1, (h + 1) // 2, (w + 1) // 2
             if nxt is not None:
-                chain = ifx.conv_proj_chain_kernel_name(desc(b.c3, h2, h2), dp, desc(nxt.c1, h2, h2))
+                chain = ifx.conv_proj_chain_kernel_name(desc(b.c3, h2, h2), dp,
+                                                        desc(nxt.c1, h2, h2, ifx.OUT_PHASE if nps else 0))
             names.append(chain if chain is not None else ifx.conv_kernel_name(desc(b.c3, h2, h2), dp))
         elif chain is not None:
             names.append(chain)
@@ -264,6 +271,7 @@ def net_kernel_names(net_spec, nb: int, nhwc: bool = True) -> list:
             names.append(ifx.conv_kernel_name(desc(b.c3, h2, h2)))
         have_t1 = chain is not None
         x_even = have_t1 and y_even
+        t1_ps = have_t1 and nps
         h = w = h2
     return names
 
@@ -611,15 +619,32 @@ def main():
         launches.append(conv_launch(stem, wl.net.stem, nb, 224, 224, lambda: stem.run(x_blk[:nb], cur, None, stream)))
         h = ww = 56
         state = {"cur": cur, "nxt": nxt}
-        have_t1 = x_even = False
+        have_t1 = x_even = t1_ps = False
+
+        def phase_in_ok(d):  # a stride-2 3x3 reading the phase-split layout (the driver's rule)
+            q = ifx.ConvDesc.from_buffer_copy(d)
+            q.flags |= ifx.IN_PHASE
+            return d.kh == 3 and d.stride == 2 and d.pad == 1 and d.h % 2 == 0 and d.w % 2 == 0 \
+                and ifx.conv_validate(q) == 0
+
         for bi, (bs, db) in enumerate(zip(wl.net.blocks, net.blocks)):
             c1, c2, c3 = (with_batch(d, nb) for d in db.convs)
+            if not have_t1:  # conv1 launched on its own: phase-split output for a stride-2 conv2
+                q = ifx.ConvDesc.from_buffer_copy(c1.desc)
+                q.flags |= ifx.OUT_PHASE
+                t1_ps = phase_in_ok(c2.desc) and ifx.conv_validate(q) == 0
+                if t1_ps:
+                    c1.desc.flags |= ifx.OUT_PHASE
+            if t1_ps:
+                c2.desc.flags |= ifx.IN_PHASE
             pj = with_batch(db.proj, nb) if db.proj is not None else None
             if pj is not None and x_even:  # the projection reads the subsampled block input
                 pj.desc.stride, pj.desc.h, pj.desc.w = 1, (pj.desc.h + 1) // 2, (pj.desc.w + 1) // 2
             h2 = c2.out_hw[0]
             nb_blk = net.blocks[bi + 1] if bi + 1 < len(net.blocks) else None
             c1n = with_batch(nb_blk.convs[0], nb) if nb_blk is not None else None
+            if c1n is not None and phase_in_ok(with_batch(nb_blk.convs[1], nb).desc):
+                c1n.desc.flags |= ifx.OUT_PHASE
             y_even = nb_blk is not None and reads_input_even(wl.net.blocks[bi + 1])
             c3c = with_batch(db.convs[2], nb)
             if y_even:
@@ -669,6 +694,7 @@ def main():
                 launches.append(conv_launch(c3, bs.c3, nb, h2, h2, mk(c3, t2, "nxt", "cur")))
             have_t1 = chain is not None
             x_even = have_t1 and y_even
+            t1_ps = have_t1 and bool(c1n.desc.flags & ifx.OUT_PHASE)
 
             def swap():
                 state["cur"], state["nxt"] = state["nxt"], state["cur"]

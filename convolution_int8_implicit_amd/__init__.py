@@ -21,7 +21,7 @@ from typing import Optional, Sequence
 import torch
 
 __all__ = [
-    "RELU", "RESIDUAL", "MAXPOOL", "OUT_I32", "INPUT_NHWC", "OUT_EVEN", "IfxError", "ConvDesc", "BlockParams", "NetParams", "lib",
+    "RELU", "RESIDUAL", "MAXPOOL", "OUT_I32", "INPUT_NHWC", "OUT_EVEN", "OUT_PHASE", "IN_PHASE", "IfxError", "ConvDesc", "BlockParams", "NetParams", "lib",
     "conv_desc", "conv_validate", "conv_out_dims", "act_bytes", "wpack_bytes", "pack_act", "unpack_act",
     "pack_weights", "conv_fused", "conv_chain_fused", "conv_chain_kernel_name", "conv_proj_chain_fused",
     "conv_proj_chain_kernel_name", "conv_kernel_name",
@@ -30,7 +30,7 @@ __all__ = [
     "net_forward", "NetGraph", "fold_bn", "BnFold", "status_string", "last_hip_error", "version", "LIB_PATH",
 ]
 
-RELU, RESIDUAL, MAXPOOL, OUT_I32, INPUT_NHWC, OUT_EVEN = 1, 2, 4, 8, 16, 32
+RELU, RESIDUAL, MAXPOOL, OUT_I32, INPUT_NHWC, OUT_EVEN, OUT_PHASE, IN_PHASE = 1, 2, 4, 8, 16, 32, 64, 128
 STATUS = {0: "IFX_OK", 1: "IFX_E_NULL", 2: "IFX_E_SHAPE", 3: "IFX_E_UNSUPPORTED", 4: "IFX_E_ALIGN",
           5: "IFX_E_WORKSPACE", 6: "IFX_E_HIP"}
 

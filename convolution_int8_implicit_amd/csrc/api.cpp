@@ -84,6 +84,9 @@ struct Dims {
     int oh, ow;   // tensor written (pooled when MAXPOOL)
 };
 
+ifx::ConvArgs conv_args(const ifx_conv_desc *d, const Dims &dm, const int8_t *x, const int8_t *w, const int32_t *bias,
+                        const int32_t *mult, const int32_t *shift, const int8_t *res, void *y);
+
 ifx_status check_desc(const ifx_conv_desc *d, Kind *kind, Dims *dims)
 {
     if (!d) return IFX_E_NULL;
@@ -91,7 +94,8 @@ ifx_status check_desc(const ifx_conv_desc *d, Kind *kind, Dims *dims)
         d->stride <= 0 || d->pad < 0)
         return IFX_E_SHAPE;
     const uint32_t f = d->flags;
-    if (f & ~(uint32_t)(IFX_RELU | IFX_RESIDUAL | IFX_MAXPOOL | IFX_OUT_I32 | IFX_INPUT_NHWC))
+    if (f & ~(uint32_t)(IFX_RELU | IFX_RESIDUAL | IFX_MAXPOOL | IFX_OUT_I32 | IFX_INPUT_NHWC | IFX_OUT_PHASE |
+                        IFX_IN_PHASE))
         return IFX_E_UNSUPPORTED;
     Dims dm;
     dm.ho = out_dim(d->h, d->kh, d->stride, d->pad);
@@ -121,6 +125,11 @@ ifx_status check_desc(const ifx_conv_desc *d, Kind *kind, Dims *dims)
     if ((long long)d->n * dm.ho * dm.wo > 0x7fffffffLL || (long long)d->n * d->h * d->w > 0x7fffffffLL ||
         (long long)d->c_out * 16 > 0x7fffffffLL)
         return IFX_E_SHAPE;
+    if (f & (IFX_OUT_PHASE | IFX_IN_PHASE)) {  // the general kernel's phase-split layout
+        if (k != kGeneric) return IFX_E_UNSUPPORTED;
+        const ifx::ConvArgs a = conv_args(d, dm, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
+        if (!ifx::conv_phase_supported(a, kh, kw)) return IFX_E_UNSUPPORTED;
+    }
     if (kind) *kind = k;
     if (dims) *dims = dm;
     return IFX_OK;
@@ -201,6 +210,8 @@ ifx::ConvArgs conv_args(const ifx_conv_desc *d, const Dims &dm, const int8_t *x,
     a.residual = (d->flags & IFX_RESIDUAL) ? 1 : 0;
     a.out_i32 = (d->flags & IFX_OUT_I32) ? 1 : 0;
     a.out_even = 0;
+    a.in_ps = (d->flags & IFX_IN_PHASE) ? 1 : 0;
+    a.out_ps = (d->flags & IFX_OUT_PHASE) ? 1 : 0;
     a.ksplit = 1;
     a.kb_per = 0;
     ifx::fastdiv_magic((unsigned)(dm.ho * dm.wo), &a.howo_mul, &a.howo_shr);
@@ -250,6 +261,8 @@ ifx_status plan_block(const ifx_block_params *p, int n, BlockPlan *plan)
         if (plan->kind[i] != kGeneric) return IFX_E_UNSUPPORTED;
         if (d[i].flags & IFX_OUT_I32) return IFX_E_UNSUPPORTED;
     }
+    for (int i = 0; i < nd; ++i)  // layouts between a block's convolutions are the driver's choice
+        if (d[i].flags & (IFX_OUT_PHASE | IFX_IN_PHASE)) return IFX_E_UNSUPPORTED;
     if (!flags_plain(d[0].flags) || !flags_plain(d[1].flags)) return IFX_E_UNSUPPORTED;
     if (!(d[2].flags & IFX_RESIDUAL) || (d[2].flags & (IFX_MAXPOOL | IFX_OUT_I32))) return IFX_E_UNSUPPORTED;
     if (p->has_proj && !flags_plain(d[3].flags)) return IFX_E_UNSUPPORTED;
@@ -300,7 +313,7 @@ bool chain_fusable(const ifx_conv_desc *d3, const Dims &m3, const ifx_conv_desc 
 {
     if (d3->kh != 1 || d3->kw != 1 || d3->stride != 1 || d3->pad != 0) return false;
     if (d1->kh != 1 || d1->kw != 1 || d1->stride != 1 || d1->pad != 0) return false;
-    if (d3->flags != (IFX_RESIDUAL | IFX_RELU) || (d1->flags & ~(uint32_t)IFX_RELU)) return false;
+    if (d3->flags != (IFX_RESIDUAL | IFX_RELU) || (d1->flags & ~(uint32_t)(IFX_RELU | IFX_OUT_PHASE))) return false;
     if (d1->n != d3->n || d1->h != m3.oh || d1->w != m3.ow || d1->c_in != d3->c_out) return false;
     const ifx::ConvArgs a = conv_args(d3, m3, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
     const ifx::ConvArgs b = conv_args(d1, m1, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
@@ -327,17 +340,38 @@ bool proj_chain_fusable(const ifx_conv_desc *d3, const Dims &m3, const ifx_conv_
     return ifx::conv1x1_proj_chain_supported(a, pj, b);
 }
 
-// Launch a validated block for batch n; workspace already checked.  skip_c1: the block's conv1
-// output is already in the workspace's t1 (the previous block chained it).  x_even (with skip_c1
-// and a stride-2 1x1 projection only): x holds only the input's even rows and columns, and the
-// projection runs with stride 1 on it.  next (or null): the following block; when this block's
+// How one block of a network hands data to the next.  In (for this block): its conv1 output is
+// already in t1 (the previous block chained it), possibly phase-split, and its input x holds only
+// the even pixels.  Out (for the next block): the same three facts about what this block left.
+struct BlockFlow {
+    bool have_t1 = false, t1_ps = false, x_even = false;
+};
+
+// A stride-2 pad-1 3x3 on even sizes whose kernel reads the phase-split layout.
+bool phase_in_ok(const ifx_conv_desc &d)
+{
+    if (!(d.kh == 3 && d.kw == 3 && d.stride == 2 && d.pad == 1 && !(d.h & 1) && !(d.w & 1))) return false;
+    ifx_conv_desc q = d;
+    q.flags |= IFX_IN_PHASE;
+    return check_desc(&q, nullptr, nullptr) == IFX_OK;
+}
+
+// The same convolution as a launch of its own writing the phase-split layout.
+bool phase_out_ok(const ifx_conv_desc &d)
+{
+    ifx_conv_desc q = d;
+    q.flags |= IFX_OUT_PHASE;
+    return check_desc(&q, nullptr, nullptr) == IFX_OK;
+}
+
+// Launch a validated block for batch n; workspace already checked.  `in` describes what the
+// previous block left (see BlockFlow).  next (or null): the following block; when this block's
 // conv3 chains with next's conv1, both run as one launch that also leaves next's t1 in the
-// workspace, and *chained is set; if next reads its input only that way, y receives only the
-// even rows and columns and *y_even is set.
+// workspace (phase-split when next's conv2 reads it so), and y receives only the even pixels if
+// next reads its input only through its conv1 and a stride-2 projection; *out says so.
 ifx_status run_block(const ifx_block_params *p, const BlockPlan &plan, int n, const int8_t *x, int8_t *y,
-                     int8_t *ws, int32_t *part, size_t part_bytes, hipStream_t s, bool skip_c1 = false,
-                     const ifx_block_params *next = nullptr, bool *chained = nullptr, bool x_even = false,
-                     bool *y_even = nullptr)
+                     int8_t *ws, int32_t *part, size_t part_bytes, hipStream_t s, const BlockFlow &in = BlockFlow(),
+                     const ifx_block_params *next = nullptr, BlockFlow *out = nullptr)
 {
     ifx_conv_desc d[4];
     const int nd = p->has_proj ? 4 : 3;
@@ -345,19 +379,27 @@ ifx_status run_block(const ifx_block_params *p, const BlockPlan &plan, int n, co
         d[i] = p->d[i];
         d[i].n = n;
     }
-    if (chained) *chained = false;
-    if (y_even) *y_even = false;
-    if (x_even) {
-        if (!skip_c1 || !reads_input_even(p)) return IFX_E_UNSUPPORTED;
+    if (out) *out = BlockFlow();
+    if (in.x_even) {
+        if (!in.have_t1 || !reads_input_even(p)) return IFX_E_UNSUPPORTED;
         d[3].stride = 1;  // the same output pixels, read from the subsampled input
         d[3].h = (d[3].h + 1) / 2;
         d[3].w = (d[3].w + 1) / 2;
     }
+    // t1 between conv1 and a stride-2 conv2 goes phase-split when both kernels handle it
+    bool t1_ps;
+    if (in.have_t1) {
+        t1_ps = in.t1_ps;
+    } else {
+        t1_ps = phase_in_ok(d[1]) && phase_out_ok(d[0]);
+        if (t1_ps) d[0].flags |= IFX_OUT_PHASE;
+    }
+    if (t1_ps) d[1].flags |= IFX_IN_PHASE;
     int8_t *t1 = ws;
     int8_t *t2 = ws + plan.t1;
     int8_t *sc = ws + plan.t1 + plan.t2;
     ifx_status st;
-    if (!skip_c1) {
+    if (!in.have_t1) {
         st = run_conv(&d[0], kGeneric, plan.dims[0], x, p->w_blk[0], p->bias[0], p->mult[0], p->shift[0], nullptr, t1,
                       s, part, part_bytes);
         if (st != IFX_OK) return st;
@@ -365,24 +407,36 @@ ifx_status run_block(const ifx_block_params *p, const BlockPlan &plan, int n, co
     st = run_conv(&d[1], kGeneric, plan.dims[1], t1, p->w_blk[1], p->bias[1], p->mult[1], p->shift[1], nullptr, t2, s,
                   part, part_bytes);
     if (st != IFX_OK) return st;
-    const int8_t *res = x;
-    if (p->has_proj && next && proj_fusable(&d[2], &d[3])) {
-        ifx_conv_desc d1 = next->d[0];
+    // next's conv1 descriptor when this block could chain it (phase-split for a stride-2 conv2)
+    ifx_conv_desc d1;
+    Dims m1;
+    bool can_chain = false;
+    if (next) {
+        d1 = next->d[0];
         d1.n = n;
-        Dims m1;
-        if (check_desc(&d1, nullptr, &m1) == IFX_OK &&
-            proj_chain_fusable(&d[2], plan.dims[2], &d[3], plan.dims[3], &d1, m1)) {
-            // conv3, its projection and the next block's conv1 in one launch
-            const ifx::ConvArgs a = conv_args(&d[2], plan.dims[2], t2, p->w_blk[2], p->bias[2], p->mult[2],
-                                              p->shift[2], nullptr, y);
-            const ifx::ConvArgs pj = conv_args(&d[3], plan.dims[3], x, p->w_blk[3], p->bias[3], p->mult[3],
-                                               p->shift[3], nullptr, nullptr);
-            const ifx::ConvArgs b = conv_args(&d1, m1, y, next->w_blk[0], next->bias[0], next->mult[0],
-                                              next->shift[0], nullptr, t1);
-            st = hip_status(ifx::launch_conv1x1_proj_chain(a, pj, b, s));
-            if (st == IFX_OK && chained) *chained = true;
-            return st;
+        can_chain = check_desc(&d1, nullptr, &m1) == IFX_OK;
+        if (can_chain) {
+            ifx_conv_desc nd1 = next->d[1];
+            nd1.n = n;
+            if (phase_in_ok(nd1)) d1.flags |= IFX_OUT_PHASE;
         }
+    }
+    const int8_t *res = x;
+    if (p->has_proj && can_chain && proj_fusable(&d[2], &d[3]) &&
+        proj_chain_fusable(&d[2], plan.dims[2], &d[3], plan.dims[3], &d1, m1)) {
+        // conv3, its projection and the next block's conv1 in one launch
+        const ifx::ConvArgs a = conv_args(&d[2], plan.dims[2], t2, p->w_blk[2], p->bias[2], p->mult[2], p->shift[2],
+                                          nullptr, y);
+        const ifx::ConvArgs pj = conv_args(&d[3], plan.dims[3], x, p->w_blk[3], p->bias[3], p->mult[3], p->shift[3],
+                                           nullptr, nullptr);
+        const ifx::ConvArgs b = conv_args(&d1, m1, y, next->w_blk[0], next->bias[0], next->mult[0], next->shift[0],
+                                          nullptr, t1);
+        st = hip_status(ifx::launch_conv1x1_proj_chain(a, pj, b, s));
+        if (st == IFX_OK && out) {
+            out->have_t1 = true;
+            out->t1_ps = b.out_ps != 0;
+        }
+        return st;
     }
     if (p->has_proj) {
         if (proj_fusable(&d[2], &d[3])) {
@@ -397,25 +451,20 @@ ifx_status run_block(const ifx_block_params *p, const BlockPlan &plan, int n, co
                       sc, s, part, part_bytes);
         if (st != IFX_OK) return st;
         res = sc;
-    } else if (next) {
-        ifx_conv_desc d1 = next->d[0];
-        d1.n = n;
-        Dims m1;
-        if (check_desc(&d1, nullptr, &m1) == IFX_OK && chain_fusable(&d[2], plan.dims[2], &d1, m1)) {
-            // conv3 and the next block's conv1 in one launch: the block output is read from LDS
-            ifx::ConvArgs a = conv_args(&d[2], plan.dims[2], t2, p->w_blk[2], p->bias[2], p->mult[2],
-                                        p->shift[2], x, y);
-            const bool even = y_even && reads_input_even(next);
-            a.out_even = even ? 1 : 0;
-            const ifx::ConvArgs b = conv_args(&d1, m1, y, next->w_blk[0], next->bias[0], next->mult[0],
-                                              next->shift[0], nullptr, t1);
-            st = hip_status(ifx::launch_conv1x1_chain(a, b, s));
-            if (st == IFX_OK) {
-                if (chained) *chained = true;
-                if (y_even) *y_even = even;
-            }
-            return st;
+    } else if (can_chain && chain_fusable(&d[2], plan.dims[2], &d1, m1)) {
+        // conv3 and the next block's conv1 in one launch: the block output is read from LDS
+        ifx::ConvArgs a = conv_args(&d[2], plan.dims[2], t2, p->w_blk[2], p->bias[2], p->mult[2], p->shift[2], x, y);
+        const bool even = reads_input_even(next);
+        a.out_even = even ? 1 : 0;
+        const ifx::ConvArgs b = conv_args(&d1, m1, y, next->w_blk[0], next->bias[0], next->mult[0], next->shift[0],
+                                          nullptr, t1);
+        st = hip_status(ifx::launch_conv1x1_chain(a, b, s));
+        if (st == IFX_OK && out) {
+            out->have_t1 = true;
+            out->t1_ps = b.out_ps != 0;
+            out->x_even = even;
         }
+        return st;
     }
     return run_conv(&d[2], kGeneric, plan.dims[2], t2, p->w_blk[2], p->bias[2], p->mult[2], p->shift[2], res, y, s,
                     part, part_bytes);
@@ -951,8 +1000,7 @@ ifx_status run_net(const ifx_net_params *p, const NetPlan &plan, const int8_t *x
                       nullptr, act[0], s);
         if (st != IFX_OK) break;
         int cur = 0;
-        bool have_t1 = false;  // the previous block chained this block's conv1 into t1
-        bool x_even = false;   // ... and stored only the even pixels of this block's input
+        BlockFlow flow;  // what the previous block left for this one
         for (int b = 0; b < p->n_blocks; ++b) {
             BlockPlan bp;
             st = plan_block(&p->blocks[b], nb, &bp);
@@ -962,12 +1010,11 @@ ifx_status run_net(const ifx_net_params *p, const NetPlan &plan, const int8_t *x
             lay.t1 = plan.t1;
             lay.t2 = plan.t2;
             const ifx_block_params *next = b + 1 < p->n_blocks ? &p->blocks[b + 1] : nullptr;
-            bool chained = false, y_even = false;
-            st = run_block(&p->blocks[b], lay, nb, act[cur], act[cur ^ 1], bws, part, plan.part, s, have_t1, next,
-                           &chained, x_even, &y_even);
+            BlockFlow left;
+            st = run_block(&p->blocks[b], lay, nb, act[cur], act[cur ^ 1], bws, part, plan.part, s, flow, next,
+                           &left);
             if (st != IFX_OK) break;
-            have_t1 = chained;
-            x_even = y_even;
+            flow = left;
             cur ^= 1;
         }
         if (st != IFX_OK) break;

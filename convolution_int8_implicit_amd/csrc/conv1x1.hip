@@ -738,7 +738,13 @@ __global__ __launch_bounds__(256, kChainPerCu) void conv1x1_chain_kernel(ConvArg
                     if (m0 + row < b.m) {
                         int d, hw;
                         split_px(to, row, d, hw);
-                        int8_t *dst = t1 + ((unsigned)d * t1_img + (unsigned)hw * 32);
+                        unsigned pix = (unsigned)hw;
+                        if (b.out_ps) {  // phase-split t1: the pixel's parity plane, then its place
+                            const int oy = fdiv(hw, a.wo_mul, a.wo_shr), ox = hw - oy * a.wo;
+                            pix = (unsigned)(((oy & 1) * 2 + (ox & 1)) * (to.HoWo >> 2) + (oy >> 1) * (a.wo >> 1) +
+                                             (ox >> 1));
+                        }
+                        int8_t *dst = t1 + ((unsigned)d * t1_img + pix * 32);
                         if (MT2 == 1) {
                             *(unsigned *)dst = requant_quad_p<MD, RELU1>(acc2[pg][0], r2[0]);
                         } else {
@@ -1012,6 +1018,7 @@ hipError_t launch_conv1x1_proj(const ConvArgs &a, const ConvArgs &pj, hipStream_
 // next block's conv1 (b: 1x1, unit stride, 256 -> 64 or 128 channels, same pixels).
 bool conv1x1_chain_supported(const ConvArgs &a, const ConvArgs &b)
 {
+    if (a.in_ps || a.out_ps || b.in_ps || (b.out_ps && ((b.ho | b.wo) & 1))) return false;
     return a.i1 <= 2 && a.oc == kChainC && a.stride == 1 && a.pad == 0 && a.residual && a.relu && !a.out_i32 &&
            b.i1 * 32 == kChainC && (b.oc == 64 || b.oc == 128) && b.stride == 1 && b.pad == 0 && !b.residual &&
            !b.out_i32 && a.m == b.m && a.ho == b.h && a.wo == b.w && a.n == b.n && b.ho == b.h && b.wo == b.w;
@@ -1026,7 +1033,8 @@ hipError_t launch_conv1x1_chain(const ConvArgs &a, const ConvArgs &b, hipStream_
 // channels, no ReLU), computed in the kernel.
 bool conv1x1_proj_chain_supported(const ConvArgs &a, const ConvArgs &pj, const ConvArgs &b)
 {
-    return conv1x1_chain_supported(a, b) && b.oc == 64 && !a.out_even && pj.i1 <= 2 && pj.oc == a.oc &&
+    return conv1x1_chain_supported(a, b) && b.oc == 64 && !a.out_even && !pj.in_ps && !pj.out_ps && pj.i1 <= 2 &&
+           pj.oc == a.oc &&
            pj.stride == 1 && pj.pad == 0 && !pj.relu && !pj.residual && !pj.out_i32 && pj.m == a.m &&
            pj.ho == a.ho && pj.wo == a.wo && pj.h == a.h && pj.w == a.w && pj.n == a.n;
 }

@@ -26,6 +26,9 @@ struct ConvArgs {
     int nkb;               // kh * kw * i1 (32-wide reduction blocks)
     int relu, residual, out_i32;
     int out_even;          // store only the even rows and columns of the output (chained conv3)
+    // phase-split layout [n][c1][2][2][h/2][w/2][32] (even sizes): plane (y % 2, x % 2) holds the
+    // pixels of that row and column parity, so a stride-2 3x3 reads contiguous runs for every tap
+    int in_ps, out_ps;
     // split-K (partial launches only): workgroup row blockIdx.y covers 32-channel blocks
     // [blockIdx.y * kb_per, +kb_per) of the reduction and writes its int32 sums, without the
     // bias, to slice blockIdx.y of y ([ksplit][m][oc]); ksplit = 1 is the whole reduction
@@ -114,6 +117,9 @@ struct FoldArgs {
 };
 
 hipError_t launch_conv(const ConvArgs &a, int kh, int kw, hipStream_t s);
+// Whether the kernel launch_conv_split picks for `a` honours a.in_ps / a.out_ps (the general
+// kernel does; a launch it would split over K is not given a phase-split output).
+bool conv_phase_supported(const ConvArgs &a, int kh, int kw);
 // Bytes of int32 partial sums launch_conv_split would use for `a` (0: it would not split).  A
 // convolution on few output tiles with a long reduction is split over workgroups along K.
 size_t splitk_bytes(const ConvArgs &a, int kh, int kw);

@@ -84,10 +84,25 @@ enum {
     IFX_INPUT_NHWC = 16u, /* stem only: the input is the compact NHWC image [n, h, w, c_in]
                              int8 instead of the packed layout (the input pack is folded
                              into the stem's loads) */
-    IFX_OUT_EVEN = 32u    /* d3 of ifx_conv_chain_fused only: the block output is stored
+    IFX_OUT_EVEN = 32u,   /* d3 of ifx_conv_chain_fused only: the block output is stored
                              only at even rows and columns, the pixels a stride-2 1x1
                              projection reads */
+    IFX_OUT_PHASE = 64u,  /* the output is stored phase-split (layout below; even Ho, Wo) */
+    IFX_IN_PHASE = 128u   /* 3x3 stride 2 pad 1 only: the input is phase-split (even H, W) */
 };
+
+/*
+ * Phase-split layout of a packed tensor with even height and width:
+ * [N, C1, 2, 2, H/2, W/2, 32], plane (py, px) holding the pixels (2i + py, 2j + px).
+ * The same bytes as [N, C1, H, W, 32], permuted so that every tap of a stride-2 3x3
+ * convolution reads runs of consecutive pixels (a plain layout gives it 32-byte
+ * pieces 64 bytes apart).  The flags are accepted only where the general
+ * implicit-GEMM kernel runs the convolution and would not split it over K
+ * (ifx_conv_validate answers IFX_E_UNSUPPORTED for the stem, the small-K 1x1
+ * and haloed 3x3 shapes, IFX_OUT_I32 and odd sizes); the shortcut and the output
+ * keep the plain layout unless IFX_OUT_PHASE.  ifx_net_forward uses the layout
+ * between conv1 and a stride-2 conv2 of a bottleneck.
+ */
 
 /*
  * One convolution.  Supported (kh, kw, stride, pad):

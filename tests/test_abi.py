@@ -51,6 +51,12 @@ def D(n=1, h=28, w=28, ci=128, co=512, k=1, s=1, p=0, f=ifx.RELU | ifx.RESIDUAL)
     (D(h=224, w=224, ci=3, co=64, k=7, s=2, p=3, f=ifx.RELU | ifx.MAXPOOL | ifx.INPUT_NHWC), 0),
     (D(f=ifx.RELU | ifx.INPUT_NHWC), 3), (D(k=3, p=1, f=ifx.INPUT_NHWC), 3),
     (D(f=ifx.RELU | ifx.RESIDUAL | ifx.OUT_EVEN), 3),  # a flag of the chained call only
+    # phase-split layouts: the general kernel only, even sizes, never with int32 output
+    (D(ci=512, co=256, f=ifx.RELU | ifx.OUT_PHASE), 0), (D(ci=128, f=ifx.RELU | ifx.OUT_PHASE), 3),
+    (D(ci=512, h=27, w=28, f=ifx.OUT_PHASE), 3), (D(ci=512, f=ifx.OUT_I32 | ifx.OUT_PHASE), 3),
+    (D(ci=256, co=256, k=3, s=2, p=1, f=ifx.IN_PHASE), 0), (D(ci=256, k=3, s=1, p=1, f=ifx.IN_PHASE), 3),
+    (D(ci=256, h=27, k=3, s=2, p=1, f=ifx.IN_PHASE), 3), (D(ci=256, k=1, s=2, f=ifx.IN_PHASE), 3),
+    (D(ci=64, co=64, h=56, w=56, k=3, s=1, p=1, f=ifx.OUT_PHASE), 3),  # the haloed 3x3
 ])
 def test_descriptor_validation(d, st):
     assert ifx.conv_validate(d) == st

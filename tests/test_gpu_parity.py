@@ -82,6 +82,17 @@ def gpu_conv(ifx, x, w, bias, mult, shift, k, s, p, flags, residual=None, check_
     return ifx.unpack_act(y, oc).cpu().numpy()
 
 
+def to_phase(t):
+    """Packed [n, c1, h, w, 32] -> phase-split [n, c1, 2, 2, h/2, w/2, 32] (ifx.h's permutation)."""
+    n, c1, h, w, _ = t.shape
+    return t.view(n, c1, h // 2, 2, w // 2, 2, 32).permute(0, 1, 3, 5, 2, 4, 6).contiguous()
+
+
+def from_phase(t, n, c1, h, w):
+    """Phase-split bytes -> packed [n, c1, h, w, 32]."""
+    return t.view(n, c1, 2, 2, h // 2, w // 2, 32).permute(0, 1, 4, 2, 5, 3, 6).reshape(n, c1, h, w, 32)
+
+
 def params(rng, oc, shift_lo=8, shift_hi=16):
     return (rand(rng, oc, -(1 << 16), 1 << 16, np.int32), rand(rng, oc, 1 << 30, (1 << 31) - 1, np.int32),
             rand(rng, oc, shift_lo, shift_hi, np.int32))
@@ -241,6 +252,66 @@ def test_ring_1x1_shortcut(ifx, orc, shape, flags):
     idx = sorted({0, n // 2, n - 1})
     exp = orc.conv_fused(x[idx], wt, bias, mult, shift, 1, 0, flags, res[idx])
     np.testing.assert_array_equal(got[idx], exp)
+
+
+# The phase-split layout between a bottleneck's conv1 and its stride-2 conv2: conv1 (the general
+# kernel: 1x1 with K > 128, or a 3x3) stores its output as four parity planes, and the stride-2 3x3
+# reads them, each tap a run of consecutive pixels.  Outputs are compared after undoing the
+# permutation; inputs are permuted from the plain packed tensor.
+PHASE_OUT_SHAPES = [
+    (2, 28, 28, 512, 256, 1, 1, 0),   # res4.1 conv1
+    (3, 14, 14, 1024, 512, 1, 1, 0),  # res5.1 conv1, 3 images of 196 pixels across tiles
+    (2, 10, 6, 160, 200, 1, 1, 0),    # ragged channels, 5 input blocks
+    (1, 12, 8, 96, 64, 3, 1, 1),      # a 3x3 producer (256x64 tiles)
+]
+PHASE_IN_SHAPES = [
+    (2, 28, 28, 256, 256, 3, 2, 1),   # res4.1 conv2 (128x256 tiles)
+    (2, 56, 56, 128, 128, 3, 2, 1),   # res3.1 conv2
+    (3, 14, 14, 512, 512, 3, 2, 1),   # res5.1 conv2: 7x7 outputs
+    (1, 10, 6, 96, 72, 3, 2, 1),      # odd output width, ragged channels
+]
+
+
+@pytest.mark.parametrize("shape", PHASE_OUT_SHAPES)
+@pytest.mark.parametrize("flags", [0, 1])
+def test_phase_split_output(ifx, orc, shape, flags):
+    n, h, w, c, oc, k, s, p = shape
+    note(f"phase-split output {shape} flags={flags}")
+    rng = np.random.default_rng(sum(shape) + 3 * flags)
+    x = rand(rng, (n, h, w, c), 0, 127)
+    wt = rand(rng, (oc, k, k, c), -127, 127)
+    bias, mult, shift = params(rng, oc)
+    d = ifx.conv_desc(n, h, w, c, oc, k, k, s, p, flags | ifx.OUT_PHASE)
+    ho, wo = ifx.conv_out_dims(d)
+    c1 = (oc + 31) // 32
+    y, whole = guarded(ifx.act_bytes(n, ho, wo, oc))
+    dp = ifx.conv_desc(n, h, w, c, oc, k, k, s, p, flags)  # the plain descriptor packs the weights
+    ifx.conv_fused(d, ifx.pack_act(cu(x)), ifx.pack_weights(dp, cu(wt)), cu(bias), cu(mult), cu(shift), None, y)
+    torch.cuda.synchronize()
+    check_guards(whole)
+    got = ifx.unpack_act(from_phase(y, n, c1, ho, wo).contiguous(), oc).cpu().numpy()
+    np.testing.assert_array_equal(got, orc.conv_fused(x, wt, bias, mult, shift, s, p, flags))
+
+
+@pytest.mark.parametrize("shape", PHASE_IN_SHAPES)
+@pytest.mark.parametrize("flags", [0, 1])
+def test_phase_split_input(ifx, orc, shape, flags):
+    n, h, w, c, oc, k, s, p = shape
+    note(f"phase-split input {shape} flags={flags}")
+    rng = np.random.default_rng(sum(shape) + 5 * flags)
+    x = rand(rng, (n, h, w, c), 0, 127)
+    wt = rand(rng, (oc, k, k, c), -127, 127)
+    bias, mult, shift = params(rng, oc)
+    d = ifx.conv_desc(n, h, w, c, oc, k, k, s, p, flags | ifx.IN_PHASE)
+    dp = ifx.conv_desc(n, h, w, c, oc, k, k, s, p, flags)
+    ho, wo = ifx.conv_out_dims(d)
+    xb = ifx.pack_act(cu(x)).view(n, (c + 31) // 32, h, w, 32)
+    y, whole = guarded(ifx.act_bytes(n, ho, wo, oc))
+    ifx.conv_fused(d, to_phase(xb), ifx.pack_weights(dp, cu(wt)), cu(bias), cu(mult), cu(shift), None, y)
+    torch.cuda.synchronize()
+    check_guards(whole)
+    got = ifx.unpack_act(y.view(n, (oc + 31) // 32, ho, wo, 32), oc).cpu().numpy()
+    np.testing.assert_array_equal(got, orc.conv_fused(x, wt, bias, mult, shift, s, p, flags))
 
 
 def test_requant_edges(ifx, orc):

@@ -181,7 +181,8 @@ def test_workload4_every_layer_sampled(ifx, orc):
     grids: the fused stem reading the NHWC images; per bottleneck conv1 (unless the previous
     block chained it), conv2, then conv3 fused with its projection, or chained with the next
     block's conv1 where the library reports that pair as chainable (conv3 with its projection
-    too), or alone.  A chained block
+    too), or alone.  conv1 of a block whose conv2 has stride 2 stores its output phase-split
+    (IFX_OUT_PHASE, also through the chained launch) for conv2 (IFX_IN_PHASE).  A chained block
     output whose next reader is a stride-2 projection is stored at its even pixels only
     (IFX_OUT_EVEN), and that projection then runs with stride 1 on the subsampled tensor.  After
     each layer the sampled images (the first and last of the batch, one in each pass, and two
@@ -201,7 +202,16 @@ def test_workload4_every_layer_sampled(ifx, orc):
         d.n = n
         return d
 
-    chained = 0
+    def with_flag(d, f):
+        q = ifx.ConvDesc.from_buffer_copy(d)
+        q.flags |= f
+        return q
+
+    def phase_in_ok(d):  # a stride-2 3x3 that reads the phase-split layout (the driver's rule)
+        return (d.kh == 3 and d.stride == 2 and d.pad == 1 and d.h % 2 == 0 and d.w % 2 == 0
+                and ifx.conv_validate(with_flag(d, ifx.IN_PHASE)) == 0)
+
+    chained = phases = 0
     for p0 in (0, half):
         mine = [i for i, r in enumerate(rows) if p0 <= r < p0 + half]
         local = [rows[i] - p0 for i in mine]
@@ -214,17 +224,30 @@ def test_workload4_every_layer_sampled(ifx, orc):
         got = ifx.unpack_act(t[local].contiguous(), 64).cpu().numpy()
         np.testing.assert_array_equal(got, trace[0][mine], err_msg="stem")
         t1 = None  # the block's conv1 output when the previous block chained it
+        t1_ps = False  # ... stored phase-split
         t_even = False  # t holds only the even pixels of the block input
         for bi, blk in enumerate(net.blocks):
             c1, c2, c3 = blk.convs
+            d2 = at(c2, half)
             if t1 is None:
+                d1o = at(c1, half)
+                t1_ps = phase_in_ok(d2) and ifx.conv_validate(with_flag(d1o, ifx.OUT_PHASE)) == 0
                 t1 = model.empty_act(half, *c1.out_hw, c1.spec.c_out)
-                ifx.conv_fused(at(c1, half), t, c1.w_blk, c1.bias, c1.mult, c1.shift, None, t1)
+                ifx.conv_fused(with_flag(d1o, ifx.OUT_PHASE) if t1_ps else d1o, t, c1.w_blk, c1.bias, c1.mult,
+                               c1.shift, None, t1)
+            phases += t1_ps
             t2 = model.empty_act(half, *c2.out_hw, c2.spec.c_out)
-            ifx.conv_fused(at(c2, half), t1, c2.w_blk, c2.bias, c2.mult, c2.shift, None, t2)
+            ifx.conv_fused(with_flag(d2, ifx.IN_PHASE) if t1_ps else d2, t1, c2.w_blk, c2.bias, c2.mult, c2.shift,
+                           None, t2)
             nb_ = net.blocks[bi + 1] if bi + 1 < len(net.blocks) else None
             nxt = nb_.convs[0] if nb_ is not None else None
-            t1 = None
+            # the next block's conv1 as a chained launch writes phase-split for a stride-2 conv2
+            d1n = None
+            if nxt is not None:
+                d1n = at(nxt, half)
+                if phase_in_ok(at(nb_.convs[1], half)):
+                    d1n = with_flag(d1n, ifx.OUT_PHASE)
+            t1, t1_ps = None, False
             y_even = False
             d3 = at(c3, half)
             if blk.proj is not None:
@@ -233,16 +256,17 @@ def test_workload4_every_layer_sampled(ifx, orc):
                 if t_even:  # the projection's stride-2 pixels, already subsampled
                     dp.stride, dp.h, dp.w = 1, (dp.h + 1) // 2, (dp.w + 1) // 2
                 y = model.empty_act(half, *c3.out_hw, c3.spec.c_out)
-                if nxt is not None and ifx.conv_proj_chain_kernel_name(d3, dp, at(nxt, half)) is not None:
+                if nxt is not None and ifx.conv_proj_chain_kernel_name(d3, dp, d1n) is not None:
                     t1 = model.empty_act(half, *nxt.out_hw, nxt.spec.c_out)
+                    t1_ps = bool(d1n.flags & ifx.OUT_PHASE)
                     ifx.conv_proj_chain_fused(d3, t2, c3.w_blk, c3.bias, c3.mult, c3.shift, dp, t, pj.w_blk,
-                                              pj.bias, pj.mult, pj.shift, y, at(nxt, half), nxt.w_blk, nxt.bias,
+                                              pj.bias, pj.mult, pj.shift, y, d1n, nxt.w_blk, nxt.bias,
                                               nxt.mult, nxt.shift, t1)
                     chained += 1
                 else:
                     ifx.conv_proj_fused(d3, t2, c3.w_blk, c3.bias, c3.mult, c3.shift, dp, t,
                                         pj.w_blk, pj.bias, pj.mult, pj.shift, y)
-            elif nxt is not None and ifx.conv_chain_kernel_name(d3, at(nxt, half)) is not None:
+            elif nxt is not None and ifx.conv_chain_kernel_name(d3, d1n) is not None:
                 pn = nb_.proj
                 y_even = pn is not None and pn.spec.k == 1 and pn.spec.stride == 2
                 if y_even:
@@ -251,7 +275,8 @@ def test_workload4_every_layer_sampled(ifx, orc):
                 else:
                     y = model.empty_act(half, *c3.out_hw, c3.spec.c_out)
                 t1 = model.empty_act(half, *nxt.out_hw, nxt.spec.c_out)
-                ifx.conv_chain_fused(d3, t2, c3.w_blk, c3.bias, c3.mult, c3.shift, t, y, at(nxt, half),
+                t1_ps = bool(d1n.flags & ifx.OUT_PHASE)
+                ifx.conv_chain_fused(d3, t2, c3.w_blk, c3.bias, c3.mult, c3.shift, t, y, d1n,
                                      nxt.w_blk, nxt.bias, nxt.mult, nxt.shift, t1)
                 chained += 1
             else:
@@ -266,6 +291,7 @@ def test_workload4_every_layer_sampled(ifx, orc):
         del t
         torch.cuda.synchronize()
     assert chained == 6  # res2.1 -> res2.2 (with its projection), res2.2 -> res2.3, res2.3 -> res3.1; both passes
+    assert phases == 6   # res3.1, res4.1, res5.1 conv2 read a phase-split conv1 output; both passes
 
 
 @pytest.mark.parametrize("n", [1, 3])
