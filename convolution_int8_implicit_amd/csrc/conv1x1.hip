@@ -407,27 +407,33 @@ hipError_t launch_1x1_res(const ConvArgs &a, hipStream_t s)
 // registers and adds it in conv3's epilogue, as the fused projection kernel does; y is staged in
 // one region after the ring (conv1' with 64 output channels only: the projection's weights and
 // parameters take the registers that 128 would need).
-constexpr int kChainC = 256;      // block-output channels (four waves x 64)
-constexpr int kChainA = 4096;     // a tile's conv3 activations (or projection input): [64 rows][64 B]
-constexpr int kChainPerCu = 2;    // resident workgroups per CU
+// The block output has 64 NW channels (NW waves: 256 at res2, 512 at res3); conv3 has KS 64-byte
+// K-steps (K <= 64 NW / 4 ... 128).
+constexpr int kChainA = 4096;  // one K-step of a tile's conv3 input (or projection input): [64 rows][64 B]
 
-template <bool PROJ>
+template <int NW, int KS, bool PROJ>
 struct ChainLay {
-    // slot: conv3 activations + the four shortcut / y regions; y is computed in place
-    static constexpr int SLOT = kChainA + 4 * 4096;
-    static constexpr int NB = 4;    // ring depth (tiles resident in LDS)
-    static constexpr int DMA = 5;   // DMAs per wave per tile: 1 activation, 4 shortcut
+    // slot: KS K-steps of conv3 activations + the NW shortcut / y regions; y is computed in place
+    static constexpr int SLOT = KS * kChainA + NW * 4096;
+    static constexpr int NB = 4;                     // ring depth (tiles resident in LDS)
+    static constexpr int PER_CU = NW == 4 ? 2 : 1;   // resident workgroups per CU
+    static constexpr int ADMA = KS * 4 / NW;         // activation DMAs per wave per tile
+    static constexpr int DMA = ADMA + 4;             // + 4 shortcut DMAs
     static constexpr int LDS = NB * SLOT;
+    static_assert(ADMA >= 1 && ADMA * NW == KS * 4, "every wave issues the same DMAs");
 };
 template <>
-struct ChainLay<true> {
+struct ChainLay<4, 1, true> {
     // slot: conv3 activations + projection input; y in one region after the ring
     static constexpr int SLOT = 2 * kChainA;
     static constexpr int NB = 6;
-    static constexpr int DMA = 2;   // 1 activation, 1 projection input
+    static constexpr int PER_CU = 2;
+    static constexpr int ADMA = 1;
+    static constexpr int DMA = 2;  // 1 activation, 1 projection input
     static constexpr int LDS = NB * SLOT + 4 * 4096;
 };
-static_assert(kChainPerCu * ChainLay<false>::LDS <= kLdsBytes && kChainPerCu * ChainLay<true>::LDS <= kLdsBytes,
+static_assert(2 * ChainLay<4, 1, false>::LDS <= kLdsBytes && 2 * ChainLay<4, 1, true>::LDS <= kLdsBytes &&
+                  ChainLay<8, 2, false>::LDS <= kLdsBytes,
               "ring fits the LDS");
 
 // Physical LDS byte of logical 16-byte chunk k of row r in a [rows][64 B] swizzled region.
@@ -469,42 +475,48 @@ __device__ __forceinline__ void split_px(const TileOrg &t, int r, int &d, int &h
     }
 }
 
-// Rows 16 wave .. +15 of a 64-pixel tile of q's input (K <= 64: two 32-channel blocks, zero past
-// q.i1) into a [64 rows][64 B] swizzled region: one DMA per wave.
-__device__ __forceinline__ void tile_rows_issue(const ConvArgs &q, const TileOrg &t, int8_t *dst, int wave, int lane)
+// Rows 16 grp .. +15 of K-step ks (32-channel blocks 2 ks, 2 ks + 1, zero past q.i1) of a 64-pixel
+// tile of q's input into a [64 rows][64 B] swizzled region: one DMA.
+__device__ __forceinline__ void tile_rows_issue(const ConvArgs &q, const TileOrg &t, int8_t *dst, int grp, int ks,
+                                                int lane)
 {
     const unsigned plane = (unsigned)t.HoWo * 32;  // bytes of one 32-channel block of an image
     const unsigned in_img = (unsigned)q.i1 * plane;
     const v4i rs = make_rsrc(q.x + (long long)t.img0 * in_img, (long long)(q.n - t.img0) * in_img);
-    const int row = 16 * wave + (lane >> 2);
-    const int lch = (lane & 3) ^ swz(row);  // logical chunk: input channels 16 lch .. +15
-    const int sel = lch >> 1;
+    const int row = 16 * grp + (lane >> 2);
+    const int lch = (lane & 3) ^ swz(row);  // logical chunk: input channels 64 ks + 16 lch .. +15
+    const int blk = 2 * ks + (lch >> 1);
     int d, hw;
     split_px(t, row, d, hw);
-    const bool ok = t.m0 + row < q.m && sel < q.i1;
-    const unsigned off = (unsigned)d * in_img + (unsigned)sel * plane + (unsigned)hw * 32 + (lch & 1) * 16;
-    load16_lds_stream(rs, dst + wave * 1024, ok ? off : kOOB);
+    const bool ok = t.m0 + row < q.m && blk < q.i1;
+    const unsigned off = (unsigned)d * in_img + (unsigned)blk * plane + (unsigned)hw * 32 + (lch & 1) * 16;
+    load16_lds_stream(rs, dst + grp * 1024, ok ? off : kOOB);
 }
 
 // This wave's DMAs of the tile at pixel m0 (m0 >= a.m: every load is out of range, so the
 // slot fills with zeros and the count of DMAs stays the same): conv3 activation rows 16 wave ..
 // +15 into the slot's first 4 KB, then the shortcut bytes of channels 64 wave .. +63 into the
 // wave's region or, with PROJ, the projection input's rows into the second 4 KB.
-template <bool PROJ>
+template <int NW, int KS, bool PROJ>
 __device__ __forceinline__ void chain_issue(const ConvArgs &a, const ConvArgs &pj, int8_t *buf, int m0, int wave,
                                             int lane)
 {
+    using L = ChainLay<NW, KS, PROJ>;
     const TileOrg t = tile_org(a, m0);
     const unsigned plane = (unsigned)t.HoWo * 32;
-    tile_rows_issue(a, t, buf, wave, lane);
+#pragma unroll
+    for (int j = 0; j < L::ADMA; ++j) {  // 16-row group q % 4 of K-step q / 4
+        const int q = j * NW + wave;
+        tile_rows_issue(a, t, buf + (q >> 2) * kChainA, q & 3, q >> 2, lane);
+    }
     if (PROJ) {
-        tile_rows_issue(pj, t, buf + kChainA, wave, lane);
+        tile_rows_issue(pj, t, buf + kChainA, wave, 0, lane);
         return;
     }
     {
         const unsigned out_img = (unsigned)a.oc1 * plane;
         const v4i rsR = make_rsrc(a.res + (long long)t.img0 * out_img, (long long)(a.n - t.img0) * out_img);
-        int8_t *const Rw = buf + kChainA + wave * 4096;
+        int8_t *const Rw = buf + KS * kChainA + wave * 4096;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int row = 16 * j + (lane >> 2);
@@ -528,21 +540,26 @@ __device__ __forceinline__ v4i chain_weights(const ConvArgs &q, int o, int kc)
     return *(const v4i *)(q.wt + ((long long)(o1 * q.i1 + kb) * q.o2 + o2i) * 32 + (kc & 1) * 16);
 }
 
-// Phase 2's output channel for row r (0..15) of channel tile mt of a wave: N1 = 64 gives each
-// wave 16 consecutive channels; N1 = 128 gives it 32 (one 32-channel block) with rows ordered so
-// that accumulator row 4g + i of tiles 0 and 1 are channels 8g + i and 8g + 4 + i.
-template <int N1>
+// Phase 2's output channel for row r (0..15) of channel tile mt of a wave that owns CPW conv1'
+// channels: CPW = 16 gives it 16 consecutive channels; CPW = 32 gives it 32 (one 32-channel block)
+// with rows ordered so that accumulator row 4g + i of tiles 0 and 1 are channels 8g + i and
+// 8g + 4 + i.
+template <int CPW>
 __device__ __forceinline__ int chain_ch2(int wave, int mt, int r)
 {
-    return N1 == 64 ? 16 * wave + r : 32 * wave + 8 * (r >> 2) + 4 * mt + (r & 3);
+    static_assert(CPW == 16 || CPW == 32, "16 or 32 conv1' channels per wave");
+    return CPW == 16 ? 16 * wave + r : 32 * wave + 8 * (r >> 2) + 4 * mt + (r & 3);
 }
 
-template <int N1, bool RELU1, bool EVEN, bool PROJ>
-__global__ __launch_bounds__(256, kChainPerCu) void conv1x1_chain_kernel(ConvArgs a, ConvArgs b, ConvArgs pj,
-                                                                          int tiles)
+template <int NW, int KS, int N1, bool RELU1, bool EVEN, bool PROJ>
+__global__ __launch_bounds__(64 * NW, (ChainLay<NW, KS, PROJ>::PER_CU)) void conv1x1_chain_kernel(ConvArgs a,
+                                                                                                   ConvArgs b,
+                                                                                                   ConvArgs pj,
+                                                                                                   int tiles)
 {
-    using L = ChainLay<PROJ>;
-    constexpr int MT2 = N1 / 64;  // phase-2 channel tiles per wave
+    using L = ChainLay<NW, KS, PROJ>;
+    constexpr int CPW = N1 / NW;   // conv1' channels per wave
+    constexpr int MT2 = CPW / 16;  // phase-2 channel tiles per wave
     __shared__ __attribute__((aligned(1024))) int8_t smem[L::LDS];
 
     const int tid = threadIdx.x;
@@ -556,14 +573,16 @@ __global__ __launch_bounds__(256, kChainPerCu) void conv1x1_chain_kernel(ConvArg
     const int ntile = (tiles - 1 - first) / (int)gridDim.x + 1;
 
     // ---- weights and parameters into registers (before any DMA, so their waits are short)
-    v4i w3[4];  // phase-1 column operand: lane (c, g), tile tn -> channel ch0 + 4c + tn, bytes 16g ..
+    v4i w3[KS][4];  // phase-1 column operand: lane (c, g), tile tn -> channel ch0 + 4c + tn, bytes 64s + 16g ..
 #pragma unroll
-    for (int tn = 0; tn < 4; ++tn) w3[tn] = chain_weights(a, ch0 + 4 * c + tn, g);
-    v4i w1[MT2][4];  // phase-2 row operand: lane (c, g), K-step s -> channel chain_ch2(c), bytes 64s + 16g ..
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int tn = 0; tn < 4; ++tn) w3[s][tn] = chain_weights(a, ch0 + 4 * c + tn, 4 * s + g);
+    v4i w1[MT2][NW];  // phase-2 row operand: lane (c, g), K-step s -> channel chain_ch2(c), bytes 64s + 16g ..
 #pragma unroll
     for (int mt = 0; mt < MT2; ++mt)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) w1[mt][s] = chain_weights(b, chain_ch2<N1>(wave, mt, c), 4 * s + g);
+        for (int s = 0; s < NW; ++s) w1[mt][s] = chain_weights(b, chain_ch2<CPW>(wave, mt, c), 4 * s + g);
     RqPacked r1;
     int mode1;
     {
@@ -589,7 +608,7 @@ __global__ __launch_bounds__(256, kChainPerCu) void conv1x1_chain_kernel(ConvArg
         RqLane r[MT2];
 #pragma unroll
         for (int mt = 0; mt < MT2; ++mt) {
-            const int cb = chain_ch2<N1>(wave, mt, 4 * g);  // the lane's 4 consecutive channels
+            const int cb = chain_ch2<CPW>(wave, mt, 4 * g);  // the lane's 4 consecutive channels
             const int md = rq_setup<false, RELU1>(r[mt], *(const v4i *)(b.bias + cb), *(const v4i *)(b.mult + cb),
                                                   *(const v4i *)(b.shift + cb), false, cb, b.oc);
             mode2 = (md == 0 || mode2 == 0) ? 0 : (md == 1 && mode2 == 1 ? 1 : 2);  // valid for both sets
@@ -601,7 +620,7 @@ __global__ __launch_bounds__(256, kChainPerCu) void conv1x1_chain_kernel(ConvArg
     // ---- ring prologue: tiles 0 .. NB-2 (tiles past the end load zeros)
     auto tile_m0 = [&](int j) { const int t = first + j * (int)gridDim.x; return t < tiles ? t * 64 : a.m; };
 #pragma unroll
-    for (int j = 0; j < L::NB - 1; ++j) chain_issue<PROJ>(a, pj, smem + j * L::SLOT, tile_m0(j), wave, lane);
+    for (int j = 0; j < L::NB - 1; ++j) chain_issue<NW, KS, PROJ>(a, pj, smem + j * L::SLOT, tile_m0(j), wave, lane);
 
     for (int j = 0; j < ntile; ++j) {
         int8_t *const buf = smem + (j % L::NB) * L::SLOT;
@@ -610,11 +629,12 @@ __global__ __launch_bounds__(256, kChainPerCu) void conv1x1_chain_kernel(ConvArg
         // leaves only theirs in flight (pending stores only make the wait longer)
         wait_vmcnt<(L::NB - 2) * L::DMA>();
         ring_barrier();  // tile j visible to every wave; every wave is done with tile j - 1
-        chain_issue<PROJ>(a, pj, smem + ((j + L::NB - 1) % L::NB) * L::SLOT, tile_m0(j + L::NB - 1), wave, lane);
+        chain_issue<NW, KS, PROJ>(a, pj, smem + ((j + L::NB - 1) % L::NB) * L::SLOT, tile_m0(j + L::NB - 1), wave,
+                                  lane);
 
         // ---- phase 1: conv3, 64 pixels x this wave's 64 channels, one K-step, in two halves of
         //      32 pixels (half the accumulators live at a time)
-        int8_t *const Rb = PROJ ? smem + L::NB * L::SLOT : buf + kChainA;  // the four y regions
+        int8_t *const Rb = PROJ ? smem + L::NB * L::SLOT : buf + KS * kChainA;  // the NW y regions
         int8_t *const Rw = Rb + wave * 4096;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -654,13 +674,17 @@ __global__ __launch_bounds__(256, kChainPerCu) void conv1x1_chain_kernel(ConvArg
                         rr[t][i] = *(const unsigned *)(Rw + swz_at(16 * (2 * h + t) + 4 * i + g, c >> 2) + 4 * (c & 3));
             }
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const int tm = 2 * h + t;
-                const v4i af = *(const v4i *)(buf + swz_at(16 * tm + 4 * (c & 3) + (c >> 2), g));
+            for (int s = 0; s < KS; ++s)
 #pragma unroll
-                for (int tn = 0; tn < 4; ++tn)
-                    acc[t][tn] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, w3[tn], (v4i){0, 0, 0, 0}, 0, 0, 0);
-            }
+                for (int t = 0; t < 2; ++t) {
+                    const int tm = 2 * h + t;
+                    const v4i af = *(const v4i *)(buf + s * kChainA + swz_at(16 * tm + 4 * (c & 3) + (c >> 2), g));
+#pragma unroll
+                    for (int tn = 0; tn < 4; ++tn)
+                        acc[t][tn] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, w3[s][tn],
+                                                                           s == 0 ? (v4i){0, 0, 0, 0} : acc[t][tn],
+                                                                           0, 0, 0);
+                }
             auto rq = [&](auto md) __attribute__((always_inline)) {
                 constexpr int MD = decltype(md)::value;
 #pragma unroll
@@ -710,11 +734,11 @@ __global__ __launch_bounds__(256, kChainPerCu) void conv1x1_chain_kernel(ConvArg
             }
         }
 
-        // ---- phase 2: conv1' = W1 . y^T, this wave's N1/4 channels x 64 pixels, K = 256 (the
-        //      four regions); lane (c, g) gets channels chain_ch2(4g .. 4g+3) of pixel 16 pg + c
+        // ---- phase 2: conv1' = W1 . y^T, this wave's CPW channels x 64 pixels, K = 64 NW (the
+        //      NW regions); lane (c, g) gets channels chain_ch2(4g .. 4g+3) of pixel 16 pg + c
         v4i acc2[4][MT2];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
+        for (int s = 0; s < NW; ++s) {
             const int8_t *const Rs = Rb + s * 4096;
 #pragma unroll
             for (int pg = 0; pg < 4; ++pg) {
@@ -726,7 +750,7 @@ __global__ __launch_bounds__(256, kChainPerCu) void conv1x1_chain_kernel(ConvArg
             }
         }
         {
-            const int cb = chain_ch2<N1>(wave, 0, 4 * g);
+            const int cb = chain_ch2<CPW>(wave, 0, 4 * g);
             const unsigned plane = (unsigned)to.HoWo * 32;
             const unsigned t1_img = (unsigned)b.oc1 * plane;
             int8_t *const t1 = (int8_t *)b.y + (long long)to.img0 * t1_img + (unsigned)(cb >> 5) * plane + (cb & 31);
@@ -766,42 +790,56 @@ __global__ __launch_bounds__(256, kChainPerCu) void conv1x1_chain_kernel(ConvArg
     wait_vmcnt<0>();  // the ring's last (zero-fill) DMAs land before the workgroup's LDS is released
 }
 
-template <int N1, bool RELU1, bool EVEN, bool PROJ>
+template <int NW, int KS, int N1, bool RELU1, bool EVEN, bool PROJ>
 hipError_t launch_chain_k(const ConvArgs &a, const ConvArgs &b, const ConvArgs &pj, long long tiles, hipStream_t s)
 {
+    using L = ChainLay<NW, KS, PROJ>;
     int cus = 0;
     const hipError_t e = current_cus(&cus);
     if (e != hipSuccess) return e;
-    const long long grid = tiles < (long long)kChainPerCu * cus ? tiles : (long long)kChainPerCu * cus;
-    hipLaunchKernelGGL((conv1x1_chain_kernel<N1, RELU1, EVEN, PROJ>), dim3((unsigned)grid), dim3(256), 0, s, a, b,
-                       pj, (int)tiles);
+    const long long slots = (long long)L::PER_CU * cus;
+    const long long grid = tiles < slots ? tiles : slots;
+    hipLaunchKernelGGL((conv1x1_chain_kernel<NW, KS, N1, RELU1, EVEN, PROJ>), dim3((unsigned)grid), dim3(64 * NW), 0,
+                       s, a, b, pj, (int)tiles);
     return hipGetLastError();
 }
 
-// pj: the block's projection (conv3's shortcut computed in the kernel) or null (DMA'd shortcut).
-template <int N1>
+template <int NW, int KS, int N1, bool PROJ>
+hipError_t launch_chain_flags(const ConvArgs &a, const ConvArgs &b, const ConvArgs &pj, long long tiles,
+                              hipStream_t s)
+{
+    const bool relu = b.relu != 0, even = a.out_even != 0;
+    if constexpr (PROJ) {  // the projection's block output is read whole by the next block
+        if (even) return hipErrorInvalidValue;
+    } else {
+        if (even)
+            return relu ? launch_chain_k<NW, KS, N1, true, true, PROJ>(a, b, pj, tiles, s)
+                        : launch_chain_k<NW, KS, N1, false, true, PROJ>(a, b, pj, tiles, s);
+    }
+    return relu ? launch_chain_k<NW, KS, N1, true, false, PROJ>(a, b, pj, tiles, s)
+                : launch_chain_k<NW, KS, N1, false, false, PROJ>(a, b, pj, tiles, s);
+}
+
+// The instances: 256-channel block outputs (four waves, conv3 K <= 64) chained with a conv1 to 64
+// or 128 channels, with the projection (conv1 to 64) or without; 512-channel block outputs (eight
+// waves, conv3 K <= 128) chained with a conv1 to 128 channels.  pj: the block's projection (conv3's
+// shortcut computed in the kernel) or null (DMA'd shortcut).
 hipError_t launch_chain(const ConvArgs &a, const ConvArgs &b, const ConvArgs *pj, hipStream_t s)
 {
+    const int nw = a.oc / 64, ks = a.i1 <= 2 && nw == 4 ? 1 : 2;
     const bool relu = b.relu != 0, even = a.out_even != 0, proj = pj != nullptr;
-    if (answer_query("conv1x1_chain_kernel<%d, %s, %s, %s>", N1, tf(relu), tf(even), tf(proj))) return hipSuccess;
+    if (answer_query("conv1x1_chain_kernel<%d, %d, %d, %s, %s, %s>", nw, ks, b.oc, tf(relu), tf(even), tf(proj)))
+        return hipSuccess;
     const long long tiles = (a.m + 63) / 64;
     if (tiles <= 0) return hipSuccess;
     if (tiles > 0x7fffffffLL / 64) return hipErrorInvalidConfiguration;
-    if (proj) {
-        // the projection's weights and parameters fit the registers beside 64 conv1 channels only
-        if constexpr (N1 == 64) {
-            if (even) return hipErrorInvalidValue;
-            return relu ? launch_chain_k<N1, true, false, true>(a, b, *pj, tiles, s)
-                        : launch_chain_k<N1, false, false, true>(a, b, *pj, tiles, s);
-        } else {
-            return hipErrorInvalidValue;
-        }
+    if (nw == 4 && ks == 1) {
+        if (proj) return b.oc == 64 ? launch_chain_flags<4, 1, 64, true>(a, b, *pj, tiles, s) : hipErrorInvalidValue;
+        if (b.oc == 64) return launch_chain_flags<4, 1, 64, false>(a, b, a, tiles, s);
+        if (b.oc == 128) return launch_chain_flags<4, 1, 128, false>(a, b, a, tiles, s);
     }
-    if (even)
-        return relu ? launch_chain_k<N1, true, true, false>(a, b, a, tiles, s)
-                    : launch_chain_k<N1, false, true, false>(a, b, a, tiles, s);
-    return relu ? launch_chain_k<N1, true, false, false>(a, b, a, tiles, s)
-                : launch_chain_k<N1, false, false, false>(a, b, a, tiles, s);
+    if (nw == 8 && ks == 2 && !proj && b.oc == 128) return launch_chain_flags<8, 2, 128, false>(a, b, a, tiles, s);
+    return hipErrorInvalidValue;
 }
 
 
@@ -1014,26 +1052,30 @@ hipError_t launch_conv1x1_proj(const ConvArgs &a, const ConvArgs &pj, hipStream_
     return a.oc1 * 32 > 64 ? launch_1x1_proj_k<128, 128>(a, pj, s) : launch_1x1_proj_k<256, 64>(a, pj, s);
 }
 
-// conv3 (a: 1x1, unit stride, K <= 64, 256 output channels, shortcut and ReLU) chained with the
-// next block's conv1 (b: 1x1, unit stride, 256 -> 64 or 128 channels, same pixels).
+// conv3 (a: 1x1, unit stride, shortcut and ReLU) chained with the next block's conv1 (b: 1x1, unit
+// stride, the same pixels): a 256-channel block output with conv3 K <= 64 and conv1 to 64 or 128
+// channels, or a 512-channel one with conv3 K <= 128 and conv1 to 128.
 bool conv1x1_chain_supported(const ConvArgs &a, const ConvArgs &b)
 {
     if (a.in_ps || a.out_ps || b.in_ps || (b.out_ps && ((b.ho | b.wo) & 1))) return false;
-    return a.i1 <= 2 && a.oc == kChainC && a.stride == 1 && a.pad == 0 && a.residual && a.relu && !a.out_i32 &&
-           b.i1 * 32 == kChainC && (b.oc == 64 || b.oc == 128) && b.stride == 1 && b.pad == 0 && !b.residual &&
-           !b.out_i32 && a.m == b.m && a.ho == b.h && a.wo == b.w && a.n == b.n && b.ho == b.h && b.wo == b.w;
+    const bool shape = (a.oc == 256 && a.i1 <= 2 && (b.oc == 64 || b.oc == 128)) ||
+                       (a.oc == 512 && a.i1 <= 4 && b.oc == 128);
+    return shape && a.stride == 1 && a.pad == 0 && a.residual && a.relu && !a.out_i32 && b.i1 * 32 == a.oc &&
+           b.stride == 1 && b.pad == 0 && !b.residual && !b.out_i32 && a.m == b.m && a.ho == b.h && a.wo == b.w &&
+           a.n == b.n && b.ho == b.h && b.wo == b.w;
 }
 
 hipError_t launch_conv1x1_chain(const ConvArgs &a, const ConvArgs &b, hipStream_t s)
 {
-    return b.oc == 64 ? launch_chain<64>(a, b, nullptr, s) : launch_chain<128>(a, b, nullptr, s);
+    return launch_chain(a, b, nullptr, s);
 }
 
 // The same with conv3's shortcut its 1x1 projection pj (unit stride, K <= 64, conv3's pixels and
 // channels, no ReLU), computed in the kernel.
 bool conv1x1_proj_chain_supported(const ConvArgs &a, const ConvArgs &pj, const ConvArgs &b)
 {
-    return conv1x1_chain_supported(a, b) && b.oc == 64 && !a.out_even && !pj.in_ps && !pj.out_ps && pj.i1 <= 2 &&
+    return conv1x1_chain_supported(a, b) && a.oc == 256 && b.oc == 64 && !a.out_even && !pj.in_ps && !pj.out_ps &&
+           pj.i1 <= 2 &&
            pj.oc == a.oc &&
            pj.stride == 1 && pj.pad == 0 && !pj.relu && !pj.residual && !pj.out_i32 && pj.m == a.m &&
            pj.ho == a.ho && pj.wo == a.wo && pj.h == a.h && pj.w == a.w && pj.n == a.n;
@@ -1041,7 +1083,7 @@ bool conv1x1_proj_chain_supported(const ConvArgs &a, const ConvArgs &pj, const C
 
 hipError_t launch_conv1x1_proj_chain(const ConvArgs &a, const ConvArgs &pj, const ConvArgs &b, hipStream_t s)
 {
-    return b.oc == 64 ? launch_chain<64>(a, b, &pj, s) : hipErrorInvalidValue;
+    return launch_chain(a, b, &pj, s);
 }
 
 hipError_t launch_conv1x1_small_k(const ConvArgs &a, hipStream_t s)

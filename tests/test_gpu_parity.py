@@ -526,46 +526,51 @@ def test_conv_proj_chain_fused(ifx, orc, shape):
     np.testing.assert_array_equal(ifx.unpack_act(t1.view(n, 2, h, w, 32), 64).cpu().numpy(), exp_t1)
 
 
-# (n, h, w, conv3 input channels, conv1 output channels, conv1 flags, y at even pixels only)
+# (n, h, w, conv3 input channels, block-output channels, conv1 output channels, conv1 flags,
+#  y at even pixels only, t1 phase-split)
 CHAIN_SHAPES = [
-    (2, 56, 56, 64, 64, 1, False),    # the res2.2 -> res2.3 shape
-    (1, 56, 56, 64, 128, 1, True),    # the res2.3 -> res3.1 shape (res3.1's projection has stride 2)
-    (1, 56, 56, 64, 128, 1, False),
-    (3, 9, 7, 40, 64, 0, False),      # 189 pixels: a ragged last tile; conv1 without ReLU
-    (3, 9, 7, 40, 128, 1, True),      # odd height and width: the last row and column are even
-    (1, 5, 5, 32, 128, 0, False),     # one partial tile
-    (2, 6, 10, 64, 64, 0, True),      # even sizes, tiles spanning images
+    (2, 56, 56, 64, 256, 64, 1, False, False),    # the res2.2 -> res2.3 shape
+    (1, 56, 56, 64, 256, 128, 1, True, True),     # res2.3 -> res3.1 (a stride-2 projection and conv2 follow)
+    (1, 56, 56, 64, 256, 128, 1, False, False),
+    (3, 9, 7, 40, 256, 64, 0, False, False),      # 189 pixels: a ragged last tile; conv1 without ReLU
+    (3, 9, 7, 40, 256, 128, 1, True, False),      # odd height and width: the last row and column are even
+    (1, 6, 6, 32, 256, 128, 0, False, True),      # one partial tile
+    (2, 6, 10, 64, 256, 64, 0, True, False),      # even sizes, tiles spanning images
+    (3, 28, 28, 128, 512, 128, 1, False, False),  # the res3.2 -> res3.3 shape (eight waves, K = 128)
+    (2, 7, 9, 96, 512, 128, 0, False, False),     # K = 96 (second K-step half zero), ragged tiles
 ]
 
 
 @pytest.mark.parametrize("shape", CHAIN_SHAPES)
 def test_conv_chain_fused(ifx, orc, shape):
-    n, h, w, c3in, n1, f1, even = shape
+    n, h, w, c3in, cb, n1, f1, even, ps = shape
     note(f"chain {shape}")
     rng = np.random.default_rng(sum(shape) * 11)
     t2 = rand(rng, (n, h, w, c3in), 0, 127)
-    res = rand(rng, (n, h, w, 256), -128, 127)
-    w3 = rand(rng, (256, 1, 1, c3in), -127, 127)
-    w1 = rand(rng, (n1, 1, 1, 256), -127, 127)
-    b3, m3, s3 = params(rng, 256, 0, 20)
+    res = rand(rng, (n, h, w, cb), -128, 127)
+    w3 = rand(rng, (cb, 1, 1, c3in), -127, 127)
+    w1 = rand(rng, (n1, 1, 1, cb), -127, 127)
+    b3, m3, s3 = params(rng, cb, 0, 20)
     b1, m1, s1 = params(rng, n1, 0, 20)
-    d3p = ifx.conv_desc(n, h, w, c3in, 256, 1, 1, 1, 0, ifx.RESIDUAL | ifx.RELU)  # for the weight pack
-    d3 = ifx.conv_desc(n, h, w, c3in, 256, 1, 1, 1, 0, ifx.RESIDUAL | ifx.RELU | (ifx.OUT_EVEN if even else 0))
-    d1 = ifx.conv_desc(n, h, w, 256, n1, 1, 1, 1, 0, f1)
+    d3p = ifx.conv_desc(n, h, w, c3in, cb, 1, 1, 1, 0, ifx.RESIDUAL | ifx.RELU)  # for the weight packs
+    d1p = ifx.conv_desc(n, h, w, cb, n1, 1, 1, 1, 0, f1)
+    d3 = ifx.conv_desc(n, h, w, c3in, cb, 1, 1, 1, 0, ifx.RESIDUAL | ifx.RELU | (ifx.OUT_EVEN if even else 0))
+    d1 = ifx.conv_desc(n, h, w, cb, n1, 1, 1, 1, 0, f1 | (ifx.OUT_PHASE if ps else 0))
     assert ifx.conv_chain_kernel_name(d3, d1).endswith(", true, false>" if even else ", false, false>")
     hy, wy = ((h + 1) // 2, (w + 1) // 2) if even else (h, w)
-    y, yw = guarded(ifx.act_bytes(n, hy, wy, 256))
+    y, yw = guarded(ifx.act_bytes(n, hy, wy, cb))
     t1, tw = guarded(ifx.act_bytes(n, h, w, n1))
     ifx.conv_chain_fused(d3, ifx.pack_act(cu(t2)), ifx.pack_weights(d3p, cu(w3)), cu(b3), cu(m3), cu(s3),
-                         ifx.pack_act(cu(res)), y, d1, ifx.pack_weights(d1, cu(w1)), cu(b1), cu(m1), cu(s1), t1)
+                         ifx.pack_act(cu(res)), y, d1, ifx.pack_weights(d1p, cu(w1)), cu(b1), cu(m1), cu(s1), t1)
     torch.cuda.synchronize()
     check_guards(yw)
     check_guards(tw)
     exp_y = orc.conv_fused(t2, w3, b3, m3, s3, 1, 0, ifx.RESIDUAL | ifx.RELU, res)
     exp_t1 = orc.conv_fused(exp_y, w1, b1, m1, s1, 1, 0, f1)
-    got_y = ifx.unpack_act(y.view(n, 8, hy, wy, 32), 256).cpu().numpy()
+    got_y = ifx.unpack_act(y.view(n, cb // 32, hy, wy, 32), cb).cpu().numpy()
     np.testing.assert_array_equal(got_y, exp_y[:, ::2, ::2] if even else exp_y)
-    np.testing.assert_array_equal(ifx.unpack_act(t1.view(n, n1 // 32, h, w, 32), n1).cpu().numpy(), exp_t1)
+    t1p = from_phase(t1, n, n1 // 32, h, w).contiguous() if ps else t1.view(n, n1 // 32, h, w, 32)
+    np.testing.assert_array_equal(ifx.unpack_act(t1p, n1).cpu().numpy(), exp_t1)
 
 
 # ------------------------------------------------------------------ stem
