@@ -757,6 +757,18 @@ def main():
     roof["avg_launch_us"] = round(avg_t * 1e6, 2)
     roof["work_per_launch"] = {"ops": dom["ops"] // dom["launches"], "bytes": dom["bytes"] // dom["launches"]}
     kernel_share = {k: round(v["time"] / reps * passes * 1e3, 3) for k, v in per_kernel.items()}
+    # per instance and step: launches, ops, algorithmic bytes and the sum of its launches' floors
+    kernel_work = {}
+    for nm, o, b, _ in launches:
+        if nm is None:
+            continue
+        kw = kernel_work.setdefault(nm, {"launches": 0, "ops": 0, "bytes": 0, "floor_ms": 0.0})
+        kw["launches"] += passes
+        kw["ops"] += passes * o
+        kw["bytes"] += passes * b
+        kw["floor_ms"] += passes * max(o / PEAK_I8, b / PEAK_HBM) * 1e3
+    for kw in kernel_work.values():
+        kw["floor_ms"] = round(kw["floor_ms"], 3)
     # the step's floor: every launch at its own bound (ops / int8 peak or algorithmic bytes / HBM),
     # summed over the launches of all passes, plus the head
     floor_s = passes * sum(max(o / PEAK_I8, b / PEAK_HBM) for nm, o, b, _ in launches if nm is not None) + head_floor
@@ -780,6 +792,7 @@ def main():
         "floor_ms": round(floor_s * 1e3, 4),
         "floor_frac": round(floor_s / sec_per_step, 4),
         "kernel_ms_per_step": kernel_share,
+        "kernel_work_per_step": kernel_work,
         "roofline": roof,
         **extra,
     }
