@@ -854,40 +854,49 @@ hipError_t launch_chain(const ConvArgs &a, const ConvArgs &b, const ConvArgs *pj
 // there by its own wave, so a tile needs one barrier.  These layers read and write ~60 KB of HBM
 // per 64-pixel tile for ~1.5 MOP of MFMA work: the bytes in flight, not the arithmetic, set the
 // rate.
-template <int NW, int KS>
+// KP > 0: the layer's shortcut is its 1x1 projection (stride 1, KP K-steps; the first block of a
+// stage, whose stride-2 input the previous block stored subsampled): a slot holds the projection's
+// input tile instead of the shortcut, each wave requantises the projection of its 64 channels (no
+// ReLU) into registers and adds it in the epilogue, and y is staged in one region per wave after
+// the ring.
+template <int NW, int KS, int KP = 0>
 struct RingCfg {
-    static constexpr int A = KS * 4096;           // activations: KS x [64 rows][64 B]
-    static constexpr int BUF = A + NW * 4096;     // + shortcut / output, one region per wave
+    static constexpr int A = KS * 4096;                  // activations: KS x [64 rows][64 B]
+    static constexpr int X = KP * 4096;                  // projection input: KP x [64 rows][64 B]
+    static constexpr int BUF = A + (KP ? X : NW * 4096);  // + shortcut / output, one region per wave
+    static constexpr int YST = KP ? NW * 4096 : 0;       // output staging after the ring (projection)
     static constexpr int PER_CU = NW == 4 ? 2 : 1;
-    static constexpr int NB = kLdsBytes / PER_CU / BUF > 4 ? 4 : kLdsBytes / PER_CU / BUF;
-    static constexpr int ADMA = KS * 4 / NW;      // activation DMAs per wave per tile
-    static constexpr int DMA = ADMA + 4;          // + four shortcut DMAs
+    static constexpr int AVAIL = kLdsBytes / PER_CU - YST;
+    static constexpr int NBMAX = KP ? 6 : 4;
+    static constexpr int NB = AVAIL / BUF > NBMAX ? NBMAX : AVAIL / BUF;
+    static constexpr int ADMA = KS * 4 / NW;             // activation DMAs per wave per tile
+    static constexpr int XDMA = KP * 4 / NW;             // projection-input DMAs per wave per tile
+    static constexpr int DMA = ADMA + (KP ? XDMA : 4);   // (+ four shortcut DMAs without a projection)
+    static constexpr int LDS = NB * BUF + YST;
     static_assert(ADMA >= 1 && ADMA * NW == KS * 4, "every wave issues the same DMAs");
+    static_assert(XDMA * NW == KP * 4, "every wave issues the same DMAs");
     static_assert(NB >= 3, "a ring of at least three tiles");
 };
 
-template <int NW, int KS>
-__device__ __forceinline__ void ring_issue(const ConvArgs &a, int8_t *buf, int m0, int wave, int lane)
+template <int NW, int KS, int KP>
+__device__ __forceinline__ void ring_issue(const ConvArgs &a, const ConvArgs &pj, int8_t *buf, int m0, int wave,
+                                           int lane)
 {
-    using C = RingCfg<NW, KS>;
+    using C = RingCfg<NW, KS, KP>;
     const TileOrg t = tile_org(a, m0);
     const unsigned plane = (unsigned)t.HoWo * 32;
-    {
-        const unsigned in_img = (unsigned)a.i1 * plane;
-        const v4i rsA = make_rsrc(a.x + (long long)t.img0 * in_img, (long long)(a.n - t.img0) * in_img);
 #pragma unroll
-        for (int j = 0; j < C::ADMA; ++j) {
-            const int q = j * NW + wave;  // 16-row group q % 4 of K-step q / 4
-            const int s = q >> 2;
-            const int row = 16 * (q & 3) + (lane >> 2);
-            const int lch = (lane & 3) ^ swz(row);
-            const int blk = 2 * s + (lch >> 1);
-            int d, hw;
-            split_px(t, row, d, hw);
-            const bool ok = m0 + row < a.m && blk < a.i1;
-            const unsigned off = (unsigned)d * in_img + (unsigned)blk * plane + (unsigned)hw * 32 + (lch & 1) * 16;
-            load16_lds_stream(rsA, buf + s * 4096 + (q & 3) * 1024, ok ? off : kOOB);
+    for (int j = 0; j < C::ADMA; ++j) {  // 16-row group q % 4 of K-step q / 4
+        const int q = j * NW + wave;
+        tile_rows_issue(a, t, buf + (q >> 2) * 4096, q & 3, q >> 2, lane);
+    }
+    if (KP) {
+#pragma unroll
+        for (int j = 0; j < C::XDMA; ++j) {
+            const int q = j * NW + wave;
+            tile_rows_issue(pj, t, buf + C::A + (q >> 2) * 4096, q & 3, q >> 2, lane);
         }
+        return;
     }
     {
         const unsigned out_img = (unsigned)a.oc1 * plane;
@@ -906,18 +915,19 @@ __device__ __forceinline__ void ring_issue(const ConvArgs &a, int8_t *buf, int m
     }
 }
 
-template <int NW, int KS, bool RELU>
-__global__ __launch_bounds__(64 * NW, (RingCfg<NW, KS>::PER_CU)) void conv1x1_ring_kernel(ConvArgs a, int tiles)
+template <int NW, int KS, int KP, bool RELU>
+__global__ __launch_bounds__(64 * NW, (RingCfg<NW, KS, KP>::PER_CU)) void conv1x1_ring_kernel(ConvArgs a,
+                                                                                               ConvArgs pj,
+                                                                                               int tiles)
 {
-    using C = RingCfg<NW, KS>;
-    __shared__ __attribute__((aligned(1024))) int8_t smem[C::NB * C::BUF];
+    using C = RingCfg<NW, KS, KP>;
+    __shared__ __attribute__((aligned(1024))) int8_t smem[C::LDS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c = lane & 15, g = lane >> 4;
     const int ch0 = 64 * wave;
-    const int HoWo = a.ho * a.wo;
     const int first = blockIdx.x;
     if (first >= tiles) return;
     const int ntile = (tiles - 1 - first) / (int)gridDim.x + 1;
@@ -937,10 +947,23 @@ __global__ __launch_bounds__(64 * NW, (RingCfg<NW, KS>::PER_CU)) void conv1x1_ri
                                     *(const v4i *)(a.shift + ch0 + 4 * c), false, ch0 + 4 * c, a.oc);
         rp = rq_pack(r, mode);
     }
+    v4i wp[KP ? KP : 1][4];  // the projection's weights (KP > 0)
+    RqPacked rpj;
+    int modep = 0;
+    if (KP) {
+#pragma unroll
+        for (int s = 0; s < KP; ++s)
+#pragma unroll
+            for (int tn = 0; tn < 4; ++tn) wp[s][tn] = chain_weights(pj, ch0 + 4 * c + tn, 4 * s + g);
+        RqLane r;
+        modep = rq_setup<false, false>(r, *(const v4i *)(pj.bias + ch0 + 4 * c), *(const v4i *)(pj.mult + ch0 + 4 * c),
+                                       *(const v4i *)(pj.shift + ch0 + 4 * c), false, ch0 + 4 * c, pj.oc);
+        rpj = rq_pack(r, modep);
+    }
 
     auto tile_m0 = [&](int j) { const int t = first + j * (int)gridDim.x; return t < tiles ? t * 64 : a.m; };
 #pragma unroll
-    for (int j = 0; j < C::NB - 1; ++j) ring_issue<NW, KS>(a, smem + j * C::BUF, tile_m0(j), wave, lane);
+    for (int j = 0; j < C::NB - 1; ++j) ring_issue<NW, KS, KP>(a, pj, smem + j * C::BUF, tile_m0(j), wave, lane);
 
     int8_t *y = (int8_t *)a.y;
     const int k4 = lane & 3;
@@ -950,44 +973,90 @@ __global__ __launch_bounds__(64 * NW, (RingCfg<NW, KS>::PER_CU)) void conv1x1_ri
         const int m0 = tile_m0(j);
         wait_vmcnt<(C::NB - 2) * C::DMA>();  // tile j landed (loads complete in issue order)
         ring_barrier();                        // ... for every wave; every wave is done with tile j - 1
-        ring_issue<NW, KS>(a, smem + ((j + C::NB - 1) % C::NB) * C::BUF, tile_m0(j + C::NB - 1), wave, lane);
+        ring_issue<NW, KS, KP>(a, pj, smem + ((j + C::NB - 1) % C::NB) * C::BUF, tile_m0(j + C::NB - 1), wave,
+                               lane);
 
-        int8_t *const Rw = buf + C::A + wave * 4096;
+        // the wave's output region: its shortcut bytes in the slot (requantised in place), or its
+        // own staging region after the ring
+        int8_t *const Rw = KP ? smem + C::NB * C::BUF + wave * 4096 : buf + C::A + wave * 4096;
+        auto contract = [&](v4i (&acc)[4][4], const int8_t *src, const v4i (*wt)[4], int steps, int tm)
+            __attribute__((always_inline)) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {  // two halves of 32 pixels
-            v4i acc[4][4];
+            for (int s = 0; s < steps; ++s) {
+                const v4i af = *(const v4i *)(src + s * 4096 + swz_at(16 * tm + 4 * (c & 3) + (c >> 2), g));
 #pragma unroll
-            for (int s = 0; s < KS; ++s)
+                for (int tn = 0; tn < 4; ++tn)
+                    acc[tm & 1][tn] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, wt[s][tn], s == 0 ? (v4i){0, 0, 0, 0}
+                                                                                                   : acc[tm & 1][tn],
+                                                                            0, 0, 0);
+            }
+        };
+        auto store_rows = [&](auto md, const v4i (&acc)[4][4], int tm, const unsigned *rr)
+            __attribute__((always_inline)) {
+            constexpr int MD = decltype(md)::value;
 #pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const int tm = 2 * h + t;
-                    const v4i af = *(const v4i *)(buf + s * 4096 + swz_at(16 * tm + 4 * (c & 3) + (c >> 2), g));
+            for (int i = 0; i < 4; ++i)
+                *(unsigned *)(Rw + swz_at(16 * tm + 4 * i + g, c >> 2) + 4 * (c & 3)) =
+                    requant_row_p<MD, true, RELU>(acc, tm & 1, i, rp, rr[i]);
+        };
+        if constexpr (KP > 0) {
+            // one 16-pixel row block at a time: the projection, requantised into shortcut words, then
+            // conv3 (keeps the live accumulators to one block)
 #pragma unroll
-                    for (int tn = 0; tn < 4; ++tn)
-                        acc[t][tn] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, w[s][tn], s == 0 ? (v4i){0, 0, 0, 0}
-                                                                                                 : acc[t][tn], 0, 0, 0);
-                }
-            auto rq = [&](auto md) __attribute__((always_inline)) {
-                constexpr int MD = decltype(md)::value;
-                unsigned rr[2][4];
+            for (int tm = 0; tm < 4; ++tm) {
+                v4i acc[4][4];
+                unsigned rr[4];
+                contract(acc, buf + C::A, wp, KP, tm);
+                auto rqp = [&](auto md) __attribute__((always_inline)) {
+                    constexpr int MD = decltype(md)::value;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) rr[i] = requant_row_p<MD, false, false>(acc, tm & 1, i, rpj, 0u);
+                };
+                if (modep == 0)
+                    rqp(Slot0());
+                else if (modep == 1)
+                    rqp(Slot1());
+                else
+                    rqp(Slot2());
+                contract(acc, buf, w, KS, tm);
+                if (mode == 0)
+                    store_rows(Slot0(), acc, tm, rr);
+                else if (mode == 1)
+                    store_rows(Slot1(), acc, tm, rr);
+                else
+                    store_rows(Slot2(), acc, tm, rr);
+            }
+        } else {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {  // two halves of 32 pixels
+                v4i acc[4][4];
+                unsigned rr[2][4];  // the shortcut words of rows 16 (2h + t) + 4i + g, channels 4c ..
 #pragma unroll
                 for (int t = 0; t < 2; ++t)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         rr[t][i] = *(const unsigned *)(Rw + swz_at(16 * (2 * h + t) + 4 * i + g, c >> 2) + 4 * (c & 3));
 #pragma unroll
-                for (int t = 0; t < 2; ++t)
+                for (int s = 0; s < KS; ++s)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        *(unsigned *)(Rw + swz_at(16 * (2 * h + t) + 4 * i + g, c >> 2) + 4 * (c & 3)) =
-                            requant_row_p<MD, true, RELU>(acc, t, i, rp, rr[t][i]);
-            };
-            if (mode == 0)
-                rq(Slot0());
-            else if (mode == 1)
-                rq(Slot1());
-            else
-                rq(Slot2());
+                    for (int t = 0; t < 2; ++t) {
+                        const int tm = 2 * h + t;
+                        const v4i af = *(const v4i *)(buf + s * 4096 + swz_at(16 * tm + 4 * (c & 3) + (c >> 2), g));
+#pragma unroll
+                        for (int tn = 0; tn < 4; ++tn)
+                            acc[t][tn] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, w[s][tn], s == 0 ? (v4i){0, 0, 0, 0}
+                                                                                                     : acc[t][tn], 0, 0, 0);
+                    }
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    if (mode == 0)
+                        store_rows(Slot0(), acc, 2 * h + t, rr[t]);
+                    else if (mode == 1)
+                        store_rows(Slot1(), acc, 2 * h + t, rr[t]);
+                    else
+                        store_rows(Slot2(), acc, 2 * h + t, rr[t]);
+                }
+            }
         }
         wave_lds_sync();  // the wave's own region: no other wave reads it
         v4i v[4];
@@ -1010,11 +1079,12 @@ __global__ __launch_bounds__(64 * NW, (RingCfg<NW, KS>::PER_CU)) void conv1x1_ri
     wait_vmcnt<0>();  // the ring's last (zero-fill) DMAs land before the workgroup's LDS is released
 }
 
-template <int NW, int KS>
-hipError_t launch_ring(const ConvArgs &a, hipStream_t s)
+// pj: the projection (KP > 0) or `a` itself (unused)
+template <int NW, int KS, int KP>
+hipError_t launch_ring(const ConvArgs &a, const ConvArgs &pj, hipStream_t s)
 {
-    using C = RingCfg<NW, KS>;
-    if (answer_query("conv1x1_ring_kernel<%d, %d, %s>", NW, KS, tf(a.relu != 0))) return hipSuccess;
+    using C = RingCfg<NW, KS, KP>;
+    if (answer_query("conv1x1_ring_kernel<%d, %d, %d, %s>", NW, KS, KP, tf(a.relu != 0))) return hipSuccess;
     const long long tiles = (a.m + 63) / 64;
     if (tiles <= 0) return hipSuccess;
     if (tiles > 0x7fffffffLL / 64) return hipErrorInvalidConfiguration;
@@ -1024,11 +1094,11 @@ hipError_t launch_ring(const ConvArgs &a, hipStream_t s)
     const long long slots = (long long)C::PER_CU * cus;
     const long long grid = tiles < slots ? tiles : slots;
     if (a.relu)
-        hipLaunchKernelGGL((conv1x1_ring_kernel<NW, KS, true>), dim3((unsigned)grid), dim3(64 * NW), 0, s, a,
+        hipLaunchKernelGGL((conv1x1_ring_kernel<NW, KS, KP, true>), dim3((unsigned)grid), dim3(64 * NW), 0, s, a, pj,
                            (int)tiles);
     else
-        hipLaunchKernelGGL((conv1x1_ring_kernel<NW, KS, false>), dim3((unsigned)grid), dim3(64 * NW), 0, s, a,
-                           (int)tiles);
+        hipLaunchKernelGGL((conv1x1_ring_kernel<NW, KS, KP, false>), dim3((unsigned)grid), dim3(64 * NW), 0, s, a,
+                           pj, (int)tiles);
     return hipGetLastError();
 }
 
@@ -1086,12 +1156,28 @@ hipError_t launch_conv1x1_proj_chain(const ConvArgs &a, const ConvArgs &pj, cons
     return launch_chain(a, b, &pj, s);
 }
 
+// conv3 (a: 1x1, unit stride, 64 < K <= 128, 512 output channels, its shortcut the projection)
+// with its 1x1 projection pj (unit stride, 128 < K <= 256: the first block of res3, whose stride-2
+// input arrives subsampled) in the persistent ring kernel.
+bool conv1x1_ring_proj_supported(const ConvArgs &a, const ConvArgs &pj)
+{
+    return a.oc == 512 && a.i1 > 2 && a.i1 <= 4 && a.stride == 1 && a.pad == 0 && !a.out_i32 && !a.in_ps &&
+           !a.out_ps && pj.oc == a.oc && pj.i1 > 4 && pj.i1 <= 8 && pj.stride == 1 && pj.pad == 0 && !pj.relu &&
+           !pj.residual && !pj.out_i32 && !pj.in_ps && !pj.out_ps && pj.n == a.n && pj.h == a.ho && pj.w == a.wo &&
+           a.h == a.ho && a.w == a.wo && pj.m == a.m;
+}
+
+hipError_t launch_conv1x1_ring_proj(const ConvArgs &a, const ConvArgs &pj, hipStream_t s)
+{
+    return launch_ring<8, 2, 4>(a, pj, s);
+}
+
 hipError_t launch_conv1x1_small_k(const ConvArgs &a, hipStream_t s)
 {
     // unit-stride layers with a shortcut and 256 or 512 output channels: the persistent ring kernel
     if (a.residual && a.stride == 1 && a.pad == 0 && a.ho == a.h && a.wo == a.w) {
-        if (a.oc == 256) return a.i1 <= 2 ? launch_ring<4, 1>(a, s) : launch_ring<4, 2>(a, s);
-        if (a.oc == 512 && a.i1 > 2) return launch_ring<8, 2>(a, s);
+        if (a.oc == 256) return a.i1 <= 2 ? launch_ring<4, 1, 0>(a, a, s) : launch_ring<4, 2, 0>(a, a, s);
+        if (a.oc == 512 && a.i1 > 2) return launch_ring<8, 2, 0>(a, a, s);
     }
     const bool wide = a.oc1 * 32 > 64;
     if (a.i1 <= 2) return wide ? launch_1x1_res<128, 128, 1>(a, s) : launch_1x1_res<256, 64, 1>(a, s);

@@ -481,6 +481,41 @@ def test_projection_block(ifx, orc, shape):
         np.testing.assert_array_equal(got, exp)
 
 
+# conv3 (64 < K <= 128, 512 output channels) with a unit-stride 1x1 projection (128 < K <= 256) in
+# the persistent ring kernel: (n, h, w, conv3 input channels, projection input channels)
+RING_PROJ_SHAPES = [
+    (4, 28, 28, 128, 256),   # res3.1 after its input was stored subsampled
+    (3, 9, 7, 100, 200),     # ragged last tile, padded channel blocks on both inputs
+    (1, 5, 6, 96, 160),      # one partial tile, three and five K-blocks
+]
+
+
+@pytest.mark.parametrize("shape", RING_PROJ_SHAPES)
+def test_ring_projection(ifx, orc, shape):
+    from oracle.ref import ConvParams
+    n, h, w, c3in, cpin = shape
+    note(f"ring projection {shape}")
+    rng = np.random.default_rng(sum(shape) * 17)
+    t = rand(rng, (n, h, w, c3in), 0, 127)
+    x = rand(rng, (n, h, w, cpin), 0, 127)
+    w3 = rand(rng, (512, 1, 1, c3in), -127, 127)
+    wp = rand(rng, (512, 1, 1, cpin), -127, 127)
+    b3, m3, s3 = params(rng, 512, 0, 20)
+    bp, mp, sp = params(rng, 512, 0, 20)
+    d3 = ifx.conv_desc(n, h, w, c3in, 512, 1, 1, 1, 0, ifx.RESIDUAL | ifx.RELU)
+    dp = ifx.conv_desc(n, h, w, cpin, 512, 1, 1, 1, 0, 0)
+    assert ifx.conv_kernel_name(d3, dp).startswith("conv1x1_ring_kernel<8, 2, 4, true>")
+    y, yw = guarded(ifx.act_bytes(n, h, w, 512))
+    ifx.conv_proj_fused(d3, ifx.pack_act(cu(t)), ifx.pack_weights(d3, cu(w3)), cu(b3), cu(m3), cu(s3),
+                        dp, ifx.pack_act(cu(x)), ifx.pack_weights(dp, cu(wp)), cu(bp), cu(mp), cu(sp), y)
+    torch.cuda.synchronize()
+    check_guards(yw)
+    got = ifx.unpack_act(y.view(n, 16, h, w, 32), 512).cpu().numpy()
+    sc = orc.conv_layer(x, ConvParams(wp, bp, mp, sp, 1, 0), 0)
+    exp = orc.conv_layer(t, ConvParams(w3, b3, m3, s3, 1, 0), ifx.RESIDUAL | ifx.RELU, residual=sc)
+    np.testing.assert_array_equal(got, exp)
+
+
 # ------------------------------------------------------------------ conv3 chained with the next conv1
 # (n, h, w, c_in of conv3, conv1 output channels, conv1 flags): conv3 is 1x1 c_in -> 256 with
 # shortcut and ReLU, conv1 1x1 256 -> N1; pixel counts that are and are not multiples of the
