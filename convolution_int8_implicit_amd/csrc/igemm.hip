@@ -33,11 +33,15 @@
 namespace ifx {
 namespace {
 
-template <int BM, int BN, int ST>
+// BM x BN tiles, a ring of ST stages; each wave owns a 64 x WN sub-tile (WN = 64 or 128: a wider
+// sub-tile reuses each activation fragment for twice the MACs, halving the LDS reads per MAC)
+template <int BM, int BN, int ST, int WN = 64>
 struct IgCfg {
     static constexpr int WAVES_M = BM / 64;
-    static constexpr int WAVES = WAVES_M * (BN / 64);
-    static_assert(WAVES == 4 || WAVES == 8, "four or eight waves, one 64x64 sub-tile each");
+    static constexpr int WNH = WN / 64;  // 64-channel halves of a wave's sub-tile
+    static constexpr int WAVES = WAVES_M * (BN / WN);
+    static_assert(WN == 64 || WN == 128, "64- or 128-channel wave sub-tiles");
+    static_assert(WAVES == 4 || WAVES == 8 || WAVES == 16, "four, eight or sixteen waves");
     static constexpr int THREADS = 64 * WAVES;
     static constexpr int A_CH = BM / 32;  // 32-row chunks of a tile's pixels
     static constexpr int B_CH = BN / 32;  // 32-row chunks of a tile's output channels
@@ -45,18 +49,21 @@ struct IgCfg {
     static constexpr int BI = 2 * B_CH / WAVES;  // weight DMAs per wave per K-step
     static_assert(AI * WAVES == 2 * A_CH && BI * WAVES == 2 * B_CH, "whole DMAs");
     static constexpr int STAGE = (BM + BN) * 64;  // A: [2][BM][32 B], then B: [2][BN][32 B]
-    static constexpr int PARAM = WAVES * 768;     // per wave: bias, mult, shift of its 64 channels
+    static constexpr int PARAM = WAVES * WNH * 768;  // per wave and half: bias, mult, shift of 64 channels
     static constexpr int LPS = AI + BI;          // DMAs per wave per stage
     // ring | parameters | shortcut tile (RES) | parameters of the projection (PROJ)
     static constexpr int lds(bool res) { return ST * STAGE + PARAM + (res ? BM * BN : 0); }  // ring | params | shortcut
-    // at most four waves per SIMD (so up to 128 VGPRs each), as LDS allows
+    // at most four waves per SIMD (so up to 128 VGPRs each; two, with up to 256, for the wide
+    // sub-tile's accumulators), as LDS allows
+    static constexpr int MAXW = WN == 64 ? 16 : 8;
     static constexpr int wg_per_cu(bool res)
     {
-        return kLdsBytes / lds(res) > 16 / WAVES ? 16 / WAVES : kLdsBytes / lds(res);
+        return kLdsBytes / lds(res) > MAXW / WAVES ? MAXW / WAVES : kLdsBytes / lds(res);
     }
     // the epilogue stages each wave's 64x64 output in the ring slot no wave reads any more, or,
     // when the waves' 4 KB parts do not fit one slot, across the ring after a workgroup barrier
-    static constexpr bool STAGE_IN_SLOT = WAVES * 4096 <= STAGE;
+    static constexpr bool STAGE_IN_SLOT = WAVES * WNH * 4096 <= STAGE;
+    static_assert(WAVES * WNH * 4096 <= ST * STAGE, "the output staging fits the ring");
 };
 
 // LDS layouts of one operand block of a stage (32 K-bytes per row, two 16-byte halves h).
@@ -90,6 +97,16 @@ struct Slot {
     static constexpr int value = V;
 };
 
+// f(Slot<I>()), ..., f(Slot<N - 1>()), unrolled at compile time
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    if constexpr (I < N) {
+        f(Slot<I>());
+        static_for<I + 1, N>(f);
+    }
+}
+
 // Requantise the wave's accumulators (MODE picked by a wave vote on the shifts) into the LDS tile
 // at rbase (row stride 64 B), adding the shortcut bytes already there when RES.  ADD_BIAS: the
 // accumulators do not hold the bias yet.
@@ -107,11 +124,12 @@ __device__ __forceinline__ void requant_to_lds(const v4i (&acc)[4][4], int8_t *r
 // bottleneck whose shortcut is the 1x1 projection `pj` of the block input: the tile's
 // projection is computed first and requantised (no ReLU) into the LDS that otherwise receives
 // a shortcut tile, so the shortcut never goes through HBM.
-template <int KH, int KW, int BM, int BN, int ST, bool RES, bool RELU, bool PROJ>
-__global__ __launch_bounds__((IgCfg<BM, BN, ST>::THREADS), (IgCfg<BM, BN, ST>::wg_per_cu(RES)))
+template <int KH, int KW, int BM, int BN, int ST, int WN, bool RES, bool RELU, bool PROJ>
+__global__ __launch_bounds__((IgCfg<BM, BN, ST, WN>::THREADS), (IgCfg<BM, BN, ST, WN>::wg_per_cu(RES)))
 void igemm_kernel(ConvArgs a, ConvArgs pj, int tiles_n, int per_xcd)
 {
-    using C = IgCfg<BM, BN, ST>;
+    using C = IgCfg<BM, BN, ST, WN>;
+    constexpr int WNH = C::WNH;
     constexpr int NWV = C::WAVES;
     static_assert(!PROJ || (RES && KH == 1 && KW == 1), "a projection shortcut feeds a 1x1 shortcut conv");
     static_assert(!PROJ || ST == 2, "the stream switches convolutions one stage ahead");
@@ -121,9 +139,11 @@ void igemm_kernel(ConvArgs a, ConvArgs pj, int tiles_n, int per_xcd)
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm0 = (wave % C::WAVES_M) * 64;
-    const int wn0 = (wave / C::WAVES_M) * 64;
-    int8_t *const Pw = Pm + wave * 768;                 // bias, mult, shift of the wave's 64 channels
-    int8_t *const Rres = Pm + C::PARAM + wave * 4096;  // RES: the wave's [64 pixels][64 B] shortcut
+    const int wn0 = (wave / C::WAVES_M) * WN;
+    // half hh of the wave's channels (64 each): parameters at Pw + 768 hh (bias, mult, shift), the
+    // RES shortcut / output staging [64 pixels][64 B] at Rres + 4096 hh
+    int8_t *const Pw = Pm + wave * WNH * 768;
+    int8_t *const Rres = Pm + C::PARAM + wave * WNH * 4096;
 
     // tile: XCD x (blockIdx & 7) owns M-tiles [x * per_xcd, (x + 1) * per_xcd), so neighbouring
     // pixel tiles (which share 3x3 halo rows) and the N-tiles of one pixel tile share an L2
@@ -146,11 +166,14 @@ void igemm_kernel(ConvArgs a, ConvArgs pj, int tiles_n, int per_xcd)
     // rows 16 apart sit 4 lines (512 B) apart with the same slot; weight row 4c + tn sits at
     // the slot of row 4c XOR 32 tn
     const int a_frag = (g >> 1) * (BM * 32) + a_swz(wm0 + 4 * (c & 3) + (c >> 2), g & 1);
-    int b_frag[4];
+    int b_frag[WNH][4];
 #pragma unroll
-    for (int tn = 0; tn < 4; ++tn) b_frag[tn] = (BM * 64 + (g >> 1) * (BN * 32) + b_swz(wn0 + 4 * c, g & 1)) ^ (tn << 5);
+    for (int hh = 0; hh < WNH; ++hh)
+#pragma unroll
+        for (int tn = 0; tn < 4; ++tn)
+            b_frag[hh][tn] = (BM * 64 + (g >> 1) * (BN * 32) + b_swz(wn0 + 64 * hh + 4 * c, g & 1)) ^ (tn << 5);
 
-    v4i acc[4][4];
+    v4i acc[WNH][4][4];
 
     // ---- per-lane DMA plans of convolution q.  Activation DMA j of wave w fills chunk
     //      (4j + w) % A_CH of block (4j + w) / A_CH: the lane's pixel, its tap-validity mask and
@@ -283,10 +306,10 @@ void igemm_kernel(ConvArgs a, ConvArgs pj, int tiles_n, int per_xcd)
 
     issue(0);
     // per-channel parameters and the shortcut part of this wave
-    auto issue_params = [&](const ConvArgs &q, int8_t *dst) __attribute__((always_inline)) {
+    auto issue_params = [&](const ConvArgs &q, int8_t *dst, int chh) __attribute__((always_inline)) {
         if (lane < 16) {
-            const bool v = ch0 + 4 * lane < q.oc;
-            const unsigned off = v ? (unsigned)(ch0 + 4 * lane) * 4 : kOOB;
+            const bool v = chh + 4 * lane < q.oc;
+            const unsigned off = v ? (unsigned)(chh + 4 * lane) * 4 : kOOB;
             load16_lds(make_rsrc(q.bias, (long long)q.oc * 4), dst, off);
             if (!q.out_i32) {
                 load16_lds(make_rsrc(q.mult, (long long)q.oc * 4), dst + 256, off);
@@ -294,23 +317,28 @@ void igemm_kernel(ConvArgs a, ConvArgs pj, int tiles_n, int per_xcd)
             }
         }
     };
-    issue_params(a, Pw);
+#pragma unroll
+    for (int hh = 0; hh < WNH; ++hh) issue_params(a, Pw + 768 * hh, ch0 + 64 * hh);
     // PROJ: the projection's parameters wait in the wave's shortcut region, which the
     // projection's requantisation overwrites only after reading them
-    if (PROJ) issue_params(pj, Rres);
+    if (PROJ)
+#pragma unroll
+        for (int hh = 0; hh < WNH; ++hh) issue_params(pj, Rres + 4096 * hh, ch0 + 64 * hh);
     if (RES && !PROJ) {
         const v4i rsR = make_rsrc(a.res + (long long)img0 * out_img, (long long)(a.n - img0) * out_img);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int p = m0 + wm0 + 16 * j + (lane >> 2);
-            const int oc = ch0 + (lane & 3) * 16;
-            unsigned off = kOOB;
-            if (p < a.m && oc < a.oc1 * 32) {
-                const int b = fdiv(p, a.howo_mul, a.howo_shr), hw = p - b * HoWo;
-                off = (unsigned)((((long long)(b - img0) * a.oc1 + (oc >> 5)) * HoWo + hw) * 32 + (oc & 31));
+        for (int hh = 0; hh < WNH; ++hh)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int p = m0 + wm0 + 16 * j + (lane >> 2);
+                const int oc = ch0 + 64 * hh + (lane & 3) * 16;
+                unsigned off = kOOB;
+                if (p < a.m && oc < a.oc1 * 32) {
+                    const int b = fdiv(p, a.howo_mul, a.howo_shr), hw = p - b * HoWo;
+                    off = (unsigned)((((long long)(b - img0) * a.oc1 + (oc >> 5)) * HoWo + hw) * 32 + (oc & 31));
+                }
+                load16_lds_stream(rsR, Rres + 4096 * hh + j * 1024, off);
             }
-            load16_lds_stream(rsR, Rres + j * 1024, off);
-        }
     }
     // Stages after the tile inputs, so the first wait needs no count of them.  A stream that fits
     // the ring (nsteps <= ST, the short 1x1 convolutions) is requested whole, up front; a longer
@@ -339,7 +367,7 @@ void igemm_kernel(ConvArgs a, ConvArgs pj, int tiles_n, int per_xcd)
     // ever cleared; the per-channel bias enters in the requantisation (folded into its added
     // constant, free in the common mode).
 
-    static_assert(ST == 2 || ST == 3, "the waits below count at most one later stage in flight");
+    static_assert(ST >= 2 && ST <= 4, "a ring of two to four stages");
     // step s reads ring slot SL = s % ST, a compile-time constant so the fragment addresses
     // need no per-step arithmetic
     auto step = [&](auto slot, auto first, int s) __attribute__((always_inline)) {
@@ -349,24 +377,32 @@ void igemm_kernel(ConvArgs a, ConvArgs pj, int tiles_n, int per_xcd)
         // before them may stay in flight (one when up front, ST-2 in the ring)
         if (upfront ? s + 1 < nsteps : (ST > 2 && s + ST - 2 < nsteps))
             wait_vmcnt<(ST > 2 ? ST - 2 : 1) * C::LPS>();
+        else if (!upfront && ST > 3 && s + 1 < nsteps)
+            wait_vmcnt<C::LPS>();  // the ring's tail: one later stage in flight
         else
             wait_vmcnt<0>();
         ring_barrier();  // ... and every other wave's; stage s-1's slot is free again
         if (!upfront && s + ST - 1 < nsteps) issue((SL + ST - 1) % ST);
         const int8_t *st = smem + SL * C::STAGE;
-        v4i af[4], bf[4];
+        v4i af[4], bf[WNH][4];
 #pragma unroll
         for (int tm = 0; tm < 4; ++tm) af[tm] = *(const v4i *)(st + a_frag + 512 * tm);
 #pragma unroll
-        for (int tn = 0; tn < 4; ++tn) bf[tn] = *(const v4i *)(st + b_frag[tn]);
+        for (int hh = 0; hh < WNH; ++hh)
 #pragma unroll
-        for (int tm = 0; tm < 4; ++tm)
+            for (int tn = 0; tn < 4; ++tn) bf[hh][tn] = *(const v4i *)(st + b_frag[hh][tn]);
 #pragma unroll
-            for (int tn = 0; tn < 4; ++tn)
-                if constexpr (FIRST)
-                    acc[tm][tn] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[tm], bf[tn], (v4i){0, 0, 0, 0}, 0, 0, 0);
-                else
-                    acc[tm][tn] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[tm], bf[tn], acc[tm][tn], 0, 0, 0);
+        for (int hh = 0; hh < WNH; ++hh)
+#pragma unroll
+            for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+                for (int tn = 0; tn < 4; ++tn)
+                    if constexpr (FIRST)
+                        acc[hh][tm][tn] =
+                            __builtin_amdgcn_mfma_i32_16x16x64_i8(af[tm], bf[hh][tn], (v4i){0, 0, 0, 0}, 0, 0, 0);
+                    else
+                        acc[hh][tm][tn] =
+                            __builtin_amdgcn_mfma_i32_16x16x64_i8(af[tm], bf[hh][tn], acc[hh][tm][tn], 0, 0, 0);
     };
     // fused form (ST == 2): steps s0 <= s < s1 of one contraction, none its first, slots alternating
     // inside the loop (a run-time slot choice per step would merge two register allocations of the
@@ -399,7 +435,10 @@ void igemm_kernel(ConvArgs a, ConvArgs pj, int tiles_n, int per_xcd)
             run_range(n1 - 1, n1);
         }
         // the projection is complete: its requantised output (no ReLU) is the shortcut
-        requant_to_lds<false, false, true>(acc, Rres + g * 64 + 4 * c, Rres, c, ocl, pj.oc);
+#pragma unroll
+        for (int hh = 0; hh < WNH; ++hh)
+            requant_to_lds<false, false, true>(acc[hh], Rres + 4096 * hh + g * 64 + 4 * c, Rres + 4096 * hh, c,
+                                               ocl + 64 * hh, pj.oc);
         if (n1 & 1)
             step(Slot<1>(), Slot<1>(), n1);
         else
@@ -407,79 +446,92 @@ void igemm_kernel(ConvArgs a, ConvArgs pj, int tiles_n, int per_xcd)
         run_range(n1 + 1, nsteps);
     } else {
         step(Slot<0>(), Slot<1>(), 0);
-        if (1 < nsteps) step(Slot<1>(), Slot<0>(), 1);
-        if (ST > 2 && 2 < nsteps) step(Slot<ST - 1>(), Slot<0>(), 2);
-        for (int s = ST; s < nsteps; s += ST) {
-            step(Slot<0>(), Slot<0>(), s);
-            if (s + 1 < nsteps) step(Slot<1>(), Slot<0>(), s + 1);
-            if (ST > 2 && s + 2 < nsteps) step(Slot<ST - 1>(), Slot<0>(), s + 2);
-        }
+        static_for<1, ST>([&](auto sl) __attribute__((always_inline)) {
+            if (decltype(sl)::value < nsteps) step(sl, Slot<0>(), decltype(sl)::value);
+        });
+        for (int s = ST; s < nsteps; s += ST)
+            static_for<0, ST>([&](auto sl) __attribute__((always_inline)) {
+                if (s + decltype(sl)::value < nsteps) step(sl, Slot<0>(), s + decltype(sl)::value);
+            });
     }
     if (a.out_i32) {
         // a split-K part writes its own slice of partial sums; the bias is added once, after the sum
         int32_t *y = (int32_t *)a.y + (a.ksplit > 1 ? (long long)blockIdx.y * a.m * a.oc : 0LL);
-        const bool vec = (a.oc & 3) == 0 && ocl + 3 < a.oc;
-        const v4i bias4 = a.ksplit > 1 ? (v4i){0, 0, 0, 0}
-                                       : *(const v4i *)(Pw + c * 16);  // zero past Oc (out-of-range DMA lanes)
 #pragma unroll
-        for (int tm = 0; tm < 4; ++tm)
+        for (int hh = 0; hh < WNH; ++hh) {
+            const int oh = ocl + 64 * hh;
+            const bool vec = (a.oc & 3) == 0 && oh + 3 < a.oc;
+            const v4i bias4 = a.ksplit > 1 ? (v4i){0, 0, 0, 0}
+                                           : *(const v4i *)(Pw + 768 * hh + c * 16);  // zero past Oc
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int p = pbase + 16 * tm + 4 * i + g;
-                if (p >= a.m) continue;
-                const long long off = (long long)p * a.oc + ocl;
-                const v4i v = (v4i){acc[tm][0][i], acc[tm][1][i], acc[tm][2][i], acc[tm][3][i]} + bias4;
-                if (vec) {
-                    *(v4i *)(y + off) = v;
-                } else {
+            for (int tm = 0; tm < 4; ++tm)
 #pragma unroll
-                    for (int tn = 0; tn < 4; ++tn)
-                        if (ocl + tn < a.oc) y[off + tn] = v[tn];
+                for (int i = 0; i < 4; ++i) {
+                    const int p = pbase + 16 * tm + 4 * i + g;
+                    if (p >= a.m) continue;
+                    const long long off = (long long)p * a.oc + oh;
+                    const v4i v =
+                        (v4i){acc[hh][tm][0][i], acc[hh][tm][1][i], acc[hh][tm][2][i], acc[hh][tm][3][i]} + bias4;
+                    if (vec) {
+                        *(v4i *)(y + off) = v;
+                    } else {
+#pragma unroll
+                        for (int tn = 0; tn < 4; ++tn)
+                            if (oh + tn < a.oc) y[off + tn] = v[tn];
+                    }
                 }
-            }
+        }
         return;
     }
     // staging: the shortcut tile itself (requantised in place), else free ring memory
     if (!RES && !C::STAGE_IN_SLOT) ring_barrier();
-    int8_t *const Rw = RES ? Rres : smem + (C::STAGE_IN_SLOT ? (nsteps % ST) * C::STAGE : 0) + wave * 4096;
-    requant_to_lds<RES, RELU, true>(acc, Rw + g * 64 + 4 * c, Pw, c, ocl, a.oc);
+    int8_t *const Rw =
+        RES ? Rres : smem + (C::STAGE_IN_SLOT ? (nsteps % ST) * C::STAGE : 0) + wave * WNH * 4096;
+#pragma unroll
+    for (int hh = 0; hh < WNH; ++hh)
+        requant_to_lds<RES, RELU, true>(acc[hh], Rw + 4096 * hh + g * 64 + 4 * c, Pw + 768 * hh, c, ocl + 64 * hh,
+                                        a.oc);
     wave_lds_sync();
 
-    // 16-byte stores of the wave's 64 pixels x 64 channels
+    // 16-byte stores of the wave's 64 pixels x 64 (or 128) channels
+    if (pbase >= a.m) return;
     int8_t *y = (int8_t *)a.y;
     const int k = lane & 3;
-    const int och = ch0 + 16 * k;  // first channel of this lane's chunk
-    if (och >= a.oc1 * 32 || pbase >= a.m) return;
     const int b0 = fdiv(pbase, a.howo_mul, a.howo_shr);
     const int hw0 = pbase - b0 * HoWo;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int prow = 16 * j + (lane >> 2);
-        if (pbase + prow >= a.m) break;
-        int b = b0, hw = hw0 + prow;
-        while (hw >= HoWo) {
-            hw -= HoWo;
-            ++b;
+    for (int hh = 0; hh < WNH; ++hh) {
+        const int och = ch0 + 64 * hh + 16 * k;  // first channel of this lane's chunk
+        if (och >= a.oc1 * 32) break;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int prow = 16 * j + (lane >> 2);
+            if (pbase + prow >= a.m) break;
+            int b = b0, hw = hw0 + prow;
+            while (hw >= HoWo) {
+                hw -= HoWo;
+                ++b;
+            }
+            const v4i v = *(const v4i *)(Rw + 4096 * hh + prow * 64 + 16 * k);
+            long long pix = hw;
+            if (a.out_ps) {  // phase-split output: the pixel's parity plane, then its place in it
+                const int oy = fdiv(hw, a.wo_mul, a.wo_shr), ox = hw - oy * a.wo;
+                pix = (long long)((oy & 1) * 2 + (ox & 1)) * (HoWo >> 2) + (oy >> 1) * (a.wo >> 1) + (ox >> 1);
+            }
+            int8_t *dst = y + (((long long)b * a.oc1 + (och >> 5)) * HoWo + pix) * 32 + (och & 31);
+            if (RES)
+                store16_stream(dst, v);
+            else
+                *(v4i *)dst = v;
         }
-        const v4i v = *(const v4i *)(Rw + prow * 64 + 16 * k);
-        long long pix = hw;
-        if (a.out_ps) {  // phase-split output: the pixel's parity plane, then its place in it
-            const int oy = fdiv(hw, a.wo_mul, a.wo_shr), ox = hw - oy * a.wo;
-            pix = (long long)((oy & 1) * 2 + (ox & 1)) * (HoWo >> 2) + (oy >> 1) * (a.wo >> 1) + (ox >> 1);
-        }
-        int8_t *dst = y + (((long long)b * a.oc1 + (och >> 5)) * HoWo + pix) * 32 + (och & 31);
-        if (RES)
-            store16_stream(dst, v);
-        else
-            *(v4i *)dst = v;
     }
 }
 
-template <int KH, int KW, int BM, int BN, int ST, bool RES, bool PROJ>
+template <int KH, int KW, int BM, int BN, int ST, bool RES, bool PROJ, int WN = 64>
 hipError_t launch_ig(const ConvArgs &a, const ConvArgs &pj, hipStream_t s)
 {
-    if (answer_query("igemm_kernel<%d, %d, %d, %d, %d, %s, %s, %s>", KH, KW, BM, BN, ST, tf(RES), tf(a.relu != 0),
-                     tf(PROJ)))
+    if (answer_query("igemm_kernel<%d, %d, %d, %d, %d, %d, %s, %s, %s>", KH, KW, BM, BN, ST, WN, tf(RES),
+                     tf(a.relu != 0), tf(PROJ)))
         return hipSuccess;
     const int tiles_n = (a.oc1 * 32 + BN - 1) / BN;
     const long long tiles_m = (a.m + BM - 1) / BM;
@@ -492,11 +544,13 @@ hipError_t launch_ig(const ConvArgs &a, const ConvArgs &pj, hipStream_t s)
     if (imgs * (long long)a.i1 * a.h * a.w * 32 >= 0x7fffffffLL) return hipErrorInvalidValue;
     if (PROJ && imgs * (long long)pj.i1 * pj.h * pj.w * 32 >= 0x7fffffffLL) return hipErrorInvalidValue;
     if (a.relu)
-        hipLaunchKernelGGL((igemm_kernel<KH, KW, BM, BN, ST, RES, true, PROJ>), dim3((unsigned)grid, (unsigned)(a.ksplit > 1 ? a.ksplit : 1)), dim3(IgCfg<BM, BN, ST>::THREADS), 0, s,
-                           a, pj, tiles_n, (int)per);
+        hipLaunchKernelGGL((igemm_kernel<KH, KW, BM, BN, ST, WN, RES, true, PROJ>),
+                           dim3((unsigned)grid, (unsigned)(a.ksplit > 1 ? a.ksplit : 1)),
+                           dim3(IgCfg<BM, BN, ST, WN>::THREADS), 0, s, a, pj, tiles_n, (int)per);
     else
-        hipLaunchKernelGGL((igemm_kernel<KH, KW, BM, BN, ST, RES, false, PROJ>), dim3((unsigned)grid, (unsigned)(a.ksplit > 1 ? a.ksplit : 1)), dim3(IgCfg<BM, BN, ST>::THREADS), 0,
-                           s, a, pj, tiles_n, (int)per);
+        hipLaunchKernelGGL((igemm_kernel<KH, KW, BM, BN, ST, WN, RES, false, PROJ>),
+                           dim3((unsigned)grid, (unsigned)(a.ksplit > 1 ? a.ksplit : 1)),
+                           dim3(IgCfg<BM, BN, ST, WN>::THREADS), 0, s, a, pj, tiles_n, (int)per);
     return hipGetLastError();
 }
 
@@ -517,6 +571,12 @@ hipError_t launch_ig_k(const ConvArgs &a, hipStream_t s)
     // faster (28x28x256: 147 -> 131 us per 1024 images)
     if (KH == 3 && a.stride == 2 && a.oc1 * 32 >= 256 && !a.in_ps)
         return launch_ig<3, 3, 128, 256, ST, false, false>(a, a, s);
+    // 3x3 layers with 512 output channels, and the phase-split strided ones with 256 or more: four
+    // waves of 64x128 sub-tiles on a three-stage ring (two workgroups per CU) read each activation
+    // fragment for twice the MACs; 5-12 % faster there (7x7x512: 112 -> 106 us, strided 14x14x512:
+    // 129 -> 113 us per 1024 images), slower for 256 channels at unit stride and for 128
+    if (KH == 3 && !a.out_i32 && (a.oc1 * 32 >= 512 || (a.in_ps && a.oc1 * 32 >= 256)))
+        return launch_ig<3, 3, 128, 256, 3, false, false, 128>(a, a, s);
     return wide ? launch_ig<KH, KW, 128, 128, ST, false, false>(a, a, s)
                 : launch_ig<KH, KW, 256, 64, ST, false, false>(a, a, s);
 }
@@ -526,6 +586,7 @@ hipError_t launch_ig_k(const ConvArgs &a, hipStream_t s)
 hipError_t launch_conv_proj(const ConvArgs &a, const ConvArgs &pj, hipStream_t s)
 {
     if (conv1x1_proj_supported(a, pj)) return launch_conv1x1_proj(a, pj, s);
+    if (conv1x1_ring_proj_supported(a, pj)) return launch_conv1x1_ring_proj(a, pj, s);
     constexpr int ST = 2;
     if (a.oc1 * 32 > 64) return launch_ig<1, 1, 128, 128, ST, true, true>(a, pj, s);
     return launch_ig<1, 1, 256, 64, ST, true, true>(a, pj, s);

@@ -176,7 +176,7 @@ FUSED_SHAPES = [
     (1, 11, 10, 192, 136, 1, 2, 0),  # strided, exactly 3 K-steps, ragged output channels
     (1, 6, 7, 256, 384, 1, 1, 0),    # 4 K-steps through the ring
     (2, 5, 5, 320, 256, 1, 1, 0),    # 5 K-steps through the ring
-    # strided 3x3 with >= 256 output channels: 128x256 tiles of eight waves
+    # strided 3x3 with >= 256 output channels on the plain layout: 128x256 tiles of eight waves
     (2, 9, 11, 64, 256, 3, 2, 1),
     (1, 8, 7, 96, 288, 3, 2, 1),     # ragged output channels, odd channel-block count
     # stride-1 3x3, <= 64 input channels, 48 <= W <= 62: the haloed-window kernel (flags 0 and 1;
@@ -185,6 +185,10 @@ FUSED_SHAPES = [
     (3, 13, 50, 40, 96, 3, 1, 1),    # ragged last band (13 rows), two channel blocks, padded channels
     (1, 7, 62, 32, 64, 3, 1, 1),     # widest window (pitch 64), one channel block
     (2, 5, 48, 64, 200, 3, 1, 1),    # narrowest, four output-channel tiles, padding in the last
+    # 3x3 with >= 512 output channels (flags 0 and 1): four waves of 64x128 sub-tiles on a
+    # three-stage ring; with a shortcut the general kernel runs
+    (2, 9, 11, 64, 512, 3, 1, 1),    # two 128x256 tiles across images, a ragged pixel tile
+    (1, 7, 7, 96, 520, 3, 1, 1),     # ragged output channels: a partial 64-channel half
 ]
 
 
@@ -265,7 +269,7 @@ PHASE_OUT_SHAPES = [
     (1, 12, 8, 96, 64, 3, 1, 1),      # a 3x3 producer (256x64 tiles)
 ]
 PHASE_IN_SHAPES = [
-    (2, 28, 28, 256, 256, 3, 2, 1),   # res4.1 conv2 (128x256 tiles)
+    (2, 28, 28, 256, 256, 3, 2, 1),   # res4.1 conv2 (128x256 tiles of 64x128 sub-tiles)
     (2, 56, 56, 128, 128, 3, 2, 1),   # res3.1 conv2
     (3, 14, 14, 512, 512, 3, 2, 1),   # res5.1 conv2: 7x7 outputs
     (1, 10, 6, 96, 72, 3, 2, 1),      # odd output width, ragged channels
