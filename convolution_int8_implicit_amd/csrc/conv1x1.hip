@@ -174,7 +174,7 @@ __device__ __forceinline__ void store_wave_tile(const ConvArgs &a, const int8_t 
 }
 
 template <int BM, int BN, int NST, bool RES, bool RELU>
-__global__ __launch_bounds__((C1Cfg<BM, BN, NST>::THREADS), (C1Cfg<BM, BN, NST>::WG_PER_CU))
+__global__ __launch_bounds__((C1Cfg<BM, BN, NST>::THREADS), (waves_per_simd(C1Cfg<BM, BN, NST>::THREADS, C1Cfg<BM, BN, NST>::WG_PER_CU)))
 void conv1x1_kernel(ConvArgs a, int tiles_n)
 {
     using C = C1Cfg<BM, BN, NST>;
@@ -268,7 +268,8 @@ struct C1PCfg {
 };
 
 template <int BM, int BN, int NSP, int NSA, bool RELU>
-__global__ __launch_bounds__((C1PCfg<BM, BN, NSP, NSA>::THREADS), (C1PCfg<BM, BN, NSP, NSA>::WG_PER_CU))
+__global__ __launch_bounds__((C1PCfg<BM, BN, NSP, NSA>::THREADS),
+                              (waves_per_simd(C1PCfg<BM, BN, NSP, NSA>::THREADS, C1PCfg<BM, BN, NSP, NSA>::WG_PER_CU)))
 void conv1x1_proj_kernel(ConvArgs a, ConvArgs pj, int tiles_n)
 {
     using P = C1PCfg<BM, BN, NSP, NSA>;
@@ -552,7 +553,7 @@ __device__ __forceinline__ int chain_ch2(int wave, int mt, int r)
 }
 
 template <int NW, int KS, int N1, bool RELU1, bool EVEN, bool PROJ>
-__global__ __launch_bounds__(64 * NW, (ChainLay<NW, KS, PROJ>::PER_CU)) void conv1x1_chain_kernel(ConvArgs a,
+__global__ __launch_bounds__(64 * NW, (waves_per_simd(64 * NW, ChainLay<NW, KS, PROJ>::PER_CU))) void conv1x1_chain_kernel(ConvArgs a,
                                                                                                    ConvArgs b,
                                                                                                    ConvArgs pj,
                                                                                                    int tiles)
@@ -916,7 +917,7 @@ __device__ __forceinline__ void ring_issue(const ConvArgs &a, const ConvArgs &pj
 }
 
 template <int NW, int KS, int KP, bool RELU>
-__global__ __launch_bounds__(64 * NW, (RingCfg<NW, KS, KP>::PER_CU)) void conv1x1_ring_kernel(ConvArgs a,
+__global__ __launch_bounds__(64 * NW, (waves_per_simd(64 * NW, RingCfg<NW, KS, KP>::PER_CU))) void conv1x1_ring_kernel(ConvArgs a,
                                                                                                ConvArgs pj,
                                                                                                int tiles)
 {

@@ -104,6 +104,11 @@ namespace ifx {
 typedef ifx_v4i v4i;
 
 constexpr int kLdsBytes = 160 * 1024;  // LDS per CU on gfx950
+// The second operand of __launch_bounds__ on this target is the minimum number of waves per SIMD
+// (which caps the registers per wave at 512 / that), not workgroups per CU: workgroups of
+// `threads` threads, `per_cu` of them resident on a CU's four SIMDs.
+constexpr int waves_per_simd(int threads, int per_cu) { return (threads / 64 * per_cu + 3) / 4; }
+
 constexpr unsigned kOOB = 0x80000000u;  // offset past every buffer range: loads return zero
 constexpr int kCachePolicyNT = 2;       // buffer instruction cache-policy operand: non-temporal
 

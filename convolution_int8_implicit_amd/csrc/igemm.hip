@@ -125,7 +125,8 @@ __device__ __forceinline__ void requant_to_lds(const v4i (&acc)[4][4], int8_t *r
 // projection is computed first and requantised (no ReLU) into the LDS that otherwise receives
 // a shortcut tile, so the shortcut never goes through HBM.
 template <int KH, int KW, int BM, int BN, int ST, int WN, bool RES, bool RELU, bool PROJ>
-__global__ __launch_bounds__((IgCfg<BM, BN, ST, WN>::THREADS), (IgCfg<BM, BN, ST, WN>::wg_per_cu(RES)))
+__global__ __launch_bounds__((IgCfg<BM, BN, ST, WN>::THREADS),
+                              (waves_per_simd(IgCfg<BM, BN, ST, WN>::THREADS, IgCfg<BM, BN, ST, WN>::wg_per_cu(RES))))
 void igemm_kernel(ConvArgs a, ConvArgs pj, int tiles_n, int per_xcd)
 {
     using C = IgCfg<BM, BN, ST, WN>;
@@ -617,7 +618,7 @@ constexpr int kHaloWinDma = kHaloWin / 1024 / 8;        // window DMAs per wave 
 static_assert(kHaloWinDma * 8 * 1024 == kHaloWin, "whole window DMAs per wave");
 
 template <bool RELU>
-__global__ __launch_bounds__(512, 1) void conv3x3_halo_kernel(ConvArgs a, int bands, int tiles_n, int per_wg)
+__global__ __launch_bounds__(512, waves_per_simd(512, 1)) void conv3x3_halo_kernel(ConvArgs a, int bands, int tiles_n, int per_wg)
 {
     __shared__ __attribute__((aligned(1024))) int8_t smem[kHaloLds];
     int8_t *const WB = smem;                      // [tap][block][64 rows][32 B], slots as b_swz

@@ -350,7 +350,7 @@ __device__ __forceinline__ void compute_unit(const StemArgs &a, const Unit &g, c
 constexpr int kStemPerCu = 2;
 
 template <int PATH>
-__global__ __launch_bounds__(kThreads, kStemPerCu) void stem_kernel(StemArgs a, int units, int per_xcd)
+__global__ __launch_bounds__(kThreads, waves_per_simd(kThreads, kStemPerCu)) void stem_kernel(StemArgs a, int units, int per_xcd)
 {
     __shared__ __attribute__((aligned(1024))) int8_t sWin[kWinBytes];
     __shared__ __attribute__((aligned(1024))) int8_t sStage[PATH == kNhwc3 ? kStageBytes : 16];
