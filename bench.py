@@ -259,7 +259,7 @@ def net_kernel_names(net_spec, nb: int, nhwc: bool = True) -> list:
                                                desc(nxt.c1, h2, h2, ifx.OUT_PHASE if nps else 0))
         if b.proj is not None:
             dp = desc(b.proj, h, w)
-            if x_even:
+            if x_even:  # the block input's even pixels (only them, or a second copy of them)
                 dp.stride, dp.h, dp.w = 1, (h + 1) // 2, (w + 1) // 2
             if nxt is not None:
                 chain = ifx.conv_proj_chain_kernel_name(desc(b.c3, h2, h2), dp,
@@ -270,7 +270,9 @@ def net_kernel_names(net_spec, nb: int, nhwc: bool = True) -> list:
         else:
             names.append(ifx.conv_kernel_name(desc(b.c3, h2, h2)))
         have_t1 = chain is not None
-        x_even = have_t1 and y_even
+        # an unchained conv3 stores the even pixels a second time for a stride-2 projection
+        x_even = (have_t1 and y_even) or (chain is None and b.proj is None and nxt is not None
+                                          and reads_input_even(nxt) and ifx.conv_even_supported(desc(b.c3, h2, h2)))
         t1_ps = have_t1 and nps
         h = w = h2
     return names
@@ -620,6 +622,8 @@ def main():
         h = ww = 56
         state = {"cur": cur, "nxt": nxt}
         have_t1 = x_even = t1_ps = False
+        xe_buf = None  # the even-pixel copy an unchained conv3 leaves for a stride-2 projection
+        x_xe = False
 
         def phase_in_ok(d):  # a stride-2 3x3 reading the phase-split layout (the driver's rule)
             q = ifx.ConvDesc.from_buffer_copy(d)
@@ -638,8 +642,9 @@ def main():
             if t1_ps:
                 c2.desc.flags |= ifx.IN_PHASE
             pj = with_batch(db.proj, nb) if db.proj is not None else None
-            if pj is not None and x_even:  # the projection reads the subsampled block input
+            if pj is not None and (x_even or x_xe):  # the projection reads the subsampled block input
                 pj.desc.stride, pj.desc.h, pj.desc.w = 1, (pj.desc.h + 1) // 2, (pj.desc.w + 1) // 2
+            pj_in = xe_buf if x_xe else "cur"
             h2 = c2.out_hw[0]
             nb_blk = net.blocks[bi + 1] if bi + 1 < len(net.blocks) else None
             c1n = with_batch(nb_blk.convs[0], nb) if nb_blk is not None else None
@@ -661,10 +666,16 @@ def main():
                     c.run(xin, o, res, stream)
                 return f
 
-            def mk_proj(c3_, pj_):
+            def mk_proj(c3_, pj_, px):
                 def f():
                     ifx.conv_proj_fused(c3_.desc, t2, c3_.w_blk, c3_.bias, c3_.mult, c3_.shift, pj_.desc,
-                                        state["cur"], pj_.w_blk, pj_.bias, pj_.mult, pj_.shift, state["nxt"], stream)
+                                        state[px] if isinstance(px, str) else px, pj_.w_blk, pj_.bias, pj_.mult,
+                                        pj_.shift, state["nxt"], stream)
+                return f
+            def mk_even(c3_, ye):
+                def f():
+                    ifx.conv_fused_even(c3_.desc, t2, c3_.w_blk, c3_.bias, c3_.mult, c3_.shift, state["cur"],
+                                        state["nxt"], ye, stream)
                 return f
             def mk_chain(c3_, c1n_):
                 def f():
@@ -686,12 +697,21 @@ def main():
                                                   pchain, mk_pchain(c3, pj, c1n)))
                 chain = pchain
             elif pj is not None:
-                launches.append(proj_launch(c3, pj, bs.c3, bs.proj, nb, h2, h2, h, ww, mk_proj(c3, pj)))
+                launches.append(proj_launch(c3, pj, bs.c3, bs.proj, nb, h2, h2, h, ww, mk_proj(c3, pj, pj_in)))
             elif chain is not None:
                 launches.append(chain_launch(c3c, c1n, bs.c3, wl.net.blocks[bi + 1].c1, nb, h2, h2, chain,
                                              mk_chain(c3c, c1n), y_even))
+            elif y_even and ifx.conv_even_supported(c3.desc):
+                # conv3 alone, storing its output's even pixels a second time for the next block's
+                # stride-2 projection (the driver's rule)
+                eb = ifx.act_bytes(nb, (h2 + 1) // 2, (h2 + 1) // 2, bs.c3.c_out)
+                if xe_buf is None or xe_buf.numel() < eb:
+                    xe_buf = torch.empty(eb, dtype=torch.int8, device="cuda")
+                name, ops_, byts_, _ = conv_launch(c3, bs.c3, nb, h2, h2, None)
+                launches.append((name, ops_, byts_ + eb, mk_even(c3, xe_buf)))
             else:
                 launches.append(conv_launch(c3, bs.c3, nb, h2, h2, mk(c3, t2, "nxt", "cur")))
+            x_xe = chain is None and pj is None and y_even and ifx.conv_even_supported(c3.desc)
             have_t1 = chain is not None
             x_even = have_t1 and y_even
             t1_ps = have_t1 and bool(c1n.desc.flags & ifx.OUT_PHASE)

@@ -23,7 +23,7 @@ import torch
 __all__ = [
     "RELU", "RESIDUAL", "MAXPOOL", "OUT_I32", "INPUT_NHWC", "OUT_EVEN", "OUT_PHASE", "IN_PHASE", "IfxError", "ConvDesc", "BlockParams", "NetParams", "lib",
     "conv_desc", "conv_validate", "conv_out_dims", "act_bytes", "wpack_bytes", "pack_act", "unpack_act",
-    "pack_weights", "conv_fused", "conv_chain_fused", "conv_chain_kernel_name", "conv_proj_chain_fused",
+    "pack_weights", "conv_fused", "conv_fused_even", "conv_even_supported", "conv_chain_fused", "conv_chain_kernel_name", "conv_proj_chain_fused",
     "conv_proj_chain_kernel_name", "conv_kernel_name",
     "block_workspace_bytes", "block_forward", "block_forward_noalloc",
     "BLOCK_SCRATCH_BYTES", "net_workspace_bytes",
@@ -95,6 +95,8 @@ def lib() -> ctypes.CDLL:
         "ifx_unpack_act": ([vp, vp, i32, i32, i32, i32, vp], i32),
         "ifx_pack_weights": ([D, vp, vp, vp], i32),
         "ifx_conv_fused": ([D, vp, vp, vp, vp, vp, vp, vp, vp], i32),
+        "ifx_conv_fused_even": ([D, vp, vp, vp, vp, vp, vp, vp, vp, vp], i32),
+        "ifx_conv_even_supported": ([D], i32),
         "ifx_conv_proj_fused": ([D, vp, vp, vp, vp, vp, D, vp, vp, vp, vp, vp, vp, vp], i32),
         "ifx_block_workspace_bytes": ([ctypes.POINTER(BlockParams)], sz),
         "ifx_block_forward": ([ctypes.POINTER(BlockParams), vp, vp, vp, sz, vp], i32),
@@ -209,6 +211,18 @@ def conv_fused(d: ConvDesc, x_blk, w_blk, bias, mult, shift, residual, y, stream
     _dev(x_blk, w_blk, bias, mult, shift, residual, y)
     _check(lib().ifx_conv_fused(ctypes.byref(d), _ptr(x_blk), _ptr(w_blk), _ptr(bias), _ptr(mult), _ptr(shift),
                                 _ptr(residual), _ptr(y), _stream(stream)), "ifx_conv_fused")
+
+
+def conv_fused_even(d: ConvDesc, x_blk, w_blk, bias, mult, shift, residual, y, y_even, stream=None) -> None:
+    """ifx_conv_fused that also writes the output's even pixels densely to y_even (ifx_conv_fused_even)."""
+    _dev(x_blk, w_blk, bias, mult, shift, residual, y, y_even)
+    _check(lib().ifx_conv_fused_even(ctypes.byref(d), _ptr(x_blk), _ptr(w_blk), _ptr(bias), _ptr(mult), _ptr(shift),
+                                     _ptr(residual), _ptr(y), _ptr(y_even), _stream(stream)), "ifx_conv_fused_even")
+
+
+def conv_even_supported(d: ConvDesc) -> bool:
+    """Whether ifx_conv_fused_even(d, ...) runs (host-only query)."""
+    return bool(lib().ifx_conv_even_supported(ctypes.byref(d)))
 
 
 def conv_proj_fused(d3: ConvDesc, t_blk, w3_blk, bias3, mult3, shift3, dp: ConvDesc, x_blk, wp_blk, biasp, multp,

@@ -38,6 +38,7 @@ struct ArmedQuery {
     {
         q.name[0] = 0;
         q.answered = false;
+        q.even_copy = false;
         ifx::armed_query() = &q;
     }
     ~ArmedQuery() { ifx::armed_query() = nullptr; }
@@ -210,6 +211,7 @@ ifx::ConvArgs conv_args(const ifx_conv_desc *d, const Dims &dm, const int8_t *x,
     a.residual = (d->flags & IFX_RESIDUAL) ? 1 : 0;
     a.out_i32 = (d->flags & IFX_OUT_I32) ? 1 : 0;
     a.out_even = 0;
+    a.y_even = nullptr;
     a.in_ps = (d->flags & IFX_IN_PHASE) ? 1 : 0;
     a.out_ps = (d->flags & IFX_OUT_PHASE) ? 1 : 0;
     a.ksplit = 1;
@@ -218,6 +220,19 @@ ifx::ConvArgs conv_args(const ifx_conv_desc *d, const Dims &dm, const int8_t *x,
     ifx::fastdiv_magic((unsigned)dm.wo, &a.wo_mul, &a.wo_shr);
     ifx::fastdiv_magic((unsigned)a.o2, &a.o2_mul, &a.o2_shr);
     return a;
+}
+
+// The network driver's rule too: the kernel that runs d (with split-K partial sums of part_bytes
+// available) writes an even-pixel copy.
+bool even_copy_ok(const ifx_conv_desc *d, const Dims &dm, int32_t *part, size_t part_bytes)
+{
+    if (d->flags & (IFX_OUT_I32 | IFX_OUT_PHASE | IFX_MAXPOOL)) return false;
+    ArmedQuery aq;
+    if (hip_status(ifx::launch_conv_split(conv_args(d, dm, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                                    nullptr),
+                                          d->kh, d->kw, part, part_bytes, nullptr)) != IFX_OK)
+        return false;
+    return aq.q.answered && aq.q.even_copy;
 }
 
 ifx_status check_conv_ptrs(const ifx_conv_desc *d, const int8_t *x, const int8_t *w, const int32_t *bias,
@@ -345,6 +360,7 @@ bool proj_chain_fusable(const ifx_conv_desc *d3, const Dims &m3, const ifx_conv_
 // the even pixels.  Out (for the next block): the same three facts about what this block left.
 struct BlockFlow {
     bool have_t1 = false, t1_ps = false, x_even = false;
+    const int8_t *xe = nullptr;  // or: the block input's even pixels, densely (its projection's input)
 };
 
 // A stride-2 pad-1 3x3 on even sizes whose kernel reads the phase-split layout.
@@ -368,7 +384,10 @@ bool phase_out_ok(const ifx_conv_desc &d)
 // previous block left (see BlockFlow).  next (or null): the following block; when this block's
 // conv3 chains with next's conv1, both run as one launch that also leaves next's t1 in the
 // workspace (phase-split when next's conv2 reads it so), and y receives only the even pixels if
-// next reads its input only through its conv1 and a stride-2 projection; *out says so.
+// next reads its input only through its conv1 and a stride-2 projection; *out says so.  When this
+// block's conv3 runs alone and next has such a projection (fused), the conv3 kernel also writes
+// y's even pixels into the workspace's shortcut region, where next's projection reads them with
+// unit stride (out->xe).
 ifx_status run_block(const ifx_block_params *p, const BlockPlan &plan, int n, const int8_t *x, int8_t *y,
                      int8_t *ws, int32_t *part, size_t part_bytes, hipStream_t s, const BlockFlow &in = BlockFlow(),
                      const ifx_block_params *next = nullptr, BlockFlow *out = nullptr)
@@ -380,12 +399,13 @@ ifx_status run_block(const ifx_block_params *p, const BlockPlan &plan, int n, co
         d[i].n = n;
     }
     if (out) *out = BlockFlow();
-    if (in.x_even) {
-        if (!in.have_t1 || !reads_input_even(p)) return IFX_E_UNSUPPORTED;
+    if ((in.x_even && !in.have_t1) || ((in.x_even || in.xe) && !reads_input_even(p))) return IFX_E_UNSUPPORTED;
+    if (in.x_even || in.xe) {
         d[3].stride = 1;  // the same output pixels, read from the subsampled input
         d[3].h = (d[3].h + 1) / 2;
         d[3].w = (d[3].w + 1) / 2;
     }
+    const int8_t *const px = in.xe ? in.xe : x;  // the projection's input
     // t1 between conv1 and a stride-2 conv2 goes phase-split when both kernels handle it
     bool t1_ps;
     if (in.have_t1) {
@@ -427,8 +447,8 @@ ifx_status run_block(const ifx_block_params *p, const BlockPlan &plan, int n, co
         // conv3, its projection and the next block's conv1 in one launch
         const ifx::ConvArgs a = conv_args(&d[2], plan.dims[2], t2, p->w_blk[2], p->bias[2], p->mult[2], p->shift[2],
                                           nullptr, y);
-        const ifx::ConvArgs pj = conv_args(&d[3], plan.dims[3], x, p->w_blk[3], p->bias[3], p->mult[3], p->shift[3],
-                                           nullptr, nullptr);
+        const ifx::ConvArgs pj = conv_args(&d[3], plan.dims[3], px, p->w_blk[3], p->bias[3], p->mult[3],
+                                           p->shift[3], nullptr, nullptr);
         const ifx::ConvArgs b = conv_args(&d1, m1, y, next->w_blk[0], next->bias[0], next->mult[0], next->shift[0],
                                           nullptr, t1);
         st = hip_status(ifx::launch_conv1x1_proj_chain(a, pj, b, s));
@@ -443,10 +463,11 @@ ifx_status run_block(const ifx_block_params *p, const BlockPlan &plan, int n, co
             // conv3 and the projection in one kernel: the shortcut never goes through HBM
             const ifx::ConvArgs a = conv_args(&d[2], plan.dims[2], t2, p->w_blk[2], p->bias[2], p->mult[2],
                                               p->shift[2], nullptr, y);
-            const ifx::ConvArgs pj = conv_args(&d[3], plan.dims[3], x, p->w_blk[3], p->bias[3], p->mult[3],
+            const ifx::ConvArgs pj = conv_args(&d[3], plan.dims[3], px, p->w_blk[3], p->bias[3], p->mult[3],
                                                p->shift[3], nullptr, nullptr);
             return hip_status(ifx::launch_conv_proj(a, pj, s));
         }
+        if (in.xe) return IFX_E_UNSUPPORTED;  // the shortcut region holds the projection's input
         st = run_conv(&d[3], kGeneric, plan.dims[3], x, p->w_blk[3], p->bias[3], p->mult[3], p->shift[3], nullptr,
                       sc, s, part, part_bytes);
         if (st != IFX_OK) return st;
@@ -465,6 +486,21 @@ ifx_status run_block(const ifx_block_params *p, const BlockPlan &plan, int n, co
             out->x_even = even;
         }
         return st;
+    }
+    if (next && out && !p->has_proj && reads_input_even(next)) {
+        // next's projection, fused, reading this output's even pixels from the shortcut region
+        ifx_conv_desc n2 = next->d[2], n3 = next->d[3];
+        n2.n = n3.n = n;
+        n3.stride = 1;
+        const Dims &m2 = plan.dims[2];
+        const size_t even_bytes = act_bytes(n, (m2.ho + 1) / 2, (m2.wo + 1) / 2, d[2].c_out);
+        if (proj_fusable(&n2, &n3) && even_bytes <= plan.sc && even_copy_ok(&d[2], m2, part, part_bytes)) {
+            ifx::ConvArgs a = conv_args(&d[2], m2, t2, p->w_blk[2], p->bias[2], p->mult[2], p->shift[2], res, y);
+            a.y_even = sc;
+            st = hip_status(ifx::launch_conv_split(a, d[2].kh, d[2].kw, part, part_bytes, s));
+            if (st == IFX_OK) out->xe = sc;
+            return st;
+        }
     }
     return run_conv(&d[2], kGeneric, plan.dims[2], t2, p->w_blk[2], p->bias[2], p->mult[2], p->shift[2], res, y, s,
                     part, part_bytes);
@@ -753,6 +789,33 @@ ifx_status ifx_conv_fused(const ifx_conv_desc *d, const int8_t *x_blk, const int
                     (hipStream_t)stream);
 }
 
+ifx_status ifx_conv_fused_even(const ifx_conv_desc *d, const int8_t *x_blk, const int8_t *w_blk, const int32_t *bias,
+                               const int32_t *mult, const int32_t *shift, const int8_t *residual, void *y,
+                               int8_t *y_even, void *stream)
+{
+    Kind k;
+    Dims dm;
+    ifx_status st = check_desc(d, &k, &dm);
+    if (st != IFX_OK) return st;
+    st = check_conv_ptrs(d, x_blk, w_blk, bias, mult, shift, residual, y);
+    if (st != IFX_OK) return st;
+    if (!y_even) return IFX_E_NULL;
+    if (!aligned16(y_even)) return IFX_E_ALIGN;
+    if (k != kGeneric || !even_copy_ok(d, dm, nullptr, 0)) return IFX_E_UNSUPPORTED;
+    ifx::ConvArgs a = conv_args(d, dm, x_blk, w_blk, bias, mult, shift,
+                                (d->flags & IFX_RESIDUAL) ? residual : nullptr, y);
+    a.y_even = y_even;
+    return hip_status(ifx::launch_conv_split(a, d->kh, d->kw, nullptr, 0, (hipStream_t)stream));
+}
+
+int32_t ifx_conv_even_supported(const ifx_conv_desc *d)
+{
+    Kind k;
+    Dims dm;
+    if (check_desc(d, &k, &dm) != IFX_OK || k != kGeneric) return 0;
+    return even_copy_ok(d, dm, nullptr, 0) ? 1 : 0;
+}
+
 ifx_status ifx_conv_kernel_name(const ifx_conv_desc *d, char *buf, size_t len)
 {
     Kind k;
@@ -1009,6 +1072,7 @@ ifx_status run_net(const ifx_net_params *p, const NetPlan &plan, const int8_t *x
             BlockPlan lay = bp;
             lay.t1 = plan.t1;
             lay.t2 = plan.t2;
+            lay.sc = plan.sc;
             const ifx_block_params *next = b + 1 < p->n_blocks ? &p->blocks[b + 1] : nullptr;
             BlockFlow left;
             st = run_block(&p->blocks[b], lay, nb, act[cur], act[cur ^ 1], bws, part, plan.part, s, flow, next,

@@ -1067,6 +1067,12 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd(64 * NW, RingCfg<NW, KS, K
         const unsigned plane = (unsigned)to.HoWo * 32;
         const unsigned out_img = (unsigned)a.oc1 * plane;
         int8_t *const ybase = y + (long long)to.img0 * out_img + (unsigned)(och >> 5) * plane + (och & 31);
+        // the even-pixel copy (y_even): its plane is ceil(ho / 2) x ceil(wo / 2)
+        const int we = (a.wo + 1) >> 1;
+        const unsigned plane_e = (unsigned)(((a.ho + 1) >> 1) * we) * 32;
+        const unsigned img_e = (unsigned)a.oc1 * plane_e;
+        int8_t *const ebase =
+            a.y_even ? a.y_even + (long long)to.img0 * img_e + (unsigned)(och >> 5) * plane_e + (och & 31) : nullptr;
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
             const int row = 16 * jj + (lane >> 2);
@@ -1074,6 +1080,12 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd(64 * NW, RingCfg<NW, KS, K
                 int d, hw;
                 split_px(to, row, d, hw);
                 store16_stream(ybase + ((unsigned)d * out_img + (unsigned)hw * 32), v[jj]);
+                if (ebase) {
+                    const int oy = fdiv(hw, a.wo_mul, a.wo_shr), ox = hw - oy * a.wo;
+                    if (!((oy | ox) & 1))
+                        store16_stream(ebase + ((unsigned)d * img_e + (unsigned)((oy >> 1) * we + (ox >> 1)) * 32),
+                                       v[jj]);
+                }
             }
         }
     }
@@ -1085,7 +1097,8 @@ template <int NW, int KS, int KP>
 hipError_t launch_ring(const ConvArgs &a, const ConvArgs &pj, hipStream_t s)
 {
     using C = RingCfg<NW, KS, KP>;
-    if (answer_query("conv1x1_ring_kernel<%d, %d, %d, %s>", NW, KS, KP, tf(a.relu != 0))) return hipSuccess;
+    if (answer_query_even(KP == 0, "conv1x1_ring_kernel<%d, %d, %d, %s>", NW, KS, KP, tf(a.relu != 0)))
+        return hipSuccess;
     const long long tiles = (a.m + 63) / 64;
     if (tiles <= 0) return hipSuccess;
     if (tiles > 0x7fffffffLL / 64) return hipErrorInvalidConfiguration;

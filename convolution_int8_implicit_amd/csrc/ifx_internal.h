@@ -26,6 +26,9 @@ struct ConvArgs {
     int nkb;               // kh * kw * i1 (32-wide reduction blocks)
     int relu, residual, out_i32;
     int out_even;          // store only the even rows and columns of the output (chained conv3)
+    // or null: also store the even rows and columns of the output, densely, here
+    // ([n, oc1, ceil(ho / 2), ceil(wo / 2), 32]): the input of a following stride-2 projection
+    int8_t *y_even;
     // phase-split layout [n][c1][2][2][h/2][w/2][32] (even sizes): plane (y % 2, x % 2) holds the
     // pixels of that row and column parity, so a stride-2 3x3 reads contiguous runs for every tap
     int in_ps, out_ps;
@@ -46,10 +49,31 @@ struct ConvArgs {
 struct KernelQuery {
     char name[160];
     bool answered;
+    bool even_copy;  // the answering launcher writes ConvArgs::y_even
 };
 KernelQuery *&armed_query();  // this thread's armed query, or null
 
 // Called first by every leaf launcher: true when a query took the call (nothing to launch).
+// even_copy: the launcher writes ConvArgs::y_even.
+inline bool answer_query_e(bool even_copy, const char *fmt, va_list ap)
+{
+    KernelQuery *q = armed_query();
+    if (!q) return false;
+    if (!q->answered) {
+        vsnprintf(q->name, sizeof(q->name), fmt, ap);
+        q->answered = true;
+        q->even_copy = even_copy;
+    }
+    return true;
+}
+inline bool answer_query_even(bool even_copy, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    const bool r = answer_query_e(even_copy, fmt, ap);
+    va_end(ap);
+    return r;
+}
 inline bool answer_query(const char *fmt, ...)
 {
     KernelQuery *q = armed_query();
@@ -60,6 +84,7 @@ inline bool answer_query(const char *fmt, ...)
         vsnprintf(q->name, sizeof(q->name), fmt, ap);
         va_end(ap);
         q->answered = true;
+        q->even_copy = false;
     }
     return true;
 }

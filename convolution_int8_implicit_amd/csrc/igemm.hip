@@ -500,6 +500,8 @@ void igemm_kernel(ConvArgs a, ConvArgs pj, int tiles_n, int per_xcd)
     const int k = lane & 3;
     const int b0 = fdiv(pbase, a.howo_mul, a.howo_shr);
     const int hw0 = pbase - b0 * HoWo;
+    const int we = (a.wo + 1) >> 1;  // the even-pixel copy (y_even): ceil(ho / 2) x ceil(wo / 2) planes
+    const long long plane_e = (long long)((a.ho + 1) >> 1) * we;
 #pragma unroll
     for (int hh = 0; hh < WNH; ++hh) {
         const int och = ch0 + 64 * hh + 16 * k;  // first channel of this lane's chunk
@@ -524,6 +526,13 @@ void igemm_kernel(ConvArgs a, ConvArgs pj, int tiles_n, int per_xcd)
                 store16_stream(dst, v);
             else
                 *(v4i *)dst = v;
+            if (a.y_even) {
+                const int oy = fdiv(hw, a.wo_mul, a.wo_shr), ox = hw - oy * a.wo;
+                if (!((oy | ox) & 1))
+                    store16_stream(a.y_even + (((long long)b * a.oc1 + (och >> 5)) * plane_e + (oy >> 1) * we +
+                                               (ox >> 1)) * 32 + (och & 31),
+                                   v);
+            }
         }
     }
 }
@@ -531,8 +540,8 @@ void igemm_kernel(ConvArgs a, ConvArgs pj, int tiles_n, int per_xcd)
 template <int KH, int KW, int BM, int BN, int ST, bool RES, bool PROJ, int WN = 64>
 hipError_t launch_ig(const ConvArgs &a, const ConvArgs &pj, hipStream_t s)
 {
-    if (answer_query("igemm_kernel<%d, %d, %d, %d, %d, %d, %s, %s, %s>", KH, KW, BM, BN, ST, WN, tf(RES),
-                     tf(a.relu != 0), tf(PROJ)))
+    if (answer_query_even(!a.out_i32, "igemm_kernel<%d, %d, %d, %d, %d, %d, %s, %s, %s>", KH, KW, BM, BN, ST, WN,
+                          tf(RES), tf(a.relu != 0), tf(PROJ)))
         return hipSuccess;
     const int tiles_n = (a.oc1 * 32 + BN - 1) / BN;
     const long long tiles_m = (a.m + BM - 1) / BM;

@@ -166,6 +166,25 @@ ifx_status ifx_conv_fused(const ifx_conv_desc *d, const int8_t *x_blk, const int
                           const int8_t *residual, void *y, void *stream);
 
 /*
+ * ifx_conv_fused that also writes the output's even pixels (rows and columns
+ * 0, 2, 4, ...) a second time, densely, to y_even [n, ceil(c_out/32),
+ * ceil(ho/2), ceil(wo/2), 32].  A stride-2 pad-0 1x1 convolution reads exactly
+ * those pixels (the projection shortcut of the Inspur article's section 2.2
+ * stage-entry block), so the block that follows can run its projection with
+ * unit stride on y_even and read contiguous runs instead of every other
+ * 32-byte piece; y itself is written as by ifx_conv_fused.
+ *   y_even     16-byte aligned, must not overlap the other tensors
+ * Returns IFX_E_UNSUPPORTED, launching nothing, when the kernel that runs d
+ * does not write the copy (ifx_conv_even_supported says which); IFX_OUT_I32,
+ * IFX_OUT_PHASE and IFX_MAXPOOL descriptors are never supported.
+ */
+ifx_status ifx_conv_fused_even(const ifx_conv_desc *d, const int8_t *x_blk, const int8_t *w_blk,
+                               const int32_t *bias, const int32_t *mult, const int32_t *shift,
+                               const int8_t *residual, void *y, int8_t *y_even, void *stream);
+/* Host-only: 1 when ifx_conv_fused_even(d, ...) would run, 0 when not or when d is invalid. */
+int32_t ifx_conv_even_supported(const ifx_conv_desc *d);
+
+/*
  * Conv3 of a bottleneck together with its projection shortcut, as one launch.
  * The Inspur conv-merge article (section 2.1) merges operators into one kernel
  * so that a tensor passed between them is neither written to nor read back from

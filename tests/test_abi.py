@@ -128,6 +128,31 @@ def test_conv_proj_fused_validation():
     assert call(D(k=5, p=2), dp) == 3
 
 
+def test_conv_fused_even_validation():
+    """The even-pixel copy: pointers, alignment and the kernel's support are checked on the host,
+    and nothing is launched on an error."""
+    L = ifx.lib()
+    fake = ctypes.c_void_p(0x100000)
+    odd = ctypes.c_void_p(0x100001)
+    R = ifx.RESIDUAL | ifx.RELU
+    d = D(n=2, h=28, w=28, ci=128, co=512, f=R)  # a res3 conv3 (ring kernel)
+
+    def call(dd, ye=fake, y=fake, res=fake):
+        return L.ifx_conv_fused_even(ctypes.byref(dd), fake, fake, fake, fake, fake, res, y, ye, None)
+
+    assert L.ifx_conv_even_supported(ctypes.byref(d)) == 1
+    assert L.ifx_conv_even_supported(ctypes.byref(D(n=2, h=14, w=14, ci=256, co=1024, f=R))) == 1  # general kernel
+    assert L.ifx_conv_even_supported(ctypes.byref(D(n=2, h=6, w=6, ci=64, co=128, f=ifx.RELU))) == 0  # small-K 1x1
+    assert L.ifx_conv_even_supported(ctypes.byref(D(n=2, h=6, w=6, ci=256, co=128, f=ifx.OUT_I32))) == 0
+    assert L.ifx_conv_even_supported(ctypes.byref(D(k=5, p=2))) == 0  # invalid descriptor
+    assert L.ifx_conv_even_supported(None) == 0
+    assert call(d, ye=None) == 1
+    assert call(d, res=None) == 1
+    assert call(d, ye=odd) == 4
+    assert call(D(n=2, h=6, w=6, ci=64, co=128, f=ifx.RELU)) == 3
+    assert call(D(k=5, p=2)) == 3
+
+
 def _block(n=2, proj=True, c3_flags=ifx.RESIDUAL | ifx.RELU, c2_cin=64):
     p = ifx.BlockParams()
     p.d[0] = D(n=n, h=8, w=8, ci=256, co=64, f=ifx.RELU)

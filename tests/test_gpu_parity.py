@@ -485,6 +485,59 @@ def test_projection_block(ifx, orc, shape):
         np.testing.assert_array_equal(got, exp)
 
 
+# A conv3 with shortcut that also stores its output's even pixels (ifx_conv_fused_even):
+# (n, h, w, c_in, c_out, k): the ring kernel (K <= 128, 256 / 512 channels) and the general kernel
+EVEN_COPY_SHAPES = [
+    (3, 28, 28, 128, 512, 1),  # res3.4 conv3 (ring kernel), 2352 pixels across images
+    (2, 14, 14, 256, 1024, 1),  # res4.6 conv3 (general kernel)
+    (3, 7, 7, 512, 2048, 1),   # odd sizes: a 4x4 copy of a 7x7 output
+    (2, 9, 11, 96, 256, 1),    # ring kernel with odd height, ragged last tile
+    (1, 9, 9, 64, 128, 3),     # a 3x3 general-kernel conv3
+]
+
+
+@pytest.mark.parametrize("shape", EVEN_COPY_SHAPES)
+@pytest.mark.parametrize("flags", [2, 3])
+def test_conv_fused_even_copy(ifx, orc, shape, flags):
+    n, h, w, c, oc, k = shape
+    note(f"even copy {shape} flags={flags}")
+    rng = np.random.default_rng(sum(shape) * 19 + flags)
+    x = rand(rng, (n, h, w, c), 0, 127)
+    wt = rand(rng, (oc, k, k, c), -127, 127)
+    bias, mult, shift = params(rng, oc)
+    r = rand(rng, (n, h, w, oc), -128, 127)
+    d = ifx.conv_desc(n, h, w, c, oc, k, k, 1, k // 2, flags)
+    assert ifx.conv_even_supported(d)
+    he, we = (h + 1) // 2, (w + 1) // 2
+    y, yw = guarded(ifx.act_bytes(n, h, w, oc))
+    ye, ew = guarded(ifx.act_bytes(n, he, we, oc))
+    ifx.conv_fused_even(d, ifx.pack_act(cu(x)), ifx.pack_weights(d, cu(wt)), cu(bias), cu(mult), cu(shift),
+                        ifx.pack_act(cu(r)), y, ye)
+    torch.cuda.synchronize()
+    check_guards(yw)
+    check_guards(ew)
+    exp = orc.conv_fused(x, wt, bias, mult, shift, 1, k // 2, flags, r)
+    got = ifx.unpack_act(y.view(n, (oc + 31) // 32, h, w, 32), oc).cpu().numpy()
+    np.testing.assert_array_equal(got, exp)
+    got_e = ifx.unpack_act(ye.view(n, (oc + 31) // 32, he, we, 32), oc).cpu().numpy()
+    np.testing.assert_array_equal(got_e, exp[:, ::2, ::2])
+
+
+def test_conv_fused_even_unsupported(ifx):
+    """A kernel that does not write the copy refuses the call and launches nothing."""
+    d = ifx.conv_desc(2, 6, 6, 64, 128, 1, 1, 1, 0, ifx.RELU)  # the small-K 1x1 kernel
+    assert not ifx.conv_even_supported(d)
+    x = torch.zeros(ifx.act_bytes(2, 6, 6, 64), dtype=torch.int8, device="cuda")
+    w = ifx.pack_weights(d, torch.zeros((128, 1, 1, 64), dtype=torch.int8, device="cuda"))
+    p = torch.zeros(128, dtype=torch.int32, device="cuda")
+    y = torch.full((ifx.act_bytes(2, 6, 6, 128),), 5, dtype=torch.int8, device="cuda")
+    ye = torch.full((ifx.act_bytes(2, 3, 3, 128),), 5, dtype=torch.int8, device="cuda")
+    with pytest.raises(ifx.IfxError):
+        ifx.conv_fused_even(d, x, w, p, p, p, None, y, ye)
+    torch.cuda.synchronize()
+    assert bool((y == 5).all()) and bool((ye == 5).all())
+
+
 # conv3 (64 < K <= 128, 512 output channels) with a unit-stride 1x1 projection (128 < K <= 256) in
 # the persistent ring kernel: (n, h, w, conv3 input channels, projection input channels)
 RING_PROJ_SHAPES = [

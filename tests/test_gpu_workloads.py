@@ -184,7 +184,9 @@ def test_workload4_every_layer_sampled(ifx, orc):
     too), or alone.  conv1 of a block whose conv2 has stride 2 stores its output phase-split
     (IFX_OUT_PHASE, also through the chained launch) for conv2 (IFX_IN_PHASE).  A chained block
     output whose next reader is a stride-2 projection is stored at its even pixels only
-    (IFX_OUT_EVEN), and that projection then runs with stride 1 on the subsampled tensor.  After
+    (IFX_OUT_EVEN), and that projection then runs with stride 1 on the subsampled tensor; an
+    unchained block output with such a reader is stored whole and its even pixels a second time
+    (ifx_conv_fused_even), and the projection reads that copy with stride 1.  After
     each layer the sampled images (the first and last of the batch, one in each pass, and two
     more) are compared byte for byte with the oracle: the pooled stem output and all 16 block
     outputs (the stored pixels of the subsampled one)."""
@@ -211,7 +213,7 @@ def test_workload4_every_layer_sampled(ifx, orc):
         return (d.kh == 3 and d.stride == 2 and d.pad == 1 and d.h % 2 == 0 and d.w % 2 == 0
                 and ifx.conv_validate(with_flag(d, ifx.IN_PHASE)) == 0)
 
-    chained = phases = 0
+    chained = phases = evens = 0
     for p0 in (0, half):
         mine = [i for i, r in enumerate(rows) if p0 <= r < p0 + half]
         local = [rows[i] - p0 for i in mine]
@@ -226,6 +228,7 @@ def test_workload4_every_layer_sampled(ifx, orc):
         t1 = None  # the block's conv1 output when the previous block chained it
         t1_ps = False  # ... stored phase-split
         t_even = False  # t holds only the even pixels of the block input
+        t_xe = None  # or: the block input's even pixels, a second copy
         for bi, blk in enumerate(net.blocks):
             c1, c2, c3 = blk.convs
             d2 = at(c2, half)
@@ -248,23 +251,24 @@ def test_workload4_every_layer_sampled(ifx, orc):
                 if phase_in_ok(at(nb_.convs[1], half)):
                     d1n = with_flag(d1n, ifx.OUT_PHASE)
             t1, t1_ps = None, False
-            y_even = False
+            y_even, ye = False, None
             d3 = at(c3, half)
             if blk.proj is not None:
                 pj = blk.proj
                 dp = at(pj, half)
-                if t_even:  # the projection's stride-2 pixels, already subsampled
+                if t_even or t_xe is not None:  # the projection's stride-2 pixels, already subsampled
                     dp.stride, dp.h, dp.w = 1, (dp.h + 1) // 2, (dp.w + 1) // 2
+                px = t_xe if t_xe is not None else t
                 y = model.empty_act(half, *c3.out_hw, c3.spec.c_out)
                 if nxt is not None and ifx.conv_proj_chain_kernel_name(d3, dp, d1n) is not None:
                     t1 = model.empty_act(half, *nxt.out_hw, nxt.spec.c_out)
                     t1_ps = bool(d1n.flags & ifx.OUT_PHASE)
-                    ifx.conv_proj_chain_fused(d3, t2, c3.w_blk, c3.bias, c3.mult, c3.shift, dp, t, pj.w_blk,
+                    ifx.conv_proj_chain_fused(d3, t2, c3.w_blk, c3.bias, c3.mult, c3.shift, dp, px, pj.w_blk,
                                               pj.bias, pj.mult, pj.shift, y, d1n, nxt.w_blk, nxt.bias,
                                               nxt.mult, nxt.shift, t1)
                     chained += 1
                 else:
-                    ifx.conv_proj_fused(d3, t2, c3.w_blk, c3.bias, c3.mult, c3.shift, dp, t,
+                    ifx.conv_proj_fused(d3, t2, c3.w_blk, c3.bias, c3.mult, c3.shift, dp, px,
                                         pj.w_blk, pj.bias, pj.mult, pj.shift, y)
             elif nxt is not None and ifx.conv_chain_kernel_name(d3, d1n) is not None:
                 pn = nb_.proj
@@ -281,19 +285,29 @@ def test_workload4_every_layer_sampled(ifx, orc):
                 chained += 1
             else:
                 y = model.empty_act(half, *c3.out_hw, c3.spec.c_out)
-                ifx.conv_fused(d3, t2, c3.w_blk, c3.bias, c3.mult, c3.shift, t, y)
+                pn = nb_.proj if nb_ is not None else None
+                if pn is not None and pn.spec.k == 1 and pn.spec.stride == 2 and ifx.conv_even_supported(d3):
+                    ye = model.empty_act(half, (c3.out_hw[0] + 1) // 2, (c3.out_hw[1] + 1) // 2, c3.spec.c_out)
+                    ifx.conv_fused_even(d3, t2, c3.w_blk, c3.bias, c3.mult, c3.shift, t, y, ye)
+                    evens += 1
+                else:
+                    ifx.conv_fused(d3, t2, c3.w_blk, c3.bias, c3.mult, c3.shift, t, y)
             torch.cuda.synchronize()
             del t2, t
             got = ifx.unpack_act(y[local].contiguous(), c3.spec.c_out).cpu().numpy()
             exp = trace[1 + bi][mine]
             np.testing.assert_array_equal(got, exp[:, ::2, ::2] if y_even else exp, err_msg=f"block {bi}")
-            t, t_even = y, y_even
+            if ye is not None:
+                got = ifx.unpack_act(ye[local].contiguous(), c3.spec.c_out).cpu().numpy()
+                np.testing.assert_array_equal(got, exp[:, ::2, ::2], err_msg=f"block {bi} even copy")
+            t, t_even, t_xe = y, y_even, ye
         del t
         torch.cuda.synchronize()
     # res2.1 -> res2.2 (with its projection), res2.2 -> res2.3, res2.3 -> res3.1, res3.2 -> res3.3,
     # res3.3 -> res3.4; both passes
     assert chained == 10
     assert phases == 6   # res3.1, res4.1, res5.1 conv2 read a phase-split conv1 output; both passes
+    assert evens == 4    # res3.4 and res4.6 also store their outputs' even pixels; both passes
 
 
 @pytest.mark.parametrize("n", [1, 3])
