@@ -860,54 +860,58 @@ hipError_t launch_chain(const ConvArgs &a, const ConvArgs &b, const ConvArgs *pj
 // input tile instead of the shortcut, each wave requantises the projection of its 64 channels (no
 // ReLU) into registers and adds it in the epilogue, and y is staged in one region per wave after
 // the ring.
-template <int NW, int KS, int KP = 0>
+template <int NW, int KS, int KP = 0, int TR = 64>
 struct RingCfg {
-    static constexpr int A = KS * 4096;                  // activations: KS x [64 rows][64 B]
-    static constexpr int X = KP * 4096;                  // projection input: KP x [64 rows][64 B]
-    static constexpr int BUF = A + (KP ? X : NW * 4096);  // + shortcut / output, one region per wave
-    static constexpr int YST = KP ? NW * 4096 : 0;       // output staging after the ring (projection)
+    static constexpr int KB = TR * 64;                   // one K-step of a tile: [TR rows][64 B]
+    static constexpr int A = KS * KB;                    // activations
+    static constexpr int X = KP * KB;                    // projection input
+    static constexpr int BUF = A + (KP ? X : NW * KB);   // + shortcut / output, one region per wave
+    static constexpr int YST = KP ? NW * KB : 0;         // output staging after the ring (projection)
     static constexpr int PER_CU = NW == 4 ? 2 : 1;
     static constexpr int AVAIL = kLdsBytes / PER_CU - YST;
-    static constexpr int NBMAX = KP ? 6 : 4;
+    static constexpr int NBMAX = (KP || TR == 32) ? 6 : 4;
     static constexpr int NB = AVAIL / BUF > NBMAX ? NBMAX : AVAIL / BUF;
-    static constexpr int ADMA = KS * 4 / NW;             // activation DMAs per wave per tile
-    static constexpr int XDMA = KP * 4 / NW;             // projection-input DMAs per wave per tile
-    static constexpr int DMA = ADMA + (KP ? XDMA : 4);   // (+ four shortcut DMAs without a projection)
+    static constexpr int GRPS = TR / 16;                 // 16-row groups of a tile (1 KB DMAs per K-step)
+    static constexpr int ADMA = KS * GRPS / NW;          // activation DMAs per wave per tile
+    static constexpr int XDMA = KP * GRPS / NW;          // projection-input DMAs per wave per tile
+    static constexpr int DMA = ADMA + (KP ? XDMA : GRPS);  // (+ the shortcut DMAs without a projection)
     static constexpr int LDS = NB * BUF + YST;
-    static_assert(ADMA >= 1 && ADMA * NW == KS * 4, "every wave issues the same DMAs");
-    static_assert(XDMA * NW == KP * 4, "every wave issues the same DMAs");
+    static_assert(TR == 64 || (TR == 32 && KP == 0), "32-pixel tiles without a projection only");
+    static_assert(ADMA >= 1 && ADMA * NW == KS * GRPS, "every wave issues the same DMAs");
+    static_assert(XDMA * NW == KP * GRPS, "every wave issues the same DMAs");
     static_assert(NB >= 3, "a ring of at least three tiles");
 };
 
-template <int NW, int KS, int KP>
+// soc: the first output channel of the workgroup's slice
+template <int NW, int KS, int KP, int TR>
 __device__ __forceinline__ void ring_issue(const ConvArgs &a, const ConvArgs &pj, int8_t *buf, int m0, int wave,
-                                           int lane)
+                                           int lane, int soc)
 {
-    using C = RingCfg<NW, KS, KP>;
+    using C = RingCfg<NW, KS, KP, TR>;
     const TileOrg t = tile_org(a, m0);
     const unsigned plane = (unsigned)t.HoWo * 32;
 #pragma unroll
-    for (int j = 0; j < C::ADMA; ++j) {  // 16-row group q % 4 of K-step q / 4
+    for (int j = 0; j < C::ADMA; ++j) {  // 16-row group q % GRPS of K-step q / GRPS
         const int q = j * NW + wave;
-        tile_rows_issue(a, t, buf + (q >> 2) * 4096, q & 3, q >> 2, lane);
+        tile_rows_issue(a, t, buf + (q / C::GRPS) * C::KB, q % C::GRPS, q / C::GRPS, lane);
     }
     if (KP) {
 #pragma unroll
         for (int j = 0; j < C::XDMA; ++j) {
             const int q = j * NW + wave;
-            tile_rows_issue(pj, t, buf + C::A + (q >> 2) * 4096, q & 3, q >> 2, lane);
+            tile_rows_issue(pj, t, buf + C::A + (q / C::GRPS) * C::KB, q % C::GRPS, q / C::GRPS, lane);
         }
         return;
     }
     {
         const unsigned out_img = (unsigned)a.oc1 * plane;
         const v4i rsR = make_rsrc(a.res + (long long)t.img0 * out_img, (long long)(a.n - t.img0) * out_img);
-        int8_t *const Rw = buf + C::A + wave * 4096;
+        int8_t *const Rw = buf + C::A + wave * C::KB;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < C::GRPS; ++j) {
             const int row = 16 * j + (lane >> 2);
             const int k = (lane & 3) ^ swz(row);
-            const int oc = 64 * wave + 16 * k;
+            const int oc = soc + 64 * wave + 16 * k;
             int d, hw;
             split_px(t, row, d, hw);
             const unsigned off = (unsigned)d * out_img + (unsigned)(oc >> 5) * plane + (unsigned)hw * 32 + (oc & 31);
@@ -916,22 +920,27 @@ __device__ __forceinline__ void ring_issue(const ConvArgs &a, const ConvArgs &pj
     }
 }
 
-template <int NW, int KS, int KP, bool RELU>
-__global__ __launch_bounds__(64 * NW, (waves_per_simd(64 * NW, RingCfg<NW, KS, KP>::PER_CU))) void conv1x1_ring_kernel(ConvArgs a,
+template <int NW, int KS, int KP, int TR, bool RELU>
+__global__ __launch_bounds__(64 * NW, (waves_per_simd(64 * NW, RingCfg<NW, KS, KP, TR>::PER_CU))) void conv1x1_ring_kernel(ConvArgs a,
                                                                                                ConvArgs pj,
-                                                                                               int tiles)
+                                                                                               int tiles, int slices)
 {
-    using C = RingCfg<NW, KS, KP>;
+    using C = RingCfg<NW, KS, KP, TR>;
     __shared__ __attribute__((aligned(1024))) int8_t smem[C::LDS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c = lane & 15, g = lane >> 4;
-    const int ch0 = 64 * wave;
-    const int first = blockIdx.x;
+    // slices > 1 (no projection): workgroup b owns output channels [64 NW (b % slices), +64 NW)
+    // and walks tiles b / slices, + gridDim.x / slices, ...
+    const int slice = (int)(blockIdx.x % (unsigned)slices);
+    const int soc = slice * 64 * NW;
+    const int ch0 = soc + 64 * wave;
+    const int first = (int)(blockIdx.x / (unsigned)slices);
+    const int gstride = (int)(gridDim.x / (unsigned)slices);
     if (first >= tiles) return;
-    const int ntile = (tiles - 1 - first) / (int)gridDim.x + 1;
+    const int ntile = (tiles - 1 - first) / gstride + 1;
 
     // weights (column operand: lane (c, g), tile tn -> channel ch0 + 4c + tn, K-step s bytes
     // 64s + 16g ..) and parameters into registers, before any DMA
@@ -962,9 +971,10 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd(64 * NW, RingCfg<NW, KS, K
         rpj = rq_pack(r, modep);
     }
 
-    auto tile_m0 = [&](int j) { const int t = first + j * (int)gridDim.x; return t < tiles ? t * 64 : a.m; };
+    auto tile_m0 = [&](int j) { const int t = first + j * gstride; return t < tiles ? t * TR : a.m; };
 #pragma unroll
-    for (int j = 0; j < C::NB - 1; ++j) ring_issue<NW, KS, KP>(a, pj, smem + j * C::BUF, tile_m0(j), wave, lane);
+    for (int j = 0; j < C::NB - 1; ++j)
+        ring_issue<NW, KS, KP, TR>(a, pj, smem + j * C::BUF, tile_m0(j), wave, lane, soc);
 
     int8_t *y = (int8_t *)a.y;
     const int k4 = lane & 3;
@@ -974,17 +984,17 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd(64 * NW, RingCfg<NW, KS, K
         const int m0 = tile_m0(j);
         wait_vmcnt<(C::NB - 2) * C::DMA>();  // tile j landed (loads complete in issue order)
         ring_barrier();                        // ... for every wave; every wave is done with tile j - 1
-        ring_issue<NW, KS, KP>(a, pj, smem + ((j + C::NB - 1) % C::NB) * C::BUF, tile_m0(j + C::NB - 1), wave,
-                               lane);
+        ring_issue<NW, KS, KP, TR>(a, pj, smem + ((j + C::NB - 1) % C::NB) * C::BUF, tile_m0(j + C::NB - 1),
+                                   wave, lane, soc);
 
         // the wave's output region: its shortcut bytes in the slot (requantised in place), or its
         // own staging region after the ring
-        int8_t *const Rw = KP ? smem + C::NB * C::BUF + wave * 4096 : buf + C::A + wave * 4096;
+        int8_t *const Rw = KP ? smem + C::NB * C::BUF + wave * C::KB : buf + C::A + wave * C::KB;
         auto contract = [&](v4i (&acc)[4][4], const int8_t *src, const v4i (*wt)[4], int steps, int tm)
             __attribute__((always_inline)) {
 #pragma unroll
             for (int s = 0; s < steps; ++s) {
-                const v4i af = *(const v4i *)(src + s * 4096 + swz_at(16 * tm + 4 * (c & 3) + (c >> 2), g));
+                const v4i af = *(const v4i *)(src + s * C::KB + swz_at(16 * tm + 4 * (c & 3) + (c >> 2), g));
 #pragma unroll
                 for (int tn = 0; tn < 4; ++tn)
                     acc[tm & 1][tn] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, wt[s][tn], s == 0 ? (v4i){0, 0, 0, 0}
@@ -1029,7 +1039,7 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd(64 * NW, RingCfg<NW, KS, K
             }
         } else {
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {  // two halves of 32 pixels
+            for (int h = 0; h < TR / 32; ++h) {  // halves of 32 pixels
                 v4i acc[4][4];
                 unsigned rr[2][4];  // the shortcut words of rows 16 (2h + t) + 4i + g, channels 4c ..
 #pragma unroll
@@ -1042,7 +1052,7 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd(64 * NW, RingCfg<NW, KS, K
 #pragma unroll
                     for (int t = 0; t < 2; ++t) {
                         const int tm = 2 * h + t;
-                        const v4i af = *(const v4i *)(buf + s * 4096 + swz_at(16 * tm + 4 * (c & 3) + (c >> 2), g));
+                        const v4i af = *(const v4i *)(buf + s * C::KB + swz_at(16 * tm + 4 * (c & 3) + (c >> 2), g));
 #pragma unroll
                         for (int tn = 0; tn < 4; ++tn)
                             acc[t][tn] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, w[s][tn], s == 0 ? (v4i){0, 0, 0, 0}
@@ -1060,9 +1070,9 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd(64 * NW, RingCfg<NW, KS, K
             }
         }
         wave_lds_sync();  // the wave's own region: no other wave reads it
-        v4i v[4];
+        v4i v[C::GRPS];
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) v[jj] = *(const v4i *)(Rw + swz_at(16 * jj + (lane >> 2), k4));
+        for (int jj = 0; jj < C::GRPS; ++jj) v[jj] = *(const v4i *)(Rw + swz_at(16 * jj + (lane >> 2), k4));
         const TileOrg to = tile_org(a, m0);
         const unsigned plane = (unsigned)to.HoWo * 32;
         const unsigned out_img = (unsigned)a.oc1 * plane;
@@ -1074,7 +1084,7 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd(64 * NW, RingCfg<NW, KS, K
         int8_t *const ebase =
             a.y_even ? a.y_even + (long long)to.img0 * img_e + (unsigned)(och >> 5) * plane_e + (och & 31) : nullptr;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
+        for (int jj = 0; jj < C::GRPS; ++jj) {
             const int row = 16 * jj + (lane >> 2);
             if (m0 + row < a.m) {
                 int d, hw;
@@ -1092,27 +1102,33 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd(64 * NW, RingCfg<NW, KS, K
     wait_vmcnt<0>();  // the ring's last (zero-fill) DMAs land before the workgroup's LDS is released
 }
 
-// pj: the projection (KP > 0) or `a` itself (unused)
-template <int NW, int KS, int KP>
+// pj: the projection (KP > 0) or `a` itself (unused); TR: pixels per tile (64, or 32 for a
+// deeper ring)
+template <int NW, int KS, int KP, int TR = 64>
 hipError_t launch_ring(const ConvArgs &a, const ConvArgs &pj, hipStream_t s)
 {
-    using C = RingCfg<NW, KS, KP>;
-    if (answer_query_even(KP == 0, "conv1x1_ring_kernel<%d, %d, %d, %s>", NW, KS, KP, tf(a.relu != 0)))
+    using C = RingCfg<NW, KS, KP, TR>;
+    if (answer_query_even(KP == 0, "conv1x1_ring_kernel<%d, %d, %d, %d, %s>", NW, KS, KP, TR, tf(a.relu != 0)))
         return hipSuccess;
-    const long long tiles = (a.m + 63) / 64;
+    const long long tiles = (a.m + TR - 1) / TR;
     if (tiles <= 0) return hipSuccess;
-    if (tiles > 0x7fffffffLL / 64) return hipErrorInvalidConfiguration;
+    if (tiles > 0x7fffffffLL / TR) return hipErrorInvalidConfiguration;
     int cus = 0;
     const hipError_t e = current_cus(&cus);
     if (e != hipSuccess) return e;
-    const long long slots = (long long)C::PER_CU * cus;
-    const long long grid = tiles < slots ? tiles : slots;
+    // output-channel slices of 64 NW channels (one without a projection's fixed pairing)
+    const int slices = KP ? 1 : a.oc / (64 * NW);
+    if (!KP && (slices < 1 || slices * 64 * NW != a.oc)) return hipErrorInvalidValue;
+    const long long slots = (long long)C::PER_CU * cus / slices * slices;
+    const long long want = tiles * slices;
+    long long grid = want < slots ? want : slots;
+    if (grid < slices) grid = slices;
     if (a.relu)
-        hipLaunchKernelGGL((conv1x1_ring_kernel<NW, KS, KP, true>), dim3((unsigned)grid), dim3(64 * NW), 0, s, a, pj,
-                           (int)tiles);
+        hipLaunchKernelGGL((conv1x1_ring_kernel<NW, KS, KP, TR, true>), dim3((unsigned)grid), dim3(64 * NW), 0, s,
+                           a, pj, (int)tiles, slices);
     else
-        hipLaunchKernelGGL((conv1x1_ring_kernel<NW, KS, KP, false>), dim3((unsigned)grid), dim3(64 * NW), 0, s, a,
-                           pj, (int)tiles);
+        hipLaunchKernelGGL((conv1x1_ring_kernel<NW, KS, KP, TR, false>), dim3((unsigned)grid), dim3(64 * NW), 0, s,
+                           a, pj, (int)tiles, slices);
     return hipGetLastError();
 }
 
@@ -1185,6 +1201,19 @@ hipError_t launch_conv1x1_ring_proj(const ConvArgs &a, const ConvArgs &pj, hipSt
 {
     return launch_ring<8, 2, 4>(a, pj, s);
 }
+
+// The 1x1 conv3 with shortcut of res4 (K = 256, 1024 output channels): the ring kernel with all
+// four K-steps of weights in registers, in slices of 512 output channels, on 32-pixel tiles (a
+// 64-pixel slot, 48 KB, would leave a ring of three), for batches that give every CU's workgroup
+// a run of tiles (at least 1024 tiles of 32 pixels).
+bool conv1x1_ring_wide_supported(const ConvArgs &a)
+{
+    return a.residual && a.stride == 1 && a.pad == 0 && a.ho == a.h && a.wo == a.w && a.i1 > 4 && a.i1 <= 8 &&
+           a.oc >= 512 && a.oc % 512 == 0 && a.m >= 64 * 512 && !a.out_i32 && !a.in_ps && !a.out_ps &&
+           !a.out_even && a.ksplit <= 1;
+}
+
+hipError_t launch_conv1x1_ring_wide(const ConvArgs &a, hipStream_t s) { return launch_ring<8, 4, 0, 32>(a, a, s); }
 
 hipError_t launch_conv1x1_small_k(const ConvArgs &a, hipStream_t s)
 {

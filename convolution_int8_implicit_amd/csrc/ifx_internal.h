@@ -161,6 +161,8 @@ hipError_t launch_fold_bn(const FoldArgs &f, int32_t *bias, int32_t *mult, int32
 bool conv1x1_small_k_supported(const ConvArgs &a, int kh, int kw);
 bool conv1x1_proj_supported(const ConvArgs &a, const ConvArgs &pj);
 bool conv1x1_ring_proj_supported(const ConvArgs &a, const ConvArgs &pj);
+bool conv1x1_ring_wide_supported(const ConvArgs &a);
+hipError_t launch_conv1x1_ring_wide(const ConvArgs &a, hipStream_t s);
 hipError_t launch_conv1x1_ring_proj(const ConvArgs &a, const ConvArgs &pj, hipStream_t s);
 hipError_t launch_conv1x1_proj(const ConvArgs &a, const ConvArgs &pj, hipStream_t s);
 hipError_t launch_conv1x1_small_k(const ConvArgs &a, hipStream_t s);

@@ -569,6 +569,7 @@ hipError_t launch_ig_k(const ConvArgs &a, hipStream_t s)
 {
     constexpr int ST = 2;
     const bool wide = a.oc1 * 32 > 64;
+    if (KH == 1 && KW == 1 && conv1x1_ring_wide_supported(a)) return launch_conv1x1_ring_wide(a, s);
     if (a.residual)
         return wide ? launch_ig<KH, KW, 128, 128, ST, true, false>(a, a, s)
                     : launch_ig<KH, KW, 256, 64, ST, true, false>(a, a, s);

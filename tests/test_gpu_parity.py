@@ -237,6 +237,11 @@ RING_SHAPES = [
     (40, 56, 56, 96, 256),    # K = 96 (two K-steps, the second half zero): three-deep ring
     (3, 7, 7, 128, 512),      # 147 pixels: tiles spanning images, a ragged last tile
     (1, 5, 5, 32, 256),       # one partial tile, K = 32
+    # K of 160..256 and 512 / 1024 / 1536 output channels: weights of four K-steps in registers,
+    # workgroups in slices of 512 channels (at least 512 tiles)
+    (168, 14, 14, 256, 1024),  # the res4 conv3 shape: two slices
+    (700, 7, 7, 224, 512),     # seven channel blocks (the last K-step half empty), ragged last tile
+    (33, 32, 32, 160, 1536),   # three slices, five channel blocks
 ]
 
 
@@ -489,7 +494,8 @@ def test_projection_block(ifx, orc, shape):
 # (n, h, w, c_in, c_out, k): the ring kernel (K <= 128, 256 / 512 channels) and the general kernel
 EVEN_COPY_SHAPES = [
     (3, 28, 28, 128, 512, 1),  # res3.4 conv3 (ring kernel), 2352 pixels across images
-    (2, 14, 14, 256, 1024, 1),  # res4.6 conv3 (general kernel)
+    (2, 14, 14, 256, 1024, 1),  # res4.6 conv3 shape at batch 2 (general kernel)
+    (168, 14, 14, 256, 1024, 1),  # ... at a batch of 512+ tiles (ring kernel, two channel slices)
     (3, 7, 7, 512, 2048, 1),   # odd sizes: a 4x4 copy of a 7x7 output
     (2, 9, 11, 96, 256, 1),    # ring kernel with odd height, ragged last tile
     (1, 9, 9, 64, 128, 3),     # a 3x3 general-kernel conv3
@@ -561,7 +567,7 @@ def test_ring_projection(ifx, orc, shape):
     bp, mp, sp = params(rng, 512, 0, 20)
     d3 = ifx.conv_desc(n, h, w, c3in, 512, 1, 1, 1, 0, ifx.RESIDUAL | ifx.RELU)
     dp = ifx.conv_desc(n, h, w, cpin, 512, 1, 1, 1, 0, 0)
-    assert ifx.conv_kernel_name(d3, dp).startswith("conv1x1_ring_kernel<8, 2, 4, true>")
+    assert ifx.conv_kernel_name(d3, dp).startswith("conv1x1_ring_kernel<8, 2, 4, 64, true>")
     y, yw = guarded(ifx.act_bytes(n, h, w, 512))
     ifx.conv_proj_fused(d3, ifx.pack_act(cu(t)), ifx.pack_weights(d3, cu(w3)), cu(b3), cu(m3), cu(s3),
                         dp, ifx.pack_act(cu(x)), ifx.pack_weights(dp, cu(wp)), cu(bp), cu(mp), cu(sp), y)
