@@ -497,8 +497,8 @@ def ceilings(stream) -> dict:
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="net",
                     choices=["net", "net26_b1", "conv1x1", "conv1x1_b1", "block", "stem"])
     ap.add_argument("--sub-batch", type=int, default=None)
