@@ -40,8 +40,13 @@ KERNEL_SOURCES = {
     "conv1x1_chain_kernel": ["conv1x1.hip", "device_common.h", "ifx_internal.h"],
     "conv1x1_ring_kernel": ["conv1x1.hip", "device_common.h", "ifx_internal.h"],
     "conv3x3_halo_kernel": ["igemm.hip", "device_common.h", "ifx_internal.h"],
+    "conv3x3_win_kernel": ["igemm.hip", "device_common.h", "ifx_internal.h"],
     "stem_kernel": ["stem.hip", "device_common.h", "ifx_internal.h"],
 }
+
+
+# a library kernel instance inside a profiler's kernel name
+KERNEL_RE = r"((?:conv1x1_chain|conv1x1_ring|conv1x1_proj|conv1x1|conv3x3_halo|conv3x3_win|igemm|stem)_kernel<[^>]*>)"
 
 
 def source_digest(kernel: str) -> str:
@@ -80,7 +85,7 @@ def summarize_pmc(fetch_csv: str, write_csv: str, calib_bytes: int, out: str, wo
     from collections import defaultdict
 
     def short(name):
-        m = re.search(r"((?:conv1x1_chain|conv1x1_ring|conv1x1_proj|conv1x1|conv3x3_halo|igemm|stem)_kernel<[^>]*>)", name)
+        m = re.search(KERNEL_RE, name)
         if m:
             return m.group(1)
         return "copy" if "bitwise_not" in name else None
@@ -151,7 +156,7 @@ def summarize_trace(trace_csv: str, stats_csv: str, out: str, workload: str, not
     last_pool = max((int(r["Dispatch_Id"]) for r in rows if "avgpool_kernel" in r["Kernel_Name"]), default=-1)
     rep = defaultdict(list)
     for r in rows:
-        m = re.search(r"((?:conv1x1_chain|conv1x1_ring|conv1x1_proj|conv1x1|conv3x3_halo|igemm|stem)_kernel<[^>]*>)", r["Kernel_Name"])
+        m = re.search(KERNEL_RE, r["Kernel_Name"])
         if m and int(r["Dispatch_Id"]) > last_pool:
             rep[m.group(1)].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
     lines += ["#", "# per-launch replays only (one conv launch at a time on one stream; bench.py's",
@@ -178,7 +183,7 @@ def summarize_counters(csvs, out: str, workload: str, note: str):
             rows = list(csv.DictReader(fh))
         last_pool = max((int(r["Dispatch_Id"]) for r in rows if "avgpool_kernel" in r["Kernel_Name"]), default=-1)
         for r in rows:
-            m = re.search(r"((?:conv1x1_chain|conv1x1_ring|conv1x1_proj|conv1x1|conv3x3_halo|igemm|stem)_kernel<[^>]*>)", r["Kernel_Name"])
+            m = re.search(KERNEL_RE, r["Kernel_Name"])
             if m and int(r["Dispatch_Id"]) > last_pool:
                 per[m.group(1)][r["Counter_Name"]].append(float(r["Counter_Value"]))
     counters = sorted({c for k in per.values() for c in k})

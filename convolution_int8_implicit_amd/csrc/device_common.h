@@ -210,8 +210,8 @@ __device__ __forceinline__ int rq_setup(RqLane &r, v4i bias4, v4i mult4, v4i shi
 
 // One tile row of a lane: its 4 channels of row 16tm + 4i + g requantised (mode MODE), plus the
 // shortcut bytes rr when RES, clamped (ReLU or not) and packed into one word.
-template <int MODE, bool RES, bool RELU>
-__device__ __forceinline__ unsigned requant_row(const v4i (&acc)[4][4], int tm, int i, const RqLane &r, unsigned rr)
+template <int MODE, bool RES, bool RELU, int TM>
+__device__ __forceinline__ unsigned requant_row(const v4i (&acc)[TM][4], int tm, int i, const RqLane &r, unsigned rr)
 {
     int q[4];
 #pragma unroll
@@ -296,14 +296,14 @@ __device__ __forceinline__ unsigned requant_quad_p(v4i acc, const RqPacked &p)
     return pack4(q[0], q[1], q[2], q[3]);
 }
 
-// Requantise a wave's 64x64 accumulator tile into the LDS staging tile (row stride BN),
+// Requantise a wave's (16 TM)x64 accumulator tile into the LDS staging tile (row stride BN),
 // adding the shortcut bytes already there when RES.  Lane (g, c) owns tile rows
 // 16tm + 4i + g and the 4 bytes at column 4c.
-template <int MODE, bool RES, bool RELU, int BN>
-__device__ __forceinline__ void requant_tile(const v4i (&acc)[4][4], int8_t *rbase, const RqLane &r)
+template <int MODE, bool RES, bool RELU, int BN, int TM>
+__device__ __forceinline__ void requant_tile(const v4i (&acc)[TM][4], int8_t *rbase, const RqLane &r)
 {
 #pragma unroll
-    for (int tm = 0; tm < 4; ++tm)
+    for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             unsigned *rp = (unsigned *)(rbase + (16 * tm + 4 * i) * BN);
@@ -312,8 +312,8 @@ __device__ __forceinline__ void requant_tile(const v4i (&acc)[4][4], int8_t *rba
 }
 
 // The three modes dispatched on rq_setup's wave-uniform choice.
-template <bool RES, bool RELU, int BN>
-__device__ __forceinline__ void requant_tile_any(int mode, const v4i (&acc)[4][4], int8_t *rbase, const RqLane &r)
+template <bool RES, bool RELU, int BN, int TM>
+__device__ __forceinline__ void requant_tile_any(int mode, const v4i (&acc)[TM][4], int8_t *rbase, const RqLane &r)
 {
     if (mode == 0)
         requant_tile<0, RES, RELU, BN>(acc, rbase, r);

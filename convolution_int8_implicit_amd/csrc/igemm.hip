@@ -564,11 +564,297 @@ hipError_t launch_ig(const ConvArgs &a, const ConvArgs &pj, hipStream_t s)
     return hipGetLastError();
 }
 
+// ---- stride-1 3x3 over 128 or more input channels: haloed windows per 64-channel chunk ------
+//
+// The general kernel fetches each activation row again for every tap: nine 64-byte K-steps per
+// pixel and 64 input channels.  Here a workgroup's tile is 224 output pixels of whole rows (8 rows
+// of a 28-wide image, 16 of a 14-wide one) by 128 output channels, and the reduction runs over
+// 64-channel chunks and, inside a chunk, over the nine taps.  A chunk's input window is fetched
+// once, into one of two buffers, while the previous chunk computes; each tap's weights stream
+// through a ring of three 8 KB stages.  Per K-step the activation DMA falls from 64 bytes per
+// output pixel to about 7, and each weight byte serves 224 pixels instead of 128.
+//
+// Window rows: for a tile whose first output row is row y0 of image i0, output pixel (image i,
+// row y, column x) reads, at tap (ky, kx), window row (i - i0)(H + 2) + (y - y0) + ky and window
+// column x + kx.  Every image the tile touches thus contributes the rows it needs plus one halo
+// row above and one below (zero outside the image).  The window pitch P (16 or 32 pixels, at
+// least W + 2) is a multiple of 16, so a row shifted by ky keeps its slot swizzle and each lane
+// needs base addresses only for the three column shifts.  The order of the reduction differs
+// from the weight layout's, which integer sums do not see.
+
+constexpr int kWinTile = 224;                  // output pixels per tile (14 groups of 16)
+constexpr int kWinPx = 384;                    // window pixels per 32-channel block (rows x P)
+constexpr int kWinBuf = 2 * kWinPx * 32;       // one chunk's window, two blocks: 24 KB
+constexpr int kWinStage = 128 * 64;            // one K-step of 128 channels' weights: 8 KB
+constexpr int kWinRows = kWinTile / 2;         // output pixels per wave (two waves along M)
+constexpr int kWinLds = 2 * kWinBuf + 3 * kWinStage + 4 * 768;
+constexpr int kWinDma = 2 * kWinPx / 32 / 4;   // window DMAs per wave per chunk (6)
+static_assert(4 * kWinRows * 64 <= 2 * kWinBuf, "the output tile is staged over the windows");
+static_assert(2 * kWinLds <= kLdsBytes, "two workgroups per CU");
+
+template <int P, bool RELU>
+__global__ __launch_bounds__(256, waves_per_simd(256, 2)) void conv3x3_win_kernel(ConvArgs a, int tiles_n, int per_xcd,
+                                                                                  int tr)
+{
+    constexpr int TM = kWinRows / 16;  // 16-row groups per wave (7)
+    __shared__ __attribute__((aligned(1024))) int8_t smem[kWinLds];
+    int8_t *const Bs = smem + 2 * kWinBuf;  // weight ring [slot][block][128 rows][32 B], slots as b_swz
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    int8_t *const Pw = Bs + 3 * kWinStage + wave * 768;
+    const int mw = wave & 1, nw = wave >> 1;  // the wave's 112 pixels and 64 channels
+
+    // tile: XCD x (blockIdx & 7) owns pixel tiles [x * per_xcd, (x + 1) * per_xcd), so tiles that
+    // share halo rows, and the channel tiles of one pixel tile, share an L2
+    const int xcd = blockIdx.x & 7;
+    const int kk = blockIdx.x >> 3;
+    const int mq = kk / tiles_n;
+    const int m0 = (xcd * per_xcd + mq) * kWinTile;
+    if (m0 >= a.m) return;
+    const int n0 = (kk - mq * tiles_n) * 128;
+    const int ch0 = n0 + 64 * nw;
+
+    const int H = a.h, W = a.w, HW = H * W, H2 = H + 2;
+    const int img0 = fdiv(m0, a.howo_mul, a.howo_shr);
+    const int y0 = fdiv(m0 - img0 * HW, a.wo_mul, a.wo_shr);
+    const int segs = fdiv(m0 + kWinTile - 1, a.howo_mul, a.howo_shr) - img0 + 1;  // images touched
+    const int rows = tr + 2 * segs;                                                // window rows read
+    const long long in_img = (long long)a.i1 * HW * 32;
+    const v4i rsA = make_rsrc(a.x + (long long)img0 * in_img, (long long)(a.n - img0) * in_img);
+
+    // window DMA q = 4j + wave fills 32 window pixels (1 KB) of block q / 12: with P = 32 one
+    // window row, with P = 16 two (lanes 32-63 take the second).  A lane's column is the same in
+    // every DMA; a row's source (image, input row), or its absence (halo rows outside the image,
+    // rows the tile does not read), is wave-uniform.
+    const int dr = dma_a_row(lane);
+    const int lx = (dr & (P - 1)) - 1;
+    const bool lsecond = P == 16 && dr >= 16;
+    const unsigned lane_off = (unsigned)(lx * 32 + dma_a_h(lane) * 16);
+    const bool col_ok = (unsigned)lx < (unsigned)W;
+    auto row_src = [&](int wr) __attribute__((always_inline)) {  // chunk-0 offset of window row wr, or -1
+        int u = wr + y0, sg = 0;
+        while (u >= H2) {
+            u -= H2;
+            ++sg;
+        }
+        const int r_in = u - 1;
+        const bool ok = wr < rows && (unsigned)r_in < (unsigned)H && img0 + sg < a.n;
+        return ok ? (sg * a.i1 * HW + r_in * W) * 32 : -1;
+    };
+    auto issue_window = [&](int chunk, int buf) __attribute__((always_inline)) {
+        int8_t *const dst = smem + buf * kWinBuf;
+#pragma unroll
+        for (int j = 0; j < kWinDma; ++j) {
+            const int q = 4 * j + wave;
+            const int blk = q >= 12 ? 1 : 0;
+            const int cq = q - 12 * blk;
+            const int src = P == 32 ? row_src(cq) : (lsecond ? row_src(2 * cq + 1) : row_src(2 * cq));
+            const unsigned off =
+                src >= 0 && col_ok ? (unsigned)(src + (2 * chunk + blk) * HW * 32) + lane_off : kOOB;
+            load16_lds(rsA, dst + blk * (kWinPx * 32) + cq * 1024, off);
+        }
+    };
+
+    // weight DMA q = 4j + wave fills 32 rows of block q / 4 of a stage
+    const int wblk = a.o2 * 32;
+    const int wrows = ((a.oc + a.o2 - 1) / a.o2) * a.o2;
+    const v4i rsB = make_rsrc(a.wt, (long long)wrows * 9 * a.i1 * 32);
+    int b_off[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int q = 4 * j + wave;
+        const int R = n0 + 32 * (q & 3) + dma_b_row(lane);
+        const int o1 = fdiv(R, a.o2_mul, a.o2_shr);
+        b_off[j] = o1 * (9 * a.i1 * wblk) + (q >> 2) * wblk + (R - o1 * a.o2) * 32 + dma_b_h(lane) * 16;
+    }
+    auto issue_b = [&](int tap, int chunk, int slot) __attribute__((always_inline)) {
+        // opaque per step: otherwise each tap's offset is hoisted out of the loop into a register
+        int add = (tap * a.i1 + 2 * chunk) * wblk;
+        asm volatile("" : "+s"(add));
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int q = 4 * j + wave;
+            load16_lds(rsB, Bs + slot * kWinStage + (q >> 2) * 4096 + (q & 3) * 1024, (unsigned)(b_off[j] + add));
+        }
+    };
+
+    // per-channel parameters of the wave's 64 channels, then chunk 0's window and two weight stages
+    if (lane < 16) {
+        const unsigned off = (unsigned)(ch0 + 4 * lane) * 4;
+        load16_lds(make_rsrc(a.bias, (long long)a.oc * 4), Pw, off);
+        load16_lds(make_rsrc(a.mult, (long long)a.oc * 4), Pw + 256, off);
+        load16_lds(make_rsrc(a.shift, (long long)a.oc * 4), Pw + 512, off);
+    }
+    issue_window(0, 0);
+    issue_b(0, 0, 0);
+    issue_b(1, 0, 1);
+
+    // fragment addresses: lane (c, g) reads half g % 2 of block g / 2 of output pixel
+    // 16 tm + 4 (c % 4) + c / 4 of the wave's rows (window-relative, per column shift), and
+    // weight row 4c + tn of the wave's channels
+    const int c = lane & 15;
+    const int g = lane >> 4;
+    int abase[TM][3];
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+        const int p = m0 + kWinRows * mw + 16 * tm + 4 * (c & 3) + (c >> 2);
+        const int i = fdiv(p, a.howo_mul, a.howo_shr);
+        const int rem = p - i * HW;
+        const int y = fdiv(rem, a.wo_mul, a.wo_shr);
+        const int R0 = ((i - img0) * H2 + y - y0) * P + (rem - y * W);
+#pragma unroll
+        for (int kx = 0; kx < 3; ++kx) abase[tm][kx] = (g >> 1) * (kWinPx * 32) + a_swz(R0 + kx, g & 1);
+    }
+    int b_frag[4];
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn) b_frag[tn] = ((g >> 1) * 4096 + b_swz(64 * nw + 4 * c, g & 1)) ^ (tn << 5);
+
+    v4i acc[TM][4];
+
+    // K-step (chunk, tap T) reads window buffer chunk % 2 and weight slot T % 3 (nine taps per
+    // chunk keep the slot a compile-time constant).  Its weights were requested two steps before;
+    // the next chunk's window is requested at tap 0, after that step's barrier has freed the
+    // buffer.  Loads complete in order, so each wait counts what this wave requested later: the
+    // next step's weights (2), and at taps 1 and 2 also the next window (kWinDma).
+    // (the first step takes 0 as the MFMAs' C operand, so no accumulator is ever cleared)
+    auto step = [&](auto tap, auto buf, auto first, int chunk, bool last) __attribute__((always_inline)) {
+        constexpr int T = decltype(tap)::value, BUF = decltype(buf)::value;
+        constexpr bool FIRST = decltype(first)::value != 0;
+        if constexpr (T == 1 || T == 2) {
+            if (last)
+                wait_vmcnt<2>();
+            else
+                wait_vmcnt<2 + kWinDma>();
+        } else if constexpr (T == 8) {
+            if (last)
+                wait_vmcnt<0>();
+            else
+                wait_vmcnt<2>();
+        } else {
+            wait_vmcnt<2>();
+        }
+        // every wave's part of this step has landed, and every wave's reads of step - 1 are done
+        // (the compiler may sink a step's last fragment reads past the next barrier; the slot and
+        // window this step refills must not be overwritten under them)
+        lds_barrier();
+        if constexpr (T <= 6)
+            issue_b(T + 2, chunk, (T + 2) % 3);
+        else if (!last)
+            issue_b(T - 7, chunk + 1, (T + 2) % 3);
+        if constexpr (T == 0)
+            if (!last) issue_window(chunk + 1, BUF ^ 1);
+        const int8_t *const win = smem + BUF * kWinBuf + (T / 3) * P * 32;  // offsets in the instructions
+        const int8_t *const bst = Bs + (T % 3) * kWinStage;
+        v4i bf[4], af[TM];
+#pragma unroll
+        for (int tn = 0; tn < 4; ++tn) bf[tn] = *(const v4i *)(bst + b_frag[tn]);
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm) af[tm] = *(const v4i *)(win + abase[tm][T % 3]);
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+            for (int tn = 0; tn < 4; ++tn)
+                acc[tm][tn] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[tm], bf[tn],
+                                                                    FIRST ? (v4i){0, 0, 0, 0} : acc[tm][tn], 0, 0, 0);
+    };
+    // chunks ck (window buffer 0) and ck + 1 (buffer 1)
+    auto pair = [&](auto first, int ck, bool last) __attribute__((always_inline)) {
+        // opaque per pair of chunks: otherwise every (buffer, tap, row group) address is hoisted out
+        // of the loop into a register of its own
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+            for (int kx = 0; kx < 3; ++kx) asm volatile("" : "+v"(abase[tm][kx]));
+        static_for<0, 9>([&](auto t) __attribute__((always_inline)) {
+            step(t, Slot<0>(), Slot<(decltype(first)::value && decltype(t)::value == 0) ? 1 : 0>(), ck, false);
+        });
+        static_for<0, 9>([&](auto t) __attribute__((always_inline)) { step(t, Slot<1>(), Slot<0>(), ck + 1, last); });
+    };
+    const int nc = a.i1 >> 1;  // 64-channel chunks (an even number)
+    pair(Slot<1>(), 0, nc <= 2);
+    for (int ck = 2; ck < nc; ck += 2) pair(Slot<0>(), ck, ck + 2 >= nc);
+
+    // every wave's fragment reads are done: the windows take the staged output tile
+    lds_barrier();
+    int8_t *const Rw = smem + wave * (kWinRows * 64);
+    RqLane r;
+    const int mode = rq_setup<false, RELU>(r, *(const v4i *)(Pw + c * 16), *(const v4i *)(Pw + 256 + c * 16),
+                                           *(const v4i *)(Pw + 512 + c * 16), false, ch0 + 4 * c, a.oc);
+    requant_tile_any<false, RELU, 64>(mode, acc, Rw + g * 64 + 4 * c, r);
+    wave_lds_sync();
+
+    // 16-byte stores: lane -> row 16 j + lane / 4 of the wave's pixels, channels och .. och + 15
+    const int k = lane & 3;
+    const int och = ch0 + 16 * k;
+    const int we = (a.wo + 1) >> 1;  // the even-pixel copy: ceil(ho / 2) x ceil(wo / 2) planes
+    const long long plane_e = (long long)((a.ho + 1) >> 1) * we;
+    int p = m0 + kWinRows * mw + (lane >> 2);
+    int b = fdiv(p, a.howo_mul, a.howo_shr), hw = p - b * HW;  // rows 16 apart: at most one image apart
+#pragma unroll
+    for (int j = 0; j < TM; ++j, p += 16, hw += 16) {
+        if (hw >= HW) {
+            hw -= HW;
+            ++b;
+        }
+        if (p >= a.m) break;
+        const v4i v = *(const v4i *)(Rw + (16 * j + (lane >> 2)) * 64 + 16 * k);
+        *(v4i *)((int8_t *)a.y + (((long long)b * a.oc1 + (och >> 5)) * HW + hw) * 32 + (och & 31)) = v;
+        if (a.y_even) {
+            const int oy = fdiv(hw, a.wo_mul, a.wo_shr), ox = hw - oy * W;
+            if (!((oy | ox) & 1))
+                store16_stream(a.y_even + (((long long)b * a.oc1 + (och >> 5)) * plane_e + (oy >> 1) * we + (ox >> 1)) *
+                                              32 + (och & 31),
+                               v);
+        }
+    }
+}
+
+bool conv3x3_win_supported(const ConvArgs &a, int kh, int kw)
+{
+    if (kh != 3 || kw != 3 || a.stride != 1 || a.pad != 1 || a.ho != a.h || a.wo != a.w) return false;
+    if (a.residual || a.out_i32 || a.in_ps || a.out_ps || a.out_even || a.ksplit > 1) return false;
+    if (a.i1 % 4 != 0 || a.oc % 128 != 0 || a.oc1 * 32 != a.oc || a.o2 % 32 != 0) return false;
+    if (a.w < 1 || kWinTile % a.w != 0 || a.w + 2 > 32 || a.h * a.w < 16) return false;
+    const int pitch = a.w + 2 <= 16 ? 16 : 32;
+    const int tr = kWinTile / a.w;
+    const int segs = (tr - 1 + a.h - 1) / a.h + 1;  // most images a run of tr rows touches
+    if ((tr + 2 * segs) * pitch > kWinPx) return false;
+    if ((long long)segs * a.i1 * a.h * a.w * 32 >= 0x7fffffffLL) return false;
+    // enough tiles for one per CU
+    return (long long)(a.m + kWinTile - 1) / kWinTile * (a.oc / 128) >= 256;
+}
+
+hipError_t launch_conv3x3_win(const ConvArgs &a, hipStream_t s)
+{
+    const int pitch = a.w + 2 <= 16 ? 16 : 32;
+    if (answer_query_even(true, "conv3x3_win_kernel<%d, %s>", pitch, tf(a.relu != 0))) return hipSuccess;
+    const int tiles_n = a.oc / 128;
+    const long long tiles_m = (a.m + kWinTile - 1) / kWinTile;
+    const long long per = (tiles_m + 7) / 8;
+    const long long grid = 8 * per * tiles_n;
+    if (grid <= 0) return hipSuccess;
+    if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    const int tr = kWinTile / a.w;
+    if (pitch == 16) {
+        if (a.relu)
+            hipLaunchKernelGGL((conv3x3_win_kernel<16, true>), dim3((unsigned)grid), dim3(256), 0, s, a, tiles_n, (int)per, tr);
+        else
+            hipLaunchKernelGGL((conv3x3_win_kernel<16, false>), dim3((unsigned)grid), dim3(256), 0, s, a, tiles_n, (int)per, tr);
+    } else {
+        if (a.relu)
+            hipLaunchKernelGGL((conv3x3_win_kernel<32, true>), dim3((unsigned)grid), dim3(256), 0, s, a, tiles_n, (int)per, tr);
+        else
+            hipLaunchKernelGGL((conv3x3_win_kernel<32, false>), dim3((unsigned)grid), dim3(256), 0, s, a, tiles_n, (int)per, tr);
+    }
+    return hipGetLastError();
+}
+
 template <int KH, int KW>
 hipError_t launch_ig_k(const ConvArgs &a, hipStream_t s)
 {
     constexpr int ST = 2;
     const bool wide = a.oc1 * 32 > 64;
+    if (KH == 3 && KW == 3 && conv3x3_win_supported(a, KH, KW)) return launch_conv3x3_win(a, s);
     if (KH == 1 && KW == 1 && conv1x1_ring_wide_supported(a)) return launch_conv1x1_ring_wide(a, s);
     if (a.residual)
         return wide ? launch_ig<KH, KW, 128, 128, ST, true, false>(a, a, s)
@@ -747,8 +1033,9 @@ __global__ __launch_bounds__(512, waves_per_simd(512, 1)) void conv3x3_halo_kern
                             af, bf[tn], (ky == 0 && kx == 0) ? (v4i){0, 0, 0, 0} : acc[tm][tn], 0, 0, 0);
                 }
             }
-        // every wave's fragment reads of this window are done: it takes the 4 KB staging tiles
-        ring_barrier();
+        // every wave's fragment reads of this window are done (waited for: the compiler may leave
+        // the last ones in flight here): it takes the 4 KB staging tiles
+        lds_barrier();
         int8_t *const Rw = (int8_t *)win + wave * 4096;
         requant_to_lds<false, RELU, true>(acc, Rw + g * 64 + 4 * c, Pw, c, n0 + 4 * c, a.oc);
         wave_lds_sync();

@@ -226,6 +226,64 @@ def test_halo_window_multi_band(ifx, orc, n, oc, flags):
     np.testing.assert_array_equal(got, orc.conv_fused(x, wt, bias, mult, shift, 1, 1, flags))
 
 
+# Unit-stride 3x3 layers over a multiple of 128 input channels, with 128-channel output tiles, on
+# 14- or 28-wide images, run the haloed-window kernel: tiles of 224 pixels in whole rows (8 of a
+# 28-wide image, 16 of a 14-wide one), whose windows take one halo row above and below every
+# image a tile touches (a 16-row tile of 14-row images touches up to three), the reduction in
+# 64-channel chunks, and a ragged last tile.  Sampled images are compared, among them the first
+# two (the first tile that spans an image boundary) and the last two.
+WIN_SHAPES = [
+    (80, 28, 28, 128, 128),   # res3 conv2: 280 tiles, one pair of chunks
+    (150, 14, 14, 256, 256),  # res4 conv2: 132 pixel tiles (the last one quarter full) x 2
+    (74, 28, 28, 512, 128),   # four pairs of chunks
+    (300, 14, 14, 128, 384),  # three output-channel tiles, a half-full last pixel tile
+]
+
+
+@pytest.mark.parametrize("shape", WIN_SHAPES)
+@pytest.mark.parametrize("flags", [0, 1])
+def test_window_3x3(ifx, orc, shape, flags):
+    n, h, w, c, oc = shape
+    note(f"window 3x3 {shape} flags={flags}")
+    rng = np.random.default_rng(sum(shape) * 11 + flags)
+    x = rand(rng, (n, h, w, c), 0, 127)
+    wt = rand(rng, (oc, 3, 3, c), -127, 127)
+    # shifts 0-20 take the general requantisation, 8-16 the fast forms
+    bias, mult, shift = params(rng, oc, 0, 20) if flags == 0 else params(rng, oc)
+    d = ifx.conv_desc(n, h, w, c, oc, 3, 3, 1, 1, flags)
+    assert ifx.conv_kernel_name(d).startswith("conv3x3_win_kernel<")
+    got = gpu_conv(ifx, x, wt, bias, mult, shift, 3, 1, 1, flags)
+    idx = sorted({0, 1, 2, n // 2, n - 2, n - 1})
+    exp = orc.conv_fused(x[idx], wt, bias, mult, shift, 1, 1, flags)
+    np.testing.assert_array_equal(got[idx], exp)
+
+
+def test_window_3x3_even_copy(ifx, orc):
+    """The haloed-window kernel also writes the even-pixel copy when asked."""
+    n, h, w, c, oc = 80, 28, 28, 128, 128
+    note("window 3x3 even copy")
+    rng = np.random.default_rng(2024)
+    x = rand(rng, (n, h, w, c), 0, 127)
+    wt = rand(rng, (oc, 3, 3, c), -127, 127)
+    bias, mult, shift = params(rng, oc)
+    d = ifx.conv_desc(n, h, w, c, oc, 3, 3, 1, 1, ifx.RELU)
+    assert ifx.conv_kernel_name(d).startswith("conv3x3_win_kernel<")
+    assert ifx.conv_even_supported(d)
+    y, yw = guarded(ifx.act_bytes(n, h, w, oc))
+    ye, ew = guarded(ifx.act_bytes(n, h // 2, w // 2, oc))
+    ifx.conv_fused_even(d, ifx.pack_act(cu(x)), ifx.pack_weights(d, cu(wt)), cu(bias), cu(mult), cu(shift), None,
+                        y, ye)
+    torch.cuda.synchronize()
+    check_guards(yw)
+    check_guards(ew)
+    idx = [0, 1, n - 1]
+    exp = orc.conv_fused(x[idx], wt, bias, mult, shift, 1, 1, ifx.RELU)
+    got = ifx.unpack_act(y.view(n, oc // 32, h, w, 32), oc).cpu().numpy()
+    np.testing.assert_array_equal(got[idx], exp)
+    got_e = ifx.unpack_act(ye.view(n, oc // 32, h // 2, w // 2, 32), oc).cpu().numpy()
+    np.testing.assert_array_equal(got_e[idx], exp[:, ::2, ::2])
+
+
 # 1x1 layers with a shortcut, unit stride and 256 or 512 output channels run on persistent
 # workgroups (two per CU for 256 channels, one for 512) that walk 64-pixel tiles through a ring
 # of 3-4 LDS buffers.  These batches give every workgroup several tiles, more than the ring holds,
