@@ -548,6 +548,43 @@ def test_projection_block(ifx, orc, shape):
         np.testing.assert_array_equal(got, exp)
 
 
+# conv3 + projection with 256 or more output channels over at least 2048 tiles of 128x256 runs
+# the wide-tile form that keeps the requantised projection in registers: (n, ho, c_mid, c_in,
+# c_out, projection stride).  Sampled images are compared.
+PROJ_WIDE_SHAPES = [
+    (340, 14, 256, 512, 1024, 2),  # res4.1: stride-2 projection on 28x28, a ragged last tile
+    (672, 7, 512, 1024, 2048, 1),  # res5.1 on the even-pixel copy (stride 1)
+]
+
+
+@pytest.mark.parametrize("shape", PROJ_WIDE_SHAPES)
+def test_projection_wide_tiles(ifx, orc, shape):
+    from oracle.ref import ConvParams
+    n, ho, c_mid, c_in, c_out, s = shape
+    note(f"projection wide tiles {shape}")
+    rng = np.random.default_rng(sum(shape) * 17)
+    hi = ho * s
+    t = rand(rng, (n, ho, ho, c_mid), 0, 127)
+    x = rand(rng, (n, hi, hi, c_in), 0, 127)
+    w3 = rand(rng, (c_out, 1, 1, c_mid), -127, 127)
+    wp = rand(rng, (c_out, 1, 1, c_in), -127, 127)
+    p3 = params(rng, c_out, 0, 20) if s == 2 else params(rng, c_out)
+    pp = params(rng, c_out, 0, 20) if s == 2 else params(rng, c_out)
+    d3 = ifx.conv_desc(n, ho, ho, c_mid, c_out, 1, 1, 1, 0, ifx.RESIDUAL | ifx.RELU)
+    dp = ifx.conv_desc(n, hi, hi, c_in, c_out, 1, 1, s, 0, 0)
+    assert ifx.conv_kernel_name(d3, dp) == "igemm_kernel<1, 1, 128, 256, 2, 128, true, true, true>"
+    y, whole = guarded(ifx.act_bytes(n, ho, ho, c_out))
+    ifx.conv_proj_fused(d3, ifx.pack_act(cu(t)), ifx.pack_weights(d3, cu(w3)), *(cu(v) for v in p3), dp,
+                        ifx.pack_act(cu(x)), ifx.pack_weights(dp, cu(wp)), *(cu(v) for v in pp), y)
+    torch.cuda.synchronize()
+    check_guards(whole)
+    idx = sorted({0, 1, n // 2, n - 1})
+    got = ifx.unpack_act(y.view(n, c_out // 32, ho, ho, 32), c_out).cpu().numpy()[idx]
+    sc = orc.conv_layer(x[idx], ConvParams(wp, *pp, s, 0), 0)
+    exp = orc.conv_layer(t[idx], ConvParams(w3, *p3, 1, 0), ifx.RESIDUAL | ifx.RELU, residual=sc)
+    np.testing.assert_array_equal(got, exp)
+
+
 # A conv3 with shortcut that also stores its output's even pixels (ifx_conv_fused_even):
 # (n, h, w, c_in, c_out, k): the ring kernel (K <= 128, 256 / 512 channels) and the general kernel
 EVEN_COPY_SHAPES = [
