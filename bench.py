@@ -493,10 +493,51 @@ def ceilings(stream) -> dict:
     def mfma():
         ops[0] = ifx.probe_mfma_i8(out, blocks, 4096, stream)
     t_mfma = time_steps(mfma, stream, 10, 2)
+    cus = props.multi_processor_count
+
+    def per_clk_cu(rate):  # bytes per second -> bytes per clock per CU at the nominal 2.4 GHz
+        return round(rate / cus / 2.4e9, 1)
+    # buffer->LDS DMA of contiguous 1 KB runs from a 2 MiB (L2-resident) buffer
+    src = torch.ones(2 << 20, dtype=torch.int8, device="cuda")
+    dout = torch.empty(4 * 4 * cus, dtype=torch.int32, device="cuda")
+    moved = [0]
+
+    def dma():
+        moved[0] = ifx.probe_dma_lds(src, dout, 4 * cus, 256, stream)
+    t_dma = time_steps(dma, stream, 10, 2)
+    # ds_read_b128 lane patterns: linear; the general kernel's swizzled activation and weight
+    # fragment reads (lane (c, g): pixel row 4(c % 4) + c / 4, weight row 4c; half g % 2 of block
+    # g / 2 of a 128-row tile); the same activation reads from unswizzled 64-byte rows
+    def a_swz(row, h):
+        return ((row >> 2) << 7) | (((((row & 3) ^ ((row >> 2) & 3)) << 1) | (h ^ (row & 1))) << 4)
+
+    def b_swz(row, h):
+        return ((row >> 2) << 7) | ((((row & 3) << 1 | h) ^ ((row >> 2) & 6)) << 4)
+    lanes = [(l & 15, l >> 4) for l in range(64)]
+    patterns = {
+        "linear": [16 * l for l in range(64)],
+        "act_fragment": [(g >> 1) * 4096 + a_swz(4 * (c & 3) + (c >> 2), g & 1) for c, g in lanes],
+        "weight_fragment": [(g >> 1) * 4096 + b_swz(4 * c, g & 1) for c, g in lanes],
+        "act_rows_unswizzled": [(4 * (c & 3) + (c >> 2)) * 64 + 16 * g for c, g in lanes],
+    }
+    lout = torch.empty(4 * cus, dtype=torch.int32, device="cuda")
+    lds = {}
+    for name, offs in patterns.items():
+        o = torch.tensor(offs, dtype=torch.int32, device="cuda")
+        rd = [0]
+
+        def lread():
+            rd[0] = ifx.probe_lds_read(o, lout, 4 * cus, 64, stream)
+        t_rd = time_steps(lread, stream, 10, 2)
+        lds[name] = per_clk_cu(rd[0] / t_rd)
     return {"copy_gbps": round(2 * nbytes / t_copy / 1e9, 1), "copy_frac_hbm": round(2 * nbytes / t_copy / PEAK_HBM, 4),
             "mfma_i8_tops": round(ops[0] / t_mfma / 1e12, 1), "mfma_frac_peak": round(ops[0] / t_mfma / PEAK_I8, 4),
+            "dma_lds_tbps": round(moved[0] / t_dma / 1e12, 2), "dma_lds_bytes_per_clk_cu": per_clk_cu(moved[0] / t_dma),
+            "lds_read_bytes_per_clk_cu": lds,
             "note": "copy: 1 GiB read + 1 GiB written by 16-byte non-temporal vector loads/stores; "
-                    f"mfma: {blocks} workgroups x 4 waves x a 4x4 tile of independent v_mfma_i32_16x16x64_i8 chains"}
+                    f"mfma: {blocks} workgroups x 4 waves x a 4x4 tile of independent v_mfma_i32_16x16x64_i8 chains; "
+                    "dma: 1 KB buffer->LDS runs from a 2 MiB buffer, 16 waves per CU; lds: 8 independent "
+                    "ds_read_b128 per wave and round, 16 waves per CU; per-clock figures at the nominal 2.4 GHz"}
 
 
 def main():

@@ -117,6 +117,8 @@ def lib() -> ctypes.CDLL:
         "ifx_status_string": ([i32], ctypes.c_char_p),
         "ifx_probe_copy": ([vp, vp, sz, vp], i32),
         "ifx_probe_mfma_i8": ([vp, i32, i32, vp], i32),
+        "ifx_probe_dma_lds": ([vp, sz, i32, i32, vp, vp], i32),
+        "ifx_probe_lds_read": ([vp, i32, i32, vp, vp], i32),
         "ifx_last_hip_error": ([], i32),
         "ifx_version": ([], i32),
     }
@@ -312,6 +314,25 @@ def probe_mfma_i8(out: torch.Tensor, blocks: int, iters: int, stream=None) -> in
     assert out.dtype == torch.int32 and out.numel() >= 4 * blocks
     _check(lib().ifx_probe_mfma_i8(_ptr(out), blocks, iters, _stream(stream)), "ifx_probe_mfma_i8")
     return blocks * 4 * iters * 16 * 32768
+
+
+def probe_dma_lds(src: torch.Tensor, out: torch.Tensor, blocks: int, iters: int, stream=None) -> int:
+    """Buffer->LDS DMA rate probe (ifx_probe.h) over the bytes of src; returns the bytes it moves."""
+    _dev(src, out)
+    nbytes = src.numel() * src.element_size()
+    assert out.dtype == torch.int32 and out.numel() >= 4 * blocks
+    _check(lib().ifx_probe_dma_lds(_ptr(src), nbytes, blocks, iters, _ptr(out), _stream(stream)),
+           "ifx_probe_dma_lds")
+    return blocks * 4 * iters * 8192
+
+
+def probe_lds_read(offsets: torch.Tensor, out: torch.Tensor, blocks: int, iters: int, stream=None) -> int:
+    """ds_read_b128 rate probe (ifx_probe.h) for the lane byte offsets (64 int32); returns the bytes it reads."""
+    _dev(offsets, out)
+    assert offsets.dtype == torch.int32 and offsets.numel() == 64
+    assert out.dtype == torch.int32 and out.numel() >= blocks
+    _check(lib().ifx_probe_lds_read(_ptr(offsets), blocks, iters, _ptr(out), _stream(stream)), "ifx_probe_lds_read")
+    return blocks * 4 * iters * 8 * 1024
 
 
 # Bytes of the library-held scratch ifx_block_forward_noalloc uses (IFX_BLOCK_SCRATCH_BYTES).

@@ -1,7 +1,10 @@
 // Practical-ceiling probes of the device, for the measurements that report
 // each kernel against its roofline: a streaming copy (the HBM rate a plain
-// read + write stream reaches) and an int8 MFMA loop (the matrix-core rate
-// with no memory traffic).  Not part of the convolution path.
+// read + write stream reaches), an int8 MFMA loop (the matrix-core rate with
+// no memory traffic), the buffer->LDS DMA rate of contiguous 1 KB runs from an
+// L2-resident buffer (how the convolution kernels stage their operands), and
+// the ds_read_b128 rate of a given lane pattern (LDS bank conflicts).  Not
+// part of the convolution path.
 #include "ifx_probe.h"
 
 #include <hip/hip_runtime.h>
@@ -48,6 +51,55 @@ __global__ __launch_bounds__(256) void probe_mfma_kernel(int *out, int iters, in
     if (lane == 0) out[blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)] = s.x + s.y + s.z + s.w;
 }
 
+// Each wave moves 8 contiguous 1 KB runs per round from src into its own 8 KB of LDS by
+// buffer->LDS DMA, then waits for them: run j of round i of wave w is 1 KB piece
+// (8 (w iters + i) + j) mod pieces of src, so a src that fits L2 is read from L2.
+constexpr int kProbeDmaLds = 4 * 8192;
+__global__ __launch_bounds__(256) void probe_dma_lds_kernel(const int8_t *src, unsigned pieces, int iters, int *out)
+{
+    __shared__ __attribute__((aligned(1024))) int8_t lds[kProbeDmaLds];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const v4i rs = make_rsrc(src, (long long)pieces * 1024);
+    const unsigned w = blockIdx.x * 4u + (unsigned)wave;
+    int8_t *const mine = lds + wave * 8192;
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const unsigned piece = (8u * (w * (unsigned)iters + (unsigned)i) + (unsigned)j) % pieces;
+            load16_lds(rs, mine + j * 1024, piece * 1024u + (unsigned)lane * 16u);
+        }
+        wait_vmcnt<0>();
+    }
+    wave_lds_sync();
+    const v4i v = *(const v4i *)(mine + lane * 16);
+    if (lane == 0) out[w] = v.x ^ v.y ^ v.z ^ v.w;
+}
+
+// Each wave issues 8 independent ds_read_b128 per round, lane l at byte offsets[l] (masked into a
+// 16 KB buffer, 16-byte aligned) plus 1 KB j (the same banks), and keeps the data live with an
+// empty asm statement, so no other instruction competes with the reads.
+constexpr int kProbeLds = 16384;
+__global__ __launch_bounds__(256) void probe_lds_read_kernel(const int *offsets, int iters, int *out)
+{
+    __shared__ __attribute__((aligned(1024))) int8_t lds[kProbeLds + 8 * 1024];
+    const int lane = threadIdx.x & 63;
+    for (int i = threadIdx.x; i < (kProbeLds + 8 * 1024) / 16; i += blockDim.x)
+        *(v4i *)(lds + 16 * i) = (v4i){i, i ^ 5, i + 7, (int)blockIdx.x};
+    __syncthreads();
+    const int off = offsets[lane] & (kProbeLds - 16);
+    v4i keep = {0, 0, 0, 0};
+    for (int it = 0; it < iters; ++it) {
+        v4i v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = *(const v4i *)(lds + off + j * 1024);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) asm volatile("" : : "v"(v[j]));
+        keep = v[it & 7];
+    }
+    if (keep.x == 0x7fffffff) out[blockIdx.x] = keep.y;
+}
+
 }  // namespace
 }  // namespace ifx
 
@@ -74,6 +126,26 @@ int32_t ifx_probe_mfma_i8(int32_t *out, int32_t blocks, int32_t iters, void *str
     if (blocks <= 0 || iters <= 0) return 2;
     hipLaunchKernelGGL(ifx::probe_mfma_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, out,
                        iters, 7);
+    return hipGetLastError() == hipSuccess ? 0 : 6;
+}
+
+int32_t ifx_probe_dma_lds(const void *src, size_t bytes, int32_t blocks, int32_t iters, int32_t *out,
+                          void *stream)
+{
+    if (!src || !out) return 1;
+    if (blocks <= 0 || iters <= 0 || bytes < 1024 || (bytes & 1023u) || bytes > 0x7fffffffu) return 2;
+    if ((uintptr_t)src & 15u) return 4;
+    hipLaunchKernelGGL(ifx::probe_dma_lds_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
+                       (const int8_t *)src, (unsigned)(bytes / 1024), iters, out);
+    return hipGetLastError() == hipSuccess ? 0 : 6;
+}
+
+int32_t ifx_probe_lds_read(const int32_t *offsets, int32_t blocks, int32_t iters, int32_t *out, void *stream)
+{
+    if (!offsets || !out) return 1;
+    if (blocks <= 0 || iters <= 0) return 2;
+    hipLaunchKernelGGL(ifx::probe_lds_read_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
+                       offsets, iters, out);
     return hipGetLastError() == hipSuccess ? 0 : 6;
 }
 

@@ -37,6 +37,30 @@ int32_t ifx_probe_copy(const void *src, void *dst, size_t bytes, void *stream);
  */
 int32_t ifx_probe_mfma_i8(int32_t *out, int32_t blocks, int32_t iters, void *stream);
 
+/*
+ * Buffer->LDS DMA rate: `blocks` workgroups of four waves, each wave running
+ * `iters` rounds of 8 DMAs of one contiguous 1 KB run each (16 bytes per lane)
+ * from src into its own LDS, waiting for them at the end of the round -- the
+ * way the convolution kernels stage their operands.  src is a DEVICE buffer of
+ * `bytes` (a multiple of 1024, at most 2^31 - 1), 16-byte aligned; the runs
+ * cycle through it, so a buffer that fits the L2 is read from L2.  Writes one
+ * int32 per wave to out (DEVICE, blocks * 4 elements).
+ * Bytes moved = blocks * 4 * iters * 8192.
+ */
+int32_t ifx_probe_dma_lds(const void *src, size_t bytes, int32_t blocks, int32_t iters, int32_t *out,
+                          void *stream);
+
+/*
+ * LDS read rate of one lane pattern: `blocks` workgroups of four waves, each
+ * wave running `iters` rounds of 8 independent ds_read_b128, lane l reading the
+ * 16 bytes at LDS byte offset offsets[l] (+ j KB; offsets is a DEVICE array of
+ * 64 int32, taken modulo 16 KB and rounded down to 16 bytes).  Bank conflicts
+ * of the pattern show as a lower rate.  out: DEVICE, `blocks` int32 (written
+ * only in a case that does not occur; it keeps the reads live).
+ * Bytes read = blocks * 4 * iters * 8 * 1024.
+ */
+int32_t ifx_probe_lds_read(const int32_t *offsets, int32_t blocks, int32_t iters, int32_t *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif
