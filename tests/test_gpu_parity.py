@@ -796,13 +796,15 @@ def test_stem_nhwc_input(ifx, orc, n, h, w, c):
 
 # ------------------------------------------------------------------ small networks: pool and head
 @pytest.mark.parametrize("n,h,w,nblk", [(2, 40, 44, 0), (1, 224, 224, 0), (3, 16, 16, 1), (1, 9, 12, 1),
-                                        (515, 16, 16, 1)])
+                                        (515, 16, 16, 1), (4097, 9, 12, 0)])
 def test_small_net_pool_and_head(ifx, orc, n, h, w, nblk):
     """Stem -> 0 or 1 bottleneck -> average pool -> FC through ifx_net_forward: the pool over
     9 to 3136 pixels per plane (pixel groups of the wave left partly empty) and the int32
     logits equal the oracle's; a batch run in single-image passes gives the same logits.
     515 images run as two concurrent halves (258 + 257) on two streams, eagerly and recorded
-    as one graph (fork and join inside the capture), replayed with other work between."""
+    as one graph (fork and join inside the capture), replayed with other work between.  4097
+    images give halves of 4098 and 4096 pooled planes: the pool's eight-planes-per-wave
+    mapping, with a partly filled last wave."""
     from oracle.ref import BlockParams as OracleBlock, ConvParams
     note(f"small net n={n} h={h} w={w} blocks={nblk}")
     rng = np.random.default_rng(n * 1000 + h + w + nblk)
