@@ -96,7 +96,7 @@ def summarize_pmc(fetch_csv: str, write_csv: str, calib_bytes: int, out: str, wo
             rows = [r for r in csv.DictReader(fh) if r["Counter_Name"] == counter]
         # only the per-launch replays, which follow the network's last average-pool dispatch:
         # they are the launches the roofline times (the forward's concurrent passes are not)
-        last_pool = max((int(r["Dispatch_Id"]) for r in rows if "avgpool_kernel" in r["Kernel_Name"]), default=-1)
+        last_pool = max((int(r["Dispatch_Id"]) for r in rows if "avgpool" in r["Kernel_Name"]), default=-1)
         for r in rows:
             k = short(r["Kernel_Name"])
             if k and (k == "copy" or int(r["Dispatch_Id"]) > last_pool):
@@ -153,7 +153,7 @@ def summarize_trace(trace_csv: str, stats_csv: str, out: str, workload: str, not
                          f'{float(r["MinNs"]):.0f} | {float(r["MaxNs"]):.0f}')
     with open(trace_csv) as fh:
         rows = list(csv.DictReader(fh))
-    last_pool = max((int(r["Dispatch_Id"]) for r in rows if "avgpool_kernel" in r["Kernel_Name"]), default=-1)
+    last_pool = max((int(r["Dispatch_Id"]) for r in rows if "avgpool" in r["Kernel_Name"]), default=-1)
     rep = defaultdict(list)
     for r in rows:
         m = re.search(KERNEL_RE, r["Kernel_Name"])
@@ -181,7 +181,7 @@ def summarize_counters(csvs, out: str, workload: str, note: str):
     for path in csvs:
         with open(path) as fh:
             rows = list(csv.DictReader(fh))
-        last_pool = max((int(r["Dispatch_Id"]) for r in rows if "avgpool_kernel" in r["Kernel_Name"]), default=-1)
+        last_pool = max((int(r["Dispatch_Id"]) for r in rows if "avgpool" in r["Kernel_Name"]), default=-1)
         for r in rows:
             m = re.search(KERNEL_RE, r["Kernel_Name"])
             if m and int(r["Dispatch_Id"]) > last_pool:
