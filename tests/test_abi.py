@@ -293,3 +293,37 @@ def test_graph_entry_points_validate_before_recording():
     assert h.value is None                                                        # cleared on error
     assert L.ifx_graph_launch(None, None) == 1
     assert L.ifx_graph_destroy(None) == 0
+
+
+def test_dispatch_of_the_network_shapes():
+    """The kernel instance each ResNet-50 layer shape launches at 1024 images (one pass of a batch
+    of 2048), as the host-only name query reports it without a GPU, and the boundaries of the
+    haloed-window 3x3 and of the wide-tile fused projection."""
+    R, RR = ifx.RELU, ifx.RESIDUAL | ifx.RELU
+
+    def name(n, h, w, c, oc, k, s, p, flags):
+        return ifx.conv_kernel_name(ifx.conv_desc(n, h, w, c, oc, k, k, s, p, flags))
+
+    win = "conv3x3_win_kernel<"
+    # unit-stride 3x3 over a multiple of 128 channels on 28- and 14-wide images, enough tiles
+    assert name(1024, 28, 28, 128, 128, 3, 1, 1, R) == win + "32, true>"
+    assert name(1024, 14, 14, 256, 256, 3, 1, 1, R) == win + "16, true>"
+    assert name(1024, 14, 14, 256, 256, 3, 1, 1, 0) == win + "16, false>"
+    # not on 7-wide images (the window would exceed 384 pixels), not below one tile per CU, not
+    # with 64 channels (the res2 kernel), a shortcut, stride 2 or 96 channels
+    assert not name(1024, 7, 7, 512, 512, 3, 1, 1, R).startswith(win)
+    assert not name(64, 28, 28, 128, 128, 3, 1, 1, R).startswith(win)
+    assert name(1024, 56, 56, 64, 64, 3, 1, 1, R) == "conv3x3_halo_kernel<true>"
+    assert not name(1024, 28, 28, 128, 128, 3, 1, 1, RR).startswith(win)
+    assert not name(1024, 28, 28, 128, 128, 3, 2, 1, R).startswith(win)
+    assert not name(1024, 28, 28, 96, 128, 3, 1, 1, R).startswith(win)
+
+    def proj_name(n, ho, cmid, cin, cout, s):
+        d3 = ifx.conv_desc(n, ho, ho, cmid, cout, 1, 1, 1, 0, RR)
+        dp = ifx.conv_desc(n, ho * s, ho * s, cin, cout, 1, 1, s, 0, 0)
+        return ifx.conv_kernel_name(d3, dp)
+
+    wide = "igemm_kernel<1, 1, 128, 256, 2, 128, true, true, true>"
+    assert proj_name(1024, 14, 256, 512, 1024, 1) == wide  # res4.1 on the even-pixel copy
+    assert proj_name(1024, 7, 512, 1024, 2048, 1) == wide  # res5.1
+    assert proj_name(97, 14, 256, 512, 1024, 1) == "igemm_kernel<1, 1, 128, 128, 2, 64, true, true, true>"
