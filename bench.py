@@ -560,6 +560,8 @@ def main():
                     help="write profiles/<--counters-name>.txt from rocprofv3 --pmc runs and exit")
     ap.add_argument("--counters-name", default=None, help="file name (without .txt) for --summarize-counters")
     ap.add_argument("--note", default="", help="command lines recorded in the --summarize-* output")
+    ap.add_argument("--per-launch", action="store_true",
+                    help="also print each replayed launch's average time against its own floor (stderr)")
     ap.add_argument("--packed-input", action="store_true",
                     help="feed the stem a packed NC/32HW32 input made by a separate pack kernel in the step")
     args = ap.parse_args()
@@ -797,6 +799,14 @@ def main():
             b.record(stream)
             evs.append((name, ops, byts, a, b))
     torch.cuda.synchronize()
+    if args.per_launch:
+        # launch i of every repetition: its average time, its own floor, and the fraction
+        real = [(nm, o, b) for nm, o, b, _ in launches if nm is not None]
+        print("# launch | kernel | avg us | floor us | floor / avg", file=sys.stderr)
+        for i, (nm, o, b) in enumerate(real):
+            t = sum(ev[3].elapsed_time(ev[4]) for ev in evs[i::len(real)]) * 1e3 / reps
+            fl = max(o / PEAK_I8, b / PEAK_HBM) * 1e6
+            print(f"{i} | {nm} | {t:.1f} | {fl:.1f} | {fl / t:.3f}", file=sys.stderr)
     per_kernel = {}
     for name, ops, byts, a, b in evs:
         d = per_kernel.setdefault(name, {"time": 0.0, "ops": 0, "bytes": 0, "launches": 0})

@@ -99,6 +99,10 @@ __device__ void ifx_raw_buffer_load_lds(ifx_v4i rsrc, __attribute__((address_spa
                                         unsigned voffset, int soffset, int offset,
                                         int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
 
+// Buffer store of 16 bytes; a lane whose offset lies past the resource's range writes nothing.
+__device__ void ifx_raw_buffer_store_v4i32(ifx_v4i vdata, ifx_v4i rsrc, unsigned voffset, int soffset,
+                                           int aux) __asm("llvm.amdgcn.raw.buffer.store.v4i32");
+
 namespace ifx {
 
 typedef ifx_v4i v4i;

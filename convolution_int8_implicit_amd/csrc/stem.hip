@@ -209,15 +209,18 @@ __device__ __forceinline__ void conv_row(const int8_t *wrow, const v4i (&wf)[4][
     }
 }
 
-// Requantise the 16 pooled accumulators of a lane (channels ch0 + 4 tn + i, held at m[tn][i])
-// and pack them into 16 output bytes.  MODE 0: general form (ReLU if relu); 1: shift >= 2 with
-// ReLU; 2: shift >= 2, no ReLU.
-template <int MODE>
-__device__ __forceinline__ v4i requant16(const v4i (&m)[4], const ChanParams &P, int ch0, bool relu)
+// Requantise channel groups K0 and K0 + 1 of a lane's 16 pooled accumulators (channels
+// ch0 + 4 k + i, held at m[k][i]) and pack them into words 0 and 1 of the result: half of the
+// lane's 16 output bytes.  MODE 0: general form (ReLU if relu); 1: shift >= 2 with ReLU;
+// 2: shift >= 2, no ReLU.
+template <int MODE, int K0>
+__device__ __forceinline__ v2i requant8(const v4i (&m)[4], const ChanParams &P, int ch0, bool relu)
 {
-    v4i out;
+    v2i out;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = K0; k < K0 + 2; ++k) {
+        // one channel group's parameters in flight at a time (register pressure)
+        if (k > K0) asm volatile("" ::: "memory");
         const int ch = ch0 + 4 * k;
         int r[4];
         if (MODE == 1) {
@@ -245,7 +248,7 @@ __device__ __forceinline__ v4i requant16(const v4i (&m)[4], const ChanParams &P,
                 r[i] = min(max(v, -128), 127);
             }
         }
-        out[k] = (int)pack4(r[0], r[1], r[2], r[3]);
+        out[k - K0] = (int)pack4(r[0], r[1], r[2], r[3]);
     }
     return out;
 }
@@ -258,7 +261,8 @@ __device__ __forceinline__ v4i requant16(const v4i (&m)[4], const ChanParams &P,
 //
 // Software pipeline: once the vertical maximum of pooled row p is taken, rows 2p and 2p + 1
 // are dead, and the matrix pipe computes convolution rows 2p + 3 and 2p + 4 into their
-// registers while the VALU finishes row p (the horizontal maximum, the requantisation).  Rows
+// registers while the VALU finishes row p (the horizontal maximum, and half of a pair's
+// requantisation, see requant_lo / requant_store).  Rows
 // live in three rotating register sets (row r in set r % 3); the band is unrolled so every set
 // index is a constant.
 template <int MODE>
@@ -307,24 +311,40 @@ __device__ __forceinline__ void compute_unit(const StemArgs &a, const Unit &g, c
                 }
             }
     };
-    auto requant_store = [&](int pp) __attribute__((always_inline)) {
-        // the parameters are re-read from LDS each time (a fence keeps the compiler from
-        // hoisting all 64 of a lane's words out of the band)
+    // A pair of pooled rows is requantised in two halves, each in a scheduling region that also
+    // issues 32 MFMAs of later convolution rows: channel groups 0-1 right after the pair's second
+    // row is pooled, groups 2-3 in the next pooled row's region, before its pooling overwrites
+    // pm.  Both halves are computed in every lane, outside the store's branch (the empty register
+    // barriers), so the compiler can interleave them with the matrix instructions instead of
+    // running them on their own after the branch.  The parameters are re-read from LDS each time
+    // (a fence keeps the compiler from hoisting all 64 of a lane's words out of the band).
+    const long long out_img = 2LL * a.ph * a.pw * 32;  // the image's two 32-channel blocks
+    const v4i ys = make_rsrc(a.y + (long long)g.b * out_img, out_img);
+    v2i q01;
+    auto requant_lo = [&]() __attribute__((always_inline)) {
         asm volatile("" ::: "memory");
-        const v4i q = requant16<MODE>(pm, P, 16 * grp, a.relu != 0);
+        q01 = requant8<MODE, 0>(pm, P, 16 * grp, a.relu != 0);
+        asm volatile("" : "+v"(q01));
+    };
+    auto requant_store = [&](int pp) __attribute__((always_inline)) {
+        asm volatile("" ::: "memory");
+        v2i q23 = requant8<MODE, 2>(pm, P, 16 * grp, a.relu != 0);
+        asm volatile("" : "+v"(q23));
+        const v4i q = {q01.x, q01.y, q23.x, q23.y};
         // before the unit's last store, this wave's memory operations are waited for: the next
         // unit's raw rows (requested a whole unit of work ago) and the earlier stores.  Loads and
         // stores share one counter whose order is not guaranteed between them, so this is a
         // wait for zero; at the top of the next unit no store is left to wait for but this one.
         if (pp == kPR / 2 - 1) wait_vmcnt<0>();
         // odd lanes: pooled row 2pp, column (c - 1) / 2 of the strip; even lanes: row 2pp + 1,
-        // column c / 2
+        // column c / 2.  A buffer store with no branch (a branch would end the scheduling region
+        // and leave the next pooling without matrix work to overlap): lanes without an output
+        // (c >= 14, or a row or column past the image) take an offset past the range.
         const int py = g.py0 + 2 * pp + ((c & 1) ? 0 : 1);
         const int px = g.px0 + kSP * wave + (c >> 1);
-        if (c < 14 && py < a.ph && px < a.pw) {
-            int8_t *dst = a.y + ((((long long)g.b * 2 + (grp >> 1)) * a.ph + py) * a.pw + px) * 32 + 16 * (grp & 1);
-            store16_stream(dst, q);
-        }
+        const bool ok = c < 14 && py < a.ph && px < a.pw;
+        const unsigned off = ok ? (unsigned)((((grp >> 1) * a.ph + py) * a.pw + px) * 32 + 16 * (grp & 1)) : kOOB;
+        ifx_raw_buffer_store_v4i32(q, ys, off, 0, kCachePolicyNT);
     };
 
     row(0);
@@ -340,9 +360,15 @@ __device__ __forceinline__ void compute_unit(const StemArgs &a, const Unit &g, c
             row(2 * p + 3);
             row(2 * p + 4);
         }
-        pool(p);
-        if (p & 1) requant_store(p >> 1);
+        if (p & 1) {
+            pool(p);
+            requant_lo();
+        } else {
+            if (p > 0) requant_store((p >> 1) - 1);
+            pool(p);
+        }
     }
+    requant_store(kPR / 2 - 1);
 }
 
 // Workgroups resident per CU: the register budget (at most 256 VGPRs, two waves per SIMD)
