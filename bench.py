@@ -530,14 +530,26 @@ def ceilings(stream) -> dict:
             rd[0] = ifx.probe_lds_read(o, lout, 4 * cus, 64, stream)
         t_rd = time_steps(lread, stream, 10, 2)
         lds[name] = per_clk_cu(rd[0] / t_rd)
+    # VALU issue rate: SIMD cycles (at the nominal clock) per wave-level step of each operation pair
+    vout = torch.empty(8 * cus, dtype=torch.int32, device="cuda")
+    valu = {}
+    for kind, name in ((0, "mad_i64_i32+ashr (requant core)"), (1, "add+xor"), (2, "cvt_f64+fma_f64+cvt_i32")):
+        nst = [0]
+
+        def vrun():
+            nst[0] = ifx.probe_valu(kind, vout, 8 * cus, 2048, stream)
+        t_v = time_steps(vrun, stream, 10, 2)
+        valu[name] = round(t_v * 2.4e9 * 4 * cus / nst[0], 2)
     return {"copy_gbps": round(2 * nbytes / t_copy / 1e9, 1), "copy_frac_hbm": round(2 * nbytes / t_copy / PEAK_HBM, 4),
             "mfma_i8_tops": round(ops[0] / t_mfma / 1e12, 1), "mfma_frac_peak": round(ops[0] / t_mfma / PEAK_I8, 4),
             "dma_lds_tbps": round(moved[0] / t_dma / 1e12, 2), "dma_lds_bytes_per_clk_cu": per_clk_cu(moved[0] / t_dma),
-            "lds_read_bytes_per_clk_cu": lds,
+            "lds_read_bytes_per_clk_cu": lds, "valu_simd_cycles_per_wave_step": valu,
             "note": "copy: 1 GiB read + 1 GiB written by 16-byte non-temporal vector loads/stores; "
                     f"mfma: {blocks} workgroups x 4 waves x a 4x4 tile of independent v_mfma_i32_16x16x64_i8 chains; "
                     "dma: 1 KB buffer->LDS runs from a 2 MiB buffer, 16 waves per CU; lds: 8 independent "
-                    "ds_read_b128 per wave and round, 16 waves per CU; per-clock figures at the nominal 2.4 GHz"}
+                    "ds_read_b128 per wave and round, 16 waves per CU; valu: 8 independent chains per lane, 32 waves "
+                    "per CU, one wave-level step of a pair = two instructions (three for the f64 form); "
+                    "per-clock figures at the nominal 2.4 GHz"}
 
 
 def main():

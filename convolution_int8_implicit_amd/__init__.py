@@ -119,6 +119,7 @@ def lib() -> ctypes.CDLL:
         "ifx_probe_mfma_i8": ([vp, i32, i32, vp], i32),
         "ifx_probe_dma_lds": ([vp, sz, i32, i32, vp, vp], i32),
         "ifx_probe_lds_read": ([vp, i32, i32, vp, vp], i32),
+        "ifx_probe_valu": ([i32, vp, i32, i32, vp], i32),
         "ifx_last_hip_error": ([], i32),
         "ifx_version": ([], i32),
     }
@@ -333,6 +334,15 @@ def probe_lds_read(offsets: torch.Tensor, out: torch.Tensor, blocks: int, iters:
     assert out.dtype == torch.int32 and out.numel() >= blocks
     _check(lib().ifx_probe_lds_read(_ptr(offsets), blocks, iters, _ptr(out), _stream(stream)), "ifx_probe_lds_read")
     return blocks * 4 * iters * 8 * 1024
+
+
+def probe_valu(kind: int, out: torch.Tensor, blocks: int, iters: int, stream=None) -> int:
+    """VALU issue-rate probe (ifx_probe.h) of one operation pair (kind 0: requantisation core,
+    1: integer add + xor, 2: the f64 form); returns the wave-level chain steps it runs."""
+    _dev(out)
+    assert out.dtype == torch.int32 and out.numel() >= blocks
+    _check(lib().ifx_probe_valu(kind, _ptr(out), blocks, iters, _stream(stream)), "ifx_probe_valu")
+    return blocks * 4 * iters * 8
 
 
 # Bytes of the library-held scratch ifx_block_forward_noalloc uses (IFX_BLOCK_SCRATCH_BYTES).

@@ -100,6 +100,36 @@ __global__ __launch_bounds__(256) void probe_lds_read_kernel(const int *offsets,
     if (keep.x == 0x7fffffff) out[blockIdx.x] = keep.y;
 }
 
+// VALU issue rate of the fixed-point requantisation core against plain integer work: each lane
+// runs `iters` rounds of 8 independent chains of one operation pair (kind 0: v_mad_i64_i32 then
+// an arithmetic shift of the high word, the mode-1 requantisation; 1: an integer add then an
+// xor; 2: int32 -> f64, an f64 fused multiply-add, f64 -> int32, the exact double-precision
+// alternative).  The operands are launch arguments, so nothing folds at compile time; each
+// lane's result is kept live by a store that happens only for an impossible value.
+template <int KIND>
+__global__ __launch_bounds__(256) void probe_valu_kernel(int *out, int iters, int m, long long add, int sh, double dm,
+                                                         double dc)
+{
+    int v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = (int)threadIdx.x * 7 + j;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (KIND == 0)
+                v[j] = ((int)(((long long)v[j] * m + add) >> 32)) >> sh;
+            else if (KIND == 1)
+                v[j] = (v[j] + m) ^ sh;
+            else
+                v[j] = (int)__builtin_fma((double)v[j], dm, dc);
+        }
+    }
+    int s = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s += v[j];
+    if (s == 0x12345678) out[blockIdx.x] = s;
+}
+
 }  // namespace
 }  // namespace ifx
 
@@ -146,6 +176,21 @@ int32_t ifx_probe_lds_read(const int32_t *offsets, int32_t blocks, int32_t iters
     if (blocks <= 0 || iters <= 0) return 2;
     hipLaunchKernelGGL(ifx::probe_lds_read_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
                        offsets, iters, out);
+    return hipGetLastError() == hipSuccess ? 0 : 6;
+}
+
+int32_t ifx_probe_valu(int32_t kind, int32_t *out, int32_t blocks, int32_t iters, void *stream)
+{
+    if (!out) return 1;
+    if (blocks <= 0 || iters <= 0 || kind < 0 || kind > 2) return 2;
+    const dim3 g((unsigned)blocks), b(256);
+    const hipStream_t st = (hipStream_t)stream;
+    if (kind == 0)
+        hipLaunchKernelGGL(ifx::probe_valu_kernel<0>, g, b, 0, st, out, iters, 1234567, (1LL << 40) + 5, 9, 1e-5, 0.5);
+    else if (kind == 1)
+        hipLaunchKernelGGL(ifx::probe_valu_kernel<1>, g, b, 0, st, out, iters, 1234567, (1LL << 40) + 5, 9, 1e-5, 0.5);
+    else
+        hipLaunchKernelGGL(ifx::probe_valu_kernel<2>, g, b, 0, st, out, iters, 1234567, (1LL << 40) + 5, 9, 1e-5, 0.5);
     return hipGetLastError() == hipSuccess ? 0 : 6;
 }
 

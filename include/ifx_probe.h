@@ -61,6 +61,19 @@ int32_t ifx_probe_dma_lds(const void *src, size_t bytes, int32_t blocks, int32_t
  */
 int32_t ifx_probe_lds_read(const int32_t *offsets, int32_t blocks, int32_t iters, int32_t *out, void *stream);
 
+/*
+ * VALU issue rate of one operation pair: `blocks` workgroups of four waves,
+ * each lane running `iters` rounds of 8 independent chains of
+ *   kind 0: v_mad_i64_i32 + an arithmetic shift of the high word (the
+ *           fixed-point requantisation core of the fused epilogue),
+ *   kind 1: an integer add + an xor (plain full-rate integer work),
+ *   kind 2: int32 -> f64, an f64 fused multiply-add, f64 -> int32 (an exact
+ *           double-precision form of the same requantisation, for comparison).
+ * out: DEVICE, `blocks` int32 (written only for an impossible value).
+ * Chain steps = blocks * 256 * iters * 8.
+ */
+int32_t ifx_probe_valu(int32_t kind, int32_t *out, int32_t blocks, int32_t iters, void *stream);
+
 #ifdef __cplusplus
 }
 #endif
