@@ -794,6 +794,30 @@ def test_stem_nhwc_input(ifx, orc, n, h, w, c):
         np.testing.assert_array_equal(got, orc.conv_fused(x, wt, bias, mult, shift, 2, 3, flags))
 
 
+@pytest.mark.parametrize("nhwc", [False, True])
+def test_stem_requant_edges(ifx, orc, nhwc):
+    """The stem's three requantisation forms on pooled accumulators: shifts 0 and 1 (the general
+    form), the tie-correcting form without ReLU (mult 2^30, shift 2: ties at y = 8j + 4), mult 0,
+    1 and 2^31 - 1, through the packed and the compact NHWC input paths.  The pooled maximum is
+    what gets requantised, which the epilogue allows for mult >= 0 only, so no mult is negative."""
+    note(f"stem requant edges nhwc={nhwc}")
+    rng = np.random.default_rng(31 + nhwc)
+    n, h, w, c = 2, 40, 44, 3
+    x = rand(rng, (n, h, w, c), -128, 127)
+    wt = rand(rng, (64, 7, 7, c), -8, 8)  # small weights: many pooled sums near the tie points
+    bias = rand(rng, 64, -(1 << 10), 1 << 10, np.int32)
+    shift = np.tile(np.array([0, 1, 2, 3, 31, 30, 16, 8], np.int32), 8)
+    mult = np.tile(np.array([1 << 30, (1 << 31) - 1, 0, 1, (1 << 31) - 1, 1 << 29, 12345, 1 << 30], np.int32), 8)
+    # the tie case with a negative bias: about 2 % of the pooled sums are negative exact ties inside the
+    # int8 range, where rounding half away from zero and half up differ
+    ties = (rand(rng, 64, -9000, -5000, np.int32), np.full(64, 1 << 30, np.int32), np.full(64, 2, np.int32))
+    extra = ifx.INPUT_NHWC if nhwc else 0
+    for b_, m_, s_ in ((bias, mult, shift), ties):
+        for flags in (ifx.RELU | ifx.MAXPOOL, ifx.MAXPOOL):
+            got = gpu_conv(ifx, x, wt, b_, m_, s_, 7, 2, 3, flags | extra)
+            np.testing.assert_array_equal(got, orc.conv_fused(x, wt, b_, m_, s_, 2, 3, flags))
+
+
 # ------------------------------------------------------------------ small networks: pool and head
 @pytest.mark.parametrize("n,h,w,nblk", [(2, 40, 44, 0), (1, 224, 224, 0), (3, 16, 16, 1), (1, 9, 12, 1),
                                         (515, 16, 16, 1), (4097, 9, 12, 0)])
