@@ -493,6 +493,11 @@ def ceilings(stream) -> dict:
     def mfma():
         ops[0] = ifx.probe_mfma_i8(out, blocks, 4096, stream)
     t_mfma = time_steps(mfma, stream, 10, 2)
+    ops_d = [0]
+
+    def mfma_data():
+        ops_d[0] = ifx.probe_mfma_i8_data(out, blocks, 1024, stream)
+    t_mfma_d = time_steps(mfma_data, stream, 10, 2)
     cus = props.multi_processor_count
 
     def per_clk_cu(rate):  # bytes per second -> bytes per clock per CU at the nominal 2.4 GHz
@@ -542,10 +547,14 @@ def ceilings(stream) -> dict:
         valu[name] = round(t_v * 2.4e9 * 4 * cus / nst[0], 2)
     return {"copy_gbps": round(2 * nbytes / t_copy / 1e9, 1), "copy_frac_hbm": round(2 * nbytes / t_copy / PEAK_HBM, 4),
             "mfma_i8_tops": round(ops[0] / t_mfma / 1e12, 1), "mfma_frac_peak": round(ops[0] / t_mfma / PEAK_I8, 4),
+            "mfma_i8_changing_operands_tops": round(ops_d[0] / t_mfma_d / 1e12, 1),
+            "mfma_changing_operands_frac_peak": round(ops_d[0] / t_mfma_d / PEAK_I8, 4),
             "dma_lds_tbps": round(moved[0] / t_dma / 1e12, 2), "dma_lds_bytes_per_clk_cu": per_clk_cu(moved[0] / t_dma),
             "lds_read_bytes_per_clk_cu": lds, "valu_simd_cycles_per_wave_step": valu,
             "note": "copy: 1 GiB read + 1 GiB written by 16-byte non-temporal vector loads/stores; "
-                    f"mfma: {blocks} workgroups x 4 waves x a 4x4 tile of independent v_mfma_i32_16x16x64_i8 chains; "
+                    f"mfma: {blocks} workgroups x 4 waves x a 4x4 tile of independent v_mfma_i32_16x16x64_i8 chains on "
+                    "constant register operands; mfma_i8_changing_operands: the same cycling four sets of random "
+                    "operand bits, so each instruction multiplies fresh bytes; "
                     "dma: 1 KB buffer->LDS runs from a 2 MiB buffer, 16 waves per CU; lds: 8 independent "
                     "ds_read_b128 per wave and round, 16 waves per CU; valu: 8 independent chains per lane, 32 waves "
                     "per CU, one wave-level step of a pair = two instructions (three for the f64 form); "

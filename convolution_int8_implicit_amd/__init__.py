@@ -117,6 +117,7 @@ def lib() -> ctypes.CDLL:
         "ifx_status_string": ([i32], ctypes.c_char_p),
         "ifx_probe_copy": ([vp, vp, sz, vp], i32),
         "ifx_probe_mfma_i8": ([vp, i32, i32, vp], i32),
+        "ifx_probe_mfma_i8_data": ([vp, i32, i32, vp], i32),
         "ifx_probe_dma_lds": ([vp, sz, i32, i32, vp, vp], i32),
         "ifx_probe_lds_read": ([vp, i32, i32, vp, vp], i32),
         "ifx_probe_valu": ([i32, vp, i32, i32, vp], i32),
@@ -315,6 +316,14 @@ def probe_mfma_i8(out: torch.Tensor, blocks: int, iters: int, stream=None) -> in
     assert out.dtype == torch.int32 and out.numel() >= 4 * blocks
     _check(lib().ifx_probe_mfma_i8(_ptr(out), blocks, iters, _stream(stream)), "ifx_probe_mfma_i8")
     return blocks * 4 * iters * 16 * 32768
+
+
+def probe_mfma_i8_data(out: torch.Tensor, blocks: int, iters: int, stream=None) -> int:
+    """int8 MFMA rate probe with operands that change every instruction (ifx_probe.h); returns its ops."""
+    _dev(out)
+    assert out.dtype == torch.int32 and out.numel() >= 4 * blocks
+    _check(lib().ifx_probe_mfma_i8_data(_ptr(out), blocks, iters, _stream(stream)), "ifx_probe_mfma_i8_data")
+    return blocks * 4 * iters * 4 * 16 * 32768
 
 
 def probe_dma_lds(src: torch.Tensor, out: torch.Tensor, blocks: int, iters: int, stream=None) -> int:

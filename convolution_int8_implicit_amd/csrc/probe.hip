@@ -51,6 +51,54 @@ __global__ __launch_bounds__(256) void probe_mfma_kernel(int *out, int iters, in
     if (lane == 0) out[blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)] = s.x + s.y + s.z + s.w;
 }
 
+// The same tile shape with operands that change from one MFMA to the next, as a contraction's do:
+// four sets of random operand bits (a 32-bit integer hash of the lane and a counter) cycled
+// through, so every instruction multiplies fresh bytes.  The matrix pipe's rate with toggling
+// inputs, against the constant operands above.
+__device__ __forceinline__ unsigned probe_hash(unsigned x)
+{
+    x ^= x >> 16;
+    x *= 0x7feb352du;
+    x ^= x >> 15;
+    x *= 0x846ca68bu;
+    x ^= x >> 16;
+    return x;
+}
+
+__global__ __launch_bounds__(256) void probe_mfma_data_kernel(int *out, int iters, unsigned seed)
+{
+    const int lane = threadIdx.x & 63;
+    v4i af[4][4], bf[4][4], acc[4][4];
+    unsigned h = seed ^ ((blockIdx.x * 256u + threadIdx.x) * 0x9e3779b9u);
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                h = probe_hash(h + 1u);
+                af[st][t][e] = (int)h;
+                h = probe_hash(h + 1u);
+                bf[st][t][e] = (int)h;
+            }
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+#pragma unroll
+            for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+                for (int tn = 0; tn < 4; ++tn)
+                    acc[tm][tn] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                        af[st][tm], bf[st][tn], (it == 0 && st == 0) ? (v4i){0, 0, 0, 0} : acc[tm][tn], 0, 0, 0);
+    }
+    v4i sum = {0, 0, 0, 0};
+#pragma unroll
+    for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+        for (int tn = 0; tn < 4; ++tn) sum += acc[tm][tn];
+    if (lane == 0) out[blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)] = sum.x + sum.y + sum.z + sum.w;
+}
+
 // Each wave moves 8 contiguous 1 KB runs per round from src into its own 8 KB of LDS by
 // buffer->LDS DMA, then waits for them: run j of round i of wave w is 1 KB piece
 // (8 (w iters + i) + j) mod pieces of src, so a src that fits L2 is read from L2.
@@ -156,6 +204,15 @@ int32_t ifx_probe_mfma_i8(int32_t *out, int32_t blocks, int32_t iters, void *str
     if (blocks <= 0 || iters <= 0) return 2;
     hipLaunchKernelGGL(ifx::probe_mfma_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, out,
                        iters, 7);
+    return hipGetLastError() == hipSuccess ? 0 : 6;
+}
+
+int32_t ifx_probe_mfma_i8_data(int32_t *out, int32_t blocks, int32_t iters, void *stream)
+{
+    if (!out) return 1;
+    if (blocks <= 0 || iters <= 0) return 2;
+    hipLaunchKernelGGL(ifx::probe_mfma_data_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, out,
+                       iters, 0x5eedu);
     return hipGetLastError() == hipSuccess ? 0 : 6;
 }
 

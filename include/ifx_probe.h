@@ -38,6 +38,16 @@ int32_t ifx_probe_copy(const void *src, void *dst, size_t bytes, void *stream);
 int32_t ifx_probe_mfma_i8(int32_t *out, int32_t blocks, int32_t iters, void *stream);
 
 /*
+ * The same with operands that change from one MFMA to the next: four sets of
+ * random operand bits per lane (an integer hash of the lane and a counter),
+ * cycled, so every instruction multiplies fresh bytes as a contraction's MFMAs
+ * do (the matrix pipe's power, and with it its clock, depends on how many
+ * operand bits toggle).  out: DEVICE, blocks * 4 elements.
+ * Ops = blocks * 4 * iters * 4 * 16 * 32768.
+ */
+int32_t ifx_probe_mfma_i8_data(int32_t *out, int32_t blocks, int32_t iters, void *stream);
+
+/*
  * Buffer->LDS DMA rate: `blocks` workgroups of four waves, each wave running
  * `iters` rounds of 8 DMAs of one contiguous 1 KB run each (16 bytes per lane)
  * from src into its own LDS, waiting for them at the end of the round -- the
