@@ -437,3 +437,62 @@ int orc_fold_bn(int c_out, double x_scale, double y_scale, double eps, int w_per
     }
     return ORC_OK;
 }
+
+/*
+ * Quantisation of the input image and dequantisation of the logits (Alibaba
+ * inference article, Hanguang 800 section: the accelerator takes integer
+ * data, and the quantisation before the engine and the dequantisation after
+ * it, which had run on the host and taken most of the latency, belong with
+ * the accelerated pre- and post-processing).  The page prints no formula.
+ * The reading, with the path's symmetric int8 codes (real = s_x * code, zero
+ * point 0), one IEEE single-precision operation at a time (round to nearest
+ * even, no fused multiply-add):
+ *   fp32 image:  t = x * mult[ch]
+ *   uint8 image: t = ((float)u - mean[ch]) * mult[ch]
+ *                (the per-channel mean subtraction and 1 / (std * s_x)
+ *                scaling of an ImageNet-style pre-processing, fused into the
+ *                quantisation)
+ *   code = saturate_int8(round_half_away(t)); a NaN t gives code 0
+ * where ch = element index mod c (NHWC: channels innermost), and
+ *   logits:      y = (float)q * scale.
+ */
+static int8_t orc_code_of(float t)
+{
+    if (t != t) return 0;
+    double r = orc_round_half_away((double)t);
+    if (r > 127.0) r = 127.0;
+    if (r < -128.0) r = -128.0;
+    return (int8_t)r;
+}
+
+int orc_quantize_f32(const float *x, int64_t count, int c, const float *mult, int8_t *q)
+{
+    if (c <= 0 || count < 0 || count % c) return ORC_E_ARG;
+    for (int64_t i = 0; i < count; i++) {
+        float t = x[i] * mult[i % c];
+        q[i] = orc_code_of(t);
+    }
+    return ORC_OK;
+}
+
+int orc_quantize_u8(const uint8_t *x, int64_t count, int c, const float *mean, const float *mult, int8_t *q)
+{
+    if (c <= 0 || count < 0 || count % c) return ORC_E_ARG;
+    for (int64_t i = 0; i < count; i++) {
+        int ch = (int)(i % c);
+        float d = (float)x[i] - mean[ch];
+        float t = d * mult[ch];
+        q[i] = orc_code_of(t);
+    }
+    return ORC_OK;
+}
+
+int orc_dequantize_i32(const int32_t *q, int64_t count, float scale, float *y)
+{
+    if (count < 0) return ORC_E_ARG;
+    for (int64_t i = 0; i < count; i++) {
+        float v = (float)q[i];
+        y[i] = v * scale;
+    }
+    return ORC_OK;
+}

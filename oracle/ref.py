@@ -71,6 +71,12 @@ def _load():
     lib.orc_pack_weights_stem.argtypes = [vp, i32, i32, vp]
     lib.orc_pack_weights_stem.restype = i32
     f64 = ctypes.c_double
+    lib.orc_quantize_f32.argtypes = [vp, i64, i32, vp, vp]
+    lib.orc_quantize_f32.restype = i32
+    lib.orc_quantize_u8.argtypes = [vp, i64, i32, vp, vp, vp]
+    lib.orc_quantize_u8.restype = i32
+    lib.orc_dequantize_i32.argtypes = [vp, i64, ctypes.c_float, vp]
+    lib.orc_dequantize_i32.restype = i32
     lib.orc_fold_bn.argtypes = [i32, f64, f64, f64, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.orc_fold_bn.restype = i32
     return lib
@@ -302,3 +308,33 @@ def fold_bn(x_scale, y_scale, eps, w_scale, gamma, beta, mean, var, conv_bias=No
                        _ptr(mean), _ptr(var), *[_ptr(o) for o in outs])
     _check(rc, "fold_bn")
     return tuple(outs)
+
+
+def quantize_f32(x, mult) -> np.ndarray:
+    """fp32 NHWC image -> int8 codes (orc_quantize_f32): code = sat8(round_half_away(x * mult[ch])),
+    one float32 multiply; ch is the last axis.  mult: float32 [c]."""
+    x = _c(x, np.float32)
+    mult = _c(mult, np.float32).ravel()
+    q = np.empty(x.shape, np.int8)
+    _check(lib().orc_quantize_f32(_ptr(x), x.size, mult.size, _ptr(mult), _ptr(q)), "quantize_f32")
+    return q
+
+
+def quantize_u8(x, mean, mult) -> np.ndarray:
+    """uint8 NHWC image -> int8 codes (orc_quantize_u8): code = sat8(round_half_away(((float)u -
+    mean[ch]) * mult[ch])), float32 operations; ch is the last axis."""
+    x = _c(x, np.uint8)
+    mean = _c(mean, np.float32).ravel()
+    mult = _c(mult, np.float32).ravel()
+    assert mean.size == mult.size
+    q = np.empty(x.shape, np.int8)
+    _check(lib().orc_quantize_u8(_ptr(x), x.size, mult.size, _ptr(mean), _ptr(mult), _ptr(q)), "quantize_u8")
+    return q
+
+
+def dequantize_i32(q, scale) -> np.ndarray:
+    """int32 codes (the logits) -> float32 (orc_dequantize_i32): y = (float)q * scale."""
+    q = _c(q, np.int32)
+    y = np.empty(q.shape, np.float32)
+    _check(lib().orc_dequantize_i32(_ptr(q), q.size, float(np.float32(scale)), _ptr(y)), "dequantize_i32")
+    return y

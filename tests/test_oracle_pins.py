@@ -568,3 +568,98 @@ def test_p15_folded_epilogue_matches_float_model(orc):
                 assert got == want, (o, int(acc))
                 checked += 1
     assert checked > 0.8 * n * 40
+
+
+# ------------------------------------------------------------------ P18, P19: input quantisation, logits
+def _sat8(v: int) -> int:
+    return max(-128, min(127, v))
+
+
+def _away(fr: Fraction) -> int:
+    """Round half away from zero of an exact rational."""
+    a = abs(fr)
+    q = int(a)
+    if a - q >= Fraction(1, 2):
+        q += 1
+    return q if fr >= 0 else -q
+
+
+def test_p18_quantize_closed_forms(orc):
+    """fp32 image codes: mult = 2^-k and x = j 2^k give code sat8(j) exactly; x = (2n + 1) / 2 at
+    mult 1 are exact ties, rounded away from zero; huge, infinite and NaN products saturate or
+    give 0; the channel is the last axis."""
+    for k in range(5):
+        j = np.arange(-140, 141, dtype=np.int64)
+        x = (j * 2 ** k).astype(np.float32).reshape(-1, 1)
+        m = np.array([2.0 ** -k], np.float32)
+        np.testing.assert_array_equal(orc.quantize_f32(x, m).ravel(), np.clip(j, -128, 127))
+    n = np.arange(-21, 21)
+    x = ((2 * n + 1) / 2).astype(np.float32).reshape(-1, 1)
+    want = np.where(n >= 0, n + 1, n)  # (2n+1)/2 away from zero: n + 1 above 0, n below
+    np.testing.assert_array_equal(orc.quantize_f32(x, np.ones(1, np.float32)).ravel(), want)
+    x = np.array([[1e30], [-1e30], [np.inf], [-np.inf], [np.nan], [127.49], [127.5], [-128.49], [-128.5]],
+                 np.float32)
+    np.testing.assert_array_equal(orc.quantize_f32(x, np.ones(1, np.float32)).ravel(),
+                                  [127, -128, 127, -128, 0, 127, 127, -128, -128])
+    # three channels with different multipliers: element (p, ch) takes mult[ch]
+    x = np.tile(np.array([10.0, 10.0, 10.0], np.float32), (4, 1))
+    np.testing.assert_array_equal(orc.quantize_f32(x, np.array([1.0, 0.5, 0.25], np.float32)),
+                                  np.tile([10, 5, 3], (4, 1)))  # 2.5 rounds away to 3
+
+
+def test_p18_quantize_rounds_the_float32_product(orc):
+    """The code is the rounding of the float32 product (one IEEE single multiply), not of the
+    exact product: on pairs (x, mult) placed next to half-integers, where the two roundings
+    disagree, the oracle follows the float32 one.  numpy's float32 multiply gives that product;
+    the rounding decisions are taken in exact rationals."""
+    rng = np.random.default_rng(18)
+    differ = agree = 0
+    xs, ms = [], []
+    for _ in range(400):
+        m = np.float32(rng.uniform(0.01, 2.0))
+        k = int(rng.integers(-100, 100))
+        x0 = np.float32((k + 0.5) / float(m))
+        for step in range(-3, 4):
+            x = x0
+            for _ in range(abs(step)):
+                x = np.nextafter(x, np.float32(np.inf if step > 0 else -np.inf), dtype=np.float32)
+            xs.append(x)
+            ms.append(m)
+    xs = np.array(xs, np.float32)
+    ms = np.array(ms, np.float32)
+    got = np.array([orc.quantize_f32(np.array([[x]], np.float32), np.array([m], np.float32))[0, 0]
+                    for x, m in zip(xs, ms)])
+    for x, m, g in zip(xs, ms, got):
+        fl = np.float32(x) * np.float32(m)          # IEEE single product
+        want_fl = _sat8(_away(Fraction(float(fl))))
+        want_ex = _sat8(_away(Fraction(float(x)) * Fraction(float(m))))
+        assert g == want_fl, (float(x), float(m))
+        differ += want_fl != want_ex
+        agree += want_fl == want_ex
+    assert differ > 0 and agree > 0
+
+
+def test_p18_quantize_u8_closed_forms(orc):
+    """uint8 image codes over all 256 values: mean 128, mult 1 gives u - 128; mean 127.5, mult 1
+    gives the ties u - 127.5 rounded away from zero; mean 0, mult 1/2 gives u / 2 rounded away
+    and saturated; channels take their own mean and mult."""
+    u = np.arange(256, dtype=np.uint8).reshape(-1, 1)
+    one = np.ones(1, np.float32)
+    np.testing.assert_array_equal(orc.quantize_u8(u, [128.0], one).ravel(), np.arange(256) - 128)
+    ui = np.arange(256)
+    np.testing.assert_array_equal(orc.quantize_u8(u, [127.5], one).ravel(), np.minimum(np.where(ui >= 128, ui - 127, ui - 128), 127))
+    np.testing.assert_array_equal(orc.quantize_u8(u, [0.0], [0.5]).ravel(), np.minimum((ui + 1) // 2, 127))
+    x = np.tile(np.array([200, 200, 200], np.uint8), (3, 1))
+    got = orc.quantize_u8(x, [100.0, 150.0, 250.0], [0.5, 1.0, 2.0])
+    np.testing.assert_array_equal(got, np.tile([50, 50, -100], (3, 1)))
+
+
+def test_p19_dequantize_logits(orc):
+    """y = (float)q * scale: exact for |q| < 2^24 and scale a power of two; beyond 2^24 the int32 ->
+    float32 conversion rounds to nearest even first (2^24 + 1 -> 2^24, -(2^24 + 3) -> -(2^24 + 4))."""
+    q = np.array([0, 1, -1, 5, -7, 123456, -(1 << 23)], np.int32)
+    for k in range(-3, 4):
+        np.testing.assert_array_equal(orc.dequantize_i32(q, 2.0 ** k), (q.astype(np.float64) * 2.0 ** k).astype(np.float32))
+    q = np.array([(1 << 24) + 1, -((1 << 24) + 3), (1 << 31) - 1, -(1 << 31)], np.int32)
+    np.testing.assert_array_equal(orc.dequantize_i32(q, 1.0),
+                                  np.array([1 << 24, -((1 << 24) + 4), 2.0 ** 31, -(2.0 ** 31)], np.float32))
