@@ -85,6 +85,7 @@ def lib() -> ctypes.CDLL:
         raise RuntimeError(f"libifx.so not built ({LIB_PATH}); run python -m convolution_int8_implicit_amd.build")
     L = ctypes.CDLL(LIB_PATH)
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    i64 = ctypes.c_int64
     D = ctypes.POINTER(ConvDesc)
     sigs = {
         "ifx_conv_validate": ([D], i32),
@@ -92,6 +93,9 @@ def lib() -> ctypes.CDLL:
         "ifx_act_bytes": ([i32, i32, i32, i32], sz),
         "ifx_wpack_bytes": ([D], sz),
         "ifx_pack_act": ([vp, vp, i32, i32, i32, i32, vp], i32),
+        "ifx_quantize_f32": ([vp, vp, i64, i32, vp, vp], i32),
+        "ifx_quantize_u8": ([vp, vp, i64, i32, vp, vp, vp], i32),
+        "ifx_dequantize_i32": ([vp, vp, i64, ctypes.c_float, vp], i32),
         "ifx_unpack_act": ([vp, vp, i32, i32, i32, i32, vp], i32),
         "ifx_pack_weights": ([D, vp, vp, vp], i32),
         "ifx_conv_fused": ([D, vp, vp, vp, vp, vp, vp, vp, vp], i32),
@@ -186,6 +190,42 @@ def pack_act(x_nhwc: torch.Tensor, out: Optional[torch.Tensor] = None, stream=No
     if out is None:
         out = torch.empty((n, (c + 31) // 32, h, w, 32), dtype=torch.int8, device=x_nhwc.device)
     _check(lib().ifx_pack_act(_ptr(x_nhwc), _ptr(out), n, h, w, c, _stream(stream)), "ifx_pack_act")
+    return out
+
+
+def quantize_f32(x: torch.Tensor, mult: torch.Tensor, out: Optional[torch.Tensor] = None,
+                 stream=None) -> torch.Tensor:
+    """float32 NHWC image -> int8 codes (ifx_quantize_f32); mult: float32 [c], c the last axis."""
+    _dev(x, mult, out)
+    assert x.dtype == torch.float32 and mult.dtype == torch.float32
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.int8, device=x.device)
+    _check(lib().ifx_quantize_f32(_ptr(x), _ptr(out), x.numel(), mult.numel(), _ptr(mult), _stream(stream)),
+           "ifx_quantize_f32")
+    return out
+
+
+def quantize_u8(x: torch.Tensor, mean: torch.Tensor, mult: torch.Tensor, out: Optional[torch.Tensor] = None,
+                stream=None) -> torch.Tensor:
+    """uint8 NHWC image -> int8 codes (ifx_quantize_u8); mean, mult: float32 [c], c the last axis."""
+    _dev(x, mean, mult, out)
+    assert x.dtype == torch.uint8 and mean.dtype == torch.float32 and mult.dtype == torch.float32
+    assert mean.numel() == mult.numel()
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.int8, device=x.device)
+    _check(lib().ifx_quantize_u8(_ptr(x), _ptr(out), x.numel(), mult.numel(), _ptr(mean), _ptr(mult),
+                                 _stream(stream)), "ifx_quantize_u8")
+    return out
+
+
+def dequantize_i32(q: torch.Tensor, scale: float, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """int32 results (the logits) -> float32 (ifx_dequantize_i32): (float)q * scale."""
+    _dev(q, out)
+    assert q.dtype == torch.int32
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    _check(lib().ifx_dequantize_i32(_ptr(q), _ptr(out), q.numel(), float(scale), _stream(stream)),
+           "ifx_dequantize_i32")
     return out
 
 

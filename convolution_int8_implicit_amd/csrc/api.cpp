@@ -728,6 +728,36 @@ ifx_status ifx_pack_act(const int8_t *x_nhwc, int8_t *x_blk, int32_t n, int32_t 
     return hip_status(ifx::launch_pack_act(x_nhwc, x_blk, n, h, w, c, (hipStream_t)stream));
 }
 
+ifx_status ifx_quantize_f32(const float *x, int8_t *q, int64_t count, int32_t c, const float *mult, void *stream)
+{
+    if (!x || !q || !mult) return IFX_E_NULL;
+    if (c < 1 || count < 0 || count > 0x7fffffffLL || count % c) return IFX_E_SHAPE;
+    if (!aligned16(x) || !aligned16(q) || (reinterpret_cast<uintptr_t>(mult) & 3u)) return IFX_E_ALIGN;
+    if (count == 0) return IFX_OK;
+    return hip_status(ifx::launch_quantize(x, false, q, (int)count, c, nullptr, mult, (hipStream_t)stream));
+}
+
+ifx_status ifx_quantize_u8(const uint8_t *x, int8_t *q, int64_t count, int32_t c, const float *mean,
+                           const float *mult, void *stream)
+{
+    if (!x || !q || !mean || !mult) return IFX_E_NULL;
+    if (c < 1 || count < 0 || count > 0x7fffffffLL || count % c) return IFX_E_SHAPE;
+    if (!aligned16(x) || !aligned16(q) || (reinterpret_cast<uintptr_t>(mean) & 3u) ||
+        (reinterpret_cast<uintptr_t>(mult) & 3u))
+        return IFX_E_ALIGN;
+    if (count == 0) return IFX_OK;
+    return hip_status(ifx::launch_quantize(x, true, q, (int)count, c, mean, mult, (hipStream_t)stream));
+}
+
+ifx_status ifx_dequantize_i32(const int32_t *q, float *y, int64_t count, float scale, void *stream)
+{
+    if (!q || !y) return IFX_E_NULL;
+    if (count < 0 || count > 0x7fffffffLL) return IFX_E_SHAPE;
+    if (!aligned16(q) || !aligned16(y)) return IFX_E_ALIGN;
+    if (count == 0) return IFX_OK;
+    return hip_status(ifx::launch_dequantize(q, y, (int)count, scale, (hipStream_t)stream));
+}
+
 ifx_status ifx_unpack_act(const int8_t *x_blk, int8_t *x_nhwc, int32_t n, int32_t h, int32_t w, int32_t c,
                           void *stream)
 {

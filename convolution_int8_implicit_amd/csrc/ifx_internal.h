@@ -155,6 +155,10 @@ hipError_t launch_conv_split(const ConvArgs &a, int kh, int kw, int32_t *part, s
 // `pj` (same output pixels and channels, no ReLU): the projection's requantised output is the
 // shortcut and never reaches HBM; a.res is not read.
 hipError_t launch_conv_proj(const ConvArgs &a, const ConvArgs &pj, hipStream_t s);
+// input quantisation (fp32 or uint8 NHWC image -> int8 codes) and logits dequantisation, quant.hip
+hipError_t launch_quantize(const void *x, bool u8, int8_t *q, int count, int c, const float *mean, const float *mult,
+                           hipStream_t s);
+hipError_t launch_dequantize(const int32_t *q, float *y, int count, float scale, hipStream_t s);
 hipError_t launch_fold_bn(const FoldArgs &f, int32_t *bias, int32_t *mult, int32_t *shift, int32_t *status,
                           hipStream_t s);
 // 1x1 convolutions with at most 128 input channels (conv1x1.hip)

@@ -418,6 +418,41 @@ ifx_status ifx_fold_bn(const ifx_bn_fold *f, int32_t *bias, int32_t *mult, int32
                        void *stream);
 
 /*
+ * Quantisation of the input image on the device (Alibaba inference article,
+ * Hanguang 800 section: the engine runs on integer data, and the
+ * quantisation before it, which had run on the host and taken most of the
+ * latency, moves into the accelerated pre-processing).  The result is the
+ * compact int8 NHWC image the stem reads with IFX_INPUT_NHWC, in the path's
+ * symmetric codes (real = s_x * code).  Element i of the NHWC tensor
+ * (channels innermost) belongs to channel ch = i % c:
+ *   ifx_quantize_f32: code = sat8(round_half_away(x * mult[ch]))
+ *   ifx_quantize_u8:  code = sat8(round_half_away(((float)u - mean[ch]) * mult[ch]))
+ *                     (an ImageNet-style per-channel mean subtraction and
+ *                     1 / (std * s_x) scaling fused into the quantisation)
+ * One IEEE single-precision operation at a time (round to nearest even, no
+ * fused multiply-add), round half away from zero, saturation to [-128, 127];
+ * a NaN product gives code 0 and an infinite one saturates.
+ *   x      DEVICE, `count` float32 or uint8 elements, 16-byte aligned
+ *   q      DEVICE, `count` int8, 16-byte aligned, not overlapping x
+ *   mean, mult  DEVICE float32 [c], 4-byte aligned
+ *   count  0 <= count < 2^31 and a multiple of c (c >= 1)
+ * Errors (nothing is launched): IFX_E_NULL, IFX_E_SHAPE, IFX_E_ALIGN.
+ */
+ifx_status ifx_quantize_f32(const float *x, int8_t *q, int64_t count, int32_t c, const float *mult, void *stream);
+ifx_status ifx_quantize_u8(const uint8_t *x, int8_t *q, int64_t count, int32_t c, const float *mean,
+                           const float *mult, void *stream);
+
+/*
+ * Dequantisation of int32 results, the FC's logits, after the engine (the
+ * same article):  y = (float)q * scale  (the int32 -> float32 conversion
+ * rounds to nearest even beyond 2^24; then one single-precision multiply).
+ *   q, y   DEVICE, `count` elements each, 16-byte aligned, not overlapping
+ *   count  0 <= count < 2^31
+ * Errors (nothing is launched): IFX_E_NULL, IFX_E_SHAPE, IFX_E_ALIGN.
+ */
+ifx_status ifx_dequantize_i32(const int32_t *q, float *y, int64_t count, float scale, void *stream);
+
+/*
  * Host-only: the kernel instance ifx_conv_fused(d, ...) launches, named as
  * profilers print it (e.g. "igemm_kernel<3, 3, 128, 128, 2, false, true,
  * false>"), written NUL-terminated into buf.  The name comes from the very

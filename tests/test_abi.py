@@ -327,3 +327,31 @@ def test_dispatch_of_the_network_shapes():
     assert proj_name(1024, 14, 256, 512, 1024, 1) == wide  # res4.1 on the even-pixel copy
     assert proj_name(1024, 7, 512, 1024, 2048, 1) == wide  # res5.1
     assert proj_name(97, 14, 256, 512, 1024, 1) == "igemm_kernel<1, 1, 128, 128, 2, 64, true, true, true>"
+
+
+def test_quantisation_validation():
+    """ifx_quantize_f32 / ifx_quantize_u8 / ifx_dequantize_i32 reject null, shape and alignment
+    errors before any launch (an empty tensor is a no-op)."""
+    import convolution_int8_implicit_amd as ifx
+    L = ifx.lib()
+    fake = ctypes.c_void_p(0x100000)
+    odd = ctypes.c_void_p(0x100001)
+    word = ctypes.c_void_p(0x100004)      # 4-byte aligned: fine for mean/mult, not for x, q or y
+    assert L.ifx_quantize_f32(None, fake, 12, 3, fake, None) == 1
+    assert L.ifx_quantize_f32(fake, fake, 12, 3, None, None) == 1
+    assert L.ifx_quantize_f32(fake, fake, 13, 3, fake, None) == 2      # not a multiple of c
+    assert L.ifx_quantize_f32(fake, fake, 12, 0, fake, None) == 2
+    assert L.ifx_quantize_f32(fake, fake, -3, 3, fake, None) == 2
+    assert L.ifx_quantize_f32(fake, fake, 1 << 31, 1, fake, None) == 2
+    assert L.ifx_quantize_f32(word, fake, 12, 3, fake, None) == 4
+    assert L.ifx_quantize_f32(fake, odd, 12, 3, fake, None) == 4
+    assert L.ifx_quantize_f32(fake, fake, 12, 3, odd, None) == 4
+    assert L.ifx_quantize_f32(fake, fake, 0, 3, word, None) == 0
+    assert L.ifx_quantize_u8(fake, fake, 12, 3, None, fake, None) == 1
+    assert L.ifx_quantize_u8(fake, fake, 12, 5, fake, fake, None) == 2
+    assert L.ifx_quantize_u8(fake, fake, 12, 3, odd, fake, None) == 4
+    assert L.ifx_quantize_u8(odd, fake, 12, 3, fake, fake, None) == 4
+    assert L.ifx_dequantize_i32(None, fake, 4, 1.0, None) == 1
+    assert L.ifx_dequantize_i32(fake, fake, -1, 1.0, None) == 2
+    assert L.ifx_dequantize_i32(fake, word, 4, 1.0, None) == 4
+    assert L.ifx_dequantize_i32(fake, fake, 0, 1.0, None) == 0

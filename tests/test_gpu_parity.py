@@ -963,3 +963,74 @@ def test_fold_bn_feeds_the_fused_conv(ifx, orc):
     b_, m_, s_ = bias.cpu().numpy(), mult.cpu().numpy(), shift.cpu().numpy()
     got = gpu_conv(ifx, x, wt, b_, m_, s_, 3, 1, 1, ifx.RELU)
     np.testing.assert_array_equal(got, orc.conv_fused(x, wt, b_, m_, s_, 1, 1, ifx.RELU))
+
+
+# ------------------------------------------------------------------ input quantisation, logits
+def _round_up16(n):
+    return (n + 15) // 16 * 16
+
+
+@pytest.mark.parametrize("shape", [(2, 224, 224, 3), (1, 7, 5, 3), (3, 1, 1, 1), (1, 3, 3, 5), (1, 1, 1, 6)])
+def test_quantize_f32(ifx, orc, shape):
+    """fp32 NHWC image -> int8 codes, element by element against the oracle: random values, exact
+    ties (channel 0 has mult 1), saturation, +-inf and NaN; counts with a ragged tail (count % 4)
+    written inside guard bands."""
+    note(f"quantize_f32 {shape}")
+    rng = np.random.default_rng(sum(shape) + 11)
+    c = shape[-1]
+    x = rng.normal(0, 60, shape).astype(np.float32)
+    mult = rng.uniform(0.5, 2.0, c).astype(np.float32)
+    mult[0] = 1.0
+    flat = x.reshape(-1)
+    ch0 = flat[0::c]
+    k = min(ch0.size, 64)
+    ch0[:k] = np.arange(k) - k // 2 + 0.5            # exact ties at mult 1
+    flat[0::c] = ch0
+    specials = np.array([np.nan, np.inf, -np.inf, 1e30, -1e30, 127.5, -128.5], np.float32)
+    m = min(specials.size, flat.size)
+    flat[flat.size - m:] = specials[:m]
+    q, whole = guarded(_round_up16(flat.size))
+    ifx.quantize_f32(cu(x), cu(mult), out=q[:flat.size].view(shape))
+    torch.cuda.synchronize()
+    check_guards(whole)
+    np.testing.assert_array_equal(q[:flat.size].cpu().numpy().reshape(shape), orc.quantize_f32(x, mult))
+
+
+@pytest.mark.parametrize("shape", [(2, 224, 224, 3), (1, 9, 7, 3), (2, 1, 1, 1), (1, 2, 3, 5)])
+def test_quantize_u8(ifx, orc, shape):
+    """uint8 NHWC image -> int8 codes with ImageNet-style float32 means and 1 / (std * s_x)
+    multipliers, and a channel with mean 127.5 and mult 1 (every code an exact tie)."""
+    note(f"quantize_u8 {shape}")
+    rng = np.random.default_rng(sum(shape) + 23)
+    c = shape[-1]
+    x = rand(rng, shape, 0, 255, np.uint8)
+    mean = np.resize(np.array([123.675, 116.28, 103.53], np.float32), c)
+    mult = np.resize((1.0 / (np.array([58.395, 57.12, 57.375]) * 0.02)).astype(np.float32), c)
+    mean[0], mult[0] = 127.5, 1.0
+    n = x.size
+    q, whole = guarded(_round_up16(n))
+    ifx.quantize_u8(cu(x), cu(mean), cu(mult), out=q[:n].view(shape))
+    torch.cuda.synchronize()
+    check_guards(whole)
+    np.testing.assert_array_equal(q[:n].cpu().numpy().reshape(shape), orc.quantize_u8(x, mean, mult))
+
+
+@pytest.mark.parametrize("shape", [(2048, 1000), (37, 1000), (1, 3), (5, 1)])
+def test_dequantize_logits(ifx, orc, shape):
+    """int32 logits -> float32: full-range values (conversions that round beyond 2^24) and a scale
+    that is not a power of two, compared bit for bit."""
+    note(f"dequantize {shape}")
+    rng = np.random.default_rng(shape[0] + shape[1])
+    q = rand(rng, shape, -(1 << 31), (1 << 31) - 1, np.int32)
+    flat = q.reshape(-1)
+    edge = np.array([(1 << 24) + 1, -((1 << 24) + 3), (1 << 31) - 1, -(1 << 31), 0], np.int32)
+    flat[:min(edge.size, flat.size)] = edge[:flat.size]
+    scale = np.float32(0.0123)
+    n = q.size
+    y, whole = guarded(_round_up16(4 * n), torch.float32)
+    ifx.dequantize_i32(cu(q), float(scale), out=y[:n].view(shape))
+    torch.cuda.synchronize()
+    check_guards(whole)
+    got = y[:n].cpu().numpy().reshape(shape)
+    want = orc.dequantize_i32(q, scale)
+    np.testing.assert_array_equal(got.view(np.int32), want.view(np.int32))
