@@ -471,6 +471,20 @@ def extra_configs(stream, steps: int, warmup: int, skip: str) -> dict:
         del w
         gc.collect()
         torch.cuda.empty_cache()
+    # the on-device input quantisation of a whole batch (fp32 NHWC image -> int8 codes): HBM-bound,
+    # 4 bytes read and 1 written per element
+    import convolution_int8_implicit_amd as ifx
+    shape = (2048, 224, 224, 3)
+    g = torch.Generator(device="cuda").manual_seed(7)
+    x = torch.randn(shape, generator=g, device="cuda") * 60.0
+    mult = torch.tensor([1.0, 0.9, 1.1], dtype=torch.float32, device="cuda")
+    q = torch.empty(shape, dtype=torch.int8, device="cuda")
+    t = time_steps(lambda: ifx.quantize_f32(x, mult, out=q, stream=stream), stream, min(steps, 50), warmup)
+    byts = 5 * x.numel()
+    out["quantize_f32"] = {"workload": "fp32 NHWC image -> int8 codes, 2048 x 224 x 224 x 3", "us": round(t * 1e6, 2),
+                           "alg_gbps": round(byts / t / 1e9, 1), "frac_hbm": round(byts / t / PEAK_HBM, 4)}
+    del x, q
+    torch.cuda.empty_cache()
     return out
 
 
