@@ -822,6 +822,13 @@ def main():
             launches = [conv_launch(dcs[0], wl.convs[0], n, wl.h, wl.w, w["step"])]
     reps = max(1, min(args.steps, 5) if args.workload == "net" else args.steps)
     evs = []
+    # The replay feeds the stream one launch at a time, so a pause of the host (a garbage-collector
+    # pass over the many small ctypes objects) can leave the GPU idle between a launch's start event
+    # and its kernel, which the event pair would then count as kernel time: no collection runs
+    # while the replays are issued.
+    import gc
+    gc.collect()
+    gc.disable()
     torch.cuda.synchronize()
     for _ in range(reps):
         for name, ops, byts, fn in launches:
@@ -834,6 +841,7 @@ def main():
             b.record(stream)
             evs.append((name, ops, byts, a, b))
     torch.cuda.synchronize()
+    gc.enable()
     if args.per_launch:
         # launch i of every repetition: its average time, its own floor, and the fraction
         real = [(nm, o, b) for nm, o, b, _ in launches if nm is not None]
