@@ -1034,3 +1034,30 @@ def test_dequantize_logits(ifx, orc, shape):
     got = y[:n].cpu().numpy().reshape(shape)
     want = orc.dequantize_i32(q, scale)
     np.testing.assert_array_equal(got.view(np.int32), want.view(np.int32))
+
+
+@pytest.mark.parametrize("u8", [False, True])
+def test_quantized_image_feeds_the_stem(ifx, orc, u8):
+    """The pre-processing and the stem chained on the device: an fp32 (or uint8) NHWC image quantised
+    by ifx_quantize_* and read by the fused stem (IFX_INPUT_NHWC) equals the oracle's quantisation
+    followed by the oracle's stem."""
+    note(f"quantize -> stem u8={u8}")
+    rng = np.random.default_rng(41 + u8)
+    n, h, w, c = 2, 64, 64, 3
+    mult = np.array([0.9, 1.1, 0.75], np.float32)
+    if u8:
+        x = rand(rng, (n, h, w, c), 0, 255, np.uint8)
+        mean = np.array([123.675, 116.28, 103.53], np.float32)
+        q = ifx.quantize_u8(cu(x), cu(mean), cu(mult))
+        q_ref = orc.quantize_u8(x, mean, mult)
+    else:
+        x = rng.normal(0, 70, (n, h, w, c)).astype(np.float32)
+        q = ifx.quantize_f32(cu(x), cu(mult))
+        q_ref = orc.quantize_f32(x, mult)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(q.cpu().numpy(), q_ref)
+    wt = rand(rng, (64, 7, 7, c), -127, 127)
+    bias, mult_s, shift = params(rng, 64)
+    flags = ifx.RELU | ifx.MAXPOOL
+    got = gpu_conv(ifx, q.cpu().numpy(), wt, bias, mult_s, shift, 7, 2, 3, flags | ifx.INPUT_NHWC)
+    np.testing.assert_array_equal(got, orc.conv_fused(q_ref, wt, bias, mult_s, shift, 2, 3, flags))
